@@ -1,0 +1,386 @@
+/*
+ * moe_oracle.cpp -- plain CPU reference for the MoE verify-pass layer.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the CPU
+ * baseline of the benchmark, never by the product path.  Written for
+ * readability, not speed: loops in the order of the definitions, fp64
+ * accumulation, no blocking, no fusion.
+ *
+ * Sources (web pages; sections as titled there):
+ *  [MoE]  "Deep Dive into Mixture of Experts: From 1991 to DeepSeek-V3"
+ *         s1 "1991: Where It Started"            -- dense mixture
+ *         s2 "2017: The Sparse-Gating Leap"      -- logits, top-k, softmax
+ *                                                   over the k, weighted sum
+ *         s5 "DeepSeek-V3 and the Current State of the Art"
+ *                                                -- shared experts, weight 1
+ *  [SDM]  "Speculative Decoding for Mixture-of-Experts Models: Expert Bytes,
+ *         Kernel Bandwidth and the Best Draft Length", abstract
+ *                                                -- per-slot vs dedup bytes
+ *
+ * Readings taken where the pages are silent (each also used by the tests):
+ *  R1  experts are SwiGLU FFNs, W2 (silu(W1 x) . W3 x), no biases; the pages
+ *      only write experts[idx](x).
+ *  R2  top-k order is (logit descending, expert index ascending); slot 0 is
+ *      the largest, as a topk routine returns it.  The comparison is made on
+ *      the logits rounded to fp32, the precision the GPU path decides in,
+ *      since the pages fix none.  Near-ties (gap < tie_eps) are flagged.
+ *  R3  the softmax is over the k selected logits (the sketch's comment says
+ *      it is renormalised over just the top-k).
+ *  R4  bf16 weight configs round the token to bf16 before the experts and the
+ *      SwiGLU product to bf16 before W2 (round to nearest, ties to even,
+ *      taken on the fp32 value as the GPU path does); fp32 configs round
+ *      nothing.
+ *  R5  the dense mixture of s1 uses the same softmax gate over all E experts.
+ */
+#include "moe_oracle.h"
+
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <thread>
+#include <vector>
+
+namespace {
+
+bool shape_ok(const oracle_shape *s) {
+  return s && s->d > 0 && s->E > 0 && s->k > 0 && s->k <= s->E && s->f > 0 &&
+         s->S >= 0 && (s->wdtype == ORACLE_F32 || s->wdtype == ORACLE_BF16);
+}
+
+size_t elem_bytes(const oracle_shape *s) { return s->wdtype == ORACLE_BF16 ? 2 : 4; }
+
+/* value of the n-th element of a weight array of the shape's type */
+double weight_at(const oracle_shape *s, const void *base, size_t n) {
+  if (s->wdtype == ORACLE_F32) return (double)((const float *)base)[n];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[n] << 16;
+  float v;
+  std::memcpy(&v, &bits, 4);
+  return (double)v;
+}
+
+float bf16_bits_to_float(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float v;
+  std::memcpy(&v, &bits, 4);
+  return v;
+}
+
+/* R4: the rounding applied to activations on bf16 configs */
+double act_round(const oracle_shape *s, double v) {
+  if (s->wdtype == ORACLE_F32) return v;
+  return (double)bf16_bits_to_float(oracle_bf16_rne((float)v));
+}
+
+double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+const void *offset_weights(const oracle_shape *s, const void *base, size_t elems) {
+  return (const void *)((const char *)base + elems * elem_bytes(s));
+}
+
+/* pointers to W1, W3, W2 of routed expert e (shared=false) or shared expert e */
+void expert_mats(const oracle_shape *s, const oracle_weights *wts, int e, bool shared,
+                 const void **W1, const void **W3, const void **W2) {
+  size_t fd = (size_t)s->f * (size_t)s->d;
+  const void *w13 = shared ? wts->ws13 : wts->w13;
+  const void *w2 = shared ? wts->ws2 : wts->w2;
+  *W1 = offset_weights(s, w13, (size_t)e * 2 * fd);
+  *W3 = offset_weights(s, w13, ((size_t)e * 2 + 1) * fd);
+  *W2 = offset_weights(s, w2, (size_t)e * fd);
+}
+
+/* R2: does expert a come before expert b in the selection order? */
+bool before(const std::vector<float> &key, int a, int b) {
+  if (key[a] != key[b]) return key[a] > key[b];
+  return a < b;
+}
+
+/* Run a list of independent jobs over n_threads std::threads. */
+template <class Job>
+void run_jobs(size_t n_jobs, int n_threads, const Job &job) {
+  if (n_threads <= 1 || n_jobs <= 1) {
+    for (size_t i = 0; i < n_jobs; ++i) job(i);
+    return;
+  }
+  size_t nt = std::min<size_t>((size_t)n_threads, n_jobs);
+  std::vector<std::thread> pool;
+  for (size_t w = 0; w < nt; ++w)
+    pool.emplace_back([&, w]() {
+      for (size_t i = w; i < n_jobs; i += nt) job(i);
+    });
+  for (auto &th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+uint16_t oracle_bf16_rne(float x) {
+  uint32_t bits;
+  std::memcpy(&bits, &x, 4);
+  if (std::isnan(x)) return (uint16_t)((bits >> 16) | 0x0040u);
+  /* The two bf16 neighbours of x: truncation toward zero, and one unit of
+   * the last place further from zero.  Choose the nearer; on a tie, the one
+   * whose last mantissa bit is 0. */
+  uint16_t lo = (uint16_t)(bits >> 16);
+  uint16_t hi = (uint16_t)(lo + 1);
+  if ((bits & 0xFFFFu) == 0) return lo;
+  double xv = (double)x;
+  double dlo = std::fabs(xv - (double)bf16_bits_to_float(lo));
+  double dhi = std::fabs((double)bf16_bits_to_float(hi) - xv);
+  if (std::isinf(bf16_bits_to_float(hi)) && !std::isinf(x)) {
+    /* hi overflowed to infinity: it still counts as the value 2^128 */
+    dhi = std::ldexp(1.0, 128) - std::fabs(xv);
+  }
+  if (dlo < dhi) return lo;
+  if (dhi < dlo) return hi;
+  return (lo & 1u) ? hi : lo;
+}
+
+int oracle_gate_logits(const oracle_shape *s, const float *gate_w, const float *x,
+                       int32_t n_tokens, double *logits) {
+  if (!shape_ok(s) || !gate_w || !x || !logits || n_tokens < 0) return -1;
+  /* [MoE] s2: logits = x @ gate_weights, one score per expert */
+  for (int t = 0; t < n_tokens; ++t)
+    for (int e = 0; e < s->E; ++e) {
+      double acc = 0.0;
+      for (int i = 0; i < s->d; ++i)
+        acc += (double)x[(size_t)t * s->d + i] * (double)gate_w[(size_t)e * s->d + i];
+      logits[(size_t)t * s->E + e] = acc;
+    }
+  return 0;
+}
+
+int oracle_route(const oracle_shape *s, const float *gate_w, const float *x,
+                 int32_t n_tokens, double tie_eps, double *logits, int32_t *idx,
+                 double *w, double *margin, uint8_t *flags) {
+  if (!shape_ok(s) || !gate_w || !x || !idx || !w || n_tokens < 0) return -1;
+  const int E = s->E, k = s->k;
+  std::vector<double> L((size_t)n_tokens * E);
+  oracle_gate_logits(s, gate_w, x, n_tokens, L.data());
+  if (logits) std::memcpy(logits, L.data(), L.size() * sizeof(double));
+
+  for (int t = 0; t < n_tokens; ++t) {
+    const double *Lt = &L[(size_t)t * E];
+    std::vector<float> key(E);
+    for (int e = 0; e < E; ++e) key[e] = (float)Lt[e];
+
+    /* [MoE] s2: top_k_vals, top_k_idx = topk(logits, k).  Selection by
+     * repeated search for the best remaining expert under R2. */
+    std::vector<int> order;
+    std::vector<bool> taken(E, false);
+    int rounds = (k < E) ? k + 1 : k; /* one more for the margin */
+    for (int r = 0; r < rounds; ++r) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || before(key, e, best))) best = e;
+      taken[best] = true;
+      order.push_back(best);
+    }
+    for (int j = 0; j < k; ++j) idx[(size_t)t * k + j] = order[j];
+
+    /* [MoE] s2: top_k_weights = softmax(top_k_vals), renormalised over the k */
+    double vmax = Lt[order[0]];
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += std::exp(Lt[order[j]] - vmax);
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = std::exp(Lt[order[j]] - vmax) / denom;
+
+    double m = (k < E) ? Lt[order[k - 1]] - Lt[order[k]]
+                       : std::numeric_limits<double>::infinity();
+    if (margin) margin[t] = m;
+    if (flags) {
+      uint8_t fl = 0;
+      if (m < tie_eps) fl |= ORACLE_FLAG_BOUNDARY;
+      for (int j = 0; j + 1 < k; ++j)
+        if (Lt[order[j]] - Lt[order[j + 1]] < tie_eps) fl |= ORACLE_FLAG_ORDER;
+      flags[t] = fl;
+    }
+  }
+  return 0;
+}
+
+int oracle_expert(const oracle_shape *s, const void *W1, const void *W3, const void *W2,
+                  const float *x, double *out) {
+  if (!shape_ok(s) || !W1 || !W3 || !W2 || !x || !out) return -1;
+  const int d = s->d, f = s->f;
+  /* R4: the token as the experts see it */
+  std::vector<double> xt(d);
+  for (int i = 0; i < d; ++i) xt[i] = act_round(s, (double)x[i]);
+  /* R1: a = silu(W1 xt) * (W3 xt), rounded per R4 */
+  std::vector<double> a(f);
+  for (int r = 0; r < f; ++r) {
+    double h = 0.0, g = 0.0;
+    for (int i = 0; i < d; ++i) {
+      h += weight_at(s, W1, (size_t)r * d + i) * xt[i];
+      g += weight_at(s, W3, (size_t)r * d + i) * xt[i];
+    }
+    double prod = silu(h) * g;
+    a[r] = (s->wdtype == ORACLE_BF16) ? act_round(s, (double)(float)prod) : prod;
+  }
+  /* out = W2 a */
+  for (int c = 0; c < d; ++c) {
+    double acc = 0.0;
+    for (int r = 0; r < f; ++r) acc += weight_at(s, W2, (size_t)c * f + r) * a[r];
+    out[c] = acc;
+  }
+  return 0;
+}
+
+int oracle_layer(const oracle_shape *s, const oracle_weights *wts, const float *x,
+                 int32_t n_tokens, const int32_t *idx, const double *w, int32_t engine,
+                 int32_t n_threads, double *y, uint64_t *bytes, int32_t *n_unique) {
+  if (!shape_ok(s) || !wts || !wts->w13 || !wts->w2 || !x || !idx || !w || !y ||
+      n_tokens < 0 || (engine != 0 && engine != 1))
+    return -1;
+  if (s->S > 0 && (!wts->ws13 || !wts->ws2)) return -1;
+  const int d = s->d, k = s->k, S = s->S, N = n_tokens;
+  for (size_t i = 0; i < (size_t)N * k; ++i)
+    if (idx[i] < 0 || idx[i] >= s->E) return -1;
+  const uint64_t Be = 3ull * (uint64_t)d * (uint64_t)s->f * elem_bytes(s);
+
+  /* o[t][j] = expert_{idx[t][j]}(x_t);  osh[t][s] = shared_s(x_t) */
+  std::vector<double> o((size_t)N * k * d), osh((size_t)N * S * d);
+
+  /* One job = one expert evaluation on one token. */
+  struct Job {
+    int t, slot, e;
+    bool shared;
+  };
+  std::vector<Job> jobs;
+  uint64_t routed_bytes = 0;
+  int32_t U = 0;
+  if (engine == 0) {
+    /* [SDM] per-slot: every (token, slot) reads its expert */
+    for (int t = 0; t < N; ++t)
+      for (int j = 0; j < k; ++j) {
+        jobs.push_back({t, j, idx[(size_t)t * k + j], false});
+        routed_bytes += Be;
+      }
+    std::vector<bool> seen(s->E, false);
+    for (size_t i = 0; i < (size_t)N * k; ++i)
+      if (!seen[idx[i]]) { seen[idx[i]] = true; ++U; }
+  } else {
+    /* [SDM] dedup: each distinct selected expert is read once per pass and
+     * applied to every (token, slot) that chose it */
+    for (int e = 0; e < s->E; ++e) {
+      bool used = false;
+      for (int t = 0; t < N; ++t)
+        for (int j = 0; j < k; ++j)
+          if (idx[(size_t)t * k + j] == e) {
+            jobs.push_back({t, j, e, false});
+            used = true;
+          }
+      if (used) {
+        routed_bytes += Be;
+        ++U;
+      }
+    }
+  }
+  /* [MoE] s5: shared experts run on every token, read once per pass */
+  for (int sh = 0; sh < S; ++sh)
+    for (int t = 0; t < N; ++t) jobs.push_back({t, sh, sh, true});
+
+  run_jobs(jobs.size(), n_threads, [&](size_t i) {
+    const Job &jb = jobs[i];
+    const void *W1, *W3, *W2;
+    expert_mats(s, wts, jb.e, jb.shared, &W1, &W3, &W2);
+    double *dst = jb.shared ? &osh[((size_t)jb.t * S + jb.slot) * d]
+                            : &o[((size_t)jb.t * k + jb.slot) * d];
+    oracle_expert(s, W1, W3, W2, x + (size_t)jb.t * d, dst);
+  });
+
+  /* [MoE] s2 / s5: output = sum over slots of weight * expert output, then the
+   * shared experts; slot order in both engines */
+  for (int t = 0; t < N; ++t)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += w[(size_t)t * k + j] * o[((size_t)t * k + j) * d + c];
+      for (int sh = 0; sh < S; ++sh) acc += osh[((size_t)t * S + sh) * d + c];
+      y[(size_t)t * d + c] = acc;
+    }
+  if (bytes) {
+    bytes[0] = routed_bytes;
+    bytes[1] = (uint64_t)S * Be;
+  }
+  if (n_unique) *n_unique = U;
+  return 0;
+}
+
+int oracle_dense_mixture(const oracle_shape *s, const float *gate_w,
+                         const oracle_weights *wts, const float *x, int32_t n_tokens,
+                         double *y) {
+  if (!shape_ok(s) || !gate_w || !wts || !x || !y || n_tokens < 0) return -1;
+  if (s->S > 0 && (!wts->ws13 || !wts->ws2)) return -1;
+  const int d = s->d, E = s->E, S = s->S;
+  std::vector<double> L((size_t)n_tokens * E), out(d);
+  oracle_gate_logits(s, gate_w, x, n_tokens, L.data());
+  for (int t = 0; t < n_tokens; ++t) {
+    /* [MoE] s1: the gate weights every expert and every expert runs (R5) */
+    double vmax = L[(size_t)t * E];
+    for (int e = 1; e < E; ++e) vmax = std::max(vmax, L[(size_t)t * E + e]);
+    double denom = 0.0;
+    for (int e = 0; e < E; ++e) denom += std::exp(L[(size_t)t * E + e] - vmax);
+    std::vector<double> acc(d, 0.0);
+    for (int e = 0; e < E; ++e) {
+      double p = std::exp(L[(size_t)t * E + e] - vmax) / denom;
+      const void *W1, *W3, *W2;
+      expert_mats(s, wts, e, false, &W1, &W3, &W2);
+      oracle_expert(s, W1, W3, W2, x + (size_t)t * d, out.data());
+      for (int c = 0; c < d; ++c) acc[c] += p * out[c];
+    }
+    for (int sh = 0; sh < S; ++sh) {
+      const void *W1, *W3, *W2;
+      expert_mats(s, wts, sh, true, &W1, &W3, &W2);
+      oracle_expert(s, W1, W3, W2, x + (size_t)t * d, out.data());
+      for (int c = 0; c < d; ++c) acc[c] += out[c];
+    }
+    for (int c = 0; c < d; ++c) y[(size_t)t * d + c] = acc[c];
+  }
+  return 0;
+}
+
+int oracle_pass_bytes(const oracle_shape *s, const int32_t *idx, int32_t n_tokens,
+                      uint64_t *perslot, uint64_t *dedup, uint64_t *shared,
+                      int32_t *n_unique) {
+  if (!shape_ok(s) || !idx || n_tokens < 0) return -1;
+  const uint64_t Be = 3ull * (uint64_t)s->d * (uint64_t)s->f * elem_bytes(s);
+  std::vector<bool> seen(s->E, false);
+  int32_t U = 0;
+  for (size_t i = 0; i < (size_t)n_tokens * s->k; ++i) {
+    if (idx[i] < 0 || idx[i] >= s->E) return -1;
+    if (!seen[idx[i]]) { seen[idx[i]] = true; ++U; }
+  }
+  /* [SDM] per-slot reads once per token and slot; dedup once per pass */
+  if (perslot) *perslot = (uint64_t)n_tokens * (uint64_t)s->k * Be;
+  if (dedup) *dedup = (uint64_t)U * Be;
+  if (shared) *shared = (uint64_t)s->S * Be;
+  if (n_unique) *n_unique = U;
+  return 0;
+}
+
+int oracle_compact(const oracle_shape *s, const int32_t *idx, int32_t n_tokens,
+                   int32_t *counts, int32_t *offs, int32_t *list, int32_t *uniq,
+                   int32_t *n_unique) {
+  if (!shape_ok(s) || !idx || !counts || !offs || !list || !uniq || !n_unique ||
+      n_tokens < 0)
+    return -1;
+  const int E = s->E;
+  const size_t slots = (size_t)n_tokens * s->k;
+  for (size_t i = 0; i < slots; ++i)
+    if (idx[i] < 0 || idx[i] >= E) return -1;
+  int32_t U = 0, pos = 0;
+  for (int e = 0; e < E; ++e) {
+    offs[e] = pos;
+    int32_t c = 0;
+    for (size_t i = 0; i < slots; ++i)
+      if (idx[i] == e) list[pos + c++] = (int32_t)i;
+    counts[e] = c;
+    pos += c;
+    uniq[e] = -1;
+    if (c > 0) uniq[U++] = e;
+  }
+  offs[E] = pos;
+  *n_unique = U;
+  return 0;
+}
+
+}  // extern "C"
