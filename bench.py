@@ -1,0 +1,363 @@
+#!/usr/bin/env python3
+"""Benchmark: µs and effective HBM GB/s per n-token MoE verify pass, per-slot
+vs dedup, on one MI355X.
+
+Workload (default): the DeepSeek-V2-Lite-shaped MoE layer (d_model 2048, 64
+routed experts top-6 + 2 shared, SwiGLU d_ff 1408, bf16 weights, fp32 gate),
+hidden states an AR(1) chain with rho 0.85, verify passes of n = 1..16
+tokens.  Weights and inputs are seeded synthetic draws made on the GPU.
+
+A step is one verify pass of n tokens (default n = 16) through the whole
+path for both engines: gate + top-k + softmax, then the per-slot expert pass;
+gate + top-k + softmax, then the dedup expert pass (compaction, expert FFNs,
+shared experts, combine).  Each engine call streams a different layer from a
+rotation of weight sets larger than the on-chip caches, so no call finds the
+previous call's experts cached.  `value` is the step's algorithmic bytes
+(gate + requested expert bytes of both engines) over its time, inputs
+resident in HBM.
+
+The JSON line also carries the n = 1..16 sweep (µs and GB/s per engine, the
+dedup byte share u(n), the bandwidth ratio r(n), measured and predicted
+crossovers), the roofline of the dominant kernel (the W1/W3 + SwiGLU kernel,
+timed with HIP events on the launch stream) and the CPU oracle timed on
+this host as a reported baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from speculative_decode_verify_gate_amd import binding as B  # noqa: E402
+from speculative_decode_verify_gate_amd import synth  # noqa: E402
+
+METRIC = "µs & effective HBM GB/s per n-token MoE verify pass, per-slot vs dedup"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Engines:
+    """Route + expert pass for both engines with reusable workspaces."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        self.shape = B.shape_of(cfg)
+        self.ws_route = B.Workspace()
+        self.ws_ps = B.Workspace()
+        self.ws_dd = B.Workspace()
+        self.nu = torch.zeros((1,), dtype=torch.int32, device="cuda")
+
+    def route(self, lay, x):
+        return B.route(self.shape, lay["gate_w"], x, ws=self.ws_route)
+
+    def perslot(self, lay, x, idx, w, y):
+        return B.expert_pass_perslot(self.shape, lay, x, idx, w, y=y, ws=self.ws_ps)
+
+    def dedup(self, lay, x, idx, w, y):
+        return B.expert_pass_dedup(self.shape, lay, x, idx, w, y=y, n_unique=self.nu,
+                                   ws=self.ws_dd)
+
+
+def expert_bytes(cfg):
+    return 3 * cfg.d * cfg.f * cfg.wbytes
+
+
+def gate_bytes(cfg):
+    return cfg.d * cfg.E * 4
+
+
+def unique_count(idx_host, E):
+    v = idx_host.reshape(-1)
+    v = v[(v >= 0) & (v < E)]
+    return int(np.unique(v).size)
+
+
+def run_sweep(cfg, eng, layers, xs, n_values, reps):
+    """Per n: reps passes per engine, each on the next layer of the rotation.
+    Returns a list of per-n records."""
+    out = []
+    nL = len(layers)
+    turn = 0
+    Be = expert_bytes(cfg)
+    for n in n_values:
+        N = cfg.tokens(n)
+        y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+        ev = []
+        # keep the GPU busy while the host queues the whole batch, so that no
+        # event pair measures host launch latency
+        torch.cuda._sleep(20_000_000)
+        for rep in range(reps):
+            x = xs[(n, rep)]
+            rec = {}
+            for name in ("perslot", "dedup"):
+                lay = layers[turn % nL]
+                turn += 1
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record()
+                idx, w = eng.route(lay, x)
+                e1.record()
+                getattr(eng, name)(lay, x, idx, w, y)
+                e2.record()
+                rec[name] = (e0, e1, e2, idx)
+            ev.append(rec)
+        torch.cuda.synchronize()
+        t = {"perslot": [], "dedup": []}
+        tr = {"perslot": [], "dedup": []}
+        U = {"perslot": [], "dedup": []}
+        for rec in ev:
+            for name, (e0, e1, e2, idx) in rec.items():
+                tr[name].append(e0.elapsed_time(e1) * 1e3)
+                t[name].append(e1.elapsed_time(e2) * 1e3)
+                U[name].append(unique_count(idx.cpu().numpy(), cfg.E))
+        k, S = cfg.k, cfg.S
+        r = {"n": n, "tokens": N}
+        for name in ("perslot", "dedup"):
+            us = float(np.median(t[name]))
+            routed = (N * k * Be) if name == "perslot" else float(np.mean(U[name])) * Be
+            req = routed + S * Be
+            r[name] = {"us": round(us, 2), "us_p10": round(float(np.percentile(t[name], 10)), 2),
+                       "us_p90": round(float(np.percentile(t[name], 90)), 2),
+                       "route_us": round(float(np.median(tr[name])), 2),
+                       "requested_MB": round(req / 1e6, 3),
+                       "GBs": round(req / us / 1e3, 1),
+                       "hbm_frac": round(req / us / 1e3 / HBM_PEAK_GBS, 3),
+                       "routed_GBs": round(routed / us / 1e3, 1)}
+        u_bar = float(np.mean(U["dedup"])) / (N * k)
+        r["u_bar"] = round(u_bar, 4)
+        r["U_mean"] = round(float(np.mean(U["dedup"])), 2)
+        # r(n): effective routed-byte bandwidth of dedup over that of per-slot
+        r["r"] = round(r["dedup"]["routed_GBs"] / r["perslot"]["routed_GBs"], 4)
+        r["dedup_faster"] = r["dedup"]["us"] < r["perslot"]["us"]
+        out.append(r)
+        log(f"  n={n:2d} perslot {r['perslot']['us']:8.1f} us {r['perslot']['GBs']:7.0f} GB/s | "
+            f"dedup {r['dedup']['us']:8.1f} us {r['dedup']['GBs']:7.0f} GB/s | "
+            f"u={u_bar:.3f} r={r['r']:.3f}")
+    return out
+
+
+def timed_steps(cfg, eng, layers, x, steps, warmup):
+    """The headline step at one pass size, K timed steps after W warmups."""
+    nL = len(layers)
+    N = x.shape[0]
+    y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+    turn = 0
+
+    def one_step(record):
+        nonlocal turn
+        evs = []
+        for name in ("perslot", "dedup"):
+            lay = layers[turn % nL]
+            turn += 1
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            idx, w = eng.route(lay, x)
+            getattr(eng, name)(lay, x, idx, w, y)
+            if record:
+                e1.record()
+                evs.append((name, e0, e1, idx))
+        return evs
+
+    for _ in range(warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    B.timing_read()            # drop anything recorded before
+    B.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    all_ev = []
+    for _ in range(steps):
+        all_ev.append(one_step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.timing_enable(False)
+    kt = B.timing_read()
+    per = {"perslot": [], "dedup": []}
+    us_list = {"perslot": [], "dedup": []}
+    for evs in all_ev:
+        for name, e0, e1, idx in evs:
+            us_list[name].append(e0.elapsed_time(e1) * 1e3)
+            per[name].append(unique_count(idx.cpu().numpy(), cfg.E))
+    return wall, kt, us_list, per
+
+
+def cpu_baseline(cfg, layer, x, seconds):
+    """The CPU oracle (as written, not tuned) on the same pass, on this host."""
+    import oracle as O
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    s = O.Shape(cfg.d, cfg.E, cfg.k, cfg.f, cfg.S, O.BF16 if cfg.wdtype == "bf16" else O.F32)
+    x_np = x.cpu().numpy()
+    gate = layer["gate_w"].cpu().numpy()
+    r = O.route(s, gate, x_np)
+    used = np.unique(r["idx"])
+    hdt = np.uint16 if cfg.wdtype == "bf16" else np.float32
+    host_w13 = np.zeros((cfg.E,) + tuple(layer["w13"].shape[1:]), hdt)
+    host_w2 = np.zeros((cfg.E,) + tuple(layer["w2"].shape[1:]), hdt)
+    for e in used:
+        host_w13[e] = synth.to_host_bits(layer["w13"][e])
+        host_w2[e] = synth.to_host_bits(layer["w2"][e])
+    ws13, ws2 = synth.to_host_bits(layer["ws13"]), synth.to_host_bits(layer["ws2"])
+    passes = 0
+    t0 = time.perf_counter()
+    U = 0
+    while True:
+        r = O.route(s, gate, x_np)
+        _, rb, sb, U = O.layer(s, host_w13, host_w2, ws13, ws2, x_np, r["idx"], r["w"],
+                               engine="dedup", n_threads=threads)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / passes
+    req = gate_bytes(cfg) + (U + cfg.S) * expert_bytes(cfg)
+    return {"value": round(req / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "us_per_pass": round(dt * 1e6, 1),
+            "sample": f"{passes} oracle pass(es) of the n={x.shape[0] // cfg.n_seq} "
+                      f"{cfg.name} verify pass (route + dedup layer, fp64), "
+                      f"{threads} threads, {dt * passes:.1f} s"}
+
+
+def traffic_record(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "speculative_decode_verify_gate_amd", "csrc", "expert.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="v2lite", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--n", type=int, default=None, help="pass size of the timed step")
+    ap.add_argument("--layers", type=int, default=None, help="weight sets in the rotation")
+    ap.add_argument("--reps", type=int, default=24, help="passes per n in the sweep")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the layer is not sharded across GPUs in this "
+              "build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    cfg = synth.CONFIGS[args.config]
+    n_head = args.n or max(cfg.n_values)
+    layer_bytes = (cfg.E + cfg.S) * expert_bytes(cfg)
+    n_layers = args.layers or max(2, min(8, int(8e9 // layer_bytes)))
+    log(f"[bench] {cfg.name}: {n_layers} weight sets of {layer_bytes / 1e9:.2f} GB, "
+        f"timed step n={n_head}")
+    layers = []
+    for L in range(n_layers):
+        layers.append(synth.make_layer(cfg, "cuda", layer=L))
+        torch.cuda.synchronize()
+        log(f"[bench] weights {L + 1}/{n_layers} drawn")
+    eng = Engines(cfg)
+
+    sweep = None
+    if not args.no_sweep:
+        xs = {(n, rep): synth.make_hidden(cfg, n, rep, "cuda")
+              for n in cfg.n_values for rep in range(args.reps)}
+        log("[bench] sweep warmup")
+        run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 2)
+        log("[bench] sweep")
+        sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps)
+        del xs
+
+    x = synth.make_hidden(cfg, n_head, 99, "cuda")
+    log(f"[bench] timed steps: {args.warmup} warmup + {args.steps}")
+    wall, kt, us_list, U_list = timed_steps(cfg, eng, layers, x, args.steps, args.warmup)
+    N = cfg.tokens(n_head)
+    Be = expert_bytes(cfg)
+    ps_bytes = gate_bytes(cfg) + (N * cfg.k + cfg.S) * Be
+    dd_bytes = [gate_bytes(cfg) + (u + cfg.S) * Be for u in U_list["dedup"]]
+    step_bytes = ps_bytes + float(np.mean(dd_bytes))
+    ms_step = wall / args.steps * 1e3
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: W1/W3 + SwiGLU, algorithmic bytes per launch =
+    # (instances streamed) x (2 d f bytes of one instance's W1 and W3)
+    up_unit = 2 * cfg.d * cfg.f * cfg.wbytes
+    up_ms, up_launches = kt["up"]
+    up_units = sum(N * cfg.k + cfg.S for _ in U_list["perslot"]) + \
+        sum(u + cfg.S for u in U_list["dedup"])
+    up_bytes = up_units * up_unit
+    up_avg_us = up_ms * 1e3 / max(1, up_launches)
+    achieved = up_bytes / (up_ms * 1e-3) / 1e9 if up_ms > 0 else None
+    traffic = traffic_record("expert_up", cfg.name)
+
+    engines_at_head = {}
+    for name in ("perslot", "dedup"):
+        us = float(np.median(us_list[name]))
+        b = ps_bytes if name == "perslot" else float(np.mean(dd_bytes))
+        engines_at_head[name] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
+                                 "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 3)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.wdtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}-shaped MoE layer, one verify pass of n={n_head}"
+                               f" tokens{' x %d sequences' % cfg.n_seq if cfg.n_seq > 1 else ''}"
+                               f", per-slot and dedup engines",
+                   "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
+                   "shared_experts": cfg.S, "weights": cfg.wdtype, "rho": cfg.rho,
+                   "tokens": N, "weight_sets_rotated": n_layers},
+        "engines_at_step_n": engines_at_head,
+        "roofline": {"bound": "hbm", "kernel": "expert_up (W1/W3 + SwiGLU)",
+                     "achieved": None if achieved is None else round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
+                     "avg_launch_us": round(up_avg_us, 2), "launches": up_launches,
+                     "unit_bytes": up_unit},
+        "kernel_ms": {k: round(v[0], 3) for k, v in kt.items()},
+        "kernel_launches": {k: v[1] for k, v in kt.items()},
+    }
+    if sweep is not None:
+        out["sweep"] = sweep
+        cross_m = next((r["n"] for r in sweep if r["dedup_faster"]), None)
+        cross_p = next((r["n"] for r in sweep if r["u_bar"] < r["r"]), None)
+        out["crossover"] = {"measured": cross_m if cross_m is not None else "never",
+                            "predicted_u_lt_r": cross_p if cross_p is not None else "never"}
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(cfg, layers[0], x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

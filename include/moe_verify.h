@@ -1,0 +1,182 @@
+/*
+ * moe_verify.h -- C ABI of the MI355X (gfx950) MoE verify-pass library.
+ *
+ * One sparsely-gated MoE layer evaluated over one speculative-decoding
+ * verification pass of N tokens: gate logits, top-k selection, softmax over
+ * the k selected logits, SwiGLU expert FFNs combined by those weights, plus
+ * always-on shared experts.  Two engines compute the same layer output:
+ *   per-slot -- every (token, slot) streams its expert's weights, so a pass
+ *               requests N*k expert-sized reads;
+ *   dedup    -- every distinct selected expert is streamed once per pass and
+ *               applied to all tokens that chose it (U expert-sized reads).
+ * Sources: "Deep Dive into Mixture of Experts: From 1991 to DeepSeek-V3",
+ * sections 2 (top-k sparse gating) and 5 (shared experts); "Speculative
+ * Decoding for Mixture-of-Experts Models: Expert Bytes, Kernel Bandwidth and
+ * the Best Draft Length", abstract (per-slot versus deduplicating engines,
+ * requested bytes); "Building a Terminal Based LLM Inference Internals
+ * Explorer - Part 3: Speculative Decoding", section "The Flow" (one verify
+ * pass scores the newest token plus the gamma drafts, so n = gamma + 1).
+ *
+ * Conventions shared by every call:
+ *  - All tensors are dense row-major.  Device pointers are owned by the
+ *    caller; the library never allocates, frees or synchronises in these
+ *    calls.  Work is enqueued on `stream` (a hipStream_t passed as void*,
+ *    NULL = the null stream) and is complete when the stream is.
+ *  - Every call returns a moe_status.  Arguments are validated on the host
+ *    before anything is enqueued; on an error nothing is enqueued and no
+ *    output is written.  A failed launch returns MOE_ERR_HIP.
+ *  - Workspace: the device calls take (workspace, workspace_bytes).  With
+ *    workspace == NULL the call stores the bytes it needs for this shape and
+ *    token count in *workspace_bytes and returns MOE_OK without launching.
+ *    Otherwise *workspace_bytes is the size supplied; a smaller size than
+ *    needed returns MOE_ERR_WORKSPACE.  The workspace needs no
+ *    initialisation, must be 256-byte aligned, and may not be shared by
+ *    calls that can run concurrently.
+ *  - Routing entries passed to the expert passes must lie in [0, E); that
+ *    cannot be checked on the host without a copy, so an out-of-range entry
+ *    is treated on the device as an empty slot (no weights read, zero
+ *    contribution) rather than read out of bounds.
+ *  - Limits: 1 <= N <= MOE_MAX_TOKENS, 1 <= k <= min(E, MOE_MAX_TOPK),
+ *    N*k <= MOE_MAX_SLOTS, E <= MOE_MAX_EXPERTS, 0 <= S <= MOE_MAX_SHARED,
+ *    d_model and d_ff multiples of 32 (so each lane moves whole 16-byte
+ *    vectors), violations return MOE_ERR_INVALID_ARG (count limits) or
+ *    MOE_ERR_UNSUPPORTED (alignment limits).
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status_code {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, count out of range, bad dtype */
+  MOE_ERR_UNSUPPORTED = -2, /* well-formed but outside what the kernels do */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than required */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or launch failed */
+};
+
+/* expert weight element type (the gate and activations are always fp32) */
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+#define MOE_MAX_TOKENS 64
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_SLOTS 512
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_SHARED 4
+
+typedef struct moe_shape {
+  int32_t d_model;   /* d: hidden width */
+  int32_t n_experts; /* E: routed experts */
+  int32_t top_k;     /* k: experts selected per token */
+  int32_t d_ff;      /* f: inner width of every expert */
+  int32_t n_shared;  /* S: always-on shared experts (weight 1) */
+  int32_t wdtype;    /* moe_dtype of the expert weights */
+} moe_shape;
+
+/* Expert weights, device pointers, element type wdtype.
+ *   w13  [E][2][f][d]  row r of w13[e][0] is row r of W1 (gate projection),
+ *                      of w13[e][1] row r of W3 (up projection)
+ *   w2   [E][d][f]     W2 (down projection)
+ *   ws13 [S][2][f][d], ws2 [S][d][f]  shared experts; NULL iff S == 0.
+ * Expert e computes  W2 * (silu(W1 xt) . (W3 xt))  with xt = x rounded to
+ * bf16 (nearest-even) and the product rounded to bf16 before W2 when
+ * wdtype == MOE_BF16; nothing is rounded for MOE_F32.  Accumulation is fp32. */
+typedef struct moe_expert_weights {
+  const void *w13;
+  const void *w2;
+  const void *ws13;
+  const void *ws2;
+} moe_expert_weights;
+
+/* Gate + top-k + softmax over the k ("Deep Dive into Mixture of Experts",
+ * section 2: logits = x @ gate_weights, top_k of the logits, softmax of the
+ * selected values).
+ *   gate_w   [E][d] fp32 device (row e scores expert e)
+ *   x        [N][d] fp32 device hidden states of the pass
+ *   logits   [N][E] fp32 device output, or NULL
+ *   topk_idx [N][k] int32 device output: slot j holds the j-th expert in the
+ *            order (logit descending, expert index ascending)
+ *   topk_w   [N][k] fp32 device output: exp(L_j - L_0) / sum_i exp(L_i - L_0)
+ *   margin   [N]    fp32 device output L_(k) - L_(k+1) (+inf if k == E), or
+ *            NULL; a small margin marks a near-tie at the selection boundary. */
+int moe_route(const moe_shape *shape, const float *gate_w, const float *x,
+              int32_t n_tokens, float *logits, int32_t *topk_idx, float *topk_w,
+              float *margin, void *workspace, size_t *workspace_bytes, void *stream);
+
+/* Per-slot expert pass ("Speculative Decoding for Mixture-of-Experts
+ * Models", abstract: a per-slot engine reads each selected expert once per
+ * token).  Every (token t, slot j) streams expert topk_idx[t][j]; shared
+ * experts are streamed once for all tokens.
+ *   x        [N][d] fp32 device
+ *   topk_idx [N][k] int32 device, topk_w [N][k] fp32 device (any routing,
+ *            e.g. the output of moe_route)
+ *   y        [N][d] fp32 device output:
+ *            y[t] = sum_j topk_w[t][j] * expert_{topk_idx[t][j]}(x_t)
+ *                   + sum_s shared_s(x_t), summed in slot order. */
+int moe_expert_pass_perslot(const moe_shape *shape, const moe_expert_weights *weights,
+                            const float *x, int32_t n_tokens, const int32_t *topk_idx,
+                            const float *topk_w, float *y, void *workspace,
+                            size_t *workspace_bytes, void *stream);
+
+/* Deduplicating expert pass (same abstract: a deduplicating engine reads each
+ * selected expert once per pass).  Same arguments and the same y as the
+ * per-slot pass; in addition
+ *   n_unique [1] int32 device output (or NULL): U, the number of distinct
+ *            valid experts in topk_idx.
+ * The workspace begins with the routing-trace compaction, int32 each:
+ *   [0]                 U
+ *   [1 .. E]            counts[e]: slots that chose expert e
+ *   [E+1 .. 2E+1]       offs[e]: exclusive prefix sum of counts (E+1 values)
+ *   [2E+2 .. 3E+1]      uniq[u]: the experts with counts > 0, ascending
+ *                       (entries at u >= U are unspecified)
+ *   [3E+2 .. 3E+1+N*k]  list: slot ids t*k+j grouped by expert in uniq
+ *                       order, ascending within an expert
+ * valid once the stream has completed the call. */
+int moe_expert_pass_dedup(const moe_shape *shape, const moe_expert_weights *weights,
+                          const float *x, int32_t n_tokens, const int32_t *topk_idx,
+                          const float *topk_w, float *y, int32_t *n_unique,
+                          void *workspace, size_t *workspace_bytes, void *stream);
+
+/* Requested expert bytes of one pass, on the host (same abstract: step time
+ * is the bytes each kernel requests over its effective bandwidth).
+ * B_e = 3 * d * f * sizeof(weight); perslot = N*k*B_e, dedup = U*B_e,
+ * shared = S*B_e, n_unique = U.  topk_idx_host is host memory; an entry
+ * outside [0, E) returns MOE_ERR_INVALID_ARG.  Any output pointer may be
+ * NULL.  Synchronous, pure, thread-safe. */
+int moe_pass_bytes(const moe_shape *shape, const int32_t *topk_idx_host, int32_t n_tokens,
+                   uint64_t *perslot_bytes, uint64_t *dedup_bytes, uint64_t *shared_bytes,
+                   int32_t *n_unique);
+
+/* Human-readable name of a status code (static storage). */
+const char *moe_status_string(int status);
+
+/* Per-kernel timing, for measurement.  While enabled, every kernel the calls
+ * above launch is bracketed by a pair of HIP events recorded on the call's
+ * stream, and moe_timing_read() adds up the elapsed time per kernel kind.
+ * Kernel kinds (index into the arrays): */
+enum moe_kernel_kind {
+  MOE_K_GATE = 0,     /* gate logits, split over K */
+  MOE_K_TOPK = 1,     /* top-k + softmax per token */
+  MOE_K_COMPACT = 2,  /* routing-trace compaction (dedup) */
+  MOE_K_UP = 3,       /* W1/W3 + SwiGLU over all expert instances */
+  MOE_K_DOWN = 4,     /* W2 over all expert instances */
+  MOE_K_COMBINE = 5,  /* weighted sum in slot order + shared experts */
+  MOE_K_COUNT = 6
+};
+/* on != 0 enables, 0 disables.  Not thread-safe; meant for one driver thread. */
+int moe_timing_enable(int on);
+/* Waits for every recorded event pair, adds their elapsed times to ms[kind],
+ * their number to launches[kind] (arrays of MOE_K_COUNT), and clears the
+ * record.  Either array may be NULL. */
+int moe_timing_read(double *ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_VERIFY_H */

@@ -1,0 +1,223 @@
+"""ctypes binding of libmoeverify.so (include/moe_verify.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the HIP stream, status codes become exceptions.  Every step of
+the layer runs in the library's gfx950 kernels; there is no fallback, and
+loading fails loudly when the library has not been built.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeverify.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MAX_TOKENS, MAX_TOPK, MAX_SLOTS, MAX_EXPERTS, MAX_SHARED = 64, 16, 512, 256, 4
+KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine")
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+class Shape(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("d_ff", C.c_int32), ("n_shared", C.c_int32), ("wdtype", C.c_int32)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("w13", C.c_void_p), ("w2", C.c_void_p), ("ws13", C.c_void_p),
+                ("ws2", C.c_void_p)]
+
+
+def load():
+    """Load the built library (never builds; never falls back)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m speculative_decode_verify_gate_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    P, i32, sz = C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)
+    lib.moe_route.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
+    lib.moe_expert_pass_perslot.argtypes = [P, P, P, i32, P, P, P, P, sz, P]
+    lib.moe_expert_pass_dedup.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
+    lib.moe_pass_bytes.argtypes = [P, P, i32, P, P, P, P]
+    lib.moe_status_string.argtypes = [C.c_int]
+    lib.moe_status_string.restype = C.c_char_p
+    lib.moe_timing_enable.argtypes = [C.c_int]
+    lib.moe_timing_read.argtypes = [P, P]
+    for fn in ("moe_route", "moe_expert_pass_perslot", "moe_expert_pass_dedup",
+               "moe_pass_bytes", "moe_timing_enable", "moe_timing_read"):
+        getattr(lib, fn).restype = C.c_int
+    _lib = lib
+    return lib
+
+
+_NEED = {}
+
+
+def _shape_key(shape):
+    return (shape.d_model, shape.n_experts, shape.top_k, shape.d_ff, shape.n_shared,
+            shape.wdtype)
+
+
+def _need(fn, shape, n, query):
+    """Workspace bytes of a call, asked once per (call, shape, token count)."""
+    key = (fn, _shape_key(shape), n)
+    if key not in _NEED:
+        need = C.c_size_t(0)
+        _check(fn, query(C.byref(need)))
+        _NEED[key] = need.value
+    return _NEED[key]
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise MoeError(fn, rc, load().moe_status_string(rc).decode())
+
+
+def make_shape(d_model, n_experts, top_k, d_ff, n_shared=0, wdtype="bf16"):
+    wd = {"bf16": MOE_BF16, "f32": MOE_F32, MOE_BF16: MOE_BF16, MOE_F32: MOE_F32}[wdtype]
+    return Shape(d_model, n_experts, top_k, d_ff, n_shared, wd)
+
+
+def shape_of(cfg):
+    """Shape of a synth.LayerConfig."""
+    return make_shape(cfg.d, cfg.E, cfg.k, cfg.f, cfg.S, cfg.wdtype)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on the GPU "
+                         f"(got {t.dtype} on {t.device}, contiguous={t.is_contiguous()})")
+    return t
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Workspace:
+    """A grow-only device byte buffer reused across calls (256-byte aligned)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def _weights(shape, w):
+    wdt = torch.bfloat16 if shape.wdtype == MOE_BF16 else torch.float32
+    keep = [_dev(w["w13"], wdt, "w13"), _dev(w["w2"], wdt, "w2"),
+            _dev(w.get("ws13"), wdt, "ws13"), _dev(w.get("ws2"), wdt, "ws2")]
+    return keep, Weights(*[None if t is None else t.data_ptr() for t in keep])
+
+
+def route(shape, gate_w, x, *, idx=None, w=None, logits=None, margin=None, ws=None):
+    """Gate logits, top-k and softmax over the k.  Returns (idx int32 [N][k],
+    w fp32 [N][k]); logits [N][E] and margin [N] are filled when given."""
+    lib = load()
+    gate_w = _dev(gate_w, torch.float32, "gate_w")
+    x = _dev(x, torch.float32, "x")
+    n = x.shape[0]
+    if idx is None:
+        idx = torch.empty((n, shape.top_k), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((n, shape.top_k), dtype=torch.float32, device=x.device)
+    _dev(idx, torch.int32, "idx"), _dev(w, torch.float32, "w")
+    _dev(logits, torch.float32, "logits"), _dev(margin, torch.float32, "margin")
+    need = _need("moe_route", shape, n, lambda nb: lib.moe_route(
+        C.byref(shape), _ptr(gate_w), _ptr(x), n, None, _ptr(idx), _ptr(w), None, None, nb,
+        None))
+    ws = ws or Workspace(x.device)
+    buf = ws.get(need)
+    have = C.c_size_t(buf.numel())
+    _check("moe_route", lib.moe_route(C.byref(shape), _ptr(gate_w), _ptr(x), n, _ptr(logits),
+                                      _ptr(idx), _ptr(w), _ptr(margin), _ptr(buf),
+                                      C.byref(have), _stream()))
+    return idx, w
+
+
+def _expert_pass(fn, shape, weights, x, idx, w, y, ws, n_unique=None):
+    lib = load()
+    keep, cw = _weights(shape, weights)
+    x = _dev(x, torch.float32, "x")
+    idx = _dev(idx, torch.int32, "idx")
+    w = _dev(w, torch.float32, "w")
+    n = x.shape[0]
+    if y is None:
+        y = torch.empty((n, shape.d_model), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    extra = [] if n_unique is False else [None]
+    need = _need(fn, shape, n, lambda nb: getattr(lib, fn)(
+        C.byref(shape), C.byref(cw), _ptr(x), n, _ptr(idx), _ptr(w), _ptr(y), *extra, None, nb,
+        None))
+    ws = ws or Workspace(x.device)
+    buf = ws.get(need)
+    have = C.c_size_t(buf.numel())
+    extra = [] if n_unique is False else [_ptr(n_unique)]
+    _check(fn, getattr(lib, fn)(C.byref(shape), C.byref(cw), _ptr(x), n, _ptr(idx), _ptr(w),
+                                _ptr(y), *extra, _ptr(buf), C.byref(have), _stream()))
+    del keep
+    return y
+
+
+def expert_pass_perslot(shape, weights, x, idx, w, *, y=None, ws=None):
+    """Per-slot engine.  weights: dict with w13, w2 (and ws13, ws2 when the
+    shape has shared experts).  Returns y fp32 [N][d]."""
+    return _expert_pass("moe_expert_pass_perslot", shape, weights, x, idx, w, y, ws,
+                        n_unique=False)
+
+
+def expert_pass_dedup(shape, weights, x, idx, w, *, y=None, n_unique=None, ws=None):
+    """Deduplicating engine; n_unique (int32 [1] on the GPU) receives U."""
+    _dev(n_unique, torch.int32, "n_unique")
+    return _expert_pass("moe_expert_pass_dedup", shape, weights, x, idx, w, y, ws,
+                        n_unique=n_unique)
+
+
+def pass_bytes(shape, idx_host):
+    """Requested bytes of a pass from a host routing trace:
+    (perslot, dedup, shared, n_unique)."""
+    lib = load()
+    t = torch.as_tensor(idx_host).to(torch.int32).contiguous()
+    if t.is_cuda:
+        raise ValueError("pass_bytes takes a host routing trace")
+    out = (C.c_uint64 * 3)()
+    u = C.c_int32(0)
+    base = C.addressof(out)
+    _check("moe_pass_bytes", lib.moe_pass_bytes(C.byref(shape), C.c_void_p(t.data_ptr()),
+                                                t.shape[0], C.c_void_p(base),
+                                                C.c_void_p(base + 8), C.c_void_p(base + 16),
+                                                C.byref(u)))
+    return int(out[0]), int(out[1]), int(out[2]), int(u.value)
+
+
+def timing_enable(on=True):
+    _check("moe_timing_enable", load().moe_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """{kind: (total_ms, launches)} accumulated since the last read."""
+    ms = (C.c_double * 6)()
+    cnt = (C.c_int64 * 6)()
+    _check("moe_timing_read", load().moe_timing_read(C.addressof(ms), C.addressof(cnt)))
+    return {k: (ms[i], int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}

@@ -1,0 +1,301 @@
+// abi.cpp -- the C ABI of include/moe_verify.h: argument validation,
+// workspace sizing, the launch sequence of each call and the optional
+// per-kernel event timing.  Kernels live in router.hip, compact.hip and
+// expert.hip.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kernels.h"
+#include "moe_verify.h"
+
+namespace {
+
+using moe::align_up;
+
+constexpr size_t kAlign = 256;
+
+int check_shape(const moe_shape *s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->d_model <= 0 || s->d_ff <= 0 || s->n_experts <= 0 || s->top_k <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->top_k > s->n_experts || s->top_k > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (s->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared < 0 || s->n_shared > MOE_MAX_SHARED) return MOE_ERR_INVALID_ARG;
+  if (s->wdtype != MOE_F32 && s->wdtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->d_model % 32 != 0 || s->d_ff % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  // 16-row tiles index rows with 32-bit ints
+  if ((int64_t)s->d_model * s->d_ff > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(const moe_shape *s, int32_t n) {
+  if (n < 1 || n > MOE_MAX_TOKENS) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)n * s->top_k > MOE_MAX_SLOTS) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+bool aligned(const void *p) { return ((uintptr_t)p % kAlign) == 0; }
+
+size_t wbytes(const moe_shape *s) { return s->wdtype == MOE_BF16 ? 2 : 4; }
+
+// rows of the per-instance activation / output buffers: N*k routed + S*N shared
+size_t entry_rows(const moe_shape *s, int n) {
+  return (size_t)n * s->top_k + (size_t)s->n_shared * n;
+}
+
+size_t route_ws(const moe_shape *s, int n) {
+  return align_up((size_t)moe::gate_splits(s->d_model) * n * s->n_experts * sizeof(float),
+                  kAlign);
+}
+
+size_t cmp_ws(const moe_shape *s, int n) {
+  moe::CompactLayout L{s->n_experts, n * s->top_k};
+  return align_up((size_t)L.total() * sizeof(int32_t), kAlign);
+}
+
+size_t abuf_ws(const moe_shape *s, int n) {
+  return align_up(entry_rows(s, n) * s->d_ff * wbytes(s), kAlign);
+}
+
+size_t obuf_ws(const moe_shape *s, int n) {
+  return align_up(entry_rows(s, n) * s->d_model * sizeof(float), kAlign);
+}
+
+// Workspace query / size check shared by the device calls.  Returns
+// MOE_OK and sets *launch when the call should go ahead.
+int workspace_gate(void *ws, size_t *ws_bytes, size_t need, bool *launch) {
+  *launch = false;
+  if (!ws_bytes) return MOE_ERR_INVALID_ARG;
+  if (!ws) {
+    *ws_bytes = need;
+    return MOE_OK;
+  }
+  if (!aligned(ws)) return MOE_ERR_INVALID_ARG;
+  if (*ws_bytes < need) return MOE_ERR_WORKSPACE;
+  *launch = true;
+  return MOE_OK;
+}
+
+// ---- per-kernel event timing
+struct EventPair {
+  int kind;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<EventPair> pending;
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t take() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t st, F &&launch) {
+  Timing &tm = timing();
+  if (!tm.on) return launch();
+  hipEvent_t a, b;
+  {
+    std::lock_guard<std::mutex> lk(tm.mu);
+    a = tm.take();
+    b = tm.take();
+  }
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t err = hipEventRecord(a, st);
+  if (err == hipSuccess) err = launch();
+  if (err == hipSuccess) err = hipEventRecord(b, st);
+  std::lock_guard<std::mutex> lk(tm.mu);
+  tm.pending.push_back({kind, a, b});
+  return err;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int check_weights(const moe_shape *s, const moe_expert_weights *w) {
+  if (!w || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared > 0 && (!w->ws13 || !w->ws2)) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared == 0 && (w->ws13 || w->ws2)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x, int32_t n,
+                const int32_t *idx, const float *tw, float *y, int32_t *n_unique, bool dedup,
+                void *ws, size_t *ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
+  if ((rc = check_weights(s, w)) != MOE_OK) return rc;
+  if (!x || !idx || !tw || !y) return MOE_ERR_INVALID_ARG;
+  const size_t c_bytes = dedup ? cmp_ws(s, n) : 0;
+  const size_t a_bytes = abuf_ws(s, n);
+  const size_t need = c_bytes + a_bytes + obuf_ws(s, n);
+  bool launch;
+  if ((rc = workspace_gate(ws, ws_bytes, need, &launch)) != MOE_OK || !launch) return rc;
+
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char *base = (unsigned char *)ws;
+  int32_t *cmp = dedup ? (int32_t *)base : nullptr;
+  const bool bf16 = s->wdtype == MOE_BF16;
+
+  moe::ExpertArgs a{};
+  a.w13 = w->w13;
+  a.w2 = w->w2;
+  a.ws13 = w->ws13;
+  a.ws2 = w->ws2;
+  a.x = x;
+  a.idx = idx;
+  a.cmp = cmp;
+  a.abuf = base + c_bytes;
+  a.obuf = (float *)(base + c_bytes + a_bytes);
+  a.d = s->d_model;
+  a.f = s->d_ff;
+  a.E = s->n_experts;
+  a.k = s->top_k;
+  a.S = s->n_shared;
+  a.N = n;
+  a.dedup = dedup ? 1 : 0;
+  const int slots = n * s->top_k;
+  a.n_routed = dedup ? (slots < s->n_experts ? slots : s->n_experts) : slots;
+
+  hipError_t err = hipSuccess;
+  if (dedup)
+    err = timed(MOE_K_COMPACT, st, [&] {
+      return moe::launch_compact(idx, n, s->top_k, s->n_experts, cmp, n_unique, st);
+    });
+  if (err == hipSuccess) {
+    a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true);
+    err = timed(MOE_K_UP, st, [&] { return moe::launch_up(a, bf16, st); });
+  }
+  if (err == hipSuccess) {
+    a.lds_bytes = moe::expert_lds_bytes(n, s->d_ff, bf16, false);
+    err = timed(MOE_K_DOWN, st, [&] { return moe::launch_down(a, bf16, st); });
+  }
+  if (err == hipSuccess)
+    err = timed(MOE_K_COMBINE, st, [&] {
+      return moe::launch_combine(a.obuf, idx, tw, n, s->top_k, s->n_shared, s->d_model,
+                                 s->n_experts, y, st);
+    });
+  return status_of(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route(const moe_shape *s, const float *gate_w, const float *x, int32_t n,
+              float *logits, int32_t *topk_idx, float *topk_w, float *margin, void *ws,
+              size_t *ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
+  if (!gate_w || !x || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  bool launch;
+  if ((rc = workspace_gate(ws, ws_bytes, route_ws(s, n), &launch)) != MOE_OK || !launch)
+    return rc;
+  hipStream_t st = (hipStream_t)stream;
+  float *part = (float *)ws;
+  hipError_t err = timed(MOE_K_GATE, st, [&] {
+    return moe::launch_gate(gate_w, x, n, s->d_model, s->n_experts, part, st);
+  });
+  if (err == hipSuccess)
+    err = timed(MOE_K_TOPK, st, [&] {
+      return moe::launch_topk(part, moe::gate_splits(s->d_model), n, s->n_experts, s->top_k,
+                              logits, topk_idx, topk_w, margin, st);
+    });
+  return status_of(err);
+}
+
+int moe_expert_pass_perslot(const moe_shape *s, const moe_expert_weights *w, const float *x,
+                            int32_t n, const int32_t *idx, const float *tw, float *y,
+                            void *ws, size_t *ws_bytes, void *stream) {
+  return expert_pass(s, w, x, n, idx, tw, y, nullptr, false, ws, ws_bytes, stream);
+}
+
+int moe_expert_pass_dedup(const moe_shape *s, const moe_expert_weights *w, const float *x,
+                          int32_t n, const int32_t *idx, const float *tw, float *y,
+                          int32_t *n_unique, void *ws, size_t *ws_bytes, void *stream) {
+  return expert_pass(s, w, x, n, idx, tw, y, n_unique, true, ws, ws_bytes, stream);
+}
+
+int moe_pass_bytes(const moe_shape *s, const int32_t *idx, int32_t n, uint64_t *perslot,
+                   uint64_t *dedup, uint64_t *shared, int32_t *n_unique) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
+  if (!idx) return MOE_ERR_INVALID_ARG;
+  const int E = s->n_experts;
+  std::vector<unsigned char> seen((size_t)E, 0);
+  int32_t U = 0;
+  const size_t slots = (size_t)n * s->top_k;
+  for (size_t i = 0; i < slots; ++i) {
+    const int32_t e = idx[i];
+    if (e < 0 || e >= E) return MOE_ERR_INVALID_ARG;
+    if (!seen[(size_t)e]) {
+      seen[(size_t)e] = 1;
+      ++U;
+    }
+  }
+  const uint64_t be = 3ull * (uint64_t)s->d_model * (uint64_t)s->d_ff * wbytes(s);
+  if (perslot) *perslot = (uint64_t)slots * be;
+  if (dedup) *dedup = (uint64_t)U * be;
+  if (shared) *shared = (uint64_t)s->n_shared * be;
+  if (n_unique) *n_unique = U;
+  return MOE_OK;
+}
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_timing_enable(int on) {
+  Timing &tm = timing();
+  std::lock_guard<std::mutex> lk(tm.mu);
+  tm.on = on != 0;
+  return MOE_OK;
+}
+
+int moe_timing_read(double *ms, int64_t *launches) {
+  Timing &tm = timing();
+  std::lock_guard<std::mutex> lk(tm.mu);
+  int rc = MOE_OK;
+  for (const EventPair &p : tm.pending) {
+    float el = 0.f;
+    if (hipEventSynchronize(p.stop) != hipSuccess ||
+        hipEventElapsedTime(&el, p.start, p.stop) != hipSuccess) {
+      rc = MOE_ERR_HIP;
+    } else {
+      if (ms) ms[p.kind] += (double)el;
+      if (launches) launches[p.kind] += 1;
+    }
+    tm.pool.push_back(p.start);
+    tm.pool.push_back(p.stop);
+  }
+  tm.pending.clear();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// kernels.h -- internal launch interface between the C ABI (abi.cpp) and the
+// gfx950 kernels.  Not installed; the public interface is include/moe_verify.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_verify.h"
+
+namespace moe {
+
+// Geometry shared by the launchers and the workspace sizing in abi.cpp.
+constexpr int kWave = 64;
+constexpr int kTile = 16;               // MFMA output tile is 16 rows x 16 tokens
+constexpr int kWavesPerBlock = 4;       // expert kernels: one 16-row tile per wave
+constexpr int kRowsPerBlock = kTile * kWavesPerBlock;
+constexpr int kGateKPerBlock = 256;     // gate logits: K elements per workgroup
+constexpr int kLdsBudget = 72 * 1024;   // bytes of staged activations per workgroup
+                                        // (two workgroups fit the 160 KB of a CU)
+constexpr int kLdsPad = 8;              // elements of padding per staged row
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Offsets (int32 elements) of the compaction record at the head of the dedup
+// workspace; the layout is part of the public contract.
+struct CompactLayout {
+  int E, slots;
+  __host__ __device__ int u() const { return 0; }
+  __host__ __device__ int counts() const { return 1; }
+  __host__ __device__ int offs() const { return 1 + E; }
+  __host__ __device__ int uniq() const { return 2 + 2 * E; }
+  __host__ __device__ int list() const { return 2 + 3 * E; }
+  __host__ __device__ int total() const { return 2 + 3 * E + slots; }
+};
+
+struct ExpertArgs {
+  const void *w13, *w2, *ws13, *ws2;
+  const float *x;         // [N][d]
+  const int32_t *idx;     // [N][k]
+  const int32_t *cmp;     // compaction record (dedup) or nullptr
+  void *abuf;             // [N*k + S*N][f] SwiGLU outputs, weight element type
+  float *obuf;            // [N*k + S*N][d] expert outputs
+  int d, f, E, k, S, N;
+  int dedup;              // 0: instance i is slot i; 1: instance u is uniq[u]
+  int n_routed;           // routed instances in the grid
+  int lds_bytes;          // dynamic LDS per workgroup
+};
+
+int gate_splits(int d);
+
+hipError_t launch_gate(const float *gate_w, const float *x, int N, int d, int E,
+                       float *part, hipStream_t st);
+hipError_t launch_topk(const float *part, int splits, int N, int E, int k, float *logits,
+                       int32_t *idx, float *w, float *margin, hipStream_t st);
+hipError_t launch_compact(const int32_t *idx, int N, int k, int E, int32_t *cmp,
+                          int32_t *n_unique, hipStream_t st);
+// bf16 != 0 selects bf16 weights, else fp32.
+hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_down(const ExpertArgs &a, bool bf16, hipStream_t st);
+hipError_t launch_combine(const float *obuf, const int32_t *idx, const float *w, int N,
+                          int k, int S, int d, int E, float *y, hipStream_t st);
+
+// Dynamic LDS for the expert kernels at this token count (activations of up
+// to min(N, 64) tokens staged per window).
+int expert_lds_bytes(int N, int K, bool bf16, bool up);
+
+}  // namespace moe

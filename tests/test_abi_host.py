@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports every function include/moe_verify.h declares, arguments are
+validated before anything is launched, workspace queries answer without
+launching, and the host byte accounting matches the oracle bit for bit."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from speculative_decode_verify_gate_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for fn in ("moe_route", "moe_expert_pass_perslot", "moe_expert_pass_dedup",
+               "moe_pass_bytes"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    for fn in _declared():
+        assert hasattr(lib, fn), fn
+
+
+def _shape(**kw):
+    base = dict(d_model=2048, n_experts=64, top_k=6, d_ff=1408, n_shared=2, wdtype="bf16")
+    base.update(kw)
+    return B.make_shape(**base)
+
+
+FAKE = C.c_void_p(0x100000)   # never dereferenced: every case fails validation first
+
+
+def _route(shape, n=4, gate=FAKE, x=FAKE, idx=FAKE, w=FAKE, ws=FAKE, nbytes=1 << 30):
+    sz = C.c_size_t(nbytes)
+    return B.load().moe_route(C.byref(shape), gate, x, n, None, idx, w, None, ws,
+                              C.byref(sz), None), sz.value
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(top_k=0), -1), (dict(top_k=65), -1), (dict(n_experts=300, top_k=6), -1),
+    (dict(n_shared=5), -1), (dict(wdtype=7), -1), (dict(d_model=2040), -2),
+    (dict(d_ff=1400), -2), (dict(top_k=17, n_experts=64), -1),
+])
+def test_bad_shapes_are_rejected(bad, code):
+    shape = _shape(**{k: v for k, v in bad.items() if k != "wdtype"})
+    if "wdtype" in bad:
+        shape.wdtype = bad["wdtype"]
+    assert _route(shape)[0] == code
+
+
+def test_bad_token_counts_and_pointers_are_rejected():
+    s = _shape()
+    assert _route(s, n=0)[0] == -1
+    assert _route(s, n=65)[0] == -1
+    assert _route(_shape(top_k=16, n_experts=64), n=33)[0] == -1   # 528 slots > 512
+    assert _route(s, gate=None)[0] == -1
+    assert _route(s, idx=None)[0] == -1
+    assert _route(s, ws=C.c_void_p(0x100010))[0] == -1              # misaligned workspace
+    assert _route(s, nbytes=16)[0] == -3                             # workspace too small
+
+
+def test_workspace_queries_answer_without_launching():
+    for n in (1, 16, 64):
+        s = _shape(n_experts=256, top_k=8, d_model=7168, d_ff=2048, n_shared=1)
+        rc, need = _route(s, n=n, ws=None, nbytes=0)
+        assert rc == 0 and need >= 4 * n * 256 * (7168 // 256)
+        lib = B.load()
+        cw = B.Weights(0x100000, 0x100000, 0x100000, 0x100000)
+        for fn, extra in (("moe_expert_pass_perslot", []), ("moe_expert_pass_dedup", [None])):
+            sz = C.c_size_t(0)
+            rc = getattr(lib, fn)(C.byref(s), C.byref(cw), FAKE, n, FAKE, FAKE, FAKE, *extra,
+                                  None, C.byref(sz), None)
+            assert rc == 0
+            rows = n * 8 + n * 1
+            assert sz.value >= rows * 2048 * 2 + rows * 7168 * 4
+            if fn.endswith("dedup"):
+                assert sz.value >= rows * 2048 * 2 + rows * 7168 * 4 + 4 * (3 * 256 + 2 + n * 8)
+
+
+def test_expert_pass_rejects_missing_shared_weights():
+    lib = B.load()
+    s = _shape()
+    sz = C.c_size_t(0)
+    cw = B.Weights(0x100000, 0x100000, None, None)
+    rc = lib.moe_expert_pass_perslot(C.byref(s), C.byref(cw), FAKE, 4, FAKE, FAKE, FAKE,
+                                     None, C.byref(sz), None)
+    assert rc == -1
+    s0 = _shape(n_shared=0)
+    cw2 = B.Weights(0x100000, 0x100000, 0x100000, None)
+    rc = lib.moe_expert_pass_perslot(C.byref(s0), C.byref(cw2), FAKE, 4, FAKE, FAKE, FAKE,
+                                     None, C.byref(sz), None)
+    assert rc == -1
+
+
+def test_pass_bytes_matches_oracle_bit_exact():
+    rng = np.random.default_rng(0)
+    for (d, E, k, f, S, wd) in [(256, 8, 2, 512, 0, "f32"), (4096, 8, 2, 14336, 0, "bf16"),
+                                (2048, 64, 6, 1408, 2, "bf16"), (7168, 256, 8, 2048, 1, "bf16")]:
+        s = B.make_shape(d, E, k, f, S, wd)
+        so = O.Shape(d, E, k, f, S, O.BF16 if wd == "bf16" else O.F32)
+        for n in (1, 2, 7, 16, 64):
+            if n * k > 512:
+                continue
+            idx = np.stack([rng.choice(E, k, replace=False) for _ in range(n)]).astype(np.int32)
+            assert B.pass_bytes(s, idx) == O.pass_bytes(so, idx)
+    with pytest.raises(B.MoeError):
+        B.pass_bytes(B.make_shape(256, 8, 2, 512), np.array([[0, 8]], dtype=np.int32))
+
+
+def test_status_strings():
+    lib = B.load()
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(-3) == b"workspace too small"

@@ -1,0 +1,263 @@
+"""GPU parity: the gfx950 library against the CPU oracle, through the C ABI.
+
+Bars: routing indices and byte counts bit-exact (ties to the lower index;
+tokens whose oracle margin or in-top-k gap is below 1e-4 are flagged and
+exempt from the index comparison, and counted); gate logits within 1e-4
+absolute; layer outputs within 1e-2 (bf16 weights, fp32 accumulation) or
+1e-5 (fp32 weights) of max|y_ref|; per-slot and dedup outputs bitwise
+identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from speculative_decode_verify_gate_amd import binding as B
+from speculative_decode_verify_gate_amd import synth
+from helpers import (LOGIT_ATOL, OUT_RTOL, TIE_EPS, WEIGHT_ATOL, host_layer, oracle_y,
+                     oshape, rel_err, small_config, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _check_route(cfg, gate_w_dev, x_dev, gate_w_np, x_np):
+    shape = B.shape_of(cfg)
+    n = x_dev.shape[0]
+    logits = torch.empty((n, cfg.E), dtype=torch.float32, device="cuda")
+    margin = torch.empty((n,), dtype=torch.float32, device="cuda")
+    idx, w = B.route(shape, gate_w_dev, x_dev, logits=logits, margin=margin)
+    torch.cuda.synchronize()
+    ref = O.route(oshape(cfg), gate_w_np, x_np, tie_eps=TIE_EPS)
+    assert np.max(np.abs(logits.cpu().numpy() - ref["logits"])) <= LOGIT_ATOL
+    ok = ref["flags"] == 0
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi[ok], ref["idx"][ok]), "routing differs on an unflagged token"
+    # flagged tokens still select a valid top-k of the GPU's own logits
+    gw = w.cpu().numpy()
+    assert np.all(np.abs(gw.sum(axis=1) - 1.0) <= 1e-6)
+    assert np.all(np.abs(gw[ok] - ref["w"][ok]) <= WEIGHT_ATOL)
+    if cfg.k < cfg.E:
+        assert np.all(np.abs(margin.cpu().numpy()[ok] - ref["margin"][ok]) <= LOGIT_ATOL)
+    for t in range(n):
+        assert len(set(gi[t].tolist())) == cfg.k and gi[t].min() >= 0 and gi[t].max() < cfg.E
+    return idx, w, ref, int((~ok).sum())
+
+
+def _run_both(cfg, lay_dev, x_dev, idx_dev, w_dev):
+    shape = B.shape_of(cfg)
+    y_ps = B.expert_pass_perslot(shape, lay_dev, x_dev, idx_dev, w_dev)
+    nu = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    ws = B.Workspace()
+    y_dd = B.expert_pass_dedup(shape, lay_dev, x_dev, idx_dev, w_dev, n_unique=nu, ws=ws)
+    torch.cuda.synchronize()
+    return y_ps, y_dd, int(nu.item()), ws
+
+
+# ------------------------------------------------------------- small shapes
+
+SMALL = [
+    # name, d, E, k, f, S, wdtype  (f=192: row groups with a ragged tail)
+    ("f32-ragged", 256, 8, 2, 192, 1, "f32"),
+    ("bf16-ragged", 256, 8, 2, 192, 1, "bf16"),
+    ("bf16-v2like", 512, 64, 6, 352, 2, "bf16"),
+    ("bf16-top1", 256, 16, 1, 128, 0, "bf16"),
+    ("bf16-single-expert", 128, 1, 1, 96, 0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+@pytest.mark.parametrize("n", [1, 3, 16, 17, 64])
+def test_small_layer_parity(case, n):
+    name, d, E, k, f, S, wdt = case
+    if n * k > B.MAX_SLOTS:
+        pytest.skip("beyond the slot limit")
+    cfg = small_config(name, d, E, k, f, S, wdt)
+    _say(f"[small] {name} n={n}")
+    lay = synth.make_layer(cfg, "cpu")
+    x = synth.make_hidden(cfg, n, 0, "cpu")
+    host = host_layer(lay)
+    x_np = x.numpy()
+    lay_dev, x_dev = to_dev(lay), x.cuda()
+    idx, w, ref, flagged = _check_route(cfg, lay_dev["gate_w"], x_dev, host["gate_w"], x_np)
+    # the expert passes are compared on the oracle's routing, so that a
+    # near-tie cannot move an output between experts
+    idx_o = torch.from_numpy(ref["idx"]).cuda()
+    w_o = torch.from_numpy(ref["w"].astype(np.float32)).cuda()
+    y_ps, y_dd, U, ws = _run_both(cfg, lay_dev, x_dev, idx_o, w_o)
+    y_ref, rb, sb, U_ref = oracle_y(cfg, host, x_np, ref["idx"], ref["w"].astype(np.float32))
+    assert U == U_ref
+    assert torch.equal(y_ps, y_dd), "per-slot and dedup outputs differ"
+    err = rel_err(y_ps.cpu().numpy(), y_ref)
+    _say(f"   rel err {err:.3e}  U={U}  flagged={flagged}")
+    assert err <= OUT_RTOL[wdt]
+    # the compaction record at the head of the dedup workspace
+    c = O.compact(oshape(cfg), ref["idx"])
+    rec = ws.buf[: 4 * (3 * E + 2 + n * k)].view(torch.int32).cpu().numpy()
+    assert rec[0] == c["n_unique"]
+    assert np.array_equal(rec[1:1 + E], c["counts"])
+    assert np.array_equal(rec[1 + E:2 + 2 * E], c["offs"])
+    assert np.array_equal(rec[2 + 2 * E:2 + 2 * E + U], c["uniq"])
+    assert np.array_equal(rec[2 + 3 * E:2 + 3 * E + n * k], c["list"])
+    # byte counts: host library call vs oracle, bit-exact
+    assert B.pass_bytes(B.shape_of(cfg), ref["idx"]) == O.pass_bytes(oshape(cfg), ref["idx"])
+
+
+def test_dedup_heavy_expert_over_64_tokens():
+    """One expert chosen by every token of a 64-token pass (m = 64) and by
+    several slots of the same token (duplicates in a caller's routing)."""
+    cfg = small_config("heavy", 256, 8, 4, 128, 1, "bf16")
+    n = 64
+    lay = synth.make_layer(cfg, "cpu")
+    x = synth.make_hidden(cfg, n, 0, "cpu")
+    host = host_layer(lay)
+    rng = np.random.default_rng(3)
+    idx = np.stack([np.concatenate([[5], rng.choice([0, 1, 2, 3, 4, 6, 7], 3, replace=False)])
+                    for _ in range(n)]).astype(np.int32)
+    idx[7] = [5, 5, 5, 2]          # duplicates: expert 5 appears 66 times in all
+    w = rng.random((n, 4)).astype(np.float32)
+    lay_dev = to_dev(lay)
+    y_ps, y_dd, U, _ = _run_both(cfg, lay_dev, x.cuda(), torch.from_numpy(idx).cuda(),
+                                 torch.from_numpy(w).cuda())
+    y_ref, _, _, U_ref = oracle_y(cfg, host, x.numpy(), idx, w)
+    assert U == U_ref
+    assert torch.equal(y_ps, y_dd)
+    assert rel_err(y_ps.cpu().numpy(), y_ref) <= OUT_RTOL["bf16"]
+
+
+def test_out_of_range_routing_is_an_empty_slot():
+    cfg = small_config("oob", 256, 8, 2, 128, 0, "bf16")
+    lay = synth.make_layer(cfg, "cpu")
+    x = synth.make_hidden(cfg, 4, 0, "cpu")
+    host = host_layer(lay)
+    idx = np.array([[1, 2], [3, 99], [-1, 0], [4, 5]], dtype=np.int32)
+    w = np.full((4, 2), 0.5, dtype=np.float32)
+    y_ps, y_dd, U, _ = _run_both(cfg, to_dev(lay), x.cuda(), torch.from_numpy(idx).cuda(),
+                                 torch.from_numpy(w).cuda())
+    assert torch.equal(y_ps, y_dd) and U == 6
+    # reference: the invalid slots contribute nothing
+    keep = (idx >= 0) & (idx < 8)
+    y_ref = np.zeros((4, 256))
+    for t in range(4):
+        for j in range(2):
+            if keep[t, j]:
+                e = idx[t, j]
+                o = O.expert(oshape(cfg), host["w13"][e, 0], host["w13"][e, 1], host["w2"][e],
+                             x.numpy()[t])
+                y_ref[t] += w[t, j] * o
+    assert rel_err(y_ps.cpu().numpy(), y_ref) <= OUT_RTOL["bf16"]
+
+
+def test_k_equals_E_matches_dense_mixture():
+    cfg = small_config("dense", 256, 8, 8, 128, 1, "f32")
+    lay = synth.make_layer(cfg, "cpu")
+    x = synth.make_hidden(cfg, 5, 0, "cpu")
+    host = host_layer(lay)
+    lay_dev = to_dev(lay)
+    idx, w = B.route(B.shape_of(cfg), lay_dev["gate_w"], x.cuda())
+    y_ps, y_dd, U, _ = _run_both(cfg, lay_dev, x.cuda(), idx, w)
+    yd = O.dense_mixture(oshape(cfg), host["gate_w"], host["w13"], host["w2"], host["ws13"],
+                         host["ws2"], x.numpy())
+    assert U == 8 and torch.equal(y_ps, y_dd)
+    assert rel_err(y_ps.cpu().numpy(), yd) <= OUT_RTOL["f32"]
+
+
+def test_router_ties_pick_lowest_index():
+    cfg = small_config("ties", 256, 16, 3, 64, 0, "f32")
+    lay = synth.make_layer(cfg, "cpu")
+    gw = lay["gate_w"].clone()
+    gw[9] = gw[2]
+    gw[11] = gw[2]
+    x = synth.make_hidden(cfg, 8, 0, "cpu")
+    idx, w = B.route(B.shape_of(cfg), gw.cuda(), x.cuda())
+    ref = O.route(oshape(cfg), gw.numpy(), x.numpy())
+    gi = idx.cpu().numpy()
+    for t in range(8):
+        sel = gi[t].tolist()
+        for a_, b_ in [(2, 9), (9, 11), (2, 11)]:
+            if b_ in sel:
+                assert a_ in sel and sel.index(a_) < sel.index(b_)
+    assert np.array_equal(gi, ref["idx"])
+
+
+def test_runs_are_bitwise_deterministic():
+    cfg = small_config("det", 512, 64, 6, 352, 2, "bf16")
+    lay_dev = to_dev(synth.make_layer(cfg, "cpu"))
+    x = synth.make_hidden(cfg, 16, 0, "cpu").cuda()
+    outs = []
+    for _ in range(3):
+        idx, w = B.route(B.shape_of(cfg), lay_dev["gate_w"], x)
+        y_ps, y_dd, U, _ = _run_both(cfg, lay_dev, x, idx, w)
+        outs.append((idx.clone(), y_ps.clone(), y_dd.clone()))
+    for o in outs[1:]:
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(o, outs[0]))
+
+
+def test_mfma_column_position_does_not_change_results():
+    """A token's output bits do not depend on which other tokens share its
+    MFMA tile: each token alone equals the same token inside a 16-token pass."""
+    cfg = small_config("colpos", 512, 4, 1, 256, 0, "bf16")
+    lay_dev = to_dev(synth.make_layer(cfg, "cpu"))
+    x = synth.make_hidden(cfg, 16, 0, "cpu").cuda()
+    idx = torch.zeros((16, 1), dtype=torch.int32, device="cuda")
+    w = torch.ones((16, 1), dtype=torch.float32, device="cuda")
+    shape = B.shape_of(cfg)
+    y_all = B.expert_pass_dedup(shape, lay_dev, x, idx, w)
+    for t in (0, 5, 15):
+        y_one = B.expert_pass_dedup(shape, lay_dev, x[t:t + 1].contiguous(), idx[:1], w[:1])
+        torch.cuda.synchronize()
+        assert torch.equal(y_one[0], y_all[t])
+
+
+# ------------------------------------------------------------- full-size configs
+
+def _full_case(name, n, rep=0, tokens=None):
+    cfg = synth.CONFIGS[name]
+    _say(f"[full] {name} n={n} rep={rep}")
+    lay_dev = synth.make_layer(cfg, "cuda")
+    x_dev = synth.make_hidden(cfg, n, rep, "cuda")
+    gate_np = lay_dev["gate_w"].cpu().numpy()
+    x_np = x_dev.cpu().numpy()
+    idx, w, ref, flagged = _check_route(cfg, lay_dev["gate_w"], x_dev, gate_np, x_np)
+    y_ps, y_dd, U, _ = _run_both(cfg, lay_dev, x_dev, idx, w)
+    assert torch.equal(y_ps, y_dd)
+    gi = idx.cpu().numpy()
+    assert U == O.pass_bytes(oshape(cfg), gi)[3]
+    # oracle on the GPU's own routing, on sampled tokens, fetching only the
+    # experts those tokens use
+    toks = np.arange(x_np.shape[0]) if tokens is None else np.asarray(tokens)
+    used = np.unique(gi[toks])
+    hdt = np.uint16 if cfg.wdtype == "bf16" else np.float32
+    host = {"w13": np.zeros((cfg.E,) + tuple(lay_dev["w13"].shape[1:]), hdt),
+            "w2": np.zeros((cfg.E,) + tuple(lay_dev["w2"].shape[1:]), hdt)}
+    for e in used:
+        host["w13"][e] = synth.to_host_bits(lay_dev["w13"][e])
+        host["w2"][e] = synth.to_host_bits(lay_dev["w2"][e])
+    host["ws13"] = synth.to_host_bits(lay_dev["ws13"])
+    host["ws2"] = synth.to_host_bits(lay_dev["ws2"])
+    y_ref, _, _, _ = oracle_y(cfg, host, x_np, gi, w.cpu().numpy(), tokens=toks)
+    err = rel_err(y_ps.cpu().numpy()[toks], y_ref)
+    _say(f"   rel err {err:.3e}  U={U}  flagged={flagged}")
+    assert err <= OUT_RTOL[cfg.wdtype]
+    del lay_dev
+    torch.cuda.empty_cache()
+
+
+def test_full_tiny():
+    _full_case("tiny", 4)
+
+
+@pytest.mark.parametrize("n", [1, 16])
+def test_full_v2lite(n):
+    _full_case("v2lite", n, tokens=[0, n - 1])
+
+
+def test_full_mixtral():
+    _full_case("mixtral", 8, tokens=[0, 7])
+
+
+def test_full_v3():
+    _full_case("v3", 16, tokens=[0, 63])
