@@ -144,50 +144,43 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps):
     return out
 
 
-def timed_steps(cfg, eng, layers, x, steps, warmup):
-    """The headline step at one pass size, K timed steps after W warmups."""
+def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=()):
+    """The headline step at one pass size: K timed steps after W warmups,
+    bracketed by device synchronisation.  With kernel_events, the library
+    brackets launches of those kernel kinds with HIP events on the launch
+    stream; otherwise nothing is recorded inside the timed region."""
     nL = len(layers)
     N = x.shape[0]
     y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
     turn = 0
+    idxs = {"perslot": [], "dedup": []}
 
-    def one_step(record):
+    def one_step(keep):
         nonlocal turn
-        evs = []
         for name in ("perslot", "dedup"):
             lay = layers[turn % nL]
             turn += 1
-            if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
             idx, w = eng.route(lay, x)
             getattr(eng, name)(lay, x, idx, w, y)
-            if record:
-                e1.record()
-                evs.append((name, e0, e1, idx))
-        return evs
+            if keep:
+                idxs[name].append(idx)
 
     for _ in range(warmup):
         one_step(False)
     torch.cuda.synchronize()
     B.timing_read()            # drop anything recorded before
-    B.timing_enable(True)
+    if kernel_events:
+        B.timing_enable(kernel_events)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    all_ev = []
     for _ in range(steps):
-        all_ev.append(one_step(True))
+        one_step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    B.timing_enable(False)
+    B.timing_enable(())
     kt = B.timing_read()
-    per = {"perslot": [], "dedup": []}
-    us_list = {"perslot": [], "dedup": []}
-    for evs in all_ev:
-        for name, e0, e1, idx in evs:
-            us_list[name].append(e0.elapsed_time(e1) * 1e3)
-            per[name].append(unique_count(idx.cpu().numpy(), cfg.E))
-    return wall, kt, us_list, per
+    U = {k: [unique_count(i.cpu().numpy(), cfg.E) for i in v] for k, v in idxs.items()}
+    return wall, kt, U
 
 
 def cpu_baseline(cfg, layer, x, seconds):
@@ -234,9 +227,10 @@ def traffic_record(kernel, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "speculative_decode_verify_gate_amd", "csrc", "expert.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    sha = hashlib.sha256()
+    for f in rec.get("source_files", []):
+        sha.update(open(os.path.join(ROOT, f), "rb").read())
+    if rec.get("source_sha256") != sha.hexdigest():
         return None
     return rec
 
@@ -253,6 +247,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (for scaling HBM "
+                         "byte counters) and print its byte counts")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -264,6 +261,18 @@ def main():
         print("bench.py needs the GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "launches": 5,
+                          "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}))
+        return
 
     cfg = synth.CONFIGS[args.config]
     n_head = args.n or max(cfg.n_values)
@@ -290,7 +299,7 @@ def main():
 
     x = synth.make_hidden(cfg, n_head, 99, "cuda")
     log(f"[bench] timed steps: {args.warmup} warmup + {args.steps}")
-    wall, kt, us_list, U_list = timed_steps(cfg, eng, layers, x, args.steps, args.warmup)
+    wall, _, U_list = timed_steps(cfg, eng, layers, x, args.steps, args.warmup)
     N = cfg.tokens(n_head)
     Be = expert_bytes(cfg)
     ps_bytes = gate_bytes(cfg) + (N * cfg.k + cfg.S) * Be
@@ -299,23 +308,26 @@ def main():
     ms_step = wall / args.steps * 1e3
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: W1/W3 + SwiGLU, algorithmic bytes per launch =
-    # (instances streamed) x (2 d f bytes of one instance's W1 and W3)
+    # Dominant kernel: W1/W3 + SwiGLU.  Timed live in a second timed region of
+    # the same steps in which the library brackets only that kernel with HIP
+    # events.  Algorithmic bytes per launch = (instances streamed) x (bytes of
+    # one instance's W1 and W3 = 2 d f s_w).
+    log("[bench] timed steps with up-kernel events")
+    _, kt, U_ev = timed_steps(cfg, eng, layers, x, args.steps, args.warmup,
+                              kernel_events=("up",))
     up_unit = 2 * cfg.d * cfg.f * cfg.wbytes
     up_ms, up_launches = kt["up"]
-    up_units = sum(N * cfg.k + cfg.S for _ in U_list["perslot"]) + \
-        sum(u + cfg.S for u in U_list["dedup"])
+    up_units = sum(N * cfg.k + cfg.S for _ in U_ev["perslot"]) + \
+        sum(u + cfg.S for u in U_ev["dedup"])
     up_bytes = up_units * up_unit
     up_avg_us = up_ms * 1e3 / max(1, up_launches)
     achieved = up_bytes / (up_ms * 1e-3) / 1e9 if up_ms > 0 else None
     traffic = traffic_record("expert_up", cfg.name)
 
-    engines_at_head = {}
-    for name in ("perslot", "dedup"):
-        us = float(np.median(us_list[name]))
-        b = ps_bytes if name == "perslot" else float(np.mean(dd_bytes))
-        engines_at_head[name] = {"us": round(us, 2), "GBs": round(b / us / 1e3, 1),
-                                 "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 3)}
+    engines_at_head = None
+    if sweep is not None:
+        rec = next(r for r in sweep if r["n"] == n_head)
+        engines_at_head = {k: rec[k] for k in ("perslot", "dedup")}
 
     out = {
         "metric": METRIC,
@@ -337,15 +349,16 @@ def main():
                    "shared_experts": cfg.S, "weights": cfg.wdtype, "rho": cfg.rho,
                    "tokens": N, "weight_sets_rotated": n_layers},
         "engines_at_step_n": engines_at_head,
+        "step_bytes": int(step_bytes),
         "roofline": {"bound": "hbm", "kernel": "expert_up (W1/W3 + SwiGLU)",
                      "achieved": None if achieved is None else round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
+                     "algorithmic_bytes_per_launch": int(up_bytes / max(1, up_launches)),
                      "avg_launch_us": round(up_avg_us, 2), "launches": up_launches,
                      "unit_bytes": up_unit},
-        "kernel_ms": {k: round(v[0], 3) for k, v in kt.items()},
-        "kernel_launches": {k: v[1] for k, v in kt.items()},
+        "up_kernel_ms_total": round(up_ms, 3),
     }
     if sweep is not None:
         out["sweep"] = sweep

@@ -132,8 +132,8 @@ int moe_expert_pass_perslot(const moe_shape *shape, const moe_expert_weights *we
  *   [0]                 U
  *   [1 .. E]            counts[e]: slots that chose expert e
  *   [E+1 .. 2E+1]       offs[e]: exclusive prefix sum of counts (E+1 values)
- *   [2E+2 .. 3E+1]      uniq[u]: the experts with counts > 0, ascending
- *                       (entries at u >= U are unspecified)
+ *   [2E+2 .. 3E+1]      uniq[u]: the experts with counts > 0, ascending,
+ *                       then -1 for u >= U
  *   [3E+2 .. 3E+1+N*k]  list: slot ids t*k+j grouped by expert in uniq
  *                       order, ascending within an expert
  * valid once the stream has completed the call. */
@@ -155,21 +155,24 @@ int moe_pass_bytes(const moe_shape *shape, const int32_t *topk_idx_host, int32_t
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_string(int status);
 
-/* Per-kernel timing, for measurement.  While enabled, every kernel the calls
- * above launch is bracketed by a pair of HIP events recorded on the call's
- * stream, and moe_timing_read() adds up the elapsed time per kernel kind.
- * Kernel kinds (index into the arrays): */
+/* Per-kernel timing, for measurement.  While enabled, every kernel of a
+ * selected kind that the calls above launch is bracketed by a pair of HIP
+ * events recorded on the call's stream, and moe_timing_read() adds up the
+ * elapsed time per kernel kind.  Each event pair adds a few microseconds of
+ * idle time around its kernel, so select only the kinds being measured.
+ * Kernel kinds (bit positions of the mask, indices into the arrays): */
 enum moe_kernel_kind {
-  MOE_K_GATE = 0,     /* gate logits, split over K */
-  MOE_K_TOPK = 1,     /* top-k + softmax per token */
-  MOE_K_COMPACT = 2,  /* routing-trace compaction (dedup) */
-  MOE_K_UP = 3,       /* W1/W3 + SwiGLU over all expert instances */
-  MOE_K_DOWN = 4,     /* W2 over all expert instances */
-  MOE_K_COMBINE = 5,  /* weighted sum in slot order + shared experts */
+  MOE_K_GATE = 0,    /* gate logits, split over K */
+  MOE_K_TOPK = 1,    /* top-k + softmax per token */
+  MOE_K_COMPACT = 2, /* routing-trace compaction (dedup) */
+  MOE_K_UP = 3,      /* W1/W3 + SwiGLU over all expert instances */
+  MOE_K_DOWN = 4,    /* W2 over all expert instances */
+  MOE_K_COMBINE = 5, /* weighted sum in slot order + shared experts */
   MOE_K_COUNT = 6
 };
-/* on != 0 enables, 0 disables.  Not thread-safe; meant for one driver thread. */
-int moe_timing_enable(int on);
+/* mask: bit (1 << kind) selects a kernel kind; 0 disables timing.  Not
+ * meant for concurrent use from several host threads. */
+int moe_timing_enable(int mask);
 /* Waits for every recorded event pair, adds their elapsed times to ms[kind],
  * their number to launches[kind] (arrays of MOE_K_COUNT), and clears the
  * record.  Either array may be NULL. */

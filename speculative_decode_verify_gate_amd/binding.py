@@ -11,7 +11,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoeverify.so")
+LIB_PATH = os.environ.get("MOE_VERIFY_LIB") or os.path.join(_HERE, "libmoeverify.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MAX_TOKENS, MAX_TOPK, MAX_SLOTS, MAX_EXPERTS, MAX_SHARED = 64, 16, 512, 256, 4
@@ -211,13 +211,18 @@ def pass_bytes(shape, idx_host):
     return int(out[0]), int(out[1]), int(out[2]), int(u.value)
 
 
-def timing_enable(on=True):
-    _check("moe_timing_enable", load().moe_timing_enable(1 if on else 0))
+def timing_enable(kinds=KERNEL_KINDS):
+    """Bracket the launches of the given kernel kinds with HIP events
+    (an empty sequence disables timing)."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    _check("moe_timing_enable", load().moe_timing_enable(mask))
 
 
 def timing_read():
     """{kind: (total_ms, launches)} accumulated since the last read."""
-    ms = (C.c_double * 6)()
-    cnt = (C.c_int64 * 6)()
+    ms = (C.c_double * len(KERNEL_KINDS))()
+    cnt = (C.c_int64 * len(KERNEL_KINDS))()
     _check("moe_timing_read", load().moe_timing_read(C.addressof(ms), C.addressof(cnt)))
     return {k: (ms[i], int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}

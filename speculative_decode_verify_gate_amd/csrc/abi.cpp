@@ -1,7 +1,7 @@
 // abi.cpp -- the C ABI of include/moe_verify.h: argument validation,
 // workspace sizing, the launch sequence of each call and the optional
-// per-kernel event timing.  Kernels live in router.hip, compact.hip and
-// expert.hip.
+// per-kernel event timing.  Kernels live in router.hip and expert.hip
+// (the dedup compaction routine in compact.h).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -63,6 +63,7 @@ size_t obuf_ws(const moe_shape *s, int n) {
   return align_up(entry_rows(s, n) * s->d_model * sizeof(float), kAlign);
 }
 
+
 // Workspace query / size check shared by the device calls.  Returns
 // MOE_OK and sets *launch when the call should go ahead.
 int workspace_gate(void *ws, size_t *ws_bytes, size_t need, bool *launch) {
@@ -86,7 +87,7 @@ struct EventPair {
 
 struct Timing {
   std::mutex mu;
-  bool on = false;
+  int mask = 0;
   std::vector<EventPair> pending;
   std::vector<hipEvent_t> pool;
 
@@ -110,7 +111,7 @@ Timing &timing() {
 template <class F>
 hipError_t timed(int kind, hipStream_t st, F &&launch) {
   Timing &tm = timing();
-  if (!tm.on) return launch();
+  if (!(tm.mask & (1 << kind))) return launch();
   hipEvent_t a, b;
   {
     std::lock_guard<std::mutex> lk(tm.mu);
@@ -151,7 +152,6 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
 
   hipStream_t st = (hipStream_t)stream;
   unsigned char *base = (unsigned char *)ws;
-  int32_t *cmp = dedup ? (int32_t *)base : nullptr;
   const bool bf16 = s->wdtype == MOE_BF16;
 
   moe::ExpertArgs a{};
@@ -161,7 +161,9 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.ws2 = w->ws2;
   a.x = x;
   a.idx = idx;
-  a.cmp = cmp;
+  a.w = tw;
+  a.y = y;
+  a.cmp = dedup ? (int32_t *)base : nullptr;
   a.abuf = base + c_bytes;
   a.obuf = (float *)(base + c_bytes + a_bytes);
   a.d = s->d_model;
@@ -177,21 +179,17 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   hipError_t err = hipSuccess;
   if (dedup)
     err = timed(MOE_K_COMPACT, st, [&] {
-      return moe::launch_compact(idx, n, s->top_k, s->n_experts, cmp, n_unique, st);
+      return moe::launch_compact(idx, n, s->top_k, s->n_experts, (int32_t *)base, n_unique, st);
     });
-  if (err == hipSuccess) {
-    a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true);
+  a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true);
+  if (err == hipSuccess)
     err = timed(MOE_K_UP, st, [&] { return moe::launch_up(a, bf16, st); });
-  }
   if (err == hipSuccess) {
     a.lds_bytes = moe::expert_lds_bytes(n, s->d_ff, bf16, false);
     err = timed(MOE_K_DOWN, st, [&] { return moe::launch_down(a, bf16, st); });
   }
   if (err == hipSuccess)
-    err = timed(MOE_K_COMBINE, st, [&] {
-      return moe::launch_combine(a.obuf, idx, tw, n, s->top_k, s->n_shared, s->d_model,
-                                 s->n_experts, y, st);
-    });
+    err = timed(MOE_K_COMBINE, st, [&] { return moe::launch_combine(a, st); });
   return status_of(err);
 }
 
@@ -271,10 +269,10 @@ const char *moe_status_string(int status) {
   }
 }
 
-int moe_timing_enable(int on) {
+int moe_timing_enable(int mask) {
   Timing &tm = timing();
   std::lock_guard<std::mutex> lk(tm.mu);
-  tm.on = on != 0;
+  tm.mask = mask & ((1 << MOE_K_COUNT) - 1);
   return MOE_OK;
 }
 

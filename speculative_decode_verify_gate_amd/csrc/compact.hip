@@ -88,6 +88,8 @@ __global__ __launch_bounds__(512) void compact_kernel(const int32_t *__restrict_
     cmp[L.counts() + e] = cnt[e];
     cmp[L.offs() + e] = offs[e];
     if (cnt[e] > 0) cmp[L.uniq() + upos[e]] = e;
+    // entries past U mark "no instance": an expert block reads uniq[u] alone
+    if (e >= upos[E]) cmp[L.uniq() + e] = -1;
   }
   if (tid == 0) {
     cmp[L.offs() + E] = offs[E];

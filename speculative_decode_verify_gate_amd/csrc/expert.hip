@@ -14,21 +14,23 @@
 // Up kernel:   A = rows of W1 and W3 ([f][d]), B = the instance's tokens
 //              (fp32 x rounded to bf16), out = bf16(silu(h) * g) per token.
 // Down kernel: A = rows of W2 ([d][f]), B = the up kernel's rows, out = fp32
-//              per (instance entry) rows of the expert output buffer.
+//              rows of the expert output buffer, one per (instance entry).
 //
 // Decode-time MoE is bound by weight bytes (the same page, section 6), so the
 // kernels are laid out to stream weights:
-//  - a workgroup owns one instance and 64 output rows; each wave owns one
-//    16-row MFMA tile and streams those rows over the whole K with 16-byte
-//    loads (4 lanes cover 64 contiguous bytes of a row per load), two chunks
-//    in flight through register double buffering;
-//  - the instance's tokens are the MFMA B operand (16 tokens per tile, up
-//    to 4 tiles): staged once per K window in LDS, read with ds_read_b128,
-//    never re-read from global per row tile;
-//  - the MFMA v_mfma_f32_16x16x32_bf16 (fp32: 16x16x4) sums each output
-//    element over K in a fixed step order that does not depend on which
-//    other tokens share the tile, so a token gets the same bits whether it
-//    is alone (per-slot) or batched with others (dedup).
+//  - a workgroup owns one 16-row MFMA tile of one instance; its four waves
+//    take the K dimension in 4-step chunks, round-robin, so every workgroup
+//    is short (one tile) and there are many of them to balance the chip;
+//  - each lane streams 16-byte vectors (4 lanes cover 64 contiguous bytes of
+//    a row per load), with the next chunk always in flight (register double
+//    buffering in branch-free code, so waits are exact);
+//  - the instance's tokens are the MFMA B operand (16 tokens per tile, up to
+//    4 tiles), staged once per K window in LDS and read with ds_read_b128;
+//  - the four waves' partial sums are added in wave order through LDS, and
+//    the MFMA (v_mfma_f32_16x16x32_bf16; fp32: 16x16x4) sums each output over
+//    K in a fixed step order that does not depend on which other tokens share
+//    the tile, so a token gets the same bits alone (per-slot) or batched with
+//    others (dedup).
 #include <math.h>
 
 #include "kernels.h"
@@ -75,30 +77,28 @@ struct WT<false> {
 
 __device__ inline u32x4 ldg16(const unsigned char *p) { return *(const u32x4 *)p; }
 
-// Steps per register chunk: the up kernel streams two matrices.
-template <bool UP, int CTMAX>
-struct Chunking {
-  static constexpr int kSteps = UP ? 8 : (CTMAX == 1 ? 16 : 8);
-};
+constexpr int kSpc = 4;                           // MFMA steps per chunk
+constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 
 template <bool BF16, bool UP, int CTMAX>
 __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   using T = WT<BF16>;
-  constexpr int SPC = Chunking<UP, CTMAX>::kSteps;
+  constexpr int SPC = kSpc;
+  constexpr int NW = kWavesPerBlock;
   constexpr int CHUNK = SPC * T::kStep;             // K elements per chunk
   constexpr int EB = T::kBytes;
   constexpr int GROUP = CTMAX * kTile;              // tokens per MFMA pass
   constexpr int ITEM = 16 / EB;                     // elements per 16-byte item
 
-  extern __shared__ __align__(16) unsigned char lds[];  // staged token rows
+  extern __shared__ __align__(16) unsigned char lds[];  // staged tokens / partials
   __shared__ int ent_row[MOE_MAX_SLOTS];
   __shared__ int ent_tok[MOE_MAX_SLOTS];
 
   const int R = UP ? a.f : a.d;  // output rows
   const int K = UP ? a.d : a.f;  // reduction length
-  const int RG = (R + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int inst = blockIdx.x / RG;
-  const int rgrp = blockIdx.x - inst * RG;
+  const int RT = R / kTile;      // 16-row tiles per instance
+  const int inst = blockIdx.x / RT;
+  const int rt = blockIdx.x - inst * RT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -107,63 +107,84 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   const CompactLayout CL{a.E, a.N * a.k};
   const size_t fd = (size_t)a.f * (size_t)a.d;
 
-  // ---- the instance: expert matrices and token entries (uniform per block)
-  int m;
-  const unsigned char *wA, *wB = nullptr;
-  int list_base = 0, shared_s = -1;
+  // ---- the instance's expert: one dependent load before the weight stream
+  int e = -1, shared_s = -1;
   if (inst < a.n_routed) {
-    int e;
-    if (!a.dedup) {
-      e = a.idx[inst];
-      if (e < 0 || e >= a.E) return;
-      m = 1;
-    } else {
-      if (inst >= a.cmp[CL.u()]) return;
-      e = a.cmp[CL.uniq() + inst];
-      m = a.cmp[CL.counts() + e];
-      list_base = a.cmp[CL.offs() + e];
-    }
-    if (UP) {
-      wA = (const unsigned char *)a.w13 + (size_t)e * 2 * fd * EB;
-      wB = wA + fd * EB;
-    } else {
-      wA = (const unsigned char *)a.w2 + (size_t)e * fd * EB;
-    }
+    e = a.dedup ? a.cmp[CL.uniq() + inst] : a.idx[inst];
+    if (e < 0 || e >= a.E) return;  // past U (dedup) or an empty slot
   } else {
     shared_s = inst - a.n_routed;
     if (shared_s >= a.S) return;
-    m = a.N;
+  }
+  const unsigned char *wA, *wB = nullptr;
+  {
+    const unsigned char *base13 =
+        (const unsigned char *)(shared_s < 0 ? a.w13 : a.ws13);
+    const unsigned char *base2 = (const unsigned char *)(shared_s < 0 ? a.w2 : a.ws2);
+    const size_t ex = (size_t)(shared_s < 0 ? e : shared_s);
     if (UP) {
-      wA = (const unsigned char *)a.ws13 + (size_t)shared_s * 2 * fd * EB;
+      wA = base13 + ex * 2 * fd * EB;
       wB = wA + fd * EB;
     } else {
-      wA = (const unsigned char *)a.ws2 + (size_t)shared_s * fd * EB;
+      wA = base2 + ex * fd * EB;
     }
   }
-  for (int c = tid; c < m; c += blockDim.x) {
-    int row;
-    if (shared_s >= 0)
-      row = a.N * a.k + shared_s * a.N + c;
-    else
-      row = a.dedup ? a.cmp[CL.list() + list_base + c] : inst;
-    ent_row[c] = row;
-    ent_tok[c] = (shared_s >= 0) ? c : row / a.k;
-  }
-
-  const int rt = rgrp * kWavesPerBlock + wave;  // this wave's 16-row tile
-  const bool active = rt * kTile < R;
   const int nsteps = K / T::kStep;
   const int nchunks = (nsteps + SPC - 1) / SPC;
   const unsigned char *rowA = wA + (size_t)(rt * kTile + r) * K * EB;
   const unsigned char *rowB = UP ? wB + (size_t)(rt * kTile + r) * K * EB : nullptr;
   const int lane_k = g * T::kPerLane;
 
+  // Issue the 16-byte weight loads of one chunk.  Branch-free on purpose: the
+  // compiler can then count outstanding loads exactly and wait only for the
+  // chunk being consumed while the next one is in flight.  Steps past the end
+  // of K (last chunk only) re-read the last step; compute() ignores them.
+  auto issue = [&](int ch, u32x4 (&d1)[SPC], u32x4 (&d3)[SPC]) {
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+      const int step = min(ch * SPC + s, nsteps - 1);
+      const size_t off = (size_t)(step * T::kStep + lane_k) * EB;
+      d1[s] = ldg16(rowA + off);
+      if (UP) d3[s] = ldg16(rowB + off);
+    }
+  };
+
+  u32x4 ra1[SPC], ra3[SPC], rb1[SPC], rb3[SPC];
+  // the first chunk of this wave leaves before the token lists are read
+  // (every window holds at least NW chunks, so chunk `wave` is in window 0)
+  if (wave < nchunks) issue(wave, ra1, ra3);
+
+  // ---- token entries of the instance
+  int m;
+  if (shared_s >= 0) {
+    m = a.N;
+    for (int c = tid; c < m; c += kBlock) {
+      ent_row[c] = a.N * a.k + shared_s * a.N + c;
+      ent_tok[c] = c;
+    }
+  } else if (a.dedup) {
+    m = a.cmp[CL.counts() + e];
+    const int base = a.cmp[CL.offs() + e];
+    for (int c = tid; c < m; c += kBlock) {
+      const int row = a.cmp[CL.list() + base + c];
+      ent_row[c] = row;
+      ent_tok[c] = row / a.k;
+    }
+  } else {
+    m = 1;
+    if (tid == 0) {
+      ent_row[0] = inst;
+      ent_tok[0] = inst / a.k;
+    }
+  }
+
   for (int c0 = 0; c0 < m; c0 += GROUP) {
     const int mg = min(m - c0, GROUP);
-    // K window staged in LDS: as many whole chunks as fit for mg rows
-    int KW = ((a.lds_bytes / (mg * EB)) - kLdsPad) / CHUNK * CHUNK;
-    KW = min(KW, nchunks * CHUNK);
-    const int cpw = KW / CHUNK;
+    const int n_ct = (mg + kTile - 1) / kTile;
+    // K window staged in LDS: a multiple of NW chunks (at least NW)
+    int cpw = ((a.lds_bytes / (mg * EB)) - kLdsPad) / CHUNK / NW * NW;
+    cpw = max(NW, min(cpw, (nchunks + NW - 1) / NW * NW));
+    const int KW = cpw * CHUNK;
     const int stride = KW + kLdsPad;  // elements per staged row
 
     f32x4 acc1[CTMAX], acc3[CTMAX];
@@ -172,48 +193,54 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
       acc1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc3[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    u32x4 ra1[SPC], ra3[SPC], rb1[SPC], rb3[SPC];
 
-    auto load_chunk = [&](int ch, u32x4 (&d1)[SPC], u32x4 (&d3)[SPC]) {
-#pragma unroll
-      for (int s = 0; s < SPC; ++s) {
-        if (ch * SPC + s < nsteps) {
-          const size_t off = (size_t)(ch * CHUNK + s * T::kStep + lane_k) * EB;
-          d1[s] = ldg16(rowA + off);
-          if (UP) d3[s] = ldg16(rowB + off);
-        }
-      }
-    };
-
-    auto stage_window = [&](int w) {
-      const int k0 = w * KW;
+    // Stage rows [c0, c0+mg) of the B operand for K range [k0, k0+KW).
+    // Loads are batched (IB per thread) before any LDS write so a thread has
+    // several requests in flight instead of one round trip per item.
+    auto stage_window = [&](int k0) {
+      constexpr int IB = (UP && BF16) ? 4 : 8;
       const int kw = min(KW, K - k0);
       const int items = kw / ITEM;
-      for (int it = tid; it < mg * items; it += blockDim.x) {
-        const int c = it / items;
-        const int q = it - c * items;
-        const int kk = k0 + q * ITEM;
-        u32x4 v;
-        if (UP) {
-          const float *src = a.x + (size_t)ent_tok[c0 + c] * K + kk;
-          if (BF16) {
-            const f32x4 lo = *(const f32x4 *)src;
-            const f32x4 hi = *(const f32x4 *)(src + 4);
-            bf16x8 b;
-            b[0] = (__bf16)lo.x; b[1] = (__bf16)lo.y; b[2] = (__bf16)lo.z; b[3] = (__bf16)lo.w;
-            b[4] = (__bf16)hi.x; b[5] = (__bf16)hi.y; b[6] = (__bf16)hi.z; b[7] = (__bf16)hi.w;
-            v = __builtin_bit_cast(u32x4, b);
+      const int total = mg * items;
+      for (int base = 0; base < total; base += IB * kBlock) {
+        u32x4 v[IB];
+#pragma unroll
+        for (int u = 0; u < IB; ++u) {
+          const int it = min(base + u * kBlock + tid, total - 1);
+          const int c = it / items;
+          const int kk = k0 + (it - c * items) * ITEM;
+          if (UP) {
+            const float *src = a.x + (size_t)ent_tok[c0 + c] * K + kk;
+            if (BF16) {
+              const f32x4 lo = *(const f32x4 *)src;
+              const f32x4 hi = *(const f32x4 *)(src + 4);
+              bf16x8 b;
+              b[0] = (__bf16)lo.x; b[1] = (__bf16)lo.y; b[2] = (__bf16)lo.z; b[3] = (__bf16)lo.w;
+              b[4] = (__bf16)hi.x; b[5] = (__bf16)hi.y; b[6] = (__bf16)hi.z; b[7] = (__bf16)hi.w;
+              v[u] = __builtin_bit_cast(u32x4, b);
+            } else {
+              v[u] = *(const u32x4 *)src;
+            }
           } else {
-            v = *(const u32x4 *)src;
+            v[u] = ldg16((const unsigned char *)a.abuf +
+                         ((size_t)ent_row[c0 + c] * K + kk) * EB);
           }
-        } else {
-          v = ldg16((const unsigned char *)a.abuf + ((size_t)ent_row[c0 + c] * K + kk) * EB);
         }
-        *(u32x4 *)(lds + ((size_t)c * stride + q * ITEM) * EB) = v;
+#pragma unroll
+        for (int u = 0; u < IB; ++u) {
+          const int it = base + u * kBlock + tid;
+          if (it < total) {
+            const int c = it / items;
+            const int q = it - c * items;
+            *(u32x4 *)(lds + ((size_t)c * stride + q * ITEM) * EB) = v[u];
+          }
+        }
       }
     };
 
-    auto compute_chunk = [&](int ch, const u32x4 (&s1)[SPC], const u32x4 (&s3)[SPC]) {
+    // MFMAs of one chunk.  The B fragment of a lane is token column
+    // ct*16 + r; columns past the group read a valid row and are zeroed.
+    auto compute = [&](int ch, const u32x4 (&s1)[SPC], const u32x4 (&s3)[SPC]) {
       const int kin = (ch % cpw) * CHUNK;  // offset inside the window
 #pragma unroll
       for (int s = 0; s < SPC; ++s) {
@@ -221,10 +248,11 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
           const int off = kin + s * T::kStep + lane_k;
 #pragma unroll
           for (int ct = 0; ct < CTMAX; ++ct) {
-            if (ct * kTile < mg) {
+            if (ct == 0 || ct < n_ct) {
               const int col = ct * kTile + r;
-              u32x4 b = u32x4{0u, 0u, 0u, 0u};
-              if (col < mg) b = *(const u32x4 *)(lds + ((size_t)col * stride + off) * EB);
+              const int row = min(col, mg - 1);
+              u32x4 b = *(const u32x4 *)(lds + ((size_t)row * stride + off) * EB);
+              if (col >= mg) b = u32x4{0u, 0u, 0u, 0u};
               acc1[ct] = T::mma(s1[s], b, acc1[ct]);
               if (UP) acc3[ct] = T::mma(s3[s], b, acc3[ct]);
             }
@@ -233,62 +261,84 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
       }
     };
 
-    auto step = [&](int ch, u32x4 (&c1)[SPC], u32x4 (&c3)[SPC], u32x4 (&n1)[SPC],
-                    u32x4 (&n3)[SPC]) {
-      if (ch % cpw == 0) {
-        __syncthreads();  // readers of the previous window are done
-        stage_window(ch / cpw);
-        __syncthreads();
-      }
-      if (active && ch + 1 < nchunks) load_chunk(ch + 1, n1, n3);
-      if (active) compute_chunk(ch, c1, c3);
-    };
-
-    if (active) load_chunk(0, ra1, ra3);
-    for (int ch = 0; ch < nchunks; ch += 2) {
-      step(ch, ra1, ra3, rb1, rb3);
-      if (ch + 1 < nchunks) step(ch + 1, rb1, rb3, ra1, ra3);
-    }
-
-    // ---- epilogue: lane holds rows 4g..4g+3 of its tile for token column r
-    if (active) {
-      const int row0 = rt * kTile + 4 * g;
-#pragma unroll
-      for (int ct = 0; ct < CTMAX; ++ct) {
-        const int col = ct * kTile + r;
-        if (ct * kTile < mg && col < mg) {
-          const int orow = ent_row[c0 + col];
-          if (UP) {
-            float act[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float h = acc1[ct][v];
-              act[v] = h / (1.0f + expf(-h)) * acc3[ct][v];
-            }
-            unsigned char *dst = (unsigned char *)a.abuf + ((size_t)orow * a.f + row0) * EB;
-            if (BF16) {
-              bf16x4 b;
-              b[0] = (__bf16)act[0]; b[1] = (__bf16)act[1];
-              b[2] = (__bf16)act[2]; b[3] = (__bf16)act[3];
-              *(u32x2 *)dst = __builtin_bit_cast(u32x2, b);
-            } else {
-              *(f32x4 *)dst = f32x4{act[0], act[1], act[2], act[3]};
-            }
-          } else {
-            *(f32x4 *)(a.obuf + (size_t)orow * a.d + row0) = acc1[ct];
-          }
+    for (int w0 = 0; w0 < nchunks; w0 += cpw) {
+      const int w1 = min(w0 + cpw, nchunks);
+      int c = w0 + wave;  // this wave's chunks: c, c + NW, ... < w1
+      if (!(c0 == 0 && w0 == 0) && c < w1) issue(c, ra1, ra3);
+      __syncthreads();  // readers of the previous window are done
+      stage_window(w0 * CHUNK);
+      __syncthreads();
+      if (c < w1) {
+        // steady state: two chunks per iteration, next chunk always in flight
+        for (; c + 2 * NW < w1; c += 2 * NW) {
+          issue(c + NW, rb1, rb3);
+          compute(c, ra1, ra3);
+          issue(c + 2 * NW, ra1, ra3);
+          compute(c + NW, rb1, rb3);
+        }
+        if (c + NW < w1) {
+          issue(c + NW, rb1, rb3);
+          compute(c, ra1, ra3);
+          compute(c + NW, rb1, rb3);
+        } else {
+          compute(c, ra1, ra3);
         }
       }
     }
-    __syncthreads();  // LDS rows are restaged by the next token group
+
+    // ---- the four waves' partial sums, added in wave order; wave ct then
+    // finishes token tile ct (lane holds rows 4g..4g+3 for token column r)
+    __syncthreads();  // every wave is done with the staged rows
+    f32x4 *red = (f32x4 *)lds;  // [UP ? 2 : 1][NW][CTMAX][64]
+#pragma unroll
+    for (int ct = 0; ct < CTMAX; ++ct) {
+      if (ct < n_ct) {
+        red[(wave * CTMAX + ct) * kWave + lane] = acc1[ct];
+        if (UP) red[((NW + wave) * CTMAX + ct) * kWave + lane] = acc3[ct];
+      }
+    }
+    __syncthreads();
+    if (wave < n_ct) {
+      const int ct = wave;
+      f32x4 h = red[ct * kWave + lane];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) h += red[(w * CTMAX + ct) * kWave + lane];
+      f32x4 gg = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (UP) {
+        gg = red[(NW * CTMAX + ct) * kWave + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) gg += red[((NW + w) * CTMAX + ct) * kWave + lane];
+      }
+      const int col = ct * kTile + r;
+      if (col < mg) {
+        const int orow = ent_row[c0 + col];
+        const int row0 = rt * kTile + 4 * g;
+        if (UP) {
+          float act[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) act[v] = h[v] / (1.0f + expf(-h[v])) * gg[v];
+          unsigned char *dst = (unsigned char *)a.abuf + ((size_t)orow * a.f + row0) * EB;
+          if (BF16) {
+            bf16x4 b;
+            b[0] = (__bf16)act[0]; b[1] = (__bf16)act[1];
+            b[2] = (__bf16)act[2]; b[3] = (__bf16)act[3];
+            *(u32x2 *)dst = __builtin_bit_cast(u32x2, b);
+          } else {
+            *(f32x4 *)dst = f32x4{act[0], act[1], act[2], act[3]};
+          }
+        } else {
+          *(f32x4 *)(a.obuf + (size_t)orow * a.d + row0) = h;
+        }
+      }
+    }
+    __syncthreads();  // partials are overwritten by the next token group
   }
 }
 
 template <bool BF16, bool UP>
 hipError_t launch_expert(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
-  const int RG = (R + kRowsPerBlock - 1) / kRowsPerBlock;
-  const int blocks = (a.n_routed + a.S) * RG;
+  const int blocks = (a.n_routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   const bool wide = a.N > kTile;
   // allow more than the default 64 KB of dynamic LDS, once per kernel
@@ -301,32 +351,53 @@ hipError_t launch_expert(const ExpertArgs &a, hipStream_t st) {
   if (set_wide != hipSuccess) return set_wide;
   if (set_narrow != hipSuccess) return set_narrow;
   if (wide)
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4>), dim3(blocks), dim3(256), a.lds_bytes, st,
-                       a);
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4>), dim3(blocks), dim3(kBlock), a.lds_bytes,
+                       st, a);
   else
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1>), dim3(blocks), dim3(256), a.lds_bytes, st,
-                       a);
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1>), dim3(blocks), dim3(kBlock), a.lds_bytes,
+                       st, a);
   return hipGetLastError();
 }
 
-// y[t] = sum_j w[t][j] * o[t*k+j] + sum_s o[N*k + s*N + t], slot order, fp32.
+// y[t] = sum_j w[t][j] * o[t*k+j] + sum_s o[N*k + s*N + t], in slot order,
+// fp32.  The rows read do not depend on the routing values, so every load a
+// thread needs (its k+S expert rows, the k indices and weights) is issued
+// before the first is used: one memory round trip.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ obuf,
                                                       const int32_t *__restrict__ idx,
                                                       const float *__restrict__ w, int N, int k,
                                                       int S, int d, int E,
                                                       float *__restrict__ y) {
+  constexpr int J = MOE_MAX_TOPK + MOE_MAX_SHARED;
   const int t = blockIdx.y;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (c >= d) return;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if (e < 0 || e >= E) continue;
-    const float wt = w[t * k + j];
-    const f32x4 o = *(const f32x4 *)(obuf + (size_t)(t * k + j) * d + c);
-    acc += wt * o;
+  f32x4 ov[J];
+  int ej[MOE_MAX_TOPK];
+  float wj[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < k + S) {
+      const int row = (j < k) ? t * k + j : N * k + (j - k) * N + t;
+      ov[j] = *(const f32x4 *)(obuf + (size_t)row * d + c);
+    }
   }
-  for (int s = 0; s < S; ++s) acc += *(const f32x4 *)(obuf + (size_t)(N * k + s * N + t) * d + c);
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      ej[j] = idx[t * k + j];
+      wj[j] = w[t * k + j];
+    }
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < k) {
+      if (ej[j] >= 0 && ej[j] < E) acc += wj[j] * ov[j];
+    } else if (j < k + S) {
+      acc += ov[j];
+    }
+  }
   *(f32x4 *)(y + (size_t)t * d + c) = acc;
 }
 
@@ -336,14 +407,21 @@ int expert_lds_bytes(int N, int K, bool bf16, bool up) {
   const int eb = bf16 ? 2 : 4;
   const int ctmax = N > kTile ? 4 : 1;
   const int step = bf16 ? 32 : 16;
-  const int spc = up ? 8 : (ctmax == 1 ? 16 : 8);
-  const int chunk = spc * step;
-  const int kpad = (K + chunk - 1) / chunk * chunk;
+  const int chunk = kSpc * step;
   const int rows = ctmax * kTile;
-  const size_t whole = (size_t)rows * (kpad + kLdsPad) * eb;
-  const size_t least = (size_t)rows * (chunk + kLdsPad) * eb;
+  const int kpad = (K + kWavesPerBlock * chunk - 1) / (kWavesPerBlock * chunk) *
+                   (kWavesPerBlock * chunk);
+  // the whole K for as many token rows as an instance can have (at most N
+  // unless a caller's routing repeats an expert within a token)
+  const int rows_n = N < rows ? N : rows;
+  const size_t whole = (size_t)rows_n * (kpad + kLdsPad) * eb;
+  // at least one chunk per wave for a full token group, and room for the
+  // waves' partial sums
+  const size_t least = (size_t)rows * (kWavesPerBlock * chunk + kLdsPad) * eb;
+  const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * ctmax * kWave * 16;
   size_t bytes = whole < (size_t)kLdsBudget ? whole : (size_t)kLdsBudget;
   if (bytes < least) bytes = least;
+  if (bytes < partials) bytes = partials;
   return (int)bytes;
 }
 
@@ -355,10 +433,10 @@ hipError_t launch_down(const ExpertArgs &a, bool bf16, hipStream_t st) {
   return bf16 ? launch_expert<true, false>(a, st) : launch_expert<false, false>(a, st);
 }
 
-hipError_t launch_combine(const float *obuf, const int32_t *idx, const float *w, int N, int k,
-                          int S, int d, int E, float *y, hipStream_t st) {
-  dim3 grid((d / 4 + 255) / 256, N);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, obuf, idx, w, N, k, S, d, E, y);
+hipError_t launch_combine(const ExpertArgs &a, hipStream_t st) {
+  dim3 grid((a.d / 4 + 255) / 256, a.N);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, a.obuf, a.idx, a.w, a.N, a.k, a.S,
+                     a.d, a.E, a.y);
   return hipGetLastError();
 }
 

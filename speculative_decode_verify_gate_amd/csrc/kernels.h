@@ -13,11 +13,11 @@ namespace moe {
 // Geometry shared by the launchers and the workspace sizing in abi.cpp.
 constexpr int kWave = 64;
 constexpr int kTile = 16;               // MFMA output tile is 16 rows x 16 tokens
-constexpr int kWavesPerBlock = 4;       // expert kernels: one 16-row tile per wave
-constexpr int kRowsPerBlock = kTile * kWavesPerBlock;
+constexpr int kWavesPerBlock = 4;       // expert kernels: waves per 16-row tile
+
 constexpr int kGateKPerBlock = 256;     // gate logits: K elements per workgroup
-constexpr int kLdsBudget = 72 * 1024;   // bytes of staged activations per workgroup
-                                        // (two workgroups fit the 160 KB of a CU)
+constexpr int kLdsBudget = 36 * 1024;   // bytes of staged activations per workgroup
+                                        // (four workgroups fit the 160 KB of a CU)
 constexpr int kLdsPad = 8;              // elements of padding per staged row
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -38,28 +38,31 @@ struct ExpertArgs {
   const void *w13, *w2, *ws13, *ws2;
   const float *x;         // [N][d]
   const int32_t *idx;     // [N][k]
+  const float *w;         // [N][k] routing weights
+  float *y;               // [N][d] layer output
   const int32_t *cmp;     // compaction record (dedup) or nullptr
   void *abuf;             // [N*k + S*N][f] SwiGLU outputs, weight element type
   float *obuf;            // [N*k + S*N][d] expert outputs
   int d, f, E, k, S, N;
-  int dedup;              // 0: instance i is slot i; 1: instance u is uniq[u]
+  int dedup;              // 0: instance i is slot i; 1: instance u is the
+                          //    u-th distinct selected expert
   int n_routed;           // routed instances in the grid
   int lds_bytes;          // dynamic LDS per workgroup
 };
 
 int gate_splits(int d);
+hipError_t launch_compact(const int32_t *idx, int N, int k, int E, int32_t *cmp,
+                          int32_t *n_unique, hipStream_t st);
 
 hipError_t launch_gate(const float *gate_w, const float *x, int N, int d, int E,
                        float *part, hipStream_t st);
 hipError_t launch_topk(const float *part, int splits, int N, int E, int k, float *logits,
                        int32_t *idx, float *w, float *margin, hipStream_t st);
-hipError_t launch_compact(const int32_t *idx, int N, int k, int E, int32_t *cmp,
-                          int32_t *n_unique, hipStream_t st);
-// bf16 != 0 selects bf16 weights, else fp32.
+// Expert pass = up kernel, down kernel, combine kernel.  bf16 selects bf16
+// weights, else fp32.
 hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_down(const ExpertArgs &a, bool bf16, hipStream_t st);
-hipError_t launch_combine(const float *obuf, const int32_t *idx, const float *w, int N,
-                          int k, int S, int d, int E, float *y, hipStream_t st);
+hipError_t launch_combine(const ExpertArgs &a, hipStream_t st);
 
 // Dynamic LDS for the expert kernels at this token count (activations of up
 // to min(N, 64) tokens staged per window).

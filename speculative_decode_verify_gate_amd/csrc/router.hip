@@ -107,17 +107,41 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ part
   const int lane = threadIdx.x;
   float v[kMaxExpertsPerLane];
   bool taken[kMaxExpertsPerLane];
+  const int n_q = (E + 63) / 64;
+#pragma unroll
+  for (int q = 0; q < kMaxExpertsPerLane; ++q) v[q] = 0.f;
+  // Sum the K-split partials in split order.  Loads of 8 splits (for every
+  // expert of the lane) are issued together so the partials, written by the
+  // gate kernel on other XCDs, cost one memory round trip per 8 splits.
+  for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+    float pv[kMaxExpertsPerLane][8];
+#pragma unroll
+    for (int q = 0; q < kMaxExpertsPerLane; ++q) {
+      if (q < n_q) {
+        const int e = min(q * 64 + lane, E - 1);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sp = min(sp0 + u, splits - 1);
+          pv[q][u] = part[((size_t)sp * N + t) * E + e];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxExpertsPerLane; ++q)
+      if (q < n_q) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (sp0 + u < splits) v[q] += pv[q][u];
+      }
+  }
 #pragma unroll
   for (int q = 0; q < kMaxExpertsPerLane; ++q) {
     const int e = q * 64 + lane;
-    taken[q] = true;
-    v[q] = -INFINITY;
+    taken[q] = !(e < E);
     if (e < E) {
-      float s = 0.f;
-      for (int sp = 0; sp < splits; ++sp) s += part[((size_t)sp * N + t) * E + e];
-      v[q] = s;
-      taken[q] = false;
-      if (logits) logits[(size_t)t * E + e] = s;
+      if (logits) logits[(size_t)t * E + e] = v[q];
+    } else {
+      v[q] = -INFINITY;
     }
   }
 
