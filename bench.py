@@ -183,9 +183,12 @@ def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=()):
     return wall, kt, U
 
 
-def cpu_baseline(cfg, layer, x, seconds):
-    """The CPU oracle (as written, not tuned) on the same pass, on this host."""
+def cpu_baseline(cfg, x, seconds):
+    """The CPU oracle (as written, not tuned) on the same pass, on this host,
+    with the row-major weights of layer 0 (the same seeded draw)."""
     import oracle as O
+
+    layer = synth.make_layer(cfg, "cuda", layer=0)
 
     threads = min(16, len(os.sched_getaffinity(0)))
     s = O.Shape(cfg.d, cfg.E, cfg.k, cfg.f, cfg.S, O.BF16 if cfg.wdtype == "bf16" else O.F32)
@@ -281,10 +284,14 @@ def main():
     log(f"[bench] {cfg.name}: {n_layers} weight sets of {layer_bytes / 1e9:.2f} GB, "
         f"timed step n={n_head}")
     layers = []
+    shape = B.shape_of(cfg)
     for L in range(n_layers):
-        layers.append(synth.make_layer(cfg, "cuda", layer=L))
+        rows = synth.make_layer(cfg, "cuda", layer=L)
+        # resident weights are kept in the MFMA-tiled layout (packed once)
+        layers.append(B.pack_weights(shape, rows))
         torch.cuda.synchronize()
-        log(f"[bench] weights {L + 1}/{n_layers} drawn")
+        del rows
+        log(f"[bench] weights {L + 1}/{n_layers} drawn and packed")
     eng = Engines(cfg)
 
     sweep = None
@@ -347,7 +354,8 @@ def main():
                                f", per-slot and dedup engines",
                    "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
                    "shared_experts": cfg.S, "weights": cfg.wdtype, "rho": cfg.rho,
-                   "tokens": N, "weight_sets_rotated": n_layers},
+                   "tokens": N, "weight_sets_rotated": n_layers,
+                   "weight_layout": "MFMA-tiled (packed once)"},
         "engines_at_step_n": engines_at_head,
         "step_bytes": int(step_bytes),
         "roofline": {"bound": "hbm", "kernel": "expert_up (W1/W3 + SwiGLU)",
@@ -368,7 +376,9 @@ def main():
                             "predicted_u_lt_r": cross_p if cross_p is not None else "never"}
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
-        out["cpu_baseline"] = cpu_baseline(cfg, layers[0], x, args.cpu_seconds)
+        del layers
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -78,11 +78,26 @@ typedef struct moe_shape {
   int32_t wdtype;    /* moe_dtype of the expert weights */
 } moe_shape;
 
+/* Layout of every expert matrix W with R rows and K columns (W1, W3: R = f,
+ * K = d; W2: R = d, K = f):
+ *   MOE_LAYOUT_ROWS   row-major [R][K].
+ *   MOE_LAYOUT_TILED  16-row x STEP-column fragments stored contiguously in
+ *                     the order the MFMA consumes them, STEP = 32 for bf16 and
+ *                     16 for fp32: fragment (rt, s) occupies the 1024 bytes at
+ *                     offset (rt * K/STEP + s) * 1024 of the matrix, and its
+ *                     16-byte unit L (0..63) holds W[16 rt + L % 16]
+ *                     [STEP s + (L / 16) * STEP/4 .. + STEP/4).  Same size as
+ *                     ROWS; moe_pack_weights() converts.  Every weight load of
+ *                     the expert kernels is then one contiguous 1 KB block.
+ * Each matrix starts where it starts in the row-major arrays below. */
+enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILED = 1 };
+
 /* Expert weights, device pointers, element type wdtype.
- *   w13  [E][2][f][d]  row r of w13[e][0] is row r of W1 (gate projection),
- *                      of w13[e][1] row r of W3 (up projection)
+ *   w13  [E][2][f][d]  w13[e][0] is W1 (gate projection), w13[e][1] is W3
+ *                      (up projection)
  *   w2   [E][d][f]     W2 (down projection)
  *   ws13 [S][2][f][d], ws2 [S][d][f]  shared experts; NULL iff S == 0.
+ *   layout             moe_layout of all four arrays.
  * Expert e computes  W2 * (silu(W1 xt) . (W3 xt))  with xt = x rounded to
  * bf16 (nearest-even) and the product rounded to bf16 before W2 when
  * wdtype == MOE_BF16; nothing is rounded for MOE_F32.  Accumulation is fp32. */
@@ -91,7 +106,16 @@ typedef struct moe_expert_weights {
   const void *w2;
   const void *ws13;
   const void *ws2;
+  int32_t layout;
 } moe_expert_weights;
+
+/* Convert n_sets expert sets from MOE_LAYOUT_ROWS to MOE_LAYOUT_TILED:
+ * w13_rows [n][2][f][d] -> w13_tiled, w2_rows [n][d][f] -> w2_tiled (device
+ * pointers, element type wdtype, outputs must not overlap the inputs).
+ * Either pair may be NULL to skip it.  Asynchronous on stream; a one-time
+ * preparation of resident weights, not part of a pass. */
+int moe_pack_weights(const moe_shape *shape, int32_t n_sets, const void *w13_rows,
+                     const void *w2_rows, void *w13_tiled, void *w2_tiled, void *stream);
 
 /* Gate + top-k + softmax over the k ("Deep Dive into Mixture of Experts",
  * section 2: logits = x @ gate_weights, top_k of the logits, softmax of the

@@ -33,7 +33,10 @@ class Shape(C.Structure):
 
 class Weights(C.Structure):
     _fields_ = [("w13", C.c_void_p), ("w2", C.c_void_p), ("ws13", C.c_void_p),
-                ("ws2", C.c_void_p)]
+                ("ws2", C.c_void_p), ("layout", C.c_int32)]
+
+
+LAYOUTS = {"rows": 0, "tiled": 1}
 
 
 def load():
@@ -50,12 +53,13 @@ def load():
     lib.moe_expert_pass_perslot.argtypes = [P, P, P, i32, P, P, P, P, sz, P]
     lib.moe_expert_pass_dedup.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
     lib.moe_pass_bytes.argtypes = [P, P, i32, P, P, P, P]
+    lib.moe_pack_weights.argtypes = [P, i32, P, P, P, P, P]
     lib.moe_status_string.argtypes = [C.c_int]
     lib.moe_status_string.restype = C.c_char_p
     lib.moe_timing_enable.argtypes = [C.c_int]
     lib.moe_timing_read.argtypes = [P, P]
     for fn in ("moe_route", "moe_expert_pass_perslot", "moe_expert_pass_dedup",
-               "moe_pass_bytes", "moe_timing_enable", "moe_timing_read"):
+               "moe_pass_bytes", "moe_pack_weights", "moe_timing_enable", "moe_timing_read"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -128,7 +132,26 @@ def _weights(shape, w):
     wdt = torch.bfloat16 if shape.wdtype == MOE_BF16 else torch.float32
     keep = [_dev(w["w13"], wdt, "w13"), _dev(w["w2"], wdt, "w2"),
             _dev(w.get("ws13"), wdt, "ws13"), _dev(w.get("ws2"), wdt, "ws2")]
-    return keep, Weights(*[None if t is None else t.data_ptr() for t in keep])
+    ptrs = [None if t is None else t.data_ptr() for t in keep]
+    return keep, Weights(*ptrs, LAYOUTS[w.get("layout", "rows")])
+
+
+def pack_weights(shape, weights):
+    """Copy of a row-major weight dict in MOE_LAYOUT_TILED (new device
+    tensors of the same shapes; the gate is shared, not copied)."""
+    lib = load()
+    out = dict(weights)
+    out["layout"] = "tiled"
+    for a, b in (("w13", "w2"), ("ws13", "ws2")):
+        if weights.get(a) is None:
+            continue
+        src13, src2 = weights[a], weights[b]
+        dst13, dst2 = torch.empty_like(src13), torch.empty_like(src2)
+        _check("moe_pack_weights", lib.moe_pack_weights(
+            C.byref(shape), src13.shape[0], _ptr(src13), _ptr(src2), _ptr(dst13), _ptr(dst2),
+            _stream()))
+        out[a], out[b] = dst13, dst2
+    return out
 
 
 def route(shape, gate_w, x, *, idx=None, w=None, logits=None, margin=None, ws=None):

@@ -131,6 +131,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 int check_weights(const moe_shape *s, const moe_expert_weights *w) {
   if (!w || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
+  if (w->layout != MOE_LAYOUT_ROWS && w->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (s->n_shared > 0 && (!w->ws13 || !w->ws2)) return MOE_ERR_INVALID_ARG;
   if (s->n_shared == 0 && (w->ws13 || w->ws2)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
@@ -173,6 +174,7 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.S = s->n_shared;
   a.N = n;
   a.dedup = dedup ? 1 : 0;
+  a.tiled = w->layout == MOE_LAYOUT_TILED ? 1 : 0;
   const int slots = n * s->top_k;
   a.n_routed = dedup ? (slots < s->n_experts ? slots : s->n_experts) : slots;
 
@@ -230,6 +232,32 @@ int moe_expert_pass_dedup(const moe_shape *s, const moe_expert_weights *w, const
                           int32_t n, const int32_t *idx, const float *tw, float *y,
                           int32_t *n_unique, void *ws, size_t *ws_bytes, void *stream) {
   return expert_pass(s, w, x, n, idx, tw, y, n_unique, true, ws, ws_bytes, stream);
+}
+
+int moe_pack_weights(const moe_shape *s, int32_t n_sets, const void *w13_rows,
+                     const void *w2_rows, void *w13_tiled, void *w2_tiled, void *stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (n_sets < 0) return MOE_ERR_INVALID_ARG;
+  if ((w13_rows == nullptr) != (w13_tiled == nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((w2_rows == nullptr) != (w2_tiled == nullptr)) return MOE_ERR_INVALID_ARG;
+  const size_t eb = wbytes(s);
+  const size_t fd = (size_t)s->d_model * s->d_ff * eb;
+  auto overlap = [](const void *a, size_t na, const void *b, size_t nb) {
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + nb && pb < pa + na;
+  };
+  if (w13_rows && overlap(w13_rows, 2 * fd * n_sets, w13_tiled, 2 * fd * n_sets))
+    return MOE_ERR_INVALID_ARG;
+  if (w2_rows && overlap(w2_rows, fd * n_sets, w2_tiled, fd * n_sets)) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = s->wdtype == MOE_BF16;
+  hipError_t err = hipSuccess;
+  if (w13_rows)  // W1 and W3: 2 n matrices of [f][d]
+    err = moe::launch_pack(w13_rows, w13_tiled, s->d_ff, s->d_model, 2LL * n_sets, bf16, st);
+  if (err == hipSuccess && w2_rows)  // W2: n matrices of [d][f]
+    err = moe::launch_pack(w2_rows, w2_tiled, s->d_model, s->d_ff, (long long)n_sets, bf16, st);
+  return status_of(err);
 }
 
 int moe_pass_bytes(const moe_shape *s, const int32_t *idx, int32_t n, uint64_t *perslot,

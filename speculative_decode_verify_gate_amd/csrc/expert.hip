@@ -77,10 +77,17 @@ struct WT<false> {
 
 __device__ inline u32x4 ldg16(const unsigned char *p) { return *(const u32x4 *)p; }
 
+// Weights in the tiled layout are read exactly once per use, in contiguous
+// 1 KB fragments: nontemporal loads keep them from displacing the staged
+// activations and expert rows that are re-read.
+__device__ inline u32x4 ldg16_once(const unsigned char *p) {
+  return __builtin_nontemporal_load((const u32x4 *)p);
+}
+
 constexpr int kSpc = 4;                           // MFMA steps per chunk
 constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 
-template <bool BF16, bool UP, int CTMAX>
+template <bool BF16, bool UP, int CTMAX, bool TILED>
 __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   using T = WT<BF16>;
   constexpr int SPC = kSpc;
@@ -131,9 +138,20 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   }
   const int nsteps = K / T::kStep;
   const int nchunks = (nsteps + SPC - 1) / SPC;
-  const unsigned char *rowA = wA + (size_t)(rt * kTile + r) * K * EB;
-  const unsigned char *rowB = UP ? wB + (size_t)(rt * kTile + r) * K * EB : nullptr;
   const int lane_k = g * T::kPerLane;
+  // Where this lane's 16 bytes of step `step` start.  Row-major: row
+  // 16 rt + r, columns kStep*step + lane_k.  Tiled: fragment (rt, step) is
+  // 1 KB and the lane's unit is its lane index (the layout stores exactly the
+  // MFMA A-operand order), so a wave's load is one contiguous kilobyte.
+  const unsigned char *rowA, *rowB = nullptr;
+  if (TILED) {
+    rowA = wA + ((size_t)rt * nsteps * kWave + lane) * 16;
+    if (UP) rowB = wB + ((size_t)rt * nsteps * kWave + lane) * 16;
+  } else {
+    rowA = wA + ((size_t)(rt * kTile + r) * K + lane_k) * EB;
+    if (UP) rowB = wB + ((size_t)(rt * kTile + r) * K + lane_k) * EB;
+  }
+  const size_t step_bytes = TILED ? (size_t)kWave * 16 : (size_t)T::kStep * EB;
 
   // Issue the 16-byte weight loads of one chunk.  Branch-free on purpose: the
   // compiler can then count outstanding loads exactly and wait only for the
@@ -143,9 +161,14 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
 #pragma unroll
     for (int s = 0; s < SPC; ++s) {
       const int step = min(ch * SPC + s, nsteps - 1);
-      const size_t off = (size_t)(step * T::kStep + lane_k) * EB;
-      d1[s] = ldg16(rowA + off);
-      if (UP) d3[s] = ldg16(rowB + off);
+      const size_t off = (size_t)step * step_bytes;
+      if (TILED) {
+        d1[s] = ldg16_once(rowA + off);
+        if (UP) d3[s] = ldg16_once(rowB + off);
+      } else {
+        d1[s] = ldg16(rowA + off);
+        if (UP) d3[s] = ldg16(rowB + off);
+      }
     }
   };
 
@@ -335,28 +358,59 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   }
 }
 
-template <bool BF16, bool UP>
-hipError_t launch_expert(const ExpertArgs &a, hipStream_t st) {
+template <bool BF16, bool UP, bool TILED>
+hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
   const int blocks = (a.n_routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   const bool wide = a.N > kTile;
   // allow more than the default 64 KB of dynamic LDS, once per kernel
   static const hipError_t set_wide = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      kLdsBudget);
+      (const void *)expert_kernel<BF16, UP, 4, TILED>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   static const hipError_t set_narrow = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      kLdsBudget);
+      (const void *)expert_kernel<BF16, UP, 1, TILED>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (set_wide != hipSuccess) return set_wide;
   if (set_narrow != hipSuccess) return set_narrow;
   if (wide)
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4>), dim3(blocks), dim3(kBlock), a.lds_bytes,
-                       st, a);
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED>), dim3(blocks), dim3(kBlock),
+                       a.lds_bytes, st, a);
   else
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1>), dim3(blocks), dim3(kBlock), a.lds_bytes,
-                       st, a);
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1, TILED>), dim3(blocks), dim3(kBlock),
+                       a.lds_bytes, st, a);
   return hipGetLastError();
+}
+
+template <bool BF16, bool UP>
+hipError_t launch_expert(const ExpertArgs &a, hipStream_t st) {
+  return a.tiled ? launch_expert_layout<BF16, UP, true>(a, st)
+                 : launch_expert_layout<BF16, UP, false>(a, st);
+}
+
+// Row-major -> tiled, one thread per 16-byte unit of the output.  Unit u of a
+// matrix: fragment u / 64 = (rt, step), lane L = u % 64 -> source row
+// 16 rt + L % 16, columns STEP step + (L / 16) STEP/4 (see moe_verify.h).
+template <int STEP, int EB>
+__global__ __launch_bounds__(256) void pack_kernel(const unsigned char *__restrict__ src,
+                                                   unsigned char *__restrict__ dst, int R, int K,
+                                                   long long n_mats) {
+  const long long units_per_mat = (long long)R * K * EB / 16;
+  const long long total = units_per_mat * n_mats;
+  const int nsteps = K / STEP;
+  for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+       u += (long long)gridDim.x * blockDim.x) {
+    const long long mat = u / units_per_mat;
+    const long long q = u - mat * units_per_mat;
+    const long long frag = q / 64;
+    const int L = (int)(q - frag * 64);
+    const int rt = (int)(frag / nsteps);
+    const int step = (int)(frag - (long long)rt * nsteps);
+    const int row = rt * kTile + (L % 16);
+    const int col = step * STEP + (L / 16) * (STEP / 4);
+    const unsigned char *s = src + ((size_t)mat * R * K + (size_t)row * K + col) * EB;
+    *(u32x4 *)(dst + (size_t)u * 16) = *(const u32x4 *)s;
+  }
 }
 
 // y[t] = sum_j w[t][j] * o[t*k+j] + sum_s o[N*k + s*N + t], in slot order,
@@ -431,6 +485,21 @@ hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st) {
 
 hipError_t launch_down(const ExpertArgs &a, bool bf16, hipStream_t st) {
   return bf16 ? launch_expert<true, false>(a, st) : launch_expert<false, false>(a, st);
+}
+
+hipError_t launch_pack(const void *src, void *dst, int R, int K, long long n_mats, bool bf16,
+                       hipStream_t st) {
+  const long long units = (long long)R * K * (bf16 ? 2 : 4) / 16 * n_mats;
+  if (units == 0) return hipSuccess;
+  const long long want = (units + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  if (bf16)
+    hipLaunchKernelGGL((pack_kernel<32, 2>), dim3(blocks), dim3(256), 0, st,
+                       (const unsigned char *)src, (unsigned char *)dst, R, K, n_mats);
+  else
+    hipLaunchKernelGGL((pack_kernel<16, 4>), dim3(blocks), dim3(256), 0, st,
+                       (const unsigned char *)src, (unsigned char *)dst, R, K, n_mats);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const ExpertArgs &a, hipStream_t st) {

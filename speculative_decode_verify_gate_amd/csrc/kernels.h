@@ -44,6 +44,7 @@ struct ExpertArgs {
   void *abuf;             // [N*k + S*N][f] SwiGLU outputs, weight element type
   float *obuf;            // [N*k + S*N][d] expert outputs
   int d, f, E, k, S, N;
+  int tiled;              // weight layout: 0 row-major, 1 MOE_LAYOUT_TILED
   int dedup;              // 0: instance i is slot i; 1: instance u is the
                           //    u-th distinct selected expert
   int n_routed;           // routed instances in the grid
@@ -63,6 +64,9 @@ hipError_t launch_topk(const float *part, int splits, int N, int E, int k, float
 hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_down(const ExpertArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_combine(const ExpertArgs &a, hipStream_t st);
+// Row-major -> MOE_LAYOUT_TILED for n_mats matrices of R x K.
+hipError_t launch_pack(const void *src, void *dst, int R, int K, long long n_mats, bool bf16,
+                       hipStream_t st);
 
 // Dynamic LDS for the expert kernels at this token count (activations of up
 // to min(N, 64) tokens staged per window).

@@ -124,3 +124,23 @@ def test_status_strings():
     lib = B.load()
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace too small"
+
+
+def test_bad_layout_and_pack_arguments_are_rejected():
+    lib = B.load()
+    s = _shape()
+    sz = C.c_size_t(0)
+    cw = B.Weights(0x100000, 0x100000, 0x100000, 0x100000, 7)
+    rc = lib.moe_expert_pass_perslot(C.byref(s), C.byref(cw), FAKE, 4, FAKE, FAKE, FAKE,
+                                     None, C.byref(sz), None)
+    assert rc == -1
+    # overlapping source and destination
+    rc = lib.moe_pack_weights(C.byref(s), 2, C.c_void_p(0x100000), None,
+                              C.c_void_p(0x100000 + 4096), None, None)
+    assert rc == -1
+    # a source without a destination
+    rc = lib.moe_pack_weights(C.byref(s), 2, C.c_void_p(0x100000), None, None, None, None)
+    assert rc == -1
+    assert lib.moe_pack_weights(C.byref(s), -1, None, None, None, None, None) == -1
+    # nothing to do is fine and launches nothing
+    assert lib.moe_pack_weights(C.byref(s), 3, None, None, None, None, None) == 0

@@ -47,6 +47,39 @@ def _check_route(cfg, gate_w_dev, x_dev, gate_w_np, x_np):
     return idx, w, ref, int((~ok).sum())
 
 
+def _pack_numpy(W, step):
+    """MOE_LAYOUT_TILED of one row-major [R][K] matrix, from the header's
+    definition: fragment (rt, s) is 1 KB at (rt * K/step + s) * 1 KB; its
+    16-byte unit L holds row 16 rt + L % 16, columns step*s + (L//16)*step/4."""
+    R, K = W.shape
+    q = step // 4
+    n_s = K // step
+    out = np.empty(R * K, W.dtype)
+    for rt in range(R // 16):
+        for s_ in range(n_s):
+            base = (rt * n_s + s_) * 64 * q
+            for L in range(64):
+                c0 = step * s_ + (L // 16) * q
+                out[base + L * q: base + (L + 1) * q] = W[16 * rt + L % 16, c0:c0 + q]
+    return out
+
+
+@pytest.mark.parametrize("wdt", ["bf16", "f32"])
+def test_pack_matches_layout_definition(wdt):
+    cfg = small_config("pack", 128, 3, 1, 96, 1, wdt)
+    lay = synth.make_layer(cfg, "cpu")
+    shape = B.shape_of(cfg)
+    packed = B.pack_weights(shape, to_dev(lay))
+    torch.cuda.synchronize()
+    step = 32 if wdt == "bf16" else 16
+    for key in ("w13", "w2", "ws13", "ws2"):
+        src = synth.to_host_bits(lay[key])
+        got = synth.to_host_bits(packed[key]).reshape(src.shape[0], -1)
+        mats = src.reshape(-1, src.shape[-2], src.shape[-1])
+        want = np.concatenate([_pack_numpy(m, step).reshape(-1) for m in mats])
+        assert np.array_equal(got.reshape(-1), want), key
+
+
 def _run_both(cfg, lay_dev, x_dev, idx_dev, w_dev):
     shape = B.shape_of(cfg)
     y_ps = B.expert_pass_perslot(shape, lay_dev, x_dev, idx_dev, w_dev)
@@ -91,6 +124,10 @@ def test_small_layer_parity(case, n):
     y_ref, rb, sb, U_ref = oracle_y(cfg, host, x_np, ref["idx"], ref["w"].astype(np.float32))
     assert U == U_ref
     assert torch.equal(y_ps, y_dd), "per-slot and dedup outputs differ"
+    # the tiled weight layout feeds the MFMA the same operands: same bits
+    tiled = B.pack_weights(B.shape_of(cfg), lay_dev)
+    y_ps_t, y_dd_t, U_t, _ = _run_both(cfg, tiled, x_dev, idx_o, w_o)
+    assert U_t == U and torch.equal(y_ps_t, y_ps) and torch.equal(y_dd_t, y_dd)
     err = rel_err(y_ps.cpu().numpy(), y_ref)
     _say(f"   rel err {err:.3e}  U={U}  flagged={flagged}")
     assert err <= OUT_RTOL[wdt]
@@ -222,7 +259,9 @@ def _full_case(name, n, rep=0, tokens=None):
     gate_np = lay_dev["gate_w"].cpu().numpy()
     x_np = x_dev.cpu().numpy()
     idx, w, ref, flagged = _check_route(cfg, lay_dev["gate_w"], x_dev, gate_np, x_np)
-    y_ps, y_dd, U, _ = _run_both(cfg, lay_dev, x_dev, idx, w)
+    tiled = B.pack_weights(B.shape_of(cfg), {k: lay_dev[k] for k in ("w13", "w2", "ws13", "ws2")})
+    y_ps, y_dd, U, _ = _run_both(cfg, tiled, x_dev, idx, w)
+    del tiled
     assert torch.equal(y_ps, y_dd)
     gi = idx.cpu().numpy()
     assert U == O.pass_bytes(oshape(cfg), gi)[3]
