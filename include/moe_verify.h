@@ -29,9 +29,11 @@
  *    workspace == NULL the call stores the bytes it needs for this shape and
  *    token count in *workspace_bytes and returns MOE_OK without launching.
  *    Otherwise *workspace_bytes is the size supplied; a smaller size than
- *    needed returns MOE_ERR_WORKSPACE.  The workspace needs no
- *    initialisation, must be 256-byte aligned, and may not be shared by
- *    calls that can run concurrently.
+ *    needed returns MOE_ERR_WORKSPACE.  A workspace must be 256-byte
+ *    aligned and may not be shared by calls that can run concurrently.  The
+ *    expert-pass workspaces need no initialisation; the first 256 bytes of a
+ *    moe_route workspace must be zero before its first use, and every call
+ *    leaves them zero again (they count the workgroups that have finished).
  *  - Routing entries passed to the expert passes must lie in [0, E); that
  *    cannot be checked on the host without a copy, so an out-of-range entry
  *    is treated on the device as an empty slot (no weights read, zero
@@ -186,8 +188,9 @@ const char *moe_status_string(int status);
  * idle time around its kernel, so select only the kinds being measured.
  * Kernel kinds (bit positions of the mask, indices into the arrays): */
 enum moe_kernel_kind {
-  MOE_K_GATE = 0,    /* gate logits, split over K */
-  MOE_K_TOPK = 1,    /* top-k + softmax per token */
+  MOE_K_GATE = 0,    /* gate logits, split over K; when the partial logits of
+                        the pass fit 64 KB this launch also does the top-k */
+  MOE_K_TOPK = 1,    /* top-k + softmax per token (larger gates only) */
   MOE_K_COMPACT = 2, /* routing-trace compaction (dedup) */
   MOE_K_UP = 3,      /* W1/W3 + SwiGLU over all expert instances */
   MOE_K_DOWN = 4,    /* W2 over all expert instances */

@@ -116,7 +116,8 @@ def _stream():
 
 
 class Workspace:
-    """A grow-only device byte buffer reused across calls (256-byte aligned)."""
+    """A grow-only device byte buffer reused across calls (256-byte aligned,
+    zero-filled when allocated, as a routing workspace requires)."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -124,7 +125,7 @@ class Workspace:
 
     def get(self, nbytes):
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
 

@@ -45,9 +45,10 @@ size_t entry_rows(const moe_shape *s, int n) {
   return (size_t)n * s->top_k + (size_t)s->n_shared * n;
 }
 
+// [arrival counter | partial logits [splits][N][E]]
 size_t route_ws(const moe_shape *s, int n) {
-  return align_up((size_t)moe::gate_splits(s->d_model) * n * s->n_experts * sizeof(float),
-                  kAlign);
+  return kAlign + align_up((size_t)moe::gate_splits(s->d_model) * n * s->n_experts *
+                               sizeof(float), kAlign);
 }
 
 size_t cmp_ws(const moe_shape *s, int n) {
@@ -62,7 +63,6 @@ size_t abuf_ws(const moe_shape *s, int n) {
 size_t obuf_ws(const moe_shape *s, int n) {
   return align_up(entry_rows(s, n) * s->d_model * sizeof(float), kAlign);
 }
-
 
 // Workspace query / size check shared by the device calls.  Returns
 // MOE_OK and sets *launch when the call should go ahead.
@@ -210,15 +210,23 @@ int moe_route(const moe_shape *s, const float *gate_w, const float *x, int32_t n
   if ((rc = workspace_gate(ws, ws_bytes, route_ws(s, n), &launch)) != MOE_OK || !launch)
     return rc;
   hipStream_t st = (hipStream_t)stream;
-  float *part = (float *)ws;
-  hipError_t err = timed(MOE_K_GATE, st, [&] {
-    return moe::launch_gate(gate_w, x, n, s->d_model, s->n_experts, part, st);
-  });
-  if (err == hipSuccess)
-    err = timed(MOE_K_TOPK, st, [&] {
-      return moe::launch_topk(part, moe::gate_splits(s->d_model), n, s->n_experts, s->top_k,
-                              logits, topk_idx, topk_w, margin, st);
-    });
+  moe::RouteArgs a{};
+  a.gate_w = gate_w;
+  a.x = x;
+  a.N = n;
+  a.d = s->d_model;
+  a.E = s->n_experts;
+  a.k = s->top_k;
+  a.splits = moe::gate_splits(s->d_model);
+  a.done = (unsigned *)ws;
+  a.part = (float *)((unsigned char *)ws + kAlign);
+  a.logits = logits;
+  a.idx = topk_idx;
+  a.w = topk_w;
+  a.margin = margin;
+  hipError_t err = timed(MOE_K_GATE, st, [&] { return moe::launch_gate(a, st); });
+  if (err == hipSuccess && !moe::route_fused(n, s->d_model, s->n_experts))
+    err = timed(MOE_K_TOPK, st, [&] { return moe::launch_topk(a, st); });
   return status_of(err);
 }
 

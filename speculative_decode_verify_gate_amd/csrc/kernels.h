@@ -51,14 +51,28 @@ struct ExpertArgs {
   int lds_bytes;          // dynamic LDS per workgroup
 };
 
+// Routing.  Partial logits of all splits at most this many bytes: one launch
+// (the last gate workgroup also runs the top-k); otherwise gate + top-k.
+constexpr int kFusedRouteBytes = 64 * 1024;
+
+struct RouteArgs {
+  const float *gate_w, *x;
+  int N, d, E, k, splits;
+  float *part;                // [splits][N][E] partial logits
+  unsigned *done;             // arrival counter (one launch): zero on entry and exit
+  float *logits;              // [N][E] or nullptr
+  int32_t *idx;               // [N][k]
+  float *w;                   // [N][k]
+  float *margin;              // [N] or nullptr
+};
+
 int gate_splits(int d);
+bool route_fused(int N, int d, int E);
+hipError_t launch_gate(const RouteArgs &a, hipStream_t st);
+hipError_t launch_topk(const RouteArgs &a, hipStream_t st);
 hipError_t launch_compact(const int32_t *idx, int N, int k, int E, int32_t *cmp,
                           int32_t *n_unique, hipStream_t st);
 
-hipError_t launch_gate(const float *gate_w, const float *x, int N, int d, int E,
-                       float *part, hipStream_t st);
-hipError_t launch_topk(const float *part, int splits, int N, int E, int k, float *logits,
-                       int32_t *idx, float *w, float *margin, hipStream_t st);
 // Expert pass = up kernel, down kernel, combine kernel.  bf16 selects bf16
 // weights, else fp32.
 hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st);

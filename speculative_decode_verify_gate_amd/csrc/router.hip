@@ -4,14 +4,21 @@
 // logits = x @ gate_weights, keep the k largest, weights = softmax of the k
 // selected values.  Ties are broken toward the lower expert index.
 //
-// Two launches.  The gate GEMM [N x d] x [d x E] streams the fp32 gate matrix
-// once with fp32 MFMA (16 experts x 16 tokens per tile), split over K so
-// that enough workgroups stream it; each split writes fp32 partial logits.
-// The top-k kernel sums the partials in a fixed order (deterministic), then a
-// single wavefront per token runs k rounds of a (value desc, index asc)
-// argmax butterfly across the 64 lanes.
+// The gate GEMM [N x d] x [d x E] streams the fp32 gate matrix once with
+// fp32 MFMA (16 experts x 16 tokens per tile), split over K so that enough
+// workgroups stream it; each split yields fp32 partial logits.  Logits are
+// the partials summed in split order (deterministic).  Top-k: every
+// (token, expert) pair finds its rank under (value desc, index asc) by
+// counting, in LDS, the experts ahead of it; ranks below k are the slots.
+//
+// When all partials of a pass are small (at most 64 KB), one launch does
+// everything: the gate workgroups hand their partials over with
+// device-coherent stores and the last one to arrive sums them and runs the
+// top-k for every token.  Larger gates (e.g. 256 experts x 7168) use a second
+// launch for the top-k.
 #include <math.h>
 
+#include "coherent.h"
 #include "kernels.h"
 
 namespace moe {
@@ -22,17 +29,63 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kGateWaves = 4;
 constexpr int kGateKPerWave = kGateKPerBlock / kGateWaves;  // 64 = 4 steps of 16
 constexpr int kMaxColTiles = 4;                              // N <= 64
+constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
 
-// Partial logits of one 16-expert tile over one K split.
-// part[split][t][e] = sum over the split's K range of x[t][i] * gate_w[e][i].
-__global__ __launch_bounds__(256) void gate_kernel(const float *__restrict__ gate_w,
-                                                   const float *__restrict__ x, int N, int d,
-                                                   int E, float *__restrict__ part) {
+
+// Top-k + softmax of n_tok tokens whose logits sit in LDS (L[t][E]), by the
+// nth threads of the caller.  Each (token, expert) pair counts the experts
+// that rank before it in the order (logit desc, index asc): a strict total
+// order, so ranks are unique and equal the position a stable descending sort
+// gives.  Ranks 0..k-1 are the selection in slot order; rank k gives the
+// margin.  sel_v / sel_e: LDS [n_tok][MOE_MAX_TOPK + 1].  t0 is the global
+// index of token 0.  Ends with a barrier of the caller's threads.
+__device__ inline void select_topk(const float *L, int n_tok, int t0, const RouteArgs &a,
+                                   int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
+                                   int (*sel_e)[MOE_MAX_TOPK + 1]) {
+  const int E = a.E, k = a.k;
+  for (int p = tid; p < n_tok * E; p += nth) {
+    const int t = p / E;
+    const int e = p - t * E;
+    const float *row = L + (size_t)t * E;
+    const float v = row[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const float u = row[j];
+      rank += (u > v || (u == v && j < e)) ? 1 : 0;
+    }
+    if (rank <= k) {
+      sel_v[t][rank] = v;
+      sel_e[t][rank] = e;
+    }
+    if (a.logits) a.logits[(size_t)(t0 + t) * E + e] = v;
+  }
+  __syncthreads();
+  for (int p = tid; p < n_tok * k; p += nth) {
+    const int t = p / k;
+    const int j = p - t * k;
+    const float v0 = sel_v[t][0];
+    float denom = 0.f;
+    for (int i = 0; i < k; ++i) denom += expf(sel_v[t][i] - v0);
+    a.idx[(size_t)(t0 + t) * k + j] = sel_e[t][j];
+    a.w[(size_t)(t0 + t) * k + j] = expf(sel_v[t][j] - v0) / denom;
+    if (j == 0 && a.margin)
+      a.margin[t0 + t] = (k < E) ? sel_v[t][k - 1] - sel_v[t][k] : INFINITY;
+  }
+  __syncthreads();
+}
+
+// Partial logits of one 16-expert tile over one K split,
+// part[split][t][e] = sum over the split's K range of x[t][i] * gate_w[e][i];
+// with FUSED, the last workgroup also finishes the routing.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
+  const int N = a.N, d = a.d, E = a.E;
   const int n_et = (E + kTile - 1) / kTile;
   const int et = blockIdx.x % n_et;
   const int split = blockIdx.x / n_et;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int r = lane & 15;  // A row (expert) / B column (token) of this lane
   const int g = lane >> 4;  // K group of this lane
   const int n_ct = (N + kTile - 1) / kTile;
@@ -50,18 +103,18 @@ __global__ __launch_bounds__(256) void gate_kernel(const float *__restrict__ gat
   for (int s = 0; s < kGateKPerWave / 16; ++s) {
     const int k0 = k_begin + s * 16;
     if (k0 >= d) break;
-    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (expert < E) a = *(const f32x4 *)(gate_w + (size_t)expert * d + k0 + 4 * g);
+    f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (expert < E) av = *(const f32x4 *)(a.gate_w + (size_t)expert * d + k0 + 4 * g);
 #pragma unroll
     for (int ct = 0; ct < kMaxColTiles; ++ct) {
       if (ct < n_ct) {
         const int tok = ct * kTile + r;
         f32x4 b = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tok < N) b = *(const f32x4 *)(x + (size_t)tok * d + k0 + 4 * g);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[ct], 0, 0, 0);
+        if (tok < N) b = *(const f32x4 *)(a.x + (size_t)tok * d + k0 + 4 * g);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, b.x, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, b.y, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, b.z, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, b.w, acc[ct], 0, 0, 0);
       }
     }
   }
@@ -80,39 +133,80 @@ __global__ __launch_bounds__(256) void gate_kernel(const float *__restrict__ gat
     // lane holds rows (experts) 4g..4g+3 of the tile for token column r
     const int tok = ct * kTile + r;
     if (tok < N) {
-      float *dst = part + ((size_t)split * N + tok) * E;
+      float *dst = a.part + ((size_t)split * N + tok) * E;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int e = et * kTile + 4 * g + v;
-        if (e < E) dst[e] = s[v];
+        if (e < E) {
+          if (FUSED)
+            store_coherent(dst + e, s[v]);
+          else
+            dst[e] = s[v];
+        }
       }
     }
   }
+  if (!FUSED) return;
+
+  // ---- the last workgroup to finish sums the partials and routes
+  __shared__ int s_last;
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    // arrivals counted in the caller's workspace (zero before first use);
+    // the last workgroup puts it back to zero for the next call
+    s_last = atomicAdd(a.done, 1u) == gridDim.x - 1;
+    if (s_last) atomicExch(a.done, 0u);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  extern __shared__ float Ls[];  // [N][E] logits
+  const int splits = a.splits;
+  const int NE = N * E;
+  for (int i0 = 0; i0 < NE; i0 += 4 * 256) {
+    // the loads of 4 logits x 8 splits are issued before any is summed
+    for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+      float pv[4][8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = min(i0 + q * 256 + tid, NE - 1);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          pv[q][u] = load_coherent(a.part + (size_t)min(sp0 + u, splits - 1) * NE + i);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = i0 + q * 256 + tid;
+        if (i < NE) {
+          float acc_l = (sp0 == 0) ? 0.f : Ls[i];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (sp0 + u < splits) acc_l += pv[q][u];
+          Ls[i] = acc_l;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  __shared__ float sel_v[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
+  __shared__ int sel_e[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
+  select_topk(Ls, N, 0, a, tid, blockDim.x, sel_v, sel_e);
 }
 
-__device__ inline bool ranks_before(float v1, int e1, float v2, int e2) {
-  return v1 > v2 || (v1 == v2 && e1 < e2);
-}
-
-constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
-
-// One wavefront per token.
-__global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ part, int splits,
-                                                  int N, int E, int k,
-                                                  float *__restrict__ logits,
-                                                  int32_t *__restrict__ idx,
-                                                  float *__restrict__ w,
-                                                  float *__restrict__ margin) {
+// Unfused top-k: one wavefront per token sums its partials in split order.
+__global__ __launch_bounds__(64) void topk_kernel(RouteArgs a) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
-  float v[kMaxExpertsPerLane];
-  bool taken[kMaxExpertsPerLane];
+  const int N = a.N, E = a.E, splits = a.splits;
+  __shared__ float Ls[MOE_MAX_EXPERTS];
+  __shared__ float sel_v[1][MOE_MAX_TOPK + 1];
+  __shared__ int sel_e[1][MOE_MAX_TOPK + 1];
   const int n_q = (E + 63) / 64;
+  float v[kMaxExpertsPerLane];
 #pragma unroll
   for (int q = 0; q < kMaxExpertsPerLane; ++q) v[q] = 0.f;
-  // Sum the K-split partials in split order.  Loads of 8 splits (for every
-  // expert of the lane) are issued together so the partials, written by the
-  // gate kernel on other XCDs, cost one memory round trip per 8 splits.
+  // Loads of 8 splits (for every expert of the lane) are issued together so
+  // the partials cost one memory round trip per 8 splits.
   for (int sp0 = 0; sp0 < splits; sp0 += 8) {
     float pv[kMaxExpertsPerLane][8];
 #pragma unroll
@@ -122,7 +216,7 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ part
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int sp = min(sp0 + u, splits - 1);
-          pv[q][u] = part[((size_t)sp * N + t) * E + e];
+          pv[q][u] = a.part[((size_t)sp * N + t) * E + e];
         }
       }
     }
@@ -137,76 +231,34 @@ __global__ __launch_bounds__(64) void topk_kernel(const float *__restrict__ part
 #pragma unroll
   for (int q = 0; q < kMaxExpertsPerLane; ++q) {
     const int e = q * 64 + lane;
-    taken[q] = !(e < E);
-    if (e < E) {
-      if (logits) logits[(size_t)t * E + e] = v[q];
-    } else {
-      v[q] = -INFINITY;
-    }
-  }
-
-  __shared__ float sel_v[MOE_MAX_TOPK + 1];
-  __shared__ int sel_e[MOE_MAX_TOPK + 1];
-  const int rounds = (k < E) ? k + 1 : k;
-  for (int rd = 0; rd < rounds; ++rd) {
-    // best untaken candidate of this lane
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < kMaxExpertsPerLane; ++q) {
-      const int e = q * 64 + lane;
-      if (!taken[q] && (be == 0x7fffffff || ranks_before(v[q], e, bv, be))) {
-        bv = v[q];
-        be = e;
-      }
-    }
-    // butterfly: every lane ends with the same (unique) winner
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (oe != 0x7fffffff && (be == 0x7fffffff || ranks_before(ov, oe, bv, be))) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) {
-#pragma unroll
-      for (int q = 0; q < kMaxExpertsPerLane; ++q)
-        if (q == (be >> 6)) taken[q] = true;
-    }
-    if (lane == 0) {
-      sel_v[rd] = bv;
-      sel_e[rd] = be;
-    }
+    if (e < E) Ls[e] = v[q];
   }
   __syncthreads();
-  if (lane < k) {
-    const float v0 = sel_v[0];
-    float denom = 0.f;
-    for (int j = 0; j < k; ++j) denom += expf(sel_v[j] - v0);
-    idx[(size_t)t * k + lane] = sel_e[lane];
-    w[(size_t)t * k + lane] = expf(sel_v[lane] - v0) / denom;
-  }
-  if (lane == 0 && margin) margin[t] = (k < E) ? sel_v[k - 1] - sel_v[k] : INFINITY;
+  select_topk(Ls, 1, t, a, lane, 64, sel_v, sel_e);
 }
 
 }  // namespace
 
 int gate_splits(int d) { return (d + kGateKPerBlock - 1) / kGateKPerBlock; }
 
-hipError_t launch_gate(const float *gate_w, const float *x, int N, int d, int E, float *part,
-                       hipStream_t st) {
-  const int n_et = (E + kTile - 1) / kTile;
-  const int blocks = n_et * gate_splits(d);
-  hipLaunchKernelGGL(gate_kernel, dim3(blocks), dim3(256), 0, st, gate_w, x, N, d, E, part);
+bool route_fused(int N, int d, int E) {
+  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes;
+}
+
+hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
+  const int n_et = (a.E + kTile - 1) / kTile;
+  const int blocks = n_et * a.splits;
+  if (route_fused(a.N, a.d, a.E)) {
+    const size_t lds = (size_t)a.N * a.E * sizeof(float);
+    hipLaunchKernelGGL(gate_kernel<true>, dim3(blocks), dim3(256), lds, st, a);
+  } else {
+    hipLaunchKernelGGL(gate_kernel<false>, dim3(blocks), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *part, int splits, int N, int E, int k, float *logits,
-                       int32_t *idx, float *w, float *margin, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3(N), dim3(64), 0, st, part, splits, N, E, k, logits,
-                     idx, w, margin);
+hipError_t launch_topk(const RouteArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel, dim3(a.N), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

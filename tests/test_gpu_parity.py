@@ -220,6 +220,25 @@ def test_router_ties_pick_lowest_index():
     assert np.array_equal(gi, ref["idx"])
 
 
+@pytest.mark.parametrize("E,d", [(64, 512), (256, 2048)])
+def test_route_reuses_its_workspace(E, d):
+    """One routing workspace across many calls (its arrival counter must be
+    back at zero after every call); each call checked against the oracle."""
+    cfg = small_config("reuse", d, E, 6, 64, 0, "bf16")
+    lay = synth.make_layer(cfg, "cpu")
+    gw = lay["gate_w"].cuda()
+    ws = B.Workspace()
+    for rep, n in enumerate([1, 16, 3, 64, 7, 16, 1, 33] * 2):
+        if n * cfg.k > B.MAX_SLOTS:
+            continue
+        x = synth.make_hidden(cfg, n, rep, "cpu")
+        idx, w = B.route(B.shape_of(cfg), gw, x.cuda(), ws=ws)
+        ref = O.route(oshape(cfg), lay["gate_w"].numpy(), x.numpy(), tie_eps=TIE_EPS)
+        ok = ref["flags"] == 0
+        assert np.array_equal(idx.cpu().numpy()[ok], ref["idx"][ok]), (rep, n)
+        assert int(ws.buf[:4].view(torch.int32).item()) == 0
+
+
 def test_runs_are_bitwise_deterministic():
     cfg = small_config("det", 512, 64, 6, 352, 2, "bf16")
     lay_dev = to_dev(synth.make_layer(cfg, "cpu"))
