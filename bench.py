@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from speculative_decode_verify_gate_amd import binding as B  # noqa: E402
+from speculative_decode_verify_gate_amd import stepmodel  # noqa: E402
 from speculative_decode_verify_gate_amd import synth  # noqa: E402
 
 METRIC = "µs & effective HBM GB/s per n-token MoE verify pass, per-slot vs dedup"
@@ -67,6 +68,12 @@ class Engines:
                                    ws=self.ws_dd)
 
 
+def hold_gpu(ms):
+    """Keep the current stream busy for about `ms` milliseconds (a spin
+    kernel), so that work queued behind it starts back to back."""
+    torch.cuda._sleep(int(max(ms, 1.0) * 2.4e6))
+
+
 def expert_bytes(cfg):
     return 3 * cfg.d * cfg.f * cfg.wbytes
 
@@ -94,7 +101,7 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps):
         ev = []
         # keep the GPU busy while the host queues the whole batch, so that no
         # event pair measures host launch latency
-        torch.cuda._sleep(20_000_000)
+        hold_gpu(0.3 * reps)
         for rep in range(reps):
             x = xs[(n, rep)]
             rec = {}
@@ -141,6 +148,152 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps):
         log(f"  n={n:2d} perslot {r['perslot']['us']:8.1f} us {r['perslot']['GBs']:7.0f} GB/s | "
             f"dedup {r['dedup']['us']:8.1f} us {r['dedup']['GBs']:7.0f} GB/s | "
             f"u={u_bar:.3f} r={r['r']:.3f}")
+    return out
+
+
+def calibrate(cfg, eng, layers, xs, xreps, sweep, reps):
+    """One-layer calibration of the step-time model t = B / BW + t0.
+    Per-slot: B = N k B_e at every n, timed on the standard routing trace
+    (the sweep).  Dedup: at every n, crafted routings with exactly U
+    distinct experts for U spread over k .. min(E, N k), B = U B_e.  Shared
+    experts and the gate are the same in both engines and land in t0.
+    Returns the fits and, per n, r(n) = BW_dd(n) / BW_ps."""
+    Be = expert_bytes(cfg)
+    k, E = cfg.k, cfg.E
+    ns = [r["n"] for r in sweep]
+    fit_ps = stepmodel.fit_line([cfg.tokens(n) * k * Be for n in ns],
+                                [r["perslot"]["us"] for r in sweep])
+    nL = len(layers)
+    turn = 0
+    points = []
+    per_n = {}
+    for n in ns:
+        N = cfg.tokens(n)
+        y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+        grid = sorted({int(round(u)) for u in np.linspace(k, min(E, N * k), 6)})
+        meas = []
+        for gi, U in enumerate(grid):
+            idx_np, w_np = synth.crafted_routing(N, k, E, U, seed=cfg.seed * 10**4 + n * 100 + gi)
+            idx = torch.from_numpy(idx_np).cuda()
+            w = torch.from_numpy(w_np).cuda()
+            evs = []
+            hold_gpu(0.1 * reps)
+            for rep in range(reps):
+                lay = layers[turn % nL]
+                turn += 1
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record()
+                eng.dedup(lay, xs[(n, rep % xreps)], idx, w, y)
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            meas.append((U, us))
+            points.append((n, U * Be, us))
+        rec = {"U": [m[0] for m in meas], "us": [round(m[1], 2) for m in meas]}
+        if len(grid) >= 2:
+            f = stepmodel.fit_line([m[0] * Be for m in meas], [m[1] for m in meas])
+            r, r_sd = stepmodel.bandwidth_ratio(f, fit_ps)
+            rec.update({"fit": f.as_dict(), "r": round(r, 4), "r_sd": round(r_sd, 4)})
+            rec["_fit"] = f
+        per_n[n] = rec
+        log(f"  calib n={n:2d} U={rec['U']} us={rec['us']}"
+            + (f" r={rec['r']:.3f}" if "r" in rec else ""))
+    fit_dd = stepmodel.fit_line([p[1] for p in points], [p[2] for p in points])
+    r_all, r_all_sd = stepmodel.bandwidth_ratio(fit_dd, fit_ps)
+    return {"perslot": fit_ps, "dedup_pooled": fit_dd, "r_pooled": (r_all, r_all_sd),
+            "per_n": per_n}
+
+
+def predict_from_calibration(cfg, calib, n, u_bar):
+    """Model prediction at pass size n and byte share u: (r(n), saving us,
+    its standard error).  Uses the per-n dedup fit where one exists, else
+    the pooled one."""
+    N = cfg.tokens(n)
+    b_ps = N * cfg.k * expert_bytes(cfg)
+    rec = calib["per_n"].get(n, {})
+    f_dd = rec.get("_fit", calib["dedup_pooled"])
+    r, r_sd = stepmodel.bandwidth_ratio(f_dd, calib["perslot"])
+    sav, sav_sd = stepmodel.predicted_saving(calib["perslot"], f_dd, b_ps, u_bar * b_ps)
+    return r, r_sd, sav, sav_sd
+
+
+def calibration_json(calib):
+    return {"model": "t_us = bytes / BW + t0 (routed expert bytes; shared experts and "
+                     "gate in t0)",
+            "perslot": calib["perslot"].as_dict(),
+            "dedup_pooled": calib["dedup_pooled"].as_dict(),
+            "r_pooled": round(calib["r_pooled"][0], 4),
+            "r_pooled_sd": round(calib["r_pooled"][1], 4),
+            "dedup_by_n": {str(n): {k: v for k, v in rec.items() if k != "_fit"}
+                           for n, rec in calib["per_n"].items()}}
+
+
+def rho_sweep(cfg, eng, layers, calib, reps):
+    """The layer stack at each rho: per (rho, n), `reps` stack passes per
+    engine, each pass running every layer on the same hidden states (route
+    + expert pass per layer).  A route-only stack pass is timed too, so the
+    expert-pass share is the difference.  U is read from the dedup engine's
+    device counter of every layer pass."""
+    nL = len(layers)
+    Be = expert_bytes(cfg)
+    out = []
+    ns = list(cfg.n_values)
+    for ri, rho in enumerate(cfg.rhos):
+        recs = []
+        for n in ns:
+            N = cfg.tokens(n)
+            y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+            nu = torch.zeros((reps * nL,), dtype=torch.int32, device="cuda")
+            xs = [synth.make_hidden(cfg, n, rep, "cuda", rho=rho, rho_index=ri)
+                  for rep in range(reps)]
+            t = {"route": [], "perslot": [], "dedup": []}
+            evs = []
+            for rep in range(reps):
+                x = xs[rep]
+                row = {}
+                for name in ("route", "perslot", "dedup"):
+                    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                    # the host queues the whole stack pass while the GPU waits
+                    hold_gpu(0.1 * nL)
+                    e0.record()
+                    for L in range(nL):
+                        idx, w = eng.route(layers[L], x)
+                        if name == "perslot":
+                            eng.perslot(layers[L], x, idx, w, y)
+                        elif name == "dedup":
+                            B.expert_pass_dedup(eng.shape, layers[L], x, idx, w, y=y,
+                                                n_unique=nu[rep * nL + L:rep * nL + L + 1],
+                                                ws=eng.ws_dd)
+                    e1.record()
+                    row[name] = (e0, e1)
+                evs.append(row)
+            torch.cuda.synchronize()
+            for row in evs:
+                for name, (e0, e1) in row.items():
+                    t[name].append(e0.elapsed_time(e1) * 1e3)
+            U = nu.cpu().numpy().astype(np.float64)
+            u_bar = float(U.mean()) / (N * cfg.k)
+            med = {k: float(np.median(v)) for k, v in t.items()}
+            ps = (med["perslot"] - med["route"]) / nL
+            dd = (med["dedup"] - med["route"]) / nL
+            r, r_sd, sav, sav_sd = predict_from_calibration(cfg, calib, n, u_bar)
+            rec = {"n": n, "u_bar": round(u_bar, 4), "U_mean": round(float(U.mean()), 2),
+                   "stack_us": {k: round(v, 1) for k, v in med.items()},
+                   "perslot_layer_us": round(ps, 2), "dedup_layer_us": round(dd, 2),
+                   "perslot_GBs": round((N * cfg.k + cfg.S) * Be / ps / 1e3, 1),
+                   "dedup_GBs": round((U.mean() + cfg.S) * Be / dd / 1e3, 1),
+                   "saving_us": round(ps - dd, 2),
+                   "r": round(r, 4), "r_sd": round(r_sd, 4),
+                   "predicted_saving_us": round(sav, 2),
+                   "predicted_saving_sd_us": round(sav_sd, 2),
+                   "dedup_faster": dd < ps, "u_lt_r": u_bar < r}
+            recs.append(rec)
+            log(f"  rho={rho:.2f} n={n:2d} u={u_bar:.3f} r={r:.3f} per-layer ps {ps:7.1f} "
+                f"dd {dd:7.1f} us, saving {ps - dd:6.1f} (pred {sav:6.1f} +- {sav_sd:.1f})")
+        out.append({"rho": rho, "passes_per_n": reps, "layers": nL, "by_n": recs,
+                    "crossover": {"measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in recs]),
+                                  "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_lt_r"] for r in recs])}})
     return out
 
 
@@ -246,7 +399,14 @@ def main():
     ap.add_argument("--config", default="v2lite", choices=sorted(synth.CONFIGS))
     ap.add_argument("--n", type=int, default=None, help="pass size of the timed step")
     ap.add_argument("--layers", type=int, default=None, help="weight sets in the rotation")
-    ap.add_argument("--reps", type=int, default=24, help="passes per n in the sweep")
+    ap.add_argument("--reps", type=int, default=48, help="passes per n in the sweep")
+    ap.add_argument("--calib-reps", type=int, default=16,
+                    help="passes per (n, U) point of the dedup calibration")
+    ap.add_argument("--rho-sweep", action="store_true",
+                    help="instead of the bench line: the routing-overlap sweep over the "
+                         "26-layer V2-Lite stack (one JSON document)")
+    ap.add_argument("--stack-reps", type=int, default=32,
+                    help="stack passes per (rho, n) in the rho sweep")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -277,10 +437,11 @@ def main():
                           "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}))
         return
 
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.CONFIGS["v2stack" if args.rho_sweep else args.config]
     n_head = args.n or max(cfg.n_values)
     layer_bytes = (cfg.E + cfg.S) * expert_bytes(cfg)
-    n_layers = args.layers or max(2, min(8, int(8e9 // layer_bytes)))
+    n_layers = args.layers or (cfg.layers if args.rho_sweep else
+                               max(2, min(8, int(8e9 // layer_bytes))))
     log(f"[bench] {cfg.name}: {n_layers} weight sets of {layer_bytes / 1e9:.2f} GB, "
         f"timed step n={n_head}")
     layers = []
@@ -294,15 +455,34 @@ def main():
         log(f"[bench] weights {L + 1}/{n_layers} drawn and packed")
     eng = Engines(cfg)
 
-    sweep = None
-    if not args.no_sweep:
+    sweep = calib = None
+    if not args.no_sweep or args.rho_sweep:
         xs = {(n, rep): synth.make_hidden(cfg, n, rep, "cuda")
               for n in cfg.n_values for rep in range(args.reps)}
         log("[bench] sweep warmup")
         run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 2)
         log("[bench] sweep")
         sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps)
+        log("[bench] dedup calibration on crafted routings")
+        calib = calibrate(cfg, eng, layers, xs, args.reps, sweep, args.calib_reps)
+        for r in sweep:
+            rr, rr_sd, sav, sav_sd = predict_from_calibration(cfg, calib, r["n"], r["u_bar"])
+            r["r_trace"] = r.pop("r")
+            r["r"], r["r_sd"] = round(rr, 4), round(rr_sd, 4)
+            r["predicted_saving_us"], r["predicted_saving_sd_us"] = round(sav, 2), round(sav_sd, 2)
+            r["saving_us"] = round(r["perslot"]["us"] - r["dedup"]["us"], 2)
         del xs
+
+    if args.rho_sweep:
+        log(f"[bench] rho sweep over {n_layers} layers")
+        doc = {"kind": "routing-overlap sweep",
+               "workload": f"{cfg.name}: V2-Lite-shaped layer stacked {n_layers} deep "
+                           f"({n_layers * layer_bytes / 1e9:.1f} GB of weights), "
+                           f"n = 1..{max(cfg.n_values)}",
+               "single_layer_sweep": sweep, "calibration": calibration_json(calib),
+               "by_rho": rho_sweep(cfg, eng, layers, calib, args.stack_reps)}
+        print(json.dumps(doc), flush=True)
+        return
 
     x = synth.make_hidden(cfg, n_head, 99, "cuda")
     log(f"[bench] timed steps: {args.warmup} warmup + {args.steps}")
@@ -369,11 +549,14 @@ def main():
         "up_kernel_ms_total": round(up_ms, 3),
     }
     if sweep is not None:
+        ns = [r["n"] for r in sweep]
         out["sweep"] = sweep
-        cross_m = next((r["n"] for r in sweep if r["dedup_faster"]), None)
-        cross_p = next((r["n"] for r in sweep if r["u_bar"] < r["r"]), None)
-        out["crossover"] = {"measured": cross_m if cross_m is not None else "never",
-                            "predicted_u_lt_r": cross_p if cross_p is not None else "never"}
+        out["calibration"] = calibration_json(calib)
+        out["crossover"] = {
+            "measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in sweep]),
+            "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_bar"] < r["r"] for r in sweep]),
+            "predicted_model_saving_gt_0": stepmodel.first_n(
+                ns, [r["predicted_saving_us"] > 0 for r in sweep])}
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
         del layers

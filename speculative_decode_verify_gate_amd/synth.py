@@ -27,6 +27,7 @@ on the CPU copies the drawn tensors across.
 """
 from dataclasses import dataclass, field
 import math
+import numpy as np
 
 import torch
 
@@ -154,3 +155,20 @@ def to_host_bits(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+def crafted_routing(N: int, k: int, E: int, U: int, seed: int):
+    """A routing of N tokens with exactly U distinct experts, for timing the
+    dedup engine at a chosen byte share: U experts drawn without
+    replacement, slot (t, j) takes expert number (t*k + j) mod U of them.
+    Consecutive slots of a token are distinct because k <= U, and every one
+    of the U experts is used because U <= N*k.  Weights are uniform 1/k.
+    Returns (idx int32 [N][k], w float32 [N][k]) as numpy arrays."""
+    if not (k <= U <= min(E, N * k)):
+        raise ValueError(f"U={U} outside [k, min(E, N*k)] = [{k}, {min(E, N * k)}]")
+    rng = np.random.default_rng(seed)
+    experts = rng.permutation(E)[:U]
+    slots = np.arange(N * k).reshape(N, k)
+    idx = experts[slots % U].astype(np.int32)
+    w = np.full((N, k), 1.0 / k, dtype=np.float32)
+    return idx, w

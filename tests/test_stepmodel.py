@@ -1,0 +1,104 @@
+"""Host logic of the step-time model and the crafted routings used to
+calibrate it (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from speculative_decode_verify_gate_amd import stepmodel as M
+from speculative_decode_verify_gate_amd import synth
+
+
+def _line(bw_GBs, t0, nbytes):
+    return np.asarray(nbytes, dtype=np.float64) / (bw_GBs * 1e3) + t0
+
+
+def test_exact_line_is_recovered():
+    b = np.array([1e8, 3e8, 7e8, 1.6e9])
+    f = M.fit_line(b, _line(6400.0, 11.5, b))
+    assert f.bw_GBs == pytest.approx(6400.0, rel=1e-10)
+    assert f.t0 == pytest.approx(11.5, rel=1e-10)
+    assert f.resid_sd == pytest.approx(0.0, abs=1e-9)
+    t, sd = f.predict(5e8)
+    assert t == pytest.approx(5e8 / 6.4e6 + 11.5, rel=1e-12)
+    assert sd == pytest.approx(0.0, abs=1e-6)
+
+
+def test_fit_and_errors_match_scipy_linregress():
+    rng = np.random.default_rng(7)
+    b = np.linspace(1e8, 1.7e9, 16)
+    t = _line(5500.0, 9.0, b) + rng.normal(0.0, 2.0, b.size)
+    f = M.fit_line(b, t)
+    ref = stats.linregress(b, t)
+    assert f.slope == pytest.approx(ref.slope, rel=1e-9)
+    assert f.t0 == pytest.approx(ref.intercept, rel=1e-9)
+    assert math.sqrt(f.cov[0, 0]) == pytest.approx(ref.stderr, rel=1e-6)
+    assert math.sqrt(f.cov[1, 1]) == pytest.approx(ref.intercept_stderr, rel=1e-6)
+
+
+def test_fit_needs_two_distinct_points():
+    with pytest.raises(ValueError):
+        M.fit_line([1e8], [10.0])
+    with pytest.raises(ValueError):
+        M.fit_line([1e8, 1e8], [10.0, 11.0])
+    with pytest.raises(ValueError):
+        M.fit_line([1e8, 2e8], [10.0])
+
+
+def test_ratio_and_saving_on_exact_lines():
+    b = np.array([1e8, 5e8, 9e8])
+    ps = M.fit_line(b, _line(6000.0, 10.0, b))
+    dd = M.fit_line(b, _line(4500.0, 10.0, b))
+    r, r_sd = M.bandwidth_ratio(dd, ps)
+    assert r == pytest.approx(0.75, rel=1e-10)
+    assert r_sd == pytest.approx(0.0, abs=1e-9)
+    b_ps = 1.2e9
+    for u in (0.5, 0.75, 0.9):
+        sav, sd = M.predicted_saving(ps, dd, b_ps, u * b_ps)
+        assert sav == pytest.approx(b_ps / 6e6 - u * b_ps / 4.5e6, rel=1e-9)
+        # common fixed time: dedup saves time exactly when u < r
+        if u != 0.75:
+            assert (sav > 0) == (u < r)
+        else:
+            assert sav == pytest.approx(0.0, abs=1e-9)
+
+
+def test_ratio_error_propagation_matches_monte_carlo():
+    rng = np.random.default_rng(3)
+    b = np.linspace(2e8, 1.6e9, 12)
+    ps = M.fit_line(b, _line(6000.0, 10.0, b) + rng.normal(0, 3.0, b.size))
+    dd = M.fit_line(b, _line(4000.0, 14.0, b) + rng.normal(0, 3.0, b.size))
+    r, r_sd = M.bandwidth_ratio(dd, ps)
+    a_ps = rng.normal(ps.slope, math.sqrt(ps.cov[0, 0]), 200_000)
+    a_dd = rng.normal(dd.slope, math.sqrt(dd.cov[0, 0]), 200_000)
+    mc = a_ps / a_dd
+    assert r == pytest.approx(float(np.median(mc)), rel=0.02)
+    assert r_sd == pytest.approx(float(np.std(mc)), rel=0.1)
+
+
+def test_first_n():
+    assert M.first_n([1, 2, 3, 4], [False, False, True, True]) == 3
+    assert M.first_n([1, 2, 3], [False, False, False]) == "never"
+
+
+@pytest.mark.parametrize("N,k,E,U", [(1, 6, 64, 6), (16, 6, 64, 6), (16, 6, 64, 64),
+                                     (16, 6, 64, 37), (4, 2, 8, 8), (64, 8, 256, 256),
+                                     (3, 2, 8, 5)])
+def test_crafted_routing_has_exactly_U_experts(N, k, E, U):
+    idx, w = synth.crafted_routing(N, k, E, U, seed=N * 1000 + U)
+    assert idx.shape == (N, k) and idx.dtype == np.int32
+    assert np.unique(idx).size == U
+    assert idx.min() >= 0 and idx.max() < E
+    for row in idx:
+        assert np.unique(row).size == k
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+
+
+def test_crafted_routing_rejects_impossible_U():
+    with pytest.raises(ValueError):
+        synth.crafted_routing(2, 6, 64, 5, seed=0)     # U < k
+    with pytest.raises(ValueError):
+        synth.crafted_routing(2, 6, 64, 13, seed=0)    # U > N k
+    with pytest.raises(ValueError):
+        synth.crafted_routing(16, 2, 8, 9, seed=0)     # U > E
