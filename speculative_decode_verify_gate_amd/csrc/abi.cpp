@@ -1,7 +1,7 @@
 // abi.cpp -- the C ABI of include/moe_verify.h: argument validation,
 // workspace sizing, the launch sequence of each call and the optional
 // per-kernel event timing.  Kernels live in router.hip and expert.hip
-// (the dedup compaction routine in compact.h).
+// (the dedup compaction, done inside the up kernel, in compact.h).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -167,6 +167,8 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.cmp = dedup ? (int32_t *)base : nullptr;
   a.abuf = base + c_bytes;
   a.obuf = (float *)(base + c_bytes + a_bytes);
+  a.cmp_out = dedup ? (int32_t *)base : nullptr;
+  a.n_unique = n_unique;
   a.d = s->d_model;
   a.f = s->d_ff;
   a.E = s->n_experts;
@@ -179,15 +181,10 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.n_routed = dedup ? (slots < s->n_experts ? slots : s->n_experts) : slots;
 
   hipError_t err = hipSuccess;
-  if (dedup)
-    err = timed(MOE_K_COMPACT, st, [&] {
-      return moe::launch_compact(idx, n, s->top_k, s->n_experts, (int32_t *)base, n_unique, st);
-    });
-  a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true);
-  if (err == hipSuccess)
-    err = timed(MOE_K_UP, st, [&] { return moe::launch_up(a, bf16, st); });
+  a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true, s->n_experts);
+  err = timed(MOE_K_UP, st, [&] { return moe::launch_up(a, bf16, st); });
   if (err == hipSuccess) {
-    a.lds_bytes = moe::expert_lds_bytes(n, s->d_ff, bf16, false);
+    a.lds_bytes = moe::expert_lds_bytes(n, s->d_ff, bf16, false, s->n_experts);
     err = timed(MOE_K_DOWN, st, [&] { return moe::launch_down(a, bf16, st); });
   }
   if (err == hipSuccess)

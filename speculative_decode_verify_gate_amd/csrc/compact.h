@@ -1,0 +1,159 @@
+// compact.h -- routing-trace compaction for the deduplicating engine, done
+// inside the up kernel's workgroups.
+//
+// "Speculative Decoding for Mixture-of-Experts Models: Expert Bytes, Kernel
+// Bandwidth and the Best Draft Length", abstract: a deduplicating engine
+// reads each selected expert once per pass, so it needs, per distinct
+// expert, the (token, slot) entries that chose it.  The N*k <= 512 routing
+// entries are few, so every up-kernel workgroup derives what it needs from
+// them directly (no separate launch):
+//   local_instance: the u-th distinct valid expert (ascending) and its
+//                   entries in slot order, from a 256-bit presence mask and
+//                   wave ballots;
+//   write_record:   one workgroup also writes the full compaction record for
+//                   the down kernel and the caller (counts, offsets, unique
+//                   list, grouped slot list, U).
+// Both are deterministic: masks are built with order-independent bit ORs and
+// counts with integer adds, and list order is slot order.
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+// The u-th distinct valid expert of idx[0 .. slots) in ascending order, or
+// -1 when there are at most u of them; its entries (slot s = t*k + j, in
+// increasing s) go to ent_row[] (s) and ent_tok[] (s / k), their number to
+// *m.  All threads of the workgroup call it (it contains barriers) and get
+// the same result.  slots <= 2 * blockDim.x.
+template <class Row, class Tok>
+__device__ inline int local_instance(const int32_t *__restrict__ idx, int slots, int E, int k,
+                                     int u, Row *ent_row, Tok *ent_tok, int *m) {
+  constexpr int kWords = MOE_MAX_EXPERTS / 32;
+  constexpr int kMaxWaves = 16;
+  __shared__ uint32_t pres[kWords];
+  __shared__ int wcnt[2][kMaxWaves];
+  __shared__ int s_e;
+  const int tid = threadIdx.x;
+  const int nth = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nw = nth >> 6;
+
+  if (tid < kWords) pres[tid] = 0u;
+  int es[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int s = p * nth + tid;
+    const int v = s < slots ? idx[s] : -1;
+    es[p] = (v >= 0 && v < E) ? v : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+    if (es[p] >= 0) atomicOr(&pres[es[p] >> 5], 1u << (es[p] & 31));
+  __syncthreads();
+  if (tid == 0) {
+    int e = -1, left = u;
+    for (int w = 0; w < kWords && e < 0; ++w) {
+      uint32_t bits = pres[w];
+      const int c = __popc(bits);
+      if (left < c) {
+        for (int i = 0; i < left; ++i) bits &= bits - 1u;  // drop the lowest bits
+        e = w * 32 + __ffs(bits) - 1;
+      } else {
+        left -= c;
+      }
+    }
+    s_e = e;
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0) return -1;
+
+  // entries of e in slot order: per pass, a wave's matches are counted with
+  // a ballot and placed after the matches of earlier waves and passes
+  uint64_t bal[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    bal[p] = __ballot(es[p] == e);
+    if (lane == 0) wcnt[p][wave] = __popcll(bal[p]);
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0, total = 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    int before = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+      before += (w < wave) ? wcnt[p][w] : 0;
+      all += wcnt[p][w];
+    }
+    if (es[p] == e) {
+      const int pos = base + before + __popcll(bal[p] & below);
+      const int s = p * nth + tid;
+      ent_row[pos] = (Row)s;
+      ent_tok[pos] = (Tok)(s / k);
+    }
+    base += all;
+    total += all;
+  }
+  *m = total;
+  __syncthreads();
+  return e;
+}
+
+// The full compaction record of idx (layout CompactLayout, documented in
+// moe_verify.h) and U to *n_unique (if given).  Called by one workgroup;
+// scratch is at least (2 * E + 1 + slots) ints of LDS that the caller does
+// not use meanwhile.  slots <= 2 * blockDim.x.
+__device__ inline void write_record(const int32_t *__restrict__ idx, int slots, int E,
+                                    int32_t *__restrict__ cmp, int32_t *__restrict__ n_unique,
+                                    int *scratch) {
+  const CompactLayout L{E, slots};
+  int *cnt = scratch;           // [E]
+  int *offs = cnt + E;          // [E + 1]
+  int *ev = offs + E + 1;       // [slots] expert of each slot (-1: none)
+  const int tid = threadIdx.x;
+  const int nth = blockDim.x;
+
+  for (int e = tid; e < E; e += nth) cnt[e] = 0;
+  for (int s = tid; s < slots; s += nth) {
+    const int v = idx[s];
+    ev[s] = (v >= 0 && v < E) ? v : -1;
+  }
+  __syncthreads();
+  for (int s = tid; s < slots; s += nth)
+    if (ev[s] >= 0) atomicAdd(&cnt[ev[s]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    // exclusive prefix sums of the counts and of presence (E <= 256)
+    int o = 0, up = 0;
+    for (int e = 0; e < E; ++e) {
+      offs[e] = o;
+      o += cnt[e];
+      if (cnt[e] > 0) cmp[L.uniq() + up++] = e;
+    }
+    offs[E] = o;
+    for (int q = up; q < E; ++q) cmp[L.uniq() + q] = -1;
+    cmp[L.u()] = up;
+    if (n_unique) *n_unique = up;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nth) {
+    cmp[L.counts() + e] = cnt[e];
+    cmp[L.offs() + e] = offs[e];
+  }
+  if (tid == 0) cmp[L.offs() + E] = offs[E];
+  // a slot's place in its expert's list: slots before it with that expert
+  for (int s = tid; s < slots; s += nth) {
+    const int e = ev[s];
+    if (e < 0) continue;
+    int rank = 0;
+    for (int q = 0; q < s; ++q) rank += (ev[q] == e) ? 1 : 0;
+    cmp[L.list() + offs[e] + rank] = s;
+  }
+  __syncthreads();  // scratch is free again
+}
+
+}  // namespace moe

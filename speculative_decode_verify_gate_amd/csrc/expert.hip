@@ -33,6 +33,7 @@
 //    others (dedup).
 #include <math.h>
 
+#include "compact.h"
 #include "kernels.h"
 
 namespace moe {
@@ -87,8 +88,23 @@ __device__ inline u32x4 ldg16_once(const unsigned char *p) {
 constexpr int kSpc = 4;                           // MFMA steps per chunk
 constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 
+// With 16-token tiles (CTMAX == 1) the B operand is not staged in LDS: every
+// lane loads its own token column's 16 bytes (8 bf16 or 4 fp32 elements) per
+// MFMA step straight from the L2-resident rows -- fp32 x for the up kernel
+// (rounded to bf16 in registers for bf16 weights), the up kernel's rows for
+// the down kernel -- in the same pipelined stream as the weights, so the
+// workgroup never stops for staging.  Wider tiles (N > 16) stage K windows
+// of their token rows in LDS.
+// Waves per SIMD the register allocation must leave room for: three for the
+// up kernel's direct tiles (two weight sets, two B sets, in flight), four
+// for the down kernel's; wide tiles are bounded by their staged LDS anyway.
+template <bool UP, int CTMAX>
+constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
+
 template <bool BF16, bool UP, int CTMAX, bool TILED>
-__global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
+  constexpr bool DIRECT = CTMAX == 1;
+  constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
   using T = WT<BF16>;
   constexpr int SPC = kSpc;
   constexpr int NW = kWavesPerBlock;
@@ -114,14 +130,27 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   const CompactLayout CL{a.E, a.N * a.k};
   const size_t fd = (size_t)a.f * (size_t)a.d;
 
-  // ---- the instance's expert: one dependent load before the weight stream
-  int e = -1, shared_s = -1;
-  if (inst < a.n_routed) {
-    e = a.dedup ? a.cmp[CL.uniq() + inst] : a.idx[inst];
-    if (e < 0 || e >= a.E) return;  // past U (dedup) or an empty slot
+  // ---- the instance's expert: one dependent load before the weight stream.
+  // Instances are ordered shared experts first, then routed ones (u-th
+  // distinct expert, or slot u), so the fixed shared work is dispatched
+  // first and the workgroups of absent dedup instances (u >= U) come last.
+  // The dedup up kernel finds its instance in the routing itself (workgroup
+  // 0 also writes the compaction record for the down kernel and the caller);
+  // the down kernel reads it from that record.
+  int e = -1, shared_s = -1, m = 0;
+  bool have_entries = false;
+  const int u = inst - a.S;
+  if (UP && a.dedup && blockIdx.x == 0)
+    write_record(a.idx, a.N * a.k, a.E, a.cmp_out, a.n_unique, (int *)lds);
+  if (inst < a.S) {
+    shared_s = inst;
+  } else if (UP && a.dedup) {
+    e = local_instance(a.idx, a.N * a.k, a.E, a.k, u, ent_row, ent_tok, &m);
+    if (e < 0) return;  // past U
+    have_entries = true;
   } else {
-    shared_s = inst - a.n_routed;
-    if (shared_s >= a.S) return;
+    e = a.dedup ? a.cmp[CL.uniq() + u] : a.idx[u];
+    if (e < 0 || e >= a.E) return;  // past U (dedup) or an empty slot
   }
   const unsigned char *wA, *wB = nullptr;
   {
@@ -171,15 +200,30 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
       }
     }
   };
+  // DIRECT: this lane's B operand of one chunk (its token column's row at
+  // `bsrc`, NB x 16 bytes per step), same clamping as the weights
+  const unsigned char *bsrc = nullptr;
+  constexpr int BEB = UP ? 4 : EB;  // bytes per B element in memory (x is fp32)
+  auto issue_b = [&](int ch, u32x4 (&db)[SPC][NB]) {
+#pragma unroll
+    for (int s = 0; s < SPC; ++s) {
+      const int step = min(ch * SPC + s, nsteps - 1);
+#pragma unroll
+      for (int h = 0; h < NB; ++h)
+        db[s][h] = ldg16(bsrc + (size_t)step * T::kStep * BEB + h * 16);
+    }
+  };
 
   u32x4 ra1[SPC], ra3[SPC], rb1[SPC], rb3[SPC];
+  u32x4 rab[SPC][NB], rbb[SPC][NB];  // DIRECT B operands of the two chunk sets
   // the first chunk of this wave leaves before the token lists are read
   // (every window holds at least NW chunks, so chunk `wave` is in window 0)
   if (wave < nchunks) issue(wave, ra1, ra3);
 
   // ---- token entries of the instance
-  int m;
-  if (shared_s >= 0) {
+  if (have_entries) {
+    // already placed by local_instance
+  } else if (shared_s >= 0) {
     m = a.N;
     for (int c = tid; c < m; c += kBlock) {
       ent_row[c] = a.N * a.k + shared_s * a.N + c;
@@ -196,16 +240,19 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
   } else {
     m = 1;
     if (tid == 0) {
-      ent_row[0] = inst;
-      ent_tok[0] = inst / a.k;
+      ent_row[0] = u;
+      ent_tok[0] = u / a.k;
     }
   }
+  if (DIRECT) __syncthreads();  // lanes read their columns' entries below
 
   for (int c0 = 0; c0 < m; c0 += GROUP) {
     const int mg = min(m - c0, GROUP);
     const int n_ct = (mg + kTile - 1) / kTile;
-    // K window staged in LDS: a multiple of NW chunks (at least NW)
-    int cpw = ((a.lds_bytes / (mg * EB)) - kLdsPad) / CHUNK / NW * NW;
+    // K window staged in LDS: a multiple of NW chunks (at least NW); DIRECT
+    // stages nothing and takes all of K as one window
+    int cpw = DIRECT ? (nchunks + NW - 1) / NW * NW
+                     : ((a.lds_bytes / (mg * EB)) - kLdsPad) / CHUNK / NW * NW;
     cpw = max(NW, min(cpw, (nchunks + NW - 1) / NW * NW));
     const int KW = cpw * CHUNK;
     const int stride = KW + kLdsPad;  // elements per staged row
@@ -263,7 +310,8 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
 
     // MFMAs of one chunk.  The B fragment of a lane is token column
     // ct*16 + r; columns past the group read a valid row and are zeroed.
-    auto compute = [&](int ch, const u32x4 (&s1)[SPC], const u32x4 (&s3)[SPC]) {
+    auto compute = [&](int ch, const u32x4 (&s1)[SPC], const u32x4 (&s3)[SPC],
+                       const u32x4 (&sb)[SPC][NB]) {
       const int kin = (ch % cpw) * CHUNK;  // offset inside the window
 #pragma unroll
       for (int s = 0; s < SPC; ++s) {
@@ -274,7 +322,22 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
             if (ct == 0 || ct < n_ct) {
               const int col = ct * kTile + r;
               const int row = min(col, mg - 1);
-              u32x4 b = *(const u32x4 *)(lds + ((size_t)row * stride + off) * EB);
+              u32x4 b;
+              if (DIRECT) {
+                if (NB == 2) {
+                  // 8 fp32 of x rounded to bf16 (nearest even), as when staged
+                  const f32x4 lo = __builtin_bit_cast(f32x4, sb[s][0]);
+                  const f32x4 hi = __builtin_bit_cast(f32x4, sb[s][NB - 1]);
+                  bf16x8 v;
+                  v[0] = (__bf16)lo.x; v[1] = (__bf16)lo.y; v[2] = (__bf16)lo.z; v[3] = (__bf16)lo.w;
+                  v[4] = (__bf16)hi.x; v[5] = (__bf16)hi.y; v[6] = (__bf16)hi.z; v[7] = (__bf16)hi.w;
+                  b = __builtin_bit_cast(u32x4, v);
+                } else {
+                  b = sb[s][0];
+                }
+              } else {
+                b = *(const u32x4 *)(lds + ((size_t)row * stride + off) * EB);
+              }
               if (col >= mg) b = u32x4{0u, 0u, 0u, 0u};
               acc1[ct] = T::mma(s1[s], b, acc1[ct]);
               if (UP) acc3[ct] = T::mma(s3[s], b, acc3[ct]);
@@ -284,27 +347,42 @@ __global__ __launch_bounds__(256) void expert_kernel(ExpertArgs a) {
       }
     };
 
+    if (DIRECT) {
+      // this lane's token column: row of the group's entry min(r, mg-1)
+      const int ent = c0 + min(r, mg - 1);
+      if (UP)
+        bsrc = (const unsigned char *)(a.x + (size_t)ent_tok[ent] * K + lane_k);
+      else
+        bsrc = (const unsigned char *)a.abuf + ((size_t)ent_row[ent] * K + lane_k) * EB;
+    }
     for (int w0 = 0; w0 < nchunks; w0 += cpw) {
       const int w1 = min(w0 + cpw, nchunks);
       int c = w0 + wave;  // this wave's chunks: c, c + NW, ... < w1
       if (!(c0 == 0 && w0 == 0) && c < w1) issue(c, ra1, ra3);
-      __syncthreads();  // readers of the previous window are done
-      stage_window(w0 * CHUNK);
-      __syncthreads();
+      if (DIRECT) {
+        if (c < w1) issue_b(c, rab);
+      } else {
+        __syncthreads();  // readers of the previous window are done
+        stage_window(w0 * CHUNK);
+        __syncthreads();
+      }
       if (c < w1) {
         // steady state: two chunks per iteration, next chunk always in flight
         for (; c + 2 * NW < w1; c += 2 * NW) {
           issue(c + NW, rb1, rb3);
-          compute(c, ra1, ra3);
+          if (DIRECT) issue_b(c + NW, rbb);
+          compute(c, ra1, ra3, rab);
           issue(c + 2 * NW, ra1, ra3);
-          compute(c + NW, rb1, rb3);
+          if (DIRECT) issue_b(c + 2 * NW, rab);
+          compute(c + NW, rb1, rb3, rbb);
         }
         if (c + NW < w1) {
           issue(c + NW, rb1, rb3);
-          compute(c, ra1, ra3);
-          compute(c + NW, rb1, rb3);
+          if (DIRECT) issue_b(c + NW, rbb);
+          compute(c, ra1, ra3, rab);
+          compute(c + NW, rb1, rb3, rbb);
         } else {
-          compute(c, ra1, ra3);
+          compute(c, ra1, ra3, rab);
         }
       }
     }
@@ -363,7 +441,6 @@ hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
   const int blocks = (a.n_routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
-  const bool wide = a.N > kTile;
   // allow more than the default 64 KB of dynamic LDS, once per kernel
   static const hipError_t set_wide = hipFuncSetAttribute(
       (const void *)expert_kernel<BF16, UP, 4, TILED>,
@@ -373,7 +450,7 @@ hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (set_wide != hipSuccess) return set_wide;
   if (set_narrow != hipSuccess) return set_narrow;
-  if (wide)
+  if (a.N > kTile)
     hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED>), dim3(blocks), dim3(kBlock),
                        a.lds_bytes, st, a);
   else
@@ -457,9 +534,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-int expert_lds_bytes(int N, int K, bool bf16, bool up) {
+int expert_lds_bytes(int N, int K, bool bf16, bool up, int E) {
   const int eb = bf16 ? 2 : 4;
   const int ctmax = N > kTile ? 4 : 1;
+  // the partial sums of 16-token tiles, or, in workgroup 0 of the up kernel,
+  // the compaction scratch: 2E+1 counts and offsets and one int per slot
+  if (ctmax == 1) {
+    const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * kWave * 16;
+    const size_t record = up ? (size_t)(2 * E + 1 + MOE_MAX_SLOTS) * sizeof(int) : 0;
+    return (int)(partials > record ? partials : record);
+  }
   const int step = bf16 ? 32 : 16;
   const int chunk = kSpc * step;
   const int rows = ctmax * kTile;

@@ -43,6 +43,8 @@ struct ExpertArgs {
   const int32_t *cmp;     // compaction record (dedup) or nullptr
   void *abuf;             // [N*k + S*N][f] SwiGLU outputs, weight element type
   float *obuf;            // [N*k + S*N][d] expert outputs
+  int32_t *cmp_out;       // dedup up kernel: where workgroup 0 writes the record
+  int32_t *n_unique;      // dedup up kernel: U for the caller, or nullptr
   int d, f, E, k, S, N;
   int tiled;              // weight layout: 0 row-major, 1 MOE_LAYOUT_TILED
   int dedup;              // 0: instance i is slot i; 1: instance u is the
@@ -70,11 +72,10 @@ int gate_splits(int d);
 bool route_fused(int N, int d, int E);
 hipError_t launch_gate(const RouteArgs &a, hipStream_t st);
 hipError_t launch_topk(const RouteArgs &a, hipStream_t st);
-hipError_t launch_compact(const int32_t *idx, int N, int k, int E, int32_t *cmp,
-                          int32_t *n_unique, hipStream_t st);
 
-// Expert pass = up kernel, down kernel, combine kernel.  bf16 selects bf16
-// weights, else fp32.
+// Expert pass = up kernel (in the dedup engine it also compacts the
+// routing), down kernel, combine kernel.  bf16 selects bf16 weights, else
+// fp32.
 hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_down(const ExpertArgs &a, bool bf16, hipStream_t st);
 hipError_t launch_combine(const ExpertArgs &a, hipStream_t st);
@@ -82,8 +83,9 @@ hipError_t launch_combine(const ExpertArgs &a, hipStream_t st);
 hipError_t launch_pack(const void *src, void *dst, int R, int K, long long n_mats, bool bf16,
                        hipStream_t st);
 
-// Dynamic LDS for the expert kernels at this token count (activations of up
-// to min(N, 64) tokens staged per window).
-int expert_lds_bytes(int N, int K, bool bf16, bool up);
+// Dynamic LDS for the expert kernels at this token count: the partial sums
+// (16-token tiles, which read their token columns directly), or K windows of
+// up to min(N, 64) staged token rows.
+int expert_lds_bytes(int N, int K, bool bf16, bool up, int E);
 
 }  // namespace moe
