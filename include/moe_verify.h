@@ -191,7 +191,8 @@ enum moe_kernel_kind {
   MOE_K_GATE = 0,    /* gate logits, split over K; when the partial logits of
                         the pass fit 64 KB this launch also does the top-k */
   MOE_K_TOPK = 1,    /* top-k + softmax per token (larger gates only) */
-  MOE_K_COMPACT = 2, /* routing-trace compaction (dedup) */
+  MOE_K_COMPACT = 2, /* reserved: the dedup up kernel compacts the routing
+                        itself, so no launch of this kind is made */
   MOE_K_UP = 3,      /* W1/W3 + SwiGLU over all expert instances */
   MOE_K_DOWN = 4,    /* W2 over all expert instances */
   MOE_K_COMBINE = 5, /* weighted sum in slot order + shared experts */
