@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from speculative_decode_verify_gate_amd import binding as B  # noqa: E402
+from speculative_decode_verify_gate_amd import draftlen  # noqa: E402
 from speculative_decode_verify_gate_amd import stepmodel  # noqa: E402
 from speculative_decode_verify_gate_amd import synth  # noqa: E402
 
@@ -216,6 +217,32 @@ def predict_from_calibration(cfg, calib, n, u_bar):
     r, r_sd = stepmodel.bandwidth_ratio(f_dd, calib["perslot"])
     sav, sav_sd = stepmodel.predicted_saving(calib["perslot"], f_dd, b_ps, u_bar * b_ps)
     return r, r_sd, sav, sav_sd
+
+
+def draft_length_table(sweep, draft_fracs=(0.05, 0.2), alphas=None):
+    """Best draft length per acceptance rate from the measured single-layer
+    verify-pass times t(n) (route + expert pass, medians of the sweep), for
+    each engine and for the faster of the two at every n.  The draft's time
+    per token is a fraction of t(1)."""
+    alphas = alphas or [0.3, 0.5, 0.6, 0.7, 0.8, 0.85, 0.9, 0.95, 0.98]
+    t = {name: {r["n"]: r[name]["us"] + r[name]["route_us"] for r in sweep}
+         for name in ("perslot", "dedup")}
+    t["faster"] = {n: min(t["perslot"][n], t["dedup"][n]) for n in t["perslot"]}
+    gmax = max(t["perslot"]) - 1
+    out = {"model": "best gamma maximises E[k] / (t(gamma+1) + gamma t_draft) over "
+                    f"0..{gmax}; gamma 0 is plain decoding at 1 / t(1); "
+                    "E[k] = (1 - alpha^(gamma+1)) / (1 - alpha)",
+           "alphas": alphas, "by_draft_cost": []}
+    for frac in draft_fracs:
+        td = frac * t["perslot"][1]
+        rec = {"t_draft_over_t1": frac, "t_draft_us": round(td, 2)}
+        for name, tn in t.items():
+            gs = draftlen.staircase(alphas, tn, td, gmax)
+            rec[f"best_gamma_{name}"] = gs
+            rec[f"speedup_{name}"] = [round(draftlen.round_rate(a, g, tn, td) * tn[1], 3)
+                                      for a, g in zip(alphas, gs)]
+        out["by_draft_cost"].append(rec)
+    return out
 
 
 def calibration_json(calib):
@@ -552,6 +579,7 @@ def main():
         ns = [r["n"] for r in sweep]
         out["sweep"] = sweep
         out["calibration"] = calibration_json(calib)
+        out["draft_length"] = draft_length_table(sweep)
         out["crossover"] = {
             "measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in sweep]),
             "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_bar"] < r["r"] for r in sweep]),
