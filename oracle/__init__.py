@@ -1,4 +1,5 @@
-"""CPU oracle for the MoE verify-pass layer -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the MoE verify-pass layer and the verification round --
+TEST INFRASTRUCTURE ONLY.
 
 Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never does, and this
@@ -8,4 +9,5 @@ package imports nothing from it.  The arithmetic lives in ``moe_oracle.cpp``
 from .oracle import (  # noqa: F401
     F32, BF16, FLAG_BOUNDARY, FLAG_ORDER, Shape, load, bf16_rne, gate_logits,
     route, expert, layer, dense_mixture, pass_bytes, compact, expert_bytes,
+    GREEDY, SAMPLING, sample_index, verify_gate,
 )

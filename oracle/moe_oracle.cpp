@@ -383,4 +383,95 @@ int oracle_compact(const oracle_shape *s, const int32_t *idx, int32_t n_tokens,
   return 0;
 }
 
+/* ---- verification round
+ *
+ * Readings (the page's code draws with torch.rand / torch.multinomial; here
+ * the random numbers come in as arguments):
+ *   V1 p and q are the models' distributions after the caller's temperature
+ *      and top-p filtering, the same settings on both sides, as the page
+ *      requires for the ratio to be meaningful;
+ *   V2 a draft token is accepted when u < min(1, p(x) / q(x)) and q(x) > 0;
+ *      u q(x) < p(x) says the same without a division, and the products of
+ *      two fp32 values are exact in fp64;
+ *   V3 sampling from the normalised residual max(0, p - q) is an inverse-CDF
+ *      draw over its quantized weights (oracle_sample_index): normalising is
+ *      the scaling of the target by W;
+ *   V4 a residual that quantizes to zero everywhere (p and q equal to within
+ *      2^-40) draws the correction from p itself;
+ *   V5 greedy mode accepts a draft token when it is the verifier's argmax
+ *      (ties to the lowest index) and emits the verifier's argmax at the
+ *      first mismatch, or at the bonus position. */
+int32_t oracle_sample_index(const float *weights, int32_t V, uint32_t r) {
+  if (!weights || V <= 0) return -1;
+  const double scale = 1099511627776.0; /* 2^40 */
+  uint64_t W = 0;
+  for (int32_t j = 0; j < V; ++j) {
+    const double w = weights[j] > 0.f ? (double)weights[j] : 0.0;
+    W += (uint64_t)std::floor(w * scale);
+  }
+  if (W == 0) return -1;
+  const uint64_t target = (uint64_t)(((unsigned __int128)W * r) >> 32);
+  uint64_t prefix = 0;
+  for (int32_t j = 0; j < V; ++j) {
+    const double w = weights[j] > 0.f ? (double)weights[j] : 0.0;
+    prefix += (uint64_t)std::floor(w * scale);
+    if (prefix > target) return j;
+  }
+  return -1; /* not reached: prefix ends at W > target */
+}
+
+static int32_t argmax_lowest(const float *row, int32_t V) {
+  int32_t best = 0;
+  for (int32_t j = 1; j < V; ++j)
+    if (row[j] > row[best]) best = j;
+  return best;
+}
+
+int oracle_verify_gate(int32_t gamma, int32_t V, int32_t mode, const float *p, const float *q,
+                       const int32_t *x, const float *u, uint32_t r, int32_t *n_acc,
+                       int32_t *tokens) {
+  if (gamma < 0 || V <= 0 || !p || !n_acc || !tokens || (gamma > 0 && !x)) return -1;
+  if (mode != 0 && mode != 1) return -1;
+  if (mode == 1 && gamma > 0 && (!q || !u)) return -1;
+  for (int32_t i = 0; i < gamma; ++i)
+    if (x[i] < 0 || x[i] >= V) return -1;
+  for (int32_t i = 0; i <= gamma; ++i) tokens[i] = -1;
+  std::vector<float> residual((size_t)V);
+  for (int32_t i = 0; i < gamma; ++i) {
+    const float *pi = p + (size_t)i * V;
+    bool accept;
+    if (mode == 0) {
+      accept = argmax_lowest(pi, V) == x[i]; /* V5 */
+    } else {
+      const float *qi = q + (size_t)i * V;
+      const double pv = pi[x[i]], qv = qi[x[i]];
+      accept = qv > 0.0 && (double)u[i] * qv < pv; /* V2 */
+    }
+    if (accept) {
+      tokens[i] = x[i];
+      continue;
+    }
+    /* first rejection: the round ends with the verifier's own token */
+    *n_acc = i;
+    if (mode == 0) {
+      tokens[i] = argmax_lowest(pi, V);
+      return 0;
+    }
+    const float *qi = q + (size_t)i * V;
+    for (int32_t j = 0; j < V; ++j) {
+      const float d = pi[j] - qi[j];
+      residual[j] = d > 0.f ? d : 0.f; /* max(0, p - q) */
+    }
+    int32_t c = oracle_sample_index(residual.data(), V, r); /* V3 */
+    if (c < 0) c = oracle_sample_index(pi, V, r);           /* V4 */
+    tokens[i] = c;
+    return 0;
+  }
+  /* every draft token survived: the bonus token from the last position */
+  *n_acc = gamma;
+  const float *pb = p + (size_t)gamma * V;
+  tokens[gamma] = mode == 0 ? argmax_lowest(pb, V) : oracle_sample_index(pb, V, r);
+  return 0;
+}
+
 }  // extern "C"

@@ -110,6 +110,31 @@ int oracle_compact(const oracle_shape *s, const int32_t *idx, int32_t n_tokens,
                    int32_t *counts, int32_t *offs, int32_t *list, int32_t *uniq,
                    int32_t *n_unique);
 
+/* ---- speculative-decoding verification round ("Building a Terminal Based
+ * LLM Inference Internals Explorer - Part 3: Speculative Decoding", sections
+ * "The Accept/Reject Mechanism", "A Worked Example" and "Sampling vs
+ * Greedy").
+ *
+ * Inverse-CDF sampler: weights w_j >= 0 are quantized to integers
+ * floor(w_j * 2^40); with W their sum and r a uniform 32-bit integer, the
+ * sample is the smallest index c whose inclusive prefix sum exceeds
+ * floor(W r / 2^32).  Returns -1 when W == 0. */
+int32_t oracle_sample_index(const float *weights, int32_t V, uint32_t r);
+
+/* One round for one sequence.
+ *   p      [gamma+1][V] verifier distributions (row gamma: the bonus position)
+ *   q      [gamma][V]   draft distributions (sampling mode; NULL for greedy)
+ *   x      [gamma]      draft tokens
+ *   u      [gamma]      uniforms in [0, 1) for the accept tests (sampling)
+ *   r                   32-bit uniform for the correction / bonus sample
+ *   mode               0 greedy, 1 sampling
+ * Outputs *n_acc (accepted draft tokens, 0..gamma) and tokens [gamma+1]: the
+ * accepted prefix, then the correction (first rejection) or bonus token, then
+ * -1.  Returns 0, or -1 on bad arguments. */
+int oracle_verify_gate(int32_t gamma, int32_t V, int32_t mode, const float *p, const float *q,
+                       const int32_t *x, const float *u, uint32_t r, int32_t *n_acc,
+                       int32_t *tokens);
+
 #ifdef __cplusplus
 }
 #endif

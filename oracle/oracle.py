@@ -62,6 +62,9 @@ def load():
         lib.oracle_dense_mixture.argtypes = [P, P, P, P, i32, P]
         lib.oracle_pass_bytes.argtypes = [P, P, i32, P, P, P, P]
         lib.oracle_compact.argtypes = [P, P, i32, P, P, P, P, P]
+        lib.oracle_sample_index.argtypes = [P, i32, C.c_uint32]
+        lib.oracle_sample_index.restype = i32
+        lib.oracle_verify_gate.argtypes = [i32, i32, i32, P, P, P, P, C.c_uint32, P, P]
         for fn in ("oracle_gate_logits", "oracle_route", "oracle_expert", "oracle_layer",
                    "oracle_dense_mixture", "oracle_pass_bytes", "oracle_compact"):
             getattr(lib, fn).restype = C.c_int
@@ -211,3 +214,34 @@ def compact(shape: Shape, idx):
                               _p(uniq), _p(u)), "oracle_compact")
     U = int(u[0])
     return dict(counts=counts, offs=offs, list=lst, uniq=uniq[:U].copy(), n_unique=U)
+
+
+GREEDY = 0
+SAMPLING = 1
+
+
+def sample_index(weights, r):
+    """Inverse-CDF index over floor(w * 2^40) weights with 32-bit uniform r
+    (-1 if every weight quantizes to zero)."""
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    return int(load().oracle_sample_index(w.ctypes.data, w.size, int(r) & 0xFFFFFFFF))
+
+
+def verify_gate(p, x, *, q=None, u=None, r=0, mode=SAMPLING):
+    """One verification round for one sequence: p [gamma+1][V], q [gamma][V],
+    x [gamma], u [gamma], r uint32.  Returns (n_accepted, tokens [gamma+1])."""
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    gamma = p.shape[0] - 1
+    V = p.shape[1]
+    x = np.ascontiguousarray(x, dtype=np.int32).reshape(gamma)
+    qa = None if q is None else np.ascontiguousarray(q, dtype=np.float32)
+    ua = None if u is None else np.ascontiguousarray(u, dtype=np.float32).reshape(gamma)
+    n = np.zeros(1, np.int32)
+    t = np.zeros(gamma + 1, np.int32)
+    rc = load().oracle_verify_gate(gamma, V, mode, p.ctypes.data,
+                                   None if qa is None else qa.ctypes.data, x.ctypes.data,
+                                   None if ua is None else ua.ctypes.data,
+                                   int(r) & 0xFFFFFFFF, n.ctypes.data, t.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_verify_gate: bad arguments")
+    return int(n[0]), t

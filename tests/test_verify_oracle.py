@@ -1,0 +1,117 @@
+"""Pins of the CPU oracle's speculative-decoding verification round (CPU
+only).  The round follows "Building a Terminal Based LLM Inference
+Internals Explorer - Part 3: Speculative Decoding", sections "The
+Accept/Reject Mechanism", "A Worked Example" and "Sampling vs Greedy"."""
+import numpy as np
+import pytest
+
+import oracle as O
+
+CAT, DOG, FOX = 0, 1, 2
+
+
+def _f32(v):
+    return np.asarray(v, dtype=np.float32)
+
+
+def test_worked_example_accept_probability():
+    # p_draft(cat) = 0.6, p_verify(cat) = 0.3: cat survives a 50% coin flip
+    p = _f32([[0.3, 0.5, 0.2], [0.2, 0.3, 0.5]])
+    q = _f32([[0.6, 0.3, 0.1]])
+    n, t = O.verify_gate(p, [CAT], q=q, u=[0.4999], r=0)
+    assert n == 1 and t[0] == CAT
+    n, t = O.verify_gate(p, [CAT], q=q, u=[0.5], r=0)
+    assert n == 0 and t[1] == -1
+
+
+def test_worked_example_residual_draw():
+    # residual {cat: 0, dog: 0.2, fox: 0.1}, normalised {0, 0.67, 0.33}: cat
+    # can never be the correction; dog below two thirds of the draw range
+    p = _f32([[0.3, 0.5, 0.2], [0.2, 0.3, 0.5]])
+    q = _f32([[0.6, 0.3, 0.1]])
+    res = np.maximum(p[0] - q[0], 0).astype(np.float32)
+    np.testing.assert_allclose(res / res.sum(), [0.0, 2 / 3, 1 / 3], atol=1e-6)
+    seen = set()
+    for r in np.linspace(0, 2**32 - 1, 301).astype(np.uint64):
+        n, t = O.verify_gate(p, [CAT], q=q, u=[0.9], r=int(r))
+        assert n == 0
+        seen.add(int(t[0]))
+        assert t[0] == (DOG if r < (2 / 3) * 2**32 - 2**12 else t[0])
+        assert t[0] == (FOX if r > (2 / 3) * 2**32 + 2**12 else t[0])
+    assert seen == {DOG, FOX}
+
+
+def _searchsorted_sample(w, r):
+    q = np.floor(w.astype(np.float64) * 2.0**40).astype(np.uint64)
+    W = int(q.sum(dtype=np.uint64))
+    if W == 0:
+        return -1
+    target = (W * int(r)) >> 32
+    cum = np.cumsum(q, dtype=np.uint64)
+    return int(np.searchsorted(cum, np.uint64(target), side="right"))
+
+
+def test_sampler_matches_searchsorted():
+    rng = np.random.default_rng(3)
+    for V in (1, 2, 7, 1000, 50_000):
+        w = rng.random(V).astype(np.float32)
+        w[rng.random(V) < 0.3] = 0.0
+        w /= max(w.sum(), 1e-30)
+        for r in list(rng.integers(0, 2**32, 20)) + [0, 2**32 - 1]:
+            assert O.sample_index(w, r) == _searchsorted_sample(w, r)
+    assert O.sample_index(_f32([0, 0, 0]), 123) == -1
+    assert O.sample_index(_f32([0, 1e-13, 0]), 123) == -1  # below 2^-40
+    assert O.sample_index(_f32([0, 0, 1]), 0) == 2
+
+
+def test_accept_plus_resample_reproduces_the_verifier_distribution():
+    # drawing x ~ q, accepting with min(1, p/q) and otherwise drawing from
+    # the normalised residual yields exactly p
+    rng = np.random.default_rng(11)
+    V = 6
+    p = rng.dirichlet(np.ones(V)).astype(np.float32)
+    q = rng.dirichlet(np.ones(V)).astype(np.float32)
+    P = np.stack([p, rng.dirichlet(np.ones(V)).astype(np.float32)])
+    trials = 60_000
+    xs = rng.choice(V, size=trials, p=q.astype(np.float64) / q.sum())
+    us = rng.random(trials).astype(np.float32)
+    rs = rng.integers(0, 2**32, trials)
+    counts = np.zeros(V)
+    for x, u, r in zip(xs, us, rs):
+        _, t = O.verify_gate(P, [x], q=q[None, :], u=[u], r=int(r))
+        counts[t[0]] += 1
+    freq = counts / trials
+    sd = np.sqrt(p * (1 - p) / trials)
+    assert np.all(np.abs(freq - p) < 5 * sd + 1e-6), (freq, p)
+
+
+def test_greedy_round():
+    p = _f32([[0.1, 0.7, 0.2], [0.5, 0.2, 0.3], [0.2, 0.2, 0.6]])
+    n, t = O.verify_gate(p, [1, 0], mode=O.GREEDY)
+    assert n == 2 and list(t) == [1, 0, 2]        # all accepted, bonus argmax
+    n, t = O.verify_gate(p, [1, 2], mode=O.GREEDY)
+    assert n == 1 and list(t) == [1, 0, -1]       # mismatch: verifier's argmax
+    n, t = O.verify_gate(_f32([[0.4, 0.4, 0.2], [0.1, 0.1, 0.8]]), [1], mode=O.GREEDY)
+    assert n == 0 and list(t) == [0, -1]          # tie goes to the lower index
+
+
+def test_zero_draft_probability_rejects_and_zero_residual_falls_back():
+    p = _f32([[0.25, 0.25, 0.5], [1, 0, 0]])
+    q = _f32([[0.25, 0.25, 0.5]])
+    # q(x) = p(x): always accepted, whatever u
+    n, _ = O.verify_gate(p, [2], q=q, u=[0.999], r=0)
+    assert n == 1
+    # q(x) = 0 is never accepted; with q = p elsewhere too the residual is
+    # zero, so the correction is drawn from p
+    q0 = _f32([[0.25, 0.75, 0.0]])
+    p0 = _f32([[0.25, 0.75, 0.0], [1, 0, 0]])
+    n, t = O.verify_gate(p0, [2], q=q0, u=[0.0], r=2**31)
+    assert n == 0 and t[0] == O.sample_index(p0[0], 2**31) == 1
+
+
+def test_rejects_bad_arguments():
+    p = _f32([[0.5, 0.5], [0.5, 0.5]])
+    with pytest.raises(ValueError):
+        O.verify_gate(p, [2], q=p[:1], u=[0.1])      # token outside the vocabulary
+    with pytest.raises(ValueError):
+        O.verify_gate(p, [0], q=None, u=[0.1])       # sampling needs q
