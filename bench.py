@@ -245,6 +245,50 @@ def draft_length_table(sweep, draft_fracs=(0.05, 0.2), alphas=None):
     return out
 
 
+def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200):
+    """The verification round after the verify pass: µs per call for n_seq
+    sequences with gamma drafted tokens, per mode, on seeded synthetic
+    distributions.  Bytes counted: greedy reads every row of p (n_seq
+    (gamma+1) V fp32); sampling reads the row it draws from twice over the
+    vocabulary, p and q at the first rejection (2 n_seq V fp32) -- the
+    acceptance tests' scalars are not counted."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    out = []
+    for V in vocabs:
+        logits = torch.randn((n_seq, gamma + 1, V), generator=g, device="cuda") * 3.0
+        p = torch.softmax(logits, dim=-1).contiguous()
+        q = torch.softmax(logits[:, :gamma] + 0.5 * torch.randn(
+            (n_seq, gamma, V), generator=g, device="cuda"), dim=-1).contiguous()
+        x = torch.multinomial(q.reshape(-1, V), 1, generator=g).reshape(n_seq, gamma)
+        x = x.to(torch.int32).contiguous()
+        u = torch.rand((n_seq, gamma), generator=g, device="cuda")
+        r = torch.randint(-2**31, 2**31 - 1, (n_seq,), generator=g, device="cuda",
+                          dtype=torch.int32)
+        rec = {"vocab": V, "n_seq": n_seq, "gamma": gamma}
+        for mode, name in ((B.VERIFY_GREEDY, "greedy"), (B.VERIFY_SAMPLING, "sampling")):
+            ws = B.Workspace()
+            for _ in range(10):
+                B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, ws=ws)
+            torch.cuda.synchronize()
+            evs = []
+            hold_gpu(0.1 * reps)
+            for _ in range(reps):
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record()
+                B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, ws=ws)
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            nbytes = (n_seq * (gamma + 1) * V * 4) if name == "greedy" else (2 * n_seq * V * 4)
+            rec[f"{name}_us"] = round(us, 2)
+            rec[f"{name}_GBs"] = round(nbytes / us / 1e3, 1)
+        out.append(rec)
+        log(f"  verify gate V={V}: greedy {rec['greedy_us']} us, sampling {rec['sampling_us']} us")
+    return out
+
+
 def calibration_json(calib):
     return {"model": "t_us = bytes / BW + t0 (routed expert bytes; shared experts and "
                      "gate in t0)",
@@ -429,6 +473,9 @@ def main():
     ap.add_argument("--reps", type=int, default=48, help="passes per n in the sweep")
     ap.add_argument("--calib-reps", type=int, default=16,
                     help="passes per (n, U) point of the dedup calibration")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="only time the verification round (moe_verify_gate) and print "
+                         "its JSON")
     ap.add_argument("--rho-sweep", action="store_true",
                     help="instead of the bench line: the routing-overlap sweep over the "
                          "26-layer V2-Lite stack (one JSON document)")
@@ -462,6 +509,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "launches": 5,
                           "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}))
+        return
+
+    if args.verify_only:
+        print(json.dumps({"verify_gate": verify_gate_leg()}), flush=True)
         return
 
     cfg = synth.CONFIGS["v2stack" if args.rho_sweep else args.config]
@@ -585,6 +636,9 @@ def main():
             "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_bar"] < r["r"] for r in sweep]),
             "predicted_model_saving_gt_0": stepmodel.first_n(
                 ns, [r["predicted_saving_us"] > 0 for r in sweep])}
+    if not args.no_sweep:
+        log("[bench] verification round")
+        out["verify_gate"] = verify_gate_leg()
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
         del layers

@@ -70,6 +70,13 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 #define MOE_MAX_SLOTS 512
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_SHARED 4
+#define MOE_MAX_SEQ 64     /* sequences per verification-round call */
+#define MOE_MAX_DRAFT 63   /* drafted tokens per sequence and round */
+#define MOE_MAX_VOCAB (1 << 24)
+
+/* Verification-round modes (moe_verify_gate). */
+#define MOE_VERIFY_GREEDY 0
+#define MOE_VERIFY_SAMPLING 1
 
 typedef struct moe_shape {
   int32_t d_model;   /* d: hidden width */
@@ -178,6 +185,43 @@ int moe_pass_bytes(const moe_shape *shape, const int32_t *topk_idx_host, int32_t
                    uint64_t *perslot_bytes, uint64_t *dedup_bytes, uint64_t *shared_bytes,
                    int32_t *n_unique);
 
+/* One speculative-decoding verification round for each of n_seq sequences
+ * ("Building a Terminal Based LLM Inference Internals Explorer - Part 3:
+ * Speculative Decoding", sections "The Accept/Reject Mechanism", "A Worked
+ * Example" and "Sampling vs Greedy"): the step after the verify pass.
+ *   p_verify     [n_seq][gamma+1][V] fp32 device: the verifier's
+ *                distributions at the gamma drafted positions and at the
+ *                bonus position, after the caller's temperature / top-p
+ *                filtering (the same filtering as the draft's)
+ *   q_draft      [n_seq][gamma][V] fp32 device: the draft's full
+ *                distributions (sampling; ignored and may be NULL for greedy)
+ *   draft_tokens [n_seq][gamma] int32 device, each in [0, V)
+ *   u_accept     [n_seq][gamma] fp32 device uniforms in [0, 1) (sampling)
+ *   r_sample     [n_seq] uint32 device uniforms (sampling)
+ *   n_accepted   [n_seq] int32 device output: drafted tokens kept (0..gamma)
+ *   out_tokens   [n_seq][gamma+1] int32 device output: the kept drafts, then
+ *                the verifier's correction (first rejection) or bonus token,
+ *                then -1
+ * Sampling keeps draft token i when q_i(x_i) > 0 and u_i q_i(x_i) < p_i(x_i)
+ * (u_i < min(1, p/q)); at the first rejection it draws from max(0, p_i - q_i)
+ * normalised, after a fully kept round from p at the bonus position.  A draw
+ * is an inverse CDF over integer weights floor(w * 2^40): the smallest index
+ * whose inclusive prefix sum exceeds floor(W r / 2^32), W the weight total;
+ * a residual that is zero at that precision draws from p_i instead.  Greedy
+ * keeps a draft token when it is the verifier's argmax (ties to the lowest
+ * index) and ends with the verifier's argmax.  Results are deterministic and
+ * exact (no dependence on summation order).
+ * Limits: 1 <= n_seq <= MOE_MAX_SEQ, 0 <= gamma <= MOE_MAX_DRAFT,
+ * 1 <= V <= MOE_MAX_VOCAB.  A draft token outside [0, V) cannot be checked
+ * on the host; the device treats it as rejected (never read).  Workspace as
+ * for the other calls; its
+ * first 256 bytes must be zero before its first use, and every call leaves
+ * them zero. */
+int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
+                    const float *p_verify, const float *q_draft, const int32_t *draft_tokens,
+                    const float *u_accept, const uint32_t *r_sample, int32_t *n_accepted,
+                    int32_t *out_tokens, void *workspace, size_t *workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_string(int status);
 
@@ -196,7 +240,8 @@ enum moe_kernel_kind {
   MOE_K_UP = 3,      /* W1/W3 + SwiGLU over all expert instances */
   MOE_K_DOWN = 4,    /* W2 over all expert instances */
   MOE_K_COMBINE = 5, /* weighted sum in slot order + shared experts */
-  MOE_K_COUNT = 6
+  MOE_K_VERIFY = 6,  /* verification round (moe_verify_gate) */
+  MOE_K_COUNT = 7
 };
 /* mask: bit (1 << kind) selects a kernel kind; 0 disables timing.  Not
  * meant for concurrent use from several host threads. */

@@ -15,7 +15,9 @@ LIB_PATH = os.environ.get("MOE_VERIFY_LIB") or os.path.join(_HERE, "libmoeverify
 
 MOE_F32, MOE_BF16 = 0, 1
 MAX_TOKENS, MAX_TOPK, MAX_SLOTS, MAX_EXPERTS, MAX_SHARED = 64, 16, 512, 256, 4
-KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine")
+KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine", "verify")
+VERIFY_GREEDY, VERIFY_SAMPLING = 0, 1
+MAX_SEQ, MAX_DRAFT, MAX_VOCAB = 64, 63, 1 << 24
 
 _lib = None
 
@@ -58,8 +60,10 @@ def load():
     lib.moe_status_string.restype = C.c_char_p
     lib.moe_timing_enable.argtypes = [C.c_int]
     lib.moe_timing_read.argtypes = [P, P]
+    lib.moe_verify_gate.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
     for fn in ("moe_route", "moe_expert_pass_perslot", "moe_expert_pass_dedup",
-               "moe_pass_bytes", "moe_pack_weights", "moe_timing_enable", "moe_timing_read"):
+               "moe_pass_bytes", "moe_pack_weights", "moe_timing_enable", "moe_timing_read",
+               "moe_verify_gate"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -233,6 +237,48 @@ def pass_bytes(shape, idx_host):
                                                 C.c_void_p(base + 8), C.c_void_p(base + 16),
                                                 C.byref(u)))
     return int(out[0]), int(out[1]), int(out[2]), int(u.value)
+
+
+def verify_gate(p, x, *, q=None, u=None, r=None, mode=VERIFY_SAMPLING, n_accepted=None,
+                out=None, ws=None):
+    """One verification round per sequence.  p fp32 [S][gamma+1][V], x int32
+    [S][gamma], q fp32 [S][gamma][V], u fp32 [S][gamma], r int32 [S] holding
+    uint32 bit patterns (sampling).  Returns (n_accepted int32 [S], tokens
+    int32 [S][gamma+1])."""
+    lib = load()
+    p = _dev(p, torch.float32, "p")
+    S, G1, V = p.shape
+    gamma = G1 - 1
+    x = _dev(x, torch.int32, "x")
+    if tuple(x.shape) != (S, gamma):
+        raise ValueError(f"x must be [{S}][{gamma}]")
+    if mode == VERIFY_SAMPLING:
+        q, u, r = _dev(q, torch.float32, "q"), _dev(u, torch.float32, "u"), _dev(r, torch.int32, "r")
+        if q is None or u is None or r is None:
+            raise ValueError("sampling needs q, u and r")
+        if tuple(q.shape) != (S, gamma, V) or tuple(u.shape) != (S, gamma) or tuple(r.shape) != (S,):
+            raise ValueError("q, u, r have the wrong shapes")
+    else:
+        q = u = r = None
+    if n_accepted is None:
+        n_accepted = torch.empty((S,), dtype=torch.int32, device=p.device)
+    if out is None:
+        out = torch.empty((S, gamma + 1), dtype=torch.int32, device=p.device)
+    _dev(n_accepted, torch.int32, "n_accepted"), _dev(out, torch.int32, "out")
+    key = ("verify", S, gamma, V)
+    if key not in _NEED:
+        nb = C.c_size_t(0)
+        _check("moe_verify_gate", lib.moe_verify_gate(S, gamma, V, mode, _ptr(p), _ptr(q), _ptr(x),
+                                                      _ptr(u), _ptr(r), _ptr(n_accepted),
+                                                      _ptr(out), None, C.byref(nb), None))
+        _NEED[key] = nb.value
+    ws = ws or Workspace(p.device)
+    buf = ws.get(_NEED[key])
+    have = C.c_size_t(buf.numel())
+    _check("moe_verify_gate", lib.moe_verify_gate(S, gamma, V, mode, _ptr(p), _ptr(q), _ptr(x),
+                                                  _ptr(u), _ptr(r), _ptr(n_accepted), _ptr(out),
+                                                  _ptr(buf), C.byref(have), _stream()))
+    return n_accepted, out
 
 
 def timing_enable(kinds=KERNEL_KINDS):

@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "verify.h"
 #include "moe_verify.h"
 
 namespace {
@@ -224,6 +225,34 @@ int moe_route(const moe_shape *s, const float *gate_w, const float *x, int32_t n
   hipError_t err = timed(MOE_K_GATE, st, [&] { return moe::launch_gate(a, st); });
   if (err == hipSuccess && !moe::route_fused(n, s->d_model, s->n_experts))
     err = timed(MOE_K_TOPK, st, [&] { return moe::launch_topk(a, st); });
+  return status_of(err);
+}
+
+int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
+                    const float *p_verify, const float *q_draft, const int32_t *draft_tokens,
+                    const float *u_accept, const uint32_t *r_sample, int32_t *n_accepted,
+                    int32_t *out_tokens, void *ws, size_t *ws_bytes, void *stream) {
+  if (n_seq < 1 || n_seq > MOE_MAX_SEQ || gamma < 0 || gamma > MOE_MAX_DRAFT || vocab < 1 ||
+      vocab > MOE_MAX_VOCAB)
+    return MOE_ERR_INVALID_ARG;
+  if (mode != MOE_VERIFY_GREEDY && mode != MOE_VERIFY_SAMPLING) return MOE_ERR_INVALID_ARG;
+  if (!p_verify || !n_accepted || !out_tokens || (gamma > 0 && !draft_tokens))
+    return MOE_ERR_INVALID_ARG;
+  if (mode == MOE_VERIFY_SAMPLING && (!r_sample || (gamma > 0 && (!q_draft || !u_accept))))
+    return MOE_ERR_INVALID_ARG;
+  // [arrival counters | partial results [n_seq][chunks][gamma + 1] uint64]
+  const size_t need = kAlign + align_up((size_t)n_seq * moe::verify_chunks(vocab) *
+                                            (size_t)(gamma + 1) * sizeof(uint64_t),
+                                        kAlign);
+  bool launch;
+  int rc;
+  if ((rc = workspace_gate(ws, ws_bytes, need, &launch)) != MOE_OK || !launch) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t err = timed(MOE_K_VERIFY, st, [&] {
+    return moe::launch_verify(n_seq, gamma, vocab, mode, p_verify,
+                              mode == MOE_VERIFY_SAMPLING ? q_draft : nullptr, draft_tokens,
+                              u_accept, r_sample, n_accepted, out_tokens, ws, st);
+  });
   return status_of(err);
 }
 

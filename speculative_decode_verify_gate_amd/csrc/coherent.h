@@ -21,6 +21,14 @@ __device__ inline float load_coherent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ inline void store_coherent64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint64_t load_coherent64(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait until this thread's earlier stores have completed (vmcnt(0)).  The
 // signal fence keeps the compiler from moving memory operations across it.
 __device__ inline void wait_stores() {

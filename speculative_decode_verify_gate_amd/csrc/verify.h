@@ -1,0 +1,18 @@
+// verify.h -- launch interface of the verification round (verify.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Vocabulary chunks of one verification round (2048 entries each).
+int verify_chunks(int V);
+
+// Workspace: 256 bytes of arrival counters (zero before first use, left
+// zero) + n_seq * chunks * (gamma + 1) uint64 partial results.
+hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, const float *q,
+                         const int32_t *x, const float *u, const uint32_t *r, int32_t *n_acc,
+                         int32_t *out, void *ws, hipStream_t st);
+
+}  // namespace moe

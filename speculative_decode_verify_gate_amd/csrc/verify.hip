@@ -1,0 +1,408 @@
+// verify.hip -- one speculative-decoding verification round per sequence on
+// gfx950: accept/reject of the drafted tokens against the verifier's
+// distributions, then the verifier's correction or bonus token.
+//
+// "Building a Terminal Based LLM Inference Internals Explorer - Part 3:
+// Speculative Decoding", sections "The Accept/Reject Mechanism", "A Worked
+// Example" and "Sampling vs Greedy":
+//   sampling: draft token i is kept when u_i < min(1, p_i(x_i) / q_i(x_i))
+//             (and q_i(x_i) > 0); at the first rejection the round ends with a
+//             draw from max(0, p_i - q_i) normalised; if every draft token is
+//             kept, a bonus token is drawn from p at position gamma;
+//   greedy:   a draft token is kept when it is the verifier's argmax; the
+//             round ends with the verifier's argmax at the first mismatch,
+//             or at the bonus position.
+// The random numbers are inputs.  Every decision is exact: u q(x) < p(x) in
+// fp64 (products of two fp32 values are exact there), and the draw is an
+// inverse CDF over integer weights floor(w * 2^40) with target
+// floor(W r / 2^32), so sums do not depend on their order.
+//
+// Layout of the work: a workgroup takes a 2048-entry chunk of the vocabulary
+// of one sequence (coalesced loads, 256 threads x 8).  Sampling: each
+// workgroup finds the first rejection itself (2 gamma scalar loads) and
+// writes the integer weight sum of its chunk of the row to draw from.
+// Greedy: a workgroup per (position, chunk) writes the chunk's argmax as one
+// 64-bit key (value bits above the complemented index, so the largest key is
+// the largest value at the lowest index).  The last workgroup of a sequence
+// to finish (arrival counter in the workspace) finishes the round: the
+// argmax decisions (all keys loaded at once, LDS 64-bit max per position),
+// or the chunk holding the draw target and, inside it, the entry, by
+// block-wide integer prefix sums.
+#include <stdint.h>
+
+#include "coherent.h"
+#include "kernels.h"
+#include "verify.h"
+
+namespace moe {
+namespace {
+
+constexpr int kVThreads = 256;
+constexpr int kVPer = 8;                       // entries per thread per row
+constexpr int kVChunk = kVThreads * kVPer;     // 2048
+constexpr double kQuant = 1099511627776.0;     // 2^40
+constexpr int kUnitsGreedy = 8;                // units per workgroup, at most
+constexpr int kUnitsSampling = 4;
+constexpr int kWavesV = kVThreads / 64;
+
+__device__ inline uint64_t quantize(float w) {
+  return w > 0.f ? (uint64_t)((double)w * kQuant) : 0ull;
+}
+
+// Key of value v at index j: larger value first, then lower index.
+__device__ inline uint64_t argmax_key(float v, int j) {
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // order-preserving
+  return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+__device__ inline int key_index(uint64_t k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+__device__ inline uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline uint64_t shfl_up64(uint64_t v, int d) {
+  const uint32_t lo = __shfl_up((uint32_t)v, d, 64);
+  const uint32_t hi = __shfl_up((uint32_t)(v >> 32), d, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Block-wide sum / max of one uint64 per thread (all threads get it).
+template <bool MAX>
+__device__ inline uint64_t block_reduce(uint64_t v, uint64_t *scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor64(v, m);
+    v = MAX ? (o > v ? o : v) : v + o;
+  }
+  __syncthreads();
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  uint64_t r = scratch[0];
+  for (int w = 1; w < kVThreads / 64; ++w) r = MAX ? (scratch[w] > r ? scratch[w] : r) : r + scratch[w];
+  return r;
+}
+
+// Inclusive block-wide prefix sum of one uint64 per thread (in thread
+// order); *total receives the block sum.
+__device__ inline uint64_t block_scan(uint64_t v, uint64_t *scratch, uint64_t *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = shfl_up64(v, d);
+    if (lane >= d) v += o;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[wave] = v;
+  __syncthreads();
+  uint64_t before = 0, all = 0;
+  for (int w = 0; w < kVThreads / 64; ++w) {
+    if (w < wave) before += scratch[w];
+    all += scratch[w];
+  }
+  *total = all;
+  return v + before;
+}
+
+// NU block-wide sums / maxima at once, one barrier: thread u < NU gets
+// result u (others get 0).
+template <bool MAX, int NU>
+__device__ inline uint64_t block_reduce_many(const uint64_t (&v)[NU], uint64_t (*scratch)[kWavesV]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    uint64_t x = v[u];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint64_t o = shfl_xor64(x, m);
+      x = MAX ? (o > x ? o : x) : x + o;
+    }
+    if (lane == 0) scratch[u][wave] = x;
+  }
+  __syncthreads();
+  uint64_t r = 0;
+  if ((int)threadIdx.x < NU) {
+    r = scratch[threadIdx.x][0];
+    for (int w = 1; w < kWavesV; ++w) {
+      const uint64_t y = scratch[threadIdx.x][w];
+      r = MAX ? (y > r ? y : r) : r + y;
+    }
+  }
+  return r;
+}
+
+struct VerifyArgs {
+  int n_seq, gamma, V, mode, chunks;
+  int upb;         // units (chunk, or position x chunk) per workgroup
+  const float *p, *q, *u;
+  const int32_t *x;
+  const uint32_t *r;
+  int32_t *n_acc, *out;
+  unsigned *done;  // [n_seq] arrival counters: zero on entry and exit
+  uint64_t *part;  // [n_seq][gamma + 1][chunks] (sampling: [n_seq][chunks])
+};
+
+// First rejected draft position of sequence s in sampling mode (gamma if
+// none); every thread gets it.
+__device__ inline int first_rejection(const VerifyArgs &a, int s, int *sh) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    bool reject = false;
+    if (tid < a.gamma) {
+      const int i = tid;
+      const int x = a.x[s * a.gamma + i];
+      reject = true;  // a token outside the vocabulary is rejected unread
+      if (x >= 0 && x < a.V) {
+        const size_t row = ((size_t)s * (a.gamma + 1) + i) * a.V;
+        const size_t qrow = ((size_t)s * a.gamma + i) * a.V;
+        const double pv = a.p[row + x], qv = a.q[qrow + x];
+        const double u = a.u[s * a.gamma + i];
+        reject = !(qv > 0.0 && u * qv < pv);
+      }
+    }
+    const uint64_t m = __ballot(reject);
+    if (tid == 0) *sh = m ? __ffsll((unsigned long long)m) - 1 : a.gamma;
+  }
+  __syncthreads();
+  return *sh;
+}
+
+// Weight of vocabulary entry j of the row the sampling draw uses: the
+// residual at a rejection, the bonus distribution otherwise, or (fallback,
+// residual quantized to zero) the verifier distribution itself.
+__device__ inline uint64_t draw_weight(const VerifyArgs &a, int s, int istar, bool fallback,
+                                       int j) {
+  const float pv = a.p[((size_t)s * (a.gamma + 1) + istar) * a.V + j];
+  if (istar == a.gamma || fallback) return quantize(pv);
+  const float qv = a.q[((size_t)s * a.gamma + istar) * a.V + j];
+  const float d = pv - qv;
+  return quantize(d > 0.f ? d : 0.f);
+}
+
+__global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
+  const int s = blockIdx.y, tid = threadIdx.x;
+  const int G = a.gamma;
+  const bool sampling = a.mode == MOE_VERIFY_SAMPLING;
+  // a workgroup takes upb consecutive units: chunks (sampling) or
+  // (position, chunk) pairs in position-major order (greedy)
+  const int units = sampling ? a.chunks : a.chunks * (G + 1);
+  const int u0 = blockIdx.x * a.upb;
+  const unsigned arrivals = gridDim.x;
+  __shared__ uint64_t scratch[kWavesV];
+  __shared__ uint64_t many[kUnitsGreedy][kWavesV];
+  __shared__ int sh_i;
+  __shared__ int sh_last;
+  __shared__ int xs[MOE_MAX_DRAFT + 1];  // this sequence's draft tokens
+  // loaded now, used only by the workgroup that finishes the round
+  if (tid < G) xs[tid] = a.x[s * G + tid];
+  const uint64_t rr = sampling ? (uint64_t)a.r[s] : 0ull;
+  int istar = G;
+
+  // ---- this workgroup's partial results (all loads issued before any use)
+  if (sampling) {
+    istar = first_rejection(a, s, &sh_i);
+    const float *prow = a.p + ((size_t)s * (G + 1) + istar) * a.V;
+    const float *qrow = istar < G ? a.q + ((size_t)s * G + istar) * a.V : prow;
+    float pv[kUnitsSampling][kVPer], qv[kUnitsSampling][kVPer];
+#pragma unroll
+    for (int uu = 0; uu < kUnitsSampling; ++uu)
+#pragma unroll
+      for (int k = 0; k < kVPer; ++k) {
+        const int unit = u0 + uu;
+        const int j = unit * kVChunk + k * kVThreads + tid;
+        const bool ok = uu < a.upb && unit < units && j < a.V;
+        pv[uu][k] = ok ? prow[j] : 0.f;
+        qv[uu][k] = ok && istar < G ? qrow[j] : 0.f;
+      }
+    uint64_t sum[kUnitsSampling];
+#pragma unroll
+    for (int uu = 0; uu < kUnitsSampling; ++uu) {
+      sum[uu] = 0;
+#pragma unroll
+      for (int k = 0; k < kVPer; ++k) {
+        const float d = istar < G ? pv[uu][k] - qv[uu][k] : pv[uu][k];  // residual / bonus
+        sum[uu] += quantize(d > 0.f ? d : 0.f);
+      }
+    }
+    const uint64_t r = block_reduce_many<false, kUnitsSampling>(sum, many);
+    if (tid < a.upb && u0 + tid < units) store_coherent64(a.part + (size_t)s * a.chunks + u0 + tid, r);
+  } else {
+    float pv[kUnitsGreedy][kVPer];
+#pragma unroll
+    for (int uu = 0; uu < kUnitsGreedy; ++uu) {
+      const int unit = u0 + uu;
+      const int row_i = unit / a.chunks, c = unit - row_i * a.chunks;
+      const float *row = a.p + ((size_t)s * (G + 1) + row_i) * a.V;
+#pragma unroll
+      for (int k = 0; k < kVPer; ++k) {
+        const int j = c * kVChunk + k * kVThreads + tid;
+        const bool ok = uu < a.upb && unit < units && j < a.V;
+        pv[uu][k] = ok ? row[j] : 0.f;
+      }
+    }
+    uint64_t best[kUnitsGreedy];
+#pragma unroll
+    for (int uu = 0; uu < kUnitsGreedy; ++uu) {
+      const int unit = u0 + uu;
+      const int c = unit % a.chunks;
+      best[uu] = 0;
+#pragma unroll
+      for (int k = 0; k < kVPer; ++k) {
+        const int j = c * kVChunk + k * kVThreads + tid;
+        const bool ok = uu < a.upb && unit < units && j < a.V;
+        const uint64_t key = ok ? argmax_key(pv[uu][k], j) : 0ull;
+        best[uu] = key > best[uu] ? key : best[uu];
+      }
+    }
+    const uint64_t r = block_reduce_many<true, kUnitsGreedy>(best, many);
+    if (tid < a.upb && u0 + tid < units) store_coherent64(a.part + (size_t)s * units + u0 + tid, r);
+  }
+
+  // ---- the last workgroup of the sequence finishes the round
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) {
+    sh_last = atomicAdd(a.done + s, 1u) == arrivals - 1;
+    if (sh_last) atomicExch(a.done + s, 0u);
+  }
+  __syncthreads();
+  if (!sh_last) return;
+
+  int32_t *out = a.out + (size_t)s * (G + 1);
+  if (!sampling) {
+    // all (position, chunk) keys at once: one LDS max per position
+    __shared__ unsigned long long best[MOE_MAX_DRAFT + 1];
+    __shared__ int sh_n;
+    for (int i = tid; i <= G; i += kVThreads) best[i] = 0ull;
+    __syncthreads();
+    for (int f = tid; f < units; f += kVThreads) {
+      const uint64_t k = load_coherent64(a.part + (size_t)s * units + f);
+      atomicMax(&best[f / a.chunks], (unsigned long long)k);
+    }
+    __syncthreads();
+    // kept drafts: the leading positions whose argmax is the draft token
+    if (tid < 64) {
+      const bool miss = tid < G && key_index(best[tid]) != xs[tid];
+      const uint64_t m = __ballot(miss);
+      if (tid == 0) sh_n = m ? __ffsll((unsigned long long)m) - 1 : G;
+    }
+    __syncthreads();
+    const int n = sh_n;
+    for (int i = tid; i <= G; i += kVThreads)
+      out[i] = i < n ? xs[i] : (i == n ? key_index(best[n]) : -1);
+    if (tid == 0) a.n_acc[s] = n;
+    return;
+  }
+
+  // total weight: the chunk sums (or, if the residual vanished, the
+  // verifier's own row, summed here by this workgroup alone)
+  uint64_t W = 0;
+  for (int cc = tid; cc < a.chunks; cc += kVThreads)
+    W += load_coherent64(a.part + (size_t)s * a.chunks + cc);
+  W = block_reduce<false>(W, scratch);
+  const bool fallback = W == 0 && istar < G;
+  if (fallback) {
+    W = 0;
+    for (int j = tid; j < a.V; j += kVThreads) W += draw_weight(a, s, istar, true, j);
+    W = block_reduce<false>(W, scratch);
+  }
+  const uint64_t hi = __umul64hi(W, rr), lo = W * rr;
+  const uint64_t target = (hi << 32) | (lo >> 32);  // floor(W r / 2^32) < W
+
+  // the chunk holding the target: block-wide prefix sums of the chunk sums,
+  // kVThreads chunks at a time
+  __shared__ int sh_chunk;
+  __shared__ uint64_t sh_before;
+  if (tid == 0) sh_chunk = -1;
+  uint64_t run = 0;
+  for (int c0 = 0; c0 < a.chunks; c0 += kVThreads) {
+    const int cc = c0 + tid;
+    uint64_t cs = 0;
+    if (cc < a.chunks) {
+      if (!fallback) {
+        cs = load_coherent64(a.part + (size_t)s * a.chunks + cc);
+      } else {
+        for (int k = 0; k < kVChunk; ++k) {
+          const int j = cc * kVChunk + k;
+          if (j < a.V) cs += draw_weight(a, s, istar, true, j);
+        }
+      }
+    }
+    uint64_t total;
+    const uint64_t incl = block_scan(cs, scratch, &total);
+    if (cs > 0 && run + incl > target && run + incl - cs <= target) {
+      sh_chunk = cc;
+      sh_before = run + incl - cs;
+    }
+    __syncthreads();
+    if (sh_chunk >= 0) break;
+    run += total;
+  }
+  // inside that chunk (no chunk when every weight is zero: the draw has no
+  // token, -1): its weights loaded at once, then k-major rows of kVThreads
+  // consecutive entries scanned in order
+  __shared__ int sh_pick;
+  if (tid == 0) sh_pick = -1;
+  if (sh_chunk >= 0) {
+    const int cb = sh_chunk * kVChunk;
+    uint64_t w[kVPer];
+#pragma unroll
+    for (int k = 0; k < kVPer; ++k) {
+      const int j = cb + k * kVThreads + tid;
+      w[k] = j < a.V ? draw_weight(a, s, istar, fallback, j) : 0ull;
+    }
+    run = sh_before;
+    for (int k = 0; k < kVPer; ++k) {
+      uint64_t total;
+      const uint64_t incl = block_scan(w[k], scratch, &total);
+      // the first entry whose inclusive prefix passes the target
+      if (w[k] > 0 && run + incl > target && run + incl - w[k] <= target)
+        sh_pick = cb + k * kVThreads + tid;
+      __syncthreads();
+      if (sh_pick >= 0) break;
+      run += total;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i <= G; i += kVThreads)
+    out[i] = i < istar ? xs[i] : (i == istar ? sh_pick : -1);
+  if (tid == 0) a.n_acc[s] = istar;
+}
+
+}  // namespace
+
+int verify_chunks(int V) { return (V + kVChunk - 1) / kVChunk; }
+
+hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, const float *q,
+                         const int32_t *x, const float *u, const uint32_t *r, int32_t *n_acc,
+                         int32_t *out, void *ws, hipStream_t st) {
+  VerifyArgs a{};
+  a.n_seq = n_seq;
+  a.gamma = gamma;
+  a.V = V;
+  a.mode = mode;
+  a.chunks = verify_chunks(V);
+  a.p = p;
+  a.q = q;
+  a.u = u;
+  a.x = x;
+  a.r = r;
+  a.n_acc = n_acc;
+  a.out = out;
+  a.done = (unsigned *)ws;
+  a.part = (uint64_t *)((unsigned char *)ws + 256);
+  // about 64 workgroups per sequence: the whole chip for a few sequences,
+  // without piling every chunk's arrival onto one counter
+  const bool sampling = mode == MOE_VERIFY_SAMPLING;
+  const int units = sampling ? a.chunks : a.chunks * (gamma + 1);
+  const int cap = sampling ? kUnitsSampling : kUnitsGreedy;
+  a.upb = (units + 63) / 64;
+  a.upb = a.upb < 1 ? 1 : (a.upb > cap ? cap : a.upb);
+  const int per_seq = (units + a.upb - 1) / a.upb;
+  hipLaunchKernelGGL(verify_kernel, dim3(per_seq, n_seq), dim3(kVThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

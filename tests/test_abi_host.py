@@ -144,3 +144,32 @@ def test_bad_layout_and_pack_arguments_are_rejected():
     assert lib.moe_pack_weights(C.byref(s), -1, None, None, None, None, None) == -1
     # nothing to do is fine and launches nothing
     assert lib.moe_pack_weights(C.byref(s), 3, None, None, None, None, None) == 0
+
+
+def _verify(n_seq=2, gamma=4, V=1000, mode=1, p=FAKE, q=FAKE, x=FAKE, u=FAKE, r=FAKE,
+            n=FAKE, out=FAKE, ws=None, nbytes=0):
+    nb = C.c_size_t(nbytes)
+    return B.load().moe_verify_gate(n_seq, gamma, V, mode, p, q, x, u, r, n, out, ws,
+                                    C.byref(nb), None), nb.value
+
+
+def test_verify_gate_validation_and_workspace_query():
+    ok, need = _verify()
+    assert ok == 0
+    # 256 bytes of counters + S * chunks(V) * (gamma + 1) uint64, 256-aligned
+    chunks = (1000 + 2047) // 2048
+    assert need == 256 + ((2 * chunks * 5 * 8 + 255) // 256) * 256
+    ok, need_big = _verify(n_seq=64, gamma=63, V=152064)
+    assert ok == 0 and need_big == 256 + ((64 * 75 * 64 * 8 + 255) // 256) * 256
+    bad = [dict(n_seq=0), dict(n_seq=65), dict(gamma=-1), dict(gamma=64), dict(V=0),
+           dict(V=(1 << 24) + 1), dict(mode=2), dict(p=None), dict(n=None), dict(out=None),
+           dict(x=None), dict(q=None), dict(u=None), dict(r=None)]
+    for kw in bad:
+        rc, _ = _verify(**kw)
+        assert rc == -1, kw
+    # greedy needs neither q, u nor r; gamma 0 needs no draft tokens
+    assert _verify(mode=0, q=None, u=None, r=None)[0] == 0
+    assert _verify(gamma=0, x=None, q=None, u=None)[0] == 0
+    # a workspace smaller than needed
+    rc, _ = _verify(ws=FAKE, nbytes=need - 1)
+    assert rc == -3
