@@ -31,6 +31,13 @@
  *      taken on the fp32 value as the GPU path does); fp32 configs round
  *      nothing.
  *  R5  the dense mixture of s1 uses the same softmax gate over all E experts.
+ *  R6  the per-expert bias of the DeepSeek-style sketch (s5) is added to the
+ *      logits before the top-k, and the softmax over the k takes the biased
+ *      values, as the sketch writes it.
+ *  R7  dedup within token groups (several sequences verified in one pass):
+ *      each group reads each of its distinct experts once, so a pass
+ *      requests sum over groups of U_g expert reads; one group is the dedup
+ *      engine, one token per group reads what the per-slot engine reads.
  */
 #include "moe_oracle.h"
 
@@ -110,6 +117,113 @@ void run_jobs(size_t n_jobs, int n_threads, const Job &job) {
   for (auto &th : pool) th.join();
 }
 
+/* [MoE] s2 from the logits on: top-k under R2, softmax over the k (R3),
+ * margin and near-tie flags.  L is [n_tokens][E] fp64. */
+void route_from_logits(const oracle_shape *s, const std::vector<double> &L, int32_t n_tokens,
+                       double tie_eps, double *logits, int32_t *idx, double *w,
+                       double *margin, uint8_t *flags) {
+  const int E = s->E, k = s->k;
+  if (logits) std::memcpy(logits, L.data(), L.size() * sizeof(double));
+
+  for (int t = 0; t < n_tokens; ++t) {
+    const double *Lt = &L[(size_t)t * E];
+    std::vector<float> key(E);
+    for (int e = 0; e < E; ++e) key[e] = (float)Lt[e];
+
+    /* [MoE] s2: top_k_vals, top_k_idx = topk(logits, k).  Selection by
+     * repeated search for the best remaining expert under R2. */
+    std::vector<int> order;
+    std::vector<bool> taken(E, false);
+    int rounds = (k < E) ? k + 1 : k; /* one more for the margin */
+    for (int r = 0; r < rounds; ++r) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || before(key, e, best))) best = e;
+      taken[best] = true;
+      order.push_back(best);
+    }
+    for (int j = 0; j < k; ++j) idx[(size_t)t * k + j] = order[j];
+
+    /* [MoE] s2: top_k_weights = softmax(top_k_vals), renormalised over the k */
+    double vmax = Lt[order[0]];
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += std::exp(Lt[order[j]] - vmax);
+    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = std::exp(Lt[order[j]] - vmax) / denom;
+
+    double m = (k < E) ? Lt[order[k - 1]] - Lt[order[k]]
+                       : std::numeric_limits<double>::infinity();
+    if (margin) margin[t] = m;
+    if (flags) {
+      uint8_t fl = 0;
+      if (m < tie_eps) fl |= ORACLE_FLAG_BOUNDARY;
+      for (int j = 0; j + 1 < k; ++j)
+        if (Lt[order[j]] - Lt[order[j + 1]] < tie_eps) fl |= ORACLE_FLAG_ORDER;
+      flags[t] = fl;
+    }
+  }
+}
+
+uint64_t expert_bytes(const oracle_shape *s) {
+  return 3ull * (uint64_t)s->d * (uint64_t)s->f * elem_bytes(s);
+}
+
+/* One job = one expert evaluation on one token: routed expert e for slot
+ * `slot` of token t, or shared expert `slot` (e unused) when shared. */
+struct Job {
+  int t, slot, e;
+  bool shared;
+};
+
+/* [SDM] dedup over the tokens t0 .. t1-1: every distinct selected expert,
+ * ascending, with all (token, slot) pairs of the range that chose it.
+ * Appends the jobs and returns the number of distinct experts. */
+int32_t dedup_jobs(const oracle_shape *s, const int32_t *idx, int t0, int t1,
+                   std::vector<Job> *jobs) {
+  const int k = s->k;
+  int32_t U = 0;
+  for (int e = 0; e < s->E; ++e) {
+    bool used = false;
+    for (int t = t0; t < t1; ++t)
+      for (int j = 0; j < k; ++j)
+        if (idx[(size_t)t * k + j] == e) {
+          jobs->push_back({t, j, e, false});
+          used = true;
+        }
+    if (used) ++U;
+  }
+  return U;
+}
+
+/* Runs the routed jobs plus every shared expert on every token, then
+ * [MoE] s2 / s5: y = sum over slots of weight * expert output, then the
+ * shared experts (weight 1); slot order whatever order the jobs came in. */
+void evaluate_layer(const oracle_shape *s, const oracle_weights *wts, const float *x, int N,
+                    const double *w, std::vector<Job> jobs, int n_threads, double *y) {
+  const int d = s->d, k = s->k, S = s->S;
+  /* o[t][j] = expert_{idx[t][j]}(x_t);  osh[t][s] = shared_s(x_t) */
+  std::vector<double> o((size_t)N * k * d), osh((size_t)N * S * d);
+  /* [MoE] s5: shared experts run on every token, read once per pass */
+  for (int sh = 0; sh < S; ++sh)
+    for (int t = 0; t < N; ++t) jobs.push_back({t, sh, sh, true});
+
+  run_jobs(jobs.size(), n_threads, [&](size_t i) {
+    const Job &jb = jobs[i];
+    const void *W1, *W3, *W2;
+    expert_mats(s, wts, jb.e, jb.shared, &W1, &W3, &W2);
+    double *dst = jb.shared ? &osh[((size_t)jb.t * S + jb.slot) * d]
+                            : &o[((size_t)jb.t * k + jb.slot) * d];
+    oracle_expert(s, W1, W3, W2, x + (size_t)jb.t * d, dst);
+  });
+
+  for (int t = 0; t < N; ++t)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += w[(size_t)t * k + j] * o[((size_t)t * k + j) * d + c];
+      for (int sh = 0; sh < S; ++sh) acc += osh[((size_t)t * S + sh) * d + c];
+      y[(size_t)t * d + c] = acc;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,47 +268,23 @@ int oracle_route(const oracle_shape *s, const float *gate_w, const float *x,
                  int32_t n_tokens, double tie_eps, double *logits, int32_t *idx,
                  double *w, double *margin, uint8_t *flags) {
   if (!shape_ok(s) || !gate_w || !x || !idx || !w || n_tokens < 0) return -1;
-  const int E = s->E, k = s->k;
-  std::vector<double> L((size_t)n_tokens * E);
+  std::vector<double> L((size_t)n_tokens * s->E);
   oracle_gate_logits(s, gate_w, x, n_tokens, L.data());
-  if (logits) std::memcpy(logits, L.data(), L.size() * sizeof(double));
+  route_from_logits(s, L, n_tokens, tie_eps, logits, idx, w, margin, flags);
+  return 0;
+}
 
-  for (int t = 0; t < n_tokens; ++t) {
-    const double *Lt = &L[(size_t)t * E];
-    std::vector<float> key(E);
-    for (int e = 0; e < E; ++e) key[e] = (float)Lt[e];
-
-    /* [MoE] s2: top_k_vals, top_k_idx = topk(logits, k).  Selection by
-     * repeated search for the best remaining expert under R2. */
-    std::vector<int> order;
-    std::vector<bool> taken(E, false);
-    int rounds = (k < E) ? k + 1 : k; /* one more for the margin */
-    for (int r = 0; r < rounds; ++r) {
-      int best = -1;
-      for (int e = 0; e < E; ++e)
-        if (!taken[e] && (best < 0 || before(key, e, best))) best = e;
-      taken[best] = true;
-      order.push_back(best);
-    }
-    for (int j = 0; j < k; ++j) idx[(size_t)t * k + j] = order[j];
-
-    /* [MoE] s2: top_k_weights = softmax(top_k_vals), renormalised over the k */
-    double vmax = Lt[order[0]];
-    double denom = 0.0;
-    for (int j = 0; j < k; ++j) denom += std::exp(Lt[order[j]] - vmax);
-    for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = std::exp(Lt[order[j]] - vmax) / denom;
-
-    double m = (k < E) ? Lt[order[k - 1]] - Lt[order[k]]
-                       : std::numeric_limits<double>::infinity();
-    if (margin) margin[t] = m;
-    if (flags) {
-      uint8_t fl = 0;
-      if (m < tie_eps) fl |= ORACLE_FLAG_BOUNDARY;
-      for (int j = 0; j + 1 < k; ++j)
-        if (Lt[order[j]] - Lt[order[j + 1]] < tie_eps) fl |= ORACLE_FLAG_ORDER;
-      flags[t] = fl;
-    }
-  }
+int oracle_route_biased(const oracle_shape *s, const float *gate_w, const float *bias,
+                        const float *x, int32_t n_tokens, double tie_eps, double *logits,
+                        int32_t *idx, double *w, double *margin, uint8_t *flags) {
+  if (!shape_ok(s) || !gate_w || !bias || !x || !idx || !w || n_tokens < 0) return -1;
+  std::vector<double> L((size_t)n_tokens * s->E);
+  oracle_gate_logits(s, gate_w, x, n_tokens, L.data());
+  /* [MoE] s5, DeepSeek-style routing sketch: logits = x @ gate_weights + bias,
+   * and the biased logits feed both the top-k and the softmax (R6) */
+  for (int t = 0; t < n_tokens; ++t)
+    for (int e = 0; e < s->E; ++e) L[(size_t)t * s->E + e] += (double)bias[e];
+  route_from_logits(s, L, n_tokens, tie_eps, logits, idx, w, margin, flags);
   return 0;
 }
 
@@ -232,19 +322,11 @@ int oracle_layer(const oracle_shape *s, const oracle_weights *wts, const float *
       n_tokens < 0 || (engine != 0 && engine != 1))
     return -1;
   if (s->S > 0 && (!wts->ws13 || !wts->ws2)) return -1;
-  const int d = s->d, k = s->k, S = s->S, N = n_tokens;
+  const int k = s->k, N = n_tokens;
   for (size_t i = 0; i < (size_t)N * k; ++i)
     if (idx[i] < 0 || idx[i] >= s->E) return -1;
-  const uint64_t Be = 3ull * (uint64_t)d * (uint64_t)s->f * elem_bytes(s);
+  const uint64_t Be = expert_bytes(s);
 
-  /* o[t][j] = expert_{idx[t][j]}(x_t);  osh[t][s] = shared_s(x_t) */
-  std::vector<double> o((size_t)N * k * d), osh((size_t)N * S * d);
-
-  /* One job = one expert evaluation on one token. */
-  struct Job {
-    int t, slot, e;
-    bool shared;
-  };
   std::vector<Job> jobs;
   uint64_t routed_bytes = 0;
   int32_t U = 0;
@@ -259,49 +341,47 @@ int oracle_layer(const oracle_shape *s, const oracle_weights *wts, const float *
     for (size_t i = 0; i < (size_t)N * k; ++i)
       if (!seen[idx[i]]) { seen[idx[i]] = true; ++U; }
   } else {
-    /* [SDM] dedup: each distinct selected expert is read once per pass and
-     * applied to every (token, slot) that chose it */
-    for (int e = 0; e < s->E; ++e) {
-      bool used = false;
-      for (int t = 0; t < N; ++t)
-        for (int j = 0; j < k; ++j)
-          if (idx[(size_t)t * k + j] == e) {
-            jobs.push_back({t, j, e, false});
-            used = true;
-          }
-      if (used) {
-        routed_bytes += Be;
-        ++U;
-      }
-    }
+    /* [SDM] dedup: each distinct selected expert is read once per pass */
+    U = dedup_jobs(s, idx, 0, N, &jobs);
+    routed_bytes = (uint64_t)U * Be;
   }
-  /* [MoE] s5: shared experts run on every token, read once per pass */
-  for (int sh = 0; sh < S; ++sh)
-    for (int t = 0; t < N; ++t) jobs.push_back({t, sh, sh, true});
-
-  run_jobs(jobs.size(), n_threads, [&](size_t i) {
-    const Job &jb = jobs[i];
-    const void *W1, *W3, *W2;
-    expert_mats(s, wts, jb.e, jb.shared, &W1, &W3, &W2);
-    double *dst = jb.shared ? &osh[((size_t)jb.t * S + jb.slot) * d]
-                            : &o[((size_t)jb.t * k + jb.slot) * d];
-    oracle_expert(s, W1, W3, W2, x + (size_t)jb.t * d, dst);
-  });
-
-  /* [MoE] s2 / s5: output = sum over slots of weight * expert output, then the
-   * shared experts; slot order in both engines */
-  for (int t = 0; t < N; ++t)
-    for (int c = 0; c < d; ++c) {
-      double acc = 0.0;
-      for (int j = 0; j < k; ++j) acc += w[(size_t)t * k + j] * o[((size_t)t * k + j) * d + c];
-      for (int sh = 0; sh < S; ++sh) acc += osh[((size_t)t * S + sh) * d + c];
-      y[(size_t)t * d + c] = acc;
-    }
+  evaluate_layer(s, wts, x, N, w, jobs, n_threads, y);
   if (bytes) {
     bytes[0] = routed_bytes;
-    bytes[1] = (uint64_t)S * Be;
+    bytes[1] = (uint64_t)s->S * Be;
   }
   if (n_unique) *n_unique = U;
+  return 0;
+}
+
+int oracle_layer_grouped(const oracle_shape *s, const oracle_weights *wts, const float *x,
+                         int32_t n_tokens, int32_t n_groups, const int32_t *group_start,
+                         const int32_t *idx, const double *w, int32_t n_threads, double *y,
+                         uint64_t *bytes, int32_t *n_unique) {
+  if (!shape_ok(s) || !wts || !wts->w13 || !wts->w2 || !x || !idx || !w || !y ||
+      !group_start || n_tokens < 0 || n_groups < 1)
+    return -1;
+  if (s->S > 0 && (!wts->ws13 || !wts->ws2)) return -1;
+  if (group_start[0] != 0 || group_start[n_groups] != n_tokens) return -1;
+  for (int g = 0; g < n_groups; ++g)
+    if (group_start[g + 1] <= group_start[g]) return -1;
+  for (size_t i = 0; i < (size_t)n_tokens * s->k; ++i)
+    if (idx[i] < 0 || idx[i] >= s->E) return -1;
+  const uint64_t Be = expert_bytes(s);
+
+  /* R7: the dedup formulation applied to each group's tokens on its own */
+  std::vector<Job> jobs;
+  uint64_t routed_bytes = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const int32_t Ug = dedup_jobs(s, idx, group_start[g], group_start[g + 1], &jobs);
+    routed_bytes += (uint64_t)Ug * Be;
+    if (n_unique) n_unique[g] = Ug;
+  }
+  evaluate_layer(s, wts, x, n_tokens, w, jobs, n_threads, y);
+  if (bytes) {
+    bytes[0] = routed_bytes;
+    bytes[1] = (uint64_t)s->S * Be;
+  }
   return 0;
 }
 

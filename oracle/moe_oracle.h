@@ -74,6 +74,13 @@ int oracle_route(const oracle_shape *s, const float *gate_w, const float *x,
                  int32_t n_tokens, double tie_eps, double *logits, int32_t *idx,
                  double *w, double *margin, uint8_t *flags);
 
+/* oracle_route with a per-expert bias [E] added to the logits before the
+ * top-k; the softmax over the k takes the biased values (DeepSeek-style
+ * sketch).  logits receives the biased logits. */
+int oracle_route_biased(const oracle_shape *s, const float *gate_w, const float *bias,
+                        const float *x, int32_t n_tokens, double tie_eps, double *logits,
+                        int32_t *idx, double *w, double *margin, uint8_t *flags);
+
 /* One SwiGLU expert on one token: out[d] = W2 * r(silu(W1 xt) . (W3 xt)),
  * xt = r(x), r = bf16 rounding for bf16 weights and the identity for fp32.
  * W1/W3/W2 point at that expert's matrices, element type per wdtype. */
@@ -90,6 +97,15 @@ int oracle_expert(const oracle_shape *s, const void *W1, const void *W3,
 int oracle_layer(const oracle_shape *s, const oracle_weights *wts, const float *x,
                  int32_t n_tokens, const int32_t *idx, const double *w, int32_t engine,
                  int32_t n_threads, double *y, uint64_t *bytes, int32_t *n_unique);
+
+/* The layer with dedup inside token groups: tokens group_start[g] ..
+ * group_start[g+1]-1 form group g (group_start[0] = 0, group_start[G] = N,
+ * strictly increasing).  y as oracle_layer; bytes[0] = sum_g U_g B_e,
+ * bytes[1] = S B_e; n_unique[g] = U_g (may be NULL). */
+int oracle_layer_grouped(const oracle_shape *s, const oracle_weights *wts, const float *x,
+                         int32_t n_tokens, int32_t n_groups, const int32_t *group_start,
+                         const int32_t *idx, const double *w, int32_t n_threads, double *y,
+                         uint64_t *bytes, int32_t *n_unique);
 
 /* Dense mixture: y[t] = sum_e softmax(L_t)_e * expert_e(x_t) + shared. */
 int oracle_dense_mixture(const oracle_shape *s, const float *gate_w,

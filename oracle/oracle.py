@@ -57,6 +57,8 @@ def load():
         lib.oracle_bf16_rne.restype = C.c_uint16
         lib.oracle_gate_logits.argtypes = [P, P, P, i32, P]
         lib.oracle_route.argtypes = [P, P, P, i32, C.c_double, P, P, P, P, P]
+        lib.oracle_route_biased.argtypes = [P, P, P, P, i32, C.c_double, P, P, P, P, P]
+        lib.oracle_layer_grouped.argtypes = [P, P, P, i32, i32, P, P, P, i32, P, P, P]
         lib.oracle_expert.argtypes = [P, P, P, P, P, P]
         lib.oracle_layer.argtypes = [P, P, P, i32, P, P, i32, i32, P, P, P]
         lib.oracle_dense_mixture.argtypes = [P, P, P, P, i32, P]
@@ -65,8 +67,9 @@ def load():
         lib.oracle_sample_index.argtypes = [P, i32, C.c_uint32]
         lib.oracle_sample_index.restype = i32
         lib.oracle_verify_gate.argtypes = [i32, i32, i32, P, P, P, P, C.c_uint32, P, P]
-        for fn in ("oracle_gate_logits", "oracle_route", "oracle_expert", "oracle_layer",
-                   "oracle_dense_mixture", "oracle_pass_bytes", "oracle_compact"):
+        for fn in ("oracle_gate_logits", "oracle_route", "oracle_route_biased", "oracle_expert",
+                   "oracle_layer", "oracle_layer_grouped", "oracle_dense_mixture",
+                   "oracle_pass_bytes", "oracle_compact"):
             getattr(lib, fn).restype = C.c_int
         _LIB = lib
     return _LIB
@@ -122,9 +125,10 @@ def gate_logits(shape: Shape, gate_w, x):
     return out
 
 
-def route(shape: Shape, gate_w, x, tie_eps=1e-4):
+def route(shape: Shape, gate_w, x, tie_eps=1e-4, bias=None):
     """Returns dict(logits fp64 [N][E], idx int32 [N][k], w fp64 [N][k],
-    margin fp64 [N], flags uint8 [N])."""
+    margin fp64 [N], flags uint8 [N]).  With bias [E], the DeepSeek-style
+    biased routing (oracle_route_biased)."""
     lib = load()
     gate_w, x = _f32(gate_w), _f32(x)
     n = x.shape[0]
@@ -133,9 +137,14 @@ def route(shape: Shape, gate_w, x, tie_eps=1e-4):
     w = np.empty((n, shape.k), dtype=np.float64)
     margin = np.empty((n,), dtype=np.float64)
     flags = np.empty((n,), dtype=np.uint8)
-    _check(lib.oracle_route(C.byref(shape.c()), _p(gate_w), _p(x), n, float(tie_eps),
-                            _p(logits), _p(idx), _p(w), _p(margin), _p(flags)),
-           "oracle_route")
+    outs = (_p(logits), _p(idx), _p(w), _p(margin), _p(flags))
+    if bias is None:
+        _check(lib.oracle_route(C.byref(shape.c()), _p(gate_w), _p(x), n, float(tie_eps), *outs),
+               "oracle_route")
+    else:
+        b = _f32(bias).reshape(shape.E)
+        _check(lib.oracle_route_biased(C.byref(shape.c()), _p(gate_w), _p(b), _p(x), n,
+                                       float(tie_eps), *outs), "oracle_route_biased")
     return dict(logits=logits, idx=idx, w=w, margin=margin, flags=flags)
 
 
@@ -171,6 +180,27 @@ def layer(shape: Shape, w13, w2, ws13, ws2, x, idx, w, engine="perslot", n_threa
                             int(n_threads), _p(y), _p(b), _p(u)), "oracle_layer")
     del keep
     return y, int(b[0]), int(b[1]), int(u[0])
+
+
+def layer_grouped(shape: Shape, w13, w2, ws13, ws2, x, idx, w, group_start, n_threads=1):
+    """Dedup inside token groups.  Returns (y fp64 [N][d], routed_bytes,
+    shared_bytes, n_unique per group [G])."""
+    lib = load()
+    keep, cw = _weights(shape, w13, w2, ws13, ws2)
+    x = _f32(x)
+    idx = _i32(idx)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    gs = _i32(group_start)
+    G = gs.size - 1
+    n = x.shape[0]
+    y = np.empty((n, shape.d), dtype=np.float64)
+    b = np.zeros((2,), dtype=np.uint64)
+    u = np.zeros((max(G, 1),), dtype=np.int32)
+    _check(lib.oracle_layer_grouped(C.byref(shape.c()), C.byref(cw), _p(x), n, G, _p(gs),
+                                    _p(idx), _p(w), int(n_threads), _p(y), _p(b), _p(u)),
+           "oracle_layer_grouped")
+    del keep
+    return y, int(b[0]), int(b[1]), u[:G].copy()
 
 
 def dense_mixture(shape: Shape, gate_w, w13, w2, ws13, ws2, x):
