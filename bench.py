@@ -368,6 +368,90 @@ def rho_sweep(cfg, eng, layers, calib, reps):
     return out
 
 
+def variants_leg(cfg, eng, layers, n_values, reps):
+    """The layer variants on the same passes.  Per n and repetition, three
+    engine calls on the next layers of the rotation -- per-slot, dedup over
+    the union of the sequences' tokens, and dedup per sequence (one token
+    group per sequence, moe_expert_pass_dedup_grouped) -- each after its
+    own plain route, and one DeepSeek-style biased route (per-expert bias,
+    moe_route_biased) timed alone.  U of every dedup pass is read from the
+    engines' device outputs."""
+    nL = len(layers)
+    Be = expert_bytes(cfg)
+    bias = [synth.make_bias(cfg, "cuda", layer=L) for L in range(nL)]
+    out = []
+    turn = 0
+    names = ("perslot", "union", "perseq")
+    for n in n_values:
+        N = cfg.tokens(n)
+        gs = synth.sequence_groups(cfg, n)
+        G = len(gs) - 1
+        y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+        nu_u = torch.zeros((reps,), dtype=torch.int32, device="cuda")
+        nu_g = torch.zeros((reps, G), dtype=torch.int32, device="cuda")
+        ws_g = B.Workspace()
+        xs = [synth.make_hidden(cfg, n, rep, "cuda") for rep in range(reps)]
+        idx_b = []
+        evs = []
+        hold_gpu(0.5 * reps)
+        for rep in range(reps):
+            x = xs[rep]
+            row = {}
+            for name in names:
+                lay = layers[turn % nL]
+                turn += 1
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record()
+                idx, w = eng.route(lay, x)
+                e1.record()
+                if name == "perslot":
+                    eng.perslot(lay, x, idx, w, y)
+                elif name == "union":
+                    B.expert_pass_dedup(eng.shape, lay, x, idx, w, y=y,
+                                        n_unique=nu_u[rep:rep + 1], ws=eng.ws_dd)
+                else:
+                    B.expert_pass_dedup_grouped(eng.shape, lay, x, idx, w, gs, y=y,
+                                                n_unique=nu_g[rep], ws=ws_g)
+                e2.record()
+                row[name] = (e0, e1, e2)
+            L = turn % nL
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            ib, _ = B.route(eng.shape, layers[L]["gate_w"], x, bias=bias[L], ws=eng.ws_route)
+            e1.record()
+            row["route_bias"] = (e0, e1)
+            idx_b.append(ib)
+            evs.append(row)
+        torch.cuda.synchronize()
+        t = {k: [] for k in names + ("route", "route_bias")}
+        for row in evs:
+            for name in names:
+                e0, e1, e2 = row[name]
+                t["route"].append(e0.elapsed_time(e1) * 1e3)
+                t[name].append(e1.elapsed_time(e2) * 1e3)
+            t["route_bias"].append(row["route_bias"][0].elapsed_time(row["route_bias"][1]) * 1e3)
+        med = {k: float(np.median(v)) for k, v in t.items()}
+        U_u = float(nu_u.cpu().numpy().mean())
+        U_g = nu_g.cpu().numpy().astype(np.float64)
+        U_b = float(np.mean([unique_count(i.cpu().numpy(), cfg.E) for i in idx_b]))
+        routed = {"perslot": N * cfg.k * Be, "union": U_u * Be, "perseq": U_g.sum(axis=1).mean() * Be}
+        rec = {"n": n, "tokens": N, "sequences": G,
+               "U_union": round(U_u, 2), "U_per_sequence_sum": round(float(U_g.sum(axis=1).mean()), 2),
+               "U_per_sequence_mean": round(float(U_g.mean()), 2),
+               "U_union_biased_route": round(U_b, 2),
+               "route_us": round(med["route"], 2), "route_bias_us": round(med["route_bias"], 2)}
+        for name in names:
+            req = routed[name] + cfg.S * Be
+            rec[name] = {"us": round(med[name], 2), "GBs": round(req / med[name] / 1e3, 1),
+                         "hbm_frac": round(req / med[name] / 1e3 / HBM_PEAK_GBS, 3)}
+        rec["union_saving_over_perseq_us"] = round(med["perseq"] - med["union"], 2)
+        out.append(rec)
+        log(f"  n={n:2d} x{G}: perslot {med['perslot']:8.1f} union {med['union']:8.1f} "
+            f"perseq {med['perseq']:8.1f} us | U {U_u:.1f} vs sum {rec['U_per_sequence_sum']:.1f}"
+            f" | route {med['route']:.1f} biased {med['route_bias']:.1f} us")
+    return out
+
+
 def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=()):
     """The headline step at one pass size: K timed steps after W warmups,
     bracketed by device synchronisation.  With kernel_events, the library
@@ -479,6 +563,12 @@ def main():
     ap.add_argument("--rho-sweep", action="store_true",
                     help="instead of the bench line: the routing-overlap sweep over the "
                          "26-layer V2-Lite stack (one JSON document)")
+    ap.add_argument("--variants", action="store_true",
+                    help="instead of the bench line: per-slot vs union dedup vs "
+                         "per-sequence dedup, and plain vs biased routing, over the "
+                         "config's pass sizes (one JSON document)")
+    ap.add_argument("--variant-reps", type=int, default=12,
+                    help="passes per n and engine in the variants leg")
     ap.add_argument("--stack-reps", type=int, default=32,
                     help="stack passes per (rho, n) in the rho sweep")
     ap.add_argument("--no-sweep", action="store_true")
@@ -532,6 +622,18 @@ def main():
         del rows
         log(f"[bench] weights {L + 1}/{n_layers} drawn and packed")
     eng = Engines(cfg)
+
+    if args.variants:
+        log("[bench] variants warmup")
+        variants_leg(cfg, eng, layers, cfg.n_values[:1], 2)
+        log("[bench] variants")
+        doc = {"kind": "layer variants",
+               "workload": f"{cfg.name}-shaped layer, {cfg.n_seq} sequence(s) x n = "
+                           f"{min(cfg.n_values)}..{max(cfg.n_values)} tokens per pass, "
+                           f"{n_layers} weight sets rotated",
+               "by_n": variants_leg(cfg, eng, layers, cfg.n_values, args.variant_reps)}
+        print(json.dumps(doc), flush=True)
+        return
 
     sweep = calib = None
     if not args.no_sweep or args.rho_sweep:

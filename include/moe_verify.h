@@ -70,6 +70,7 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 #define MOE_MAX_SLOTS 512
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_SHARED 4
+#define MOE_MAX_GROUPS 64  /* token groups of a grouped dedup pass */
 #define MOE_MAX_SEQ 64     /* sequences per verification-round call */
 #define MOE_MAX_DRAFT 63   /* drafted tokens per sequence and round */
 #define MOE_MAX_VOCAB (1 << 24)
@@ -141,6 +142,18 @@ int moe_route(const moe_shape *shape, const float *gate_w, const float *x,
               int32_t n_tokens, float *logits, int32_t *topk_idx, float *topk_w,
               float *margin, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* moe_route with the per-expert bias of the DeepSeek-style routing sketch
+ * ("Deep Dive into Mixture of Experts", section 5: logits = x @ gate_weights
+ * + bias, then top_k and softmax of the selected values):
+ *   bias [E] fp32 device, added to every token's logits after the gate
+ *        product; the selection, the margin, the softmax over the k and the
+ *        logits output all take the biased values.  NULL is moe_route.
+ * Other arguments, workspace and errors as for moe_route. */
+int moe_route_biased(const moe_shape *shape, const float *gate_w, const float *bias,
+                     const float *x, int32_t n_tokens, float *logits, int32_t *topk_idx,
+                     float *topk_w, float *margin, void *workspace, size_t *workspace_bytes,
+                     void *stream);
+
 /* Per-slot expert pass ("Speculative Decoding for Mixture-of-Experts
  * Models", abstract: a per-slot engine reads each selected expert once per
  * token).  Every (token t, slot j) streams expert topk_idx[t][j]; shared
@@ -175,6 +188,29 @@ int moe_expert_pass_dedup(const moe_shape *shape, const moe_expert_weights *weig
                           const float *topk_w, float *y, int32_t *n_unique,
                           void *workspace, size_t *workspace_bytes, void *stream);
 
+/* Deduplicating expert pass inside token groups, e.g. the sequences of a
+ * batch verified in one pass: each group streams each of its distinct
+ * experts once ("Speculative Decoding for Mixture-of-Experts Models",
+ * abstract, applied per group), so the pass requests sum_g U_g expert reads,
+ * between the union's U and N*k.  Same y as the other passes.
+ *   n_groups     G, 1 <= G <= MOE_MAX_GROUPS
+ *   group_start  [G+1] int32 HOST array: group g is tokens group_start[g] ..
+ *                group_start[g+1]-1; group_start[0] = 0, group_start[G] =
+ *                N, strictly increasing (else MOE_ERR_INVALID_ARG).  Read
+ *                during the call only.
+ *   n_unique     [G] int32 device output (or NULL): U_g per group.
+ * The workspace begins with G compaction records, record g at byte offset
+ * g * R, R = the 256-byte-aligned size of one record (the layout of
+ * moe_expert_pass_dedup's with N*k list entries, of which group g fills its
+ * own slots; list entries are slot ids t*k+j of the whole pass).  G = 1 with
+ * group_start = {0, N} is moe_expert_pass_dedup; one token per group
+ * streams what the per-slot pass streams. */
+int moe_expert_pass_dedup_grouped(const moe_shape *shape, const moe_expert_weights *weights,
+                                  const float *x, int32_t n_tokens, int32_t n_groups,
+                                  const int32_t *group_start, const int32_t *topk_idx,
+                                  const float *topk_w, float *y, int32_t *n_unique,
+                                  void *workspace, size_t *workspace_bytes, void *stream);
+
 /* Requested expert bytes of one pass, on the host (same abstract: step time
  * is the bytes each kernel requests over its effective bandwidth).
  * B_e = 3 * d * f * sizeof(weight); perslot = N*k*B_e, dedup = U*B_e,
@@ -184,6 +220,15 @@ int moe_expert_pass_dedup(const moe_shape *shape, const moe_expert_weights *weig
 int moe_pass_bytes(const moe_shape *shape, const int32_t *topk_idx_host, int32_t n_tokens,
                    uint64_t *perslot_bytes, uint64_t *dedup_bytes, uint64_t *shared_bytes,
                    int32_t *n_unique);
+
+/* moe_pass_bytes of a grouped dedup pass: dedup_bytes = sum_g U_g * B_e and
+ * n_unique[g] = U_g (host array of G, or NULL), for the groups of
+ * moe_expert_pass_dedup_grouped.  Host memory only; synchronous, pure,
+ * thread-safe; an entry outside [0, E) or bad groups return
+ * MOE_ERR_INVALID_ARG. */
+int moe_pass_bytes_grouped(const moe_shape *shape, const int32_t *topk_idx_host,
+                           int32_t n_tokens, int32_t n_groups, const int32_t *group_start,
+                           uint64_t *dedup_bytes, int32_t *n_unique);
 
 /* One speculative-decoding verification round for each of n_seq sequences
  * ("Building a Terminal Based LLM Inference Internals Explorer - Part 3:

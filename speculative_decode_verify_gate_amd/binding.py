@@ -18,6 +18,7 @@ MAX_TOKENS, MAX_TOPK, MAX_SLOTS, MAX_EXPERTS, MAX_SHARED = 64, 16, 512, 256, 4
 KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine", "verify")
 VERIFY_GREEDY, VERIFY_SAMPLING = 0, 1
 MAX_SEQ, MAX_DRAFT, MAX_VOCAB = 64, 63, 1 << 24
+MAX_GROUPS = 64
 
 _lib = None
 
@@ -52,6 +53,9 @@ def load():
     lib = C.CDLL(LIB_PATH)
     P, i32, sz = C.c_void_p, C.c_int32, C.POINTER(C.c_size_t)
     lib.moe_route.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
+    lib.moe_route_biased.argtypes = [P, P, P, P, i32, P, P, P, P, P, sz, P]
+    lib.moe_expert_pass_dedup_grouped.argtypes = [P, P, P, i32, i32, P, P, P, P, P, P, sz, P]
+    lib.moe_pass_bytes_grouped.argtypes = [P, P, i32, i32, P, P, P]
     lib.moe_expert_pass_perslot.argtypes = [P, P, P, i32, P, P, P, P, sz, P]
     lib.moe_expert_pass_dedup.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
     lib.moe_pass_bytes.argtypes = [P, P, i32, P, P, P, P]
@@ -61,9 +65,10 @@ def load():
     lib.moe_timing_enable.argtypes = [C.c_int]
     lib.moe_timing_read.argtypes = [P, P]
     lib.moe_verify_gate.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
-    for fn in ("moe_route", "moe_expert_pass_perslot", "moe_expert_pass_dedup",
-               "moe_pass_bytes", "moe_pack_weights", "moe_timing_enable", "moe_timing_read",
-               "moe_verify_gate"):
+    for fn in ("moe_route", "moe_route_biased", "moe_expert_pass_perslot",
+               "moe_expert_pass_dedup", "moe_expert_pass_dedup_grouped", "moe_pass_bytes",
+               "moe_pass_bytes_grouped", "moe_pack_weights", "moe_timing_enable",
+               "moe_timing_read", "moe_verify_gate"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -159,12 +164,17 @@ def pack_weights(shape, weights):
     return out
 
 
-def route(shape, gate_w, x, *, idx=None, w=None, logits=None, margin=None, ws=None):
+def route(shape, gate_w, x, *, bias=None, idx=None, w=None, logits=None, margin=None,
+          ws=None):
     """Gate logits, top-k and softmax over the k.  Returns (idx int32 [N][k],
-    w fp32 [N][k]); logits [N][E] and margin [N] are filled when given."""
+    w fp32 [N][k]); logits [N][E] and margin [N] are filled when given.  With
+    bias (fp32 [E]) the DeepSeek-style biased routing (moe_route_biased)."""
     lib = load()
     gate_w = _dev(gate_w, torch.float32, "gate_w")
     x = _dev(x, torch.float32, "x")
+    bias = _dev(bias, torch.float32, "bias")
+    if bias is not None and tuple(bias.shape) != (shape.n_experts,):
+        raise ValueError(f"bias must be [{shape.n_experts}]")
     n = x.shape[0]
     if idx is None:
         idx = torch.empty((n, shape.top_k), dtype=torch.int32, device=x.device)
@@ -178,13 +188,13 @@ def route(shape, gate_w, x, *, idx=None, w=None, logits=None, margin=None, ws=No
     ws = ws or Workspace(x.device)
     buf = ws.get(need)
     have = C.c_size_t(buf.numel())
-    _check("moe_route", lib.moe_route(C.byref(shape), _ptr(gate_w), _ptr(x), n, _ptr(logits),
-                                      _ptr(idx), _ptr(w), _ptr(margin), _ptr(buf),
-                                      C.byref(have), _stream()))
+    _check("moe_route_biased", lib.moe_route_biased(
+        C.byref(shape), _ptr(gate_w), _ptr(bias), _ptr(x), n, _ptr(logits), _ptr(idx), _ptr(w),
+        _ptr(margin), _ptr(buf), C.byref(have), _stream()))
     return idx, w
 
 
-def _expert_pass(fn, shape, weights, x, idx, w, y, ws, n_unique=None):
+def _expert_pass(fn, shape, weights, x, idx, w, y, ws, n_unique=None, groups=None):
     lib = load()
     keep, cw = _weights(shape, weights)
     x = _dev(x, torch.float32, "x")
@@ -194,16 +204,19 @@ def _expert_pass(fn, shape, weights, x, idx, w, y, ws, n_unique=None):
     if y is None:
         y = torch.empty((n, shape.d_model), dtype=torch.float32, device=x.device)
     _dev(y, torch.float32, "y")
+    # grouped pass: (G, host int32 group_start) after the token count
+    pre = [] if groups is None else [len(groups) - 1, (C.c_int32 * len(groups))(*groups)]
     extra = [] if n_unique is False else [None]
-    need = _need(fn, shape, n, lambda nb: getattr(lib, fn)(
-        C.byref(shape), C.byref(cw), _ptr(x), n, _ptr(idx), _ptr(w), _ptr(y), *extra, None, nb,
-        None))
+    need = _need((fn, None if groups is None else len(groups)), shape, n,
+                 lambda nb: getattr(lib, fn)(
+                     C.byref(shape), C.byref(cw), _ptr(x), n, *pre, _ptr(idx), _ptr(w), _ptr(y),
+                     *extra, None, nb, None))
     ws = ws or Workspace(x.device)
     buf = ws.get(need)
     have = C.c_size_t(buf.numel())
     extra = [] if n_unique is False else [_ptr(n_unique)]
-    _check(fn, getattr(lib, fn)(C.byref(shape), C.byref(cw), _ptr(x), n, _ptr(idx), _ptr(w),
-                                _ptr(y), *extra, _ptr(buf), C.byref(have), _stream()))
+    _check(fn, getattr(lib, fn)(C.byref(shape), C.byref(cw), _ptr(x), n, *pre, _ptr(idx),
+                                _ptr(w), _ptr(y), *extra, _ptr(buf), C.byref(have), _stream()))
     del keep
     return y
 
@@ -220,6 +233,45 @@ def expert_pass_dedup(shape, weights, x, idx, w, *, y=None, n_unique=None, ws=No
     _dev(n_unique, torch.int32, "n_unique")
     return _expert_pass("moe_expert_pass_dedup", shape, weights, x, idx, w, y, ws,
                         n_unique=n_unique)
+
+
+def _group_list(group_start, n):
+    gs = [int(v) for v in group_start]
+    if len(gs) < 2 or len(gs) - 1 > MAX_GROUPS:
+        raise ValueError(f"group_start needs 2 .. {MAX_GROUPS + 1} boundaries")
+    if gs[0] != 0 or gs[-1] != n or any(b <= a for a, b in zip(gs, gs[1:])):
+        raise ValueError(f"group_start must rise strictly from 0 to {n}")
+    return gs
+
+
+def expert_pass_dedup_grouped(shape, weights, x, idx, w, group_start, *, y=None,
+                              n_unique=None, ws=None):
+    """Deduplicating engine inside token groups: group g is tokens
+    group_start[g] .. group_start[g+1]-1 (a host sequence).  n_unique (int32
+    [G] on the GPU) receives U_g."""
+    _dev(n_unique, torch.int32, "n_unique")
+    gs = _group_list(group_start, x.shape[0])
+    if n_unique is not None and n_unique.numel() < len(gs) - 1:
+        raise ValueError("n_unique needs one entry per group")
+    return _expert_pass("moe_expert_pass_dedup_grouped", shape, weights, x, idx, w, y, ws,
+                        n_unique=n_unique, groups=gs)
+
+
+def pass_bytes_grouped(shape, idx_host, group_start):
+    """Requested routed bytes of a grouped dedup pass and U per group:
+    (dedup_bytes, [U_g])."""
+    lib = load()
+    t = torch.as_tensor(idx_host).to(torch.int32).contiguous()
+    if t.is_cuda:
+        raise ValueError("pass_bytes_grouped takes a host routing trace")
+    gs = _group_list(group_start, t.shape[0])
+    G = len(gs) - 1
+    out = C.c_uint64(0)
+    u = (C.c_int32 * G)()
+    _check("moe_pass_bytes_grouped", lib.moe_pass_bytes_grouped(
+        C.byref(shape), C.c_void_p(t.data_ptr()), t.shape[0], G, (C.c_int32 * (G + 1))(*gs),
+        C.byref(out), u))
+    return int(out.value), [int(v) for v in u]
 
 
 def pass_bytes(shape, idx_host):

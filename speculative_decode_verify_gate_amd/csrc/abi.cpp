@@ -52,9 +52,19 @@ size_t route_ws(const moe_shape *s, int n) {
                                sizeof(float), kAlign);
 }
 
+// one compaction record (per token group of the dedup engine)
 size_t cmp_ws(const moe_shape *s, int n) {
   moe::CompactLayout L{s->n_experts, n * s->top_k};
   return align_up((size_t)L.total() * sizeof(int32_t), kAlign);
+}
+
+// Token groups: 1 <= G <= MOE_MAX_GROUPS, gs[0] = 0, gs[G] = n, increasing.
+int check_groups(int32_t n, int32_t G, const int32_t *gs) {
+  if (G < 1 || G > MOE_MAX_GROUPS || !gs) return MOE_ERR_INVALID_ARG;
+  if (gs[0] != 0 || gs[G] != n) return MOE_ERR_INVALID_ARG;
+  for (int g = 0; g < G; ++g)
+    if (gs[g + 1] <= gs[g]) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
 }
 
 size_t abuf_ws(const moe_shape *s, int n) {
@@ -138,15 +148,19 @@ int check_weights(const moe_shape *s, const moe_expert_weights *w) {
   return MOE_OK;
 }
 
+// G token groups with boundaries gs (host) for the dedup engine; G = 1 with
+// gs = {0, n} is the whole pass.
 int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x, int32_t n,
-                const int32_t *idx, const float *tw, float *y, int32_t *n_unique, bool dedup,
-                void *ws, size_t *ws_bytes, void *stream) {
+                int32_t G, const int32_t *gs, const int32_t *idx, const float *tw, float *y,
+                int32_t *n_unique, bool dedup, void *ws, size_t *ws_bytes, void *stream) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
   if ((rc = check_weights(s, w)) != MOE_OK) return rc;
+  if ((rc = check_groups(n, G, gs)) != MOE_OK) return rc;
   if (!x || !idx || !tw || !y) return MOE_ERR_INVALID_ARG;
-  const size_t c_bytes = dedup ? cmp_ws(s, n) : 0;
+  const size_t rec_bytes = cmp_ws(s, n);
+  const size_t c_bytes = dedup ? (size_t)G * rec_bytes : 0;
   const size_t a_bytes = abuf_ws(s, n);
   const size_t need = c_bytes + a_bytes + obuf_ws(s, n);
   bool launch;
@@ -179,7 +193,18 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.dedup = dedup ? 1 : 0;
   a.tiled = w->layout == MOE_LAYOUT_TILED ? 1 : 0;
   const int slots = n * s->top_k;
-  a.n_routed = dedup ? (slots < s->n_experts ? slots : s->n_experts) : slots;
+  a.G = G;
+  a.rec_ints = (int)(rec_bytes / sizeof(int32_t));
+  int routed = 0;
+  for (int g = 0; g < G; ++g) {
+    const int gslots = (gs[g + 1] - gs[g]) * s->top_k;
+    a.gstart[g] = gs[g];
+    a.ibase[g] = routed;
+    routed += gslots < s->n_experts ? gslots : s->n_experts;
+  }
+  a.gstart[G] = gs[G];
+  a.ibase[G] = routed;
+  a.n_routed = dedup ? routed : slots;
 
   hipError_t err = hipSuccess;
   a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true, s->n_experts);
@@ -200,6 +225,13 @@ extern "C" {
 int moe_route(const moe_shape *s, const float *gate_w, const float *x, int32_t n,
               float *logits, int32_t *topk_idx, float *topk_w, float *margin, void *ws,
               size_t *ws_bytes, void *stream) {
+  return moe_route_biased(s, gate_w, nullptr, x, n, logits, topk_idx, topk_w, margin, ws,
+                          ws_bytes, stream);
+}
+
+int moe_route_biased(const moe_shape *s, const float *gate_w, const float *bias,
+                     const float *x, int32_t n, float *logits, int32_t *topk_idx,
+                     float *topk_w, float *margin, void *ws, size_t *ws_bytes, void *stream) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
   if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
@@ -210,6 +242,7 @@ int moe_route(const moe_shape *s, const float *gate_w, const float *x, int32_t n
   hipStream_t st = (hipStream_t)stream;
   moe::RouteArgs a{};
   a.gate_w = gate_w;
+  a.bias = bias;
   a.x = x;
   a.N = n;
   a.d = s->d_model;
@@ -259,13 +292,24 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
 int moe_expert_pass_perslot(const moe_shape *s, const moe_expert_weights *w, const float *x,
                             int32_t n, const int32_t *idx, const float *tw, float *y,
                             void *ws, size_t *ws_bytes, void *stream) {
-  return expert_pass(s, w, x, n, idx, tw, y, nullptr, false, ws, ws_bytes, stream);
+  const int32_t whole[2] = {0, n};
+  return expert_pass(s, w, x, n, 1, whole, idx, tw, y, nullptr, false, ws, ws_bytes, stream);
 }
 
 int moe_expert_pass_dedup(const moe_shape *s, const moe_expert_weights *w, const float *x,
                           int32_t n, const int32_t *idx, const float *tw, float *y,
                           int32_t *n_unique, void *ws, size_t *ws_bytes, void *stream) {
-  return expert_pass(s, w, x, n, idx, tw, y, n_unique, true, ws, ws_bytes, stream);
+  const int32_t whole[2] = {0, n};
+  return expert_pass(s, w, x, n, 1, whole, idx, tw, y, n_unique, true, ws, ws_bytes, stream);
+}
+
+int moe_expert_pass_dedup_grouped(const moe_shape *s, const moe_expert_weights *w,
+                                  const float *x, int32_t n, int32_t n_groups,
+                                  const int32_t *group_start, const int32_t *idx,
+                                  const float *tw, float *y, int32_t *n_unique, void *ws,
+                                  size_t *ws_bytes, void *stream) {
+  return expert_pass(s, w, x, n, n_groups, group_start, idx, tw, y, n_unique, true, ws,
+                     ws_bytes, stream);
 }
 
 int moe_pack_weights(const moe_shape *s, int32_t n_sets, const void *w13_rows,
@@ -317,6 +361,27 @@ int moe_pass_bytes(const moe_shape *s, const int32_t *idx, int32_t n, uint64_t *
   if (dedup) *dedup = (uint64_t)U * be;
   if (shared) *shared = (uint64_t)s->n_shared * be;
   if (n_unique) *n_unique = U;
+  return MOE_OK;
+}
+
+int moe_pass_bytes_grouped(const moe_shape *s, const int32_t *idx, int32_t n, int32_t G,
+                           const int32_t *gs, uint64_t *dedup, int32_t *n_unique) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
+  if ((rc = check_groups(n, G, gs)) != MOE_OK) return rc;
+  if (!idx) return MOE_ERR_INVALID_ARG;
+  uint64_t total = 0;
+  for (int g = 0; g < G; ++g) {
+    uint64_t b = 0;
+    int32_t u = 0;
+    rc = moe_pass_bytes(s, idx + (size_t)gs[g] * s->top_k, gs[g + 1] - gs[g], nullptr, &b,
+                        nullptr, &u);
+    if (rc != MOE_OK) return rc;
+    total += b;
+    if (n_unique) n_unique[g] = u;
+  }
+  if (dedup) *dedup = total;
   return MOE_OK;
 }
 

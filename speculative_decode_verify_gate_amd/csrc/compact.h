@@ -21,14 +21,16 @@
 
 namespace moe {
 
-// The u-th distinct valid expert of idx[0 .. slots) in ascending order, or
-// -1 when there are at most u of them; its entries (slot s = t*k + j, in
+// The u-th distinct valid expert of the routing entries idx[0 .. slots) in
+// ascending order, or -1 when there are at most u of them.  The entries are
+// slots slot0 .. slot0+slots-1 of the pass (a group of whole tokens; slot0
+// is a multiple of k); the expert's entries (slot s = t*k + j, in
 // increasing s) go to ent_row[] (s) and ent_tok[] (s / k), their number to
 // *m.  All threads of the workgroup call it (it contains barriers) and get
 // the same result.  slots <= 2 * blockDim.x.
 template <class Row, class Tok>
-__device__ inline int local_instance(const int32_t *__restrict__ idx, int slots, int E, int k,
-                                     int u, Row *ent_row, Tok *ent_tok, int *m) {
+__device__ inline int local_instance(const int32_t *__restrict__ idx, int slots, int slot0,
+                                     int E, int k, int u, Row *ent_row, Tok *ent_tok, int *m) {
   constexpr int kWords = MOE_MAX_EXPERTS / 32;
   constexpr int kMaxWaves = 16;
   __shared__ uint32_t pres[kWords];
@@ -91,7 +93,7 @@ __device__ inline int local_instance(const int32_t *__restrict__ idx, int slots,
     }
     if (es[p] == e) {
       const int pos = base + before + __popcll(bal[p] & below);
-      const int s = p * nth + tid;
+      const int s = slot0 + p * nth + tid;
       ent_row[pos] = (Row)s;
       ent_tok[pos] = (Tok)(s / k);
     }
@@ -103,13 +105,14 @@ __device__ inline int local_instance(const int32_t *__restrict__ idx, int slots,
   return e;
 }
 
-// The full compaction record of idx (layout CompactLayout, documented in
-// moe_verify.h) and U to *n_unique (if given).  Called by one workgroup;
-// scratch is at least (2 * E + 1 + slots) ints of LDS that the caller does
-// not use meanwhile.  slots <= 2 * blockDim.x.
-__device__ inline void write_record(const int32_t *__restrict__ idx, int slots, int E,
-                                    int32_t *__restrict__ cmp, int32_t *__restrict__ n_unique,
-                                    int *scratch) {
+// The full compaction record of the routing entries idx[0 .. slots), which
+// are slots slot0 .. slot0+slots-1 of the pass (layout CompactLayout,
+// documented in moe_verify.h; the list holds pass slot ids), and U to
+// *n_unique (if given).  Called by one workgroup; scratch is at least
+// (2 * E + 1 + slots) ints of LDS that the caller does not use meanwhile.
+__device__ inline void write_record(const int32_t *__restrict__ idx, int slots, int slot0,
+                                    int E, int32_t *__restrict__ cmp,
+                                    int32_t *__restrict__ n_unique, int *scratch) {
   const CompactLayout L{E, slots};
   int *cnt = scratch;           // [E]
   int *offs = cnt + E;          // [E + 1]
@@ -151,7 +154,7 @@ __device__ inline void write_record(const int32_t *__restrict__ idx, int slots, 
     if (e < 0) continue;
     int rank = 0;
     for (int q = 0; q < s; ++q) rank += (ev[q] == e) ? 1 : 0;
-    cmp[L.list() + offs[e] + rank] = s;
+    cmp[L.list() + offs[e] + rank] = slot0 + s;
   }
   __syncthreads();  // scratch is free again
 }

@@ -5,7 +5,8 @@
 //                    expert is streamed once per (token, slot);
 //   dedup engine:    instance u is the u-th distinct selected expert with all
 //                    the (token, slot) entries that chose it; the expert is
-//                    streamed once per pass;
+//                    streamed once per pass (or once per token group, when
+//                    the pass is split into groups such as sequences);
 //   both engines:    shared expert s is one instance over all N tokens.
 // ("Speculative Decoding for Mixture-of-Experts Models: Expert Bytes, Kernel
 // Bandwidth and the Best Draft Length", abstract; shared experts: "Deep Dive
@@ -131,26 +132,43 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   const size_t fd = (size_t)a.f * (size_t)a.d;
 
   // ---- the instance's expert: one dependent load before the weight stream.
-  // Instances are ordered shared experts first, then routed ones (u-th
-  // distinct expert, or slot u), so the fixed shared work is dispatched
-  // first and the workgroups of absent dedup instances (u >= U) come last.
-  // The dedup up kernel finds its instance in the routing itself (workgroup
-  // 0 also writes the compaction record for the down kernel and the caller);
-  // the down kernel reads it from that record.
+  // Instances are ordered shared experts first, then routed ones (slot u, or
+  // the u-th distinct expert of a token group, groups in order), so the
+  // fixed shared work is dispatched first.  The dedup up kernel finds its
+  // instance in the routing itself (workgroup g < G also writes group g's
+  // compaction record for the down kernel and the caller); the down kernel
+  // reads it from that record.
   int e = -1, shared_s = -1, m = 0;
   bool have_entries = false;
-  const int u = inst - a.S;
-  if (UP && a.dedup && blockIdx.x == 0)
-    write_record(a.idx, a.N * a.k, a.E, a.cmp_out, a.n_unique, (int *)lds);
+  int u = inst - a.S;
+  if (UP && a.dedup && blockIdx.x < a.G) {
+    const int b = blockIdx.x;
+    write_record(a.idx + a.gstart[b] * a.k, (a.gstart[b + 1] - a.gstart[b]) * a.k,
+                 a.gstart[b] * a.k, a.E, a.cmp_out + (size_t)b * a.rec_ints,
+                 a.n_unique ? a.n_unique + b : nullptr, (int *)lds);
+  }
+  int grp = 0;
+  if (a.dedup && a.G > 1 && u >= 0) {
+    // the group whose instance range holds u (bases ascend; ibase[0] = 0)
+    int hi = a.G;
+    while (hi - grp > 1) {
+      const int mid = (grp + hi) >> 1;
+      if (u >= a.ibase[mid]) grp = mid; else hi = mid;
+    }
+    u -= a.ibase[grp];
+  }
+  const int32_t *rec = a.cmp ? a.cmp + (size_t)grp * a.rec_ints : nullptr;
   if (inst < a.S) {
     shared_s = inst;
   } else if (UP && a.dedup) {
-    e = local_instance(a.idx, a.N * a.k, a.E, a.k, u, ent_row, ent_tok, &m);
-    if (e < 0) return;  // past U
+    const int s0 = a.gstart[grp] * a.k;
+    e = local_instance(a.idx + s0, (a.gstart[grp + 1] - a.gstart[grp]) * a.k, s0, a.E, a.k,
+                       u, ent_row, ent_tok, &m);
+    if (e < 0) return;  // past the group's U
     have_entries = true;
   } else {
-    e = a.dedup ? a.cmp[CL.uniq() + u] : a.idx[u];
-    if (e < 0 || e >= a.E) return;  // past U (dedup) or an empty slot
+    e = a.dedup ? rec[CL.uniq() + u] : a.idx[u];
+    if (e < 0 || e >= a.E) return;  // past the group's U (dedup) or an empty slot
   }
   const unsigned char *wA, *wB = nullptr;
   {
@@ -230,10 +248,10 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
       ent_tok[c] = c;
     }
   } else if (a.dedup) {
-    m = a.cmp[CL.counts() + e];
-    const int base = a.cmp[CL.offs() + e];
+    m = rec[CL.counts() + e];
+    const int base = rec[CL.offs() + e];
     for (int c = tid; c < m; c += kBlock) {
-      const int row = a.cmp[CL.list() + base + c];
+      const int row = rec[CL.list() + base + c];
       ent_row[c] = row;
       ent_tok[c] = row / a.k;
     }

@@ -51,6 +51,14 @@ struct ExpertArgs {
                           //    u-th distinct selected expert
   int n_routed;           // routed instances in the grid
   int lds_bytes;          // dynamic LDS per workgroup
+  // Dedup within token groups: tokens gstart[g] .. gstart[g+1]-1 form group
+  // g, whose distinct experts are routed instances ibase[g] .. ibase[g+1]-1
+  // and whose compaction record starts rec_ints int32 after group g-1's.
+  // G = 1 (one group of all N tokens) is the plain dedup engine.
+  int G;
+  int rec_ints;
+  int gstart[MOE_MAX_GROUPS + 1];
+  int ibase[MOE_MAX_GROUPS + 1];
 };
 
 // Routing.  Partial logits of all splits at most this many bytes: one launch
@@ -59,6 +67,7 @@ constexpr int kFusedRouteBytes = 64 * 1024;
 
 struct RouteArgs {
   const float *gate_w, *x;
+  const float *bias;          // [E] added to the logits, or nullptr
   int N, d, E, k, splits;
   float *part;                // [splits][N][E] partial logits
   unsigned *done;             // arrival counter (one launch): zero on entry and exit

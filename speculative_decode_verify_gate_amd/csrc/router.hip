@@ -2,7 +2,10 @@
 //
 // "Deep Dive into Mixture of Experts: From 1991 to DeepSeek-V3", section 2:
 // logits = x @ gate_weights, keep the k largest, weights = softmax of the k
-// selected values.  Ties are broken toward the lower expert index.
+// selected values.  Ties are broken toward the lower expert index.  The
+// DeepSeek-style variant of section 5 adds a per-expert bias to the logits
+// (after the split partials are summed); selection and softmax then take
+// the biased values.
 //
 // The gate GEMM [N x d] x [d x E] streams the fp32 gate matrix once with
 // fp32 MFMA (16 experts x 16 tokens per tile), split over K so that enough
@@ -182,6 +185,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             if (sp0 + u < splits) acc_l += pv[q][u];
+          if (sp0 + 8 >= splits && a.bias) acc_l += a.bias[i % E];
           Ls[i] = acc_l;
         }
       }
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(64) void topk_kernel(RouteArgs a) {
 #pragma unroll
   for (int q = 0; q < kMaxExpertsPerLane; ++q) {
     const int e = q * 64 + lane;
-    if (e < E) Ls[e] = v[q];
+    if (e < E) Ls[e] = a.bias ? v[q] + a.bias[e] : v[q];
   }
   __syncthreads();
   select_topk(Ls, 1, t, a, lane, 64, sel_v, sel_e);

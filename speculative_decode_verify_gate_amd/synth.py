@@ -32,7 +32,10 @@ import numpy as np
 import torch
 
 WEIGHT_STD = 0.02
-T_GATE, T_W13, T_W2, T_WS13, T_WS2 = 0, 1, 2, 3, 4
+T_GATE, T_W13, T_W2, T_WS13, T_WS2, T_BIAS = 0, 1, 2, 3, 4, 5
+# Scale of the synthetic per-expert routing bias: a fraction of the logit
+# spread of a unit-variance token, WEIGHT_STD * sqrt(d).
+BIAS_REL_STD = 0.25
 
 
 @dataclass(frozen=True)
@@ -117,6 +120,22 @@ def make_layer(cfg: LayerConfig, device="cpu", layer: int = 0, E=None):
         lay["ws13"] = _normal_weights((cfg.S, 2, cfg.f, cfg.d), base + T_WS13, device, wdt)
         lay["ws2"] = _normal_weights((cfg.S, cfg.d, cfg.f), base + T_WS2, device, wdt)
     return lay
+
+
+def make_bias(cfg: LayerConfig, device="cpu", layer: int = 0, scale=BIAS_REL_STD):
+    """Per-expert routing bias fp32 [E] for the DeepSeek-style biased gate:
+    N(0, (scale * WEIGHT_STD * sqrt(d))^2), i.e. a set fraction of the
+    spread of the logits.  The pages give no bias values (the bias is tuned
+    during training), so any fixed draw of comparable scale stands in."""
+    g = _gen(cfg.seed * 1000 + layer * 10 + T_BIAS, device)
+    std = scale * WEIGHT_STD * math.sqrt(cfg.d)
+    return (torch.randn((cfg.E,), generator=g, device=device) * std).contiguous()
+
+
+def sequence_groups(cfg: LayerConfig, n: int):
+    """Token boundaries of the cfg.n_seq sequences in a pass of n tokens each
+    (rows s*n .. s*n+n-1 are sequence s): [0, n, 2n, ..., n_seq*n]."""
+    return [s * n for s in range(cfg.n_seq + 1)]
 
 
 def ar1_chain(n, d, rho, gen, device):

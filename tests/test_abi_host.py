@@ -24,7 +24,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for fn in ("moe_route", "moe_expert_pass_perslot", "moe_expert_pass_dedup",
-               "moe_pass_bytes"):
+               "moe_pass_bytes", "moe_route_biased", "moe_expert_pass_dedup_grouped",
+               "moe_pass_bytes_grouped", "moe_verify_gate"):
         assert fn in names
 
 
@@ -173,3 +174,53 @@ def test_verify_gate_validation_and_workspace_query():
     # a workspace smaller than needed
     rc, _ = _verify(ws=FAKE, nbytes=need - 1)
     assert rc == -3
+
+
+def _grouped(shape, n, G, gs, ws=None, nbytes=0, idx=FAKE):
+    lib = B.load()
+    cw = B.Weights(0x100000, 0x100000, 0x100000, 0x100000)
+    sz = C.c_size_t(nbytes)
+    arr = None if gs is None else (C.c_int32 * len(gs))(*gs)
+    rc = lib.moe_expert_pass_dedup_grouped(C.byref(shape), C.byref(cw), FAKE, n, G, arr, idx,
+                                           FAKE, FAKE, None, ws, C.byref(sz), None)
+    return rc, sz.value
+
+
+def test_grouped_dedup_validation_and_workspace():
+    s = _shape(n_experts=256, top_k=8, d_model=7168, d_ff=2048, n_shared=1)
+    n = 64
+    rc1, one = _grouped(s, n, 1, [0, n])
+    assert rc1 == 0
+    sz = C.c_size_t(0)
+    cw = B.Weights(0x100000, 0x100000, 0x100000, 0x100000)
+    assert B.load().moe_expert_pass_dedup(C.byref(s), C.byref(cw), FAKE, n, FAKE, FAKE, FAKE,
+                                          None, None, C.byref(sz), None) == 0
+    assert one == sz.value                      # one group: the dedup workspace
+    rec = ((4 * (3 * 256 + 2 + n * 8)) + 255) // 256 * 256
+    rc4, four = _grouped(s, n, 4, [0, 16, 32, 48, 64])
+    assert rc4 == 0 and four == one + 3 * rec   # one compaction record per group
+    for G, gs in [(0, [0]), (2, [0, 64, 64]), (2, [1, 30, 64]), (2, [0, 30, 63]),
+                  (3, [0, 40, 20, 64]), (65, list(range(66))), (2, None)]:
+        assert _grouped(s, n, G, gs)[0] == -1, gs
+    assert _grouped(s, n, 4, [0, 16, 32, 48, 64], ws=FAKE, nbytes=four - 1)[0] == -3
+
+
+def test_grouped_pass_bytes_matches_oracle():
+    rng = np.random.default_rng(3)
+    for (d, E, k, f, S, wd) in [(256, 8, 2, 512, 0, "f32"), (7168, 256, 8, 2048, 1, "bf16"),
+                                (2048, 64, 6, 1408, 2, "bf16")]:
+        s = B.make_shape(d, E, k, f, S, wd)
+        so = O.Shape(d, E, k, f, S, O.BF16 if wd == "bf16" else O.F32)
+        for n, gs in [(4, [0, 4]), (4, [0, 1, 2, 3, 4]), (16, [0, 4, 8, 12, 16]),
+                      (13, [0, 5, 6, 13]), (64, [0, 16, 32, 48, 64])]:
+            if n * k > 512:
+                continue
+            idx = np.stack([rng.choice(E, k, replace=False) for _ in range(n)]).astype(np.int32)
+            got_b, got_u = B.pass_bytes_grouped(s, idx, gs)
+            # oracle: the plain byte count of each group's own routing
+            ref = [O.pass_bytes(so, idx[gs[g]:gs[g + 1]]) for g in range(len(gs) - 1)]
+            assert got_u == [r[3] for r in ref]
+            assert got_b == sum(r[1] for r in ref)
+            assert B.pass_bytes(s, idx)[1] <= got_b <= B.pass_bytes(s, idx)[0]
+    with pytest.raises(ValueError):
+        B.pass_bytes_grouped(B.make_shape(256, 8, 2, 512), np.zeros((4, 2), np.int32), [0, 2, 3])

@@ -1,0 +1,263 @@
+"""GPU parity of the layer variants against the CPU oracle, through the C ABI.
+
+Biased routing (DeepSeek-style sketch, "Deep Dive into Mixture of Experts:
+From 1991 to DeepSeek-V3", section 5): the bars of plain routing -- indices
+exact on unflagged tokens, logits and margins within 1e-4, weights within
+1e-5.  Grouped dedup: the layer output is bitwise the per-slot engine's, U
+per group and the per-group compaction records are exact, and the output is
+within 1e-2 (bf16) / 1e-5 (fp32) of the oracle's grouped layer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from speculative_decode_verify_gate_amd import binding as B
+from speculative_decode_verify_gate_amd import synth
+from helpers import (LOGIT_ATOL, OUT_RTOL, TIE_EPS, WEIGHT_ATOL, host_layer, oshape, rel_err,
+                     small_config, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- biased routing
+
+def _check_biased_route(cfg, gate_w, bias, x, ws=None):
+    """GPU biased route vs the oracle's on the same bits; returns the number
+    of flagged (near-tie) tokens."""
+    shape = B.shape_of(cfg)
+    n = x.shape[0]
+    logits = torch.empty((n, cfg.E), dtype=torch.float32, device="cuda")
+    margin = torch.empty((n,), dtype=torch.float32, device="cuda")
+    idx, w = B.route(shape, gate_w.cuda(), x.cuda(), bias=bias.cuda(), logits=logits,
+                     margin=margin, ws=ws)
+    torch.cuda.synchronize()
+    ref = O.route(oshape(cfg), gate_w.cpu().numpy(), x.cpu().numpy(), tie_eps=TIE_EPS,
+                  bias=bias.cpu().numpy())
+    assert np.max(np.abs(logits.cpu().numpy() - ref["logits"])) <= LOGIT_ATOL
+    ok = ref["flags"] == 0
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+    assert np.array_equal(gi[ok], ref["idx"][ok]), "biased routing differs on an unflagged token"
+    assert np.all(np.abs(gw[ok] - ref["w"][ok]) <= WEIGHT_ATOL)
+    assert np.all(np.abs(gw.sum(axis=1) - 1.0) <= 1e-6)
+    if cfg.k < cfg.E:
+        assert np.all(np.abs(margin.cpu().numpy()[ok] - ref["margin"][ok]) <= LOGIT_ATOL)
+    return int((~ok).sum())
+
+
+# fused single-launch routing (small partials) and the separate top-k launch
+ROUTE_CASES = [
+    # name, d, E, k, n
+    ("fused-64x6", 512, 64, 6, 16),
+    ("fused-8x2", 256, 8, 2, 3),
+    ("fused-ragged-E", 256, 40, 5, 17),
+    ("topk-256x8", 2048, 256, 8, 64),
+    ("topk-256x8-n1", 7168, 256, 8, 1),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+@pytest.mark.parametrize("scale", [0.25, 2.0])
+def test_biased_route_matches_oracle(case, scale):
+    name, d, E, k, n = case
+    cfg = small_config(name, d, E, k, 64, 0, "bf16")
+    _say(f"[bias] {name} n={n} scale={scale}")
+    gate_w = synth.make_layer(cfg, "cpu")["gate_w"]
+    bias = synth.make_bias(cfg, "cpu", scale=scale)
+    flagged = 0
+    ws = B.Workspace()
+    for rep in range(3):
+        x = synth.make_hidden(cfg, n, rep, "cpu")
+        flagged += _check_biased_route(cfg, gate_w, bias, x, ws=ws)
+        assert int(ws.buf[:4].view(torch.int32).item()) == 0   # arrival counter reset
+    _say(f"   flagged {flagged}")
+
+
+def test_zero_bias_is_the_plain_route():
+    cfg = small_config("zero-bias", 512, 64, 6, 64, 0, "bf16")
+    gate_w = synth.make_layer(cfg, "cuda")["gate_w"]
+    x = synth.make_hidden(cfg, 16, 0, "cuda")
+    shape = B.shape_of(cfg)
+    i0, w0 = B.route(shape, gate_w, x)
+    i1, w1 = B.route(shape, gate_w, x, bias=torch.zeros(cfg.E, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(i0, i1) and torch.equal(w0, w1)
+
+
+@pytest.mark.parametrize("d,E,k,n", [(512, 64, 6, 16), (2048, 256, 8, 64)])
+def test_large_bias_forces_an_expert(d, E, k, n):
+    cfg = small_config("force", d, E, k, 64, 0, "bf16")
+    gate_w = synth.make_layer(cfg, "cuda")["gate_w"]
+    x = synth.make_hidden(cfg, n, 0, "cuda")
+    bias = torch.zeros(E, device="cuda")
+    bias[E - 3] = 1000.0
+    idx, w = B.route(B.shape_of(cfg), gate_w, x, bias=bias)
+    torch.cuda.synchronize()
+    assert bool((idx[:, 0] == E - 3).all())
+    assert bool((w[:, 0] == 1.0).all())      # exp(-1000) is zero in fp32
+
+
+# ---------------------------------------------------------------- grouped dedup
+
+def _records(ws, E, n, k, G):
+    """G compaction records from the head of a grouped dedup workspace."""
+    rec_ints = ((4 * (3 * E + 2 + n * k)) + 255) // 256 * 64
+    buf = ws.buf[: 4 * rec_ints * G].view(torch.int32).cpu().numpy()
+    return [buf[g * rec_ints:(g + 1) * rec_ints] for g in range(G)]
+
+
+def _check_records(recs, idx_np, gs, E, k):
+    for g, rec in enumerate(recs):
+        t0, t1 = gs[g], gs[g + 1]
+        c = O.compact(O.Shape(8, E, k, 8, 0, O.F32), idx_np[t0:t1])
+        U = c["n_unique"]
+        assert rec[0] == U
+        assert np.array_equal(rec[1:1 + E], c["counts"])
+        assert np.array_equal(rec[1 + E:2 + 2 * E], c["offs"])
+        assert np.array_equal(rec[2 + 2 * E:2 + 2 * E + U], c["uniq"])
+        assert (rec[2 + 2 * E + U:2 + 3 * E] == -1).all()
+        # list entries are slot ids of the whole pass
+        ns = (t1 - t0) * k
+        assert np.array_equal(rec[2 + 3 * E:2 + 3 * E + ns], c["list"] + t0 * k)
+
+
+GROUP_CASES = [
+    # name, d, E, k, f, S, wdtype, n, group_start
+    ("bf16-4seq", 512, 64, 6, 352, 2, "bf16", 16, [0, 4, 8, 12, 16]),
+    ("bf16-ragged", 256, 16, 3, 192, 1, "bf16", 17, [0, 1, 5, 12, 17]),
+    ("bf16-wide-2seq", 256, 32, 4, 128, 1, "bf16", 64, [0, 32, 64]),
+    ("f32-3seq", 256, 8, 2, 192, 1, "f32", 9, [0, 3, 6, 9]),
+    ("bf16-top1", 256, 16, 1, 128, 0, "bf16", 6, [0, 2, 6]),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_CASES, ids=[c[0] for c in GROUP_CASES])
+def test_grouped_dedup_matches_oracle(case):
+    name, d, E, k, f, S, wdt, n, gs = case
+    cfg = small_config(name, d, E, k, f, S, wdt)
+    _say(f"[grouped] {name} n={n} groups={gs}")
+    lay = synth.make_layer(cfg, "cpu")
+    host = host_layer(lay)
+    x = synth.make_hidden(cfg, n, 0, "cpu")
+    ref = O.route(oshape(cfg), host["gate_w"], x.numpy())
+    idx_np, w_np = ref["idx"], ref["w"].astype(np.float32)
+    shape = B.shape_of(cfg)
+    x_dev, idx_dev, w_dev = x.cuda(), torch.from_numpy(idx_np).cuda(), torch.from_numpy(w_np).cuda()
+    G = len(gs) - 1
+    for layout in ("rows", "tiled"):
+        lay_dev = to_dev(lay) if layout == "rows" else B.pack_weights(shape, to_dev(lay))
+        y_ps = B.expert_pass_perslot(shape, lay_dev, x_dev, idx_dev, w_dev)
+        nu = torch.full((G,), -7, dtype=torch.int32, device="cuda")
+        ws = B.Workspace()
+        y_g = B.expert_pass_dedup_grouped(shape, lay_dev, x_dev, idx_dev, w_dev, gs,
+                                          n_unique=nu, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_ps), "grouped dedup differs from per-slot"
+        y_o, rb, sb, u_o = O.layer_grouped(oshape(cfg), host["w13"], host["w2"], host["ws13"],
+                                           host["ws2"], x.numpy(), idx_np,
+                                           w_np.astype(np.float64), gs, n_threads=8)
+        assert list(nu.cpu().numpy()) == list(u_o)
+        assert B.pass_bytes_grouped(shape, idx_np, gs) == (rb, list(u_o))
+        _check_records(_records(ws, E, n, k, G), idx_np, gs, E, k)
+        err = rel_err(y_g.cpu().numpy(), y_o)
+        _say(f"   {layout}: U_g={list(u_o)} rel err {err:.3e}")
+        assert err <= OUT_RTOL[wdt]
+
+
+def test_one_group_is_dedup_and_token_groups_are_per_slot():
+    cfg = small_config("limits", 512, 64, 6, 352, 2, "bf16")
+    lay_dev = to_dev(synth.make_layer(cfg, "cpu"))
+    shape = B.shape_of(cfg)
+    n = 12
+    x = synth.make_hidden(cfg, n, 1, "cuda")
+    idx, w = B.route(shape, lay_dev["gate_w"], x)
+    nu1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws_d, ws_g = B.Workspace(), B.Workspace()
+    y_d = B.expert_pass_dedup(shape, lay_dev, x, idx, w, n_unique=nu1, ws=ws_d)
+    nug = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y_1 = B.expert_pass_dedup_grouped(shape, lay_dev, x, idx, w, [0, n], n_unique=nug, ws=ws_g)
+    torch.cuda.synchronize()
+    assert torch.equal(y_1, y_d) and int(nug.item()) == int(nu1.item())
+    L = 4 * (3 * cfg.E + 2 + n * cfg.k)
+    assert torch.equal(ws_g.buf[:L], ws_d.buf[:L])        # the same record
+    nun = torch.zeros(n, dtype=torch.int32, device="cuda")
+    y_n = B.expert_pass_dedup_grouped(shape, lay_dev, x, idx, w, list(range(n + 1)),
+                                      n_unique=nun)
+    y_ps = B.expert_pass_perslot(shape, lay_dev, x, idx, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y_n, y_ps) and bool((nun == cfg.k).all())
+
+
+def test_grouped_workspace_reuse_and_shrinking_passes():
+    cfg = small_config("reuse-g", 256, 32, 4, 128, 1, "bf16")
+    lay = synth.make_layer(cfg, "cpu")
+    host = host_layer(lay)
+    lay_dev = to_dev(lay)
+    shape = B.shape_of(cfg)
+    ws = B.Workspace()
+    for rep, (n, gs) in enumerate([(64, [0, 16, 32, 48, 64]), (9, [0, 4, 9]), (64, [0, 64]),
+                                   (5, [0, 1, 2, 3, 4, 5]), (33, [0, 11, 22, 33])]):
+        x = synth.make_hidden(cfg, n, rep, "cpu")
+        ref = O.route(oshape(cfg), host["gate_w"], x.numpy())
+        idx_np = ref["idx"]
+        nu = torch.zeros(len(gs) - 1, dtype=torch.int32, device="cuda")
+        y_g = B.expert_pass_dedup_grouped(shape, lay_dev, x.cuda(), torch.from_numpy(idx_np).cuda(),
+                                          torch.from_numpy(ref["w"].astype(np.float32)).cuda(),
+                                          gs, n_unique=nu, ws=ws)
+        y_ps = B.expert_pass_perslot(shape, lay_dev, x.cuda(), torch.from_numpy(idx_np).cuda(),
+                                     torch.from_numpy(ref["w"].astype(np.float32)).cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_ps), (rep, n, gs)
+        assert list(nu.cpu().numpy()) == B.pass_bytes_grouped(shape, idx_np, gs)[1]
+
+
+def test_full_v3_per_sequence_dedup():
+    """The DeepSeek-V3-shaped layer, 4 sequences x 16 tokens: per-sequence
+    dedup (4 groups) against the union (1 group) and per-slot, with the oracle
+    on two sampled tokens."""
+    cfg = synth.CONFIGS["v3"]
+    n = 16
+    _say("[grouped] v3 4 x 16")
+    lay_dev = synth.make_layer(cfg, "cuda")
+    x = synth.make_hidden(cfg, n, 0, "cuda")
+    shape = B.shape_of(cfg)
+    idx, w = B.route(shape, lay_dev["gate_w"], x)
+    tiled = B.pack_weights(shape, {k: lay_dev[k] for k in ("w13", "w2", "ws13", "ws2")})
+    gs = synth.sequence_groups(cfg, n)
+    nu = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nu1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y_g = B.expert_pass_dedup_grouped(shape, tiled, x, idx, w, gs, n_unique=nu)
+    y_d = B.expert_pass_dedup(shape, tiled, x, idx, w, n_unique=nu1)
+    y_ps = B.expert_pass_perslot(shape, tiled, x, idx, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y_g, y_ps) and torch.equal(y_d, y_ps)
+    gi = idx.cpu().numpy()
+    b_g, u_g = B.pass_bytes_grouped(shape, gi, gs)
+    so = oshape(cfg)
+    assert list(nu.cpu().numpy()) == u_g == [O.pass_bytes(so, gi[a:b])[3]
+                                             for a, b in zip(gs, gs[1:])]
+    U = int(nu1.item())
+    assert U <= sum(u_g) <= 4 * n * cfg.k
+    _say(f"   U union {U}, per sequence {u_g} (sum {sum(u_g)})")
+    # oracle on tokens 0 and 63 with only the experts they use
+    toks = [0, 63]
+    used = np.unique(gi[toks])
+    host = {"w13": np.zeros((cfg.E, 2, cfg.f, cfg.d), np.uint16),
+            "w2": np.zeros((cfg.E, cfg.d, cfg.f), np.uint16),
+            "ws13": synth.to_host_bits(lay_dev["ws13"]), "ws2": synth.to_host_bits(lay_dev["ws2"])}
+    for e in used:
+        host["w13"][e] = synth.to_host_bits(lay_dev["w13"][e])
+        host["w2"][e] = synth.to_host_bits(lay_dev["w2"][e])
+    xs = x.cpu().numpy()[toks]
+    ws_ = w.cpu().numpy()[toks].astype(np.float64)
+    y_o, _, _, _ = O.layer_grouped(so, host["w13"], host["w2"], host["ws13"], host["ws2"], xs,
+                                   gi[toks], ws_, [0, 1, 2], n_threads=8)
+    err = rel_err(y_g.cpu().numpy()[toks], y_o)
+    _say(f"   rel err {err:.3e}")
+    assert err <= OUT_RTOL["bf16"]
+    del lay_dev, tiled
+    torch.cuda.empty_cache()
