@@ -190,7 +190,7 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.k = s->top_k;
   a.S = s->n_shared;
   a.N = n;
-  a.dedup = dedup ? 1 : 0;
+  a.dedup = dedup ? (G > 1 ? 2 : 1) : 0;
   a.tiled = w->layout == MOE_LAYOUT_TILED ? 1 : 0;
   const int slots = n * s->top_k;
   a.G = G;

@@ -102,7 +102,7 @@ constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 template <bool UP, int CTMAX>
 constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
 
-template <bool BF16, bool UP, int CTMAX, bool TILED>
+template <bool BF16, bool UP, int CTMAX, bool TILED, bool GROUPED>
 __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
   constexpr bool DIRECT = CTMAX == 1;
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
@@ -140,15 +140,21 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   // reads it from that record.
   int e = -1, shared_s = -1, m = 0;
   bool have_entries = false;
+  const int32_t *rec = nullptr;  // the instance's compaction record (dedup down)
+  // The group tables are read only by the grouped instantiation (dedup ==
+  // 2), so the plain engines' prologue has no extra argument loads.
+  constexpr bool grouped = GROUPED;
   int u = inst - a.S;
-  if (UP && a.dedup && blockIdx.x < a.G) {
+  if (UP && a.dedup && blockIdx.x < (grouped ? a.G : 1)) {
     const int b = blockIdx.x;
-    write_record(a.idx + a.gstart[b] * a.k, (a.gstart[b + 1] - a.gstart[b]) * a.k,
-                 a.gstart[b] * a.k, a.E, a.cmp_out + (size_t)b * a.rec_ints,
-                 a.n_unique ? a.n_unique + b : nullptr, (int *)lds);
+    const int t0 = grouped ? a.gstart[b] : 0;
+    const int t1 = grouped ? a.gstart[b + 1] : a.N;
+    write_record(a.idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E,
+                 a.cmp_out + (size_t)b * a.rec_ints, a.n_unique ? a.n_unique + b : nullptr,
+                 (int *)lds);
   }
   int grp = 0;
-  if (a.dedup && a.G > 1 && u >= 0) {
+  if (grouped && u >= 0) {
     // the group whose instance range holds u (bases ascend; ibase[0] = 0)
     int hi = a.G;
     while (hi - grp > 1) {
@@ -157,17 +163,23 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
     }
     u -= a.ibase[grp];
   }
-  const int32_t *rec = a.cmp ? a.cmp + (size_t)grp * a.rec_ints : nullptr;
   if (inst < a.S) {
     shared_s = inst;
   } else if (UP && a.dedup) {
-    const int s0 = a.gstart[grp] * a.k;
-    e = local_instance(a.idx + s0, (a.gstart[grp + 1] - a.gstart[grp]) * a.k, s0, a.E, a.k,
-                       u, ent_row, ent_tok, &m);
+    const int t0 = grouped ? a.gstart[grp] : 0;
+    const int t1 = grouped ? a.gstart[grp + 1] : a.N;
+    e = local_instance(a.idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E, a.k, u, ent_row,
+                       ent_tok, &m);
     if (e < 0) return;  // past the group's U
     have_entries = true;
   } else {
-    e = a.dedup ? rec[CL.uniq() + u] : a.idx[u];
+    // one load either way: the u-th distinct expert of the record, or slot u
+    const int32_t *src = a.idx;
+    if (a.dedup) {
+      rec = a.cmp + (grouped ? (size_t)grp * a.rec_ints : 0);
+      src = rec + CL.uniq();
+    }
+    e = src[u];
     if (e < 0 || e >= a.E) return;  // past the group's U (dedup) or an empty slot
   }
   const unsigned char *wA, *wB = nullptr;
@@ -454,33 +466,36 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   }
 }
 
-template <bool BF16, bool UP, bool TILED>
+template <bool BF16, bool UP, bool TILED, bool GROUPED>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
   const int blocks = (a.n_routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   // allow more than the default 64 KB of dynamic LDS, once per kernel
   static const hipError_t set_wide = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 4, TILED>,
+      (const void *)expert_kernel<BF16, UP, 4, TILED, GROUPED>,
       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   static const hipError_t set_narrow = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 1, TILED>,
+      (const void *)expert_kernel<BF16, UP, 1, TILED, GROUPED>,
       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (set_wide != hipSuccess) return set_wide;
   if (set_narrow != hipSuccess) return set_narrow;
   if (a.N > kTile)
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED>), dim3(blocks), dim3(kBlock),
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED, GROUPED>), dim3(blocks), dim3(kBlock),
                        a.lds_bytes, st, a);
   else
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1, TILED>), dim3(blocks), dim3(kBlock),
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1, TILED, GROUPED>), dim3(blocks), dim3(kBlock),
                        a.lds_bytes, st, a);
   return hipGetLastError();
 }
 
 template <bool BF16, bool UP>
 hipError_t launch_expert(const ExpertArgs &a, hipStream_t st) {
-  return a.tiled ? launch_expert_layout<BF16, UP, true>(a, st)
-                 : launch_expert_layout<BF16, UP, false>(a, st);
+  if (a.dedup == 2)
+    return a.tiled ? launch_expert_layout<BF16, UP, true, true>(a, st)
+                   : launch_expert_layout<BF16, UP, false, true>(a, st);
+  return a.tiled ? launch_expert_layout<BF16, UP, true, false>(a, st)
+                 : launch_expert_layout<BF16, UP, false, false>(a, st);
 }
 
 // Row-major -> tiled, one thread per 16-byte unit of the output.  Unit u of a

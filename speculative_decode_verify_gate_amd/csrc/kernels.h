@@ -48,13 +48,14 @@ struct ExpertArgs {
   int d, f, E, k, S, N;
   int tiled;              // weight layout: 0 row-major, 1 MOE_LAYOUT_TILED
   int dedup;              // 0: instance i is slot i; 1: instance u is the
-                          //    u-th distinct selected expert
+                          //    u-th distinct selected expert; 2: the same
+                          //    within each token group of the tables below
   int n_routed;           // routed instances in the grid
   int lds_bytes;          // dynamic LDS per workgroup
   // Dedup within token groups: tokens gstart[g] .. gstart[g+1]-1 form group
   // g, whose distinct experts are routed instances ibase[g] .. ibase[g+1]-1
   // and whose compaction record starts rec_ints int32 after group g-1's.
-  // G = 1 (one group of all N tokens) is the plain dedup engine.
+  // Read only when dedup == 2; the plain engines run with G = 1.
   int G;
   int rec_ints;
   int gstart[MOE_MAX_GROUPS + 1];
