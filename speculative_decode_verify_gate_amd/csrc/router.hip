@@ -33,28 +33,42 @@ constexpr int kGateWaves = 4;
 constexpr int kGateKPerWave = kGateKPerBlock / kGateWaves;  // 64 = 4 steps of 16
 constexpr int kMaxColTiles = 4;                              // N <= 64
 constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
+constexpr int kFusedRouteLds = 32 * 1024;  // one-launch routing: [N][E] logits in LDS
 
 
-// Top-k + softmax of n_tok tokens whose logits sit in LDS (L[t][E]), by the
-// nth threads of the caller.  Each (token, expert) pair counts the experts
-// that rank before it in the order (logit desc, index asc): a strict total
-// order, so ranks are unique and equal the position a stable descending sort
-// gives.  Ranks 0..k-1 are the selection in slot order; rank k gives the
-// margin.  sel_v / sel_e: LDS [n_tok][MOE_MAX_TOPK + 1].  t0 is the global
-// index of token 0.  Ends with a barrier of the caller's threads.
+// Row length of a token's logits in LDS: E rounded up to whole 16-byte
+// vectors.  The padding holds -inf at indices >= E, which never ranks ahead
+// of a real expert: it is not greater than any logit, and on equality with
+// a -inf logit the lower (real) index wins.
+__host__ __device__ inline int logit_ld(int E) { return (E + 3) & ~3; }
+
+// Top-k + softmax of n_tok tokens whose logits sit in LDS (L[t][ld], ld =
+// logit_ld(E), padded as above), by the nth threads of the caller.  Each
+// (token, expert) pair counts the experts that rank before it in the order
+// (logit desc, index asc): a strict total order, so ranks are unique and
+// equal the position a stable descending sort gives.  The row is read as
+// 16-byte vectors with several in flight.  Ranks 0..k-1 are the selection in
+// slot order; rank k gives the margin.  sel_v / sel_e: LDS [n_tok][MOE_MAX_TOPK
+// + 1].  t0 is the global index of token 0.  Ends with a barrier of the
+// caller's threads.
 __device__ inline void select_topk(const float *L, int n_tok, int t0, const RouteArgs &a,
                                    int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
                                    int (*sel_e)[MOE_MAX_TOPK + 1]) {
   const int E = a.E, k = a.k;
+  const int ld = logit_ld(E);
   for (int p = tid; p < n_tok * E; p += nth) {
     const int t = p / E;
     const int e = p - t * E;
-    const float *row = L + (size_t)t * E;
+    const float *row = L + (size_t)t * ld;
     const float v = row[e];
     int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const float u = row[j];
-      rank += (u > v || (u == v && j < e)) ? 1 : 0;
+#pragma unroll 4
+    for (int j = 0; j < ld; j += 4) {
+      const f32x4 u = *(const f32x4 *)(row + j);
+      rank += (u.x > v || (u.x == v && j < e)) ? 1 : 0;
+      rank += (u.y > v || (u.y == v && j + 1 < e)) ? 1 : 0;
+      rank += (u.z > v || (u.z == v && j + 2 < e)) ? 1 : 0;
+      rank += (u.w > v || (u.w == v && j + 3 < e)) ? 1 : 0;
     }
     if (rank <= k) {
       sel_v[t][rank] = v;
@@ -163,9 +177,14 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
-  extern __shared__ float Ls[];  // [N][E] logits
+  extern __shared__ __align__(16) float Ls[];  // [N][logit_ld(E)] logits
   const int splits = a.splits;
   const int NE = N * E;
+  const int ld = logit_ld(E);
+  for (int i = tid; i < N * (ld - E); i += 256) {
+    const int t = i / (ld - E);
+    Ls[t * ld + E + (i - t * (ld - E))] = -INFINITY;
+  }
   for (int i0 = 0; i0 < NE; i0 += 4 * 256) {
     // the loads of 4 logits x 8 splits are issued before any is summed
     for (int sp0 = 0; sp0 < splits; sp0 += 8) {
@@ -181,12 +200,14 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int i = i0 + q * 256 + tid;
         if (i < NE) {
-          float acc_l = (sp0 == 0) ? 0.f : Ls[i];
+          const int t = i / E;
+          const int e = i - t * E;
+          float acc_l = (sp0 == 0) ? 0.f : Ls[t * ld + e];
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             if (sp0 + u < splits) acc_l += pv[q][u];
-          if (sp0 + 8 >= splits && a.bias) acc_l += a.bias[i % E];
-          Ls[i] = acc_l;
+          if (sp0 + 8 >= splits && a.bias) acc_l += a.bias[e];
+          Ls[t * ld + e] = acc_l;
         }
       }
     }
@@ -197,29 +218,35 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   select_topk(Ls, N, 0, a, tid, blockDim.x, sel_v, sel_e);
 }
 
-// Unfused top-k: one wavefront per token sums its partials in split order.
-__global__ __launch_bounds__(64) void topk_kernel(RouteArgs a) {
+// Unfused top-k, one workgroup per token.  Wave w sums the partials of
+// splits w, w+4, w+8, ... (all loads of a lane issued together: one memory
+// round trip for up to 32 splits); the four wave sums are added in wave
+// order, then every thread ranks at most one expert.
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
+  constexpr int kBatch = 8;  // splits per wave and batch
   const int t = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int N = a.N, E = a.E, splits = a.splits;
-  __shared__ float Ls[MOE_MAX_EXPERTS];
+  const int ld = logit_ld(E);
+  __shared__ __align__(16) float Ls[MOE_MAX_EXPERTS];
+  __shared__ float ws_sum[kGateWaves][MOE_MAX_EXPERTS];
   __shared__ float sel_v[1][MOE_MAX_TOPK + 1];
   __shared__ int sel_e[1][MOE_MAX_TOPK + 1];
   const int n_q = (E + 63) / 64;
   float v[kMaxExpertsPerLane];
 #pragma unroll
   for (int q = 0; q < kMaxExpertsPerLane; ++q) v[q] = 0.f;
-  // Loads of 8 splits (for every expert of the lane) are issued together so
-  // the partials cost one memory round trip per 8 splits.
-  for (int sp0 = 0; sp0 < splits; sp0 += 8) {
-    float pv[kMaxExpertsPerLane][8];
+  for (int sp0 = wave; sp0 < splits; sp0 += kGateWaves * kBatch) {
+    float pv[kMaxExpertsPerLane][kBatch];
 #pragma unroll
     for (int q = 0; q < kMaxExpertsPerLane; ++q) {
       if (q < n_q) {
         const int e = min(q * 64 + lane, E - 1);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int sp = min(sp0 + u, splits - 1);
+        for (int u = 0; u < kBatch; ++u) {
+          const int sp = min(sp0 + u * kGateWaves, splits - 1);
           pv[q][u] = a.part[((size_t)sp * N + t) * E + e];
         }
       }
@@ -228,17 +255,28 @@ __global__ __launch_bounds__(64) void topk_kernel(RouteArgs a) {
     for (int q = 0; q < kMaxExpertsPerLane; ++q)
       if (q < n_q) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (sp0 + u < splits) v[q] += pv[q][u];
+        for (int u = 0; u < kBatch; ++u)
+          if (sp0 + u * kGateWaves < splits) v[q] += pv[q][u];
       }
   }
 #pragma unroll
   for (int q = 0; q < kMaxExpertsPerLane; ++q) {
     const int e = q * 64 + lane;
-    if (e < E) Ls[e] = a.bias ? v[q] + a.bias[e] : v[q];
+    if (e < E) ws_sum[wave][e] = v[q];
   }
   __syncthreads();
-  select_topk(Ls, 1, t, a, lane, 64, sel_v, sel_e);
+  if (tid < ld) {
+    float l = -INFINITY;
+    if (tid < E) {
+      l = ws_sum[0][tid];
+#pragma unroll
+      for (int w = 1; w < kGateWaves; ++w) l += ws_sum[w][tid];
+      if (a.bias) l += a.bias[tid];
+    }
+    Ls[tid] = l;
+  }
+  __syncthreads();
+  select_topk(Ls, 1, t, a, tid, blockDim.x, sel_v, sel_e);
 }
 
 }  // namespace
@@ -246,14 +284,16 @@ __global__ __launch_bounds__(64) void topk_kernel(RouteArgs a) {
 int gate_splits(int d) { return (d + kGateKPerBlock - 1) / kGateKPerBlock; }
 
 bool route_fused(int N, int d, int E) {
-  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes;
+  // the partials that one workgroup sums, and its LDS copy of the logits
+  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes &&
+         (size_t)N * logit_ld(E) * sizeof(float) <= (size_t)kFusedRouteLds;
 }
 
 hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
   const int n_et = (a.E + kTile - 1) / kTile;
   const int blocks = n_et * a.splits;
   if (route_fused(a.N, a.d, a.E)) {
-    const size_t lds = (size_t)a.N * a.E * sizeof(float);
+    const size_t lds = (size_t)a.N * logit_ld(a.E) * sizeof(float);
     hipLaunchKernelGGL(gate_kernel<true>, dim3(blocks), dim3(256), lds, st, a);
   } else {
     hipLaunchKernelGGL(gate_kernel<false>, dim3(blocks), dim3(256), 0, st, a);
@@ -262,7 +302,7 @@ hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_topk(const RouteArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3(a.N), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(a.N), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
