@@ -69,6 +69,69 @@ class Engines:
                                    ws=self.ws_dd)
 
 
+def make_stack(cfg, shape, n_layers):
+    """The weight sets, stored back to back as one stack ([L][...] arrays,
+    MFMA-tiled, packed once) and as per-layer views of it."""
+    wdt = cfg.torch_wdtype
+    E, S, d, f = cfg.E, cfg.S, cfg.d, cfg.f
+    stack = {"gate_w": torch.empty((n_layers, E, d), dtype=torch.float32, device="cuda"),
+             "w13": torch.empty((n_layers, E, 2, f, d), dtype=wdt, device="cuda"),
+             "w2": torch.empty((n_layers, E, d, f), dtype=wdt, device="cuda"),
+             "ws13": torch.empty((n_layers, S, 2, f, d), dtype=wdt, device="cuda") if S else None,
+             "ws2": torch.empty((n_layers, S, d, f), dtype=wdt, device="cuda") if S else None,
+             "layout": "tiled"}
+    for L in range(n_layers):
+        rows = synth.make_layer(cfg, "cuda", layer=L)
+        packed = B.pack_weights(shape, rows)
+        for k in ("gate_w", "w13", "w2", "ws13", "ws2"):
+            if stack[k] is not None:
+                stack[k][L].copy_(packed[k])
+        torch.cuda.synchronize()
+        del rows, packed
+        log(f"[bench] weights {L + 1}/{n_layers} drawn and packed")
+    layers = [{k: (None if stack[k] is None else stack[k][L])
+               for k in ("gate_w", "w13", "w2", "ws13", "ws2")} | {"layout": "tiled"}
+              for L in range(n_layers)]
+    return stack, layers
+
+
+def fused_stack_leg(cfg, stack, n_values, reps, rho=None, rho_index=0):
+    """The whole stack in one fused call per engine (moe_stack_pass: one
+    routing launch for every layer's gate, one up, down and combine launch
+    over every layer's instances), per n: median of `reps` calls on fresh
+    hidden states.  Returns {n: {engine: (stack_us, U per layer)}}."""
+    shape = B.shape_of(cfg)
+    nL = stack["gate_w"].shape[0]
+    out = {}
+    ws = {"perslot": B.Workspace(), "dedup": B.Workspace()}
+    for n in n_values:
+        N = cfg.tokens(n)
+        xs = [synth.make_hidden(cfg, n, rep, "cuda", rho=rho, rho_index=rho_index)
+              for rep in range(reps)]
+        idx = torch.empty((nL, N, cfg.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((nL, N, cfg.k), dtype=torch.float32, device="cuda")
+        y = torch.empty((nL, N, cfg.d), dtype=torch.float32, device="cuda")
+        nu = torch.zeros((reps, nL), dtype=torch.int32, device="cuda")
+        for name in ("perslot", "dedup"):   # warm the workspaces
+            B.stack_pass(shape, stack, xs[0], name, idx=idx, w=w, y=y, ws=ws[name])
+        torch.cuda.synchronize()
+        evs = {"perslot": [], "dedup": []}
+        hold_gpu(0.05 * reps)
+        for rep in range(reps):
+            for name in ("perslot", "dedup"):
+                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record()
+                B.stack_pass(shape, stack, xs[rep], name, idx=idx, w=w, y=y,
+                             n_unique=nu[rep] if name == "dedup" else None, ws=ws[name])
+                e1.record()
+                evs[name].append((e0, e1))
+        torch.cuda.synchronize()
+        out[n] = {name: float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs[name]]))
+                  for name in evs}
+        out[n]["U"] = nu.cpu().numpy().astype(np.float64)
+    return out
+
+
 def hold_gpu(ms):
     """Keep the current stream busy for about `ms` milliseconds (a spin
     kernel), so that work queued behind it starts back to back."""
@@ -300,12 +363,13 @@ def calibration_json(calib):
                            for n, rec in calib["per_n"].items()}}
 
 
-def rho_sweep(cfg, eng, layers, calib, reps):
+def rho_sweep(cfg, eng, layers, stack, calib, reps):
     """The layer stack at each rho: per (rho, n), `reps` stack passes per
     engine, each pass running every layer on the same hidden states (route
     + expert pass per layer).  A route-only stack pass is timed too, so the
     expert-pass share is the difference.  U is read from the dedup engine's
-    device counter of every layer pass."""
+    device counter of every layer pass.  The same passes are then timed as
+    one fused stack call per engine (moe_stack_pass)."""
     nL = len(layers)
     Be = expert_bytes(cfg)
     out = []
@@ -349,6 +413,14 @@ def rho_sweep(cfg, eng, layers, calib, reps):
             ps = (med["perslot"] - med["route"]) / nL
             dd = (med["dedup"] - med["route"]) / nL
             r, r_sd, sav, sav_sd = predict_from_calibration(cfg, calib, n, u_bar)
+            fz = fused_stack_leg(cfg, stack, [n], reps, rho=rho, rho_index=ri)[n]
+            rec_fused = {"perslot_stack_us": round(fz["perslot"], 1),
+                         "dedup_stack_us": round(fz["dedup"], 1),
+                         "perslot_layer_us": round(fz["perslot"] / nL, 2),
+                         "dedup_layer_us": round(fz["dedup"] / nL, 2),
+                         "U_mean": round(float(fz["U"].mean()), 2),
+                         "perslot_GBs": round((N * cfg.k + cfg.S) * Be * nL / fz["perslot"] / 1e3, 1),
+                         "dedup_GBs": round((fz["U"].mean() + cfg.S) * Be * nL / fz["dedup"] / 1e3, 1)}
             rec = {"n": n, "u_bar": round(u_bar, 4), "U_mean": round(float(U.mean()), 2),
                    "stack_us": {k: round(v, 1) for k, v in med.items()},
                    "perslot_layer_us": round(ps, 2), "dedup_layer_us": round(dd, 2),
@@ -358,10 +430,13 @@ def rho_sweep(cfg, eng, layers, calib, reps):
                    "r": round(r, 4), "r_sd": round(r_sd, 4),
                    "predicted_saving_us": round(sav, 2),
                    "predicted_saving_sd_us": round(sav_sd, 2),
-                   "dedup_faster": dd < ps, "u_lt_r": u_bar < r}
+                   "dedup_faster": dd < ps, "u_lt_r": u_bar < r,
+                   "fused": rec_fused}
             recs.append(rec)
             log(f"  rho={rho:.2f} n={n:2d} u={u_bar:.3f} r={r:.3f} per-layer ps {ps:7.1f} "
-                f"dd {dd:7.1f} us, saving {ps - dd:6.1f} (pred {sav:6.1f} +- {sav_sd:.1f})")
+                f"dd {dd:7.1f} us, saving {ps - dd:6.1f} (pred {sav:6.1f} +- {sav_sd:.1f}); "
+                f"fused stack per layer ps {rec_fused['perslot_layer_us']:7.1f} "
+                f"dd {rec_fused['dedup_layer_us']:7.1f} us (with routing)")
         out.append({"rho": rho, "passes_per_n": reps, "layers": nL, "by_n": recs,
                     "crossover": {"measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in recs]),
                                   "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_lt_r"] for r in recs])}})
@@ -612,15 +687,8 @@ def main():
                                max(2, min(8, int(8e9 // layer_bytes))))
     log(f"[bench] {cfg.name}: {n_layers} weight sets of {layer_bytes / 1e9:.2f} GB, "
         f"timed step n={n_head}")
-    layers = []
     shape = B.shape_of(cfg)
-    for L in range(n_layers):
-        rows = synth.make_layer(cfg, "cuda", layer=L)
-        # resident weights are kept in the MFMA-tiled layout (packed once)
-        layers.append(B.pack_weights(shape, rows))
-        torch.cuda.synchronize()
-        del rows
-        log(f"[bench] weights {L + 1}/{n_layers} drawn and packed")
+    stack, layers = make_stack(cfg, shape, n_layers)
     eng = Engines(cfg)
 
     if args.variants:
@@ -660,7 +728,7 @@ def main():
                            f"({n_layers * layer_bytes / 1e9:.1f} GB of weights), "
                            f"n = 1..{max(cfg.n_values)}",
                "single_layer_sweep": sweep, "calibration": calibration_json(calib),
-               "by_rho": rho_sweep(cfg, eng, layers, calib, args.stack_reps)}
+               "by_rho": rho_sweep(cfg, eng, layers, stack, calib, args.stack_reps)}
         print(json.dumps(doc), flush=True)
         return
 
@@ -691,6 +759,16 @@ def main():
     achieved = up_bytes / (up_ms * 1e-3) / 1e9 if up_ms > 0 else None
     traffic = traffic_record("expert_up", cfg.name)
 
+    # The same rotation as one fused stack call per engine (all layers on the
+    # step's tokens): per-layer time including routing.
+    log("[bench] fused stack over the rotation")
+    fz = fused_stack_leg(cfg, stack, [n_head], 16)[n_head]
+    fused = {"layers": n_layers, "tokens": N,
+             "perslot_stack_us": round(fz["perslot"], 1), "dedup_stack_us": round(fz["dedup"], 1),
+             "perslot_us_per_layer": round(fz["perslot"] / n_layers, 2),
+             "dedup_us_per_layer": round(fz["dedup"] / n_layers, 2),
+             "U_mean": round(float(fz["U"].mean()), 2)}
+
     engines_at_head = None
     if sweep is not None:
         rec = next(r for r in sweep if r["n"] == n_head)
@@ -717,6 +795,7 @@ def main():
                    "tokens": N, "weight_sets_rotated": n_layers,
                    "weight_layout": "MFMA-tiled (packed once)"},
         "engines_at_step_n": engines_at_head,
+        "fused_stack": fused,
         "step_bytes": int(step_bytes),
         "roofline": {"bound": "hbm", "kernel": "expert_up (W1/W3 + SwiGLU)",
                      "achieved": None if achieved is None else round(achieved, 1),
@@ -743,7 +822,7 @@ def main():
         out["verify_gate"] = verify_gate_leg()
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
-        del layers
+        del layers, stack
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

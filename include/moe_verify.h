@@ -71,9 +71,14 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_SHARED 4
 #define MOE_MAX_GROUPS 64  /* token groups of a grouped dedup pass */
+#define MOE_MAX_LAYERS 64  /* layers of one moe_stack_pass call */
 #define MOE_MAX_SEQ 64     /* sequences per verification-round call */
 #define MOE_MAX_DRAFT 63   /* drafted tokens per sequence and round */
 #define MOE_MAX_VOCAB (1 << 24)
+
+/* Engines of moe_stack_pass. */
+#define MOE_ENGINE_PERSLOT 0
+#define MOE_ENGINE_DEDUP 1
 
 /* Verification-round modes (moe_verify_gate). */
 #define MOE_VERIFY_GREEDY 0
@@ -210,6 +215,44 @@ int moe_expert_pass_dedup_grouped(const moe_shape *shape, const moe_expert_weigh
                                   const int32_t *group_start, const int32_t *topk_idx,
                                   const float *topk_w, float *y, int32_t *n_unique,
                                   void *workspace, size_t *workspace_bytes, void *stream);
+
+/* A stack of L layers of one shape, each array holding the layers back to
+ * back (device pointers):
+ *   gate_w [L][E][d] fp32;  bias [L][E] fp32 or NULL (moe_route_biased's
+ *   bias per layer);  w13 [L][E][2][f][d], w2 [L][E][d][f], ws13
+ *   [L][S][2][f][d], ws2 [L][S][d][f] (NULL iff S == 0), element type
+ *   wdtype, all in `layout`. */
+typedef struct moe_stack_weights {
+  const float *gate_w;
+  const float *bias;
+  const void *w13;
+  const void *w2;
+  const void *ws13;
+  const void *ws2;
+  int32_t layout;
+} moe_stack_weights;
+
+/* One verify pass of the same N tokens through every layer of a stack of
+ * L independent MoE layers (1 <= L <= MOE_MAX_LAYERS), fused: one routing
+ * launch for all L gates, then one up, one down and one combine launch over
+ * every layer's expert instances ("Speculative Decoding for Mixture-of-
+ * Experts Models", abstract: a pass's step time is its bytes over the
+ * kernels' bandwidth plus a fixed time, which the fused launches pay once
+ * per stack instead of once per layer).  Layer l computes exactly what
+ * moe_route_biased (moe_route when bias is NULL) followed by the chosen
+ * engine's expert pass computes on layer l's weights, bit for bit.
+ *   x         [N][d] fp32 device, the input of every layer
+ *   engine    MOE_ENGINE_PERSLOT or MOE_ENGINE_DEDUP
+ *   topk_idx  [L][N][k] int32 device output, topk_w [L][N][k] fp32 output
+ *   y         [L][N][d] fp32 device output
+ *   n_unique  [L] int32 device output (dedup), or NULL
+ * Workspace: route part first (the first 256 bytes must be zero before the
+ * first use, as for moe_route, and are left zero), then the expert-pass
+ * part; query and errors as for the other calls. */
+int moe_stack_pass(const moe_shape *shape, int32_t n_layers, const moe_stack_weights *weights,
+                   const float *x, int32_t n_tokens, int32_t engine, int32_t *topk_idx,
+                   float *topk_w, float *y, int32_t *n_unique, void *workspace,
+                   size_t *workspace_bytes, void *stream);
 
 /* Requested expert bytes of one pass, on the host (same abstract: step time
  * is the bytes each kernel requests over its effective bandwidth).

@@ -19,6 +19,8 @@ KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine", "verify")
 VERIFY_GREEDY, VERIFY_SAMPLING = 0, 1
 MAX_SEQ, MAX_DRAFT, MAX_VOCAB = 64, 63, 1 << 24
 MAX_GROUPS = 64
+MAX_LAYERS = 64
+ENGINE_PERSLOT, ENGINE_DEDUP = 0, 1
 
 _lib = None
 
@@ -39,6 +41,12 @@ class Weights(C.Structure):
                 ("ws2", C.c_void_p), ("layout", C.c_int32)]
 
 
+class StackWeights(C.Structure):
+    _fields_ = [("gate_w", C.c_void_p), ("bias", C.c_void_p), ("w13", C.c_void_p),
+                ("w2", C.c_void_p), ("ws13", C.c_void_p), ("ws2", C.c_void_p),
+                ("layout", C.c_int32)]
+
+
 LAYOUTS = {"rows": 0, "tiled": 1}
 
 
@@ -56,6 +64,7 @@ def load():
     lib.moe_route_biased.argtypes = [P, P, P, P, i32, P, P, P, P, P, sz, P]
     lib.moe_expert_pass_dedup_grouped.argtypes = [P, P, P, i32, i32, P, P, P, P, P, P, sz, P]
     lib.moe_pass_bytes_grouped.argtypes = [P, P, i32, i32, P, P, P]
+    lib.moe_stack_pass.argtypes = [P, i32, P, P, i32, i32, P, P, P, P, P, sz, P]
     lib.moe_expert_pass_perslot.argtypes = [P, P, P, i32, P, P, P, P, sz, P]
     lib.moe_expert_pass_dedup.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
     lib.moe_pass_bytes.argtypes = [P, P, i32, P, P, P, P]
@@ -67,7 +76,8 @@ def load():
     lib.moe_verify_gate.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
     for fn in ("moe_route", "moe_route_biased", "moe_expert_pass_perslot",
                "moe_expert_pass_dedup", "moe_expert_pass_dedup_grouped", "moe_pass_bytes",
-               "moe_pass_bytes_grouped", "moe_pack_weights", "moe_timing_enable",
+               "moe_pass_bytes_grouped", "moe_stack_pass", "moe_pack_weights",
+               "moe_timing_enable",
                "moe_timing_read", "moe_verify_gate"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
@@ -255,6 +265,51 @@ def expert_pass_dedup_grouped(shape, weights, x, idx, w, group_start, *, y=None,
         raise ValueError("n_unique needs one entry per group")
     return _expert_pass("moe_expert_pass_dedup_grouped", shape, weights, x, idx, w, y, ws,
                         n_unique=n_unique, groups=gs)
+
+
+def stack_pass(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=None, ws=None):
+    """One pass of the same tokens x through every layer of a stack, fused
+    (moe_stack_pass).  stack: dict with gate_w fp32 [L][E][d], optional bias
+    fp32 [L][E], w13 [L][E][2][f][d], w2 [L][E][d][f] (ws13 / ws2 [L][S]...
+    with shared experts) and layout.  engine: "perslot" or "dedup".
+    Returns (idx int32 [L][N][k], w fp32 [L][N][k], y fp32 [L][N][d]);
+    n_unique (int32 [L] on the GPU) receives U per layer."""
+    lib = load()
+    eng = {"perslot": ENGINE_PERSLOT, "dedup": ENGINE_DEDUP}[engine]
+    wdt = torch.bfloat16 if shape.wdtype == MOE_BF16 else torch.float32
+    gate_w = _dev(stack["gate_w"], torch.float32, "gate_w")
+    L = gate_w.shape[0]
+    bias = _dev(stack.get("bias"), torch.float32, "bias")
+    keep = [gate_w, bias] + [_dev(stack.get(k), wdt, k) for k in ("w13", "w2", "ws13", "ws2")]
+    for t, want in ((keep[2], (L, shape.n_experts, 2, shape.d_ff, shape.d_model)),
+                    (keep[3], (L, shape.n_experts, shape.d_model, shape.d_ff)),
+                    (gate_w, (L, shape.n_experts, shape.d_model))):
+        if tuple(t.shape) != want:
+            raise ValueError(f"stack array of shape {tuple(t.shape)}, expected {want}")
+    if bias is not None and tuple(bias.shape) != (L, shape.n_experts):
+        raise ValueError(f"bias must be [{L}][{shape.n_experts}]")
+    cw = StackWeights(*[None if t is None else t.data_ptr() for t in keep],
+                      LAYOUTS[stack.get("layout", "rows")])
+    x = _dev(x, torch.float32, "x")
+    n = x.shape[0]
+    dev = x.device
+    idx = torch.empty((L, n, shape.top_k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((L, n, shape.top_k), dtype=torch.float32, device=dev) if w is None else w
+    y = torch.empty((L, n, shape.d_model), dtype=torch.float32, device=dev) if y is None else y
+    _dev(idx, torch.int32, "idx"), _dev(w, torch.float32, "w"), _dev(y, torch.float32, "y")
+    _dev(n_unique, torch.int32, "n_unique")
+    key = ("moe_stack_pass", L, eng)
+    need = _need(key, shape, n, lambda nb: lib.moe_stack_pass(
+        C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y), None,
+        None, nb, None))
+    ws = ws or Workspace(dev)
+    buf = ws.get(need)
+    have = C.c_size_t(buf.numel())
+    _check("moe_stack_pass", lib.moe_stack_pass(
+        C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y),
+        _ptr(n_unique), _ptr(buf), C.byref(have), _stream()))
+    del keep
+    return idx, w, y
 
 
 def pass_bytes_grouped(shape, idx_host, group_start):

@@ -47,8 +47,10 @@ size_t entry_rows(const moe_shape *s, int n) {
 }
 
 // [arrival counter | partial logits [splits][N][E]]
-size_t route_ws(const moe_shape *s, int n) {
-  return kAlign + align_up((size_t)moe::gate_splits(s->d_model) * n * s->n_experts *
+// [arrival counters (one per layer, in 256 bytes) | partial logits
+//  [L][splits][N][E]]
+size_t route_ws(const moe_shape *s, int n, int L = 1) {
+  return kAlign + align_up((size_t)L * moe::gate_splits(s->d_model) * n * s->n_experts *
                                sizeof(float), kAlign);
 }
 
@@ -148,33 +150,38 @@ int check_weights(const moe_shape *s, const moe_expert_weights *w) {
   return MOE_OK;
 }
 
-// G token groups with boundaries gs (host) for the dedup engine; G = 1 with
-// gs = {0, n} is the whole pass.
-int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x, int32_t n,
-                int32_t G, const int32_t *gs, const int32_t *idx, const float *tw, float *y,
-                int32_t *n_unique, bool dedup, void *ws, size_t *ws_bytes, void *stream) {
-  int rc = check_shape(s);
-  if (rc != MOE_OK) return rc;
-  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
-  if ((rc = check_weights(s, w)) != MOE_OK) return rc;
-  if ((rc = check_groups(n, G, gs)) != MOE_OK) return rc;
-  if (!x || !idx || !tw || !y) return MOE_ERR_INVALID_ARG;
-  const size_t rec_bytes = cmp_ws(s, n);
-  const size_t c_bytes = dedup ? (size_t)G * rec_bytes : 0;
-  const size_t a_bytes = abuf_ws(s, n);
-  const size_t need = c_bytes + a_bytes + obuf_ws(s, n);
-  bool launch;
-  if ((rc = workspace_gate(ws, ws_bytes, need, &launch)) != MOE_OK || !launch) return rc;
+// Expert-pass workspace: [G * L compaction records (dedup) | abuf of every
+// layer | obuf of every layer].
+size_t expert_ws(const moe_shape *s, int n, int G, int L, bool dedup) {
+  return (dedup ? (size_t)G * L * cmp_ws(s, n) : 0) + (size_t)L * abuf_ws(s, n) +
+         (size_t)L * obuf_ws(s, n);
+}
 
-  hipStream_t st = (hipStream_t)stream;
+// Weights of L layers: layer l at l * (bytes of one layer's array).
+struct LayerWeights {
+  const void *w13, *w2, *ws13, *ws2;
+  int layout;
+};
+
+// Launches up, down and combine for L layers (L = 1: one layer) on the
+// routing idx / tw ([L][N][k]); G token groups with boundaries gs (host) for
+// the dedup engine (G = 1 with gs = {0, n}: the whole pass; L > 1 needs
+// G = 1).  Arguments are already validated and ws is big enough.
+int launch_pass(const moe_shape *s, const LayerWeights &w, int L, const float *x, int32_t n,
+                int32_t G, const int32_t *gs, const int32_t *idx, const float *tw, float *y,
+                int32_t *n_unique, bool dedup, void *ws, hipStream_t st) {
+  const size_t rec_bytes = cmp_ws(s, n);
+  const size_t c_bytes = dedup ? (size_t)G * L * rec_bytes : 0;
+  const size_t a_bytes = (size_t)L * abuf_ws(s, n);
   unsigned char *base = (unsigned char *)ws;
   const bool bf16 = s->wdtype == MOE_BF16;
+  const size_t fd = (size_t)s->d_model * s->d_ff * wbytes(s);
 
   moe::ExpertArgs a{};
-  a.w13 = w->w13;
-  a.w2 = w->w2;
-  a.ws13 = w->ws13;
-  a.ws2 = w->ws2;
+  a.w13 = w.w13;
+  a.w2 = w.w2;
+  a.ws13 = w.ws13;
+  a.ws2 = w.ws2;
   a.x = x;
   a.idx = idx;
   a.w = tw;
@@ -191,7 +198,7 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.S = s->n_shared;
   a.N = n;
   a.dedup = dedup ? (G > 1 ? 2 : 1) : 0;
-  a.tiled = w->layout == MOE_LAYOUT_TILED ? 1 : 0;
+  a.tiled = w.layout == MOE_LAYOUT_TILED ? 1 : 0;
   const int slots = n * s->top_k;
   a.G = G;
   a.rec_ints = (int)(rec_bytes / sizeof(int32_t));
@@ -205,6 +212,11 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   a.gstart[G] = gs[G];
   a.ibase[G] = routed;
   a.n_routed = dedup ? routed : slots;
+  a.L = L;
+  a.lw13 = 2 * fd * s->n_experts;
+  a.lw2 = fd * s->n_experts;
+  a.lws13 = 2 * fd * s->n_shared;
+  a.lws2 = fd * s->n_shared;
 
   hipError_t err = hipSuccess;
   a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true, s->n_experts);
@@ -215,6 +227,54 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   }
   if (err == hipSuccess)
     err = timed(MOE_K_COMBINE, st, [&] { return moe::launch_combine(a, st); });
+  return status_of(err);
+}
+
+// G token groups with boundaries gs (host) for the dedup engine; G = 1 with
+// gs = {0, n} is the whole pass.
+int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x, int32_t n,
+                int32_t G, const int32_t *gs, const int32_t *idx, const float *tw, float *y,
+                int32_t *n_unique, bool dedup, void *ws, size_t *ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
+  if ((rc = check_weights(s, w)) != MOE_OK) return rc;
+  if ((rc = check_groups(n, G, gs)) != MOE_OK) return rc;
+  if (!x || !idx || !tw || !y) return MOE_ERR_INVALID_ARG;
+  bool launch;
+  if ((rc = workspace_gate(ws, ws_bytes, expert_ws(s, n, G, 1, dedup), &launch)) != MOE_OK ||
+      !launch)
+    return rc;
+  const LayerWeights lw{w->w13, w->w2, w->ws13, w->ws2, w->layout};
+  return launch_pass(s, lw, 1, x, n, G, gs, idx, tw, y, n_unique, dedup, ws,
+                     (hipStream_t)stream);
+}
+
+// Gate + top-k + softmax for L layers (gate_w [L][E][d], bias [L][E] or
+// NULL, outputs [L][N][...]); ws holds route_ws(s, n, L) bytes with the
+// arrival counters zero.
+int launch_route(const moe_shape *s, int L, const float *gate_w, const float *bias,
+                 const float *x, int32_t n, float *logits, int32_t *idx, float *tw,
+                 float *margin, void *ws, hipStream_t st) {
+  moe::RouteArgs a{};
+  a.gate_w = gate_w;
+  a.bias = bias;
+  a.x = x;
+  a.N = n;
+  a.d = s->d_model;
+  a.E = s->n_experts;
+  a.k = s->top_k;
+  a.L = L;
+  a.splits = moe::gate_splits(s->d_model);
+  a.done = (unsigned *)ws;
+  a.part = (float *)((unsigned char *)ws + kAlign);
+  a.logits = logits;
+  a.idx = idx;
+  a.w = tw;
+  a.margin = margin;
+  hipError_t err = timed(MOE_K_GATE, st, [&] { return moe::launch_gate(a, st); });
+  if (err == hipSuccess && !moe::route_fused(n, s->d_model, s->n_experts))
+    err = timed(MOE_K_TOPK, st, [&] { return moe::launch_topk(a, st); });
   return status_of(err);
 }
 
@@ -239,26 +299,35 @@ int moe_route_biased(const moe_shape *s, const float *gate_w, const float *bias,
   bool launch;
   if ((rc = workspace_gate(ws, ws_bytes, route_ws(s, n), &launch)) != MOE_OK || !launch)
     return rc;
+  return launch_route(s, 1, gate_w, bias, x, n, logits, topk_idx, topk_w, margin, ws,
+                      (hipStream_t)stream);
+}
+
+int moe_stack_pass(const moe_shape *s, int32_t L, const moe_stack_weights *w, const float *x,
+                   int32_t n, int32_t engine, int32_t *topk_idx, float *topk_w, float *y,
+                   int32_t *n_unique, void *ws, size_t *ws_bytes, void *stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if ((rc = check_tokens(s, n)) != MOE_OK) return rc;
+  if (L < 1 || L > MOE_MAX_LAYERS) return MOE_ERR_INVALID_ARG;
+  if (engine != MOE_ENGINE_PERSLOT && engine != MOE_ENGINE_DEDUP) return MOE_ERR_INVALID_ARG;
+  if (!w || !w->gate_w || !x || !topk_idx || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  const moe_expert_weights ew{w->w13, w->w2, w->ws13, w->ws2, w->layout};
+  if ((rc = check_weights(s, &ew)) != MOE_OK) return rc;
+  const bool dedup = engine == MOE_ENGINE_DEDUP;
+  const size_t r_bytes = route_ws(s, n, L);
+  bool launch;
+  if ((rc = workspace_gate(ws, ws_bytes, r_bytes + expert_ws(s, n, 1, L, dedup), &launch)) !=
+          MOE_OK ||
+      !launch)
+    return rc;
   hipStream_t st = (hipStream_t)stream;
-  moe::RouteArgs a{};
-  a.gate_w = gate_w;
-  a.bias = bias;
-  a.x = x;
-  a.N = n;
-  a.d = s->d_model;
-  a.E = s->n_experts;
-  a.k = s->top_k;
-  a.splits = moe::gate_splits(s->d_model);
-  a.done = (unsigned *)ws;
-  a.part = (float *)((unsigned char *)ws + kAlign);
-  a.logits = logits;
-  a.idx = topk_idx;
-  a.w = topk_w;
-  a.margin = margin;
-  hipError_t err = timed(MOE_K_GATE, st, [&] { return moe::launch_gate(a, st); });
-  if (err == hipSuccess && !moe::route_fused(n, s->d_model, s->n_experts))
-    err = timed(MOE_K_TOPK, st, [&] { return moe::launch_topk(a, st); });
-  return status_of(err);
+  rc = launch_route(s, L, w->gate_w, w->bias, x, n, nullptr, topk_idx, topk_w, nullptr, ws, st);
+  if (rc != MOE_OK) return rc;
+  const int32_t whole[2] = {0, n};
+  const LayerWeights lw{w->w13, w->w2, w->ws13, w->ws2, w->layout};
+  return launch_pass(s, lw, L, x, n, 1, whole, topk_idx, topk_w, y, n_unique, dedup,
+                     (unsigned char *)ws + r_bytes, st);
 }
 
 int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,

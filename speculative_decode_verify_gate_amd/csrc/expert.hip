@@ -102,7 +102,11 @@ constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 template <bool UP, int CTMAX>
 constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
 
-template <bool BF16, bool UP, int CTMAX, bool TILED, bool GROUPED>
+// Kernel variants: the plain engines, dedup within token groups, and a stack
+// of layers (all layers' instances in one grid, layer-major).
+constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
+
+template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
 __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
   constexpr bool DIRECT = CTMAX == 1;
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
@@ -121,8 +125,41 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   const int R = UP ? a.f : a.d;  // output rows
   const int K = UP ? a.d : a.f;  // reduction length
   const int RT = R / kTile;      // 16-row tiles per instance
-  const int inst = blockIdx.x / RT;
-  const int rt = blockIdx.x - inst * RT;
+  // A stack runs each layer's grid in turn: its own weights, routing,
+  // compaction record, U and buffers; the tokens are shared.  Only the stack
+  // instantiation offsets the per-layer arrays.
+  int bid = blockIdx.x;
+  int layer = 0;
+  if (VAR == kStack) {
+    const int bpl = (a.n_routed + a.S) * RT;
+    layer = bid / bpl;
+    bid -= layer * bpl;
+  }
+  const int32_t *idx = a.idx;
+  const int32_t *cmp = a.cmp;
+  int32_t *cmp_out = a.cmp_out;
+  int32_t *n_unique = a.n_unique;
+  const unsigned char *w13 = (const unsigned char *)a.w13;
+  const unsigned char *w2 = (const unsigned char *)a.w2;
+  const unsigned char *ws13 = (const unsigned char *)a.ws13;
+  const unsigned char *ws2 = (const unsigned char *)a.ws2;
+  unsigned char *abuf = (unsigned char *)a.abuf;
+  float *obuf = a.obuf;
+  if (VAR == kStack) {
+    const size_t rows = (size_t)a.N * (a.k + a.S);
+    idx += (size_t)layer * a.N * a.k;
+    if (cmp) cmp += (size_t)layer * a.rec_ints;
+    if (cmp_out) cmp_out += (size_t)layer * a.rec_ints;
+    if (n_unique) n_unique += layer;
+    w13 += (size_t)layer * a.lw13;
+    w2 += (size_t)layer * a.lw2;
+    if (ws13) ws13 += (size_t)layer * a.lws13;
+    if (ws2) ws2 += (size_t)layer * a.lws2;
+    abuf += (size_t)layer * rows * a.f * EB;
+    obuf += (size_t)layer * rows * a.d;
+  }
+  const int inst = bid / RT;
+  const int rt = bid - inst * RT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -143,14 +180,14 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   const int32_t *rec = nullptr;  // the instance's compaction record (dedup down)
   // The group tables are read only by the grouped instantiation (dedup ==
   // 2), so the plain engines' prologue has no extra argument loads.
-  constexpr bool grouped = GROUPED;
+  constexpr bool grouped = VAR == kGrouped;
   int u = inst - a.S;
-  if (UP && a.dedup && blockIdx.x < (grouped ? a.G : 1)) {
-    const int b = blockIdx.x;
+  if (UP && a.dedup && bid < (grouped ? a.G : 1)) {
+    const int b = bid;
     const int t0 = grouped ? a.gstart[b] : 0;
     const int t1 = grouped ? a.gstart[b + 1] : a.N;
-    write_record(a.idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E,
-                 a.cmp_out + (size_t)b * a.rec_ints, a.n_unique ? a.n_unique + b : nullptr,
+    write_record(idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E,
+                 cmp_out + (size_t)b * a.rec_ints, n_unique ? n_unique + b : nullptr,
                  (int *)lds);
   }
   int grp = 0;
@@ -168,15 +205,15 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   } else if (UP && a.dedup) {
     const int t0 = grouped ? a.gstart[grp] : 0;
     const int t1 = grouped ? a.gstart[grp + 1] : a.N;
-    e = local_instance(a.idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E, a.k, u, ent_row,
+    e = local_instance(idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E, a.k, u, ent_row,
                        ent_tok, &m);
     if (e < 0) return;  // past the group's U
     have_entries = true;
   } else {
     // one load either way: the u-th distinct expert of the record, or slot u
-    const int32_t *src = a.idx;
+    const int32_t *src = idx;
     if (a.dedup) {
-      rec = a.cmp + (grouped ? (size_t)grp * a.rec_ints : 0);
+      rec = cmp + (grouped ? (size_t)grp * a.rec_ints : 0);
       src = rec + CL.uniq();
     }
     e = src[u];
@@ -184,9 +221,8 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   }
   const unsigned char *wA, *wB = nullptr;
   {
-    const unsigned char *base13 =
-        (const unsigned char *)(shared_s < 0 ? a.w13 : a.ws13);
-    const unsigned char *base2 = (const unsigned char *)(shared_s < 0 ? a.w2 : a.ws2);
+    const unsigned char *base13 = shared_s < 0 ? w13 : ws13;
+    const unsigned char *base2 = shared_s < 0 ? w2 : ws2;
     const size_t ex = (size_t)(shared_s < 0 ? e : shared_s);
     if (UP) {
       wA = base13 + ex * 2 * fd * EB;
@@ -322,7 +358,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
               v[u] = *(const u32x4 *)src;
             }
           } else {
-            v[u] = ldg16((const unsigned char *)a.abuf +
+            v[u] = ldg16((const unsigned char *)abuf +
                          ((size_t)ent_row[c0 + c] * K + kk) * EB);
           }
         }
@@ -383,7 +419,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
       if (UP)
         bsrc = (const unsigned char *)(a.x + (size_t)ent_tok[ent] * K + lane_k);
       else
-        bsrc = (const unsigned char *)a.abuf + ((size_t)ent_row[ent] * K + lane_k) * EB;
+        bsrc = (const unsigned char *)abuf + ((size_t)ent_row[ent] * K + lane_k) * EB;
     }
     for (int w0 = 0; w0 < nchunks; w0 += cpw) {
       const int w1 = min(w0 + cpw, nchunks);
@@ -448,7 +484,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
           float act[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) act[v] = h[v] / (1.0f + expf(-h[v])) * gg[v];
-          unsigned char *dst = (unsigned char *)a.abuf + ((size_t)orow * a.f + row0) * EB;
+          unsigned char *dst = abuf + ((size_t)orow * a.f + row0) * EB;
           if (BF16) {
             bf16x4 b;
             b[0] = (__bf16)act[0]; b[1] = (__bf16)act[1];
@@ -458,7 +494,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
             *(f32x4 *)dst = f32x4{act[0], act[1], act[2], act[3]};
           }
         } else {
-          *(f32x4 *)(a.obuf + (size_t)orow * a.d + row0) = h;
+          *(f32x4 *)(obuf + (size_t)orow * a.d + row0) = h;
         }
       }
     }
@@ -466,36 +502,41 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   }
 }
 
-template <bool BF16, bool UP, bool TILED, bool GROUPED>
+template <bool BF16, bool UP, bool TILED, int VAR>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
-  const int blocks = (a.n_routed + a.S) * (R / kTile);
+  const long long blocks = (long long)a.L * (a.n_routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // allow more than the default 64 KB of dynamic LDS, once per kernel
   static const hipError_t set_wide = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 4, TILED, GROUPED>,
+      (const void *)expert_kernel<BF16, UP, 4, TILED, VAR>,
       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   static const hipError_t set_narrow = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 1, TILED, GROUPED>,
+      (const void *)expert_kernel<BF16, UP, 1, TILED, VAR>,
       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
   if (set_wide != hipSuccess) return set_wide;
   if (set_narrow != hipSuccess) return set_narrow;
   if (a.N > kTile)
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED, GROUPED>), dim3(blocks), dim3(kBlock),
-                       a.lds_bytes, st, a);
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED, VAR>), dim3((unsigned)blocks),
+                       dim3(kBlock), a.lds_bytes, st, a);
   else
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1, TILED, GROUPED>), dim3(blocks), dim3(kBlock),
-                       a.lds_bytes, st, a);
+    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1, TILED, VAR>), dim3((unsigned)blocks),
+                       dim3(kBlock), a.lds_bytes, st, a);
   return hipGetLastError();
+}
+
+template <bool BF16, bool UP, int VAR>
+hipError_t launch_expert_var(const ExpertArgs &a, hipStream_t st) {
+  return a.tiled ? launch_expert_layout<BF16, UP, true, VAR>(a, st)
+                 : launch_expert_layout<BF16, UP, false, VAR>(a, st);
 }
 
 template <bool BF16, bool UP>
 hipError_t launch_expert(const ExpertArgs &a, hipStream_t st) {
-  if (a.dedup == 2)
-    return a.tiled ? launch_expert_layout<BF16, UP, true, true>(a, st)
-                   : launch_expert_layout<BF16, UP, false, true>(a, st);
-  return a.tiled ? launch_expert_layout<BF16, UP, true, false>(a, st)
-                 : launch_expert_layout<BF16, UP, false, false>(a, st);
+  if (a.L > 1) return launch_expert_var<BF16, UP, kStack>(a, st);
+  if (a.dedup == 2) return launch_expert_var<BF16, UP, kGrouped>(a, st);
+  return launch_expert_var<BF16, UP, kPlain>(a, st);
 }
 
 // Row-major -> tiled, one thread per 16-byte unit of the output.  Unit u of a
@@ -527,6 +568,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const unsigned char *__restri
 // fp32.  The rows read do not depend on the routing values, so every load a
 // thread needs (its k+S expert rows, the k indices and weights) is issued
 // before the first is used: one memory round trip.
+// A stack's layers are blockIdx.z, each with its own rows, routing and y.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ obuf,
                                                       const int32_t *__restrict__ idx,
                                                       const float *__restrict__ w, int N, int k,
@@ -534,6 +576,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
                                                       float *__restrict__ y) {
   constexpr int J = MOE_MAX_TOPK + MOE_MAX_SHARED;
   const int t = blockIdx.y;
+  const size_t layer = blockIdx.z;
+  obuf += layer * N * (k + S) * d;
+  idx += layer * N * k;
+  w += layer * N * k;
+  y += layer * N * d;
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (c >= d) return;
   f32x4 ov[J];
@@ -620,7 +667,7 @@ hipError_t launch_pack(const void *src, void *dst, int R, int K, long long n_mat
 }
 
 hipError_t launch_combine(const ExpertArgs &a, hipStream_t st) {
-  dim3 grid((a.d / 4 + 255) / 256, a.N);
+  dim3 grid((a.d / 4 + 255) / 256, a.N, a.L);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, a.obuf, a.idx, a.w, a.N, a.k, a.S,
                      a.d, a.E, a.y);
   return hipGetLastError();

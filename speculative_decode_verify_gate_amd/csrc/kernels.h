@@ -58,6 +58,12 @@ struct ExpertArgs {
   // Read only when dedup == 2; the plain engines run with G = 1.
   int G;
   int rec_ints;
+  // A stack of L layers (L = 1: one layer): layer l's weights start
+  // l * lw13 / lw2 / lws13 / lws2 bytes into the arrays, its routing,
+  // compaction record (rec_ints int32 apart), U, rows, and y follow the
+  // previous layer's.
+  int L;
+  size_t lw13, lw2, lws13, lws2;
   int gstart[MOE_MAX_GROUPS + 1];
   int ibase[MOE_MAX_GROUPS + 1];
 };
@@ -66,16 +72,18 @@ struct ExpertArgs {
 // (the last gate workgroup also runs the top-k); otherwise gate + top-k.
 constexpr int kFusedRouteBytes = 64 * 1024;
 
+// A stack of L layers routes the same N tokens through L gates; every
+// array below then holds L consecutive per-layer blocks (L = 1: one layer).
 struct RouteArgs {
-  const float *gate_w, *x;
-  const float *bias;          // [E] added to the logits, or nullptr
-  int N, d, E, k, splits;
-  float *part;                // [splits][N][E] partial logits
-  unsigned *done;             // arrival counter (one launch): zero on entry and exit
-  float *logits;              // [N][E] or nullptr
-  int32_t *idx;               // [N][k]
-  float *w;                   // [N][k]
-  float *margin;              // [N] or nullptr
+  const float *gate_w, *x;    // [L][E][d], [N][d]
+  const float *bias;          // [L][E] added to the logits, or nullptr
+  int N, d, E, k, splits, L;
+  float *part;                // [L][splits][N][E] partial logits
+  unsigned *done;             // [L] arrival counters (one launch): zero on entry and exit
+  float *logits;              // [L][N][E] or nullptr
+  int32_t *idx;               // [L][N][k]
+  float *w;                   // [L][N][k]
+  float *margin;              // [L][N] or nullptr
 };
 
 int gate_splits(int d);

@@ -93,13 +93,22 @@ __device__ inline void select_topk(const float *L, int n_tok, int t0, const Rout
 
 // Partial logits of one 16-expert tile over one K split,
 // part[split][t][e] = sum over the split's K range of x[t][i] * gate_w[e][i];
-// with FUSED, the last workgroup also finishes the routing.
+// with FUSED, the last workgroup of the layer also finishes its routing.
+// A stack of L layers (the same tokens through every layer's gate) runs as
+// L consecutive ranges of workgroups, each with its own gate, bias,
+// partials, arrival counter and outputs.
 template <bool FUSED>
 __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   const int N = a.N, d = a.d, E = a.E;
   const int n_et = (E + kTile - 1) / kTile;
-  const int et = blockIdx.x % n_et;
-  const int split = blockIdx.x / n_et;
+  // layers of a stack are consecutive ranges of n_et * splits workgroups
+  const int per_layer = n_et * a.splits;
+  const int layer = blockIdx.x / per_layer;
+  const int bid = blockIdx.x - layer * per_layer;
+  const int et = bid % n_et;
+  const int split = bid / n_et;
+  const float *gate_w = a.gate_w + (size_t)layer * E * d;
+  float *part = a.part + (size_t)layer * a.splits * N * E;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
     const int k0 = k_begin + s * 16;
     if (k0 >= d) break;
     f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (expert < E) av = *(const f32x4 *)(a.gate_w + (size_t)expert * d + k0 + 4 * g);
+    if (expert < E) av = *(const f32x4 *)(gate_w + (size_t)expert * d + k0 + 4 * g);
 #pragma unroll
     for (int ct = 0; ct < kMaxColTiles; ++ct) {
       if (ct < n_ct) {
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
     // lane holds rows (experts) 4g..4g+3 of the tile for token column r
     const int tok = ct * kTile + r;
     if (tok < N) {
-      float *dst = a.part + ((size_t)split * N + tok) * E;
+      float *dst = part + ((size_t)split * N + tok) * E;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int e = et * kTile + 4 * g + v;
@@ -172,8 +181,8 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   if (tid == 0) {
     // arrivals counted in the caller's workspace (zero before first use);
     // the last workgroup puts it back to zero for the next call
-    s_last = atomicAdd(a.done, 1u) == gridDim.x - 1;
-    if (s_last) atomicExch(a.done, 0u);
+    s_last = atomicAdd(a.done + layer, 1u) == (unsigned)per_layer - 1;
+    if (s_last) atomicExch(a.done + layer, 0u);
   }
   __syncthreads();
   if (!s_last) return;
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
         const int i = min(i0 + q * 256 + tid, NE - 1);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          pv[q][u] = load_coherent(a.part + (size_t)min(sp0 + u, splits - 1) * NE + i);
+          pv[q][u] = load_coherent(part + (size_t)min(sp0 + u, splits - 1) * NE + i);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
 #pragma unroll
           for (int u = 0; u < 8; ++u)
             if (sp0 + u < splits) acc_l += pv[q][u];
-          if (sp0 + 8 >= splits && a.bias) acc_l += a.bias[e];
+          if (sp0 + 8 >= splits && a.bias) acc_l += a.bias[(size_t)layer * E + e];
           Ls[t * ld + e] = acc_l;
         }
       }
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   __syncthreads();
   __shared__ float sel_v[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
   __shared__ int sel_e[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
-  select_topk(Ls, N, 0, a, tid, blockDim.x, sel_v, sel_e);
+  select_topk(Ls, N, layer * N, a, tid, blockDim.x, sel_v, sel_e);
 }
 
 // Unfused top-k, one workgroup per token.  Wave w sums the partials of
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
 __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   constexpr int kBatch = 8;  // splits per wave and batch
   const int t = blockIdx.x;
+  const int layer = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int sp = min(sp0 + u * kGateWaves, splits - 1);
-          pv[q][u] = a.part[((size_t)sp * N + t) * E + e];
+          pv[q][u] = a.part[(((size_t)layer * splits + sp) * N + t) * E + e];
         }
       }
     }
@@ -271,12 +281,12 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
       l = ws_sum[0][tid];
 #pragma unroll
       for (int w = 1; w < kGateWaves; ++w) l += ws_sum[w][tid];
-      if (a.bias) l += a.bias[tid];
+      if (a.bias) l += a.bias[(size_t)layer * E + tid];
     }
     Ls[tid] = l;
   }
   __syncthreads();
-  select_topk(Ls, 1, t, a, tid, blockDim.x, sel_v, sel_e);
+  select_topk(Ls, 1, layer * N + t, a, tid, blockDim.x, sel_v, sel_e);
 }
 
 }  // namespace
@@ -291,7 +301,7 @@ bool route_fused(int N, int d, int E) {
 
 hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
   const int n_et = (a.E + kTile - 1) / kTile;
-  const int blocks = n_et * a.splits;
+  const int blocks = n_et * a.splits * a.L;
   if (route_fused(a.N, a.d, a.E)) {
     const size_t lds = (size_t)a.N * logit_ld(a.E) * sizeof(float);
     hipLaunchKernelGGL(gate_kernel<true>, dim3(blocks), dim3(256), lds, st, a);
@@ -302,7 +312,7 @@ hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_topk(const RouteArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3(a.N), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(topk_kernel, dim3(a.N, a.L), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -224,3 +224,37 @@ def test_grouped_pass_bytes_matches_oracle():
             assert B.pass_bytes(s, idx)[1] <= got_b <= B.pass_bytes(s, idx)[0]
     with pytest.raises(ValueError):
         B.pass_bytes_grouped(B.make_shape(256, 8, 2, 512), np.zeros((4, 2), np.int32), [0, 2, 3])
+
+
+def _stack(shape, L=3, n=4, engine=0, w=True, ws=None, nbytes=0, gate=FAKE):
+    lib = B.load()
+    sw = B.StackWeights(gate.value if gate is not None else None, None, 0x100000, 0x100000,
+                        0x100000, 0x100000, 0) if w else None
+    sz = C.c_size_t(nbytes)
+    rc = lib.moe_stack_pass(C.byref(shape), L, None if sw is None else C.byref(sw), FAKE, n,
+                            engine, FAKE, FAKE, FAKE, None, ws, C.byref(sz), None)
+    return rc, sz.value
+
+
+def test_stack_pass_validation_and_workspace():
+    s = _shape()
+    lib = B.load()
+    rc, need3 = _stack(s, L=3, n=16, engine=1)
+    assert rc == 0
+    # route part (256 bytes of counters + L layers of partials) + expert part
+    # (L compaction records, activation and output rows)
+    r1 = C.c_size_t(0)
+    assert lib.moe_route(C.byref(s), FAKE, FAKE, 16, None, FAKE, FAKE, None, None,
+                         C.byref(r1), None) == 0
+    e1 = C.c_size_t(0)
+    cw = B.Weights(0x100000, 0x100000, 0x100000, 0x100000)
+    assert lib.moe_expert_pass_dedup(C.byref(s), C.byref(cw), FAKE, 16, FAKE, FAKE, FAKE, None,
+                                     None, C.byref(e1), None) == 0
+    parts = (r1.value - 256)
+    assert need3 == 256 + 3 * parts + 3 * e1.value
+    rc, need_ps = _stack(s, L=3, n=16, engine=0)
+    assert rc == 0 and need_ps < need3          # no compaction records
+    for kw in (dict(L=0), dict(L=65), dict(engine=2), dict(w=False), dict(gate=None),
+               dict(n=0), dict(n=65)):
+        assert _stack(s, **kw)[0] == -1, kw
+    assert _stack(s, L=3, n=16, engine=1, ws=FAKE, nbytes=need3 - 1)[0] == -3

@@ -1,0 +1,177 @@
+"""GPU checks of the fused stack pass (moe_stack_pass), through the C ABI.
+
+Every layer of the stack is the layer of "Deep Dive into Mixture of Experts:
+From 1991 to DeepSeek-V3", sections 2 and 5, on the same tokens.  The fused
+pass must give, bit for bit, what the per-layer calls give (route or biased
+route, then the engine's expert pass, on that layer's weights): routing,
+weights, U and outputs.  Layer outputs are checked against the CPU oracle on
+sampled tokens with the bars of the single-layer parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from speculative_decode_verify_gate_amd import binding as B
+from speculative_decode_verify_gate_amd import synth
+from helpers import OUT_RTOL, TIE_EPS, oshape, rel_err, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _make_stack(cfg, L, device="cuda", bias=False, tiled=True):
+    """L layers of cfg stored back to back (fresh seeds per layer)."""
+    lays = [synth.make_layer(cfg, device, layer=l) for l in range(L)]
+    stack = {k: (None if lays[0][k] is None else torch.stack([lay[k] for lay in lays]).contiguous())
+             for k in ("gate_w", "w13", "w2", "ws13", "ws2")}
+    if bias:
+        stack["bias"] = torch.stack([synth.make_bias(cfg, device, layer=l) for l in range(L)])
+    stack["layout"] = "rows"
+    if tiled:
+        shape = B.shape_of(cfg)
+        packed = B.pack_weights(shape, {k: stack[k].reshape((-1,) + tuple(stack[k].shape[2:]))
+                                        if stack[k] is not None else None
+                                        for k in ("w13", "w2", "ws13", "ws2")})
+        for k in ("w13", "w2", "ws13", "ws2"):
+            if stack[k] is not None:
+                stack[k] = packed[k].reshape(stack[k].shape)
+        stack["layout"] = "tiled"
+    return stack
+
+
+def _layer_view(stack, l):
+    return {"gate_w": stack["gate_w"][l], "w13": stack["w13"][l], "w2": stack["w2"][l],
+            "ws13": None if stack["ws13"] is None else stack["ws13"][l],
+            "ws2": None if stack["ws2"] is None else stack["ws2"][l], "layout": stack["layout"]}
+
+
+def _per_layer(cfg, stack, x, engine):
+    """The same pass as separate per-layer calls."""
+    shape = B.shape_of(cfg)
+    L = stack["gate_w"].shape[0]
+    out = []
+    for l in range(L):
+        lay = _layer_view(stack, l)
+        bias = None if stack.get("bias") is None else stack["bias"][l]
+        idx, w = B.route(shape, lay["gate_w"], x, bias=bias)
+        nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if engine == "dedup":
+            y = B.expert_pass_dedup(shape, lay, x, idx, w, n_unique=nu)
+        else:
+            y = B.expert_pass_perslot(shape, lay, x, idx, w)
+        out.append((idx, w, y, nu))
+    torch.cuda.synchronize()
+    return out
+
+
+CASES = [
+    # name, d, E, k, f, S, wdtype
+    ("bf16-small", 256, 16, 2, 128, 1, "bf16"),
+    ("bf16-v2like", 512, 64, 6, 352, 2, "bf16"),
+    ("f32-small", 256, 8, 2, 192, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("n", [1, 5, 16, 17, 64])
+@pytest.mark.parametrize("engine", ["perslot", "dedup"])
+def test_stack_equals_per_layer_calls(case, n, engine):
+    name, d, E, k, f, S, wdt = case
+    if n * k > B.MAX_SLOTS:
+        pytest.skip("beyond the slot limit")
+    cfg = small_config(name, d, E, k, f, S, wdt)
+    L = 3
+    _say(f"[stack] {name} L={L} n={n} {engine}")
+    for bias in (False, True):
+        stack = _make_stack(cfg, L, bias=bias, tiled=(n % 2 == 1))
+        x = synth.make_hidden(cfg, n, 0, "cuda")
+        nu = torch.zeros(L, dtype=torch.int32, device="cuda")
+        idx, w, y = B.stack_pass(B.shape_of(cfg), stack, x, engine, n_unique=nu)
+        torch.cuda.synchronize()
+        ref = _per_layer(cfg, stack, x, engine)
+        for l, (ri, rw, ry, rnu) in enumerate(ref):
+            assert torch.equal(idx[l], ri), (l, "routing")
+            assert torch.equal(w[l], rw), (l, "weights")
+            assert torch.equal(y[l], ry), (l, "output")
+            if engine == "dedup":
+                assert int(nu[l].item()) == int(rnu.item())
+
+
+def test_stack_matches_oracle_on_sampled_tokens():
+    cfg = small_config("stack-oracle", 512, 64, 6, 352, 2, "bf16")
+    L, n = 4, 16
+    stack = _make_stack(cfg, L, bias=True, tiled=True)
+    rows = _make_stack(cfg, L, bias=True, tiled=False)   # the same draws, row-major
+    x = synth.make_hidden(cfg, n, 3, "cuda")
+    nu = torch.zeros(L, dtype=torch.int32, device="cuda")
+    idx, w, y = B.stack_pass(B.shape_of(cfg), stack, x, "dedup", n_unique=nu)
+    torch.cuda.synchronize()
+    s = oshape(cfg)
+    xs = x.cpu().numpy()
+    for l in range(L):
+        r = O.route(s, rows["gate_w"][l].cpu().numpy(), xs, tie_eps=TIE_EPS,
+                    bias=rows["bias"][l].cpu().numpy())
+        ok = r["flags"] == 0
+        gi = idx[l].cpu().numpy()
+        assert np.array_equal(gi[ok], r["idx"][ok])
+        assert int(nu[l].item()) == O.pass_bytes(s, gi)[3]
+        host = {kk: synth.to_host_bits(rows[kk][l]) for kk in ("w13", "w2", "ws13", "ws2")}
+        toks = [0, 7, 15]
+        y_o, _, _, _ = O.layer(s, host["w13"], host["w2"], host["ws13"], host["ws2"], xs[toks],
+                               gi[toks], w[l].cpu().numpy()[toks].astype(np.float64),
+                               engine="dedup", n_threads=8)
+        err = rel_err(y[l].cpu().numpy()[toks], y_o)
+        _say(f"[stack-oracle] layer {l} rel err {err:.2e}")
+        assert err <= OUT_RTOL["bf16"]
+
+
+def test_stack_with_separate_topk_launch_and_many_layers():
+    # 256 experts x d 2048 at 64 tokens: the partial logits exceed what one
+    # workgroup sums, so the stack's routing uses the separate top-k launch
+    cfg = small_config("stack-wide", 2048, 256, 8, 64, 1, "bf16")
+    L, n = 2, 64
+    stack = _make_stack(cfg, L, bias=True)
+    x = synth.make_hidden(cfg, n, 1, "cuda")
+    for engine in ("perslot", "dedup"):
+        idx, w, y = B.stack_pass(B.shape_of(cfg), stack, x, engine)
+        torch.cuda.synchronize()
+        for l, (ri, rw, ry, _) in enumerate(_per_layer(cfg, stack, x, engine)):
+            assert torch.equal(idx[l], ri) and torch.equal(w[l], rw) and torch.equal(y[l], ry)
+    # the most layers one call takes, with one workspace over repeated calls
+    cfg = small_config("stack-64", 256, 8, 2, 64, 0, "bf16")
+    L = B.MAX_LAYERS
+    stack = _make_stack(cfg, L)
+    ws = B.Workspace()
+    for rep, n in enumerate((3, 16, 1)):
+        x = synth.make_hidden(cfg, n, rep, "cuda")
+        nu = torch.zeros(L, dtype=torch.int32, device="cuda")
+        idx, w, y = B.stack_pass(B.shape_of(cfg), stack, x, "dedup", n_unique=nu, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.buf[:256].count_nonzero().item()) == 0     # counters back at zero
+        ref = _per_layer(cfg, stack, x, "dedup")
+        for l in (0, 17, L - 1):
+            assert torch.equal(idx[l], ref[l][0]) and torch.equal(y[l], ref[l][2])
+            assert int(nu[l].item()) == int(ref[l][3].item())
+
+
+def test_full_v2lite_stack_slice():
+    """Four DeepSeek-V2-Lite-shaped layers at n = 16, both engines."""
+    cfg = synth.CONFIGS["v2lite"]
+    L, n = 4, 16
+    _say("[stack] v2lite x 4, n = 16")
+    stack = _make_stack(cfg, L)
+    x = synth.make_hidden(cfg, n, 5, "cuda")
+    for engine in ("perslot", "dedup"):
+        nu = torch.zeros(L, dtype=torch.int32, device="cuda")
+        idx, w, y = B.stack_pass(B.shape_of(cfg), stack, x, engine, n_unique=nu)
+        torch.cuda.synchronize()
+        for l, (ri, rw, ry, rnu) in enumerate(_per_layer(cfg, stack, x, engine)):
+            assert torch.equal(idx[l], ri) and torch.equal(w[l], rw) and torch.equal(y[l], ry)
+            if engine == "dedup":
+                assert int(nu[l].item()) == int(rnu.item())
+    del stack
+    torch.cuda.empty_cache()
