@@ -34,6 +34,12 @@ constexpr int kGateKPerWave = kGateKPerBlock / kGateWaves;  // 64 = 4 steps of 1
 constexpr int kMaxColTiles = 4;                              // N <= 64
 constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
 constexpr int kFusedRouteLds = 32 * 1024;  // one-launch routing: [N][E] logits in LDS
+constexpr int kFusedGateThreads = 256;     // one-launch routing: threads per workgroup
+// gate workgroup LDS shared by the wave sums and the routing's partial ranks
+constexpr int kGateScratch =
+    (kGateWaves * kMaxColTiles * 64 * 16 > (kFusedGateThreads / 64) * MOE_MAX_EXPERTS * 4)
+        ? kGateWaves * kMaxColTiles * 64 * 16
+        : (kFusedGateThreads / 64) * MOE_MAX_EXPERTS * 4;
 
 
 // Row length of a token's logits in LDS: E rounded up to whole 16-byte
@@ -42,40 +48,142 @@ constexpr int kFusedRouteLds = 32 * 1024;  // one-launch routing: [N][E] logits 
 // a -inf logit the lower (real) index wins.
 __host__ __device__ inline int logit_ld(int E) { return (E + 3) & ~3; }
 
+// Order key of expert e with logit v: order-preserving bits of v (with -0
+// taken as +0) above the complemented index, so keys compare like (logit
+// descending, index ascending) -- a strict total order in which a token's
+// rank of e is the number of its keys greater than e's.  Padding entries
+// (e >= E) get key 0, below every real key.
+__device__ inline uint64_t order_key(float v, int e) {
+  uint32_t b = __float_as_uint(v);
+  if ((b << 1) == 0u) b = 0u;                       // -0 and +0 compare equal
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)~e;
+}
+
 // Top-k + softmax of n_tok tokens whose logits sit in LDS (L[t][ld], ld =
-// logit_ld(E), padded as above), by the nth threads of the caller.  Each
-// (token, expert) pair counts the experts that rank before it in the order
-// (logit desc, index asc): a strict total order, so ranks are unique and
-// equal the position a stable descending sort gives.  The row is read as
-// 16-byte vectors with several in flight.  Ranks 0..k-1 are the selection in
-// slot order; rank k gives the margin.  sel_v / sel_e: LDS [n_tok][MOE_MAX_TOPK
-// + 1].  t0 is the global index of token 0.  Ends with a barrier of the
-// caller's threads.
+// logit_ld(E)), by the nth threads of the caller.  Lane l of a wavefront
+// owns experts l, l+64, l+128, l+192 of a token; every key of the token is
+// broadcast from its owner lane (readlane, no memory round trip) and
+// compared with the lane's own keys, counting those ahead.  With fewer
+// tokens than wavefronts, each token's keys are split over several
+// wavefronts and the partial counts added in LDS; with more, a wavefront
+// takes TPW tokens at once so their compare chains overlap.  Ranks 0..k-1
+// are the selection in slot order; rank k gives the margin.  sel_v / sel_e:
+// LDS [n_tok][MOE_MAX_TOPK + 1].  t0 is the global index of token 0.
+// QM: 64-expert quarters compiled for (E <= 64 QM).
+template <int QM, int TPW>
+__device__ inline void rank_and_select(const float *L, int n_tok, int t0, const RouteArgs &a,
+                                       int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
+                                       int (*sel_e)[MOE_MAX_TOPK + 1],
+                                       int (*part_rank)[MOE_MAX_EXPERTS]) {
+  const int E = a.E;
+  const int k = a.k;
+  const int ld = logit_ld(E);
+  const int lane = tid & 63, wave = tid >> 6, nw = nth >> 6;
+  const int nq = (E + 63) >> 6;
+  const int wpt = n_tok >= nw ? 1 : nw / n_tok;  // wavefronts per token
+  const int slice = wave % wpt;                  // this wavefront's share of the keys
+  const int tstride = nw / wpt;                  // tokens started per round
+  const int jn = (E + wpt - 1) / wpt;
+  const int j0 = slice * jn, j1 = min(E, j0 + jn);
+  // Split mode (wpt > 1) makes one round, in which a wavefront whose token
+  // index is past n_tok only takes part in the barrier.
+  for (int tb = wave / wpt; wpt > 1 || tb < n_tok; tb += tstride * TPW) {
+    float v[TPW][QM];
+    uint64_t key[TPW][QM];
+    int rank[TPW][QM];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int t = tb + tt * tstride;
+#pragma unroll
+      for (int q = 0; q < QM; ++q) {
+        const int e = q * 64 + lane;
+        const bool ok = t < n_tok && q < nq && e < E;
+        v[tt][q] = ok ? L[(size_t)t * ld + e] : -INFINITY;
+        key[tt][q] = ok ? order_key(v[tt][q], e) : 0ull;
+        rank[tt][q] = 0;
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < QM; ++qq) {
+      const int ja = max(j0 - qq * 64, 0), jb = min(j1 - qq * 64, 64);
+      if (qq >= nq || ja >= jb) continue;  // uniform
+      uint32_t hi[TPW], lo[TPW];
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        hi[tt] = (uint32_t)(key[tt][qq] >> 32);
+        lo[tt] = (uint32_t)key[tt][qq];
+      }
+      for (int j = ja; j < jb; ++j) {
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+          const uint64_t kj = ((uint64_t)__builtin_amdgcn_readlane(hi[tt], j) << 32) |
+                              (uint32_t)__builtin_amdgcn_readlane(lo[tt], j);
+#pragma unroll
+          for (int q = 0; q < QM; ++q) rank[tt][q] += kj > key[tt][q] ? 1 : 0;
+        }
+      }
+    }
+    if (wpt > 1) {
+      // one token per wavefront group: add the groups' slices
+#pragma unroll
+      for (int q = 0; q < QM; ++q) part_rank[wave][q * 64 + lane] = rank[0][q];
+      __syncthreads();
+      if (slice == 0 && tb < n_tok) {
+#pragma unroll
+        for (int q = 0; q < QM; ++q) {
+          rank[0][q] = 0;
+          for (int w = 0; w < wpt; ++w) rank[0][q] += part_rank[wave + w][q * 64 + lane];
+        }
+      }
+    }
+    if (slice == 0) {
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int t = tb + tt * tstride;
+#pragma unroll
+        for (int q = 0; q < QM; ++q) {
+          const int e = q * 64 + lane;
+          if (t < n_tok && q < nq && e < E) {
+            if (rank[tt][q] <= k) {
+              sel_v[t][rank[tt][q]] = v[tt][q];
+              sel_e[t][rank[tt][q]] = e;
+            }
+            if (a.logits) a.logits[(size_t)(t0 + t) * E + e] = v[tt][q];
+          }
+        }
+      }
+    }
+    if (wpt > 1) break;
+  }
+}
+
+template <int QM>
+__device__ inline void rank_and_select_q(const float *L, int n_tok, int t0, const RouteArgs &a,
+                                         int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
+                                         int (*sel_e)[MOE_MAX_TOPK + 1],
+                                         int (*part_rank)[MOE_MAX_EXPERTS]) {
+  const int per_wave = (n_tok + (nth >> 6) - 1) / (nth >> 6);  // tokens per wavefront
+  if (per_wave >= 4)
+    rank_and_select<QM, 4>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+  else if (per_wave >= 2)
+    rank_and_select<QM, 2>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+  else
+    rank_and_select<QM, 1>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+}
+
+// part_rank: LDS [nth / 64][MOE_MAX_EXPERTS] ints, free during the call.
 __device__ inline void select_topk(const float *L, int n_tok, int t0, const RouteArgs &a,
                                    int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
-                                   int (*sel_e)[MOE_MAX_TOPK + 1]) {
+                                   int (*sel_e)[MOE_MAX_TOPK + 1],
+                                   int (*part_rank)[MOE_MAX_EXPERTS]) {
   const int E = a.E, k = a.k;
-  const int ld = logit_ld(E);
-  for (int p = tid; p < n_tok * E; p += nth) {
-    const int t = p / E;
-    const int e = p - t * E;
-    const float *row = L + (size_t)t * ld;
-    const float v = row[e];
-    int rank = 0;
-#pragma unroll 4
-    for (int j = 0; j < ld; j += 4) {
-      const f32x4 u = *(const f32x4 *)(row + j);
-      rank += (u.x > v || (u.x == v && j < e)) ? 1 : 0;
-      rank += (u.y > v || (u.y == v && j + 1 < e)) ? 1 : 0;
-      rank += (u.z > v || (u.z == v && j + 2 < e)) ? 1 : 0;
-      rank += (u.w > v || (u.w == v && j + 3 < e)) ? 1 : 0;
-    }
-    if (rank <= k) {
-      sel_v[t][rank] = v;
-      sel_e[t][rank] = e;
-    }
-    if (a.logits) a.logits[(size_t)(t0 + t) * E + e] = v;
-  }
+  if (E <= 64)
+    rank_and_select_q<1>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+  else if (E <= 128)
+    rank_and_select_q<2>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+  else
+    rank_and_select_q<4>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
   __syncthreads();
   for (int p = tid; p < n_tok * k; p += nth) {
     const int t = p / k;
@@ -98,7 +206,7 @@ __device__ inline void select_topk(const float *L, int n_tok, int t0, const Rout
 // L consecutive ranges of workgroups, each with its own gate, bias,
 // partials, arrival counter and outputs.
 template <bool FUSED>
-__global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
+__global__ __launch_bounds__(FUSED ? kFusedGateThreads : 256) void gate_kernel(RouteArgs a) {
   const int N = a.N, d = a.d, E = a.E;
   const int n_et = (E + kTile - 1) / kTile;
   // layers of a stack are consecutive ranges of n_et * splits workgroups
@@ -118,6 +226,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
 
   const int k_begin = split * kGateKPerBlock + wave * kGateKPerWave;
   const int expert = et * kTile + r;
+  const bool mma_wave = wave < kGateWaves;
 
   f32x4 acc[kMaxColTiles];
 #pragma unroll
@@ -128,7 +237,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
 #pragma unroll
   for (int s = 0; s < kGateKPerWave / 16; ++s) {
     const int k0 = k_begin + s * 16;
-    if (k0 >= d) break;
+    if (!mma_wave || k0 >= d) break;
     f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f};
     if (expert < E) av = *(const f32x4 *)(gate_w + (size_t)expert * d + k0 + 4 * g);
 #pragma unroll
@@ -145,11 +254,15 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
     }
   }
 
-  // Sum the four waves' partials in wave order.
-  __shared__ f32x4 red[kGateWaves][kMaxColTiles][64];
+  // Sum the four waves' partials in wave order.  The buffer is reused for
+  // the partial ranks of the routing.
+  __shared__ __align__(16) unsigned char scratch[kGateScratch];
+  f32x4 (*red)[kMaxColTiles][64] = (f32x4 (*)[kMaxColTiles][64])scratch;
+  if (mma_wave) {
 #pragma unroll
-  for (int ct = 0; ct < kMaxColTiles; ++ct)
-    if (ct < n_ct) red[wave][ct][lane] = acc[ct];
+    for (int ct = 0; ct < kMaxColTiles; ++ct)
+      if (ct < n_ct) red[wave][ct][lane] = acc[ct];
+  }
   __syncthreads();
   if (wave < n_ct) {
     const int ct = wave;
@@ -190,24 +303,25 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   const int splits = a.splits;
   const int NE = N * E;
   const int ld = logit_ld(E);
-  for (int i = tid; i < N * (ld - E); i += 256) {
+  const int nth = blockDim.x;
+  for (int i = tid; i < N * (ld - E); i += nth) {
     const int t = i / (ld - E);
     Ls[t * ld + E + (i - t * (ld - E))] = -INFINITY;
   }
-  for (int i0 = 0; i0 < NE; i0 += 4 * 256) {
+  for (int i0 = 0; i0 < NE; i0 += 4 * nth) {
     // the loads of 4 logits x 8 splits are issued before any is summed
     for (int sp0 = 0; sp0 < splits; sp0 += 8) {
       float pv[4][8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int i = min(i0 + q * 256 + tid, NE - 1);
+        const int i = min(i0 + q * nth + tid, NE - 1);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
           pv[q][u] = load_coherent(part + (size_t)min(sp0 + u, splits - 1) * NE + i);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int i = i0 + q * 256 + tid;
+        const int i = i0 + q * nth + tid;
         if (i < NE) {
           const int t = i / E;
           const int e = i - t * E;
@@ -224,7 +338,7 @@ __global__ __launch_bounds__(256) void gate_kernel(RouteArgs a) {
   __syncthreads();
   __shared__ float sel_v[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
   __shared__ int sel_e[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
-  select_topk(Ls, N, layer * N, a, tid, blockDim.x, sel_v, sel_e);
+  select_topk(Ls, N, layer * N, a, tid, nth, sel_v, sel_e, (int (*)[MOE_MAX_EXPERTS])scratch);
 }
 
 // Unfused top-k, one workgroup per token.  Wave w sums the partials of
@@ -244,6 +358,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   __shared__ float ws_sum[kGateWaves][MOE_MAX_EXPERTS];
   __shared__ float sel_v[1][MOE_MAX_TOPK + 1];
   __shared__ int sel_e[1][MOE_MAX_TOPK + 1];
+  __shared__ int part_rank[kGateWaves][MOE_MAX_EXPERTS];
   const int n_q = (E + 63) / 64;
   float v[kMaxExpertsPerLane];
 #pragma unroll
@@ -286,7 +401,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
     Ls[tid] = l;
   }
   __syncthreads();
-  select_topk(Ls, 1, layer * N + t, a, tid, blockDim.x, sel_v, sel_e);
+  select_topk(Ls, 1, layer * N + t, a, tid, blockDim.x, sel_v, sel_e, part_rank);
 }
 
 }  // namespace
@@ -304,7 +419,7 @@ hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
   const int blocks = n_et * a.splits * a.L;
   if (route_fused(a.N, a.d, a.E)) {
     const size_t lds = (size_t)a.N * logit_ld(a.E) * sizeof(float);
-    hipLaunchKernelGGL(gate_kernel<true>, dim3(blocks), dim3(256), lds, st, a);
+    hipLaunchKernelGGL(gate_kernel<true>, dim3(blocks), dim3(kFusedGateThreads), lds, st, a);
   } else {
     hipLaunchKernelGGL(gate_kernel<false>, dim3(blocks), dim3(256), 0, st, a);
   }
