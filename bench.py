@@ -566,16 +566,29 @@ def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=()):
     return wall, kt, U
 
 
-def cpu_baseline(cfg, x, seconds):
-    """The CPU oracle (as written, not tuned) on the same pass, on this host,
-    with the row-major weights of layer 0 (the same seeded draw)."""
+def host_info():
+    """What the CPU baseline ran on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def oracle_pass(cfg, n, seconds, threads, rep=0):
+    """The CPU oracle (as written, not tuned) on one verify pass of n tokens
+    per sequence (route + dedup layer, fp64) with the row-major weights of
+    layer 0, repeated for about `seconds` (at least once).  Returns (seconds
+    per pass, passes, requested bytes of the pass)."""
     import oracle as O
 
     layer = synth.make_layer(cfg, "cuda", layer=0)
-
-    threads = min(16, len(os.sched_getaffinity(0)))
     s = O.Shape(cfg.d, cfg.E, cfg.k, cfg.f, cfg.S, O.BF16 if cfg.wdtype == "bf16" else O.F32)
-    x_np = x.cpu().numpy()
+    x_np = synth.make_hidden(cfg, n, rep, "cuda").cpu().numpy()
     gate = layer["gate_w"].cpu().numpy()
     r = O.route(s, gate, x_np)
     used = np.unique(r["idx"])
@@ -586,9 +599,11 @@ def cpu_baseline(cfg, x, seconds):
         host_w13[e] = synth.to_host_bits(layer["w13"][e])
         host_w2[e] = synth.to_host_bits(layer["w2"][e])
     ws13, ws2 = synth.to_host_bits(layer["ws13"]), synth.to_host_bits(layer["ws2"])
+    del layer
+    torch.cuda.empty_cache()
     passes = 0
-    t0 = time.perf_counter()
     U = 0
+    t0 = time.perf_counter()
     while True:
         r = O.route(s, gate, x_np)
         _, rb, sb, U = O.layer(s, host_w13, host_w2, ws13, ws2, x_np, r["idx"], r["w"],
@@ -597,12 +612,39 @@ def cpu_baseline(cfg, x, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = (time.perf_counter() - t0) / passes
-    req = gate_bytes(cfg) + (U + cfg.S) * expert_bytes(cfg)
+    return dt, passes, gate_bytes(cfg) + (U + cfg.S) * expert_bytes(cfg)
+
+
+def cpu_baseline(cfg, n, seconds):
+    """The oracle timed on this host on the bench step's pass: all host
+    threads (up to 16) for about `seconds`, and one pass single-threaded."""
+    threads = min(16, len(os.sched_getaffinity(0)))
+    dt, passes, req = oracle_pass(cfg, n, seconds, threads, rep=99)
+    dt1, _, _ = oracle_pass(cfg, n, 0.0, 1, rep=99)
     return {"value": round(req / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "us_per_pass": round(dt * 1e6, 1),
-            "sample": f"{passes} oracle pass(es) of the n={x.shape[0] // cfg.n_seq} "
-                      f"{cfg.name} verify pass (route + dedup layer, fp64), "
-                      f"{threads} threads, {dt * passes:.1f} s"}
+            "single_thread_us_per_pass": round(dt1 * 1e6, 1),
+            "host": host_info(),
+            "sample": f"{passes} oracle pass(es) of the n={n} {cfg.name} verify pass "
+                      f"(route + dedup layer, fp64), {threads} threads, {dt * passes:.1f} s; "
+                      f"then one pass on 1 thread"}
+
+
+def cpu_sweep(seconds):
+    """The oracle on every workload at a few pass sizes (all host threads up
+    to 16, about `seconds` per point, at least one pass)."""
+    threads = min(16, len(os.sched_getaffinity(0)))
+    points = {"tiny": (4,), "mixtral": (1, 4, 8), "v2lite": (1, 4, 8, 16), "v3": (1, 16)}
+    out = []
+    for name, ns in points.items():
+        cfg = synth.CONFIGS[name]
+        for n in ns:
+            dt, passes, req = oracle_pass(cfg, n, seconds, threads)
+            out.append({"workload": name, "n": n, "tokens": cfg.tokens(n),
+                        "us_per_pass": round(dt * 1e6, 1), "GBs": round(req / dt / 1e9, 3),
+                        "passes": passes})
+            log(f"  cpu {name} n={n}: {dt * 1e3:.1f} ms per pass")
+    return {"kind": "oracle sweep", "threads": threads, "host": host_info(), "points": out}
 
 
 def traffic_record(kernel, workload):
@@ -649,6 +691,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sweep", action="store_true",
+                    help="only time the CPU oracle on every workload at a few pass sizes "
+                         "(one JSON document)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (for scaling HBM "
                          "byte counters) and print its byte counts")
@@ -674,6 +719,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "launches": 5,
                           "read_bytes_per_launch": nbytes, "write_bytes_per_launch": nbytes}))
+        return
+
+    if args.cpu_sweep:
+        print(json.dumps(cpu_sweep(min(args.cpu_seconds, 3.0))), flush=True)
         return
 
     if args.verify_only:
@@ -824,7 +873,7 @@ def main():
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
         del layers, stack
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, n_head, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -1,0 +1,188 @@
+// Host-side driver of the C ABI (include/moe_verify.h) for AddressSanitizer
+// and UBSan builds on the CPU.  The kernel launchers are replaced by stubs
+// that check the launch descriptors the ABI builds and launch nothing, so
+// argument validation, workspace sizing, group and layer tables and the host
+// byte accounting all run for real without a GPU.  Device pointers are host
+// addresses that nothing dereferences.  Exit status 0 = every check held.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+#include "moe_verify.h"
+#include "verify.h"
+
+static int g_fail = 0;
+#define CHECK(c)                                                     \
+  do {                                                               \
+    if (!(c)) {                                                      \
+      std::fprintf(stderr, "check failed at line %d: %s\n", __LINE__, #c); \
+      ++g_fail;                                                      \
+    }                                                                \
+  } while (0)
+
+namespace moe {
+static int g_launches = 0;
+
+int gate_splits(int d) { return (d + kGateKPerBlock - 1) / kGateKPerBlock; }
+bool route_fused(int N, int d, int E) {
+  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes;
+}
+int expert_lds_bytes(int, int, bool, bool, int) { return 0; }
+int verify_chunks(int V) { return (V + 2047) / 2048; }
+
+hipError_t launch_gate(const RouteArgs &a, hipStream_t) {
+  CHECK(a.L >= 1 && a.L <= MOE_MAX_LAYERS && a.N >= 1 && a.splits == gate_splits(a.d));
+  CHECK(a.gate_w && a.x && a.idx && a.w && a.done && a.part);
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_topk(const RouteArgs &a, hipStream_t) {
+  CHECK(!route_fused(a.N, a.d, a.E));
+  ++g_launches;
+  return hipSuccess;
+}
+static void check_expert(const ExpertArgs &a) {
+  CHECK(a.G >= 1 && a.G <= MOE_MAX_GROUPS && a.L >= 1 && a.L <= MOE_MAX_LAYERS);
+  CHECK(a.gstart[0] == 0 && a.gstart[a.G] == a.N && a.ibase[0] == 0);
+  for (int g = 0; g < a.G; ++g) {
+    const int slots = (a.gstart[g + 1] - a.gstart[g]) * a.k;
+    CHECK(a.gstart[g + 1] > a.gstart[g]);
+    CHECK(a.ibase[g + 1] - a.ibase[g] == (slots < a.E ? slots : a.E));
+  }
+  CHECK(a.n_routed == (a.dedup ? a.ibase[a.G] : a.N * a.k));
+  CHECK(a.dedup == 0 || a.dedup == (a.G > 1 ? 2 : 1));
+  CHECK(a.L == 1 || a.G == 1);
+  CHECK((a.cmp != nullptr) == (a.dedup != 0) && a.abuf && a.obuf && a.y && a.x);
+  CHECK((size_t)a.rec_ints * 4 % 256 == 0 && a.rec_ints >= 2 + 3 * a.E + a.N * a.k);
+}
+hipError_t launch_up(const ExpertArgs &a, bool, hipStream_t) { check_expert(a); ++g_launches; return hipSuccess; }
+hipError_t launch_down(const ExpertArgs &a, bool, hipStream_t) { check_expert(a); ++g_launches; return hipSuccess; }
+hipError_t launch_combine(const ExpertArgs &a, hipStream_t) { check_expert(a); ++g_launches; return hipSuccess; }
+hipError_t launch_pack(const void *, void *, int R, int K, long long n, bool, hipStream_t) {
+  CHECK(R > 0 && K > 0 && n >= 0);
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, const float *,
+                         const int32_t *, const float *, const uint32_t *, int32_t *n_acc,
+                         int32_t *out, void *ws, hipStream_t) {
+  CHECK(n_seq >= 1 && gamma >= 0 && V >= 1 && (mode == 0 || mode == 1) && p && n_acc && out && ws);
+  ++g_launches;
+  return hipSuccess;
+}
+}  // namespace moe
+
+static void *fake(size_t off = 0) { return (void *)(uintptr_t)(0x100000 + off); }
+
+struct Buf {  // 256-byte aligned host buffer standing in for a workspace
+  void *p = nullptr;
+  explicit Buf(size_t n) { p = std::aligned_alloc(256, (n + 255) / 256 * 256 + 256); }
+  ~Buf() { std::free(p); }
+};
+
+int main() {
+  const moe_shape shapes[] = {{256, 8, 2, 512, 0, MOE_F32}, {2048, 64, 6, 1408, 2, MOE_BF16},
+                              {7168, 256, 8, 2048, 1, MOE_BF16}, {4096, 8, 2, 14336, 0, MOE_BF16}};
+  for (const moe_shape &s : shapes) {
+    const moe_expert_weights w{fake(), fake(), s.n_shared ? fake() : nullptr,
+                               s.n_shared ? fake() : nullptr, MOE_LAYOUT_TILED};
+    for (int n : {1, 3, 16, 17, 64}) {
+      if (n * s.top_k > MOE_MAX_SLOTS) continue;
+      size_t need = 0;
+      CHECK(moe_route(&s, (float *)fake(), (float *)fake(), n, nullptr, (int32_t *)fake(),
+                      (float *)fake(), nullptr, nullptr, &need, nullptr) == MOE_OK);
+      {
+        Buf ws(need);
+        size_t have = need;
+        CHECK(moe_route_biased(&s, (float *)fake(), (float *)fake(), (float *)fake(), n,
+                               nullptr, (int32_t *)fake(), (float *)fake(), nullptr, ws.p,
+                               &have, nullptr) == MOE_OK);
+        have = need - 1;
+        CHECK(moe_route(&s, (float *)fake(), (float *)fake(), n, nullptr, (int32_t *)fake(),
+                        (float *)fake(), nullptr, ws.p, &have, nullptr) == MOE_ERR_WORKSPACE);
+      }
+      // per-slot, dedup and grouped passes with every group count up to n
+      for (int G = 0; G <= (n < MOE_MAX_GROUPS ? n : MOE_MAX_GROUPS); ++G) {
+        std::vector<int32_t> gs;
+        if (G > 0) {
+          for (int g = 0; g <= G; ++g) gs.push_back((int32_t)((long long)g * n / G));
+        }
+        size_t nb = 0;
+        int rc;
+        if (G == 0)
+          rc = moe_expert_pass_perslot(&s, &w, (float *)fake(), n, (int32_t *)fake(),
+                                       (float *)fake(), (float *)fake(), nullptr, &nb, nullptr);
+        else
+          rc = moe_expert_pass_dedup_grouped(&s, &w, (float *)fake(), n, G, gs.data(),
+                                             (int32_t *)fake(), (float *)fake(),
+                                             (float *)fake(), nullptr, nullptr, &nb, nullptr);
+        CHECK(rc == MOE_OK && nb > 0);
+        Buf ws(nb);
+        size_t have = nb;
+        if (G == 0)
+          rc = moe_expert_pass_perslot(&s, &w, (float *)fake(), n, (int32_t *)fake(),
+                                       (float *)fake(), (float *)fake(), ws.p, &have, nullptr);
+        else
+          rc = moe_expert_pass_dedup_grouped(&s, &w, (float *)fake(), n, G, gs.data(),
+                                             (int32_t *)fake(), (float *)fake(),
+                                             (float *)fake(), (int32_t *)fake(), ws.p, &have,
+                                             nullptr);
+        CHECK(rc == MOE_OK);
+      }
+      // the stack pass at 1, 2 and the most layers, both engines
+      const moe_stack_weights sw{(float *)fake(), nullptr, fake(), fake(),
+                                 s.n_shared ? fake() : nullptr, s.n_shared ? fake() : nullptr,
+                                 MOE_LAYOUT_TILED};
+      for (int L : {1, 2, MOE_MAX_LAYERS})
+        for (int eng : {MOE_ENGINE_PERSLOT, MOE_ENGINE_DEDUP}) {
+          size_t nb = 0;
+          CHECK(moe_stack_pass(&s, L, &sw, (float *)fake(), n, eng, (int32_t *)fake(),
+                               (float *)fake(), (float *)fake(), nullptr, nullptr, &nb,
+                               nullptr) == MOE_OK);
+          Buf ws(nb);
+          size_t have = nb;
+          CHECK(moe_stack_pass(&s, L, &sw, (float *)fake(), n, eng, (int32_t *)fake(),
+                               (float *)fake(), (float *)fake(), (int32_t *)fake(), ws.p,
+                               &have, nullptr) == MOE_OK);
+        }
+      // host byte accounting reads real host routing
+      std::vector<int32_t> idx((size_t)n * s.top_k);
+      for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int32_t)((i * 7 + i / s.top_k) % s.n_experts);
+      uint64_t ps = 0, dd = 0, sh = 0;
+      int32_t U = 0;
+      CHECK(moe_pass_bytes(&s, idx.data(), n, &ps, &dd, &sh, &U) == MOE_OK);
+      const int32_t whole[2] = {0, n};
+      uint64_t dg = 0;
+      int32_t Ug = 0;
+      CHECK(moe_pass_bytes_grouped(&s, idx.data(), n, 1, whole, &dg, &Ug) == MOE_OK);
+      CHECK(dg == dd && Ug == U && U <= n * s.top_k && (uint64_t)U * 3 * s.d_model * s.d_ff <= dd);
+    }
+  }
+  // rejected arguments
+  const moe_shape s = shapes[1];
+  const int32_t bad_groups[][4] = {{1, 4, 0, 0}, {0, 2, 2, 4}, {0, 3, 2, 4}};
+  for (auto &g : bad_groups)
+    CHECK(moe_pass_bytes_grouped(&s, (int32_t *)fake(), 4, 3, g, nullptr, nullptr) ==
+          MOE_ERR_INVALID_ARG);
+  std::vector<int32_t> oob = {0, 1, 2, 3, 4, 64};
+  CHECK(moe_pass_bytes(&s, oob.data(), 1, nullptr, nullptr, nullptr, nullptr) == MOE_ERR_INVALID_ARG);
+  size_t nb = 0;
+  CHECK(moe_stack_pass(&s, MOE_MAX_LAYERS + 1, nullptr, nullptr, 4, 0, nullptr, nullptr, nullptr,
+                       nullptr, nullptr, &nb, nullptr) == MOE_ERR_INVALID_ARG);
+  // the verification round
+  for (int gamma : {0, 1, 8, MOE_MAX_DRAFT}) {
+    CHECK(moe_verify_gate(4, gamma, 102400, 1, (float *)fake(), (float *)fake(),
+                          (int32_t *)fake(), (float *)fake(), (uint32_t *)fake(),
+                          (int32_t *)fake(), (int32_t *)fake(), nullptr, &nb, nullptr) == MOE_OK);
+    Buf ws(nb);
+    size_t have = nb;
+    CHECK(moe_verify_gate(4, gamma, 102400, 1, (float *)fake(), (float *)fake(),
+                          (int32_t *)fake(), (float *)fake(), (uint32_t *)fake(),
+                          (int32_t *)fake(), (int32_t *)fake(), ws.p, &have, nullptr) == MOE_OK);
+  }
+  CHECK(moe_pack_weights(&s, 2, fake(), fake(), fake(1 << 30), fake(3u << 29), nullptr) == MOE_OK);
+  std::printf("abi driver: %d launches described, %d failed checks\n", moe::g_launches, g_fail);
+  return g_fail == 0 ? 0 : 1;
+}
