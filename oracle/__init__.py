@@ -9,5 +9,5 @@ package imports nothing from it.  The arithmetic lives in ``moe_oracle.cpp``
 from .oracle import (  # noqa: F401
     F32, BF16, FLAG_BOUNDARY, FLAG_ORDER, Shape, load, bf16_rne, gate_logits,
     route, expert, layer, layer_grouped, dense_mixture, pass_bytes, compact, expert_bytes,
-    GREEDY, SAMPLING, sample_index, verify_gate,
+    GREEDY, SAMPLING, sample_index, verify_gate, filter_probs,
 )

@@ -41,6 +41,7 @@
  */
 #include "moe_oracle.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -498,6 +499,62 @@ int32_t oracle_sample_index(const float *weights, int32_t V, uint32_t r) {
     if (prefix > target) return j;
   }
   return -1; /* not reached: prefix ends at W > target */
+}
+
+/* V6: the verifier's and the draft's distributions from their logits, as
+ * the page's verify phase builds them: softmax of logits / temperature, then
+ * top-p (nucleus) filtering -- the shortest run of tokens in the order
+ * (probability descending, index ascending) whose probability reaches top_p,
+ * the token that reaches it included, renormalised; the rest get zero.
+ * top_p >= 1 keeps every token.  fp64 throughout.  *boundary_gap (if given)
+ * receives how far the kept mass before the last kept token falls short of
+ * top_p and how far the kept mass exceeds it, the smaller of the two, and
+ * the relative gap between the last kept probability and the next one:
+ * small values mark rows whose kept set a lower precision could change. */
+int oracle_filter_probs(int32_t V, const float *logits, double temperature, double top_p,
+                        double *probs, double *boundary_gap) {
+  if (V <= 0 || !logits || !probs || !(temperature > 0.0) || !(top_p > 0.0)) return -1;
+  std::vector<double> z((size_t)V);
+  double m = -std::numeric_limits<double>::infinity();
+  for (int32_t j = 0; j < V; ++j) {
+    z[j] = (double)logits[j] / temperature;
+    if (z[j] > m) m = z[j];
+  }
+  double S = 0.0;
+  for (int32_t j = 0; j < V; ++j) {
+    z[j] = std::exp(z[j] - m);
+    S += z[j];
+  }
+  for (int32_t j = 0; j < V; ++j) probs[j] = z[j] / S;
+  if (boundary_gap) *boundary_gap = std::numeric_limits<double>::infinity();
+  if (top_p >= 1.0) return 0;
+  std::vector<int32_t> order((size_t)V);
+  for (int32_t j = 0; j < V; ++j) order[j] = j;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return probs[a] > probs[b]; });
+  double kept = 0.0;
+  int32_t n_kept = 0;
+  while (n_kept < V) {
+    kept += probs[order[n_kept]];
+    ++n_kept;
+    if (kept >= top_p) break;
+  }
+  if (boundary_gap) {
+    const double last = probs[order[n_kept - 1]];
+    const double before = kept - last;
+    double gap = std::min(std::fabs(top_p - before), std::fabs(kept - top_p));
+    if (n_kept < V) {
+      const double next = probs[order[n_kept]];
+      gap = std::min(gap, (last - next) / (last > 0.0 ? last : 1.0));
+    }
+    *boundary_gap = gap;
+  }
+  double total = 0.0;
+  for (int32_t r = 0; r < n_kept; ++r) total += probs[order[r]];
+  std::vector<char> keep((size_t)V, 0);
+  for (int32_t r = 0; r < n_kept; ++r) keep[order[r]] = 1;
+  for (int32_t j = 0; j < V; ++j) probs[j] = keep[j] ? probs[j] / total : 0.0;
+  return 0;
 }
 
 static int32_t argmax_lowest(const float *row, int32_t V) {

@@ -147,6 +147,12 @@ int32_t oracle_sample_index(const float *weights, int32_t V, uint32_t r);
  * Outputs *n_acc (accepted draft tokens, 0..gamma) and tokens [gamma+1]: the
  * accepted prefix, then the correction (first rejection) or bonus token, then
  * -1.  Returns 0, or -1 on bad arguments. */
+/* Softmax of logits / temperature, then top-p (nucleus) filtering and
+ * renormalisation (see moe_oracle.cpp, reading V6).  probs [V] fp64 out;
+ * boundary_gap may be NULL. */
+int oracle_filter_probs(int32_t V, const float *logits, double temperature, double top_p,
+                        double *probs, double *boundary_gap);
+
 int oracle_verify_gate(int32_t gamma, int32_t V, int32_t mode, const float *p, const float *q,
                        const int32_t *x, const float *u, uint32_t r, int32_t *n_acc,
                        int32_t *tokens);

@@ -67,6 +67,8 @@ def load():
         lib.oracle_sample_index.argtypes = [P, i32, C.c_uint32]
         lib.oracle_sample_index.restype = i32
         lib.oracle_verify_gate.argtypes = [i32, i32, i32, P, P, P, P, C.c_uint32, P, P]
+        lib.oracle_filter_probs.argtypes = [i32, P, C.c_double, C.c_double, P, P]
+        lib.oracle_filter_probs.restype = C.c_int
         for fn in ("oracle_gate_logits", "oracle_route", "oracle_route_biased", "oracle_expert",
                    "oracle_layer", "oracle_layer_grouped", "oracle_dense_mixture",
                    "oracle_pass_bytes", "oracle_compact"):
@@ -275,3 +277,20 @@ def verify_gate(p, x, *, q=None, u=None, r=0, mode=SAMPLING):
     if rc != 0:
         raise ValueError("oracle_verify_gate: bad arguments")
     return int(n[0]), t
+
+
+def filter_probs(logits, temperature, top_p):
+    """softmax(logits / temperature) then top-p filtering, per row of a
+    [..., V] array.  Returns (probs fp64, boundary gap per row)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    V = lg.shape[-1]
+    rows = lg.reshape(-1, V)
+    out = np.empty(rows.shape, dtype=np.float64)
+    gaps = np.empty(rows.shape[0], dtype=np.float64)
+    lib = load()
+    for i in range(rows.shape[0]):
+        g = np.zeros(1, np.float64)
+        _check(lib.oracle_filter_probs(V, rows[i].ctypes.data, float(temperature), float(top_p),
+                                       out[i].ctypes.data, g.ctypes.data), "oracle_filter_probs")
+        gaps[i] = g[0]
+    return out.reshape(lg.shape), gaps.reshape(lg.shape[:-1])

@@ -94,6 +94,15 @@ int main() {
   CHECK(oracle_verify_gate(gamma, V, 1, p.data(), q.data(), xt.data(), u.data(), 1u, &na,
                            tok.data()) != 0);
   CHECK(oracle_sample_index(p.data(), V, 0u) >= 0 && oracle_sample_index(p.data(), V, ~0u) < V);
+  std::vector<double> fp(V);
+  double gap = 0.0;
+  for (double top_p : {0.3, 0.9, 1.0}) {
+    CHECK(oracle_filter_probs(V, p.data(), 0.7, top_p, fp.data(), &gap) == 0);
+    double sum = 0.0;
+    for (double v : fp) sum += v;
+    CHECK(std::fabs(sum - 1.0) < 1e-9);
+  }
+  CHECK(oracle_filter_probs(V, p.data(), 0.0, 0.9, fp.data(), nullptr) != 0);
   std::printf("oracle driver: %d failed checks\n", g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -115,3 +115,51 @@ def test_rejects_bad_arguments():
         O.verify_gate(p, [2], q=p[:1], u=[0.1])      # token outside the vocabulary
     with pytest.raises(ValueError):
         O.verify_gate(p, [0], q=None, u=[0.1])       # sampling needs q
+
+
+# ------------------------------------------------ logits -> filtered distributions
+
+def test_filter_without_top_p_is_the_temperature_softmax():
+    import scipy.special
+    rng = np.random.default_rng(21)
+    for V, T in [(5, 1.0), (1000, 0.7), (4099, 2.5)]:
+        lg = (rng.standard_normal(V) * 3).astype(np.float32)
+        lg[rng.random(V) < 0.01] = -np.inf                    # masked tokens
+        got, _ = O.filter_probs(lg, T, 1.0)
+        ref = scipy.special.softmax(lg.astype(np.float64) / T)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-300)
+
+
+def test_filter_hand_computed():
+    # probabilities 0.5, 0.3, 0.2 (as logits): the nucleus grows by whole
+    # tokens in probability order until it holds top_p of the mass
+    lg = np.log(np.array([0.2, 0.5, 0.3], np.float32))
+    p, _ = O.filter_probs(lg, 1.0, 0.45)
+    np.testing.assert_allclose(p, [0, 1, 0], atol=1e-12)
+    p, _ = O.filter_probs(lg, 1.0, 0.7)
+    np.testing.assert_allclose(p, [0, 0.625, 0.375], atol=1e-7)
+    p, _ = O.filter_probs(lg, 1.0, 0.81)
+    np.testing.assert_allclose(p, [0.2, 0.5, 0.3], atol=1e-7)
+    # equal probabilities: the lower index comes first
+    p, _ = O.filter_probs(np.array([1, 1, 1, 0], np.float32), 1.0, 0.5)
+    np.testing.assert_allclose(p, [0.5, 0.5, 0, 0], atol=1e-12)
+
+
+def test_filter_keeps_the_minimal_prefix_of_the_sorted_order():
+    rng = np.random.default_rng(22)
+    for trial in range(40):
+        V = int(rng.integers(2, 400))
+        lg = (rng.standard_normal(V) * rng.uniform(0.3, 4)).astype(np.float32)
+        if trial % 5 == 0:
+            lg[: V // 3] = lg[0]                               # many exact ties
+        T, top_p = float(rng.uniform(0.3, 2.0)), float(rng.uniform(0.05, 0.99))
+        full, _ = O.filter_probs(lg, T, 1.0)
+        got, _ = O.filter_probs(lg, T, top_p)
+        order = sorted(range(V), key=lambda j: (-full[j], j))
+        kept = [j for j in order if got[j] > 0]
+        n = len(kept)
+        assert kept == order[:n]                               # a prefix
+        mass = full[kept].sum()
+        assert mass >= top_p and mass - full[kept[-1]] < top_p  # minimal
+        np.testing.assert_allclose(got[kept], full[kept] / mass, rtol=1e-12)
+        assert abs(got.sum() - 1.0) < 1e-12
