@@ -507,10 +507,8 @@ int32_t oracle_sample_index(const float *weights, int32_t V, uint32_t r) {
  * (probability descending, index ascending) whose probability reaches top_p,
  * the token that reaches it included, renormalised; the rest get zero.
  * top_p >= 1 keeps every token.  fp64 throughout.  *boundary_gap (if given)
- * receives how far the kept mass before the last kept token falls short of
- * top_p and how far the kept mass exceeds it, the smaller of the two, and
- * the relative gap between the last kept probability and the next one:
- * small values mark rows whose kept set a lower precision could change. */
+ * receives the smallest margin of the decision (below): small values mark
+ * rows whose kept set a lower precision could change. */
 int oracle_filter_probs(int32_t V, const float *logits, double temperature, double top_p,
                         double *probs, double *boundary_gap) {
   if (V <= 0 || !logits || !probs || !(temperature > 0.0) || !(top_p > 0.0)) return -1;
@@ -540,13 +538,25 @@ int oracle_filter_probs(int32_t V, const float *logits, double temperature, doub
     if (kept >= top_p) break;
   }
   if (boundary_gap) {
+    /* how close the row is to keeping a different set at lower precision:
+     * the kept mass against top_p on both sides of the last kept token,
+     * and the relative distance from the last kept probability to the
+     * nearest different probability above and below it (an exact tie is
+     * ordered by index in any precision; a near one may not be) */
     const double last = probs[order[n_kept - 1]];
     const double before = kept - last;
     double gap = std::min(std::fabs(top_p - before), std::fabs(kept - top_p));
-    if (n_kept < V) {
-      const double next = probs[order[n_kept]];
-      gap = std::min(gap, (last - next) / (last > 0.0 ? last : 1.0));
-    }
+    const double scale = last > 0.0 ? last : 1.0;
+    for (int32_t r = n_kept; r < V; ++r)
+      if (probs[order[r]] != last) {
+        gap = std::min(gap, (last - probs[order[r]]) / scale);
+        break;
+      }
+    for (int32_t r = n_kept - 1; r >= 0; --r)
+      if (probs[order[r]] != last) {
+        gap = std::min(gap, (probs[order[r]] - last) / scale);
+        break;
+      }
     *boundary_gap = gap;
   }
   double total = 0.0;
