@@ -308,47 +308,64 @@ def draft_length_table(sweep, draft_fracs=(0.05, 0.2), alphas=None):
     return out
 
 
-def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200):
-    """The verification round after the verify pass: µs per call for n_seq
-    sequences with gamma drafted tokens, per mode, on seeded synthetic
-    distributions.  Bytes counted: greedy reads every row of p (n_seq
-    (gamma+1) V fp32); sampling reads the row it draws from twice over the
-    vocabulary, p and q at the first rejection (2 n_seq V fp32) -- the
-    acceptance tests' scalars are not counted."""
+def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, temperature=0.7,
+                    top_p=0.9):
+    """The verification round after the verify pass, from the models' logits:
+    the verifier's and the draft's distributions (moe_verify_probs: softmax
+    of logits / temperature, top-p filtering, at the page's settings), then
+    the round (moe_verify_gate), each timed per call, for n_seq sequences with
+    gamma drafted tokens on seeded synthetic logits.  Bytes counted: the
+    filter reads and writes every row once ((2 gamma + 1) rows per sequence);
+    greedy reads every row of p (n_seq (gamma+1) V fp32); sampling reads
+    the row it draws from twice over the vocabulary, p and q at the first
+    rejection (2 n_seq V fp32) -- the acceptance tests' scalars are not
+    counted."""
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
     out = []
+
+    def timed_us(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        hold_gpu(0.1 * reps)
+        for _ in range(reps):
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            fn()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
     for V in vocabs:
-        logits = torch.randn((n_seq, gamma + 1, V), generator=g, device="cuda") * 3.0
-        p = torch.softmax(logits, dim=-1).contiguous()
-        q = torch.softmax(logits[:, :gamma] + 0.5 * torch.randn(
-            (n_seq, gamma, V), generator=g, device="cuda"), dim=-1).contiguous()
+        vlog = torch.randn((n_seq, gamma + 1, V), generator=g, device="cuda") * 3.0
+        dlog = (vlog[:, :gamma] + 0.5 * torch.randn((n_seq, gamma, V), generator=g,
+                                                     device="cuda")).contiguous()
+        p = B.verify_probs(vlog, temperature, top_p)
+        q = B.verify_probs(dlog, temperature, top_p)
         x = torch.multinomial(q.reshape(-1, V), 1, generator=g).reshape(n_seq, gamma)
         x = x.to(torch.int32).contiguous()
         u = torch.rand((n_seq, gamma), generator=g, device="cuda")
         r = torch.randint(-2**31, 2**31 - 1, (n_seq,), generator=g, device="cuda",
                           dtype=torch.int32)
-        rec = {"vocab": V, "n_seq": n_seq, "gamma": gamma}
+        rec = {"vocab": V, "n_seq": n_seq, "gamma": gamma, "temperature": temperature,
+               "top_p": top_p}
+        rows = n_seq * (2 * gamma + 1)
+        fu = timed_us(lambda: (B.verify_probs(vlog, temperature, top_p, out=p),
+                               B.verify_probs(dlog, temperature, top_p, out=q)))
+        rec["filter_us"] = round(fu, 2)
+        rec["filter_GBs"] = round(2 * rows * V * 4 / fu / 1e3, 1)
         for mode, name in ((B.VERIFY_GREEDY, "greedy"), (B.VERIFY_SAMPLING, "sampling")):
             ws = B.Workspace()
-            for _ in range(10):
-                B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, ws=ws)
-            torch.cuda.synchronize()
-            evs = []
-            hold_gpu(0.1 * reps)
-            for _ in range(reps):
-                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-                e0.record()
-                B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, ws=ws)
-                e1.record()
-                evs.append((e0, e1))
-            torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
+            us = timed_us(lambda: B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, ws=ws))
             nbytes = (n_seq * (gamma + 1) * V * 4) if name == "greedy" else (2 * n_seq * V * 4)
             rec[f"{name}_us"] = round(us, 2)
             rec[f"{name}_GBs"] = round(nbytes / us / 1e3, 1)
         out.append(rec)
-        log(f"  verify gate V={V}: greedy {rec['greedy_us']} us, sampling {rec['sampling_us']} us")
+        log(f"  verify V={V}: filter {rec['filter_us']} us, greedy {rec['greedy_us']} us, "
+            f"sampling {rec['sampling_us']} us")
     return out
 
 

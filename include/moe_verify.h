@@ -310,6 +310,28 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
                     const float *u_accept, const uint32_t *r_sample, int32_t *n_accepted,
                     int32_t *out_tokens, void *workspace, size_t *workspace_bytes, void *stream);
 
+/* The distributions a verification round compares, from the models'
+ * logits ("Building a Terminal Based LLM Inference Internals Explorer -
+ * Part 3: Speculative Decoding", sections "The Accept/Reject Mechanism" and
+ * "The Flow": softmax of logits / temperature, then top-p filtering, with
+ * the same settings for the verifier and the draft):
+ *   logits [rows][V] fp32 device (each row with at least one finite logit)
+ *   probs  [rows][V] fp32 device output: P = softmax(logits / temperature);
+ *          with top_p < 1 only the shortest run of tokens in the order
+ *          (P descending, index ascending) whose probability reaches top_p
+ *          is kept (the token that reaches it included), renormalised; the
+ *          rest are 0.  The kept set is decided on integer masses
+ *          floor(P * 2^40) against ceil(top_p * their total), exactly and
+ *          independent of summation order.  probs may not overlap logits.
+ * 0 < temperature (finite), 0 < top_p <= 1, 1 <= rows, 1 <= V <=
+ * MOE_MAX_VOCAB; violations return MOE_ERR_INVALID_ARG (more than 65535
+ * rows: MOE_ERR_UNSUPPORTED).  Workspace as for
+ * the other calls (no initialisation needed).  Feed the verifier's rows as
+ * p_verify and the draft's as q_draft. */
+int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
+                     float top_p, float *probs, void *workspace, size_t *workspace_bytes,
+                     void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_string(int status);
 
@@ -329,7 +351,8 @@ enum moe_kernel_kind {
   MOE_K_DOWN = 4,    /* W2 over all expert instances */
   MOE_K_COMBINE = 5, /* weighted sum in slot order + shared experts */
   MOE_K_VERIFY = 6,  /* verification round (moe_verify_gate) */
-  MOE_K_COUNT = 7
+  MOE_K_FILTER = 7,  /* softmax + top-p filtering (moe_verify_probs) */
+  MOE_K_COUNT = 8
 };
 /* mask: bit (1 << kind) selects a kernel kind; 0 disables timing.  Not
  * meant for concurrent use from several host threads. */

@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("MOE_VERIFY_LIB") or os.path.join(_HERE, "libmoeverify
 
 MOE_F32, MOE_BF16 = 0, 1
 MAX_TOKENS, MAX_TOPK, MAX_SLOTS, MAX_EXPERTS, MAX_SHARED = 64, 16, 512, 256, 4
-KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine", "verify")
+KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine", "verify", "filter")
 VERIFY_GREEDY, VERIFY_SAMPLING = 0, 1
 MAX_SEQ, MAX_DRAFT, MAX_VOCAB = 64, 63, 1 << 24
 MAX_GROUPS = 64
@@ -74,11 +74,12 @@ def load():
     lib.moe_timing_enable.argtypes = [C.c_int]
     lib.moe_timing_read.argtypes = [P, P]
     lib.moe_verify_gate.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
+    lib.moe_verify_probs.argtypes = [i32, i32, P, C.c_float, C.c_float, P, P, sz, P]
     for fn in ("moe_route", "moe_route_biased", "moe_expert_pass_perslot",
                "moe_expert_pass_dedup", "moe_expert_pass_dedup_grouped", "moe_pass_bytes",
                "moe_pass_bytes_grouped", "moe_stack_pass", "moe_pack_weights",
                "moe_timing_enable",
-               "moe_timing_read", "moe_verify_gate"):
+               "moe_timing_read", "moe_verify_gate", "moe_verify_probs"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -386,6 +387,35 @@ def verify_gate(p, x, *, q=None, u=None, r=None, mode=VERIFY_SAMPLING, n_accepte
                                                   _ptr(u), _ptr(r), _ptr(n_accepted), _ptr(out),
                                                   _ptr(buf), C.byref(have), _stream()))
     return n_accepted, out
+
+
+def verify_probs(logits, temperature, top_p=1.0, *, out=None, ws=None):
+    """softmax(logits / temperature) then top-p filtering, per row of an fp32
+    [..., V] tensor on the GPU (moe_verify_probs).  Returns the filtered
+    probabilities, same shape."""
+    lib = load()
+    logits = _dev(logits, torch.float32, "logits")
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    if out is None:
+        out = torch.empty_like(logits)
+    _dev(out, torch.float32, "out")
+    if out.shape != logits.shape:
+        raise ValueError("out must have the shape of logits")
+    key = ("filter", rows, V)
+    if key not in _NEED:
+        nb = C.c_size_t(0)
+        _check("moe_verify_probs", lib.moe_verify_probs(rows, V, _ptr(logits), float(temperature),
+                                                        float(top_p), _ptr(out), None,
+                                                        C.byref(nb), None))
+        _NEED[key] = nb.value
+    ws = ws or Workspace(logits.device)
+    buf = ws.get(_NEED[key])
+    have = C.c_size_t(buf.numel())
+    _check("moe_verify_probs", lib.moe_verify_probs(rows, V, _ptr(logits), float(temperature),
+                                                    float(top_p), _ptr(out), _ptr(buf),
+                                                    C.byref(have), _stream()))
+    return out
 
 
 def timing_enable(kinds=KERNEL_KINDS):

@@ -4,6 +4,7 @@
 // (the dedup compaction, done inside the up kernel, in compact.h).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <vector>
 
@@ -354,6 +355,28 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
     return moe::launch_verify(n_seq, gamma, vocab, mode, p_verify,
                               mode == MOE_VERIFY_SAMPLING ? q_draft : nullptr, draft_tokens,
                               u_accept, r_sample, n_accepted, out_tokens, ws, st);
+  });
+  return status_of(err);
+}
+
+int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
+                     float top_p, float *probs, void *ws, size_t *ws_bytes, void *stream) {
+  if (rows < 1 || vocab < 1 || vocab > MOE_MAX_VOCAB || !logits || !probs)
+    return MOE_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !(temperature < INFINITY) || !(top_p > 0.f) || !(top_p <= 1.f))
+    return MOE_ERR_INVALID_ARG;
+  const size_t n = (size_t)rows * vocab * sizeof(float);
+  const char *a = (const char *)logits, *b = (const char *)probs;
+  if (a < b + n && b < a + n) return MOE_ERR_INVALID_ARG;
+  if (rows > 65535) return MOE_ERR_UNSUPPORTED;  // rows are a grid dimension
+  bool launch;
+  int rc;
+  if ((rc = workspace_gate(ws, ws_bytes, moe::filter_ws_bytes(rows, vocab), &launch)) != MOE_OK ||
+      !launch)
+    return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t err = timed(MOE_K_FILTER, st, [&] {
+    return moe::launch_filter(rows, vocab, logits, temperature, top_p, probs, ws, st);
   });
   return status_of(err);
 }

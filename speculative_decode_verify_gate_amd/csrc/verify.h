@@ -15,4 +15,10 @@ hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, 
                          const int32_t *x, const float *u, const uint32_t *r, int32_t *n_acc,
                          int32_t *out, void *ws, hipStream_t st);
 
+// softmax(logits / temperature) then top-p filtering (rows x V fp32 in and
+// out), chunked over the chip through a workspace of filter_ws_bytes.
+size_t filter_ws_bytes(int rows, int V);
+hipError_t launch_filter(int rows, int V, const float *logits, float temperature, float top_p,
+                         float *probs, void *ws, hipStream_t st);
+
 }  // namespace moe

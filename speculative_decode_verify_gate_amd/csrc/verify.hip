@@ -371,7 +371,349 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
   if (tid == 0) a.n_acc[s] = istar;
 }
 
+// ---- the distributions from the logits (the verify phase of the same page:
+// softmax(logits / temperature), then top-p filtering, the same settings for
+// the verifier and the draft).
+//   top-p: the tokens kept are the shortest run in the order (probability
+//   descending, index ascending) whose probability reaches top_p, the token
+//   that reaches it included.  The decision uses integer masses
+//   floor(P * 2^40) against ceil(top_p * W), W their total, so it is exact
+//   and independent of summation order: a radix select over the
+//   probability bits (non-negative floats order like their bits; 8 bits a
+//   level, mass histograms) finds the probability K of the last kept token;
+//   of the tokens tied at K (all of equal mass) the first ones in index
+//   order are kept.  The kept tokens are renormalised by their mass.
+// Work split: a row is cut into kFChunk-entry chunks, one workgroup each,
+// so a few rows still fill the chip.  A short chain of launches passes
+// per-chunk results through the workspace; every workgroup of a row reduces
+// the previous launch's chunk results in the same fixed order, so all of
+// them derive the same row-wide decision:
+//   stat:  chunk max m_c and sum of exp(z - m_c), z = logit / T;
+//   prob:  the row's max and sum, P = exp(z - M) / S written to the output,
+//          and (top-p) the chunk's mass histogram of the top 8 bits added
+//          into the row's level histogram (64-bit integer atomics: the sum
+//          does not depend on their order);
+//   level: the row's selected bin of the previous level, then the chunk's
+//          histogram of the next 8 bits among the entries matching the
+//          prefix so far (three launches; the last also keeps each chunk's
+//          own histogram);
+//   write: the last level's decision, the ties ranked across chunks by the
+//          chunks' tie masses, and the kept entries renormalised.
+constexpr int kFThreads = 256;
+constexpr int kFPer = 16;
+constexpr int kFChunk = kFThreads * kFPer;  // 4096 entries per workgroup
+constexpr int kFWaves = kFThreads / 64;
+
+struct FilterArgs {
+  int V, chunks;
+  float temperature;
+  double top_p;
+  const float *logits;
+  float *probs;
+  float2 *stat;        // [rows][chunks]: (chunk max, sum of exp relative to it)
+  uint64_t *rowhist;   // [rows][4][256] mass histograms of the four levels
+  uint64_t *hist0;     // [rows][chunks][256] each chunk's last-level histogram
+  uint64_t *state;     // [rows][4]: prefix, mask, mass above, target
+};
+
+__device__ inline uint64_t mass_of(float p) { return (uint64_t)((double)p * kQuant); }
+
+template <class T, class Op>
+__device__ inline T block_all(T v, T *scratch, Op op) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = op(v, (T)__shfl_xor(v, m, 64));
+  __syncthreads();
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  T r = scratch[0];
+  for (int w = 1; w < kFWaves; ++w) r = op(r, scratch[w]);
+  return r;
+}
+
+// This workgroup's chunk: entries j = c0 + k * kFThreads + tid, k < kFPer,
+// loaded all at once (-inf past the row).
+__device__ inline void load_chunk(const float *row, int V, int c0, float (&v)[kFPer]) {
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    const int j = c0 + k * kFThreads + threadIdx.x;
+    v[k] = j < V ? row[j] : -INFINITY;
+  }
+}
+
+// The row's max and sum of exponentials from the chunks' (max, sum), in
+// chunk order (every workgroup of the row gets the same bits).
+__device__ inline float2 row_stat(const float2 *st, int chunks, float *fs) {
+  float m = -INFINITY;
+  for (int c = threadIdx.x; c < chunks; c += kFThreads) m = fmaxf(m, st[c].x);
+  m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
+  __shared__ float s_sum;
+  if (threadIdx.x == 0) {
+    float S = 0.f;
+    for (int c = 0; c < chunks; ++c)
+      if (st[c].x != -INFINITY) S += st[c].y * expf(st[c].x - m);
+    s_sum = S;
+  }
+  __syncthreads();
+  return make_float2(m, s_sum);
+}
+
+__global__ __launch_bounds__(kFThreads) void filter_stat_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x;
+  __shared__ float fs[kFWaves];
+  float v[kFPer];
+  load_chunk(a.logits + (size_t)row * a.V, a.V, c * kFChunk, v);
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) m = fmaxf(m, v[k] / a.temperature);
+  m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
+  float S = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kFPer; ++k) S += expf(v[k] / a.temperature - m);
+  }
+  S = block_all(S, fs, [](float x, float y) { return x + y; });
+  if (threadIdx.x == 0) a.stat[(size_t)row * a.chunks + c] = make_float2(m, S);
+  // the row's level histograms start empty (filled by the later launches)
+  if (c == 0 && a.top_p < 1.0)
+    for (int i = threadIdx.x; i < 4 * 256; i += kFThreads) a.rowhist[(size_t)row * 1024 + i] = 0;
+}
+
+// Selection at one level: the row's bin (h: the level's 256 row bins) where
+// the mass counted from the top reaches the target.  Updates prefix / mask / above; returns the bin's mass.
+// With top_p > 0 (the first level, whose histograms hold every entry) the
+// target is first set to ceil(top_p * W), W the total mass.
+__device__ inline uint64_t select_level(const uint64_t *h, int shift, uint64_t &target,
+                                        uint32_t &prefix, uint32_t &mask, uint64_t &above,
+                                        double top_p = 0.0) {
+  __shared__ uint64_t bins[256];
+  __shared__ uint32_t s_digit;
+  __shared__ uint64_t s_above, s_bin, s_target;
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int b = tid; b < 256; b += kFThreads) bins[b] = h[b];
+  __syncthreads();
+  if (tid < 64) {
+    uint64_t own[4], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      own[i] = bins[4 * lane + i];
+      tot += own[i];
+    }
+    uint64_t suf = tot;  // inclusive sum over lanes >= this lane
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t lo = __shfl_down((uint32_t)suf, d, 64);
+      const uint32_t hi = __shfl_down((uint32_t)(suf >> 32), d, 64);
+      if (lane + d < 64) suf += ((uint64_t)hi << 32) | lo;
+    }
+    uint64_t tg = target;
+    if (top_p > 0.0) {
+      const uint32_t lo = __shfl((uint32_t)suf, 0, 64), hi = __shfl((uint32_t)(suf >> 32), 0, 64);
+      const uint64_t W = ((uint64_t)hi << 32) | lo;  // every bin: the total mass
+      tg = (uint64_t)ceil(top_p * (double)W);
+      tg = tg < 1 ? 1 : tg;
+      if (lane == 0) s_target = tg;
+    }
+    uint64_t c = above + (suf - tot);  // mass above bin 4 lane + 3
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (c < tg && c + own[i] >= tg) {
+        s_digit = (uint32_t)(4 * lane + i);
+        s_above = c;
+        s_bin = own[i];
+      }
+      c += own[i];
+    }
+  }
+  __syncthreads();
+  if (top_p > 0.0) target = s_target;
+  prefix |= s_digit << shift;
+  mask |= 0xFFu << shift;
+  above = s_above;
+  const uint64_t bin = s_bin;
+  __syncthreads();
+  return bin;
+}
+
+// The chunk's mass histogram of bits [shift, shift+8) among entries matching
+// prefix under mask: added into the row's bins rh (device-scope integer
+// atomics) and, if own is given, also stored there for this chunk alone.
+__device__ inline void chunk_hist(const float (&p)[kFPer], int shift, uint32_t prefix,
+                                  uint32_t mask, uint64_t *rh, uint64_t *own) {
+  __shared__ unsigned long long lh[kFWaves][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int b = lane; b < 256; b += 64) lh[wave][b] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    const uint32_t key = __float_as_uint(p[k]);
+    if ((key & mask) == prefix && p[k] > 0.f)
+      atomicAdd(&lh[wave][(key >> shift) & 255u], (unsigned long long)mass_of(p[k]));
+  }
+  __syncthreads();
+  for (int b = tid; b < 256; b += kFThreads) {
+    uint64_t t = 0;
+    for (int w = 0; w < kFWaves; ++w) t += lh[w][b];
+    if (t) atomicAdd((unsigned long long *)&rh[b], (unsigned long long)t);
+    if (own) own[b] = t;
+  }
+}
+
+// The row's histogram of the level at bit `shift` (24, 16, 8, 0).
+__device__ inline uint64_t *level_hist(const FilterArgs &a, int row, int shift) {
+  return a.rowhist + (size_t)row * 1024 + (size_t)(3 - shift / 8) * 256;
+}
+
+__global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x;
+  __shared__ float fs[kFWaves];
+  const float2 ms = row_stat(a.stat + (size_t)row * a.chunks, a.chunks, fs);
+  float v[kFPer];
+  const int c0 = c * kFChunk;
+  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, v);
+  float *out = a.probs + (size_t)row * a.V;
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    const int j = c0 + k * kFThreads + threadIdx.x;
+    v[k] = expf(v[k] / a.temperature - ms.x) / ms.y;  // 0 past the row
+    if (j < a.V) out[j] = v[k];
+  }
+  if (a.top_p >= 1.0) return;
+  chunk_hist(v, 24, 0u, 0u, level_hist(a, row, 24), nullptr);
+}
+
+// Level launches: shift = 16, 8, 0, each reading the level above's
+// histograms and writing its own.
+__global__ __launch_bounds__(kFThreads) void filter_level_kernel(FilterArgs a, int shift) {
+  const int row = blockIdx.y, c = blockIdx.x;
+  uint64_t *st = a.state + (size_t)row * 4;
+  uint32_t prefix = 0, mask = 0;
+  uint64_t above = 0, target = 0;
+  if (shift != 16) {
+    prefix = (uint32_t)st[0];
+    mask = (uint32_t)st[1];
+    above = st[2];
+    target = st[3];
+  }
+  // the first selection (level 24) also sets the target from the total
+  select_level(level_hist(a, row, shift + 8), shift + 8, target, prefix, mask, above,
+               shift == 16 ? a.top_p : 0.0);
+  if (c == 0 && threadIdx.x == 0) {
+    st[0] = prefix;
+    st[1] = mask;
+    st[2] = above;
+    st[3] = target;
+  }
+  float p[kFPer];
+  const float *out = a.probs + (size_t)row * a.V;
+  const int c0 = c * kFChunk;
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    const int j = c0 + k * kFThreads + threadIdx.x;
+    p[k] = j < a.V ? out[j] : 0.f;
+  }
+  chunk_hist(p, shift, prefix, mask, level_hist(a, row, shift),
+             shift == 0 ? a.hist0 + ((size_t)row * a.chunks + c) * 256 : nullptr);
+}
+
+__global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const uint64_t *last_h = a.hist0 + (size_t)row * a.chunks * 256;  // per chunk
+  const uint64_t *st = a.state + (size_t)row * 4;
+  uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
+  uint64_t above = st[2];
+  uint64_t target = st[3];
+  const uint64_t bin = select_level(level_hist(a, row, 0), 0, target, prefix, mask, above);
+  const float pk = __uint_as_float(prefix);  // the last kept probability
+  const uint64_t mk = mass_of(pk);            // > 0: the target lies in positive mass
+  const uint64_t ties = bin / mk;             // tokens tied at pk, all of mass mk
+  const uint64_t keep = (target - above + mk - 1) / mk;
+  // ties before this chunk (each chunk's last-level bin of pk holds its ties)
+  __shared__ uint64_t s_before;
+  if (tid == 0) {
+    uint64_t b = 0;
+    for (int cc = 0; cc < c; ++cc) b += last_h[(size_t)cc * 256 + (prefix & 255u)] / mk;
+    s_before = b;
+  }
+  __syncthreads();
+  float *out = a.probs + (size_t)row * a.V;
+  const int c0 = c * kFChunk;
+  float p[kFPer];
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    const int j = c0 + k * kFThreads + tid;
+    p[k] = j < a.V ? out[j] : 0.f;
+  }
+  // rank of this chunk's ties in index order: k-major rows of kFThreads
+  // consecutive entries, counted with wave ballots
+  __shared__ uint32_t wcnt[kFPer][kFWaves];
+  const int wave = tid >> 6;
+  uint64_t bal[kFPer];
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    bal[k] = __ballot(p[k] == pk && p[k] > 0.f);
+    if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
+  }
+  __syncthreads();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t kept_mass = above + (keep < ties ? keep : ties) * mk;
+  const float total = (float)((double)kept_mass / kQuant);
+  uint64_t rank = s_before;
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    uint32_t before_w = 0, all_w = 0;
+    for (int w = 0; w < kFWaves; ++w) {
+      before_w += w < wave ? wcnt[k][w] : 0u;
+      all_w += wcnt[k][w];
+    }
+    const int j = c0 + k * kFThreads + tid;
+    const bool tie = p[k] == pk && p[k] > 0.f;
+    const uint64_t my_rank = rank + before_w + __popcll(bal[k] & below);
+    const bool kept = p[k] > pk || (tie && my_rank < keep);
+    if (j < a.V) out[j] = kept ? p[k] / total : 0.f;
+    rank += all_w;
+  }
+}
+
 }  // namespace
+
+int filter_chunks(int V) { return (V + kFChunk - 1) / kFChunk; }
+
+size_t filter_ws_bytes(int rows, int V) {
+  const size_t ch = (size_t)filter_chunks(V);
+  return align_up((size_t)rows * ch * sizeof(float2), 256) +
+         align_up((size_t)rows * 4 * 256 * sizeof(uint64_t), 256) +
+         align_up((size_t)rows * ch * 256 * sizeof(uint64_t), 256) +
+         align_up((size_t)rows * 4 * sizeof(uint64_t), 256);
+}
+
+hipError_t launch_filter(int rows, int V, const float *logits, float temperature, float top_p,
+                         float *probs, void *ws, hipStream_t st) {
+  FilterArgs a{};
+  a.V = V;
+  a.chunks = filter_chunks(V);
+  a.temperature = temperature;
+  a.top_p = top_p;
+  a.logits = logits;
+  a.probs = probs;
+  unsigned char *b = (unsigned char *)ws;
+  a.stat = (float2 *)b;
+  b += align_up((size_t)rows * a.chunks * sizeof(float2), 256);
+  a.rowhist = (uint64_t *)b;
+  b += align_up((size_t)rows * 4 * 256 * sizeof(uint64_t), 256);
+  a.hist0 = (uint64_t *)b;
+  b += align_up((size_t)rows * a.chunks * 256 * sizeof(uint64_t), 256);
+  a.state = (uint64_t *)b;
+  const dim3 grid(a.chunks, rows);
+  hipLaunchKernelGGL(filter_stat_kernel, grid, dim3(kFThreads), 0, st, a);
+  hipLaunchKernelGGL(filter_prob_kernel, grid, dim3(kFThreads), 0, st, a);
+  if (top_p < 1.f) {
+    for (int shift = 16; shift >= 0; shift -= 8)
+      hipLaunchKernelGGL(filter_level_kernel, grid, dim3(kFThreads), 0, st, a, shift);
+    hipLaunchKernelGGL(filter_write_kernel, grid, dim3(kFThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
 
 int verify_chunks(int V) { return (V + kVChunk - 1) / kVChunk; }
 

@@ -72,6 +72,13 @@ hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, 
   ++g_launches;
   return hipSuccess;
 }
+size_t filter_ws_bytes(int rows, int V) { return (size_t)rows * (V / 4096 + 1) * 4200; }
+hipError_t launch_filter(int rows, int V, const float *lg, float T, float top_p, float *out,
+                         void *ws, hipStream_t) {
+  CHECK(rows >= 1 && V >= 1 && lg && out && ws && T > 0.f && top_p > 0.f && top_p <= 1.f);
+  ++g_launches;
+  return hipSuccess;
+}
 }  // namespace moe
 
 static void *fake(size_t off = 0) { return (void *)(uintptr_t)(0x100000 + off); }
@@ -183,6 +190,16 @@ int main() {
                           (int32_t *)fake(), (int32_t *)fake(), ws.p, &have, nullptr) == MOE_OK);
   }
   CHECK(moe_pack_weights(&s, 2, fake(), fake(), fake(1 << 30), fake(3u << 29), nullptr) == MOE_OK);
+  CHECK(moe_verify_probs(36, 129280, (float *)fake(), 0.7f, 0.9f, (float *)fake(1u << 30),
+                         nullptr, &nb, nullptr) == MOE_OK && nb > 0);
+  {
+    Buf ws(nb);
+    size_t have = nb;
+    CHECK(moe_verify_probs(36, 129280, (float *)fake(), 0.7f, 0.9f, (float *)fake(1u << 30),
+                           ws.p, &have, nullptr) == MOE_OK);
+  }
+  CHECK(moe_verify_probs(2, 1000, (float *)fake(), 0.7f, 0.9f, (float *)fake(100), nullptr, &nb,
+                         nullptr) == MOE_ERR_INVALID_ARG);  // overlapping
   std::printf("abi driver: %d launches described, %d failed checks\n", moe::g_launches, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

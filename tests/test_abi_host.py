@@ -258,3 +258,24 @@ def test_stack_pass_validation_and_workspace():
                dict(n=0), dict(n=65)):
         assert _stack(s, **kw)[0] == -1, kw
     assert _stack(s, L=3, n=16, engine=1, ws=FAKE, nbytes=need3 - 1)[0] == -3
+
+
+def test_verify_probs_validation():
+    lib = B.load()
+    ok = dict(rows=2, V=1000, lg=FAKE, T=0.7, p=0.9, out=C.c_void_p(0x900000))
+    bad = [dict(rows=0), dict(V=0), dict(V=(1 << 24) + 1), dict(lg=None), dict(out=None),
+           dict(T=0.0), dict(T=-1.0), dict(T=float("inf")), dict(T=float("nan")), dict(p=0.0),
+           dict(p=1.5), dict(p=float("nan")), dict(out=C.c_void_p(0x100000 + 4000))]  # overlap
+    nb = C.c_size_t(0)
+    for kw in bad:
+        a = dict(ok, **kw)
+        rc = lib.moe_verify_probs(a["rows"], a["V"], a["lg"], a["T"], a["p"], a["out"], None,
+                                  C.byref(nb), None)
+        assert rc == -1, kw
+    # workspace query: chunk statistics, two histogram levels and the row state
+    assert lib.moe_verify_probs(36, 102400, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None, C.byref(nb),
+                                None) == 0
+    chunks = (102400 + 4095) // 4096
+    assert nb.value >= 36 * chunks * (8 + 256 * 8) + 36 * (4 * 256 * 8 + 32)
+    assert lib.moe_verify_probs(65536, 16, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None,
+                                C.byref(nb), None) == -2

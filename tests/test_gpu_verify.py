@@ -164,3 +164,98 @@ def test_draw_without_weight_gives_no_token():
     assert n_g[0] == n_o[0] == 1
     np.testing.assert_array_equal(t_g, t_o)
     assert t_g[0, 1] == -1
+
+
+# ------------------------------------------------ logits -> filtered distributions
+
+FILTER_TOL = 2e-5  # relative: what fp32 softmax arithmetic can move a probability by
+
+
+def _check_nucleus(got, lg, T, top_p):
+    """The GPU's filtered rows against the exact (fp64) softmax: its kept set
+    differs from the oracle's only by near-ties of the boundary probability,
+    is itself a valid nucleus up to the tolerance (its exact mass reaches
+    top_p, and would not without its smallest member), and its values are
+    the exact probabilities renormalised over it."""
+    full, _ = O.filter_probs(lg, T, 1.0)
+    ref, _ = O.filter_probs(lg, T, top_p)
+    for g, f, r in zip(got.reshape(-1, lg.shape[-1]), full.reshape(-1, lg.shape[-1]),
+                       ref.reshape(-1, lg.shape[-1])):
+        kg, ko = g > 0, r > 0
+        diff = kg ^ ko
+        last = f[ko].min()
+        assert np.all(np.abs(f[diff] - last) <= FILTER_TOL * last), "nuclei differ beyond near-ties"
+        mass = f[kg].sum()
+        if top_p < 1:
+            assert mass >= top_p * (1 - FILTER_TOL), "GPU nucleus below top_p"
+            assert mass - f[kg].min() < top_p * (1 + FILTER_TOL), "GPU nucleus not minimal"
+        np.testing.assert_allclose(g[kg], f[kg] / mass, rtol=FILTER_TOL, atol=1e-12)
+        assert abs(g.sum() - 1.0) < 1e-4
+
+
+def _logit_rows(rng, rows, V, ties=False, masked=False):
+    lg = (rng.standard_normal((rows, V)) * rng.uniform(0.5, 4.0, (rows, 1))).astype(np.float32)
+    if ties:
+        lg[:, : V // 4] = lg[:, :1]
+    if masked:
+        lg[rng.random((rows, V)) < 0.05] = -np.inf
+        lg[:, 0] = 1.0
+    return lg
+
+
+@pytest.mark.parametrize("V", [1, 5, 1000, 4099, 102400, 152064])
+@pytest.mark.parametrize("T,top_p", [(1.0, 1.0), (0.7, 0.9), (1.3, 0.5), (0.3, 0.95)])
+def test_filter_matches_oracle(V, T, top_p):
+    rng = np.random.default_rng(V + int(T * 100) + int(top_p * 1000))
+    _say(f"[filter] V={V} T={T} top_p={top_p}")
+    rows = 6 if V > 10000 else 12
+    for ties, masked in ((False, False), (True, False), (False, True)):
+        lg = _logit_rows(rng, rows, V, ties, masked)
+        got = B.verify_probs(torch.from_numpy(lg).cuda(), T, top_p).cpu().numpy()
+        _check_nucleus(got, lg, T, top_p)
+        if ties:
+            # exact ties are decided by index on both sides: same kept set
+            ref, _ = O.filter_probs(lg, T, top_p)
+            f, _ = O.filter_probs(lg, T, 1.0)
+            for g, r, fr in zip(got, ref, f):
+                if np.count_nonzero(fr == fr[0]) > 1 and r[0] > 0 and (r > 0).sum() < V:
+                    tied = fr == fr[0]
+                    np.testing.assert_array_equal(g[tied] > 0, r[tied] > 0)
+
+
+def test_filter_nucleus_hand_computed():
+    lg = np.log(np.array([[0.2, 0.5, 0.3], [0.2, 0.5, 0.3], [0.2, 0.5, 0.3]], np.float32))
+    cases = [(0.45, [0, 1, 0]), (0.7, [0, 0.625, 0.375]), (0.81, [0.2, 0.5, 0.3])]
+    for top_p, want in cases:
+        got = B.verify_probs(torch.from_numpy(lg).cuda(), 1.0, top_p).cpu().numpy()
+        np.testing.assert_allclose(got, np.array([want] * 3), atol=1e-6)
+    # ties: the lower indices first
+    got = B.verify_probs(torch.tensor([[1.0, 1.0, 1.0, 0.0]], device="cuda"), 1.0, 0.5)
+    np.testing.assert_allclose(got.cpu().numpy(), [[0.5, 0.5, 0, 0]], atol=1e-7)
+
+
+def test_round_from_logits_matches_oracle():
+    """Logits -> filtered p and q on the GPU -> the GPU round; the oracle's
+    round on those same distributions decides identically."""
+    rng = np.random.default_rng(31)
+    S, gamma, V, T, top_p = 4, 6, 32000, 0.7, 0.9
+    vl = _logit_rows(rng, S * (gamma + 1), V).reshape(S, gamma + 1, V)
+    dl = (vl[:, :gamma] + 0.5 * rng.standard_normal((S, gamma, V))).astype(np.float32)
+    p = B.verify_probs(torch.from_numpy(vl).cuda(), T, top_p)
+    q = B.verify_probs(torch.from_numpy(dl).cuda(), T, top_p)
+    qn = q.cpu().numpy()
+    x = np.array([[rng.choice(V, p=qn[s, i].astype(np.float64) / qn[s, i].astype(np.float64).sum())
+                   for i in range(gamma)] for s in range(S)], dtype=np.int32)
+    u = rng.random((S, gamma)).astype(np.float32)
+    r = rng.integers(0, 2**32, S, dtype=np.uint64)
+    n_g, t_g = _run_gpu(p.cpu().numpy(), qn, x, u, r, B.VERIFY_SAMPLING)
+    n_o, t_o = _run_oracle(p.cpu().numpy(), qn, x, u, r, B.VERIFY_SAMPLING)
+    np.testing.assert_array_equal(n_g, n_o)
+    np.testing.assert_array_equal(t_g, t_o)
+    # every kept or drawn token lies in the verifier's nucleus
+    pn = p.cpu().numpy()
+    for s in range(S):
+        for i in range(n_g[s] + 1):
+            tok = t_g[s, i]
+            if tok >= 0:
+                assert pn[s, min(i, gamma)][tok] > 0 or i < n_g[s]
