@@ -379,30 +379,38 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 //   that reaches it included.  The decision uses integer masses
 //   floor(P * 2^40) against ceil(top_p * W), W their total, so it is exact
 //   and independent of summation order: a radix select over the
-//   probability bits (non-negative floats order like their bits; 8 bits a
-//   level, mass histograms) finds the probability K of the last kept token;
+//   probability bits (non-negative floats order like their bits, and P <= 1
+//   leaves bits 31-30 zero) finds the probability K of the last kept token;
 //   of the tokens tied at K (all of equal mass) the first ones in index
-//   order are kept.  The kept tokens are renormalised by their mass.
+//   order are kept, i.e. those up to an index cut.  The kept tokens are
+//   renormalised by their mass.
 // Work split: a row is cut into kFChunk-entry chunks, one workgroup each,
-// so a few rows still fill the chip.  A short chain of launches passes
-// per-chunk results through the workspace; every workgroup of a row reduces
-// the previous launch's chunk results in the same fixed order, so all of
-// them derive the same row-wide decision:
-//   stat:  chunk max m_c and sum of exp(z - m_c), z = logit / T;
-//   prob:  the row's max and sum, P = exp(z - M) / S written to the output,
-//          and (top-p) the chunk's mass histogram of the top 8 bits added
-//          into the row's level histogram (64-bit integer atomics: the sum
-//          does not depend on their order);
-//   level: the row's selected bin of the previous level, then the chunk's
-//          histogram of the next 8 bits among the entries matching the
-//          prefix so far (three launches; the last also keeps each chunk's
-//          own histogram);
-//   write: the last level's decision, the ties ranked across chunks by the
-//          chunks' tie masses, and the kept entries renormalised.
+// so a few rows still fill the chip, each thread holding four 16-byte
+// groups of consecutive entries.  Four launches pass results on through
+// the workspace:
+//   stat:   chunk max m_c and sum of exp(z - m_c), z = logit / T; the row's
+//           histogram and counters cleared;
+//   prob:   the row's max and sum (a fixed-order reduction of the chunks'
+//           pairs, so every workgroup of the row gets the same bits),
+//           P = exp(z - M) / S written to the output, and (top-p) the
+//           chunk's mass histogram of bits 29-22 added into the row's
+//           (64-bit integer atomics: the sum does not depend on their
+//           order); the row's last workgroup selects the bin;
+//   gather: the chunk's entries in the selected bin (candidates) appended
+//           to the row's candidate list; the row's last workgroup finds K
+//           among them (bits 21-10, then 9-0), the number of ties at K to
+//           keep and, when only some are kept, the index cut (bits 23-12,
+//           then 11-0 of the tied indices, by counts);
+//   write:  the kept entries renormalised, the rest zeroed.
+// "The row's last workgroup" is the last one to arrive at the row's
+// arrival counter; what the others hand over to it in the same launch is
+// written and read with coherent accesses.
 constexpr int kFThreads = 256;
-constexpr int kFPer = 16;
+constexpr int kFGroups = 4;                 // 16-byte groups per thread
+constexpr int kFPer = 4 * kFGroups;         // 16 entries per thread
 constexpr int kFChunk = kFThreads * kFPer;  // 4096 entries per workgroup
 constexpr int kFWaves = kFThreads / 64;
+constexpr int kFirstShift = 22;             // first level: bits 29-22, 256 bins
 
 struct FilterArgs {
   int V, chunks;
@@ -411,9 +419,10 @@ struct FilterArgs {
   const float *logits;
   float *probs;
   float2 *stat;        // [rows][chunks]: (chunk max, sum of exp relative to it)
-  uint64_t *rowhist;   // [rows][4][256] mass histograms of the four levels
-  uint64_t *hist0;     // [rows][chunks][256] each chunk's last-level histogram
-  uint64_t *state;     // [rows][4]: prefix, mask, mass above, target
+  uint64_t *rowhist;   // [rows][256] first-level mass histogram
+  uint64_t *cand;      // [rows][V] candidates: probability bits | index << 32
+  uint64_t *state;     // [rows][8]: prefix, mask, mass above, target; K, index cut, kept mass
+  unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
 };
 
 __device__ inline uint64_t mass_of(float p) { return (uint64_t)((double)p * kQuant); }
@@ -431,248 +440,375 @@ __device__ inline T block_all(T v, T *scratch, Op op) {
   return r;
 }
 
-// This workgroup's chunk: entries j = c0 + k * kFThreads + tid, k < kFPer,
-// loaded all at once (-inf past the row).
-__device__ inline void load_chunk(const float *row, int V, int c0, float (&v)[kFPer]) {
+// Exclusive prefix of a per-thread count over the workgroup (thread order)
+// and the workgroup's total.
+__device__ inline uint32_t block_exclusive(uint32_t n, uint32_t &total) {
+  __shared__ uint32_t wtot[kFWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = n;
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    const int j = c0 + k * kFThreads + threadIdx.x;
-    v[k] = j < V ? row[j] : -INFINITY;
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  __syncthreads();
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    before += w < wave ? wtot[w] : 0u;
+    total += wtot[w];
+  }
+  return before + inc - n;
+}
+
+// Entry of this thread's group g: c0 + (g * kFThreads + tid) * 4 (+ 0..3).
+__device__ inline int entry_of(int c0, int g) { return c0 + (g * kFThreads + (int)threadIdx.x) * 4; }
+
+// This workgroup's chunk, `fill` past the row: 16-byte loads when the row
+// is 16-byte aligned and V a multiple of 4 (then a group is all in or all
+// out of the row), else per entry.
+__device__ inline void load_chunk(const float *row, int V, int c0, float (&v)[kFPer], float fill) {
+  const bool vec = (V & 3) == 0 && ((uintptr_t)row & 15) == 0;
+#pragma unroll
+  for (int g = 0; g < kFGroups; ++g) {
+    const int j = entry_of(c0, g);
+    if (vec) {
+      const float4 t = j < V ? *(const float4 *)(row + j) : make_float4(fill, fill, fill, fill);
+      v[4 * g] = t.x;
+      v[4 * g + 1] = t.y;
+      v[4 * g + 2] = t.z;
+      v[4 * g + 3] = t.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * g + e] = j + e < V ? row[j + e] : fill;
+    }
   }
 }
 
-// The row's max and sum of exponentials from the chunks' (max, sum), in
-// chunk order (every workgroup of the row gets the same bits).
+__device__ inline void store_chunk(float *row, int V, int c0, const float (&v)[kFPer]) {
+  const bool vec = (V & 3) == 0 && ((uintptr_t)row & 15) == 0;
+#pragma unroll
+  for (int g = 0; g < kFGroups; ++g) {
+    const int j = entry_of(c0, g);
+    if (vec) {
+      if (j < V) *(float4 *)(row + j) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j + e < V) row[j + e] = v[4 * g + e];
+    }
+  }
+}
+
+// The row's max and sum of exponentials from the chunks' (max, sum): a
+// fixed-order reduction, so every workgroup of the row gets the same bits.
 __device__ inline float2 row_stat(const float2 *st, int chunks, float *fs) {
   float m = -INFINITY;
   for (int c = threadIdx.x; c < chunks; c += kFThreads) m = fmaxf(m, st[c].x);
   m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
-  __shared__ float s_sum;
-  if (threadIdx.x == 0) {
-    float S = 0.f;
-    for (int c = 0; c < chunks; ++c)
-      if (st[c].x != -INFINITY) S += st[c].y * expf(st[c].x - m);
-    s_sum = S;
+  float S = 0.f;
+  for (int c = threadIdx.x; c < chunks; c += kFThreads) {
+    const float2 t = st[c];
+    if (t.x != -INFINITY) S += t.y * expf(t.x - m);
   }
-  __syncthreads();
-  return make_float2(m, s_sum);
+  S = block_all(S, fs, [](float x, float y) { return x + y; });
+  return make_float2(m, S);
 }
 
 __global__ __launch_bounds__(kFThreads) void filter_stat_kernel(FilterArgs a) {
   const int row = blockIdx.y, c = blockIdx.x;
   __shared__ float fs[kFWaves];
   float v[kFPer];
-  load_chunk(a.logits + (size_t)row * a.V, a.V, c * kFChunk, v);
+  load_chunk(a.logits + (size_t)row * a.V, a.V, c * kFChunk, v, -INFINITY);
+  // z = logit * (1 / T): one rounding more than a division, but monotone
+  // in the logit (equal logits stay equal), and the same in every launch
+  const float inv_t = 1.0f / a.temperature;
   float m = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) m = fmaxf(m, v[k] / a.temperature);
+  for (int k = 0; k < kFPer; ++k) {
+    v[k] *= inv_t;
+    m = fmaxf(m, v[k]);
+  }
   m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
   float S = 0.f;
   if (m != -INFINITY) {
 #pragma unroll
-    for (int k = 0; k < kFPer; ++k) S += expf(v[k] / a.temperature - m);
+    for (int k = 0; k < kFPer; ++k) S += expf(v[k] - m);
   }
   S = block_all(S, fs, [](float x, float y) { return x + y; });
   if (threadIdx.x == 0) a.stat[(size_t)row * a.chunks + c] = make_float2(m, S);
-  // the row's level histograms start empty (filled by the later launches)
-  if (c == 0 && a.top_p < 1.0)
-    for (int i = threadIdx.x; i < 4 * 256; i += kFThreads) a.rowhist[(size_t)row * 1024 + i] = 0;
+  // the row's histogram and counters start at zero for the later launches
+  if (a.top_p < 1.0 && c == 0) {
+    a.rowhist[(size_t)row * 256 + threadIdx.x] = 0;
+    if (threadIdx.x < 4) a.count[(size_t)row * 4 + threadIdx.x] = 0u;
+  }
 }
 
-// Selection at one level: the row's bin (h: the level's 256 row bins) where
-// the mass counted from the top reaches the target.  Updates prefix / mask / above; returns the bin's mass.
-// With top_p > 0 (the first level, whose histograms hold every entry) the
-// target is first set to ceil(top_p * W), W the total mass.
+// Selection over NB mass bins h (bits [shift, shift + log2 NB) of the
+// probability, in global memory written by this launch's other workgroups
+// and read coherently, or in LDS): the bin where the mass counted from the
+// top reaches the target.  Updates prefix / mask / above; returns the
+// bin's mass.  With top_p > 0 (the first level, whose histogram holds
+// every entry) the target is first set to ceil(top_p * W), W the total.
+template <int NB, bool GLOBAL>
 __device__ inline uint64_t select_level(const uint64_t *h, int shift, uint64_t &target,
                                         uint32_t &prefix, uint32_t &mask, uint64_t &above,
                                         double top_p = 0.0) {
-  __shared__ uint64_t bins[256];
+  constexpr int PT = NB / kFThreads;  // consecutive bins per thread
+  static_assert(PT >= 1 && NB % kFThreads == 0, "bins per thread");
+  __shared__ uint64_t wsum[kFWaves];
   __shared__ uint32_t s_digit;
-  __shared__ uint64_t s_above, s_bin, s_target;
-  const int tid = threadIdx.x, lane = tid & 63;
-  for (int b = tid; b < 256; b += kFThreads) bins[b] = h[b];
-  __syncthreads();
-  if (tid < 64) {
-    uint64_t own[4], tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      own[i] = bins[4 * lane + i];
-      tot += own[i];
-    }
-    uint64_t suf = tot;  // inclusive sum over lanes >= this lane
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t lo = __shfl_down((uint32_t)suf, d, 64);
-      const uint32_t hi = __shfl_down((uint32_t)(suf >> 32), d, 64);
-      if (lane + d < 64) suf += ((uint64_t)hi << 32) | lo;
-    }
-    uint64_t tg = target;
-    if (top_p > 0.0) {
-      const uint32_t lo = __shfl((uint32_t)suf, 0, 64), hi = __shfl((uint32_t)(suf >> 32), 0, 64);
-      const uint64_t W = ((uint64_t)hi << 32) | lo;  // every bin: the total mass
-      tg = (uint64_t)ceil(top_p * (double)W);
-      tg = tg < 1 ? 1 : tg;
-      if (lane == 0) s_target = tg;
-    }
-    uint64_t c = above + (suf - tot);  // mass above bin 4 lane + 3
-#pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      if (c < tg && c + own[i] >= tg) {
-        s_digit = (uint32_t)(4 * lane + i);
-        s_above = c;
-        s_bin = own[i];
-      }
-      c += own[i];
-    }
-  }
-  __syncthreads();
-  if (top_p > 0.0) target = s_target;
-  prefix |= s_digit << shift;
-  mask |= 0xFFu << shift;
-  above = s_above;
-  const uint64_t bin = s_bin;
-  __syncthreads();
-  return bin;
-}
-
-// The chunk's mass histogram of bits [shift, shift+8) among entries matching
-// prefix under mask: added into the row's bins rh (device-scope integer
-// atomics) and, if own is given, also stored there for this chunk alone.
-__device__ inline void chunk_hist(const float (&p)[kFPer], int shift, uint32_t prefix,
-                                  uint32_t mask, uint64_t *rh, uint64_t *own) {
-  __shared__ unsigned long long lh[kFWaves][256];
+  __shared__ uint64_t s_above, s_bin;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int b = lane; b < 256; b += 64) lh[wave][b] = 0ull;
-  __syncthreads();
+  uint64_t own[PT], tot = 0;
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    const uint32_t key = __float_as_uint(p[k]);
-    if ((key & mask) == prefix && p[k] > 0.f)
-      atomicAdd(&lh[wave][(key >> shift) & 255u], (unsigned long long)mass_of(p[k]));
+  for (int i = 0; i < PT; ++i) own[i] = GLOBAL ? load_coherent64(h + tid * PT + i) : h[tid * PT + i];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) tot += own[i];
+  uint64_t suf = tot;  // inclusive sum over the lanes >= this lane of the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t lo = __shfl_down((uint32_t)suf, d, 64);
+    const uint32_t hi = __shfl_down((uint32_t)(suf >> 32), d, 64);
+    if (lane + d < 64) suf += ((uint64_t)hi << 32) | lo;
   }
   __syncthreads();
-  for (int b = tid; b < 256; b += kFThreads) {
-    uint64_t t = 0;
-    for (int w = 0; w < kFWaves; ++w) t += lh[w][b];
-    if (t) atomicAdd((unsigned long long *)&rh[b], (unsigned long long)t);
-    if (own) own[b] = t;
+  if (lane == 0) wsum[wave] = suf;  // the wave's total
+  __syncthreads();
+  uint64_t W = 0, later = 0;  // total; mass of the later waves' bins
+#pragma unroll
+  for (int w = 0; w < kFWaves; ++w) {
+    W += wsum[w];
+    later += w > wave ? wsum[w] : 0ull;
   }
+  uint64_t tg = target;
+  if (top_p > 0.0) {
+    tg = (uint64_t)ceil(top_p * (double)W);
+    tg = tg < 1 ? 1 : tg;
+  }
+  uint64_t c = above + later + (suf - tot);  // mass of the bins above this thread's
+#pragma unroll
+  for (int i = PT - 1; i >= 0; --i) {
+    if (c < tg && c + own[i] >= tg) {  // exactly one bin of the row
+      s_digit = (uint32_t)(tid * PT + i);
+      s_above = c;
+      s_bin = own[i];
+    }
+    c += own[i];
+  }
+  __syncthreads();
+  target = tg;
+  prefix |= s_digit << shift;
+  mask |= (uint32_t)(NB - 1) << shift;
+  above = s_above;
+  return s_bin;
 }
 
-// The row's histogram of the level at bit `shift` (24, 16, 8, 0).
-__device__ inline uint64_t *level_hist(const FilterArgs &a, int row, int shift) {
-  return a.rowhist + (size_t)row * 1024 + (size_t)(3 - shift / 8) * 256;
+// Over NB count bins h in LDS, in ascending bin order: the bin where the
+// running count, starting at base, reaches rank (1-based).  Sets base to
+// the count below that bin.
+template <int NB>
+__device__ inline uint32_t rank_bin(const uint32_t *h, uint32_t rank, uint32_t &base) {
+  constexpr int PT = NB / kFThreads;
+  __shared__ uint32_t s_digit, s_base;
+  uint32_t own[PT], tot = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    own[i] = h[threadIdx.x * PT + i];
+    tot += own[i];
+  }
+  uint32_t total;
+  uint32_t c = base + block_exclusive(tot, total);  // count below this thread's bins
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    if (c < rank && c + own[i] >= rank) {
+      s_digit = threadIdx.x * PT + i;
+      s_base = c;
+    }
+    c += own[i];
+  }
+  __syncthreads();
+  base = s_base;
+  return s_digit;
 }
 
+// After this workgroup's hand-over stores and atomics: true in the last
+// workgroup of the row to arrive (n arrivals in all).
+__device__ inline bool arrive_last(unsigned *ctr, unsigned n) {
+  __shared__ int s_last;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(ctr, 1u) == n - 1;
+  __syncthreads();
+  return s_last != 0;
+}
+
+// HIST: top_p < 1 (the first-level histogram and selection follow); the
+// plain softmax instantiation reserves no histogram LDS.
+template <bool HIST>
 __global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
-  const int row = blockIdx.y, c = blockIdx.x;
+  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   __shared__ float fs[kFWaves];
   const float2 ms = row_stat(a.stat + (size_t)row * a.chunks, a.chunks, fs);
   float v[kFPer];
   const int c0 = c * kFChunk;
-  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, v);
-  float *out = a.probs + (size_t)row * a.V;
+  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, v, -INFINITY);
+  // exp(z - M) <= 1 and 1 / S <= 1 (S >= 1: the max's own term), so P <= 1
+  // and its bits 31-30 are zero; 0 past the row
+  const float inv_t = 1.0f / a.temperature, inv_s = 1.0f / ms.y;
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    const int j = c0 + k * kFThreads + threadIdx.x;
-    v[k] = expf(v[k] / a.temperature - ms.x) / ms.y;  // 0 past the row
-    if (j < a.V) out[j] = v[k];
+  for (int k = 0; k < kFPer; ++k) v[k] = expf(v[k] * inv_t - ms.x) * inv_s;
+  store_chunk(a.probs + (size_t)row * a.V, a.V, c0, v);
+  if (!HIST) return;
+  // the first level: mass per value of bits 29-22, one LDS copy per wave
+  __shared__ unsigned long long lh[kFWaves][256];
+  for (int i = tid; i < kFWaves * 256; i += kFThreads) lh[i / 256][i % 256] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k)
+    if (v[k] > 0.f)
+      atomicAdd(&lh[wave][(__float_as_uint(v[k]) >> kFirstShift) & 255u],
+                (unsigned long long)mass_of(v[k]));
+  __syncthreads();
+  uint64_t *rh = a.rowhist + (size_t)row * 256;
+  {
+    const uint64_t t = lh[0][tid] + lh[1][tid] + lh[2][tid] + lh[3][tid];
+    if (t) atomicAdd((unsigned long long *)&rh[tid], (unsigned long long)t);
   }
-  if (a.top_p >= 1.0) return;
-  chunk_hist(v, 24, 0u, 0u, level_hist(a, row, 24), nullptr);
-}
-
-// Level launches: shift = 16, 8, 0, each reading the level above's
-// histograms and writing its own.
-__global__ __launch_bounds__(kFThreads) void filter_level_kernel(FilterArgs a, int shift) {
-  const int row = blockIdx.y, c = blockIdx.x;
-  uint64_t *st = a.state + (size_t)row * 4;
-  uint32_t prefix = 0, mask = 0;
+  if (!arrive_last(a.count + (size_t)row * 4, a.chunks)) return;
+  uint32_t prefix = 0, mask = 0xC0000000u;  // bits 31-30 are zero for every entry
   uint64_t above = 0, target = 0;
-  if (shift != 16) {
-    prefix = (uint32_t)st[0];
-    mask = (uint32_t)st[1];
-    above = st[2];
-    target = st[3];
-  }
-  // the first selection (level 24) also sets the target from the total
-  select_level(level_hist(a, row, shift + 8), shift + 8, target, prefix, mask, above,
-               shift == 16 ? a.top_p : 0.0);
-  if (c == 0 && threadIdx.x == 0) {
+  select_level<256, true>(rh, kFirstShift, target, prefix, mask, above, a.top_p);
+  if (tid == 0) {
+    uint64_t *st = a.state + (size_t)row * 8;
     st[0] = prefix;
     st[1] = mask;
     st[2] = above;
     st[3] = target;
   }
-  float p[kFPer];
-  const float *out = a.probs + (size_t)row * a.V;
-  const int c0 = c * kFChunk;
-#pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    const int j = c0 + k * kFThreads + threadIdx.x;
-    p[k] = j < a.V ? out[j] : 0.f;
+}
+
+// The row's last workgroup after the gather: K, the number of ties to keep
+// and the index cut, from the row's n candidates (coherent loads).
+__device__ inline void resolve_row(const FilterArgs &a, int row, const uint64_t *cand, uint32_t n) {
+  __shared__ unsigned long long lh[4096];  // mass bins, then count bins
+  uint32_t *lc = (uint32_t *)lh;
+  const int tid = threadIdx.x;
+  uint64_t *st = a.state + (size_t)row * 8;
+  uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
+  uint64_t above = st[2], target = st[3];
+  // bits 21-10
+  for (int i = tid; i < 4096; i += kFThreads) lh[i] = 0ull;
+  __syncthreads();
+  for (uint32_t i = tid; i < n; i += kFThreads) {
+    const uint32_t key = (uint32_t)load_coherent64(cand + i);
+    atomicAdd(&lh[(key >> 10) & 4095u], (unsigned long long)mass_of(__uint_as_float(key)));
   }
-  chunk_hist(p, shift, prefix, mask, level_hist(a, row, shift),
-             shift == 0 ? a.hist0 + ((size_t)row * a.chunks + c) * 256 : nullptr);
+  __syncthreads();
+  select_level<4096, false>((const uint64_t *)lh, 10, target, prefix, mask, above);
+  // bits 9-0 of the candidates under that prefix
+  for (int i = tid; i < 1024; i += kFThreads) lh[i] = 0ull;
+  __syncthreads();
+  for (uint32_t i = tid; i < n; i += kFThreads) {
+    const uint32_t key = (uint32_t)load_coherent64(cand + i);
+    if ((key & mask) == prefix) atomicAdd(&lh[key & 1023u], (unsigned long long)mass_of(__uint_as_float(key)));
+  }
+  __syncthreads();
+  const uint64_t bin = select_level<1024, false>((const uint64_t *)lh, 0, target, prefix, mask, above);
+  const uint32_t K = prefix;                       // the last kept probability's bits
+  const uint64_t mk = mass_of(__uint_as_float(K));  // > 0: the target lies in positive mass
+  const uint64_t ties = bin / mk;                  // all of equal mass mk
+  const uint64_t keep = (target - above + mk - 1) / mk;
+  uint32_t cut = 0xFFFFFFFFu;  // every tie kept
+  if (keep < ties) {
+    // the keep-th smallest index among the ties: counts of index bits
+    // 23-12, then of bits 11-0 within that bin
+    for (int i = tid; i < 4096; i += kFThreads) lc[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kFThreads) {
+      const uint64_t e = load_coherent64(cand + i);
+      if ((uint32_t)e == K) atomicAdd(&lc[(uint32_t)(e >> 32) >> 12], 1u);
+    }
+    __syncthreads();
+    uint32_t base = 0;
+    const uint32_t hi = rank_bin<4096>(lc, (uint32_t)keep, base);
+    __syncthreads();
+    for (int i = tid; i < 4096; i += kFThreads) lc[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kFThreads) {
+      const uint64_t e = load_coherent64(cand + i);
+      const uint32_t j = (uint32_t)(e >> 32);
+      if ((uint32_t)e == K && (j >> 12) == hi) atomicAdd(&lc[j & 4095u], 1u);
+    }
+    __syncthreads();
+    const uint32_t lo = rank_bin<4096>(lc, (uint32_t)keep, base);
+    cut = (hi << 12) | lo;
+  }
+  if (tid == 0) {
+    st[4] = K;
+    st[5] = cut;
+    st[6] = above + keep * mk;  // the kept mass
+  }
+}
+
+__global__ __launch_bounds__(kFThreads) void filter_gather_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const uint64_t *st = a.state + (size_t)row * 8;
+  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
+  float p[kFPer];
+  const int c0 = c * kFChunk;
+  load_chunk(a.probs + (size_t)row * a.V, a.V, c0, p, 0.f);
+  uint32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k)
+    mine += ((__float_as_uint(p[k]) & mask) == prefix && p[k] > 0.f) ? 1u : 0u;
+  uint32_t total;
+  const uint32_t off = block_exclusive(mine, total);
+  __shared__ uint32_t s_base;
+  if (tid == 0) s_base = total ? atomicAdd(a.count + (size_t)row * 4 + 2, total) : 0u;
+  __syncthreads();
+  uint64_t *cand = a.cand + (size_t)row * a.V;
+  uint32_t at = s_base + off;
+#pragma unroll
+  for (int g = 0; g < kFGroups; ++g) {
+    const int j = entry_of(c0, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = __float_as_uint(p[4 * g + e]);
+      if ((key & mask) == prefix && p[4 * g + e] > 0.f)
+        store_coherent64(cand + at++, (uint64_t)key | ((uint64_t)(j + e) << 32));
+    }
+  }
+  if (!arrive_last(a.count + (size_t)row * 4 + 1, a.chunks)) return;
+  const uint32_t n = __hip_atomic_load(a.count + (size_t)row * 4 + 2, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  resolve_row(a, row, cand, n);
 }
 
 __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
-  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const uint64_t *last_h = a.hist0 + (size_t)row * a.chunks * 256;  // per chunk
-  const uint64_t *st = a.state + (size_t)row * 4;
-  uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
-  uint64_t above = st[2];
-  uint64_t target = st[3];
-  const uint64_t bin = select_level(level_hist(a, row, 0), 0, target, prefix, mask, above);
-  const float pk = __uint_as_float(prefix);  // the last kept probability
-  const uint64_t mk = mass_of(pk);            // > 0: the target lies in positive mass
-  const uint64_t ties = bin / mk;             // tokens tied at pk, all of mass mk
-  const uint64_t keep = (target - above + mk - 1) / mk;
-  // ties before this chunk (each chunk's last-level bin of pk holds its ties)
-  __shared__ uint64_t s_before;
-  if (tid == 0) {
-    uint64_t b = 0;
-    for (int cc = 0; cc < c; ++cc) b += last_h[(size_t)cc * 256 + (prefix & 255u)] / mk;
-    s_before = b;
-  }
-  __syncthreads();
+  const int row = blockIdx.y, c = blockIdx.x;
+  const uint64_t *st = a.state + (size_t)row * 8;
+  const float pk = __uint_as_float((uint32_t)st[4]);  // the last kept probability
+  const uint32_t cut = (uint32_t)st[5];                // ties kept up to this index
+  const float total = (float)((double)st[6] / kQuant);
   float *out = a.probs + (size_t)row * a.V;
   const int c0 = c * kFChunk;
   float p[kFPer];
+  load_chunk(out, a.V, c0, p, 0.f);
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    const int j = c0 + k * kFThreads + tid;
-    p[k] = j < a.V ? out[j] : 0.f;
-  }
-  // rank of this chunk's ties in index order: k-major rows of kFThreads
-  // consecutive entries, counted with wave ballots
-  __shared__ uint32_t wcnt[kFPer][kFWaves];
-  const int wave = tid >> 6;
-  uint64_t bal[kFPer];
+  for (int g = 0; g < kFGroups; ++g) {
+    const uint32_t j = (uint32_t)entry_of(c0, g);
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    bal[k] = __ballot(p[k] == pk && p[k] > 0.f);
-    if (lane == 0) wcnt[k][wave] = __popcll(bal[k]);
-  }
-  __syncthreads();
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  const uint64_t kept_mass = above + (keep < ties ? keep : ties) * mk;
-  const float total = (float)((double)kept_mass / kQuant);
-  uint64_t rank = s_before;
-#pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    uint32_t before_w = 0, all_w = 0;
-    for (int w = 0; w < kFWaves; ++w) {
-      before_w += w < wave ? wcnt[k][w] : 0u;
-      all_w += wcnt[k][w];
+    for (int e = 0; e < 4; ++e) {
+      const float x = p[4 * g + e];
+      const bool kept = x > pk || (x == pk && x > 0.f && j + e <= cut);
+      p[4 * g + e] = kept ? x / total : 0.f;
     }
-    const int j = c0 + k * kFThreads + tid;
-    const bool tie = p[k] == pk && p[k] > 0.f;
-    const uint64_t my_rank = rank + before_w + __popcll(bal[k] & below);
-    const bool kept = p[k] > pk || (tie && my_rank < keep);
-    if (j < a.V) out[j] = kept ? p[k] / total : 0.f;
-    rank += all_w;
   }
+  store_chunk(out, a.V, c0, p);
 }
 
 }  // namespace
@@ -682,9 +818,10 @@ int filter_chunks(int V) { return (V + kFChunk - 1) / kFChunk; }
 size_t filter_ws_bytes(int rows, int V) {
   const size_t ch = (size_t)filter_chunks(V);
   return align_up((size_t)rows * ch * sizeof(float2), 256) +
-         align_up((size_t)rows * 4 * 256 * sizeof(uint64_t), 256) +
-         align_up((size_t)rows * ch * 256 * sizeof(uint64_t), 256) +
-         align_up((size_t)rows * 4 * sizeof(uint64_t), 256);
+         align_up((size_t)rows * 256 * sizeof(uint64_t), 256) +
+         align_up((size_t)rows * V * sizeof(uint64_t), 256) +
+         align_up((size_t)rows * 8 * sizeof(uint64_t), 256) +
+         align_up((size_t)rows * 4 * sizeof(unsigned), 256);
 }
 
 hipError_t launch_filter(int rows, int V, const float *logits, float temperature, float top_p,
@@ -700,17 +837,20 @@ hipError_t launch_filter(int rows, int V, const float *logits, float temperature
   a.stat = (float2 *)b;
   b += align_up((size_t)rows * a.chunks * sizeof(float2), 256);
   a.rowhist = (uint64_t *)b;
-  b += align_up((size_t)rows * 4 * 256 * sizeof(uint64_t), 256);
-  a.hist0 = (uint64_t *)b;
-  b += align_up((size_t)rows * a.chunks * 256 * sizeof(uint64_t), 256);
+  b += align_up((size_t)rows * 256 * sizeof(uint64_t), 256);
+  a.cand = (uint64_t *)b;
+  b += align_up((size_t)rows * V * sizeof(uint64_t), 256);
   a.state = (uint64_t *)b;
+  b += align_up((size_t)rows * 8 * sizeof(uint64_t), 256);
+  a.count = (unsigned *)b;
   const dim3 grid(a.chunks, rows);
   hipLaunchKernelGGL(filter_stat_kernel, grid, dim3(kFThreads), 0, st, a);
-  hipLaunchKernelGGL(filter_prob_kernel, grid, dim3(kFThreads), 0, st, a);
   if (top_p < 1.f) {
-    for (int shift = 16; shift >= 0; shift -= 8)
-      hipLaunchKernelGGL(filter_level_kernel, grid, dim3(kFThreads), 0, st, a, shift);
+    hipLaunchKernelGGL(filter_prob_kernel<true>, grid, dim3(kFThreads), 0, st, a);
+    hipLaunchKernelGGL(filter_gather_kernel, grid, dim3(kFThreads), 0, st, a);
     hipLaunchKernelGGL(filter_write_kernel, grid, dim3(kFThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(filter_prob_kernel<false>, grid, dim3(kFThreads), 0, st, a);
   }
   return hipGetLastError();
 }

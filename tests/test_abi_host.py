@@ -272,10 +272,10 @@ def test_verify_probs_validation():
         rc = lib.moe_verify_probs(a["rows"], a["V"], a["lg"], a["T"], a["p"], a["out"], None,
                                   C.byref(nb), None)
         assert rc == -1, kw
-    # workspace query: chunk statistics, two histogram levels and the row state
+    # workspace query: chunk statistics, first-level histogram, candidate list, row state
     assert lib.moe_verify_probs(36, 102400, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None, C.byref(nb),
                                 None) == 0
     chunks = (102400 + 4095) // 4096
-    assert nb.value >= 36 * chunks * (8 + 256 * 8) + 36 * (4 * 256 * 8 + 32)
+    assert nb.value >= 36 * (chunks * 8 + 256 * 8 + 102400 * 8 + 64 + 16)
     assert lib.moe_verify_probs(65536, 16, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None,
                                 C.byref(nb), None) == -2

@@ -223,6 +223,37 @@ def test_filter_matches_oracle(V, T, top_p):
                     np.testing.assert_array_equal(g[tied] > 0, r[tied] > 0)
 
 
+def test_filter_more_workgroups_than_the_chip_holds_at_once():
+    # 300 rows x 8 chunks = 2,400 workgroups per launch, more than are
+    # resident at once: late workgroups of a launch must still start from
+    # the selection state of the launch before
+    rng = np.random.default_rng(41)
+    rows, V = 300, 32000
+    _say(f"[filter] rows={rows} V={V}")
+    lg = _logit_rows(rng, rows, V, ties=False, masked=True)
+    got = B.verify_probs(torch.from_numpy(lg).cuda(), 0.8, 0.9).cpu().numpy()
+    _check_nucleus(got, lg, 0.8, 0.9)
+
+
+def test_filter_all_tied_rows():
+    # every token of the row tied: all V entries are candidates at the
+    # boundary and the index cut decides; the kept set is the first k
+    # indices, k within one token of the oracle's (exact integer masses
+    # against the oracle's fp64 running sum)
+    V = 102400
+    lg = np.zeros((3, V), np.float32)
+    lg[1] = 2.5
+    lg[2, V // 2:] = -np.inf                      # half masked, the rest tied
+    for top_p in (0.3, 0.77):
+        _say(f"[filter] all tied, top_p={top_p}")
+        got = B.verify_probs(torch.from_numpy(lg).cuda(), 1.0, top_p).cpu().numpy()
+        ref, _ = O.filter_probs(lg, 1.0, top_p)
+        _check_nucleus(got, lg, 1.0, top_p)
+        for g, r in zip(got, ref):
+            k = int(np.count_nonzero(g))
+            assert np.all(g[:k] > 0) and abs(k - int(np.count_nonzero(r))) <= 1
+
+
 def test_filter_nucleus_hand_computed():
     lg = np.log(np.array([[0.2, 0.5, 0.3], [0.2, 0.5, 0.3], [0.2, 0.5, 0.3]], np.float32))
     cases = [(0.45, [0, 1, 0]), (0.7, [0, 0.625, 0.375]), (0.81, [0.2, 0.5, 0.3])]
