@@ -152,21 +152,28 @@ def unique_count(idx_host, E):
     return int(np.unique(v).size)
 
 
-def run_sweep(cfg, eng, layers, xs, n_values, reps):
-    """Per n: reps passes per engine, each on the next layer of the rotation.
-    Returns a list of per-n records."""
+SHORT_PASS_US = 50.0   # passes shorter than this get at least SHORT_PASS_REPS repetitions
+SHORT_PASS_REPS = 200
+
+
+def run_sweep(cfg, eng, layers, xs, n_values, reps, top_up=True):
+    """Per n: reps passes per engine (topped up to SHORT_PASS_REPS when an
+    engine's median pass is under SHORT_PASS_US), each on the next layer of
+    the rotation, each on its own hidden states.  Returns per-n records."""
     out = []
     nL = len(layers)
     turn = 0
     Be = expert_bytes(cfg)
-    for n in n_values:
-        N = cfg.tokens(n)
-        y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+
+    def batch(n, y, reps_range):
+        nonlocal turn
         ev = []
         # keep the GPU busy while the host queues the whole batch, so that no
         # event pair measures host launch latency
-        hold_gpu(0.3 * reps)
-        for rep in range(reps):
+        hold_gpu(0.3 * len(reps_range))
+        for rep in reps_range:
+            if (n, rep) not in xs:
+                xs[(n, rep)] = synth.make_hidden(cfg, n, rep, "cuda")
             x = xs[(n, rep)]
             rec = {}
             for name in ("perslot", "dedup"):
@@ -181,16 +188,29 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps):
                 rec[name] = (e0, e1, e2, idx)
             ev.append(rec)
         torch.cuda.synchronize()
+        return ev
+
+    for n in n_values:
+        N = cfg.tokens(n)
+        y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+        ev = batch(n, y, range(reps))
+        short = min(float(np.median([rec[name][1].elapsed_time(rec[name][2]) * 1e3 for rec in ev]))
+                    for name in ("perslot", "dedup")) < SHORT_PASS_US
+        if top_up and short and reps < SHORT_PASS_REPS:
+            ev += batch(n, y, range(reps, SHORT_PASS_REPS))
+        torch.cuda.synchronize()
         t = {"perslot": [], "dedup": []}
         tr = {"perslot": [], "dedup": []}
+        tt = {"perslot": [], "dedup": []}
         U = {"perslot": [], "dedup": []}
         for rec in ev:
             for name, (e0, e1, e2, idx) in rec.items():
                 tr[name].append(e0.elapsed_time(e1) * 1e3)
+                tt[name].append(e0.elapsed_time(e2) * 1e3)
                 t[name].append(e1.elapsed_time(e2) * 1e3)
                 U[name].append(unique_count(idx.cpu().numpy(), cfg.E))
         k, S = cfg.k, cfg.S
-        r = {"n": n, "tokens": N}
+        r = {"n": n, "tokens": N, "passes": len(ev)}
         for name in ("perslot", "dedup"):
             us = float(np.median(t[name]))
             routed = (N * k * Be) if name == "perslot" else float(np.mean(U[name])) * Be
@@ -198,6 +218,7 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps):
             r[name] = {"us": round(us, 2), "us_p10": round(float(np.percentile(t[name], 10)), 2),
                        "us_p90": round(float(np.percentile(t[name], 90)), 2),
                        "route_us": round(float(np.median(tr[name])), 2),
+                       "total_us": round(float(np.median(tt[name])), 2),
                        "requested_MB": round(req / 1e6, 3),
                        "GBs": round(req / us / 1e3, 1),
                        "hbm_frac": round(req / us / 1e3 / HBM_PEAK_GBS, 3),
@@ -688,7 +709,9 @@ def main():
     ap.add_argument("--config", default="v2lite", choices=sorted(synth.CONFIGS))
     ap.add_argument("--n", type=int, default=None, help="pass size of the timed step")
     ap.add_argument("--layers", type=int, default=None, help="weight sets in the rotation")
-    ap.add_argument("--reps", type=int, default=48, help="passes per n in the sweep")
+    ap.add_argument("--reps", type=int, default=50,
+                    help="passes per n and engine in the sweep (at least %d for passes "
+                         "under %g us)" % (SHORT_PASS_REPS, SHORT_PASS_US))
     ap.add_argument("--calib-reps", type=int, default=16,
                     help="passes per (n, U) point of the dedup calibration")
     ap.add_argument("--verify-only", action="store_true",
@@ -774,7 +797,7 @@ def main():
         xs = {(n, rep): synth.make_hidden(cfg, n, rep, "cuda")
               for n in cfg.n_values for rep in range(args.reps)}
         log("[bench] sweep warmup")
-        run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 2)
+        run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 2, top_up=False)
         log("[bench] sweep")
         sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps)
         log("[bench] dedup calibration on crafted routings")
