@@ -325,9 +325,10 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  *          independent of summation order.  probs may not overlap logits.
  * 0 < temperature (finite), 0 < top_p <= 1, 1 <= rows, 1 <= V <=
  * MOE_MAX_VOCAB; violations return MOE_ERR_INVALID_ARG (more than 65535
- * rows: MOE_ERR_UNSUPPORTED).  Workspace as for
- * the other calls (no initialisation needed).  Feed the verifier's rows as
- * p_verify and the draft's as q_draft. */
+ * rows: MOE_ERR_UNSUPPORTED).  Workspace as for the other calls, no
+ * initialisation needed; with top_p < 1 it holds a candidate list of up to
+ * V 8-byte entries per row, so its size is about twice that of the logits.
+ * Feed the verifier's rows as p_verify and the draft's as q_draft. */
 int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
                      float top_p, float *probs, void *workspace, size_t *workspace_bytes,
                      void *stream);
