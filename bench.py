@@ -242,6 +242,8 @@ def calibrate(cfg, eng, layers, xs, xreps, sweep, reps):
     (the sweep).  Dedup: at every n, crafted routings with exactly U
     distinct experts for U spread over k .. min(E, N k), B = U B_e.  Shared
     experts and the gate are the same in both engines and land in t0.
+    The per-slot engine is also timed on the same crafted routings, for the
+    trace-aware fit t = U B_e / BW_first + (N k - U) B_e / BW_repeat + t0.
     Returns the fits and, per n, r(n) = BW_dd(n) / BW_ps."""
     Be = expert_bytes(cfg)
     k, E = cfg.k, cfg.E
@@ -251,6 +253,7 @@ def calibrate(cfg, eng, layers, xs, xreps, sweep, reps):
     nL = len(layers)
     turn = 0
     points = []
+    ps_points = []  # (first-read bytes, repeat bytes, us) of per-slot on crafted routings
     per_n = {}
     for n in ns:
         N = cfg.tokens(n)
@@ -261,21 +264,25 @@ def calibrate(cfg, eng, layers, xs, xreps, sweep, reps):
             idx_np, w_np = synth.crafted_routing(N, k, E, U, seed=cfg.seed * 10**4 + n * 100 + gi)
             idx = torch.from_numpy(idx_np).cuda()
             w = torch.from_numpy(w_np).cuda()
-            evs = []
-            hold_gpu(0.1 * reps)
+            evs = {"dedup": [], "perslot": []}
+            hold_gpu(0.2 * reps)
             for rep in range(reps):
-                lay = layers[turn % nL]
-                turn += 1
-                e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-                e0.record()
-                eng.dedup(lay, xs[(n, rep % xreps)], idx, w, y)
-                e1.record()
-                evs.append((e0, e1))
+                for name in ("dedup", "perslot"):
+                    lay = layers[turn % nL]
+                    turn += 1
+                    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                    e0.record()
+                    getattr(eng, name)(lay, xs[(n, rep % xreps)], idx, w, y)
+                    e1.record()
+                    evs[name].append((e0, e1))
             torch.cuda.synchronize()
-            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs]))
-            meas.append((U, us))
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs["dedup"]]))
+            us_ps = float(np.median([a.elapsed_time(b) * 1e3 for a, b in evs["perslot"]]))
+            meas.append((U, us, us_ps))
             points.append((n, U * Be, us))
-        rec = {"U": [m[0] for m in meas], "us": [round(m[1], 2) for m in meas]}
+            ps_points.append((U * Be, (N * k - U) * Be, us_ps))
+        rec = {"U": [m[0] for m in meas], "us": [round(m[1], 2) for m in meas],
+               "perslot_us": [round(m[2], 2) for m in meas]}
         if len(grid) >= 2:
             f = stepmodel.fit_line([m[0] * Be for m in meas], [m[1] for m in meas])
             r, r_sd = stepmodel.bandwidth_ratio(f, fit_ps)
@@ -286,21 +293,40 @@ def calibrate(cfg, eng, layers, xs, xreps, sweep, reps):
             + (f" r={rec['r']:.3f}" if "r" in rec else ""))
     fit_dd = stepmodel.fit_line([p[1] for p in points], [p[2] for p in points])
     r_all, r_all_sd = stepmodel.bandwidth_ratio(fit_dd, fit_ps)
+    plane = stepmodel.fit_plane(*zip(*ps_points))
+    log(f"  per-slot on crafted routings: {plane.as_dict()}")
     return {"perslot": fit_ps, "dedup_pooled": fit_dd, "r_pooled": (r_all, r_all_sd),
-            "per_n": per_n}
+            "perslot_trace": plane, "per_n": per_n}
 
 
 def predict_from_calibration(cfg, calib, n, u_bar):
-    """Model prediction at pass size n and byte share u: (r(n), saving us,
-    its standard error).  Uses the per-n dedup fit where one exists, else
-    the pooled one."""
+    """Model prediction at pass size n and byte share u: (r(n), its standard
+    error, saving us, its first-order standard error, the standard deviation
+    of a measured saving about it).  Uses the per-n dedup fit where one
+    exists, else the pooled one."""
     N = cfg.tokens(n)
     b_ps = N * cfg.k * expert_bytes(cfg)
     rec = calib["per_n"].get(n, {})
     f_dd = rec.get("_fit", calib["dedup_pooled"])
     r, r_sd = stepmodel.bandwidth_ratio(f_dd, calib["perslot"])
     sav, sav_sd = stepmodel.predicted_saving(calib["perslot"], f_dd, b_ps, u_bar * b_ps)
-    return r, r_sd, sav, sav_sd
+    iv_sd = stepmodel.saving_interval_sd(calib["perslot"], f_dd, b_ps, u_bar * b_ps)
+    trace = stepmodel.predicted_saving_trace(calib["perslot_trace"], f_dd, u_bar * b_ps,
+                                             (1.0 - u_bar) * b_ps)
+    return r, r_sd, sav, sav_sd, iv_sd, trace
+
+
+def saving_check(rec, measured, sav, sav_sd, iv_sd, trace):
+    """Record the predicted saving (the line model, and the trace-aware one
+    that prices repeated per-slot reads separately), their errors and
+    whether the measured saving lies within two interval standard
+    deviations of each."""
+    rec["predicted_saving_us"], rec["predicted_saving_sd_us"] = round(sav, 2), round(sav_sd, 2)
+    rec["saving_interval_sd_us"] = round(iv_sd, 2)
+    rec["saving_within_2sd"] = bool(abs(measured - sav) <= 2 * iv_sd)
+    t_sav, t_sd, t_iv = trace
+    rec["trace_predicted_saving_us"], rec["trace_saving_interval_sd_us"] = round(t_sav, 2), round(t_iv, 2)
+    rec["trace_saving_within_2sd"] = bool(abs(measured - t_sav) <= 2 * t_iv)
 
 
 def draft_length_table(sweep, draft_fracs=(0.05, 0.2), alphas=None):
@@ -394,6 +420,9 @@ def calibration_json(calib):
     return {"model": "t_us = bytes / BW + t0 (routed expert bytes; shared experts and "
                      "gate in t0)",
             "perslot": calib["perslot"].as_dict(),
+            "perslot_trace": dict(calib["perslot_trace"].as_dict(),
+                                  model="t_us = U B_e / BW_first + (N k - U) B_e / BW_repeat + t0, "
+                                        "per-slot on the crafted routings"),
             "dedup_pooled": calib["dedup_pooled"].as_dict(),
             "r_pooled": round(calib["r_pooled"][0], 4),
             "r_pooled_sd": round(calib["r_pooled"][1], 4),
@@ -450,7 +479,7 @@ def rho_sweep(cfg, eng, layers, stack, calib, reps):
             med = {k: float(np.median(v)) for k, v in t.items()}
             ps = (med["perslot"] - med["route"]) / nL
             dd = (med["dedup"] - med["route"]) / nL
-            r, r_sd, sav, sav_sd = predict_from_calibration(cfg, calib, n, u_bar)
+            r, r_sd, sav, sav_sd, iv_sd, trace = predict_from_calibration(cfg, calib, n, u_bar)
             fz = fused_stack_leg(cfg, stack, [n], reps, rho=rho, rho_index=ri)[n]
             rec_fused = {"perslot_stack_us": round(fz["perslot"], 1),
                          "dedup_stack_us": round(fz["dedup"], 1),
@@ -466,16 +495,18 @@ def rho_sweep(cfg, eng, layers, stack, calib, reps):
                    "dedup_GBs": round((U.mean() + cfg.S) * Be / dd / 1e3, 1),
                    "saving_us": round(ps - dd, 2),
                    "r": round(r, 4), "r_sd": round(r_sd, 4),
-                   "predicted_saving_us": round(sav, 2),
-                   "predicted_saving_sd_us": round(sav_sd, 2),
                    "dedup_faster": dd < ps, "u_lt_r": u_bar < r,
                    "fused": rec_fused}
+            saving_check(rec, ps - dd, sav, sav_sd, iv_sd, trace)
             recs.append(rec)
             log(f"  rho={rho:.2f} n={n:2d} u={u_bar:.3f} r={r:.3f} per-layer ps {ps:7.1f} "
-                f"dd {dd:7.1f} us, saving {ps - dd:6.1f} (pred {sav:6.1f} +- {sav_sd:.1f}); "
+                f"dd {dd:7.1f} us, saving {ps - dd:6.1f} (pred {sav:6.1f} +- {iv_sd:.1f}); "
                 f"fused stack per layer ps {rec_fused['perslot_layer_us']:7.1f} "
                 f"dd {rec_fused['dedup_layer_us']:7.1f} us (with routing)")
         out.append({"rho": rho, "passes_per_n": reps, "layers": nL, "by_n": recs,
+                    "saving_within_2sd": f"{sum(r['saving_within_2sd'] for r in recs)} of {len(recs)}",
+                    "trace_saving_within_2sd":
+                        f"{sum(r['trace_saving_within_2sd'] for r in recs)} of {len(recs)}",
                     "crossover": {"measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in recs]),
                                   "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_lt_r"] for r in recs])}})
     return out
@@ -803,11 +834,11 @@ def main():
         log("[bench] dedup calibration on crafted routings")
         calib = calibrate(cfg, eng, layers, xs, args.reps, sweep, args.calib_reps)
         for r in sweep:
-            rr, rr_sd, sav, sav_sd = predict_from_calibration(cfg, calib, r["n"], r["u_bar"])
+            rr, rr_sd, sav, sav_sd, iv_sd, trace = predict_from_calibration(cfg, calib, r["n"], r["u_bar"])
             r["r_trace"] = r.pop("r")
             r["r"], r["r_sd"] = round(rr, 4), round(rr_sd, 4)
-            r["predicted_saving_us"], r["predicted_saving_sd_us"] = round(sav, 2), round(sav_sd, 2)
             r["saving_us"] = round(r["perslot"]["us"] - r["dedup"]["us"], 2)
+            saving_check(r, r["saving_us"], sav, sav_sd, iv_sd, trace)
         del xs
 
     if args.rho_sweep:
@@ -906,6 +937,9 @@ def main():
             "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_bar"] < r["r"] for r in sweep]),
             "predicted_model_saving_gt_0": stepmodel.first_n(
                 ns, [r["predicted_saving_us"] > 0 for r in sweep])}
+        out["saving_within_2sd"] = {
+            "line_model": f"{sum(r['saving_within_2sd'] for r in sweep)} of {len(sweep)}",
+            "trace_model": f"{sum(r['trace_saving_within_2sd'] for r in sweep)} of {len(sweep)}"}
     if not args.no_sweep:
         log("[bench] verification round")
         out["verify_gate"] = verify_gate_leg()
