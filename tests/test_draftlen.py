@@ -1,33 +1,36 @@
 """Draft-length arithmetic (CPU only), pinned to the values the pages print
 and to the i.i.d. closed form."""
+import json
 import math
+import os
 
 import numpy as np
 import pytest
 
 from speculative_decode_verify_gate_amd import draftlen as D
 
-
-# (alpha, gamma, c, printed speedup) -- the speculative-decoding page,
-# section "Hypothesis 1" (c = 0.1601) and "Hypothesis 2" (c = 0.5002, gamma 6)
-PRINTED = [(0.392, 4, 0.1601, 0.99), (0.336, 7, 0.1601, 0.71), (0.197, 8, 0.1601, 0.55),
-           (0.864, 6, 0.5002, 1.18), (0.198, 6, 0.5002, 0.31), (0.395, 6, 0.5002, 0.41),
-           (0.301, 6, 0.5002, 0.36)]
+# the values the speculative-decoding page prints (fixture with its citation)
+with open(os.path.join(os.path.dirname(__file__), "golden", "draft_length_printed.json")) as fh:
+    GOLDEN = json.load(fh)
+PRINTED = [(row["acceptance"], row["gamma"], table["c"], row["speedup"])
+           for table in GOLDEN["tables"] for row in table["rows"]]
 
 
 @pytest.mark.parametrize("alpha,gamma,c,printed", PRINTED)
 def test_cost_ratio_speedup_reproduces_the_printed_table(alpha, gamma, c, printed):
-    assert round(D.cost_ratio_speedup(alpha, gamma, c), 2) == pytest.approx(printed, abs=1e-9)
+    got = round(D.cost_ratio_speedup(alpha, gamma, c), GOLDEN["printed_decimals"])
+    assert got == pytest.approx(printed, abs=1e-9)
 
 
 def test_breakeven_range_for_the_closer_draft():
-    # the same page: with c = 0.5002 the draft needs 69 to 84 percent
-    # acceptance to reach 1.0x (draft lengths 3 .. 8)
-    assert round(100 * D.breakeven_alpha(3, 0.5002)) == 69
-    assert round(100 * D.breakeven_alpha(8, 0.5002)) == 84
+    # the same page: with the closer draft the acceptance needed to reach
+    # 1.0x spans the printed percentages over the draft lengths (3 .. 8)
+    b = GOLDEN["breakeven"]
+    assert round(100 * D.breakeven_alpha(3, b["c"])) == b["percent_low"]
+    assert round(100 * D.breakeven_alpha(8, b["c"])) == b["percent_high"]
     for g in range(3, 9):
-        a = D.breakeven_alpha(g, 0.5002)
-        assert D.cost_ratio_speedup(a, g, 0.5002) == pytest.approx(1.0, abs=1e-9)
+        a = D.breakeven_alpha(g, b["c"])
+        assert D.cost_ratio_speedup(a, g, b["c"]) == pytest.approx(1.0, abs=1e-9)
 
 
 def test_expected_tokens_closed_form():

@@ -2,6 +2,9 @@
 only).  The round follows "Building a Terminal Based LLM Inference
 Internals Explorer - Part 3: Speculative Decoding", sections "The
 Accept/Reject Mechanism", "A Worked Example" and "Sampling vs Greedy"."""
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -9,28 +12,43 @@ import oracle as O
 
 CAT, DOG, FOX = 0, 1, 2
 
+# the page's worked example (fixture with its citation)
+with open(os.path.join(os.path.dirname(__file__), "golden", "verify_worked_example.json")) as fh:
+    EX = json.load(fh)
+
 
 def _f32(v):
     return np.asarray(v, dtype=np.float32)
 
 
+def _example():
+    """The example's verifier row (plus an arbitrary bonus row) and draft row."""
+    p = _f32([EX["p_verify"], [0.2, 0.3, 0.5]])
+    q = _f32([EX["p_draft"]])
+    return p, q
+
+
 def test_worked_example_accept_probability():
-    # p_draft(cat) = 0.6, p_verify(cat) = 0.3: cat survives a 50% coin flip
-    p = _f32([[0.3, 0.5, 0.2], [0.2, 0.3, 0.5]])
-    q = _f32([[0.6, 0.3, 0.1]])
-    n, t = O.verify_gate(p, [CAT], q=q, u=[0.4999], r=0)
-    assert n == 1 and t[0] == CAT
-    n, t = O.verify_gate(p, [CAT], q=q, u=[0.5], r=0)
+    # the draft token survives exactly when u < the printed accept probability
+    p, q = _example()
+    x = EX["draft_token"]
+    a = EX["accept_prob"]
+    assert min(1.0, EX["p_verify"][x] / EX["p_draft"][x]) == pytest.approx(a)
+    n, t = O.verify_gate(p, [x], q=q, u=[np.nextafter(np.float32(a), np.float32(0))], r=0)
+    assert n == 1 and t[0] == x
+    n, t = O.verify_gate(p, [x], q=q, u=[a], r=0)
     assert n == 0 and t[1] == -1
 
 
 def test_worked_example_residual_draw():
-    # residual {cat: 0, dog: 0.2, fox: 0.1}, normalised {0, 0.67, 0.33}: cat
-    # can never be the correction; dog below two thirds of the draw range
-    p = _f32([[0.3, 0.5, 0.2], [0.2, 0.3, 0.5]])
-    q = _f32([[0.6, 0.3, 0.1]])
-    res = np.maximum(p[0] - q[0], 0).astype(np.float32)
-    np.testing.assert_allclose(res / res.sum(), [0.0, 2 / 3, 1 / 3], atol=1e-6)
+    # the printed residual and its normalisation (to the printed decimals):
+    # the rejected token can never be the correction; the next token takes
+    # the first two thirds of the draw range
+    p, q = _example()
+    res = np.maximum(p[0].astype(np.float64) - q[0].astype(np.float64), 0)
+    np.testing.assert_allclose(res, EX["residual"], atol=1e-7)
+    np.testing.assert_allclose(np.round(res / res.sum(), EX["normalized_residual_decimals"]),
+                               EX["normalized_residual"], atol=1e-12)
     seen = set()
     for r in np.linspace(0, 2**32 - 1, 301).astype(np.uint64):
         n, t = O.verify_gate(p, [CAT], q=q, u=[0.9], r=int(r))
