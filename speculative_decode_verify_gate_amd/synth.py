@@ -103,6 +103,13 @@ def _normal_weights(shape, seed, device, dtype, chunk_dim0=True):
     return out
 
 
+def make_gate(cfg: LayerConfig, device="cpu", layer: int = 0, E=None):
+    """The gate of one layer alone: fp32 [E][d], the same draw as make_layer's."""
+    E = cfg.E if E is None else E
+    return _normal_weights((E, cfg.d), cfg.seed * 1000 + layer * 10 + T_GATE, device,
+                           torch.float32, False)
+
+
 def make_layer(cfg: LayerConfig, device="cpu", layer: int = 0, E=None):
     """Weights of one layer: dict with gate_w fp32 [E][d], w13 [E][2][f][d],
     w2 [E][d][f], ws13 [S][2][f][d] / ws2 [S][d][f] (None when S == 0)."""
@@ -110,7 +117,7 @@ def make_layer(cfg: LayerConfig, device="cpu", layer: int = 0, E=None):
     base = cfg.seed * 1000 + layer * 10
     wdt = cfg.torch_wdtype
     lay = {
-        "gate_w": _normal_weights((E, cfg.d), base + T_GATE, device, torch.float32, False),
+        "gate_w": make_gate(cfg, device, layer, E),
         "w13": _normal_weights((E, 2, cfg.f, cfg.d), base + T_W13, device, wdt),
         "w2": _normal_weights((E, cfg.d, cfg.f), base + T_W2, device, wdt),
         "ws13": None,
