@@ -321,7 +321,7 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  *          (P descending, index ascending) whose probability reaches top_p
  *          is kept (the token that reaches it included), renormalised; the
  *          rest are 0.  The kept set is decided on integer masses
- *          floor(P * 2^40) against ceil(top_p * their total), exactly and
+ *          floor(P * 2^52) against ceil(top_p * their total), exactly and
  *          independent of summation order.  probs may not overlap logits.
  * 0 < temperature (finite), 0 < top_p <= 1, 1 <= rows, 1 <= V <=
  * MOE_MAX_VOCAB; violations return MOE_ERR_INVALID_ARG (more than 65535

@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 //   top-p: the tokens kept are the shortest run in the order (probability
 //   descending, index ascending) whose probability reaches top_p, the token
 //   that reaches it included.  The decision uses integer masses
-//   floor(P * 2^40) against ceil(top_p * W), W their total, so it is exact
+//   floor(P * 2^52) against ceil(top_p * W), W their total, so it is exact
 //   and independent of summation order: a radix select over the
 //   probability bits (non-negative floats order like their bits, and P <= 1
 //   leaves bits 31-30 zero) finds the probability K of the last kept token;
@@ -425,7 +425,12 @@ struct FilterArgs {
   unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
 };
 
-__device__ inline uint64_t mass_of(float p) { return (uint64_t)((double)p * kQuant); }
+// The filter's integer mass of a probability: floor(P * 2^52).  Every
+// fp32 P >= 2^-29 is then exact (24 significant bits), the rest lose less
+// than 2^-52 each, and a row's total (sum of P about 1) fits 64 bits: the
+// decision is exact on the fp32 probabilities even over 2^24 entries.
+constexpr double kMassQuant = 4503599627370496.0;  // 2^52
+__device__ inline uint64_t mass_of(float p) { return (uint64_t)((double)p * kMassQuant); }
 
 template <class T, class Op>
 __device__ inline T block_all(T v, T *scratch, Op op) {
@@ -793,7 +798,7 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
   const uint64_t *st = a.state + (size_t)row * 8;
   const float pk = __uint_as_float((uint32_t)st[4]);  // the last kept probability
   const uint32_t cut = (uint32_t)st[5];                // ties kept up to this index
-  const float total = (float)((double)st[6] / kQuant);
+  const float total = (float)((double)st[6] / kMassQuant);
   float *out = a.probs + (size_t)row * a.V;
   const int c0 = c * kFChunk;
   float p[kFPer];
