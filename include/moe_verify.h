@@ -315,7 +315,8 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  * Part 3: Speculative Decoding", sections "The Accept/Reject Mechanism" and
  * "The Flow": softmax of logits / temperature, then top-p filtering, with
  * the same settings for the verifier and the draft):
- *   logits [rows][V] fp32 device (each row with at least one finite logit)
+ *   logits [rows][V] fp32 device (each row with at least one finite logit;
+ *          -inf masks a token; logit / temperature must be finite in fp32)
  *   probs  [rows][V] fp32 device output: P = softmax(logits / temperature);
  *          with top_p < 1 only the shortest run of tokens in the order
  *          (P descending, index ascending) whose probability reaches top_p

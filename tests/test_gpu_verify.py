@@ -254,6 +254,42 @@ def test_filter_all_tied_rows():
             assert np.all(g[:k] > 0) and abs(k - int(np.count_nonzero(r))) <= 1
 
 
+MASS_ATOL = 1e-6  # absolute: what fp32 probabilities can move a running mass by
+
+
+def _check_nucleus_mass(got, lg, T, top_p):
+    """For top_p so close to 1 that the boundary lies where single tokens
+    weigh less than the fp32 rounding of the running mass: the GPU's kept
+    set is a prefix of the exact order up to near-ties, its exact mass
+    reaches top_p and is minimal within MASS_ATOL, and its values are the
+    exact probabilities renormalised over it."""
+    full, _ = O.filter_probs(lg, T, 1.0)
+    for g, f in zip(got.reshape(-1, lg.shape[-1]), full.reshape(-1, lg.shape[-1])):
+        kg = g > 0
+        assert f[kg].min() >= f[~kg].max() * (1 - FILTER_TOL) if (~kg).any() else True
+        mass = f[kg].sum()
+        assert mass >= top_p - MASS_ATOL and mass - f[kg].min() < top_p + MASS_ATOL
+        np.testing.assert_allclose(g[kg], f[kg] / mass, rtol=FILTER_TOL, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,top_p", [(0.01, 0.9), (50.0, 0.9), (1.0, 1e-6), (0.05, 0.999),
+                                     (1.0, 1 - 1e-7)])
+def test_filter_degenerate_settings(T, top_p):
+    # a near one-hot softmax, a near-flat one, a nucleus of one token and a
+    # nucleus of (almost) everything
+    rng = np.random.default_rng(int(T * 100) + int(top_p * 1e6))
+    _say(f"[filter] degenerate T={T} top_p={top_p}")
+    lg = _logit_rows(rng, 6, 50000)
+    got = B.verify_probs(torch.from_numpy(lg).cuda(), T, top_p).cpu().numpy()
+    if top_p > 1 - 1e-5:
+        _check_nucleus_mass(got, lg, T, top_p)
+    else:
+        _check_nucleus(got, lg, T, top_p)
+    if top_p == 1e-6:
+        assert np.all(np.count_nonzero(got, axis=1) == 1)
+        assert np.array_equal(got.argmax(axis=1), lg.argmax(axis=1))
+
+
 def test_filter_nucleus_hand_computed():
     lg = np.log(np.array([[0.2, 0.5, 0.3], [0.2, 0.5, 0.3], [0.2, 0.5, 0.3]], np.float32))
     cases = [(0.45, [0, 1, 0]), (0.7, [0, 0.625, 0.375]), (0.81, [0.2, 0.5, 0.3])]
