@@ -829,7 +829,7 @@ def main():
         xs = {(n, rep): synth.make_hidden(cfg, n, rep, "cuda")
               for n in cfg.n_values for rep in range(args.reps)}
         log("[bench] sweep warmup")
-        run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 2, top_up=False)
+        run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 5, top_up=False)  # 10 passes per engine
         log("[bench] sweep")
         sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps)
         log("[bench] dedup calibration on crafted routings")
