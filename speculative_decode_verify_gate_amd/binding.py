@@ -3,7 +3,9 @@
 Argument marshalling only: tensors become device pointers, the current torch
 stream becomes the HIP stream, status codes become exceptions.  Every step of
 the layer runs in the library's gfx950 kernels; there is no fallback, and
-loading fails loudly when the library has not been built.
+loading fails loudly when the library has not been built.  MOE_VERIFY_LIB,
+if set, names another build of the same library to load instead (for
+comparing two builds of the kernels in separate processes).
 """
 import ctypes as C
 import os
