@@ -773,8 +773,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the layer is not sharded across GPUs in this "
-              "build; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the layer is not sharded across GPUs; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs the GPU", file=sys.stderr)
