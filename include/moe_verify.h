@@ -297,8 +297,10 @@ int moe_pass_bytes_grouped(const moe_shape *shape, const int32_t *topk_idx_host,
  * whose inclusive prefix sum exceeds floor(W r / 2^32), W the weight total;
  * a residual that is zero at that precision draws from p_i instead.  Greedy
  * keeps a draft token when it is the verifier's argmax (ties to the lowest
- * index) and ends with the verifier's argmax.  Results are deterministic and
- * exact (no dependence on summation order).
+ * index) and ends with the verifier's argmax.  Greedy reads nothing of p but
+ * each row's argmax, which softmax, temperature and top-p keep, so the
+ * verifier's logits may be passed as p_verify directly in that mode.
+ * Results are deterministic and exact (no dependence on summation order).
  * Limits: 1 <= n_seq <= MOE_MAX_SEQ, 0 <= gamma <= MOE_MAX_DRAFT,
  * 1 <= V <= MOE_MAX_VOCAB.  A draft token outside [0, V) cannot be checked
  * on the host; the device treats it as rejected (never read).  Workspace as

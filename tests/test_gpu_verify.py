@@ -301,6 +301,24 @@ def test_filter_nucleus_hand_computed():
     np.testing.assert_allclose(got.cpu().numpy(), [[0.5, 0.5, 0, 0]], atol=1e-7)
 
 
+def test_greedy_round_reads_logits_directly():
+    """Greedy mode uses only each row's argmax, which softmax, temperature
+    and top-p keep: the round on the raw logits equals the round on the
+    filtered distributions."""
+    rng = np.random.default_rng(33)
+    S, gamma, V = 4, 8, 50000
+    vl = _logit_rows(rng, S * (gamma + 1), V, masked=True).reshape(S, gamma + 1, V)
+    vl[0, 2, 7] = vl[0, 2, 11] = vl[0, 2].max() + 1.0      # a tie for the argmax
+    x = np.where(rng.random((S, gamma)) < 0.7, vl[:, :gamma].argmax(axis=2),
+                 rng.integers(0, V, (S, gamma))).astype(np.int32)
+    p = B.verify_probs(torch.from_numpy(vl).cuda(), 0.7, 0.9).cpu().numpy()
+    n_l, t_l = _run_gpu(vl, None, x, None, None, B.VERIFY_GREEDY)
+    n_p, t_p = _run_gpu(p, None, x, None, None, B.VERIFY_GREEDY)
+    np.testing.assert_array_equal(n_l, n_p)
+    np.testing.assert_array_equal(t_l, t_p)
+    assert (np.argmax(vl[0, 2]) == 7) and (7 in t_l[0] or n_l[0] < 2)
+
+
 def test_round_from_logits_matches_oracle():
     """Logits -> filtered p and q on the GPU -> the GPU round; the oracle's
     round on those same distributions decides identically."""
