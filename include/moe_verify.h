@@ -280,7 +280,8 @@ int moe_pass_bytes_grouped(const moe_shape *shape, const int32_t *topk_idx_host,
  *   p_verify     [n_seq][gamma+1][V] fp32 device: the verifier's
  *                distributions at the gamma drafted positions and at the
  *                bonus position, after the caller's temperature / top-p
- *                filtering (the same filtering as the draft's)
+ *                filtering (the same filtering as the draft's;
+ *                moe_verify_probs computes both from the models' logits)
  *   q_draft      [n_seq][gamma][V] fp32 device: the draft's full
  *                distributions (sampling; ignored and may be NULL for greedy)
  *   draft_tokens [n_seq][gamma] int32 device, each in [0, V)
