@@ -290,6 +290,31 @@ def test_filter_degenerate_settings(T, top_p):
         assert np.array_equal(got.argmax(axis=1), lg.argmax(axis=1))
 
 
+def test_filter_unaligned_rows_and_single_finite_logits():
+    # rows that start 4 bytes past a 16-byte boundary (the scalar load path
+    # although V is a multiple of 4), a row with one finite logit, and a row
+    # with two equal finite logits (the lower index alone reaches 0.5)
+    rng = np.random.default_rng(47)
+    rows, V = 5, 4096 * 3
+    flat = torch.empty(rows * V + 1, dtype=torch.float32, device="cuda")
+    lg = _logit_rows(rng, rows, V)
+    lg[3] = -np.inf
+    lg[3, 1234] = 0.0
+    lg[4] = -np.inf
+    lg[4, 100] = lg[4, 9000] = 2.0
+    dev = flat[1:].view(rows, V)
+    dev.copy_(torch.from_numpy(lg))
+    assert dev.data_ptr() % 16 == 4
+    out = torch.empty(rows * V + 1, dtype=torch.float32, device="cuda")[1:].view(rows, V)
+    got = B.verify_probs(dev, 0.8, 0.5, out=out).cpu().numpy()
+    _check_nucleus(got[:3], lg[:3], 0.8, 0.5)
+    assert got[3, 1234] == 1.0 and np.count_nonzero(got[3]) == 1
+    assert got[4, 100] == 1.0 and np.count_nonzero(got[4]) == 1
+    # the same with top_p = 1: both tied tokens share the mass
+    full = B.verify_probs(dev, 0.8, 1.0, out=out).cpu().numpy()
+    assert full[4, 100] == full[4, 9000] == 0.5
+
+
 def test_filter_nucleus_hand_computed():
     lg = np.log(np.array([[0.2, 0.5, 0.3], [0.2, 0.5, 0.3], [0.2, 0.5, 0.3]], np.float32))
     cases = [(0.45, [0, 1, 0]), (0.7, [0, 0.625, 0.375]), (0.81, [0.2, 0.5, 0.3])]
