@@ -298,7 +298,8 @@ int moe_pass_bytes_grouped(const moe_shape *shape, const int32_t *topk_idx_host,
  * whose inclusive prefix sum exceeds floor(W r / 2^32), W the weight total;
  * a residual that is zero at that precision draws from p_i instead.  Greedy
  * keeps a draft token when it is the verifier's argmax (ties to the lowest
- * index) and ends with the verifier's argmax.  Greedy reads nothing of p but
+ * index; -0 and +0 are equal values) and ends with the verifier's argmax;
+ * p_verify must hold no NaN in that mode.  Greedy reads nothing of p but
  * each row's argmax, which softmax, temperature and top-p keep, so the
  * verifier's logits may be passed as p_verify directly in that mode.
  * Results are deterministic and exact (no dependence on summation order).

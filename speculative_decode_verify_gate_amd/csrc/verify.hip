@@ -49,9 +49,11 @@ __device__ inline uint64_t quantize(float w) {
   return w > 0.f ? (uint64_t)((double)w * kQuant) : 0ull;
 }
 
-// Key of value v at index j: larger value first, then lower index.
+// Key of value v at index j: larger value first, then lower index.  -0 and
+// +0 are equal values, so they get one key and the lower index wins.
 __device__ inline uint64_t argmax_key(float v, int j) {
   uint32_t b = __float_as_uint(v);
+  if ((b << 1) == 0u) b = 0u;                       // -0 as +0
   b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // order-preserving
   return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
 }

@@ -344,6 +344,24 @@ def test_greedy_round_reads_logits_directly():
     assert (np.argmax(vl[0, 2]) == 7) and (7 in t_l[0] or n_l[0] < 2)
 
 
+def test_greedy_argmax_signed_zeros_tie():
+    """-0.0 and +0.0 are equal values: where a row's maximum is zero and
+    occurs as both, the argmax is the lower index, whichever sign it has
+    (across chunks and inside one chunk)."""
+    V = 5000
+    vl = np.full((1, 3, V), -1.0, dtype=np.float32)
+    vl[0, 0, 100], vl[0, 0, 4000] = -0.0, 0.0      # different 2048-entry chunks
+    vl[0, 1, 10], vl[0, 1, 11] = -0.0, 0.0         # one chunk
+    vl[0, 2, 7], vl[0, 2, 3000] = 0.0, -0.0        # +0 first
+    for x0, x1 in ((100, 10), (4000, 11)):
+        x = np.array([[x0, x1]], dtype=np.int32)
+        n_g, t_g = _run_gpu(vl, None, x, None, None, B.VERIFY_GREEDY)
+        n_o, t_o = _run_oracle(vl, None, x, None, None, B.VERIFY_GREEDY)
+        np.testing.assert_array_equal(n_g, n_o)
+        np.testing.assert_array_equal(t_g, t_o)
+    assert list(t_g[0]) == [100, -1, -1] and n_g[0] == 0
+
+
 def test_round_from_logits_matches_oracle():
     """Logits -> filtered p and q on the GPU -> the GPU round; the oracle's
     round on those same distributions decides identically."""
