@@ -31,9 +31,13 @@
  *    Otherwise *workspace_bytes is the size supplied; a smaller size than
  *    needed returns MOE_ERR_WORKSPACE.  A workspace must be 256-byte
  *    aligned and may not be shared by calls that can run concurrently.  The
- *    expert-pass workspaces need no initialisation; the first 256 bytes of a
- *    moe_route workspace must be zero before its first use, and every call
+ *    expert-pass and moe_verify_probs workspaces need no initialisation;
+ *    the first 256 bytes of a moe_route, moe_stack_pass or moe_verify_gate
+ *    workspace must be zero before its first use, and every such call
  *    leaves them zero again (they count the workgroups that have finished).
+ *    The expert passes and moe_verify_probs write data there, so a
+ *    workspace they used must have those bytes zeroed again before it
+ *    serves one of the other three calls.
  *  - Routing entries passed to the expert passes must lie in [0, E); that
  *    cannot be checked on the host without a copy, so an out-of-range entry
  *    is treated on the device as an empty slot (no weights read, zero

@@ -139,15 +139,27 @@ def _stream():
 
 class Workspace:
     """A grow-only device byte buffer reused across calls (256-byte aligned,
-    zero-filled when allocated, as a routing workspace requires)."""
+    zero-filled when allocated).
+
+    Routing, the stack pass and the verification round keep arrival
+    counters in the first 256 bytes: zero before the call, zero after.  The
+    expert passes and the logits filter write data there (the compaction
+    record, the filter's statistics).  get() is told which kind of call
+    comes next and zeroes the head, with one small fill on the current
+    stream, when the call before it was of the other kind."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.buf = None
+        self.head_zero = True
 
-    def get(self, nbytes):
+    def get(self, nbytes, counters=False):
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+            self.head_zero = True
+        if counters and not self.head_zero:
+            self.buf[:256].zero_()
+        self.head_zero = counters
         return self.buf
 
 
@@ -199,7 +211,7 @@ def route(shape, gate_w, x, *, bias=None, idx=None, w=None, logits=None, margin=
         C.byref(shape), _ptr(gate_w), _ptr(x), n, None, _ptr(idx), _ptr(w), None, None, nb,
         None))
     ws = ws or Workspace(x.device)
-    buf = ws.get(need)
+    buf = ws.get(need, counters=True)
     have = C.c_size_t(buf.numel())
     _check("moe_route_biased", lib.moe_route_biased(
         C.byref(shape), _ptr(gate_w), _ptr(bias), _ptr(x), n, _ptr(logits), _ptr(idx), _ptr(w),
@@ -306,7 +318,7 @@ def stack_pass(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=No
         C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y), None,
         None, nb, None))
     ws = ws or Workspace(dev)
-    buf = ws.get(need)
+    buf = ws.get(need, counters=True)
     have = C.c_size_t(buf.numel())
     _check("moe_stack_pass", lib.moe_stack_pass(
         C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y),
@@ -383,7 +395,7 @@ def verify_gate(p, x, *, q=None, u=None, r=None, mode=VERIFY_SAMPLING, n_accepte
                                                       _ptr(out), None, C.byref(nb), None))
         _NEED[key] = nb.value
     ws = ws or Workspace(p.device)
-    buf = ws.get(_NEED[key])
+    buf = ws.get(_NEED[key], counters=True)
     have = C.c_size_t(buf.numel())
     _check("moe_verify_gate", lib.moe_verify_gate(S, gamma, V, mode, _ptr(p), _ptr(q), _ptr(x),
                                                   _ptr(u), _ptr(r), _ptr(n_accepted), _ptr(out),

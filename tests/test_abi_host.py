@@ -279,3 +279,20 @@ def test_verify_probs_validation():
     assert nb.value >= 36 * (chunks * 8 + 256 * 8 + 102400 * 8 + 64 + 16)
     assert lib.moe_verify_probs(65536, 16, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None,
                                 C.byref(nb), None) == -2
+
+
+def test_workspace_head_is_zero_for_counter_calls():
+    """A binding Workspace shared by calls of both kinds: the head that an
+    expert pass or the filter wrote is zeroed before a call that keeps
+    arrival counters there, and left alone otherwise."""
+    ws = B.Workspace("cpu")
+    buf = ws.get(1024)                       # an expert pass or the filter
+    buf[:512] = 7                            # ... writes its data at the head
+    assert int(ws.get(1024)[:256].sum()) == 256 * 7     # data call: untouched
+    buf = ws.get(1024, counters=True)        # routing, stack pass, verify round
+    assert int(buf[:256].sum()) == 0 and int(buf[256:512].sum()) == 256 * 7
+    buf[:256] = 0                            # a counter call leaves it zero
+    buf[300] = 9
+    assert int(ws.get(1024, counters=True)[300]) == 9  # no fill needed
+    grown = ws.get(4096)                     # growing reallocates, zero-filled
+    assert grown.numel() == 4096 and int(grown.sum()) == 0

@@ -239,6 +239,35 @@ def test_route_reuses_its_workspace(E, d):
         assert int(ws.buf[:4].view(torch.int32).item()) == 0
 
 
+def test_one_workspace_shared_by_every_kind_of_call():
+    """The binding zeroes the workspace head that a dedup pass or the filter
+    wrote (compaction record, filter statistics) before routing, the stack
+    pass or a verification round uses it for arrival counters: each call on
+    the shared workspace equals the same call on a fresh one."""
+    cfg = small_config("shared-ws", 512, 64, 6, 352, 2, "bf16")
+    lay = synth.make_layer(cfg, "cpu")
+    lay_dev = to_dev(lay)
+    shape = B.shape_of(cfg)
+    ws = B.Workspace()
+    rng = np.random.default_rng(5)
+    for rep, n in enumerate([16, 3, 9]):
+        x = synth.make_hidden(cfg, n, rep, "cuda")
+        idx_f, w_f = B.route(shape, lay_dev["gate_w"], x)
+        y_f = B.expert_pass_dedup(shape, lay_dev, x, idx_f, w_f)
+        y_s = B.expert_pass_dedup(shape, lay_dev, x, idx_f, w_f, ws=ws)
+        idx_s, w_s = B.route(shape, lay_dev["gate_w"], x, ws=ws)
+        lg = torch.from_numpy(rng.standard_normal((2, 3, 3000)).astype(np.float32)).cuda()
+        p_f = B.verify_probs(lg, 0.8, 0.9)
+        p_s = B.verify_probs(lg, 0.8, 0.9, ws=ws)
+        xt = p_f[:, :2].argmax(dim=2).to(torch.int32)
+        n_f, t_f = B.verify_gate(p_f, xt, mode=B.VERIFY_GREEDY)
+        n_s, t_s = B.verify_gate(p_s, xt, mode=B.VERIFY_GREEDY, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y_s, y_f) and torch.equal(idx_s, idx_f) and torch.equal(w_s, w_f)
+        assert torch.equal(p_s, p_f) and torch.equal(n_s, n_f) and torch.equal(t_s, t_f)
+        assert int(ws.buf[:256].count_nonzero()) == 0   # the round left its counters zero
+
+
 def test_runs_are_bitwise_deterministic():
     cfg = small_config("det", 512, 64, 6, 352, 2, "bf16")
     lay_dev = to_dev(synth.make_layer(cfg, "cpu"))
