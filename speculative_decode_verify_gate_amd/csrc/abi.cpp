@@ -213,6 +213,17 @@ int launch_pass(const moe_shape *s, const LayerWeights &w, int L, const float *x
   a.gstart[G] = gs[G];
   a.ibase[G] = routed;
   a.n_routed = dedup ? routed : slots;
+  // The dedup grid holds U_max = min(E, N*k) routed instances; folded, it
+  // holds ceil(U_max / 2) and a workgroup runs a second instance only when
+  // U exceeds that.  Folding pays while U stays below the fold (fewer
+  // absent workgroups to dispatch) and costs a second tile per workgroup
+  // when U nears U_max, so it is used only where the instance space is large
+  // against the k experts every token selects: E >= 8k and a fold of at
+  // least 2k.
+  const int half = (routed + 1) / 2;
+  a.fold = (dedup && G == 1 && L == 1 && s->n_experts >= 8 * s->top_k && half >= 2 * s->top_k)
+               ? half
+               : 0;
   a.L = L;
   a.lw13 = 2 * fd * s->n_experts;
   a.lw2 = fd * s->n_experts;

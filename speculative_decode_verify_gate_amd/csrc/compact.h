@@ -26,16 +26,18 @@ namespace moe {
 // slots slot0 .. slot0+slots-1 of the pass (a group of whole tokens; slot0
 // is a multiple of k); the expert's entries (slot s = t*k + j, in
 // increasing s) go to ent_row[] (s) and ent_tok[] (s / k), their number to
-// *m.  All threads of the workgroup call it (it contains barriers) and get
-// the same result.  slots <= 2 * blockDim.x.
+// *m, and the number of distinct valid experts (U) to *n_distinct.  All
+// threads of the workgroup call it (it contains barriers) and get the same
+// results.  slots <= 2 * blockDim.x.
 template <class Row, class Tok>
 __device__ inline int local_instance(const int32_t *__restrict__ idx, int slots, int slot0,
-                                     int E, int k, int u, Row *ent_row, Tok *ent_tok, int *m) {
+                                     int E, int k, int u, Row *ent_row, Tok *ent_tok, int *m,
+                                     int *n_distinct) {
   constexpr int kWords = MOE_MAX_EXPERTS / 32;
   constexpr int kMaxWaves = 16;
   __shared__ uint32_t pres[kWords];
   __shared__ int wcnt[2][kMaxWaves];
-  __shared__ int s_e;
+  __shared__ int s_e, s_u;
   const int tid = threadIdx.x;
   const int nth = blockDim.x;
   const int lane = tid & 63;
@@ -56,10 +58,12 @@ __device__ inline int local_instance(const int32_t *__restrict__ idx, int slots,
     if (es[p] >= 0) atomicOr(&pres[es[p] >> 5], 1u << (es[p] & 31));
   __syncthreads();
   if (tid == 0) {
-    int e = -1, left = u;
-    for (int w = 0; w < kWords && e < 0; ++w) {
+    int e = -1, left = u, all = 0;
+    for (int w = 0; w < kWords; ++w) {
       uint32_t bits = pres[w];
       const int c = __popc(bits);
+      all += c;
+      if (e >= 0) continue;
       if (left < c) {
         for (int i = 0; i < left; ++i) bits &= bits - 1u;  // drop the lowest bits
         e = w * 32 + __ffs(bits) - 1;
@@ -68,9 +72,11 @@ __device__ inline int local_instance(const int32_t *__restrict__ idx, int slots,
       }
     }
     s_e = e;
+    s_u = all;
   }
   __syncthreads();
   const int e = s_e;
+  *n_distinct = s_u;
   if (e < 0) return -1;
 
   // entries of e in slot order: per pass, a wave's matches are counted with

@@ -106,8 +106,13 @@ constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
 // of layers (all layers' instances in one grid, layer-major).
 constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
 
+// One tile (instance bid / RT, row tile bid % RT).  The dedup engine's
+// routed instances also report U, the number of distinct experts of the
+// pass (of the token group, when grouped), to *n_distinct.
 template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
-__global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
+__device__ __attribute__((always_inline)) inline void expert_tile(const ExpertArgs &a, int bid,
+                                                                  int *ent_row, int *ent_tok,
+                                                                  int *n_distinct) {
   constexpr bool DIRECT = CTMAX == 1;
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
   using T = WT<BF16>;
@@ -119,8 +124,6 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   constexpr int ITEM = 16 / EB;                     // elements per 16-byte item
 
   extern __shared__ __align__(16) unsigned char lds[];  // staged tokens / partials
-  __shared__ int ent_row[MOE_MAX_SLOTS];
-  __shared__ int ent_tok[MOE_MAX_SLOTS];
 
   const int R = UP ? a.f : a.d;  // output rows
   const int K = UP ? a.d : a.f;  // reduction length
@@ -128,7 +131,6 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   // A stack runs each layer's grid in turn: its own weights, routing,
   // compaction record, U and buffers; the tokens are shared.  Only the stack
   // instantiation offsets the per-layer arrays.
-  int bid = blockIdx.x;
   int layer = 0;
   if (VAR == kStack) {
     const int bpl = (a.n_routed + a.S) * RT;
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
     const int t0 = grouped ? a.gstart[grp] : 0;
     const int t1 = grouped ? a.gstart[grp + 1] : a.N;
     e = local_instance(idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E, a.k, u, ent_row,
-                       ent_tok, &m);
+                       ent_tok, &m, n_distinct);
     if (e < 0) return;  // past the group's U
     have_entries = true;
   } else {
@@ -215,6 +217,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
     if (a.dedup) {
       rec = cmp + (grouped ? (size_t)grp * a.rec_ints : 0);
       src = rec + CL.uniq();
+      *n_distinct = rec[CL.u()];
     }
     e = src[u];
     if (e < 0 || e >= a.E) return;  // past the group's U (dedup) or an empty slot
@@ -502,10 +505,31 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   }
 }
 
+// The dedup engine's grid is sized for U_max = min(E, N*k) distinct
+// experts because U is known only on the device.  With a.fold > 0 the
+// routed part is folded: workgroup (slot v, row tile rt) runs distinct
+// expert v, then v + fold if v + fold < U (fold = ceil(U_max / 2)), so the
+// grid holds half the absent instances and, while U <= fold, every
+// workgroup runs one tile.  The first tile learns U on the way: from the
+// presence mask it builds (up) or from the compaction record (down).
+template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
+__global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
+  __shared__ int ent_row[MOE_MAX_SLOTS];
+  __shared__ int ent_tok[MOE_MAX_SLOTS];
+  int U = 0;
+  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, blockIdx.x, ent_row, ent_tok, &U);
+  if (VAR != kPlain || a.fold == 0) return;
+  const int RT = (UP ? a.f : a.d) / kTile;
+  const int slot = blockIdx.x / RT;
+  if (slot < a.S || slot - a.S + a.fold >= U) return;
+  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, blockIdx.x + a.fold * RT, ent_row, ent_tok, &U);
+}
+
 template <bool BF16, bool UP, bool TILED, int VAR>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
-  const long long blocks = (long long)a.L * (a.n_routed + a.S) * (R / kTile);
+  const int routed = (VAR == kPlain && a.fold > 0) ? a.fold : a.n_routed;
+  const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // allow more than the default 64 KB of dynamic LDS, once per kernel

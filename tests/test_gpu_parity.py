@@ -239,6 +239,35 @@ def test_route_reuses_its_workspace(E, d):
         assert int(ws.buf[:4].view(torch.int32).item()) == 0
 
 
+@pytest.mark.parametrize("n", [5, 16, 64])
+def test_dedup_around_the_folded_grid(n):
+    """The dedup grid is folded in half where E >= 8k and ceil(U_max/2) >=
+    2k: a workgroup runs distinct expert v and, when U > fold, v + fold.
+    Routings with exactly U experts at k, fold - 1, fold, fold + 1 and U_max
+    (narrow and LDS-staged wide tiles) give the per-slot output bit for bit
+    and report U; one case is checked against the oracle."""
+    cfg = small_config("fold", 512, 64, 6, 352, 2, "bf16")
+    lay = synth.make_layer(cfg, "cpu")
+    host, lay_dev, shape = host_layer(lay), to_dev(lay), B.shape_of(cfg)
+    u_max = min(cfg.E, n * cfg.k)
+    fold = (u_max + 1) // 2
+    assert cfg.E >= 8 * cfg.k and fold >= 2 * cfg.k       # the folded grid runs
+    x = synth.make_hidden(cfg, n, 3, "cpu")
+    x_dev = x.cuda()
+    for U in sorted({cfg.k, fold - 1, fold, fold + 1, u_max}):
+        idx, w = synth.crafted_routing(n, cfg.k, cfg.E, U, seed=U)
+        idx_d, w_d = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+        nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y_dd = B.expert_pass_dedup(shape, lay_dev, x_dev, idx_d, w_d, n_unique=nu)
+        y_ps = B.expert_pass_perslot(shape, lay_dev, x_dev, idx_d, w_d)
+        torch.cuda.synchronize()
+        assert int(nu.item()) == U, (n, U)
+        assert torch.equal(y_dd, y_ps), (n, U)
+        if U == fold + 1:
+            y_ref = oracle_y(cfg, host, x.numpy(), idx, w)[0]
+            assert rel_err(y_dd.cpu().numpy(), y_ref) <= OUT_RTOL["bf16"], (n, U)
+
+
 def test_one_workspace_shared_by_every_kind_of_call():
     """The binding zeroes the workspace head that a dedup pass or the filter
     wrote (compaction record, filter statistics) before routing, the stack
