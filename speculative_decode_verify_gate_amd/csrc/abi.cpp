@@ -221,7 +221,7 @@ int launch_pass(const moe_shape *s, const LayerWeights &w, int L, const float *x
   // against the k experts every token selects: E >= 8k and a fold of at
   // least 2k.
   const int half = (routed + 1) / 2;
-  a.fold = (dedup && G == 1 && L == 1 && s->n_experts >= 8 * s->top_k && half >= 2 * s->top_k)
+  a.fold = (dedup && G == 1 && s->n_experts >= 8 * s->top_k && half >= 2 * s->top_k)
                ? half
                : 0;
   a.L = L;

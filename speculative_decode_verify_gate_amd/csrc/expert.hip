@@ -106,13 +106,14 @@ constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
 // of layers (all layers' instances in one grid, layer-major).
 constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
 
-// One tile (instance bid / RT, row tile bid % RT).  The dedup engine's
-// routed instances also report U, the number of distinct experts of the
-// pass (of the token group, when grouped), to *n_distinct.
+// One tile (instance bid / RT, row tile bid % RT) of layer `layer` (0
+// unless stacked).  The dedup engine's routed instances also report U, the
+// number of distinct experts of the pass (of the token group, when grouped),
+// to *n_distinct.
 template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
-__device__ __attribute__((always_inline)) inline void expert_tile(const ExpertArgs &a, int bid,
-                                                                  int *ent_row, int *ent_tok,
-                                                                  int *n_distinct) {
+__device__ __attribute__((always_inline)) inline void expert_tile(const ExpertArgs &a, int layer,
+                                                                  int bid, int *ent_row,
+                                                                  int *ent_tok, int *n_distinct) {
   constexpr bool DIRECT = CTMAX == 1;
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
   using T = WT<BF16>;
@@ -131,12 +132,6 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
   // A stack runs each layer's grid in turn: its own weights, routing,
   // compaction record, U and buffers; the tokens are shared.  Only the stack
   // instantiation offsets the per-layer arrays.
-  int layer = 0;
-  if (VAR == kStack) {
-    const int bpl = (a.n_routed + a.S) * RT;
-    layer = bid / bpl;
-    bid -= layer * bpl;
-  }
   const int32_t *idx = a.idx;
   const int32_t *cmp = a.cmp;
   int32_t *cmp_out = a.cmp_out;
@@ -507,7 +502,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
 
 // The dedup engine's grid is sized for U_max = min(E, N*k) distinct
 // experts because U is known only on the device.  With a.fold > 0 the
-// routed part is folded: workgroup (slot v, row tile rt) runs distinct
+// routed part (of every layer, when stacked) is folded: workgroup (slot v, row tile rt) runs distinct
 // expert v, then v + fold if v + fold < U (fold = ceil(U_max / 2)), so the
 // grid holds half the absent instances and, while U <= fold, every
 // workgroup runs one tile.  The first tile learns U on the way: from the
@@ -516,19 +511,26 @@ template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
 __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
   __shared__ int ent_row[MOE_MAX_SLOTS];
   __shared__ int ent_tok[MOE_MAX_SLOTS];
-  int U = 0;
-  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, blockIdx.x, ent_row, ent_tok, &U);
-  if (VAR != kPlain || a.fold == 0) return;
   const int RT = (UP ? a.f : a.d) / kTile;
-  const int slot = blockIdx.x / RT;
+  const bool folded = (VAR == kPlain || VAR == kStack) && a.fold > 0;
+  int layer = 0, bid = blockIdx.x;
+  if (VAR == kStack) {
+    const int bpl = ((folded ? a.fold : a.n_routed) + a.S) * RT;  // workgroups per layer
+    layer = bid / bpl;
+    bid -= layer * bpl;
+  }
+  int U = 0;
+  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid, ent_row, ent_tok, &U);
+  if (!folded) return;
+  const int slot = bid / RT;
   if (slot < a.S || slot - a.S + a.fold >= U) return;
-  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, blockIdx.x + a.fold * RT, ent_row, ent_tok, &U);
+  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid + a.fold * RT, ent_row, ent_tok, &U);
 }
 
 template <bool BF16, bool UP, bool TILED, int VAR>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
-  const int routed = (VAR == kPlain && a.fold > 0) ? a.fold : a.n_routed;
+  const int routed = ((VAR == kPlain || VAR == kStack) && a.fold > 0) ? a.fold : a.n_routed;
   const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -51,9 +51,9 @@ struct ExpertArgs {
                           //    u-th distinct selected expert; 2: the same
                           //    within each token group of the tables below
   int n_routed;           // routed instances (U_max for the dedup engine)
-  int fold;               // dedup, one layer, one group: routed instance
-                          // slots in the grid (each runs u, u + fold, ...),
-                          // or 0: one slot per routed instance
+  int fold;               // dedup, one group: routed instance slots per
+                          // layer in the grid (slot v runs v, then v + fold
+                          // if present), or 0: one slot per routed instance
   int lds_bytes;          // dynamic LDS per workgroup
   // Dedup within token groups: tokens gstart[g] .. gstart[g+1]-1 form group
   // g, whose distinct experts are routed instances ibase[g] .. ibase[g+1]-1

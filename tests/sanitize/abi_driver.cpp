@@ -56,13 +56,13 @@ static void check_expert(const ExpertArgs &a) {
   CHECK(a.L == 1 || a.G == 1);
   CHECK((a.cmp != nullptr) == (a.dedup != 0) && a.abuf && a.obuf && a.y && a.x);
   CHECK((size_t)a.rec_ints * 4 % 256 == 0 && a.rec_ints >= 2 + 3 * a.E + a.N * a.k);
-  // folded dedup grid: one layer, one group, half the routed slots (so two
-  // passes cover U_max), E >= 8k and a fold of at least 2k
+  // folded dedup grid: one group, half the routed slots (so two passes
+  // cover U_max), E >= 8k and a fold of at least 2k
   if (a.fold != 0) {
-    CHECK(a.dedup == 1 && a.G == 1 && a.L == 1);
+    CHECK(a.dedup == 1 && a.G == 1);
     CHECK(a.fold == (a.n_routed + 1) / 2 && 2 * a.fold >= a.n_routed);
     CHECK(a.E >= 8 * a.k && a.fold >= 2 * a.k);
-  } else if (a.dedup == 1 && a.L == 1) {
+  } else if (a.dedup == 1) {
     CHECK(a.E < 8 * a.k || (a.n_routed + 1) / 2 < 2 * a.k);
   }
 }
