@@ -203,27 +203,30 @@ int launch_pass(const moe_shape *s, const LayerWeights &w, int L, const float *x
   const int slots = n * s->top_k;
   a.G = G;
   a.rec_ints = (int)(rec_bytes / sizeof(int32_t));
-  int routed = 0;
-  for (int g = 0; g < G; ++g) {
-    const int gslots = (gs[g + 1] - gs[g]) * s->top_k;
-    a.gstart[g] = gs[g];
-    a.ibase[g] = routed;
-    routed += gslots < s->n_experts ? gslots : s->n_experts;
-  }
-  a.gstart[G] = gs[G];
-  a.ibase[G] = routed;
-  a.n_routed = dedup ? routed : slots;
   // The dedup grid holds U_max = min(E, N*k) routed instances; folded, it
   // holds ceil(U_max / 2) and a workgroup runs a second instance only when
   // U exceeds that.  Folding pays while U stays below the fold (fewer
   // absent workgroups to dispatch) and costs a second tile per workgroup
   // when U nears U_max, so it is used only where the instance space is large
   // against the k experts every token selects: E >= 8k and a fold of at
-  // least 2k.
-  const int half = (routed + 1) / 2;
-  a.fold = (dedup && G == 1 && s->n_experts >= 8 * s->top_k && half >= 2 * s->top_k)
-               ? half
-               : 0;
+  // least 2k.  Token groups fold one by one.
+  const bool large = s->n_experts >= 8 * s->top_k;
+  auto folded = [&](int m) { return (dedup && large && (m + 1) / 2 >= 2 * s->top_k) ? (m + 1) / 2 : m; };
+  int routed = 0, grid_routed = 0;
+  for (int g = 0; g < G; ++g) {
+    const int gslots = (gs[g + 1] - gs[g]) * s->top_k;
+    const int m = gslots < s->n_experts ? gslots : s->n_experts;
+    a.gstart[g] = gs[g];
+    a.ibase[g] = routed;
+    a.fbase[g] = grid_routed;
+    routed += m;
+    grid_routed += folded(m);
+  }
+  a.gstart[G] = gs[G];
+  a.ibase[G] = routed;
+  a.fbase[G] = grid_routed;
+  a.n_routed = dedup ? routed : slots;
+  a.fold = (G == 1 && folded(routed) < routed) ? folded(routed) : 0;
   a.L = L;
   a.lw13 = 2 * fd * s->n_experts;
   a.lw2 = fd * s->n_experts;

@@ -107,13 +107,15 @@ constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
 constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
 
 // One tile (instance bid / RT, row tile bid % RT) of layer `layer` (0
-// unless stacked).  The dedup engine's routed instances also report U, the
-// number of distinct experts of the pass (of the token group, when grouped),
-// to *n_distinct.
+// unless stacked).  In the dedup up kernel, writer >= 0 first writes the
+// compaction record of token group `writer` (one workgroup per group).  The
+// dedup engine's routed instances also report U, the number of distinct
+// experts of the pass (of the token group, when grouped), to *n_distinct.
 template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
 __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertArgs &a, int layer,
-                                                                  int bid, int *ent_row,
-                                                                  int *ent_tok, int *n_distinct) {
+                                                                  int bid, int writer,
+                                                                  int *ent_row, int *ent_tok,
+                                                                  int *n_distinct) {
   constexpr bool DIRECT = CTMAX == 1;
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
   using T = WT<BF16>;
@@ -179,8 +181,8 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
   // 2), so the plain engines' prologue has no extra argument loads.
   constexpr bool grouped = VAR == kGrouped;
   int u = inst - a.S;
-  if (UP && a.dedup && bid < (grouped ? a.G : 1)) {
-    const int b = bid;
+  if (UP && a.dedup && writer >= 0) {
+    const int b = writer;
     const int t0 = grouped ? a.gstart[b] : 0;
     const int t1 = grouped ? a.gstart[b + 1] : a.N;
     write_record(idx + t0 * a.k, (t1 - t0) * a.k, t0 * a.k, a.E,
@@ -502,7 +504,8 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
 
 // The dedup engine's grid is sized for U_max = min(E, N*k) distinct
 // experts because U is known only on the device.  With a.fold > 0 the
-// routed part (of every layer, when stacked) is folded: workgroup (slot v, row tile rt) runs distinct
+// routed part (of every layer, when stacked; of every token group, when
+// grouped, by the tables fbase / ibase) is folded: workgroup (slot v, row tile rt) runs distinct
 // expert v, then v + fold if v + fold < U (fold = ceil(U_max / 2)), so the
 // grid holds half the absent instances and, while U <= fold, every
 // workgroup runs one tile.  The first tile learns U on the way: from the
@@ -512,25 +515,49 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
   __shared__ int ent_row[MOE_MAX_SLOTS];
   __shared__ int ent_tok[MOE_MAX_SLOTS];
   const int RT = (UP ? a.f : a.d) / kTile;
-  const bool folded = (VAR == kPlain || VAR == kStack) && a.fold > 0;
+  int U = 0;
+  if (VAR == kGrouped) {
+    // groups fold one by one: group g's routed slots in the grid are
+    // fbase[g] .. fbase[g+1]-1, its instances ibase[g] .. ibase[g+1]-1
+    const int writer = (int)blockIdx.x < a.G ? (int)blockIdx.x : -1;
+    const int slot = blockIdx.x / RT, rt = blockIdx.x - slot * RT;
+    if (slot < a.S) {
+      expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, 0, blockIdx.x, writer, ent_row, ent_tok, &U);
+      return;
+    }
+    const int v = slot - a.S;
+    int g = 0, hi = a.G;  // the group whose grid slots hold v (bases ascend)
+    while (hi - g > 1) {
+      const int mid = (g + hi) >> 1;
+      if (v >= a.fbase[mid]) g = mid; else hi = mid;
+    }
+    const int vl = v - a.fbase[g];
+    const int fg = a.fbase[g + 1] - a.fbase[g], mg = a.ibase[g + 1] - a.ibase[g];
+    const int bid = (a.S + a.ibase[g] + vl) * RT + rt;
+    expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, 0, bid, writer, ent_row, ent_tok, &U);
+    if (fg < mg && vl + fg < U)
+      expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, 0, bid + fg * RT, -1, ent_row, ent_tok, &U);
+    return;
+  }
+  const bool folded = a.fold > 0;
   int layer = 0, bid = blockIdx.x;
   if (VAR == kStack) {
     const int bpl = ((folded ? a.fold : a.n_routed) + a.S) * RT;  // workgroups per layer
     layer = bid / bpl;
     bid -= layer * bpl;
   }
-  int U = 0;
-  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid, ent_row, ent_tok, &U);
+  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid, bid == 0 ? 0 : -1, ent_row, ent_tok,
+                                           &U);
   if (!folded) return;
   const int slot = bid / RT;
   if (slot < a.S || slot - a.S + a.fold >= U) return;
-  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid + a.fold * RT, ent_row, ent_tok, &U);
+  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid + a.fold * RT, -1, ent_row, ent_tok, &U);
 }
 
 template <bool BF16, bool UP, bool TILED, int VAR>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
-  const int routed = ((VAR == kPlain || VAR == kStack) && a.fold > 0) ? a.fold : a.n_routed;
+  const int routed = VAR == kGrouped ? a.fbase[a.G] : (a.fold > 0 ? a.fold : a.n_routed);
   const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

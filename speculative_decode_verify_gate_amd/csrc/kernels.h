@@ -54,6 +54,7 @@ struct ExpertArgs {
   int fold;               // dedup, one group: routed instance slots per
                           // layer in the grid (slot v runs v, then v + fold
                           // if present), or 0: one slot per routed instance
+                          // (grouped passes use fbase instead)
   int lds_bytes;          // dynamic LDS per workgroup
   // Dedup within token groups: tokens gstart[g] .. gstart[g+1]-1 form group
   // g, whose distinct experts are routed instances ibase[g] .. ibase[g+1]-1
@@ -69,6 +70,10 @@ struct ExpertArgs {
   size_t lw13, lw2, lws13, lws2;
   int gstart[MOE_MAX_GROUPS + 1];
   int ibase[MOE_MAX_GROUPS + 1];
+  // Grouped dedup: group g's routed slots in the grid start at fbase[g]
+  // (fbase[g+1] - fbase[g] is its instance count ibase[g+1] - ibase[g], or
+  // half of it rounded up when the group's grid is folded).
+  int fbase[MOE_MAX_GROUPS + 1];
 };
 
 // Routing.  Partial logits of all splits at most this many bytes: one launch

@@ -56,6 +56,14 @@ static void check_expert(const ExpertArgs &a) {
   CHECK(a.L == 1 || a.G == 1);
   CHECK((a.cmp != nullptr) == (a.dedup != 0) && a.abuf && a.obuf && a.y && a.x);
   CHECK((size_t)a.rec_ints * 4 % 256 == 0 && a.rec_ints >= 2 + 3 * a.E + a.N * a.k);
+  // grid slots per token group: the group's instances, or half of them
+  // rounded up where its dedup grid folds (E >= 8k, half >= 2k)
+  CHECK(a.fbase[0] == 0);
+  for (int g = 0; g < a.G; ++g) {
+    const int m = a.ibase[g + 1] - a.ibase[g], f = a.fbase[g + 1] - a.fbase[g];
+    const bool fold = a.dedup != 0 && a.E >= 8 * a.k && (m + 1) / 2 >= 2 * a.k;
+    CHECK(f == (fold ? (m + 1) / 2 : m));
+  }
   // folded dedup grid: one group, half the routed slots (so two passes
   // cover U_max), E >= 8k and a fold of at least 2k
   if (a.fold != 0) {
