@@ -261,3 +261,36 @@ def test_full_v3_per_sequence_dedup():
     assert err <= OUT_RTOL["bf16"]
     del lay_dev, tiled
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("sizes,targets", [
+    # 55 tokens (wide tiles): m_g = 64, 64, 30, 12, 64 -> folds 32, 32, 15,
+    # none (6 < 2k), 32; U_g at k, fold - 1, fold + 1, the unfolded maximum,
+    # and the folded maximum
+    ([16, 16, 5, 2, 16], [6, 31, 16, 12, 64]),
+    # 16 tokens (narrow tiles): m_g = 30, 30, 12, 24 -> folds 15, 15, none, 12
+    ([5, 5, 2, 4], [6, 16, 12, 13]),
+])
+def test_grouped_dedup_around_each_groups_fold(sizes, targets):
+    """Token groups fold their grids one by one (E >= 8k and a fold of at
+    least 2k): groups whose U_g sits below, at and above their fold, next to
+    an unfolded group, give the per-slot output bit for bit, exact U_g, and
+    the host's grouped byte count."""
+    cfg = small_config("gfold", 512, 64, 6, 352, 2, "bf16")
+    lay_dev = to_dev(synth.make_layer(cfg, "cpu"))
+    shape = B.shape_of(cfg)
+    parts = [synth.crafted_routing(n_g, cfg.k, cfg.E, U, seed=100 + i)
+             for i, (n_g, U) in enumerate(zip(sizes, targets))]
+    idx = np.concatenate([p[0] for p in parts])
+    w = np.concatenate([p[1] for p in parts])
+    gs = [0] + np.cumsum(sizes).tolist()
+    n = gs[-1]
+    x = synth.make_hidden(cfg, n, 7, "cuda")
+    idx_d, w_d = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+    nun = torch.zeros(len(sizes), dtype=torch.int32, device="cuda")
+    y_g = B.expert_pass_dedup_grouped(shape, lay_dev, x, idx_d, w_d, gs, n_unique=nun)
+    y_ps = B.expert_pass_perslot(shape, lay_dev, x, idx_d, w_d)
+    torch.cuda.synchronize()
+    assert list(nun.cpu().numpy()) == targets
+    assert torch.equal(y_g, y_ps)
+    assert B.pass_bytes_grouped(shape, idx, gs)[1] == targets
