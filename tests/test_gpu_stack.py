@@ -175,3 +175,22 @@ def test_full_v2lite_stack_slice():
                 assert int(nu[l].item()) == int(rnu.item())
     del stack
     torch.cuda.empty_cache()
+
+
+def test_stack_dedup_past_the_fold():
+    """Independent tokens (rho = 0) push U past the folded grid's half
+    (E = 64, k = 6, n = 16: U_max 64, fold 32), so some layers' workgroups
+    run a second distinct expert: the stack still equals the per-layer
+    calls bit for bit."""
+    cfg = small_config("stack-fold", 512, 64, 6, 352, 2, "bf16", rho=0.0)
+    L, n = 3, 16
+    stack = _make_stack(cfg, L, bias=False, tiled=True)
+    x = synth.make_hidden(cfg, n, 4, "cuda")
+    nu = torch.zeros(L, dtype=torch.int32, device="cuda")
+    idx, w, y = B.stack_pass(B.shape_of(cfg), stack, x, "dedup", n_unique=nu)
+    torch.cuda.synchronize()
+    assert int(nu.max().item()) > 32           # the second-tile path runs
+    for l, (ri, rw, ry, rnu) in enumerate(_per_layer(cfg, stack, x, "dedup")):
+        assert torch.equal(idx[l], ri) and torch.equal(w[l], rw), l
+        assert torch.equal(y[l], ry), l
+        assert int(nu[l].item()) == int(rnu.item()), l
