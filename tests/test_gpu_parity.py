@@ -239,14 +239,14 @@ def test_route_reuses_its_workspace(E, d):
         assert int(ws.buf[:4].view(torch.int32).item()) == 0
 
 
-@pytest.mark.parametrize("n", [5, 16, 64])
-def test_dedup_around_the_folded_grid(n):
+@pytest.mark.parametrize("n,wdt", [(5, "bf16"), (16, "bf16"), (64, "bf16"), (16, "f32")])
+def test_dedup_around_the_folded_grid(n, wdt):
     """The dedup grid is folded in half where E >= 8k and ceil(U_max/2) >=
     2k: a workgroup runs distinct expert v and, when U > fold, v + fold.
     Routings with exactly U experts at k, fold - 1, fold, fold + 1 and U_max
     (narrow and LDS-staged wide tiles) give the per-slot output bit for bit
     and report U; one case is checked against the oracle."""
-    cfg = small_config("fold", 512, 64, 6, 352, 2, "bf16")
+    cfg = small_config("fold", 512, 64, 6, 352, 2, wdt)
     lay = synth.make_layer(cfg, "cpu")
     host, lay_dev, shape = host_layer(lay), to_dev(lay), B.shape_of(cfg)
     u_max = min(cfg.E, n * cfg.k)
@@ -265,7 +265,7 @@ def test_dedup_around_the_folded_grid(n):
         assert torch.equal(y_dd, y_ps), (n, U)
         if U == fold + 1:
             y_ref = oracle_y(cfg, host, x.numpy(), idx, w)[0]
-            assert rel_err(y_dd.cpu().numpy(), y_ref) <= OUT_RTOL["bf16"], (n, U)
+            assert rel_err(y_dd.cpu().numpy(), y_ref) <= OUT_RTOL[wdt], (n, U)
 
 
 def test_one_workspace_shared_by_every_kind_of_call():
