@@ -16,11 +16,15 @@ previous call's experts cached.  `value` is the step's algorithmic bytes
 (gate + requested expert bytes of both engines) over its time, inputs
 resident in HBM.
 
-The JSON line also carries the n = 1..16 sweep (µs and GB/s per engine, the
-dedup byte share u(n), the bandwidth ratio r(n), measured and predicted
-crossovers), the roofline of the dominant kernel (the W1/W3 + SwiGLU kernel,
-timed with HIP events on the launch stream) and the CPU oracle timed on
-this host as a reported baseline.
+The last stdout line is the compact headline (under 4 KB): the value, the
+roofline of the dominant kernel (the W1/W3 + SwiGLU kernel of the dedup
+engine, whose bytes all come from HBM; per engine the up and down kernels,
+each timed with HIP events on the launch stream), the n = 1..16 sweep (µs
+and requested GB/s per engine, mean U, r(n)), the measured and predicted
+crossovers and how a bandwidth error moves them, the saving checks, and the
+CPU oracle timed on this host as a reported baseline.  The full record
+(per-pass percentiles, calibration fits, draft-length tables, verification
+round, fused stack) goes to the --details file.
 """
 import argparse
 import json
@@ -221,7 +225,7 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps, top_up=True):
                        "total_us": round(float(np.median(tt[name])), 2),
                        "requested_MB": round(req / 1e6, 3),
                        "GBs": round(req / us / 1e3, 1),
-                       "hbm_frac": round(req / us / 1e3 / HBM_PEAK_GBS, 3),
+                       "req_frac": round(req / us / 1e3 / HBM_PEAK_GBS, 3),
                        "routed_GBs": round(routed / us / 1e3, 1)}
         u_bar = float(np.mean(U["dedup"])) / (N * k)
         r["u_bar"] = round(u_bar, 4)
@@ -320,9 +324,11 @@ def predict_from_calibration(cfg, calib, n, u_bar):
 def saving_check(rec, measured, sav, sav_sd, iv_sd, trace):
     """Record the predicted saving (the line model, and the trace-aware one
     that prices repeated per-slot reads separately), their errors and
-    whether the measured saving lies within two interval standard
-    deviations of each."""
+    whether the measured saving lies within two standard deviations of the
+    line model's parameter error (the calibration's own bound), and within
+    two of the wider interval that adds each fit's residual scatter."""
     rec["predicted_saving_us"], rec["predicted_saving_sd_us"] = round(sav, 2), round(sav_sd, 2)
+    rec["saving_within_param_2sd"] = bool(abs(measured - sav) <= 2 * sav_sd)
     rec["saving_interval_sd_us"] = round(iv_sd, 2)
     rec["saving_within_2sd"] = bool(abs(measured - sav) <= 2 * iv_sd)
     t_sav, t_sd, t_iv = trace
@@ -588,7 +594,7 @@ def variants_leg(cfg, eng, layers, n_values, reps):
         for name in names:
             req = routed[name] + cfg.S * Be
             rec[name] = {"us": round(med[name], 2), "GBs": round(req / med[name] / 1e3, 1),
-                         "hbm_frac": round(req / med[name] / 1e3 / HBM_PEAK_GBS, 3)}
+                         "req_frac": round(req / med[name] / 1e3 / HBM_PEAK_GBS, 3)}
         rec["union_saving_over_perseq_us"] = round(med["perseq"] - med["union"], 2)
         out.append(rec)
         log(f"  n={n:2d} x{G}: perslot {med['perslot']:8.1f} union {med['union']:8.1f} "
@@ -597,20 +603,22 @@ def variants_leg(cfg, eng, layers, n_values, reps):
     return out
 
 
-def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=()):
+def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=(),
+                engines=("perslot", "dedup")):
     """The headline step at one pass size: K timed steps after W warmups,
-    bracketed by device synchronisation.  With kernel_events, the library
-    brackets launches of those kernel kinds with HIP events on the launch
-    stream; otherwise nothing is recorded inside the timed region."""
+    bracketed by device synchronisation; a step is route + expert pass for
+    each of `engines`.  With kernel_events, the library brackets launches of
+    those kernel kinds with HIP events on the launch stream; otherwise
+    nothing is recorded inside the timed region."""
     nL = len(layers)
     N = x.shape[0]
     y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
     turn = 0
-    idxs = {"perslot": [], "dedup": []}
+    idxs = {name: [] for name in engines}
 
     def one_step(keep):
         nonlocal turn
-        for name in ("perslot", "dedup"):
+        for name in engines:
             lay = layers[turn % nL]
             turn += 1
             idx, w = eng.route(lay, x)
@@ -634,6 +642,48 @@ def timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=()):
     kt = B.timing_read()
     U = {k: [unique_count(i.cpu().numpy(), cfg.E) for i in v] for k, v in idxs.items()}
     return wall, kt, U
+
+
+def timeline_leg(cfg, eng, layers, n_values, steps, warmup):
+    """Per pass size and engine: W warmup steps, then K steps of route +
+    expert pass queued while a spin kernel holds the GPU, so that a kernel
+    trace of the run shows each launch's duration and the gaps between
+    launches as the GPU sees them (no host launch latency).  Cases run in
+    the order n, then per-slot before dedup; the wall time per step is
+    reported beside them."""
+    nL = len(layers)
+    out = []
+    turn = 0
+    for n in n_values:
+        N = cfg.tokens(n)
+        x = synth.make_hidden(cfg, n, 99, "cuda")
+        y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+        for name in ("perslot", "dedup"):
+            log(f"[timeline] n={n} {name}: {warmup} warmup + {steps} steps")
+            for _ in range(warmup):
+                lay = layers[turn % nL]
+                turn += 1
+                idx, w = eng.route(lay, x)
+                getattr(eng, name)(lay, x, idx, w, y)
+            torch.cuda.synchronize()
+            hold_gpu(0.1 * steps)
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            idxs = []
+            for _ in range(steps):
+                lay = layers[turn % nL]
+                turn += 1
+                idx, w = eng.route(lay, x)
+                getattr(eng, name)(lay, x, idx, w, y)
+                idxs.append(idx)
+            e1.record()
+            torch.cuda.synchronize()
+            U = [unique_count(i.cpu().numpy(), cfg.E) for i in idxs]
+            out.append({"n": n, "tokens": N, "engine": name,
+                        "us_per_step": round(e0.elapsed_time(e1) * 1e3 / steps, 2),
+                        "U_mean": round(float(np.mean(U)), 2)})
+    return {"kind": "timeline", "workload": f"{cfg.name}-shaped layer, route + expert pass",
+            "steps": steps, "warmup": warmup, "by_case": out}
 
 
 def host_info():
@@ -717,11 +767,12 @@ def cpu_sweep(seconds):
     return {"kind": "oracle sweep", "threads": threads, "host": host_info(), "points": out}
 
 
-def traffic_record(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+def traffic_record(kernel, engine, workload):
+    """HBM bytes per launch of one kernel of one engine from committed
+    rocprofv3 counter runs, if they were taken on the current kernel source;
+    else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{engine}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -731,6 +782,107 @@ def traffic_record(kernel, workload):
     if rec.get("source_sha256") != sha.hexdigest():
         return None
     return rec
+
+
+def engine_kernels(cfg, eng, layers, x, steps, warmup, engine):
+    """The up (W1/W3 + SwiGLU) and down (W2) kernels of one engine, timed
+    live: K steps of route + that engine's pass, the library bracketing the
+    two kernels' launches with HIP events on the launch stream.  Algorithmic
+    bytes per launch: instances streamed (N k + S per-slot, U + S dedup) x
+    the bytes of one instance's matrices (2 d f s_w up, d f s_w down)."""
+    _, kt, U = timed_steps(cfg, eng, layers, x, steps, warmup, kernel_events=("up", "down"),
+                           engines=(engine,))
+    N = x.shape[0]
+    units = [(N * cfg.k if engine == "perslot" else u) + cfg.S for u in U[engine]]
+    out = {}
+    for kind, unit in (("up", 2 * cfg.d * cfg.f * cfg.wbytes), ("down", cfg.d * cfg.f * cfg.wbytes)):
+        ms, launches = kt[kind]
+        launches = max(1, launches)
+        algo = sum(units) * unit / launches
+        avg_us = ms * 1e3 / launches
+        achieved = algo / (avg_us * 1e-6) / 1e9 if avg_us > 0 else None
+        tr = traffic_record(f"expert_{kind}", engine, cfg.name)
+        out[kind] = {"achieved": None if achieved is None else round(achieved, 1),
+                     "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(avg_us, 2), "launches": launches,
+                     "algorithmic_bytes_per_launch": int(algo), "unit_bytes": unit,
+                     "instances_per_launch": round(sum(units) / launches, 2),
+                     "traffic": None if tr is None else tr.get("bytes_per_launch"),
+                     "traffic_frac_of_algorithmic": None if tr is None else
+                     round(tr.get("bytes_per_launch") / algo, 3)}
+    return out
+
+
+def bandwidth_sensitivity(cfg, calib, sweep, z=2.0):
+    """How an error in the calibrated bandwidths moves each result: the
+    predicted crossovers and the best draft length, recomputed with each
+    engine's bandwidth moved by z standard errors in the direction that
+    favours it and in the direction that disfavours it.  Model pass time per
+    engine: t(n) = route(n) + B(n) / BW + t0 with B_ps = N k B_e and B_dd =
+    u(n) N k B_e (shared experts in t0)."""
+    Be = expert_bytes(cfg)
+    ns = [r["n"] for r in sweep]
+    fps, fdd = calib["perslot"], calib["dedup_pooled"]
+
+    def model(bw_ps, bw_dd):
+        ps, dd = stepmodel.with_bandwidth(fps, bw_ps), stepmodel.with_bandwidth(fdd, bw_dd)
+        t = {"perslot": {}, "dedup": {}}
+        saving = []
+        for r in sweep:
+            b_ps = cfg.tokens(r["n"]) * cfg.k * Be
+            tp = ps.predict(b_ps)[0]
+            td = dd.predict(r["u_bar"] * b_ps)[0]
+            t["perslot"][r["n"]] = tp + r["perslot"]["route_us"]
+            t["dedup"][r["n"]] = td + r["dedup"]["route_us"]
+            saving.append(tp - td)
+        return t, saving
+
+    cases = {"nominal": (fps.bw_GBs, fdd.bw_GBs),
+             "dedup_favoured": (fps.bw_GBs - z * fps.bw_sd_GBs, fdd.bw_GBs + z * fdd.bw_sd_GBs),
+             "perslot_favoured": (fps.bw_GBs + z * fps.bw_sd_GBs, fdd.bw_GBs - z * fdd.bw_sd_GBs)}
+    alphas = [0.3, 0.5, 0.6, 0.7, 0.8, 0.85, 0.9, 0.95, 0.98]
+    gmax = max(ns) - 1
+    out = {"z": z, "bw_ps_GBs": [round(fps.bw_GBs, 1), round(fps.bw_sd_GBs, 1)],
+           "bw_dd_GBs": [round(fdd.bw_GBs, 1), round(fdd.bw_sd_GBs, 1)], "cases": {}}
+    stairs = {}
+    for name, (bp, bd) in cases.items():
+        t, saving = model(bp, bd)
+        # r(n) of the per-n calibration, moved by z of its own standard error
+        shift = {"nominal": 0.0, "dedup_favoured": z, "perslot_favoured": -z}[name]
+        r = [x["r"] + shift * x["r_sd"] for x in sweep]
+        td = 0.05 * t["perslot"][1]
+        stairs[name] = {e: draftlen.staircase(alphas, t[e], td, gmax) for e in ("perslot", "dedup")}
+        out["cases"][name] = {
+            "r_pooled": round(bd / bp, 4),
+            "crossover_u_lt_r": stepmodel.first_n(ns, [x["u_bar"] < rr for x, rr in zip(sweep, r)]),
+            "crossover_model_saving": stepmodel.first_n(ns, [sv > 0 for sv in saving]),
+            "best_gamma": stairs[name]}
+    out["alphas"] = alphas
+    out["t_draft_over_t1"] = 0.05
+    out["best_gamma_max_shift"] = {
+        e: max(abs(a - b) for name in cases for a, b in zip(stairs[name][e], stairs["nominal"][e]))
+        for e in ("perslot", "dedup")}
+    return out
+
+
+def compact_sweep(sweep):
+    """Per-n record of the sweep for the headline: us and requested GB/s per
+    engine, mean U and r(n)."""
+    return [{"n": r["n"], "ps_us": r["perslot"]["us"], "ps_GBs": round(r["perslot"]["GBs"]),
+             "dd_us": r["dedup"]["us"], "dd_GBs": round(r["dedup"]["GBs"]), "U": r["U_mean"],
+             "r": r["r"]} for r in sweep]
+
+
+def write_details(path, doc):
+    """The full record of a run (sweep, calibration, draft lengths,
+    verification round, kernels, CPU baseline) as one JSON file."""
+    try:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(doc, f, indent=1)
+        log(f"[bench] details written to {path}")
+    except OSError as e:
+        log(f"[bench] could not write {path}: {e}")
 
 
 def main():
@@ -766,6 +918,18 @@ def main():
     ap.add_argument("--cpu-sweep", action="store_true",
                     help="only time the CPU oracle on every workload at a few pass sizes "
                          "(one JSON document)")
+    ap.add_argument("--engine", default="both", choices=("both", "perslot", "dedup"),
+                    help="engines of the timed steps (one engine isolates its kernels for "
+                         "a profiler run)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused-stack leg after the timed steps")
+    ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
+                    help="file for the full record of the run (the last stdout line is "
+                         "the compact headline)")
+    ap.add_argument("--timeline", default=None,
+                    help="comma-separated pass sizes: instead of the bench line, K steps of "
+                         "route + pass per engine at each size, queued while the GPU is held, "
+                         "for a kernel-trace timeline (one JSON document)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (for scaling HBM "
                          "byte counters) and print its byte counts")
@@ -812,6 +976,11 @@ def main():
     stack, layers = make_stack(cfg, shape, n_layers)
     eng = Engines(cfg)
 
+    if args.timeline:
+        print(json.dumps(timeline_leg(cfg, eng, layers, [int(v) for v in args.timeline.split(",")],
+                                      args.steps, args.warmup)), flush=True)
+        return
+
     if args.variants:
         log("[bench] variants warmup")
         variants_leg(cfg, eng, layers, cfg.n_values[:1], 2)
@@ -854,53 +1023,64 @@ def main():
                            f"({n_layers * layer_bytes / 1e9:.1f} GB of weights), "
                            f"n = 1..{max(cfg.n_values)}",
                "single_layer_sweep": sweep, "calibration": calibration_json(calib),
+               "bandwidth_sensitivity": bandwidth_sensitivity(cfg, calib, sweep),
                "by_rho": rho_sweep(cfg, eng, layers, stack, calib, args.stack_reps)}
-        print(json.dumps(doc), flush=True)
+        write_details(args.details, doc)
+        print(json.dumps(rho_summary(doc)), flush=True)
         return
 
+    engines = ("perslot", "dedup") if args.engine == "both" else (args.engine,)
     x = synth.make_hidden(cfg, n_head, 99, "cuda")
-    log(f"[bench] timed steps: {args.warmup} warmup + {args.steps}")
-    wall, _, U_list = timed_steps(cfg, eng, layers, x, args.steps, args.warmup)
+    log(f"[bench] timed steps ({'+'.join(engines)}): {args.warmup} warmup + {args.steps}")
+    wall, _, U_list = timed_steps(cfg, eng, layers, x, args.steps, args.warmup, engines=engines)
     N = cfg.tokens(n_head)
     Be = expert_bytes(cfg)
-    ps_bytes = gate_bytes(cfg) + (N * cfg.k + cfg.S) * Be
-    dd_bytes = [gate_bytes(cfg) + (u + cfg.S) * Be for u in U_list["dedup"]]
-    step_bytes = ps_bytes + float(np.mean(dd_bytes))
+    step_bytes = 0.0
+    if "perslot" in engines:
+        step_bytes += gate_bytes(cfg) + (N * cfg.k + cfg.S) * Be
+    if "dedup" in engines:
+        step_bytes += float(np.mean([gate_bytes(cfg) + (u + cfg.S) * Be for u in U_list["dedup"]]))
     ms_step = wall / args.steps * 1e3
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # Dominant kernel: W1/W3 + SwiGLU.  Timed live in a second timed region of
-    # the same steps in which the library brackets only that kernel with HIP
-    # events.  Algorithmic bytes per launch = (instances streamed) x (bytes of
-    # one instance's W1 and W3 = 2 d f s_w).
-    log("[bench] timed steps with up-kernel events")
-    _, kt, U_ev = timed_steps(cfg, eng, layers, x, args.steps, args.warmup,
-                              kernel_events=("up",))
-    up_unit = 2 * cfg.d * cfg.f * cfg.wbytes
-    up_ms, up_launches = kt["up"]
-    up_units = sum(N * cfg.k + cfg.S for _ in U_ev["perslot"]) + \
-        sum(u + cfg.S for u in U_ev["dedup"])
-    up_bytes = up_units * up_unit
-    up_avg_us = up_ms * 1e3 / max(1, up_launches)
-    achieved = up_bytes / (up_ms * 1e-3) / 1e9 if up_ms > 0 else None
-    traffic = traffic_record("expert_up", cfg.name)
+    # Dominant kernels, per engine: W1/W3 + SwiGLU (up) and W2 (down), each
+    # engine timed live in a timed region of its own in which the library
+    # brackets only those kernels with HIP events on the launch stream.
+    kern = {}
+    for name in engines:
+        log(f"[bench] {name} steps with up/down kernel events")
+        kern[name] = engine_kernels(cfg, eng, layers, x, args.steps, args.warmup, name)
+    main_eng = "dedup" if "dedup" in engines else engines[0]
+    up = kern[main_eng]["up"]
+    roofline = {"bound": "hbm", "kernel": f"expert_up (W1/W3 + SwiGLU), {main_eng} engine",
+                "achieved": up["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": up["frac"], "traffic": up["traffic"],
+                "avg_launch_us": up["avg_launch_us"],
+                "algorithmic_bytes_per_launch": up["algorithmic_bytes_per_launch"],
+                "per_engine": {e: {k: {kk: v[kk] for kk in ("achieved", "frac", "avg_launch_us",
+                                                              "traffic")}
+                                   for k, v in kern[e].items()} for e in engines}}
 
-    # The same rotation as one fused stack call per engine (all layers on the
-    # step's tokens): per-layer time including routing.
-    log("[bench] fused stack over the rotation")
-    fz = fused_stack_leg(cfg, stack, [n_head], 16)[n_head]
-    fused = {"layers": n_layers, "tokens": N,
-             "perslot_stack_us": round(fz["perslot"], 1), "dedup_stack_us": round(fz["dedup"], 1),
-             "perslot_us_per_layer": round(fz["perslot"] / n_layers, 2),
-             "dedup_us_per_layer": round(fz["dedup"] / n_layers, 2),
-             "U_mean": round(float(fz["U"].mean()), 2)}
+    fused = None
+    if not args.no_fused:
+        # The same rotation as one fused stack call per engine (all layers on
+        # the step's tokens): per-layer time including routing.
+        log("[bench] fused stack over the rotation")
+        fz = fused_stack_leg(cfg, stack, [n_head], 16)[n_head]
+        fused = {"layers": n_layers, "tokens": N,
+                 "perslot_stack_us": round(fz["perslot"], 1),
+                 "dedup_stack_us": round(fz["dedup"], 1),
+                 "perslot_us_per_layer": round(fz["perslot"] / n_layers, 2),
+                 "dedup_us_per_layer": round(fz["dedup"] / n_layers, 2),
+                 "U_mean": round(float(fz["U"].mean()), 2)}
 
-    engines_at_head = None
-    if sweep is not None:
-        rec = next(r for r in sweep if r["n"] == n_head)
-        engines_at_head = {k: rec[k] for k in ("perslot", "dedup")}
-
-    out = {
+    config = {"workload": f"{cfg.name}-shaped MoE layer, one verify pass of n={n_head}"
+                          f" tokens{' x %d sequences' % cfg.n_seq if cfg.n_seq > 1 else ''}"
+                          f", {' and '.join(engines)} engine{'s' if len(engines) > 1 else ''}",
+              "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
+              "shared_experts": cfg.S, "weights": cfg.wdtype, "rho": cfg.rho,
+              "tokens": N, "weight_sets_rotated": n_layers}
+    head = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
@@ -913,48 +1093,82 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.wdtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-shaped MoE layer, one verify pass of n={n_head}"
-                               f" tokens{' x %d sequences' % cfg.n_seq if cfg.n_seq > 1 else ''}"
-                               f", per-slot and dedup engines",
-                   "d_model": cfg.d, "experts": cfg.E, "top_k": cfg.k, "d_ff": cfg.f,
-                   "shared_experts": cfg.S, "weights": cfg.wdtype, "rho": cfg.rho,
-                   "tokens": N, "weight_sets_rotated": n_layers,
-                   "weight_layout": "MFMA-tiled (packed once)"},
-        "engines_at_step_n": engines_at_head,
-        "fused_stack": fused,
-        "step_bytes": int(step_bytes),
-        "roofline": {"bound": "hbm", "kernel": "expert_up (W1/W3 + SwiGLU)",
-                     "achieved": None if achieved is None else round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": None if achieved is None else round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else traffic.get("bytes_per_launch"),
-                     "algorithmic_bytes_per_launch": int(up_bytes / max(1, up_launches)),
-                     "avg_launch_us": round(up_avg_us, 2), "launches": up_launches,
-                     "unit_bytes": up_unit},
-        "up_kernel_ms_total": round(up_ms, 3),
+        "config": config,
+        "roofline": roofline,
     }
+    details = {"headline": head, "kernels": kern, "fused_stack": fused,
+               "step_bytes": int(step_bytes)}
     if sweep is not None:
         ns = [r["n"] for r in sweep]
-        out["sweep"] = sweep
-        out["calibration"] = calibration_json(calib)
-        out["draft_length"] = draft_length_table(sweep)
-        out["crossover"] = {
-            "measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in sweep]),
-            "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_bar"] < r["r"] for r in sweep]),
-            "predicted_model_saving_gt_0": stepmodel.first_n(
-                ns, [r["predicted_saving_us"] > 0 for r in sweep])}
-        out["saving_within_2sd"] = {
-            "line_model": f"{sum(r['saving_within_2sd'] for r in sweep)} of {len(sweep)}",
-            "trace_model": f"{sum(r['trace_saving_within_2sd'] for r in sweep)} of {len(sweep)}"}
+        cross = {"measured": stepmodel.first_n(ns, [r["dedup_faster"] for r in sweep]),
+                 "predicted_u_lt_r": stepmodel.first_n(ns, [r["u_bar"] < r["r"] for r in sweep]),
+                 "predicted_model_saving_gt_0": stepmodel.first_n(
+                     ns, [r["predicted_saving_us"] > 0 for r in sweep])}
+        sens = bandwidth_sensitivity(cfg, calib, sweep)
+        checks = {"within_param_2sd": f"{sum(r['saving_within_param_2sd'] for r in sweep)} of {len(sweep)}",
+                  "within_interval_2sd": f"{sum(r['saving_within_2sd'] for r in sweep)} of {len(sweep)}",
+                  "trace_model_within_interval_2sd":
+                      f"{sum(r['trace_saving_within_2sd'] for r in sweep)} of {len(sweep)}"}
+        head["crossover"] = cross
+        head["bw_error_moves"] = {
+            "crossover_u_lt_r": [sens["cases"][c]["crossover_u_lt_r"]
+                                 for c in ("perslot_favoured", "nominal", "dedup_favoured")],
+            "crossover_model": [sens["cases"][c]["crossover_model_saving"]
+                                for c in ("perslot_favoured", "nominal", "dedup_favoured")],
+            "best_gamma_max_shift": sens["best_gamma_max_shift"]}
+        head["saving_check"] = checks
+        head["sweep"] = compact_sweep(sweep)
+        details.update({"sweep": sweep, "calibration": calibration_json(calib),
+                        "draft_length": draft_length_table(sweep), "crossover": cross,
+                        "saving_check": checks, "bandwidth_sensitivity": sens})
     if not args.no_sweep:
         log("[bench] verification round")
-        out["verify_gate"] = verify_gate_leg()
+        details["verify_gate"] = verify_gate_leg()
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds:.0f} s)")
         del layers, stack
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(cfg, n_head, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+        cb = cpu_baseline(cfg, n_head, args.cpu_seconds)
+        details["cpu_baseline"] = cb
+        head["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                   "us_per_pass")}
+    head["details"] = os.path.relpath(args.details, ROOT) if args.details else None
+    write_details(args.details, details)
+    line = json.dumps(head)
+    if len(line) > 4000 and "sweep" in head:
+        # keep the headline short enough for a log tail: drop r(n) per entry
+        for r in head["sweep"]:
+            r.pop("r", None)
+        line = json.dumps(head)
+    print(line, flush=True)
+
+
+def rho_summary(doc):
+    """Compact record of the routing-overlap sweep: per rho, crossovers,
+    saving-check counts and per n the byte share, per-layer pass times, the
+    measured and predicted saving and the fused stack's per-layer times."""
+    out = {"kind": doc["kind"], "workload": doc["workload"],
+           "calibration": {k: doc["calibration"][k] for k in ("perslot", "dedup_pooled",
+                                                               "perslot_trace", "r_pooled")},
+           "bandwidth_sensitivity": {k: doc["bandwidth_sensitivity"][k]
+                                     for k in ("z", "bw_ps_GBs", "bw_dd_GBs", "best_gamma_max_shift")},
+           "by_rho": []}
+    for rr in doc["by_rho"]:
+        recs = rr["by_n"]
+        out["by_rho"].append({
+            "rho": rr["rho"], "crossover": rr["crossover"],
+            "saving_within_param_2sd": f"{sum(r['saving_within_param_2sd'] for r in recs)} of {len(recs)}",
+            "saving_within_2sd": rr["saving_within_2sd"],
+            "trace_saving_within_2sd": rr["trace_saving_within_2sd"],
+            "by_n": [{"n": r["n"], "u": r["u_bar"], "U": r["U_mean"], "r": r["r"],
+                      "ps_layer_us": r["perslot_layer_us"], "dd_layer_us": r["dedup_layer_us"],
+                      "saving_us": r["saving_us"], "pred_us": r["predicted_saving_us"],
+                      "pred_sd_us": r["predicted_saving_sd_us"],
+                      "interval_sd_us": r["saving_interval_sd_us"],
+                      "trace_pred_us": r["trace_predicted_saving_us"],
+                      "fused_ps_layer_us": r["fused"]["perslot_layer_us"],
+                      "fused_dd_layer_us": r["fused"]["dedup_layer_us"]} for r in recs]})
+    return out
 
 
 if __name__ == "__main__":

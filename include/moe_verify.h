@@ -30,14 +30,15 @@
  *    token count in *workspace_bytes and returns MOE_OK without launching.
  *    Otherwise *workspace_bytes is the size supplied; a smaller size than
  *    needed returns MOE_ERR_WORKSPACE.  A workspace must be 256-byte
- *    aligned and may not be shared by calls that can run concurrently.  The
- *    expert-pass and moe_verify_probs workspaces need no initialisation;
- *    the first 256 bytes of a moe_route, moe_stack_pass or moe_verify_gate
- *    workspace must be zero before its first use, and every such call
- *    leaves them zero again (they count the workgroups that have finished).
- *    The expert passes and moe_verify_probs write data there, so a
- *    workspace they used must have those bytes zeroed again before it
- *    serves one of the other three calls.
+ *    aligned and may not be shared by calls that can run concurrently.
+ *    The first 256 bytes of every workspace (the head) hold arrival
+ *    counters (moe_route, moe_route_biased, moe_stack_pass and
+ *    moe_verify_gate count there the workgroups that have finished): they
+ *    must be zero before the workspace's first use, and every call leaves
+ *    them zero.  No call writes anything else there (data such as the
+ *    compaction record starts at byte 256), so one zero fill of the head
+ *    serves any later sequence of calls, of any kind and size, on the
+ *    same workspace.
  *  - Routing entries passed to the expert passes must lie in [0, E); that
  *    cannot be checked on the host without a copy, so an out-of-range entry
  *    is treated on the device as an empty slot (no weights read, zero
@@ -183,7 +184,8 @@ int moe_expert_pass_perslot(const moe_shape *shape, const moe_expert_weights *we
  * per-slot pass; in addition
  *   n_unique [1] int32 device output (or NULL): U, the number of distinct
  *            valid experts in topk_idx.
- * The workspace begins with the routing-trace compaction, int32 each:
+ * The workspace holds, from byte 256 on, the routing-trace compaction,
+ * int32 each (indices counted from that byte):
  *   [0]                 U
  *   [1 .. E]            counts[e]: slots that chose expert e
  *   [E+1 .. 2E+1]       offs[e]: exclusive prefix sum of counts (E+1 values)
@@ -208,8 +210,8 @@ int moe_expert_pass_dedup(const moe_shape *shape, const moe_expert_weights *weig
  *                N, strictly increasing (else MOE_ERR_INVALID_ARG).  Read
  *                during the call only.
  *   n_unique     [G] int32 device output (or NULL): U_g per group.
- * The workspace begins with G compaction records, record g at byte offset
- * g * R, R = the 256-byte-aligned size of one record (the layout of
+ * The workspace holds, from byte 256 on, G compaction records, record g at
+ * byte offset 256 + g * R, R = the 256-byte-aligned size of one record (the layout of
  * moe_expert_pass_dedup's with N*k list entries, of which group g fills its
  * own slots; list entries are slot ids t*k+j of the whole pass).  G = 1 with
  * group_start = {0, N} is moe_expert_pass_dedup; one token per group
@@ -250,9 +252,9 @@ typedef struct moe_stack_weights {
  *   topk_idx  [L][N][k] int32 device output, topk_w [L][N][k] fp32 output
  *   y         [L][N][d] fp32 device output
  *   n_unique  [L] int32 device output (dedup), or NULL
- * Workspace: route part first (the first 256 bytes must be zero before the
- * first use, as for moe_route, and are left zero), then the expert-pass
- * part; query and errors as for the other calls. */
+ * Workspace: the head (arrival counters, as for every call), the routing
+ * partials, then the expert-pass buffers; query and errors as for the
+ * other calls. */
 int moe_stack_pass(const moe_shape *shape, int32_t n_layers, const moe_stack_weights *weights,
                    const float *x, int32_t n_tokens, int32_t engine, int32_t *topk_idx,
                    float *topk_w, float *y, int32_t *n_unique, void *workspace,
@@ -310,9 +312,7 @@ int moe_pass_bytes_grouped(const moe_shape *shape, const int32_t *topk_idx_host,
  * Limits: 1 <= n_seq <= MOE_MAX_SEQ, 0 <= gamma <= MOE_MAX_DRAFT,
  * 1 <= V <= MOE_MAX_VOCAB.  A draft token outside [0, V) cannot be checked
  * on the host; the device treats it as rejected (never read).  Workspace as
- * for the other calls; its
- * first 256 bytes must be zero before its first use, and every call leaves
- * them zero. */
+ * for the other calls (its head holds one arrival counter per sequence). */
 int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
                     const float *p_verify, const float *q_draft, const int32_t *draft_tokens,
                     const float *u_accept, const uint32_t *r_sample, int32_t *n_accepted,
@@ -334,9 +334,10 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  *          independent of summation order.  probs may not overlap logits.
  * 0 < temperature (finite), 0 < top_p <= 1, 1 <= rows, 1 <= V <=
  * MOE_MAX_VOCAB; violations return MOE_ERR_INVALID_ARG (more than 65535
- * rows: MOE_ERR_UNSUPPORTED).  Workspace as for the other calls, no
- * initialisation needed; with top_p < 1 it holds a candidate list of up to
- * V 8-byte entries per row, so its size is about twice that of the logits.
+ * rows: MOE_ERR_UNSUPPORTED).  Workspace as for the other calls (the head
+ * is not used; after it come per-row statistics, which each call
+ * initialises itself, and a candidate list of up to V 8-byte entries per
+ * row, so its size is about twice that of the logits).
  * Feed the verifier's rows as p_verify and the draft's as q_draft. */
 int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
                      float top_p, float *probs, void *workspace, size_t *workspace_bytes,

@@ -21,14 +21,17 @@
  *  R1  experts are SwiGLU FFNs, W2 (silu(W1 x) . W3 x), no biases; the pages
  *      only write experts[idx](x).
  *  R2  top-k order is (logit descending, expert index ascending); slot 0 is
- *      the largest, as a topk routine returns it.  The comparison is made on
- *      the logits rounded to fp32, the precision the GPU path decides in,
- *      since the pages fix none.  Near-ties (gap < tie_eps) are flagged.
+ *      the largest, as a topk routine returns it.  The pages fix no
+ *      precision, so the order is taken on the logits themselves, here
+ *      their fp64 sums (within a few units of 1e-16 of the exact products'
+ *      sum at these sizes).  Near-ties (gap < tie_eps) are flagged: only
+ *      there can a computation in lower precision order them differently.
  *  R3  the softmax is over the k selected logits (the sketch's comment says
  *      it is renormalised over just the top-k).
  *  R4  bf16 weight configs round the token to bf16 before the experts and the
- *      SwiGLU product to bf16 before W2 (round to nearest, ties to even,
- *      taken on the fp32 value as the GPU path does); fp32 configs round
+ *      SwiGLU product to bf16 before W2: each is one rounding to nearest,
+ *      ties to even, of the value being rounded (the fp32 token; the
+ *      product's fp64 value, with no fp32 step between); fp32 configs round
  *      nothing.
  *  R5  the dense mixture of s1 uses the same softmax gate over all E experts.
  *  R6  the per-expert bias of the DeepSeek-style sketch (s5) is added to the
@@ -73,10 +76,10 @@ float bf16_bits_to_float(uint16_t h) {
   return v;
 }
 
-/* R4: the rounding applied to activations on bf16 configs */
+/* R4: the rounding applied to activations on bf16 configs, one step from v */
 double act_round(const oracle_shape *s, double v) {
   if (s->wdtype == ORACLE_F32) return v;
-  return (double)bf16_bits_to_float(oracle_bf16_rne((float)v));
+  return (double)bf16_bits_to_float(oracle_bf16_rne_f64(v));
 }
 
 double silu(double z) { return z / (1.0 + std::exp(-z)); }
@@ -97,7 +100,7 @@ void expert_mats(const oracle_shape *s, const oracle_weights *wts, int e, bool s
 }
 
 /* R2: does expert a come before expert b in the selection order? */
-bool before(const std::vector<float> &key, int a, int b) {
+bool before(const double *key, int a, int b) {
   if (key[a] != key[b]) return key[a] > key[b];
   return a < b;
 }
@@ -128,8 +131,7 @@ void route_from_logits(const oracle_shape *s, const std::vector<double> &L, int3
 
   for (int t = 0; t < n_tokens; ++t) {
     const double *Lt = &L[(size_t)t * E];
-    std::vector<float> key(E);
-    for (int e = 0; e < E; ++e) key[e] = (float)Lt[e];
+    const double *key = Lt;
 
     /* [MoE] s2: top_k_vals, top_k_idx = topk(logits, k).  Selection by
      * repeated search for the best remaining expert under R2. */
@@ -229,26 +231,39 @@ void evaluate_layer(const oracle_shape *s, const oracle_weights *wts, const floa
 
 extern "C" {
 
+uint16_t oracle_bf16_rne_f64(double x) {
+  const uint16_t sign = std::signbit(x) ? 0x8000u : 0u;
+  if (std::isnan(x)) return (uint16_t)(sign | 0x7FC0u);
+  const double a = std::fabs(x);
+  if (std::isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  if (a == 0.0) return sign;
+  /* bf16 keeps 8 significant bits: in [2^(e-1), 2^e) its values are the
+   * multiples of 2^(e-8), and below 2^-126 the multiples of 2^-133 (its
+   * subnormals).  Scale a to units of that spacing (exact: a power of two),
+   * split off the fraction (exact), and take the nearer multiple, the even
+   * one on a tie. */
+  int e = 0;
+  (void)std::frexp(a, &e);                 /* a = m * 2^e, 1/2 <= m < 1 */
+  const int q = std::max(e - 8, -133);
+  const double units = std::ldexp(a, -q);  /* < 2^8 */
+  const double lo = std::floor(units);
+  const double frac = units - lo;
+  double r = lo;
+  if (frac > 0.5 || (frac == 0.5 && std::fmod(lo, 2.0) != 0.0)) r = lo + 1.0;
+  const double v = std::ldexp(r, q);
+  const double max_bf16 = std::ldexp(255.0, 120);  /* 0x7F7F */
+  if (v > max_bf16) return (uint16_t)(sign | 0x7F80u);
+  const float fv = (float)v;               /* exact: v is a bf16 value */
+  uint32_t bits;
+  std::memcpy(&bits, &fv, 4);
+  return (uint16_t)(sign | (uint16_t)(bits >> 16));
+}
+
 uint16_t oracle_bf16_rne(float x) {
   uint32_t bits;
   std::memcpy(&bits, &x, 4);
   if (std::isnan(x)) return (uint16_t)((bits >> 16) | 0x0040u);
-  /* The two bf16 neighbours of x: truncation toward zero, and one unit of
-   * the last place further from zero.  Choose the nearer; on a tie, the one
-   * whose last mantissa bit is 0. */
-  uint16_t lo = (uint16_t)(bits >> 16);
-  uint16_t hi = (uint16_t)(lo + 1);
-  if ((bits & 0xFFFFu) == 0) return lo;
-  double xv = (double)x;
-  double dlo = std::fabs(xv - (double)bf16_bits_to_float(lo));
-  double dhi = std::fabs((double)bf16_bits_to_float(hi) - xv);
-  if (std::isinf(bf16_bits_to_float(hi)) && !std::isinf(x)) {
-    /* hi overflowed to infinity: it still counts as the value 2^128 */
-    dhi = std::ldexp(1.0, 128) - std::fabs(xv);
-  }
-  if (dlo < dhi) return lo;
-  if (dhi < dlo) return hi;
-  return (lo & 1u) ? hi : lo;
+  return oracle_bf16_rne_f64((double)x);   /* fp32 -> fp64 is exact */
 }
 
 int oracle_gate_logits(const oracle_shape *s, const float *gate_w, const float *x,
@@ -304,8 +319,7 @@ int oracle_expert(const oracle_shape *s, const void *W1, const void *W3, const v
       h += weight_at(s, W1, (size_t)r * d + i) * xt[i];
       g += weight_at(s, W3, (size_t)r * d + i) * xt[i];
     }
-    double prod = silu(h) * g;
-    a[r] = (s->wdtype == ORACLE_BF16) ? act_round(s, (double)(float)prod) : prod;
+    a[r] = act_round(s, silu(h) * g);
   }
   /* out = W2 a */
   for (int c = 0; c < d; ++c) {

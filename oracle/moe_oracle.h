@@ -62,12 +62,17 @@ typedef struct oracle_weights {
  * pattern.  NaN maps to a quiet NaN. */
 uint16_t oracle_bf16_rne(float x);
 
+/* Round an fp64 value to bf16 in one step, nearest with ties to even (no
+ * intermediate fp32 rounding); values at or beyond the overflow midpoint
+ * become infinity.  Returns the 16-bit pattern; NaN maps to a quiet NaN. */
+uint16_t oracle_bf16_rne_f64(double x);
+
 /* Logits L[t][e] = sum_i x[t][i] * gate_w[e][i], fp64, index order. */
 int oracle_gate_logits(const oracle_shape *s, const float *gate_w, const float *x,
                        int32_t n_tokens, double *logits);
 
 /* Top-k + softmax over the k.  idx[t][j]: j-th expert in the order
- * (fp32-rounded logit descending, expert index ascending).  w[t][j] in fp64
+ * (fp64 logit descending, expert index ascending).  w[t][j] in fp64
  * from the fp64 logits.  margin[t] = L_(k) - L_(k+1) (+inf if k == E).
  * flags[t] per ORACLE_FLAG_*.  logits/margin/flags may be NULL. */
 int oracle_route(const oracle_shape *s, const float *gate_w, const float *x,

@@ -55,6 +55,8 @@ def load():
         i32 = C.c_int32
         lib.oracle_bf16_rne.argtypes = [C.c_float]
         lib.oracle_bf16_rne.restype = C.c_uint16
+        lib.oracle_bf16_rne_f64.argtypes = [C.c_double]
+        lib.oracle_bf16_rne_f64.restype = C.c_uint16
         lib.oracle_gate_logits.argtypes = [P, P, P, i32, P]
         lib.oracle_route.argtypes = [P, P, P, i32, C.c_double, P, P, P, P, P]
         lib.oracle_route_biased.argtypes = [P, P, P, P, i32, C.c_double, P, P, P, P, P]
@@ -114,6 +116,19 @@ def bf16_rne(x):
     of = out.reshape(-1)
     for i in range(flat.size):
         of[i] = lib.oracle_bf16_rne(float(flat[i]))
+    return out
+
+
+def bf16_rne_f64(x):
+    """bf16 bit patterns of fp64 values rounded in one step, nearest-even
+    (elementwise, slow)."""
+    lib = load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat = x.reshape(-1)
+    of = out.reshape(-1)
+    for i in range(flat.size):
+        of[i] = lib.oracle_bf16_rne_f64(float(flat[i]))
     return out
 
 

@@ -141,25 +141,18 @@ class Workspace:
     """A grow-only device byte buffer reused across calls (256-byte aligned,
     zero-filled when allocated).
 
-    Routing, the stack pass and the verification round keep arrival
-    counters in the first 256 bytes: zero before the call, zero after.  The
-    expert passes and the logits filter write data there (the compaction
-    record, the filter's statistics).  get() is told which kind of call
-    comes next and zeroes the head, with one small fill on the current
-    stream, when the call before it was of the other kind."""
+    The library keeps arrival counters in the first 256 bytes of every
+    workspace and returns them to zero after each call; no call writes
+    anything else there.  The zero fill at allocation is therefore the
+    only initialisation any sequence of calls needs."""
 
     def __init__(self, device="cuda"):
         self.device = device
         self.buf = None
-        self.head_zero = True
 
-    def get(self, nbytes, counters=False):
+    def get(self, nbytes):
         if self.buf is None or self.buf.numel() < nbytes:
             self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
-            self.head_zero = True
-        if counters and not self.head_zero:
-            self.buf[:256].zero_()
-        self.head_zero = counters
         return self.buf
 
 
@@ -211,7 +204,7 @@ def route(shape, gate_w, x, *, bias=None, idx=None, w=None, logits=None, margin=
         C.byref(shape), _ptr(gate_w), _ptr(x), n, None, _ptr(idx), _ptr(w), None, None, nb,
         None))
     ws = ws or Workspace(x.device)
-    buf = ws.get(need, counters=True)
+    buf = ws.get(need)
     have = C.c_size_t(buf.numel())
     _check("moe_route_biased", lib.moe_route_biased(
         C.byref(shape), _ptr(gate_w), _ptr(bias), _ptr(x), n, _ptr(logits), _ptr(idx), _ptr(w),
@@ -282,14 +275,7 @@ def expert_pass_dedup_grouped(shape, weights, x, idx, w, group_start, *, y=None,
                         n_unique=n_unique, groups=gs)
 
 
-def stack_pass(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=None, ws=None):
-    """One pass of the same tokens x through every layer of a stack, fused
-    (moe_stack_pass).  stack: dict with gate_w fp32 [L][E][d], optional bias
-    fp32 [L][E], w13 [L][E][2][f][d], w2 [L][E][d][f] (ws13 / ws2 [L][S]...
-    with shared experts) and layout.  engine: "perslot" or "dedup".
-    Returns (idx int32 [L][N][k], w fp32 [L][N][k], y fp32 [L][N][d]);
-    n_unique (int32 [L] on the GPU) receives U per layer."""
-    lib = load()
+def _stack_args(shape, stack, x, engine, idx, w, y, n_unique):
     eng = {"perslot": ENGINE_PERSLOT, "dedup": ENGINE_DEDUP}[engine]
     wdt = torch.bfloat16 if shape.wdtype == MOE_BF16 else torch.float32
     gate_w = _dev(stack["gate_w"], torch.float32, "gate_w")
@@ -313,12 +299,24 @@ def stack_pass(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=No
     y = torch.empty((L, n, shape.d_model), dtype=torch.float32, device=dev) if y is None else y
     _dev(idx, torch.int32, "idx"), _dev(w, torch.float32, "w"), _dev(y, torch.float32, "y")
     _dev(n_unique, torch.int32, "n_unique")
+    return keep, cw, eng, L, x, n, idx, w, y
+
+
+def stack_pass(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=None, ws=None):
+    """One pass of the same tokens x through every layer of a stack, fused
+    (moe_stack_pass).  stack: dict with gate_w fp32 [L][E][d], optional bias
+    fp32 [L][E], w13 [L][E][2][f][d], w2 [L][E][d][f] (ws13 / ws2 [L][S]...
+    with shared experts) and layout.  engine: "perslot" or "dedup".
+    Returns (idx int32 [L][N][k], w fp32 [L][N][k], y fp32 [L][N][d]);
+    n_unique (int32 [L] on the GPU) receives U per layer."""
+    lib = load()
+    keep, cw, eng, L, x, n, idx, w, y = _stack_args(shape, stack, x, engine, idx, w, y, n_unique)
     key = ("moe_stack_pass", L, eng)
     need = _need(key, shape, n, lambda nb: lib.moe_stack_pass(
         C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y), None,
         None, nb, None))
-    ws = ws or Workspace(dev)
-    buf = ws.get(need, counters=True)
+    ws = ws or Workspace(x.device)
+    buf = ws.get(need)
     have = C.c_size_t(buf.numel())
     _check("moe_stack_pass", lib.moe_stack_pass(
         C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y),
@@ -395,7 +393,7 @@ def verify_gate(p, x, *, q=None, u=None, r=None, mode=VERIFY_SAMPLING, n_accepte
                                                       _ptr(out), None, C.byref(nb), None))
         _NEED[key] = nb.value
     ws = ws or Workspace(p.device)
-    buf = ws.get(_NEED[key], counters=True)
+    buf = ws.get(_NEED[key])
     have = C.c_size_t(buf.numel())
     _check("moe_verify_gate", lib.moe_verify_gate(S, gamma, V, mode, _ptr(p), _ptr(q), _ptr(x),
                                                   _ptr(u), _ptr(r), _ptr(n_accepted), _ptr(out),

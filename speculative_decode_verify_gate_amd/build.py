@@ -46,7 +46,7 @@ def build(verbose: bool = False, defines=(), out=LIB) -> str:
     """Compile and link; `defines` are extra -D macros, `out` the library path."""
     build_dir = BUILD if out == LIB else out + ".objs"
     os.makedirs(build_dir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), SOURCES))
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out + ".tmp"]
     if verbose:

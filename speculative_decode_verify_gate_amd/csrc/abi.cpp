@@ -17,6 +17,10 @@ namespace {
 using moe::align_up;
 
 constexpr size_t kAlign = 256;
+// The first kHead bytes of every workspace belong to arrival counters
+// (routing, stack pass, verification round); no call writes data there, so
+// one zero fill before a workspace's first use serves any sequence of calls.
+constexpr size_t kHead = 256;
 
 int check_shape(const moe_shape *s) {
   if (!s) return MOE_ERR_INVALID_ARG;
@@ -47,11 +51,10 @@ size_t entry_rows(const moe_shape *s, int n) {
   return (size_t)n * s->top_k + (size_t)s->n_shared * n;
 }
 
-// [arrival counter | partial logits [splits][N][E]]
-// [arrival counters (one per layer, in 256 bytes) | partial logits
+// [arrival counters (one per layer, in the head) | partial logits
 //  [L][splits][N][E]]
 size_t route_ws(const moe_shape *s, int n, int L = 1) {
-  return kAlign + align_up((size_t)L * moe::gate_splits(s->d_model) * n * s->n_experts *
+  return kHead + align_up((size_t)L * moe::gate_splits(s->d_model) * n * s->n_experts *
                                sizeof(float), kAlign);
 }
 
@@ -151,8 +154,8 @@ int check_weights(const moe_shape *s, const moe_expert_weights *w) {
   return MOE_OK;
 }
 
-// Expert-pass workspace: [G * L compaction records (dedup) | abuf of every
-// layer | obuf of every layer].
+// Expert-pass workspace after the head: [G * L compaction records (dedup) |
+// abuf of every layer | obuf of every layer].
 size_t expert_ws(const moe_shape *s, int n, int G, int L, bool dedup) {
   return (dedup ? (size_t)G * L * cmp_ws(s, n) : 0) + (size_t)L * abuf_ws(s, n) +
          (size_t)L * obuf_ws(s, n);
@@ -257,12 +260,13 @@ int expert_pass(const moe_shape *s, const moe_expert_weights *w, const float *x,
   if ((rc = check_groups(n, G, gs)) != MOE_OK) return rc;
   if (!x || !idx || !tw || !y) return MOE_ERR_INVALID_ARG;
   bool launch;
-  if ((rc = workspace_gate(ws, ws_bytes, expert_ws(s, n, G, 1, dedup), &launch)) != MOE_OK ||
+  if ((rc = workspace_gate(ws, ws_bytes, kHead + expert_ws(s, n, G, 1, dedup), &launch)) !=
+          MOE_OK ||
       !launch)
     return rc;
   const LayerWeights lw{w->w13, w->w2, w->ws13, w->ws2, w->layout};
-  return launch_pass(s, lw, 1, x, n, G, gs, idx, tw, y, n_unique, dedup, ws,
-                     (hipStream_t)stream);
+  return launch_pass(s, lw, 1, x, n, G, gs, idx, tw, y, n_unique, dedup,
+                     (unsigned char *)ws + kHead, (hipStream_t)stream);
 }
 
 // Gate + top-k + softmax for L layers (gate_w [L][E][d], bias [L][E] or
@@ -282,7 +286,7 @@ int launch_route(const moe_shape *s, int L, const float *gate_w, const float *bi
   a.L = L;
   a.splits = moe::gate_splits(s->d_model);
   a.done = (unsigned *)ws;
-  a.part = (float *)((unsigned char *)ws + kAlign);
+  a.part = (float *)((unsigned char *)ws + kHead);
   a.logits = logits;
   a.idx = idx;
   a.w = tw;
@@ -358,7 +362,7 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
   if (mode == MOE_VERIFY_SAMPLING && (!r_sample || (gamma > 0 && (!q_draft || !u_accept))))
     return MOE_ERR_INVALID_ARG;
   // [arrival counters | partial results [n_seq][chunks][gamma + 1] uint64]
-  const size_t need = kAlign + align_up((size_t)n_seq * moe::verify_chunks(vocab) *
+  const size_t need = kHead + align_up((size_t)n_seq * moe::verify_chunks(vocab) *
                                             (size_t)(gamma + 1) * sizeof(uint64_t),
                                         kAlign);
   bool launch;
@@ -385,12 +389,14 @@ int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float tem
   if (rows > 65535) return MOE_ERR_UNSUPPORTED;  // rows are a grid dimension
   bool launch;
   int rc;
-  if ((rc = workspace_gate(ws, ws_bytes, moe::filter_ws_bytes(rows, vocab), &launch)) != MOE_OK ||
+  if ((rc = workspace_gate(ws, ws_bytes, kHead + moe::filter_ws_bytes(rows, vocab), &launch)) !=
+          MOE_OK ||
       !launch)
     return rc;
   hipStream_t st = (hipStream_t)stream;
   const hipError_t err = timed(MOE_K_FILTER, st, [&] {
-    return moe::launch_filter(rows, vocab, logits, temperature, top_p, probs, ws, st);
+    return moe::launch_filter(rows, vocab, logits, temperature, top_p, probs,
+                              (unsigned char *)ws + kHead, st);
   });
   return status_of(err);
 }

@@ -86,7 +86,6 @@ __device__ inline u32x4 ldg16_once(const unsigned char *p) {
   return __builtin_nontemporal_load((const u32x4 *)p);
 }
 
-constexpr int kSpc = 4;                           // MFMA steps per chunk
 constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 
 // With 16-token tiles (CTMAX == 1) the B operand is not staged in LDS: every
@@ -561,15 +560,18 @@ hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // allow more than the default 64 KB of dynamic LDS, once per kernel
+  // the dynamic-LDS limit of each kernel, once per kernel: the most any
+  // shape asks of it (the wide tiles may exceed the default 64 KB)
   static const hipError_t set_wide = hipFuncSetAttribute(
       (const void *)expert_kernel<BF16, UP, 4, TILED, VAR>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+      hipFuncAttributeMaxDynamicSharedMemorySize, expert_lds_bound(true));
   static const hipError_t set_narrow = hipFuncSetAttribute(
       (const void *)expert_kernel<BF16, UP, 1, TILED, VAR>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
+      hipFuncAttributeMaxDynamicSharedMemorySize, expert_lds_bound(false));
   if (set_wide != hipSuccess) return set_wide;
   if (set_narrow != hipSuccess) return set_narrow;
+  if (a.lds_bytes < 0 || a.lds_bytes > expert_lds_bound(a.N > kTile))
+    return hipErrorInvalidValue;
   if (a.N > kTile)
     hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED, VAR>), dim3((unsigned)blocks),
                        dim3(kBlock), a.lds_bytes, st, a);
@@ -666,35 +668,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 }  // namespace
-
-int expert_lds_bytes(int N, int K, bool bf16, bool up, int E) {
-  const int eb = bf16 ? 2 : 4;
-  const int ctmax = N > kTile ? 4 : 1;
-  // the partial sums of 16-token tiles, or, in workgroup 0 of the up kernel,
-  // the compaction scratch: 2E+1 counts and offsets and one int per slot
-  if (ctmax == 1) {
-    const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * kWave * 16;
-    const size_t record = up ? (size_t)(2 * E + 1 + MOE_MAX_SLOTS) * sizeof(int) : 0;
-    return (int)(partials > record ? partials : record);
-  }
-  const int step = bf16 ? 32 : 16;
-  const int chunk = kSpc * step;
-  const int rows = ctmax * kTile;
-  const int kpad = (K + kWavesPerBlock * chunk - 1) / (kWavesPerBlock * chunk) *
-                   (kWavesPerBlock * chunk);
-  // the whole K for as many token rows as an instance can have (at most N
-  // unless a caller's routing repeats an expert within a token)
-  const int rows_n = N < rows ? N : rows;
-  const size_t whole = (size_t)rows_n * (kpad + kLdsPad) * eb;
-  // at least one chunk per wave for a full token group, and room for the
-  // waves' partial sums
-  const size_t least = (size_t)rows * (kWavesPerBlock * chunk + kLdsPad) * eb;
-  const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * ctmax * kWave * 16;
-  size_t bytes = whole < (size_t)kLdsBudget ? whole : (size_t)kLdsBudget;
-  if (bytes < least) bytes = least;
-  if (bytes < partials) bytes = partials;
-  return (int)bytes;
-}
 
 hipError_t launch_up(const ExpertArgs &a, bool bf16, hipStream_t st) {
   return bf16 ? launch_expert<true, true>(a, st) : launch_expert<false, true>(a, st);

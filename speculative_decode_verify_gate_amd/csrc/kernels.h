@@ -16,9 +16,12 @@ constexpr int kTile = 16;               // MFMA output tile is 16 rows x 16 toke
 constexpr int kWavesPerBlock = 4;       // expert kernels: waves per 16-row tile
 
 constexpr int kGateKPerBlock = 256;     // gate logits: K elements per workgroup
-constexpr int kLdsBudget = 36 * 1024;   // bytes of staged activations per workgroup
-                                        // (four workgroups fit the 160 KB of a CU)
+constexpr int kLdsBudget = 36 * 1024;   // staged activations per workgroup, when a
+                                        // token group's K window fits it (four
+                                        // workgroups per CU); wider windows take
+                                        // up to expert_lds_bound(true)
 constexpr int kLdsPad = 8;              // elements of padding per staged row
+constexpr int kSpc = 4;                 // expert kernels: MFMA steps per K chunk
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -94,8 +97,20 @@ struct RouteArgs {
   float *margin;              // [L][N] or nullptr
 };
 
-int gate_splits(int d);
-bool route_fused(int N, int d, int E);
+// Row length of a token's logits in the router's LDS: E rounded up to whole
+// 16-byte vectors.
+__host__ __device__ inline int logit_ld(int E) { return (E + 3) & ~3; }
+constexpr int kFusedRouteLds = 32 * 1024;  // one-launch routing: [N][E] logits in LDS
+
+inline int gate_splits(int d) { return (d + kGateKPerBlock - 1) / kGateKPerBlock; }
+
+// One launch routes the pass when the partials that its last workgroup sums
+// and that workgroup's LDS copy of the logits are small enough.
+inline bool route_fused(int N, int d, int E) {
+  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes &&
+         (size_t)N * logit_ld(E) * sizeof(float) <= (size_t)kFusedRouteLds;
+}
+
 hipError_t launch_gate(const RouteArgs &a, hipStream_t st);
 hipError_t launch_topk(const RouteArgs &a, hipStream_t st);
 
@@ -112,6 +127,45 @@ hipError_t launch_pack(const void *src, void *dst, int R, int K, long long n_mat
 // Dynamic LDS for the expert kernels at this token count: the partial sums
 // (16-token tiles, which read their token columns directly), or K windows of
 // up to min(N, 64) staged token rows.
-int expert_lds_bytes(int N, int K, bool bf16, bool up, int E);
+inline int expert_lds_bytes(int N, int K, bool bf16, bool up, int E) {
+  const int eb = bf16 ? 2 : 4;
+  const int ctmax = N > kTile ? 4 : 1;
+  // the partial sums of 16-token tiles, or, in workgroup 0 of the up kernel,
+  // the compaction scratch: 2E+1 counts and offsets and one int per slot
+  if (ctmax == 1) {
+    const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * kWave * 16;
+    const size_t record = up ? (size_t)(2 * E + 1 + MOE_MAX_SLOTS) * sizeof(int) : 0;
+    return (int)(partials > record ? partials : record);
+  }
+  const int step = bf16 ? 32 : 16;
+  const int chunk = kSpc * step;
+  const int rows = ctmax * kTile;
+  const int kpad = (K + kWavesPerBlock * chunk - 1) / (kWavesPerBlock * chunk) *
+                   (kWavesPerBlock * chunk);
+  // the whole K for as many token rows as an instance can have (at most N
+  // unless a caller's routing repeats an expert within a token)
+  const int rows_n = N < rows ? N : rows;
+  const size_t whole = (size_t)rows_n * (kpad + kLdsPad) * eb;
+  // at least one chunk per wave for a full token group, and room for the
+  // waves' partial sums
+  const size_t least = (size_t)rows * (kWavesPerBlock * chunk + kLdsPad) * eb;
+  const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * ctmax * kWave * 16;
+  size_t bytes = whole < (size_t)kLdsBudget ? whole : (size_t)kLdsBudget;
+  if (bytes < least) bytes = least;
+  if (bytes < partials) bytes = partials;
+  return (int)bytes;
+}
+
+// The most expert_lds_bytes() can ask for, over every shape: 16-token tiles
+// (wide = false) or the LDS-staged wide tiles (wide = true).  The kernels'
+// dynamic-LDS limit is set to it, and every launch is checked against it.
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int expert_lds_bound(bool wide) {
+  return wide ? cmax(cmax(kLdsBudget, 4 * kTile * (kWavesPerBlock * kSpc * 32 + kLdsPad) * 2),
+                     cmax(4 * kTile * (kWavesPerBlock * kSpc * 16 + kLdsPad) * 4,
+                          2 * kWavesPerBlock * 4 * kWave * 16))
+              : cmax(2 * kWavesPerBlock * kWave * 16,
+                     (2 * MOE_MAX_EXPERTS + 1 + MOE_MAX_SLOTS) * (int)sizeof(int));
+}
 
 }  // namespace moe

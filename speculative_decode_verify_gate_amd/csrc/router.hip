@@ -33,7 +33,6 @@ constexpr int kGateWaves = 4;
 constexpr int kGateKPerWave = kGateKPerBlock / kGateWaves;  // 64 = 4 steps of 16
 constexpr int kMaxColTiles = 4;                              // N <= 64
 constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
-constexpr int kFusedRouteLds = 32 * 1024;  // one-launch routing: [N][E] logits in LDS
 constexpr int kFusedGateThreads = 256;     // one-launch routing: threads per workgroup
 // gate workgroup LDS shared by the wave sums and the routing's partial ranks
 constexpr int kGateScratch =
@@ -41,12 +40,10 @@ constexpr int kGateScratch =
         ? kGateWaves * kMaxColTiles * 64 * 16
         : (kFusedGateThreads / 64) * MOE_MAX_EXPERTS * 4;
 
-
-// Row length of a token's logits in LDS: E rounded up to whole 16-byte
-// vectors.  The padding holds -inf at indices >= E, which never ranks ahead
-// of a real expert: it is not greater than any logit, and on equality with
-// a -inf logit the lower (real) index wins.
-__host__ __device__ inline int logit_ld(int E) { return (E + 3) & ~3; }
+// Logits sit in LDS at logit_ld(E) per token.  The padding holds -inf at
+// indices >= E, which never ranks ahead of a real expert: it is not greater
+// than any logit, and on equality with a -inf logit the lower (real) index
+// wins.
 
 // Order key of expert e with logit v: order-preserving bits of v (with -0
 // taken as +0) above the complemented index, so keys compare like (logit
@@ -405,14 +402,6 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
 }
 
 }  // namespace
-
-int gate_splits(int d) { return (d + kGateKPerBlock - 1) / kGateKPerBlock; }
-
-bool route_fused(int N, int d, int E) {
-  // the partials that one workgroup sums, and its LDS copy of the logits
-  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes &&
-         (size_t)N * logit_ld(E) * sizeof(float) <= (size_t)kFusedRouteLds;
-}
 
 hipError_t launch_gate(const RouteArgs &a, hipStream_t st) {
   const int n_et = (a.E + kTile - 1) / kTile;

@@ -160,6 +160,13 @@ def saving_interval_sd(fit_ps: LineFit, fit_dd: LineFit, b_ps, b_dd):
     return math.sqrt(sd ** 2 + fit_ps.resid_sd ** 2 + fit_dd.resid_sd ** 2)
 
 
+def with_bandwidth(fit: LineFit, bw_GBs):
+    """The same line with its bandwidth replaced (slope = 1 / BW), fixed time
+    and covariance kept: the model under a bandwidth error."""
+    return LineFit(slope=1e-3 / float(bw_GBs), t0=fit.t0, cov=fit.cov, resid_sd=fit.resid_sd,
+                   n_points=fit.n_points)
+
+
 def first_n(ns, flags):
     """Smallest n whose flag holds, or "never"."""
     for n, f in zip(ns, flags):

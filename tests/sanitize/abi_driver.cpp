@@ -25,11 +25,6 @@ static int g_fail = 0;
 namespace moe {
 static int g_launches = 0;
 
-int gate_splits(int d) { return (d + kGateKPerBlock - 1) / kGateKPerBlock; }
-bool route_fused(int N, int d, int E) {
-  return (size_t)gate_splits(d) * N * E * sizeof(float) <= (size_t)kFusedRouteBytes;
-}
-int expert_lds_bytes(int, int, bool, bool, int) { return 0; }
 int verify_chunks(int V) { return (V + 2047) / 2048; }
 
 hipError_t launch_gate(const RouteArgs &a, hipStream_t) {
@@ -38,8 +33,10 @@ hipError_t launch_gate(const RouteArgs &a, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
+static int g_topk_launches = 0;
 hipError_t launch_topk(const RouteArgs &a, hipStream_t) {
   CHECK(!route_fused(a.N, a.d, a.E));
+  ++g_topk_launches;
   ++g_launches;
   return hipSuccess;
 }
@@ -56,6 +53,8 @@ static void check_expert(const ExpertArgs &a) {
   CHECK(a.L == 1 || a.G == 1);
   CHECK((a.cmp != nullptr) == (a.dedup != 0) && a.abuf && a.obuf && a.y && a.x);
   CHECK((size_t)a.rec_ints * 4 % 256 == 0 && a.rec_ints >= 2 + 3 * a.E + a.N * a.k);
+  // the dynamic LDS the launch asks for is within the limit set on the kernel
+  CHECK(a.lds_bytes > 0 && a.lds_bytes <= expert_lds_bound(a.N > kTile));
   // grid slots per token group: the group's instances, or half of them
   // rounded up where its dedup grid folds (E >= 8k, half >= 2k)
   CHECK(a.fbase[0] == 0);
@@ -107,9 +106,14 @@ struct Buf {  // 256-byte aligned host buffer standing in for a workspace
 };
 
 int main() {
+  // the workloads' shapes, and a narrow gate with many experts whose routing
+  // takes one launch at small N and two at N = 64 (the partials fit 64 KB,
+  // the LDS copy of the logits does not)
   const moe_shape shapes[] = {{256, 8, 2, 512, 0, MOE_F32}, {2048, 64, 6, 1408, 2, MOE_BF16},
-                              {7168, 256, 8, 2048, 1, MOE_BF16}, {4096, 8, 2, 14336, 0, MOE_BF16}};
+                              {7168, 256, 8, 2048, 1, MOE_BF16}, {4096, 8, 2, 14336, 0, MOE_BF16},
+                              {256, 256, 8, 512, 0, MOE_BF16}};
   for (const moe_shape &s : shapes) {
+    const int topk_before = moe::g_topk_launches;
     const moe_expert_weights w{fake(), fake(), s.n_shared ? fake() : nullptr,
                                s.n_shared ? fake() : nullptr, MOE_LAYOUT_TILED};
     for (int n : {1, 3, 16, 17, 64}) {
@@ -182,6 +186,11 @@ int main() {
       int32_t Ug = 0;
       CHECK(moe_pass_bytes_grouped(&s, idx.data(), n, 1, whole, &dg, &Ug) == MOE_OK);
       CHECK(dg == dd && Ug == U && U <= n * s.top_k && (uint64_t)U * 3 * s.d_model * s.d_ff <= dd);
+    }
+    // the narrow many-expert gate routes N = 64 in two launches, N = 1 in one
+    if (s.d_model == 256 && s.n_experts == 256) {
+      CHECK(moe::g_topk_launches > topk_before);
+      CHECK(moe::route_fused(1, 256, 256) && !moe::route_fused(64, 256, 256));
     }
   }
   // rejected arguments

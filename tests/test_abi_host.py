@@ -241,8 +241,9 @@ def test_stack_pass_validation_and_workspace():
     lib = B.load()
     rc, need3 = _stack(s, L=3, n=16, engine=1)
     assert rc == 0
-    # route part (256 bytes of counters + L layers of partials) + expert part
-    # (L compaction records, activation and output rows)
+    # the head (256 bytes of counters), L layers of routing partials, then
+    # the expert part (L compaction records, activation and output rows); a
+    # single-layer expert pass has the same head in front of its part
     r1 = C.c_size_t(0)
     assert lib.moe_route(C.byref(s), FAKE, FAKE, 16, None, FAKE, FAKE, None, None,
                          C.byref(r1), None) == 0
@@ -251,7 +252,7 @@ def test_stack_pass_validation_and_workspace():
     assert lib.moe_expert_pass_dedup(C.byref(s), C.byref(cw), FAKE, 16, FAKE, FAKE, FAKE, None,
                                      None, C.byref(e1), None) == 0
     parts = (r1.value - 256)
-    assert need3 == 256 + 3 * parts + 3 * e1.value
+    assert need3 == 256 + 3 * parts + 3 * (e1.value - 256)
     rc, need_ps = _stack(s, L=3, n=16, engine=0)
     assert rc == 0 and need_ps < need3          # no compaction records
     for kw in (dict(L=0), dict(L=65), dict(engine=2), dict(w=False), dict(gate=None),
@@ -281,18 +282,43 @@ def test_verify_probs_validation():
                                 C.byref(nb), None) == -2
 
 
-def test_workspace_head_is_zero_for_counter_calls():
-    """A binding Workspace shared by calls of both kinds: the head that an
-    expert pass or the filter wrote is zeroed before a call that keeps
-    arrival counters there, and left alone otherwise."""
+def test_binding_workspace_is_zero_filled_and_grow_only():
+    """The binding's Workspace needs no bookkeeping between calls: the head
+    that holds arrival counters is zero at allocation and every call leaves
+    it zero.  It grows (zero-filled again) and never shrinks."""
     ws = B.Workspace("cpu")
-    buf = ws.get(1024)                       # an expert pass or the filter
-    buf[:512] = 7                            # ... writes its data at the head
-    assert int(ws.get(1024)[:256].sum()) == 256 * 7     # data call: untouched
-    buf = ws.get(1024, counters=True)        # routing, stack pass, verify round
-    assert int(buf[:256].sum()) == 0 and int(buf[256:512].sum()) == 256 * 7
-    buf[:256] = 0                            # a counter call leaves it zero
-    buf[300] = 9
-    assert int(ws.get(1024, counters=True)[300]) == 9  # no fill needed
-    grown = ws.get(4096)                     # growing reallocates, zero-filled
+    buf = ws.get(1024)
+    assert buf.numel() == 1024 and int(buf.sum()) == 0
+    buf[300] = 9                              # data beyond the head survives
+    assert int(ws.get(512)[300]) == 9 and ws.get(512).numel() == 1024
+    grown = ws.get(4096)
     assert grown.numel() == 4096 and int(grown.sum()) == 0
+
+
+def test_every_workspace_reserves_the_counter_head():
+    """Every device call's workspace starts with the 256-byte counter head:
+    the expert passes, the grouped pass and the filter, which keep no
+    counters, still ask for it and place their data after it."""
+    lib = B.load()
+    s = B.make_shape(512, 64, 6, 352, 2, "bf16")
+    nb = C.c_size_t(0)
+    n, k, E, f, d, S = 16, 6, 64, 352, 512, 2
+    rec = ((3 * E + 2 + n * k) * 4 + 255) // 256 * 256
+    rows = n * k + S * n
+    a = (rows * f * 2 + 255) // 256 * 256
+    o = (rows * d * 4 + 255) // 256 * 256
+    W = B.Weights(0x100000, 0x200000, 0x300000, 0x400000, 0)
+    assert lib.moe_expert_pass_dedup(C.byref(s), C.byref(W), FAKE, n, FAKE, FAKE, FAKE, None,
+                                     None, C.byref(nb), None) == 0
+    assert nb.value == 256 + rec + a + o
+    assert lib.moe_expert_pass_perslot(C.byref(s), C.byref(W), FAKE, n, FAKE, FAKE, FAKE, None,
+                                       C.byref(nb), None) == 0
+    assert nb.value == 256 + a + o
+    gs = (C.c_int32 * 3)(0, 5, 16)
+    assert lib.moe_expert_pass_dedup_grouped(C.byref(s), C.byref(W), FAKE, n, 2, gs, FAKE, FAKE,
+                                             FAKE, None, None, C.byref(nb), None) == 0
+    assert nb.value == 256 + 2 * rec + a + o
+    assert lib.moe_verify_probs(2, 1000, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None,
+                                C.byref(nb), None) == 0
+    assert nb.value >= 256 + 2 * 1000 * 8
+

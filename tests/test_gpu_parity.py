@@ -131,9 +131,11 @@ def test_small_layer_parity(case, n):
     err = rel_err(y_ps.cpu().numpy(), y_ref)
     _say(f"   rel err {err:.3e}  U={U}  flagged={flagged}")
     assert err <= OUT_RTOL[wdt]
-    # the compaction record at the head of the dedup workspace
+    # the compaction record, from byte 256 of the dedup workspace (the
+    # head belongs to arrival counters and stays zero)
     c = O.compact(oshape(cfg), ref["idx"])
-    rec = ws.buf[: 4 * (3 * E + 2 + n * k)].view(torch.int32).cpu().numpy()
+    assert int(ws.buf[:256].count_nonzero()) == 0
+    rec = ws.buf[256: 256 + 4 * (3 * E + 2 + n * k)].view(torch.int32).cpu().numpy()
     assert rec[0] == c["n_unique"]
     assert np.array_equal(rec[1:1 + E], c["counts"])
     assert np.array_equal(rec[1 + E:2 + 2 * E], c["offs"])
@@ -269,32 +271,64 @@ def test_dedup_around_the_folded_grid(n, wdt):
 
 
 def test_one_workspace_shared_by_every_kind_of_call():
-    """The binding zeroes the workspace head that a dedup pass or the filter
-    wrote (compaction record, filter statistics) before routing, the stack
-    pass or a verification round uses it for arrival counters: each call on
-    the shared workspace equals the same call on a fresh one."""
+    """One workspace, zeroed once at allocation and never again, serves every
+    kind of call in any order and size (routing, the three expert passes,
+    the stack pass, the filter and both verification modes): each call on
+    the shared workspace equals the same call on a fresh one, and the head
+    (arrival counters) is zero after every call."""
     cfg = small_config("shared-ws", 512, 64, 6, 352, 2, "bf16")
     lay = synth.make_layer(cfg, "cpu")
     lay_dev = to_dev(lay)
     shape = B.shape_of(cfg)
+    L = 3
+    stack = {k: (None if v is None else torch.stack([v] * L).contiguous())
+             for k, v in lay_dev.items()}
+    stack["layout"] = "rows"
     ws = B.Workspace()
     rng = np.random.default_rng(5)
-    for rep, n in enumerate([16, 3, 9]):
+
+    def head_zero():
+        torch.cuda.synchronize()
+        return int(ws.buf[:256].count_nonzero()) == 0
+
+    for rep, n in enumerate([16, 3, 9, 1, 24]):
         x = synth.make_hidden(cfg, n, rep, "cuda")
         idx_f, w_f = B.route(shape, lay_dev["gate_w"], x)
         y_f = B.expert_pass_dedup(shape, lay_dev, x, idx_f, w_f)
         y_s = B.expert_pass_dedup(shape, lay_dev, x, idx_f, w_f, ws=ws)
+        assert head_zero()
         idx_s, w_s = B.route(shape, lay_dev["gate_w"], x, ws=ws)
-        lg = torch.from_numpy(rng.standard_normal((2, 3, 3000)).astype(np.float32)).cuda()
+        assert head_zero()
+        gs = [0, n // 2, n] if n > 1 else [0, 1]
+        yg_f = B.expert_pass_dedup_grouped(shape, lay_dev, x, idx_f, w_f, gs)
+        yg_s = B.expert_pass_dedup_grouped(shape, lay_dev, x, idx_f, w_f, gs, ws=ws)
+        assert head_zero()
+        yp_f = B.expert_pass_perslot(shape, lay_dev, x, idx_f, w_f)
+        yp_s = B.expert_pass_perslot(shape, lay_dev, x, idx_f, w_f, ws=ws)
+        assert head_zero()
+        sk_f = B.stack_pass(shape, stack, x, "dedup")
+        sk_s = B.stack_pass(shape, stack, x, "dedup", ws=ws)
+        assert head_zero()
+        lg = torch.from_numpy(rng.standard_normal((2, 3, 3000 + 7 * rep)).astype(np.float32)).cuda()
         p_f = B.verify_probs(lg, 0.8, 0.9)
         p_s = B.verify_probs(lg, 0.8, 0.9, ws=ws)
+        assert head_zero()
         xt = p_f[:, :2].argmax(dim=2).to(torch.int32)
         n_f, t_f = B.verify_gate(p_f, xt, mode=B.VERIFY_GREEDY)
         n_s, t_s = B.verify_gate(p_s, xt, mode=B.VERIFY_GREEDY, ws=ws)
+        assert head_zero()
+        u = torch.from_numpy(rng.random((2, 2)).astype(np.float32)).cuda()
+        r = torch.from_numpy(rng.integers(-2**31, 2**31 - 1, 2).astype(np.int32)).cuda()
+        q = p_f[:, :2].contiguous()
+        m_f, o_f = B.verify_gate(p_f, xt, q=q, u=u, r=r, mode=B.VERIFY_SAMPLING)
+        m_s, o_s = B.verify_gate(p_s, xt, q=q, u=u, r=r, mode=B.VERIFY_SAMPLING, ws=ws)
+        assert head_zero()
         torch.cuda.synchronize()
         assert torch.equal(y_s, y_f) and torch.equal(idx_s, idx_f) and torch.equal(w_s, w_f)
+        assert torch.equal(yg_s, yg_f) and torch.equal(yp_s, yp_f)
+        assert all(torch.equal(a_, b_) for a_, b_ in zip(sk_s, sk_f))
         assert torch.equal(p_s, p_f) and torch.equal(n_s, n_f) and torch.equal(t_s, t_f)
-        assert int(ws.buf[:256].count_nonzero()) == 0   # the round left its counters zero
+        assert torch.equal(m_s, m_f) and torch.equal(o_s, o_f)
 
 
 def test_runs_are_bitwise_deterministic():
@@ -328,52 +362,81 @@ def test_mfma_column_position_does_not_change_results():
 
 # ------------------------------------------------------------- full-size configs
 
-def _full_case(name, n, rep=0, tokens=None):
-    cfg = synth.CONFIGS[name]
-    _say(f"[full] {name} n={n} rep={rep}")
-    lay_dev = synth.make_layer(cfg, "cuda")
-    x_dev = synth.make_hidden(cfg, n, rep, "cuda")
-    gate_np = lay_dev["gate_w"].cpu().numpy()
-    x_np = x_dev.cpu().numpy()
-    idx, w, ref, flagged = _check_route(cfg, lay_dev["gate_w"], x_dev, gate_np, x_np)
-    tiled = B.pack_weights(B.shape_of(cfg), {k: lay_dev[k] for k in ("w13", "w2", "ws13", "ws2")})
-    y_ps, y_dd, U, _ = _run_both(cfg, tiled, x_dev, idx, w)
-    del tiled
-    assert torch.equal(y_ps, y_dd)
-    gi = idx.cpu().numpy()
-    assert U == O.pass_bytes(oshape(cfg), gi)[3]
-    # oracle on the GPU's own routing, on sampled tokens, fetching only the
-    # experts those tokens use
-    toks = np.arange(x_np.shape[0]) if tokens is None else np.asarray(tokens)
-    used = np.unique(gi[toks])
+def _host_experts(cfg, lay_dev, used):
+    """Host bit patterns of the routed experts in `used` (others zero, never
+    read) and of the shared experts."""
     hdt = np.uint16 if cfg.wdtype == "bf16" else np.float32
     host = {"w13": np.zeros((cfg.E,) + tuple(lay_dev["w13"].shape[1:]), hdt),
             "w2": np.zeros((cfg.E,) + tuple(lay_dev["w2"].shape[1:]), hdt)}
     for e in used:
         host["w13"][e] = synth.to_host_bits(lay_dev["w13"][e])
         host["w2"][e] = synth.to_host_bits(lay_dev["w2"][e])
-    host["ws13"] = synth.to_host_bits(lay_dev["ws13"])
-    host["ws2"] = synth.to_host_bits(lay_dev["ws2"])
-    y_ref, _, _, _ = oracle_y(cfg, host, x_np, gi, w.cpu().numpy(), tokens=toks)
+    host["ws13"] = None if lay_dev["ws13"] is None else synth.to_host_bits(lay_dev["ws13"])
+    host["ws2"] = None if lay_dev["ws2"] is None else synth.to_host_bits(lay_dev["ws2"])
+    return host
+
+
+def _full_pass(cfg, lay_dev, tiled, n, rep=0, tokens=None):
+    """One verify pass of the workload end to end: the GPU routes and both
+    GPU engines run on that routing; the oracle routes the same hidden
+    states itself and runs its layer on its own routing.  Routing, U and
+    the outputs are compared on every token (or the given tokens): tokens
+    the oracle flags as near-ties are exempt from the index comparison and
+    their outputs are checked against the oracle layer on the GPU's
+    routing of that token, a valid top-k of the GPU's logits."""
+    _say(f"[full] {cfg.name} n={n} rep={rep}")
+    x_dev = synth.make_hidden(cfg, n, rep, "cuda")
+    gate_np = lay_dev["gate_w"].cpu().numpy()
+    x_np = x_dev.cpu().numpy()
+    idx, w, ref, flagged = _check_route(cfg, lay_dev["gate_w"], x_dev, gate_np, x_np)
+    y_ps, y_dd, U, _ = _run_both(cfg, tiled, x_dev, idx, w)
+    assert torch.equal(y_ps, y_dd)
+    gi, gw = idx.cpu().numpy(), w.cpu().numpy()
+    assert U == O.pass_bytes(oshape(cfg), gi)[3]
+    assert B.pass_bytes(B.shape_of(cfg), gi) == O.pass_bytes(oshape(cfg), gi)
+    ok = (ref["flags"] == 0)[:, None]
+    idx_ref = np.where(ok, ref["idx"], gi).astype(np.int32)
+    w_ref = np.where(ok, ref["w"], gw.astype(np.float64))
+    toks = np.arange(x_np.shape[0]) if tokens is None else np.asarray(tokens)
+    host = _host_experts(cfg, lay_dev, np.unique(idx_ref[toks]))
+    y_ref, _, _, _ = oracle_y(cfg, host, x_np, idx_ref, w_ref, tokens=toks, threads=16)
     err = rel_err(y_ps.cpu().numpy()[toks], y_ref)
-    _say(f"   rel err {err:.3e}  U={U}  flagged={flagged}")
+    _say(f"   {len(toks)} tokens: rel err {err:.3e}  U={U}  flagged={flagged}")
     assert err <= OUT_RTOL[cfg.wdtype]
-    del lay_dev
-    torch.cuda.empty_cache()
+
+
+def _full_layer(name):
+    cfg = synth.CONFIGS[name]
+    lay_dev = synth.make_layer(cfg, "cuda")
+    tiled = B.pack_weights(B.shape_of(cfg), {k: lay_dev[k] for k in ("w13", "w2", "ws13", "ws2")})
+    return cfg, lay_dev, tiled
 
 
 def test_full_tiny():
-    _full_case("tiny", 4)
+    cfg, lay_dev, tiled = _full_layer("tiny")
+    _full_pass(cfg, lay_dev, tiled, 4)
 
 
-@pytest.mark.parametrize("n", [1, 16])
-def test_full_v2lite(n):
-    _full_case("v2lite", n, tokens=[0, n - 1])
+def test_full_v2lite_every_token():
+    cfg, lay_dev, tiled = _full_layer("v2lite")
+    for n in (1, 2, 4, 8, 16):
+        _full_pass(cfg, lay_dev, tiled, n)
+    del lay_dev, tiled
+    torch.cuda.empty_cache()
 
 
-def test_full_mixtral():
-    _full_case("mixtral", 8, tokens=[0, 7])
+def test_full_mixtral_every_token():
+    cfg, lay_dev, tiled = _full_layer("mixtral")
+    for n in (1, 4, 8):
+        _full_pass(cfg, lay_dev, tiled, n)
+    del lay_dev, tiled
+    torch.cuda.empty_cache()
 
 
-def test_full_v3():
-    _full_case("v3", 16, tokens=[0, 63])
+def test_full_v3_one_sequence_and_every_column_tile():
+    """The V3-shaped pass of 4 sequences x 16 tokens: all of sequence 1
+    (tokens 16..31) and tokens of the other 16-token column tiles."""
+    cfg, lay_dev, tiled = _full_layer("v3")
+    _full_pass(cfg, lay_dev, tiled, 16, tokens=list(range(16, 32)) + [0, 9, 32, 40, 47, 55, 63])
+    del lay_dev, tiled
+    torch.cuda.empty_cache()

@@ -101,7 +101,7 @@ def test_stack_equals_per_layer_calls(case, n, engine):
                 assert int(nu[l].item()) == int(rnu.item())
 
 
-def test_stack_matches_oracle_on_sampled_tokens():
+def test_stack_matches_oracle_on_every_token():
     cfg = small_config("stack-oracle", 512, 64, 6, 352, 2, "bf16")
     L, n = 4, 16
     stack = _make_stack(cfg, L, bias=True, tiled=True)
@@ -120,11 +120,13 @@ def test_stack_matches_oracle_on_sampled_tokens():
         assert np.array_equal(gi[ok], r["idx"][ok])
         assert int(nu[l].item()) == O.pass_bytes(s, gi)[3]
         host = {kk: synth.to_host_bits(rows[kk][l]) for kk in ("w13", "w2", "ws13", "ws2")}
-        toks = [0, 7, 15]
-        y_o, _, _, _ = O.layer(s, host["w13"], host["w2"], host["ws13"], host["ws2"], xs[toks],
-                               gi[toks], w[l].cpu().numpy()[toks].astype(np.float64),
-                               engine="dedup", n_threads=8)
-        err = rel_err(y[l].cpu().numpy()[toks], y_o)
+        # the oracle's own routing on unflagged tokens, the GPU's on the rest
+        okc = ok[:, None]
+        idx_r = np.where(okc, r["idx"], gi).astype(np.int32)
+        w_r = np.where(okc, r["w"], w[l].cpu().numpy().astype(np.float64))
+        y_o, _, _, _ = O.layer(s, host["w13"], host["w2"], host["ws13"], host["ws2"], xs,
+                               idx_r, w_r, engine="dedup", n_threads=8)
+        err = rel_err(y[l].cpu().numpy(), y_o)
         _say(f"[stack-oracle] layer {l} rel err {err:.2e}")
         assert err <= OUT_RTOL["bf16"]
 

@@ -104,9 +104,11 @@ def test_large_bias_forces_an_expert(d, E, k, n):
 # ---------------------------------------------------------------- grouped dedup
 
 def _records(ws, E, n, k, G):
-    """G compaction records from the head of a grouped dedup workspace."""
+    """G compaction records of a grouped dedup workspace (from byte 256; the
+    head belongs to arrival counters and stays zero)."""
     rec_ints = ((4 * (3 * E + 2 + n * k)) + 255) // 256 * 64
-    buf = ws.buf[: 4 * rec_ints * G].view(torch.int32).cpu().numpy()
+    assert int(ws.buf[:256].count_nonzero()) == 0
+    buf = ws.buf[256: 256 + 4 * rec_ints * G].view(torch.int32).cpu().numpy()
     return [buf[g * rec_ints:(g + 1) * rec_ints] for g in range(G)]
 
 
@@ -183,7 +185,7 @@ def test_one_group_is_dedup_and_token_groups_are_per_slot():
     torch.cuda.synchronize()
     assert torch.equal(y_1, y_d) and int(nug.item()) == int(nu1.item())
     L = 4 * (3 * cfg.E + 2 + n * cfg.k)
-    assert torch.equal(ws_g.buf[:L], ws_d.buf[:L])        # the same record
+    assert torch.equal(ws_g.buf[:256 + L], ws_d.buf[:256 + L])   # the same record
     nun = torch.zeros(n, dtype=torch.int32, device="cuda")
     y_n = B.expert_pass_dedup_grouped(shape, lay_dev, x, idx, w, list(range(n + 1)),
                                       n_unique=nun)

@@ -88,6 +88,73 @@ def test_bf16_rne_ties_to_even_closed_form():
     assert O.bf16_rne(np.float32(np.nan))[()] & 0x7FC0 == 0x7FC0
 
 
+def _bf16_grid():
+    """Every finite non-negative bf16 value as an exact fraction, ascending,
+    with its bit pattern; 2^128 (the infinity pattern) closes the grid, as
+    IEEE overflow rounding treats it."""
+    from fractions import Fraction
+    pats = np.arange(0, 0x7F81, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    grid = [Fraction(float(v)) for v in vals[:-1]] + [Fraction(2) ** 128]
+    return grid, pats
+
+
+def _exact_nearest_even(v, grid, pats):
+    """bf16 pattern nearest to the double v, ties to the even pattern, by
+    exact comparison against the whole grid (bisection)."""
+    import bisect
+    from fractions import Fraction
+    if v != v:
+        return None
+    sign = 0x8000 if np.signbit(v) else 0
+    if np.isinf(v) or Fraction(abs(float(v))) >= grid[-1]:
+        return sign | 0x7F80
+    a = Fraction(abs(float(v)))
+    i = bisect.bisect_left(grid, a)
+    if i < len(grid) and grid[i] == a:
+        return sign | int(pats[i])
+    lo, hi = i - 1, i
+    dlo, dhi = a - grid[lo], grid[hi] - a
+    if dlo < dhi or (dlo == dhi and pats[lo] % 2 == 0):
+        return sign | int(pats[lo])
+    return sign | int(pats[hi])
+
+
+def test_bf16_rne_f64_is_the_exact_nearest_even():
+    """One-step fp64 -> bf16 rounding against exact arithmetic on the whole
+    bf16 grid: random doubles over the normal and subnormal bf16 ranges and
+    beyond its largest value, doubles a hair off and exactly on midpoints
+    (the fp32 rounding of a double can land on a midpoint that the double
+    itself is not on), signed zeros and infinities."""
+    from fractions import Fraction
+    grid, pats = _bf16_grid()
+    rng = _rng(12)
+    vals = [float(v) for v in rng.standard_normal(1500)]
+    vals += [float(v) for v in rng.standard_normal(300) * 2.0 ** rng.integers(-140, -120, 300)]
+    vals += [float(v) for v in rng.standard_normal(200) * 2.0 ** 127]
+    mids = rng.integers(1, 0x7F7F, 600)
+    for p_ in mids:
+        m = (grid[p_] + grid[p_ + 1]) / 2
+        for rel in (0.0, 2.0 ** -30, -(2.0 ** -30), 2.0 ** -52, -(2.0 ** -52)):
+            vals.append(float(m * (1 + Fraction(rel))))
+    vals += [0.0, -0.0, np.inf, -np.inf, 3.3895313892515355e38, 3.4e38, 2.0 ** -133,
+             2.0 ** -134, 3 * 2.0 ** -135, 2.0 ** -140]
+    ours = O.bf16_rne_f64(np.array(vals, dtype=np.float64))
+    for v, got in zip(vals, ours):
+        assert int(got) == _exact_nearest_even(v, grid, pats), v
+    assert O.bf16_rne_f64(np.float64(np.nan))[()] & 0x7FC0 == 0x7FC0
+
+
+def test_bf16_rne_f64_rounds_once_not_through_fp32():
+    """1 + 2^-8 + 2^-30 lies just above the midpoint of bf16 1.0 and 1 + 2^-7,
+    so its nearest bf16 is 1 + 2^-7 (0x3F81).  Its fp32 rounding is the
+    midpoint itself, which then ties to the even 1.0 (0x3F80): the oracle's
+    activation rounding must take the first, single-step answer."""
+    v = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert O.bf16_rne_f64(np.float64(v))[()] == 0x3F81
+    assert O.bf16_rne(np.float32(v))[()] == 0x3F80
+
+
 # ---------------------------------------------------------------- gate + top-k
 
 def test_gate_logits_match_numpy_matmul():
@@ -148,6 +215,20 @@ def test_weights_sum_to_one_and_top1_is_exactly_one():
                 rng.standard_normal((20, 32)).astype(np.float32))
     assert np.all(r["w"] == 1.0)
     assert np.array_equal(r["idx"][:, 0], np.argmax(r["logits"], axis=1))
+
+
+def test_order_is_taken_on_the_fp64_logits():
+    """Two logits that differ by 2^-40, far below fp32 resolution at 1: the
+    larger one is selected first although its index is higher (an fp32
+    comparison would see a tie and take the lower index), and the token is
+    flagged, since its gap is under the near-tie threshold."""
+    s = O.Shape(d=2, E=3, k=2, f=16)
+    gw = np.array([[1.0, 0.0], [1.0, 1.0], [0.5, 0.0]], dtype=np.float32)
+    x = np.array([[1.0, 2.0 ** -40]], dtype=np.float32)
+    r = O.route(s, gw, x)
+    assert r["logits"][0, 1] - r["logits"][0, 0] == 2.0 ** -40
+    assert r["idx"].tolist() == [[1, 0]]
+    assert r["flags"][0] & O.FLAG_ORDER and not r["flags"][0] & O.FLAG_BOUNDARY
 
 
 def test_exact_ties_pick_lowest_index_and_are_flagged():

@@ -170,3 +170,12 @@ def test_crafted_routing_rejects_impossible_U():
         synth.crafted_routing(2, 6, 64, 13, seed=0)    # U > N k
     with pytest.raises(ValueError):
         synth.crafted_routing(16, 2, 8, 9, seed=0)     # U > E
+
+
+def test_with_bandwidth_replaces_only_the_slope():
+    """The model under a bandwidth error: t = B / BW' + t0 with the fit's own
+    fixed time, exactly."""
+    f = M.fit_line([1e8, 2e8, 4e8], [30.0, 43.0, 71.0])
+    g = M.with_bandwidth(f, 5000.0)
+    assert g.t0 == f.t0 and abs(g.bw_GBs - 5000.0) < 1e-9
+    assert abs(g.predict(3e8)[0] - (3e8 / 5000.0 / 1e3 + f.t0)) < 1e-9
