@@ -666,7 +666,7 @@ def timeline_leg(cfg, eng, layers, n_values, steps, warmup):
                 idx, w = eng.route(lay, x)
                 getattr(eng, name)(lay, x, idx, w, y)
             torch.cuda.synchronize()
-            hold_gpu(0.1 * steps)
+            hold_gpu(0.25 * steps)
             e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
             e0.record()
             idxs = []
