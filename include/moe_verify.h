@@ -260,6 +260,24 @@ int moe_stack_pass(const moe_shape *shape, int32_t n_layers, const moe_stack_wei
                    float *topk_w, float *y, int32_t *n_unique, void *workspace,
                    size_t *workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_stack_pass with the library's own workspace instead of a caller's.
+ * The workspace is a static device array of MOE_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends; the call
+ * allocates nothing.  Arguments, outputs and results are moe_stack_pass's
+ * (bit for bit); a pass whose workspace would exceed the array returns
+ * MOE_ERR_WORKSPACE before anything is enqueued (the V2-Lite-shaped stack of
+ * 26 layers at 16 tokens needs about 38 MB, one V3-shaped layer at 64
+ * tokens about 21 MB).  All calls on one GPU share its array: calls that
+ * can overlap on one GPU (other streams, other host threads) race, so the
+ * caller serialises them. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64 << 20)
+int moe_stack_pass_noalloc(const moe_shape *shape, int32_t n_layers,
+                           const moe_stack_weights *weights, const float *x, int32_t n_tokens,
+                           int32_t engine, int32_t *topk_idx, float *topk_w, float *y,
+                           int32_t *n_unique, void *stream);
+
 /* Requested expert bytes of one pass, on the host (same abstract: step time
  * is the bytes each kernel requests over its effective bandwidth).
  * B_e = 3 * d * f * sizeof(weight); perslot = N*k*B_e, dedup = U*B_e,

@@ -67,6 +67,7 @@ def load():
     lib.moe_expert_pass_dedup_grouped.argtypes = [P, P, P, i32, i32, P, P, P, P, P, P, sz, P]
     lib.moe_pass_bytes_grouped.argtypes = [P, P, i32, i32, P, P, P]
     lib.moe_stack_pass.argtypes = [P, i32, P, P, i32, i32, P, P, P, P, P, sz, P]
+    lib.moe_stack_pass_noalloc.argtypes = [P, i32, P, P, i32, i32, P, P, P, P, P]
     lib.moe_expert_pass_perslot.argtypes = [P, P, P, i32, P, P, P, P, sz, P]
     lib.moe_expert_pass_dedup.argtypes = [P, P, P, i32, P, P, P, P, P, sz, P]
     lib.moe_pass_bytes.argtypes = [P, P, i32, P, P, P, P]
@@ -79,7 +80,8 @@ def load():
     lib.moe_verify_probs.argtypes = [i32, i32, P, C.c_float, C.c_float, P, P, sz, P]
     for fn in ("moe_route", "moe_route_biased", "moe_expert_pass_perslot",
                "moe_expert_pass_dedup", "moe_expert_pass_dedup_grouped", "moe_pass_bytes",
-               "moe_pass_bytes_grouped", "moe_stack_pass", "moe_pack_weights",
+               "moe_pass_bytes_grouped", "moe_stack_pass", "moe_stack_pass_noalloc",
+               "moe_pack_weights",
                "moe_timing_enable",
                "moe_timing_read", "moe_verify_gate", "moe_verify_probs"):
         getattr(lib, fn).restype = C.c_int
@@ -321,6 +323,19 @@ def stack_pass(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=No
     _check("moe_stack_pass", lib.moe_stack_pass(
         C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y),
         _ptr(n_unique), _ptr(buf), C.byref(have), _stream()))
+    del keep
+    return idx, w, y
+
+
+def stack_pass_noalloc(shape, stack, x, engine, *, idx=None, w=None, y=None, n_unique=None):
+    """stack_pass on the library's static device workspace
+    (moe_stack_pass_noalloc): the call allocates nothing on the device
+    (outputs not given are allocated here, by torch, before the call)."""
+    lib = load()
+    keep, cw, eng, L, x, n, idx, w, y = _stack_args(shape, stack, x, engine, idx, w, y, n_unique)
+    _check("moe_stack_pass_noalloc", lib.moe_stack_pass_noalloc(
+        C.byref(shape), L, C.byref(cw), _ptr(x), n, eng, _ptr(idx), _ptr(w), _ptr(y),
+        _ptr(n_unique), _stream()))
     del keep
     return idx, w, y
 

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libmoeverify.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["router.hip", "expert.hip", "verify.hip", "abi.cpp"]
+SOURCES = ["router.hip", "expert.hip", "verify.hip", "abi.cpp", "noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

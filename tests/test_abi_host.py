@@ -322,3 +322,20 @@ def test_every_workspace_reserves_the_counter_head():
                                 C.byref(nb), None) == 0
     assert nb.value >= 256 + 2 * 1000 * 8
 
+
+def test_noalloc_rejects_a_pass_beyond_its_array():
+    """moe_stack_pass_noalloc validates and sizes a pass before any device
+    work: the V3-shaped layer stacked 8 deep at 64 tokens needs more than
+    the static array (MOE_ERR_WORKSPACE), a bad engine is rejected."""
+    lib = B.load()
+    shape = B.make_shape(7168, 256, 8, 2048, 1, "bf16")
+    sw = B.StackWeights(0x100000, None, 0x200000, 0x300000, 0x400000, 0x500000, 1)
+    p = C.c_void_p(0x600000)
+    assert lib.moe_stack_pass_noalloc(C.byref(shape), 8, C.byref(sw), p, 64, 1, p, p, p, None,
+                                      None) == -3
+    assert lib.moe_stack_pass_noalloc(C.byref(shape), 1, C.byref(sw), p, 64, 2, p, p, p, None,
+                                      None) == -1
+    nb = C.c_size_t(0)
+    assert lib.moe_stack_pass(C.byref(shape), 1, C.byref(sw), p, 64, 1, p, p, p, None, None,
+                              C.byref(nb), None) == 0
+    assert nb.value < 64 << 20      # one V3-shaped layer at 64 tokens fits
