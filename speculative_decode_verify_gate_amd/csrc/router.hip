@@ -10,9 +10,10 @@
 // The gate GEMM [N x d] x [d x E] streams the fp32 gate matrix once with
 // fp32 MFMA (16 experts x 16 tokens per tile), split over K so that enough
 // workgroups stream it; each split yields fp32 partial logits.  Logits are
-// the partials summed in split order (deterministic).  Top-k: every
-// (token, expert) pair finds its rank under (value desc, index asc) by
-// counting, in LDS, the experts ahead of it; ranks below k are the slots.
+// the partials summed in split order (deterministic).  Top-k: a wavefront
+// per token takes k + 1 rounds of a wavefront-wide argmax in the order
+// (value descending, index ascending): round j yields slot j, round k the
+// margin.
 //
 // When all partials of a pass are small (at most 64 KB), one launch does
 // everything: the gate workgroups hand their partials over with
@@ -34,153 +35,161 @@ constexpr int kGateKPerWave = kGateKPerBlock / kGateWaves;  // 64 = 4 steps of 1
 constexpr int kMaxColTiles = 4;                              // N <= 64
 constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
 constexpr int kFusedGateThreads = 256;     // one-launch routing: threads per workgroup
-// gate workgroup LDS shared by the wave sums and the routing's partial ranks
-constexpr int kGateScratch =
-    (kGateWaves * kMaxColTiles * 64 * 16 > (kFusedGateThreads / 64) * MOE_MAX_EXPERTS * 4)
-        ? kGateWaves * kMaxColTiles * 64 * 16
-        : (kFusedGateThreads / 64) * MOE_MAX_EXPERTS * 4;
+constexpr int kGateScratch = kGateWaves * kMaxColTiles * 64 * 16;  // the waves' partial sums
 
-// Logits sit in LDS at logit_ld(E) per token.  The padding holds -inf at
-// indices >= E, which never ranks ahead of a real expert: it is not greater
-// than any logit, and on equality with a -inf logit the lower (real) index
-// wins.
+// Logits sit in LDS at logit_ld(E) per token; the selection reads only
+// indices below E.
 
-// Order key of expert e with logit v: order-preserving bits of v (with -0
-// taken as +0) above the complemented index, so keys compare like (logit
-// descending, index ascending) -- a strict total order in which a token's
-// rank of e is the number of its keys greater than e's.  Padding entries
-// (e >= E) get key 0, below every real key.
-__device__ inline uint64_t order_key(float v, int e) {
-  uint32_t b = __float_as_uint(v);
-  if ((b << 1) == 0u) b = 0u;                       // -0 and +0 compare equal
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)~e;
+// Order-preserving 32-bit key of a logit (signed compare: larger value,
+// larger key), -0 taken as +0.  kDead, below every key of a value that is
+// not a NaN, marks an expert already taken (or past E).
+__device__ inline int logit_key(float v) {
+  int b = __float_as_int(v);
+  if (b == (int)0x80000000) b = 0;
+  return b < 0 ? (b ^ 0x7FFFFFFF) : b;
+}
+__device__ inline float key_logit(int key) { return __int_as_float(key < 0 ? key ^ 0x7FFFFFFF : key); }
+constexpr int kDead = (int)0x80000000;
+
+// k from lane i - SHIFT of the same 16-lane row (DPP row_shr), kDead for
+// the first SHIFT lanes of a row.
+template <int SHIFT>
+__device__ inline int row_shr_key(int k) {
+  return __builtin_amdgcn_update_dpp(kDead, k, 0x110 + SHIFT, 0xf, 0xf, false);
 }
 
-// Top-k + softmax of n_tok tokens whose logits sit in LDS (L[t][ld], ld =
-// logit_ld(E)), by the nth threads of the caller.  Lane l of a wavefront
-// owns experts l, l+64, l+128, l+192 of a token; every key of the token is
-// broadcast from its owner lane (readlane, no memory round trip) and
-// compared with the lane's own keys, counting those ahead.  With fewer
-// tokens than wavefronts, each token's keys are split over several
-// wavefronts and the partial counts added in LDS; with more, a wavefront
-// takes TPW tokens at once so their compare chains overlap.  Ranks 0..k-1
-// are the selection in slot order; rank k gives the margin.  sel_v / sel_e:
-// LDS [n_tok][MOE_MAX_TOPK + 1].  t0 is the global index of token 0.
-// QM: 64-expert quarters compiled for (E <= 64 QM).
+// Largest key over the wavefront, returned to every lane: a max over each
+// 16-lane row by shifted DPP moves (lane 16r + 15 ends with its row's max),
+// then the four row maxima read out and combined.
+__device__ inline int wave_max_key(int k) {
+  k = max(k, row_shr_key<1>(k));
+  k = max(k, row_shr_key<2>(k));
+  k = max(k, row_shr_key<4>(k));
+  k = max(k, row_shr_key<8>(k));
+  const int r0 = __builtin_amdgcn_readlane(k, 15), r1 = __builtin_amdgcn_readlane(k, 31);
+  const int r2 = __builtin_amdgcn_readlane(k, 47), r3 = __builtin_amdgcn_readlane(k, 63);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// i from lane i - SHIFT of the same 16-lane row, kNone for the first SHIFT
+// lanes of a row; the smallest over the wavefront, returned to every lane.
+constexpr int kNone = 0x7FFFFFFF;
+template <int SHIFT>
+__device__ inline int row_shr_idx(int i) {
+  return __builtin_amdgcn_update_dpp(kNone, i, 0x110 + SHIFT, 0xf, 0xf, false);
+}
+__device__ inline int wave_min_idx(int i) {
+  i = min(i, row_shr_idx<1>(i));
+  i = min(i, row_shr_idx<2>(i));
+  i = min(i, row_shr_idx<4>(i));
+  i = min(i, row_shr_idx<8>(i));
+  const int r0 = __builtin_amdgcn_readlane(i, 15), r1 = __builtin_amdgcn_readlane(i, 31);
+  const int r2 = __builtin_amdgcn_readlane(i, 47), r3 = __builtin_amdgcn_readlane(i, 63);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+// Top-k selection of n_tok tokens whose logits sit in LDS (L[t][ld], ld =
+// logit_ld(E)), by the nth threads of the caller.  A wavefront takes a
+// token: lane l holds the keys of experts l, l+64, l+128, l+192, and each
+// round takes the largest remaining key over the wavefront and, among the
+// remaining experts holding it, the lowest index (a second wavefront
+// reduction, a min over the indices that hold it): the next slot in the
+// order (logit descending, index ascending).  Rounds 0..k-1 fill the slots, round k
+// gives the margin.  TPW tokens per wavefront go through the rounds
+// together, so their dependent steps overlap.  sel_v / sel_e: LDS
+// [n_tok][MOE_MAX_TOPK + 1].  QM: 64-expert quarters compiled for
+// (E <= 64 QM).
 template <int QM, int TPW>
-__device__ inline void rank_and_select(const float *L, int n_tok, int t0, const RouteArgs &a,
-                                       int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
-                                       int (*sel_e)[MOE_MAX_TOPK + 1],
-                                       int (*part_rank)[MOE_MAX_EXPERTS]) {
+__device__ inline void argmax_select(const float *L, int n_tok, const RouteArgs &a, int tid,
+                                     int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
+                                     int (*sel_e)[MOE_MAX_TOPK + 1]) {
   const int E = a.E;
   const int k = a.k;
   const int ld = logit_ld(E);
   const int lane = tid & 63, wave = tid >> 6, nw = nth >> 6;
-  const int nq = (E + 63) >> 6;
-  const int wpt = n_tok >= nw ? 1 : nw / n_tok;  // wavefronts per token
-  const int slice = wave % wpt;                  // this wavefront's share of the keys
-  const int tstride = nw / wpt;                  // tokens started per round
-  const int jn = (E + wpt - 1) / wpt;
-  const int j0 = slice * jn, j1 = min(E, j0 + jn);
-  // Split mode (wpt > 1) makes one round, in which a wavefront whose token
-  // index is past n_tok only takes part in the barrier.
-  for (int tb = wave / wpt; wpt > 1 || tb < n_tok; tb += tstride * TPW) {
-    float v[TPW][QM];
-    uint64_t key[TPW][QM];
-    int rank[TPW][QM];
+  const int rounds = k < E ? k + 1 : k;
+  for (int tb = wave; tb < n_tok; tb += nw * TPW) {  // uniform per wavefront
+    int key[TPW][QM];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      const int t = tb + tt * tstride;
+      const int t = tb + tt * nw;
 #pragma unroll
       for (int q = 0; q < QM; ++q) {
         const int e = q * 64 + lane;
-        const bool ok = t < n_tok && q < nq && e < E;
-        v[tt][q] = ok ? L[(size_t)t * ld + e] : -INFINITY;
-        key[tt][q] = ok ? order_key(v[tt][q], e) : 0ull;
-        rank[tt][q] = 0;
+        key[tt][q] = (t < n_tok && e < E) ? logit_key(L[(size_t)t * ld + e]) : kDead;
       }
     }
-#pragma unroll
-    for (int qq = 0; qq < QM; ++qq) {
-      const int ja = max(j0 - qq * 64, 0), jb = min(j1 - qq * 64, 64);
-      if (qq >= nq || ja >= jb) continue;  // uniform
-      uint32_t hi[TPW], lo[TPW];
+    for (int r = 0; r < rounds; ++r) {
+      int m[TPW];
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
-        hi[tt] = (uint32_t)(key[tt][qq] >> 32);
-        lo[tt] = (uint32_t)key[tt][qq];
+        m[tt] = key[tt][0];
+#pragma unroll
+        for (int q = 1; q < QM; ++q) m[tt] = max(m[tt], key[tt][q]);
       }
-      for (int j = ja; j < jb; ++j) {
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-          const uint64_t kj = ((uint64_t)__builtin_amdgcn_readlane(hi[tt], j) << 32) |
-                              (uint32_t)__builtin_amdgcn_readlane(lo[tt], j);
-#pragma unroll
-          for (int q = 0; q < QM; ++q) rank[tt][q] += kj > key[tt][q] ? 1 : 0;
-        }
-      }
-    }
-    if (wpt > 1) {
-      // one token per wavefront group: add the groups' slices
-#pragma unroll
-      for (int q = 0; q < QM; ++q) part_rank[wave][q * 64 + lane] = rank[0][q];
-      __syncthreads();
-      if (slice == 0 && tb < n_tok) {
-#pragma unroll
-        for (int q = 0; q < QM; ++q) {
-          rank[0][q] = 0;
-          for (int w = 0; w < wpt; ++w) rank[0][q] += part_rank[wave + w][q * 64 + lane];
-        }
-      }
-    }
-    if (slice == 0) {
+      for (int tt = 0; tt < TPW; ++tt) m[tt] = wave_max_key(m[tt]);
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) {
-        const int t = tb + tt * tstride;
+        // the lowest expert holding the maximum; when only NaN logits
+        // remain (no key equals the maximum), the lowest remaining expert
+        int cand = kNone;
 #pragma unroll
-        for (int q = 0; q < QM; ++q) {
-          const int e = q * 64 + lane;
-          if (t < n_tok && q < nq && e < E) {
-            if (rank[tt][q] <= k) {
-              sel_v[t][rank[tt][q]] = v[tt][q];
-              sel_e[t][rank[tt][q]] = e;
-            }
-            if (a.logits) a.logits[(size_t)(t0 + t) * E + e] = v[tt][q];
-          }
+        for (int q = QM - 1; q >= 0; --q)
+          if (key[tt][q] == m[tt] && m[tt] != kDead) cand = q * 64 + lane;
+        int e = wave_min_idx(cand);
+        if (e == kNone) {
+#pragma unroll
+          for (int q = QM - 1; q >= 0; --q)
+            if (q * 64 + lane < E && key[tt][q] != kDead) cand = q * 64 + lane;
+          e = wave_min_idx(cand);
+          if (e == kNone) e = -1;
+        }
+        const int t = tb + tt * nw;
+#pragma unroll
+        for (int q = 0; q < QM; ++q)
+          if (q * 64 + lane == e) key[tt][q] = kDead;
+        if (lane == 0 && t < n_tok && e >= 0) {
+          sel_e[t][r] = e;
+          sel_v[t][r] = key_logit(m[tt]);
         }
       }
     }
-    if (wpt > 1) break;
   }
 }
 
 template <int QM>
-__device__ inline void rank_and_select_q(const float *L, int n_tok, int t0, const RouteArgs &a,
-                                         int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
-                                         int (*sel_e)[MOE_MAX_TOPK + 1],
-                                         int (*part_rank)[MOE_MAX_EXPERTS]) {
+__device__ inline void argmax_select_q(const float *L, int n_tok, const RouteArgs &a, int tid,
+                                       int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
+                                       int (*sel_e)[MOE_MAX_TOPK + 1]) {
   const int per_wave = (n_tok + (nth >> 6) - 1) / (nth >> 6);  // tokens per wavefront
   if (per_wave >= 4)
-    rank_and_select<QM, 4>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+    argmax_select<QM, 4>(L, n_tok, a, tid, nth, sel_v, sel_e);
   else if (per_wave >= 2)
-    rank_and_select<QM, 2>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+    argmax_select<QM, 2>(L, n_tok, a, tid, nth, sel_v, sel_e);
   else
-    rank_and_select<QM, 1>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+    argmax_select<QM, 1>(L, n_tok, a, tid, nth, sel_v, sel_e);
 }
 
-// part_rank: LDS [nth / 64][MOE_MAX_EXPERTS] ints, free during the call.
+// Top-k, softmax over the k, margin and (if asked) the logits of n_tok
+// tokens whose logits sit in LDS; t0 is the global index of token 0.
 __device__ inline void select_topk(const float *L, int n_tok, int t0, const RouteArgs &a,
                                    int tid, int nth, float (*sel_v)[MOE_MAX_TOPK + 1],
-                                   int (*sel_e)[MOE_MAX_TOPK + 1],
-                                   int (*part_rank)[MOE_MAX_EXPERTS]) {
+                                   int (*sel_e)[MOE_MAX_TOPK + 1]) {
   const int E = a.E, k = a.k;
+  if (a.logits) {
+    const int ld = logit_ld(E);
+    for (int i = tid; i < n_tok * E; i += nth) {
+      const int t = i / E;
+      a.logits[(size_t)t0 * E + i] = L[(size_t)t * ld + (i - t * E)];
+    }
+  }
   if (E <= 64)
-    rank_and_select_q<1>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+    argmax_select_q<1>(L, n_tok, a, tid, nth, sel_v, sel_e);
   else if (E <= 128)
-    rank_and_select_q<2>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+    argmax_select_q<2>(L, n_tok, a, tid, nth, sel_v, sel_e);
   else
-    rank_and_select_q<4>(L, n_tok, t0, a, tid, nth, sel_v, sel_e, part_rank);
+    argmax_select_q<4>(L, n_tok, a, tid, nth, sel_v, sel_e);
   __syncthreads();
   for (int p = tid; p < n_tok * k; p += nth) {
     const int t = p / k;
@@ -251,8 +260,7 @@ __global__ __launch_bounds__(FUSED ? kFusedGateThreads : 256) void gate_kernel(R
     }
   }
 
-  // Sum the four waves' partials in wave order.  The buffer is reused for
-  // the partial ranks of the routing.
+  // Sum the four waves' partials in wave order.
   __shared__ __align__(16) unsigned char scratch[kGateScratch];
   f32x4 (*red)[kMaxColTiles][64] = (f32x4 (*)[kMaxColTiles][64])scratch;
   if (mma_wave) {
@@ -335,7 +343,7 @@ __global__ __launch_bounds__(FUSED ? kFusedGateThreads : 256) void gate_kernel(R
   __syncthreads();
   __shared__ float sel_v[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
   __shared__ int sel_e[MOE_MAX_TOKENS][MOE_MAX_TOPK + 1];
-  select_topk(Ls, N, layer * N, a, tid, nth, sel_v, sel_e, (int (*)[MOE_MAX_EXPERTS])scratch);
+  select_topk(Ls, N, layer * N, a, tid, nth, sel_v, sel_e);
 }
 
 // Unfused top-k, one workgroup per token.  Wave w sums the partials of
@@ -355,7 +363,6 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   __shared__ float ws_sum[kGateWaves][MOE_MAX_EXPERTS];
   __shared__ float sel_v[1][MOE_MAX_TOPK + 1];
   __shared__ int sel_e[1][MOE_MAX_TOPK + 1];
-  __shared__ int part_rank[kGateWaves][MOE_MAX_EXPERTS];
   const int n_q = (E + 63) / 64;
   float v[kMaxExpertsPerLane];
 #pragma unroll
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
     Ls[tid] = l;
   }
   __syncthreads();
-  select_topk(Ls, 1, layer * N + t, a, tid, blockDim.x, sel_v, sel_e, part_rank);
+  select_topk(Ls, 1, layer * N + t, a, tid, blockDim.x, sel_v, sel_e);
 }
 
 }  // namespace
