@@ -101,6 +101,15 @@ constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
 template <bool UP, int CTMAX>
 constexpr int kMinWaves = CTMAX == 1 ? (UP ? 3 : 4) : 2;
 
+// Wide down tiles are paired: a workgroup streams two consecutive 16-row
+// tiles of W2 against one staged window of its instance's activation rows,
+// as the up kernel streams W1 and W3 against one window of tokens, so the
+// staging is paid once per 32 output rows.
+template <bool UP, int CTMAX>
+constexpr bool kPairDown = !UP && CTMAX > 1;
+template <bool UP, int CTMAX>
+constexpr bool kTwoStreams = UP || kPairDown<UP, CTMAX>;
+
 // Kernel variants: the plain engines, dedup within token groups, and a stack
 // of layers (all layers' instances in one grid, layer-major).
 constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
@@ -116,6 +125,8 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
                                                                   int *ent_row, int *ent_tok,
                                                                   int *n_distinct) {
   constexpr bool DIRECT = CTMAX == 1;
+  constexpr bool PAIR = kPairDown<UP, CTMAX>;
+  constexpr bool TWO = kTwoStreams<UP, CTMAX>;  // a second weight stream (W3, or W2's next tile)
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
   using T = WT<BF16>;
   constexpr int SPC = kSpc;
@@ -129,7 +140,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
 
   const int R = UP ? a.f : a.d;  // output rows
   const int K = UP ? a.d : a.f;  // reduction length
-  const int RT = R / kTile;      // 16-row tiles per instance
+  const int RT = R / kTile / (PAIR ? 2 : 1);  // workgroup tiles per instance
   // A stack runs each layer's grid in turn: its own weights, routing,
   // compaction record, U and buffers; the tokens are shared.  Only the stack
   // instantiation offsets the per-layer arrays.
@@ -157,7 +168,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
     obuf += (size_t)layer * rows * a.d;
   }
   const int inst = bid / RT;
-  const int rt = bid - inst * RT;
+  const int rt = (bid - inst * RT) * (PAIR ? 2 : 1);  // first 16-row tile of the workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -228,6 +239,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
       wB = wA + fd * EB;
     } else {
       wA = base2 + ex * fd * EB;
+      wB = wA;  // paired: the next 16-row tile of the same W2
     }
   }
   const int nsteps = K / T::kStep;
@@ -238,12 +250,13 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
   // 1 KB and the lane's unit is its lane index (the layout stores exactly the
   // MFMA A-operand order), so a wave's load is one contiguous kilobyte.
   const unsigned char *rowA, *rowB = nullptr;
+  const int rtB = PAIR ? rt + 1 : rt;  // the second stream's tile
   if (TILED) {
     rowA = wA + ((size_t)rt * nsteps * kWave + lane) * 16;
-    if (UP) rowB = wB + ((size_t)rt * nsteps * kWave + lane) * 16;
+    if (TWO) rowB = wB + ((size_t)rtB * nsteps * kWave + lane) * 16;
   } else {
     rowA = wA + ((size_t)(rt * kTile + r) * K + lane_k) * EB;
-    if (UP) rowB = wB + ((size_t)(rt * kTile + r) * K + lane_k) * EB;
+    if (TWO) rowB = wB + ((size_t)(rtB * kTile + r) * K + lane_k) * EB;
   }
   const size_t step_bytes = TILED ? (size_t)kWave * 16 : (size_t)T::kStep * EB;
 
@@ -258,10 +271,10 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
       const size_t off = (size_t)step * step_bytes;
       if (TILED) {
         d1[s] = ldg16_once(rowA + off);
-        if (UP) d3[s] = ldg16_once(rowB + off);
+        if (TWO) d3[s] = ldg16_once(rowB + off);
       } else {
         d1[s] = ldg16(rowA + off);
-        if (UP) d3[s] = ldg16(rowB + off);
+        if (TWO) d3[s] = ldg16(rowB + off);
       }
     }
   };
@@ -405,7 +418,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
               }
               if (col >= mg) b = u32x4{0u, 0u, 0u, 0u};
               acc1[ct] = T::mma(s1[s], b, acc1[ct]);
-              if (UP) acc3[ct] = T::mma(s3[s], b, acc3[ct]);
+              if (TWO) acc3[ct] = T::mma(s3[s], b, acc3[ct]);
             }
           }
         }
@@ -455,12 +468,12 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
     // ---- the four waves' partial sums, added in wave order; wave ct then
     // finishes token tile ct (lane holds rows 4g..4g+3 for token column r)
     __syncthreads();  // every wave is done with the staged rows
-    f32x4 *red = (f32x4 *)lds;  // [UP ? 2 : 1][NW][CTMAX][64]
+    f32x4 *red = (f32x4 *)lds;  // [TWO ? 2 : 1][NW][CTMAX][64]
 #pragma unroll
     for (int ct = 0; ct < CTMAX; ++ct) {
       if (ct < n_ct) {
         red[(wave * CTMAX + ct) * kWave + lane] = acc1[ct];
-        if (UP) red[((NW + wave) * CTMAX + ct) * kWave + lane] = acc3[ct];
+        if (TWO) red[((NW + wave) * CTMAX + ct) * kWave + lane] = acc3[ct];
       }
     }
     __syncthreads();
@@ -470,7 +483,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
 #pragma unroll
       for (int w = 1; w < NW; ++w) h += red[(w * CTMAX + ct) * kWave + lane];
       f32x4 gg = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (UP) {
+      if (TWO) {
         gg = red[(NW * CTMAX + ct) * kWave + lane];
 #pragma unroll
         for (int w = 1; w < NW; ++w) gg += red[((NW + w) * CTMAX + ct) * kWave + lane];
@@ -494,6 +507,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
           }
         } else {
           *(f32x4 *)(obuf + (size_t)orow * a.d + row0) = h;
+          if (PAIR) *(f32x4 *)(obuf + (size_t)orow * a.d + row0 + kTile) = gg;
         }
       }
     }
@@ -513,7 +527,8 @@ template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
 __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
   __shared__ int ent_row[MOE_MAX_SLOTS];
   __shared__ int ent_tok[MOE_MAX_SLOTS];
-  const int RT = (UP ? a.f : a.d) / kTile;
+  // workgroup tiles per instance (paired wide down tiles: half the rows')
+  const int RT = (UP ? a.f : a.d) / kTile / (kPairDown<UP, CTMAX> ? 2 : 1);
   int U = 0;
   if (VAR == kGrouped) {
     // groups fold one by one: group g's routed slots in the grid are
@@ -557,7 +572,9 @@ template <bool BF16, bool UP, bool TILED, int VAR>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
   const int routed = VAR == kGrouped ? a.fbase[a.G] : (a.fold > 0 ? a.fold : a.n_routed);
-  const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile);
+  // wide down tiles are paired (d is a multiple of 32, so the tiles pair up)
+  const bool pair = !UP && a.N > kTile;
+  const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile) / (pair ? 2 : 1);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // the dynamic-LDS limit of each kernel, once per kernel: the most any

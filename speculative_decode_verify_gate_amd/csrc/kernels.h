@@ -149,7 +149,8 @@ inline int expert_lds_bytes(int N, int K, bool bf16, bool up, int E) {
   // at least one chunk per wave for a full token group, and room for the
   // waves' partial sums
   const size_t least = (size_t)rows * (kWavesPerBlock * chunk + kLdsPad) * eb;
-  const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * ctmax * kWave * 16;
+  // two weight streams: W1 and W3 (up), or a pair of W2 tiles (wide down)
+  const size_t partials = (size_t)2 * kWavesPerBlock * ctmax * kWave * 16;
   size_t bytes = whole < (size_t)kLdsBudget ? whole : (size_t)kLdsBudget;
   if (bytes < least) bytes = least;
   if (bytes < partials) bytes = partials;
