@@ -34,7 +34,7 @@ constexpr int kGateWaves = 4;
 constexpr int kGateKPerWave = kGateKPerBlock / kGateWaves;  // 64 = 4 steps of 16
 constexpr int kMaxColTiles = 4;                              // N <= 64
 constexpr int kMaxExpertsPerLane = MOE_MAX_EXPERTS / 64;
-constexpr int kFusedGateThreads = 256;     // one-launch routing: threads per workgroup
+constexpr int kFusedGateThreads = 512;     // one-launch routing: threads per workgroup
 constexpr int kGateScratch = kGateWaves * kMaxColTiles * 64 * 16;  // the waves' partial sums
 
 // Logits sit in LDS at logit_ld(E) per token; the selection reads only
