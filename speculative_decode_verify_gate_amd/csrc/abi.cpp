@@ -237,10 +237,10 @@ int launch_pass(const moe_shape *s, const LayerWeights &w, int L, const float *x
   a.lws2 = fd * s->n_shared;
 
   hipError_t err = hipSuccess;
-  a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true, s->n_experts);
+  a.lds_bytes = moe::expert_lds_bytes(n, s->d_model, bf16, true, s->n_experts, s->top_k);
   err = timed(MOE_K_UP, st, [&] { return moe::launch_up(a, bf16, st); });
   if (err == hipSuccess) {
-    a.lds_bytes = moe::expert_lds_bytes(n, s->d_ff, bf16, false, s->n_experts);
+    a.lds_bytes = moe::expert_lds_bytes(n, s->d_ff, bf16, false, s->n_experts, s->top_k);
     err = timed(MOE_K_DOWN, st, [&] { return moe::launch_down(a, bf16, st); });
   }
   if (err == hipSuccess)

@@ -114,53 +114,82 @@ __device__ inline int local_instance(const int32_t *__restrict__ idx, int slots,
 // The full compaction record of the routing entries idx[0 .. slots), which
 // are slots slot0 .. slot0+slots-1 of the pass (layout CompactLayout,
 // documented in moe_verify.h; the list holds pass slot ids), and U to
-// *n_unique (if given).  Called by one workgroup; scratch is at least
-// (2 * E + 1 + slots) ints of LDS that the caller does not use meanwhile.
+// *n_unique (if given).  Called by one workgroup of at least E threads;
+// scratch is record_lds_ints(E, slots) ints of LDS that the caller does not
+// use meanwhile.  Everything is parallel over experts or slots: offsets and
+// the distinct list come from one workgroup-wide exclusive scan of (count,
+// present), and a slot's place among its expert's slots is the number of
+// set bits below it in that expert's slot mask.
 __device__ inline void write_record(const int32_t *__restrict__ idx, int slots, int slot0,
                                     int E, int32_t *__restrict__ cmp,
                                     int32_t *__restrict__ n_unique, int *scratch) {
+  constexpr int kMaxWaves = 16;
+  __shared__ int wsum[kMaxWaves];
   const CompactLayout L{E, slots};
-  int *cnt = scratch;           // [E]
-  int *offs = cnt + E;          // [E + 1]
-  int *ev = offs + E + 1;       // [slots] expert of each slot (-1: none)
+  const int words = (slots + 31) >> 5;
+  int *cnt = scratch;                                // [E] counts, then offsets
+  int *ev = cnt + E;                                 // [slots] expert of each slot (-1: none)
+  uint32_t *mask = (uint32_t *)(ev + slots);         // [E][words] each expert's slots
   const int tid = threadIdx.x;
   const int nth = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
 
   for (int e = tid; e < E; e += nth) cnt[e] = 0;
+  for (int i = tid; i < E * words; i += nth) mask[i] = 0u;
   for (int s = tid; s < slots; s += nth) {
     const int v = idx[s];
     ev[s] = (v >= 0 && v < E) ? v : -1;
   }
   __syncthreads();
-  for (int s = tid; s < slots; s += nth)
-    if (ev[s] >= 0) atomicAdd(&cnt[ev[s]], 1);
+  for (int s = tid; s < slots; s += nth) {
+    const int e = ev[s];
+    if (e < 0) continue;
+    atomicAdd(&cnt[e], 1);
+    atomicOr(&mask[e * words + (s >> 5)], 1u << (s & 31));
+  }
   __syncthreads();
+  // exclusive scan over experts (thread e holds expert e) of count | present
+  // << 16; the counts sum to at most MOE_MAX_SLOTS, so the halves stay apart
+  const int c = tid < E ? cnt[tid] : 0;
+  const int mine = c | ((c > 0 ? 1 : 0) << 16);
+  int v = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == kWave - 1) wsum[wave] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < (nth >> 6); ++w) {
+    before += (w < wave) ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  const int excl = before + v - mine;
+  const int up = all >> 16;
+  if (tid < E) {
+    const int off = excl & 0xffff;
+    cnt[tid] = off;  // only this thread read cnt[tid]
+    cmp[L.counts() + tid] = c;
+    cmp[L.offs() + tid] = off;
+    if (c > 0) cmp[L.uniq() + (excl >> 16)] = tid;
+  }
+  for (int q = up + tid; q < E; q += nth) cmp[L.uniq() + q] = -1;
   if (tid == 0) {
-    // exclusive prefix sums of the counts and of presence (E <= 256)
-    int o = 0, up = 0;
-    for (int e = 0; e < E; ++e) {
-      offs[e] = o;
-      o += cnt[e];
-      if (cnt[e] > 0) cmp[L.uniq() + up++] = e;
-    }
-    offs[E] = o;
-    for (int q = up; q < E; ++q) cmp[L.uniq() + q] = -1;
+    cmp[L.offs() + E] = all & 0xffff;
     cmp[L.u()] = up;
     if (n_unique) *n_unique = up;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += nth) {
-    cmp[L.counts() + e] = cnt[e];
-    cmp[L.offs() + e] = offs[e];
-  }
-  if (tid == 0) cmp[L.offs() + E] = offs[E];
-  // a slot's place in its expert's list: slots before it with that expert
+  // a slot's place in its expert's list: its expert's slots below it
   for (int s = tid; s < slots; s += nth) {
     const int e = ev[s];
     if (e < 0) continue;
-    int rank = 0;
-    for (int q = 0; q < s; ++q) rank += (ev[q] == e) ? 1 : 0;
-    cmp[L.list() + offs[e] + rank] = slot0 + s;
+    const uint32_t *me = mask + e * words;
+    int rank = __popc(me[s >> 5] & ((1u << (s & 31)) - 1u));
+    for (int w = 0; w < (s >> 5); ++w) rank += __popc(me[w]);
+    cmp[L.list() + cnt[e] + rank] = slot0 + s;
   }
   __syncthreads();  // scratch is free again
 }

@@ -87,6 +87,7 @@ __device__ inline u32x4 ldg16_once(const unsigned char *p) {
 }
 
 constexpr int kBlock = kWavesPerBlock * kWave;    // threads per workgroup
+static_assert(kBlock >= MOE_MAX_EXPERTS, "the record writer takes one expert per thread");
 
 // With 16-token tiles (CTMAX == 1) the B operand is not staged in LDS: every
 // lane loads its own token column's 16 bytes (8 bf16 or 4 fp32 elements) per

@@ -37,6 +37,13 @@ struct CompactLayout {
   __host__ __device__ int total() const { return 2 + 3 * E + slots; }
 };
 
+// LDS ints the compaction-record writer needs for E experts and `slots`
+// routing entries: a count per expert (then its offset), the valid expert
+// of each slot, and per expert a bit mask of its slots.
+__host__ __device__ constexpr int record_lds_ints(int E, int slots) {
+  return E + slots + E * ((slots + 31) / 32);
+}
+
 struct ExpertArgs {
   const void *w13, *w2, *ws13, *ws2;
   const float *x;         // [N][d]
@@ -127,14 +134,14 @@ hipError_t launch_pack(const void *src, void *dst, int R, int K, long long n_mat
 // Dynamic LDS for the expert kernels at this token count: the partial sums
 // (16-token tiles, which read their token columns directly), or K windows of
 // up to min(N, 64) staged token rows.
-inline int expert_lds_bytes(int N, int K, bool bf16, bool up, int E) {
+inline int expert_lds_bytes(int N, int K, bool bf16, bool up, int E, int k) {
   const int eb = bf16 ? 2 : 4;
   const int ctmax = N > kTile ? 4 : 1;
-  // the partial sums of 16-token tiles, or, in workgroup 0 of the up kernel,
-  // the compaction scratch: 2E+1 counts and offsets and one int per slot
+  // the partial sums of 16-token tiles, or, in a record-writing workgroup of
+  // the up kernel, the compaction scratch (at most a pass's N k slots)
+  const size_t record = up ? (size_t)record_lds_ints(E, N * k) * sizeof(int) : 0;
   if (ctmax == 1) {
     const size_t partials = (size_t)(up ? 2 : 1) * kWavesPerBlock * kWave * 16;
-    const size_t record = up ? (size_t)(2 * E + 1 + MOE_MAX_SLOTS) * sizeof(int) : 0;
     return (int)(partials > record ? partials : record);
   }
   const int step = bf16 ? 32 : 16;
@@ -154,6 +161,7 @@ inline int expert_lds_bytes(int N, int K, bool bf16, bool up, int E) {
   size_t bytes = whole < (size_t)kLdsBudget ? whole : (size_t)kLdsBudget;
   if (bytes < least) bytes = least;
   if (bytes < partials) bytes = partials;
+  if (bytes < record) bytes = record;
   return (int)bytes;
 }
 
@@ -166,7 +174,10 @@ constexpr int expert_lds_bound(bool wide) {
                      cmax(4 * kTile * (kWavesPerBlock * kSpc * 16 + kLdsPad) * 4,
                           2 * kWavesPerBlock * 4 * kWave * 16))
               : cmax(2 * kWavesPerBlock * kWave * 16,
-                     (2 * MOE_MAX_EXPERTS + 1 + MOE_MAX_SLOTS) * (int)sizeof(int));
+                     record_lds_ints(MOE_MAX_EXPERTS, MOE_MAX_SLOTS) * (int)sizeof(int));
 }
+static_assert(expert_lds_bound(true) >=
+                  record_lds_ints(MOE_MAX_EXPERTS, MOE_MAX_SLOTS) * (int)sizeof(int),
+              "a wide up kernel's LDS must also hold the compaction scratch");
 
 }  // namespace moe

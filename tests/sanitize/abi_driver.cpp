@@ -73,7 +73,13 @@ static void check_expert(const ExpertArgs &a) {
     CHECK(a.E < 8 * a.k || (a.n_routed + 1) / 2 < 2 * a.k);
   }
 }
-hipError_t launch_up(const ExpertArgs &a, bool, hipStream_t) { check_expert(a); ++g_launches; return hipSuccess; }
+hipError_t launch_up(const ExpertArgs &a, bool, hipStream_t) {
+  check_expert(a);
+  // a record-writing workgroup's scratch fits the dynamic LDS of the launch
+  CHECK(a.dedup == 0 || a.lds_bytes >= record_lds_ints(a.E, a.N * a.k) * (int)sizeof(int));
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_down(const ExpertArgs &a, bool, hipStream_t) { check_expert(a); ++g_launches; return hipSuccess; }
 hipError_t launch_combine(const ExpertArgs &a, hipStream_t) { check_expert(a); ++g_launches; return hipSuccess; }
 hipError_t launch_pack(const void *, void *, int R, int K, long long n, bool, hipStream_t) {
