@@ -393,17 +393,23 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 //   stat:   chunk max m_c and sum of exp(z - m_c), z = logit / T; the row's
 //           histogram and counters cleared;
 //   prob:   the row's max and sum (a fixed-order reduction of the chunks'
-//           pairs, so every workgroup of the row gets the same bits),
-//           P = exp(z - M) / S written to the output, and (top-p) the
-//           chunk's mass histogram of bits 29-22 added into the row's
-//           (64-bit integer atomics: the sum does not depend on their
-//           order); the row's last workgroup selects the bin;
-//   gather: the chunk's entries in the selected bin (candidates) appended
-//           to the row's candidate list; the row's last workgroup finds K
-//           among them (bits 21-10, then 9-0), the number of ties at K to
+//           pairs, so every workgroup of the row gets the same bits) and
+//           P = exp(z - M) / S.  Without top-p P is the output.  With it,
+//           the chunk's mass histogram of bits 29-22 is added into the
+//           row's (64-bit integer atomics: the sum does not depend on their
+//           order) and the row's last workgroup selects the bin and hands
+//           M and S on; P itself is not stored;
+//   gather: P again from the logits, M and S (the same bits), the chunk's
+//           entries in the selected bin (candidates) appended to the row's
+//           candidate list; the row's last workgroup finds the last kept
+//           token among them: for a short list by ranking every candidate
+//           in the order and a running sum of the masses in that order,
+//           else by K (bits 21-10, then 9-0), the number of ties at K to
 //           keep and, when only some are kept, the index cut (bits 23-12,
 //           then 11-0 of the tied indices, by counts);
-//   write:  the kept entries renormalised, the rest zeroed.
+//   write:  P again, the kept entries renormalised, the rest zeroed.
+// Each launch issues its logits loads before the loads of what the
+// previous launch handed on, so the two round trips overlap.
 // "The row's last workgroup" is the last one to arrive at the row's
 // arrival counter; what the others hand over to it in the same launch is
 // written and read with coherent accesses.
@@ -423,7 +429,8 @@ struct FilterArgs {
   float2 *stat;        // [rows][chunks]: (chunk max, sum of exp relative to it)
   uint64_t *rowhist;   // [rows][256] first-level mass histogram
   uint64_t *cand;      // [rows][V] candidates: probability bits | index << 32
-  uint64_t *state;     // [rows][8]: prefix, mask, mass above, target; K, index cut, kept mass
+  uint64_t *state;     // [rows][8]: prefix, mask, mass above, target; K, index cut, kept
+                       // mass; the row's M and S (float bits, S in the high half)
   unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
 };
 
@@ -523,6 +530,20 @@ __device__ inline float2 row_stat(const float2 *st, int chunks, float *fs) {
   }
   S = block_all(S, fs, [](float x, float y) { return x + y; });
   return make_float2(m, S);
+}
+
+// P of a logit given the row's max M and sum S of exp(z - M): every launch
+// computes it with this one expression, so all of them get the same bits.
+// exp(z - M) <= 1 and 1 / S <= 1 (S >= 1: the max's own term), so P <= 1
+// and its bits 31-30 are zero; a -inf fill (past the row) gives 0.
+__device__ inline float prob_of(float logit, float temperature, float2 ms) {
+  return expf(logit * (1.0f / temperature) - ms.x) * (1.0f / ms.y);
+}
+
+// The row's M and S as the prob launch's last workgroup handed them on.
+__device__ inline float2 row_ms(const uint64_t *st) {
+  const uint64_t b = st[7];
+  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
 }
 
 __global__ __launch_bounds__(kFThreads) void filter_stat_kernel(FilterArgs a) {
@@ -659,17 +680,16 @@ template <bool HIST>
 __global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
   const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   __shared__ float fs[kFWaves];
-  const float2 ms = row_stat(a.stat + (size_t)row * a.chunks, a.chunks, fs);
   float v[kFPer];
   const int c0 = c * kFChunk;
   load_chunk(a.logits + (size_t)row * a.V, a.V, c0, v, -INFINITY);
-  // exp(z - M) <= 1 and 1 / S <= 1 (S >= 1: the max's own term), so P <= 1
-  // and its bits 31-30 are zero; 0 past the row
-  const float inv_t = 1.0f / a.temperature, inv_s = 1.0f / ms.y;
+  const float2 ms = row_stat(a.stat + (size_t)row * a.chunks, a.chunks, fs);
 #pragma unroll
-  for (int k = 0; k < kFPer; ++k) v[k] = expf(v[k] * inv_t - ms.x) * inv_s;
-  store_chunk(a.probs + (size_t)row * a.V, a.V, c0, v);
-  if (!HIST) return;
+  for (int k = 0; k < kFPer; ++k) v[k] = prob_of(v[k], a.temperature, ms);
+  if (!HIST) {
+    store_chunk(a.probs + (size_t)row * a.V, a.V, c0, v);
+    return;
+  }
   // the first level: mass per value of bits 29-22, one LDS copy per wave
   __shared__ unsigned long long lh[kFWaves][256];
   for (int i = tid; i < kFWaves * 256; i += kFThreads) lh[i / 256][i % 256] = 0ull;
@@ -695,6 +715,60 @@ __global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
     st[1] = mask;
     st[2] = above;
     st[3] = target;
+    st[7] = (uint64_t)__float_as_uint(ms.x) | ((uint64_t)__float_as_uint(ms.y) << 32);
+  }
+}
+
+// The row's last workgroup after the gather, for at most kDirect
+// candidates: each candidate's rank in the order (probability descending,
+// index ascending) by counting the candidates before it, their masses in
+// that order, a running sum, and the first rank at which the mass above
+// the bin plus the running sum reaches the target: that token is the last
+// one kept, its probability is K and its index the cut (the ties at K
+// after it in the order have larger indices).
+// ord and by_rank are LDS arrays of kDirect entries each (the radix
+// path's bins, which this path does not use).
+constexpr uint32_t kDirect = 512;
+__device__ inline void resolve_direct(const FilterArgs &a, int row, const uint64_t *cand, uint32_t n,
+                                      unsigned long long *ord, unsigned long long *by_rank) {
+  __shared__ uint64_t scratch[kWavesV];
+  const int tid = threadIdx.x;
+  uint64_t *st = a.state + (size_t)row * 8;
+  const uint64_t above = st[2], target = st[3];
+  for (uint32_t i = tid; i < n; i += kFThreads) {
+    const uint64_t e = load_coherent64(cand + i);
+    ord[i] = ((uint64_t)(uint32_t)e << 32) | (0xFFFFFFFFu - (uint32_t)(e >> 32));
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < n; i += kFThreads) {
+    const uint64_t o = ord[i];
+    uint32_t r = 0;
+    for (uint32_t q = 0; q < n; ++q) r += ord[q] > o ? 1u : 0u;  // keys are distinct
+    by_rank[r] = o;
+  }
+  __syncthreads();
+  static_assert(kDirect == 2 * kFThreads, "two ranks per thread");
+  const uint32_t r0 = 2 * tid, r1 = r0 + 1;
+  const uint64_t m0 = r0 < n ? mass_of(__uint_as_float((uint32_t)(by_rank[r0] >> 32))) : 0;
+  const uint64_t m1 = r1 < n ? mass_of(__uint_as_float((uint32_t)(by_rank[r1] >> 32))) : 0;
+  uint64_t all;
+  const uint64_t before = above + block_scan(m0 + m1, scratch, &all) - (m0 + m1);
+  // exactly one rank crosses: the bin holds the crossing, so the running
+  // sum over all candidates reaches the target
+  uint32_t last = 0xFFFFFFFFu;
+  uint64_t kept = 0;
+  if (r0 < n && before < target && before + m0 >= target) {
+    last = r0;
+    kept = before + m0;
+  } else if (r1 < n && before + m0 < target && before + m0 + m1 >= target) {
+    last = r1;
+    kept = before + m0 + m1;
+  }
+  if (last != 0xFFFFFFFFu) {
+    const uint64_t o = by_rank[last];
+    st[4] = o >> 32;
+    st[5] = 0xFFFFFFFFu - (uint32_t)o;
+    st[6] = kept;
   }
 }
 
@@ -702,6 +776,11 @@ __global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
 // and the index cut, from the row's n candidates (coherent loads).
 __device__ inline void resolve_row(const FilterArgs &a, int row, const uint64_t *cand, uint32_t n) {
   __shared__ unsigned long long lh[4096];  // mass bins, then count bins
+  static_assert(2 * kDirect <= 4096, "the direct path's arrays fit the bins");
+  if (n <= kDirect) {
+    resolve_direct(a, row, cand, n, lh, lh + kDirect);
+    return;
+  }
   uint32_t *lc = (uint32_t *)lh;
   const int tid = threadIdx.x;
   uint64_t *st = a.state + (size_t)row * 8;
@@ -763,11 +842,14 @@ __device__ inline void resolve_row(const FilterArgs &a, int row, const uint64_t 
 
 __global__ __launch_bounds__(kFThreads) void filter_gather_kernel(FilterArgs a) {
   const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const uint64_t *st = a.state + (size_t)row * 8;
-  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
   float p[kFPer];
   const int c0 = c * kFChunk;
-  load_chunk(a.probs + (size_t)row * a.V, a.V, c0, p, 0.f);
+  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, p, -INFINITY);
+  const uint64_t *st = a.state + (size_t)row * 8;
+  const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
+  const float2 ms = row_ms(st);
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) p[k] = prob_of(p[k], a.temperature, ms);
   uint32_t mine = 0;
 #pragma unroll
   for (int k = 0; k < kFPer; ++k)
@@ -797,14 +879,17 @@ __global__ __launch_bounds__(kFThreads) void filter_gather_kernel(FilterArgs a) 
 
 __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
   const int row = blockIdx.y, c = blockIdx.x;
+  const int c0 = c * kFChunk;
+  float p[kFPer];
+  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, p, -INFINITY);
   const uint64_t *st = a.state + (size_t)row * 8;
   const float pk = __uint_as_float((uint32_t)st[4]);  // the last kept probability
   const uint32_t cut = (uint32_t)st[5];                // ties kept up to this index
   const float total = (float)((double)st[6] / kMassQuant);
+  const float2 ms = row_ms(st);
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) p[k] = prob_of(p[k], a.temperature, ms);
   float *out = a.probs + (size_t)row * a.V;
-  const int c0 = c * kFChunk;
-  float p[kFPer];
-  load_chunk(out, a.V, c0, p, 0.f);
 #pragma unroll
   for (int g = 0; g < kFGroups; ++g) {
     const uint32_t j = (uint32_t)entry_of(c0, g);
@@ -826,6 +911,7 @@ size_t filter_ws_bytes(int rows, int V) {
   const size_t ch = (size_t)filter_chunks(V);
   return align_up((size_t)rows * ch * sizeof(float2), 256) +
          align_up((size_t)rows * 256 * sizeof(uint64_t), 256) +
+
          align_up((size_t)rows * V * sizeof(uint64_t), 256) +
          align_up((size_t)rows * 8 * sizeof(uint64_t), 256) +
          align_up((size_t)rows * 4 * sizeof(unsigned), 256);

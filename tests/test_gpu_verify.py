@@ -1,6 +1,8 @@
 """GPU verification round (moe_verify_gate) against the CPU oracle, through
 the C ABI.  Decisions are exact on both sides, so n_accepted and the tokens
 must match bit for bit."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -313,6 +315,47 @@ def test_filter_unaligned_rows_and_single_finite_logits():
     # the same with top_p = 1: both tied tokens share the mass
     full = B.verify_probs(dev, 0.8, 1.0, out=out).cpu().numpy()
     assert full[4, 100] == full[4, 9000] == 0.5
+
+
+def _exact_nucleus(P, top_p):
+    """The filter's decision written out on given fp32 probabilities P
+    [V]: integer masses floor(P 2^52), target ceil(top_p W) in fp64 with
+    top_p as the fp32 the call takes, the order (P descending, index
+    ascending), the first prefix whose mass reaches the target, and the kept
+    entries divided by that mass in fp32."""
+    m = np.floor(P.astype(np.float64) * 2.0 ** 52).astype(np.uint64)
+    W = int(m.sum(dtype=np.uint64))
+    target = max(1, math.ceil(float(np.float32(top_p)) * float(W)))
+    order = np.lexsort((np.arange(P.size), -P))
+    run = np.cumsum(m[order], dtype=np.uint64)
+    last = int(np.searchsorted(run, np.uint64(target), side="left"))
+    total = np.float32(float(run[last]) / 2.0 ** 52)
+    out = np.zeros_like(P)
+    keep = order[: last + 1]
+    out[keep] = P[keep] / total
+    return out
+
+
+def test_filter_decision_is_exact_on_its_own_probabilities():
+    """The kept set and values are exactly what the filter's integer-mass
+    rule gives on the fp32 probabilities the same library computes without
+    top-p (the same expression, the same row max and sum): bit for bit,
+    whether the row's boundary bin holds a few candidates (ranked directly)
+    or many (radix selection: long runs of exact ties)."""
+    rng = np.random.default_rng(53)
+    V = 102400
+    lg = _logit_rows(rng, 8, V)
+    lg[4:6, : V // 3] = lg[4:6, :1]                # a third of the row tied
+    lg[6] = 1.5                                    # every entry tied
+    lg[7] = np.round(lg[7] * 4) / 4                # many small tie groups
+    dev = torch.from_numpy(lg).cuda()
+    for T, top_p in ((0.7, 0.9), (1.0, 0.5), (0.3, 0.95), (1.0, 0.3)):
+        _say(f"[filter] exact decision T={T} top_p={top_p}")
+        P = B.verify_probs(dev, T, 1.0).cpu().numpy()
+        got = B.verify_probs(dev, T, top_p).cpu().numpy()
+        for r in range(lg.shape[0]):
+            want = _exact_nucleus(P[r], top_p)
+            np.testing.assert_array_equal(got[r].view(np.uint32), want.view(np.uint32))
 
 
 def test_filter_nucleus_hand_computed():
