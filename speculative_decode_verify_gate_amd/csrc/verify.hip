@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 //           candidate list; the row's last workgroup finds the last kept
 //           token among them: for a short list by ranking every candidate
 //           in the order and a running sum of the masses in that order,
-//           else by K (bits 21-10, then 9-0), the number of ties at K to
+//           else by K (bits 21-11, then 10-0), the number of ties at K to
 //           keep and, when only some are kept, the index cut (bits 23-12,
 //           then 11-0 of the tied indices, by counts);
 //   write:  P again, the kept entries renormalised, the rest zeroed.
@@ -775,8 +775,10 @@ __device__ inline void resolve_direct(const FilterArgs &a, int row, const uint64
 // The row's last workgroup after the gather: K, the number of ties to keep
 // and the index cut, from the row's n candidates (coherent loads).
 __device__ inline void resolve_row(const FilterArgs &a, int row, const uint64_t *cand, uint32_t n) {
-  __shared__ unsigned long long lh[4096];  // mass bins, then count bins
-  static_assert(2 * kDirect <= 4096, "the direct path's arrays fit the bins");
+  // mass bins (11-bit levels), then count bins (12-bit levels of 32-bit
+  // counts): 16 KB, so the gather launch keeps enough workgroups resident
+  __shared__ unsigned long long lh[2048];
+  static_assert(2 * kDirect <= 2048, "the direct path's arrays fit the bins");
   if (n <= kDirect) {
     resolve_direct(a, row, cand, n, lh, lh + kDirect);
     return;
@@ -786,24 +788,25 @@ __device__ inline void resolve_row(const FilterArgs &a, int row, const uint64_t 
   uint64_t *st = a.state + (size_t)row * 8;
   uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
   uint64_t above = st[2], target = st[3];
-  // bits 21-10
-  for (int i = tid; i < 4096; i += kFThreads) lh[i] = 0ull;
+  // bits 21-11
+  for (int i = tid; i < 2048; i += kFThreads) lh[i] = 0ull;
   __syncthreads();
   for (uint32_t i = tid; i < n; i += kFThreads) {
     const uint32_t key = (uint32_t)load_coherent64(cand + i);
-    atomicAdd(&lh[(key >> 10) & 4095u], (unsigned long long)mass_of(__uint_as_float(key)));
+    atomicAdd(&lh[(key >> 11) & 2047u], (unsigned long long)mass_of(__uint_as_float(key)));
   }
   __syncthreads();
-  select_level<4096, false>((const uint64_t *)lh, 10, target, prefix, mask, above);
-  // bits 9-0 of the candidates under that prefix
-  for (int i = tid; i < 1024; i += kFThreads) lh[i] = 0ull;
+  select_level<2048, false>((const uint64_t *)lh, 11, target, prefix, mask, above);
+  // bits 10-0 of the candidates under that prefix
+  __syncthreads();  // every thread has read its bins
+  for (int i = tid; i < 2048; i += kFThreads) lh[i] = 0ull;
   __syncthreads();
   for (uint32_t i = tid; i < n; i += kFThreads) {
     const uint32_t key = (uint32_t)load_coherent64(cand + i);
-    if ((key & mask) == prefix) atomicAdd(&lh[key & 1023u], (unsigned long long)mass_of(__uint_as_float(key)));
+    if ((key & mask) == prefix) atomicAdd(&lh[key & 2047u], (unsigned long long)mass_of(__uint_as_float(key)));
   }
   __syncthreads();
-  const uint64_t bin = select_level<1024, false>((const uint64_t *)lh, 0, target, prefix, mask, above);
+  const uint64_t bin = select_level<2048, false>((const uint64_t *)lh, 0, target, prefix, mask, above);
   const uint32_t K = prefix;                       // the last kept probability's bits
   const uint64_t mk = mass_of(__uint_as_float(K));  // > 0: the target lies in positive mass
   const uint64_t ties = bin / mk;                  // all of equal mass mk
