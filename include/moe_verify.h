@@ -367,8 +367,9 @@ const char *moe_status_string(int status);
 /* Per-kernel timing, for measurement.  While enabled, every kernel of a
  * selected kind that the calls above launch is bracketed by a pair of HIP
  * events recorded on the call's stream, and moe_timing_read() adds up the
- * elapsed time per kernel kind.  Each event pair adds a few microseconds of
- * idle time around its kernel, so select only the kinds being measured.
+ * elapsed time per kernel kind.  The events are created without a
+ * system-scope fence (they only time), yet each pair still adds some idle
+ * time around its kernel, so select only the kinds being measured.
  * Kernel kinds (bit positions of the mask, indices into the arrays): */
 enum moe_kernel_kind {
   MOE_K_GATE = 0,    /* gate logits, split over K; when the partial logits of

@@ -114,8 +114,11 @@ struct Timing {
       pool.pop_back();
       return e;
     }
+    // timing only: no system-scope fence when the event is recorded, so
+    // the pair does not add a cache write-back and invalidation around the
+    // kernel it brackets (nothing reads memory through these events)
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
   }
 };
