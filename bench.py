@@ -875,7 +875,10 @@ def compact_sweep(sweep):
 
 def write_details(path, doc):
     """The full record of a run (sweep, calibration, draft lengths,
-    verification round, kernels, CPU baseline) as one JSON file."""
+    verification round, kernels, CPU baseline) as one JSON file, when a
+    path is given."""
+    if not path:
+        return
     try:
         os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
         with open(path, "w") as f:
@@ -923,9 +926,9 @@ def main():
                          "a profiler run)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the fused-stack leg after the timed steps")
-    ap.add_argument("--details", default=os.path.join(ROOT, "gpurun_out", "bench_details.json"),
+    ap.add_argument("--details", default=None,
                     help="file for the full record of the run (the last stdout line is "
-                         "the compact headline)")
+                         "the compact headline); none is written without it")
     ap.add_argument("--timeline", default=None,
                     help="comma-separated pass sizes: instead of the bench line, K steps of "
                          "route + pass per engine at each size, queued while the GPU is held, "
