@@ -160,10 +160,54 @@ SHORT_PASS_US = 50.0   # passes shorter than this get at least SHORT_PASS_REPS r
 SHORT_PASS_REPS = 200
 
 
-def run_sweep(cfg, eng, layers, xs, n_values, reps, top_up=True):
+class SweepLog:
+    """Finished sweep points as JSON lines keyed by (leg, workload, rho, n,
+    passes): a run given the same file (--resume) takes the points it finds
+    there instead of measuring them again and appends the ones it measures,
+    so an interrupted sweep continues where it stopped.  A line cut short by
+    the interruption is ignored."""
+
+    def __init__(self, path):
+        self.path = path
+        self.done = {}
+        if path and os.path.exists(path):
+            with open(path) as f:
+                for line in f:
+                    try:
+                        d = json.loads(line)
+                        self.done[self._k(d["key"])] = d["record"]
+                    except (json.JSONDecodeError, KeyError, TypeError):
+                        continue
+
+    @staticmethod
+    def _k(key):
+        return json.dumps(key, sort_keys=True)
+
+    def get(self, key):
+        return self.done.get(self._k(key))
+
+    def put(self, key, rec):
+        if not self.path:
+            return
+        self.done[self._k(key)] = rec
+        os.makedirs(os.path.dirname(os.path.abspath(self.path)), exist_ok=True)
+        with open(self.path, "a+b") as f:
+            # a line cut short by an interruption gets its end first, so the
+            # new record starts a line of its own
+            if f.seek(0, os.SEEK_END) > 0:
+                f.seek(-1, os.SEEK_END)
+                if f.read(1) != b"\n":
+                    f.write(b"\n")
+            f.write((json.dumps({"key": key, "record": rec}) + "\n").encode())
+            f.flush()
+            os.fsync(f.fileno())
+
+
+def run_sweep(cfg, eng, layers, xs, n_values, reps, top_up=True, points=None):
     """Per n: reps passes per engine (topped up to SHORT_PASS_REPS when an
     engine's median pass is under SHORT_PASS_US), each on the next layer of
-    the rotation, each on its own hidden states.  Returns per-n records."""
+    the rotation, each on its own hidden states.  Returns per-n records;
+    with `points` (a SweepLog), n already there is taken from it."""
     out = []
     nL = len(layers)
     turn = 0
@@ -196,6 +240,12 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps, top_up=True):
 
     for n in n_values:
         N = cfg.tokens(n)
+        key = {"leg": "sweep", "workload": cfg.name, "rho": cfg.rho, "n": n, "passes": reps}
+        done = points.get(key) if points else None
+        if done is not None:
+            out.append(done)
+            log(f"  n={n:2d} taken from the sweep log")
+            continue
         y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
         ev = batch(n, y, range(reps))
         short = min(float(np.median([rec[name][1].elapsed_time(rec[name][2]) * 1e3 for rec in ev]))
@@ -234,6 +284,8 @@ def run_sweep(cfg, eng, layers, xs, n_values, reps, top_up=True):
         # r(n): effective routed-byte bandwidth of dedup over that of per-slot
         r["r"] = round(r["dedup"]["routed_GBs"] / r["perslot"]["routed_GBs"], 4)
         r["dedup_faster"] = r["dedup"]["us"] < r["perslot"]["us"]
+        if points:
+            points.put(key, r)
         out.append(r)
         log(f"  n={n:2d} perslot {r['perslot']['us']:8.1f} us {r['perslot']['GBs']:7.0f} GB/s | "
             f"dedup {r['dedup']['us']:8.1f} us {r['dedup']['GBs']:7.0f} GB/s | "
@@ -437,13 +489,63 @@ def calibration_json(calib):
                            for n, rec in calib["per_n"].items()}}
 
 
-def rho_sweep(cfg, eng, layers, stack, calib, reps):
+def rho_point(cfg, eng, layers, stack, reps, rho, ri, n):
+    """The measurements of one (rho, n) of the stack sweep: median stack-pass
+    times (route only, route + per-slot, route + dedup), the mean U of the
+    dedup layer passes, and the fused stack calls."""
+    nL = len(layers)
+    Be = expert_bytes(cfg)
+    N = cfg.tokens(n)
+    y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
+    nu = torch.zeros((reps * nL,), dtype=torch.int32, device="cuda")
+    xs = [synth.make_hidden(cfg, n, rep, "cuda", rho=rho, rho_index=ri) for rep in range(reps)]
+    t = {"route": [], "perslot": [], "dedup": []}
+    evs = []
+    for rep in range(reps):
+        x = xs[rep]
+        row = {}
+        for name in ("route", "perslot", "dedup"):
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            # the host queues the whole stack pass while the GPU waits
+            hold_gpu(0.1 * nL)
+            e0.record()
+            for L in range(nL):
+                idx, w = eng.route(layers[L], x)
+                if name == "perslot":
+                    eng.perslot(layers[L], x, idx, w, y)
+                elif name == "dedup":
+                    B.expert_pass_dedup(eng.shape, layers[L], x, idx, w, y=y,
+                                        n_unique=nu[rep * nL + L:rep * nL + L + 1],
+                                        ws=eng.ws_dd)
+            e1.record()
+            row[name] = (e0, e1)
+        evs.append(row)
+    torch.cuda.synchronize()
+    for row in evs:
+        for name, (e0, e1) in row.items():
+            t[name].append(e0.elapsed_time(e1) * 1e3)
+    U = nu.cpu().numpy().astype(np.float64)
+    fz = fused_stack_leg(cfg, stack, [n], reps, rho=rho, rho_index=ri)[n]
+    fused = {"perslot_stack_us": round(fz["perslot"], 1),
+             "dedup_stack_us": round(fz["dedup"], 1),
+             "perslot_layer_us": round(fz["perslot"] / nL, 2),
+             "dedup_layer_us": round(fz["dedup"] / nL, 2),
+             "U_mean": round(float(fz["U"].mean()), 2),
+             "perslot_GBs": round((N * cfg.k + cfg.S) * Be * nL / fz["perslot"] / 1e3, 1),
+             "dedup_GBs": round((fz["U"].mean() + cfg.S) * Be * nL / fz["dedup"] / 1e3, 1)}
+    return {"u_bar": float(U.mean()) / (N * cfg.k), "U_mean": round(float(U.mean()), 2),
+            "stack_us": {k: float(np.median(v)) for k, v in t.items()}, "fused": fused}
+
+
+def rho_sweep(cfg, eng, layers, stack, calib, reps, points=None):
     """The layer stack at each rho: per (rho, n), `reps` stack passes per
     engine, each pass running every layer on the same hidden states (route
     + expert pass per layer).  A route-only stack pass is timed too, so the
     expert-pass share is the difference.  U is read from the dedup engine's
     device counter of every layer pass.  The same passes are then timed as
-    one fused stack call per engine (moe_stack_pass)."""
+    one fused stack call per engine (moe_stack_pass).  With `points` (a
+    SweepLog), the measurements of a (rho, n) already there are taken from
+    it; what follows from the calibration is computed again."""
     nL = len(layers)
     Be = expert_bytes(cfg)
     out = []
@@ -452,54 +554,24 @@ def rho_sweep(cfg, eng, layers, stack, calib, reps):
         recs = []
         for n in ns:
             N = cfg.tokens(n)
-            y = torch.empty((N, cfg.d), dtype=torch.float32, device="cuda")
-            nu = torch.zeros((reps * nL,), dtype=torch.int32, device="cuda")
-            xs = [synth.make_hidden(cfg, n, rep, "cuda", rho=rho, rho_index=ri)
-                  for rep in range(reps)]
-            t = {"route": [], "perslot": [], "dedup": []}
-            evs = []
-            for rep in range(reps):
-                x = xs[rep]
-                row = {}
-                for name in ("route", "perslot", "dedup"):
-                    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-                    # the host queues the whole stack pass while the GPU waits
-                    hold_gpu(0.1 * nL)
-                    e0.record()
-                    for L in range(nL):
-                        idx, w = eng.route(layers[L], x)
-                        if name == "perslot":
-                            eng.perslot(layers[L], x, idx, w, y)
-                        elif name == "dedup":
-                            B.expert_pass_dedup(eng.shape, layers[L], x, idx, w, y=y,
-                                                n_unique=nu[rep * nL + L:rep * nL + L + 1],
-                                                ws=eng.ws_dd)
-                    e1.record()
-                    row[name] = (e0, e1)
-                evs.append(row)
-            torch.cuda.synchronize()
-            for row in evs:
-                for name, (e0, e1) in row.items():
-                    t[name].append(e0.elapsed_time(e1) * 1e3)
-            U = nu.cpu().numpy().astype(np.float64)
-            u_bar = float(U.mean()) / (N * cfg.k)
-            med = {k: float(np.median(v)) for k, v in t.items()}
+            key = {"leg": "rho", "workload": cfg.name, "rho": rho, "n": n, "passes": reps,
+                   "layers": nL}
+            m = points.get(key) if points else None
+            if m is None:
+                m = rho_point(cfg, eng, layers, stack, reps, rho, ri, n)
+                if points:
+                    points.put(key, m)
+            else:
+                log(f"  rho={rho:.2f} n={n:2d} taken from the sweep log")
+            u_bar, med, rec_fused = m["u_bar"], m["stack_us"], m["fused"]
             ps = (med["perslot"] - med["route"]) / nL
             dd = (med["dedup"] - med["route"]) / nL
             r, r_sd, sav, sav_sd, iv_sd, trace = predict_from_calibration(cfg, calib, n, u_bar)
-            fz = fused_stack_leg(cfg, stack, [n], reps, rho=rho, rho_index=ri)[n]
-            rec_fused = {"perslot_stack_us": round(fz["perslot"], 1),
-                         "dedup_stack_us": round(fz["dedup"], 1),
-                         "perslot_layer_us": round(fz["perslot"] / nL, 2),
-                         "dedup_layer_us": round(fz["dedup"] / nL, 2),
-                         "U_mean": round(float(fz["U"].mean()), 2),
-                         "perslot_GBs": round((N * cfg.k + cfg.S) * Be * nL / fz["perslot"] / 1e3, 1),
-                         "dedup_GBs": round((fz["U"].mean() + cfg.S) * Be * nL / fz["dedup"] / 1e3, 1)}
-            rec = {"n": n, "u_bar": round(u_bar, 4), "U_mean": round(float(U.mean()), 2),
+            rec = {"n": n, "u_bar": round(u_bar, 4), "U_mean": m["U_mean"],
                    "stack_us": {k: round(v, 1) for k, v in med.items()},
                    "perslot_layer_us": round(ps, 2), "dedup_layer_us": round(dd, 2),
                    "perslot_GBs": round((N * cfg.k + cfg.S) * Be / ps / 1e3, 1),
-                   "dedup_GBs": round((U.mean() + cfg.S) * Be / dd / 1e3, 1),
+                   "dedup_GBs": round((m["U_mean"] + cfg.S) * Be / dd / 1e3, 1),
                    "saving_us": round(ps - dd, 2),
                    "r": round(r, 4), "r_sd": round(r_sd, 4),
                    "dedup_faster": dd < ps, "u_lt_r": u_bar < r,
@@ -926,6 +998,9 @@ def main():
                          "a profiler run)")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the fused-stack leg after the timed steps")
+    ap.add_argument("--resume", default=None,
+                    help="sweep log (JSON lines): points of the n sweep and of the rho sweep "
+                         "found there are not measured again, measured ones are appended")
     ap.add_argument("--details", default=None,
                     help="file for the full record of the run (the last stdout line is "
                          "the compact headline); none is written without it")
@@ -1003,7 +1078,8 @@ def main():
         log("[bench] sweep warmup")
         run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 5, top_up=False)  # 10 passes per engine
         log("[bench] sweep")
-        sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps)
+        points = SweepLog(args.resume) if args.resume else None
+        sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps, points=points)
         log("[bench] dedup calibration on crafted routings")
         calib = calibrate(cfg, eng, layers, xs, args.reps, sweep, args.calib_reps)
         for r in sweep:
@@ -1027,7 +1103,8 @@ def main():
                            f"n = 1..{max(cfg.n_values)}",
                "single_layer_sweep": sweep, "calibration": calibration_json(calib),
                "bandwidth_sensitivity": bandwidth_sensitivity(cfg, calib, sweep),
-               "by_rho": rho_sweep(cfg, eng, layers, stack, calib, args.stack_reps)}
+               "by_rho": rho_sweep(cfg, eng, layers, stack, calib, args.stack_reps,
+                                   points=points)}
         write_details(args.details, doc)
         print(json.dumps(rho_summary(doc)), flush=True)
         return
