@@ -18,7 +18,8 @@
 // floor(W r / 2^32), so sums do not depend on their order.
 //
 // Layout of the work: a workgroup takes a 2048-entry chunk of the vocabulary
-// of one sequence (coalesced loads, 256 threads x 8).  Sampling: each
+// of one sequence, each thread 8 consecutive entries (two 16-byte loads
+// where the rows allow).  Sampling: each
 // workgroup finds the first rejection itself (2 gamma scalar loads) and
 // writes the integer weight sum of its chunk of the row to draw from.
 // Greedy: a workgroup per (position, chunk) writes the chunk's argmax as one
@@ -183,6 +184,27 @@ __device__ inline uint64_t draw_weight(const VerifyArgs &a, int s, int istar, bo
   return quantize(d > 0.f ? d : 0.f);
 }
 
+// Entries j0 .. j0+kVPer-1 of a row, 0 past V: two 16-byte loads when vec
+// (V a multiple of 4 and 16-byte aligned rows, so a group of 4 is all in
+// or all out of the row), else one by one.
+__device__ inline void load_run(const float *row, int V, int j0, bool vec, float (&v)[kVPer]) {
+  static_assert(kVPer == 8, "two groups of four");
+  if (vec) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = j0 + 4 * h;
+      const float4 t = j < V ? *(const float4 *)(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[4 * h] = t.x;
+      v[4 * h + 1] = t.y;
+      v[4 * h + 2] = t.z;
+      v[4 * h + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kVPer; ++e) v[e] = j0 + e < V ? row[j0 + e] : 0.f;
+  }
+}
+
 __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
   const int s = blockIdx.y, tid = threadIdx.x;
   const int G = a.gamma;
@@ -201,6 +223,9 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
   if (tid < G) xs[tid] = a.x[s * G + tid];
   const uint64_t rr = sampling ? (uint64_t)a.r[s] : 0ull;
   int istar = G;
+  // rows start at multiples of V entries: 16-byte aligned when V is a
+  // multiple of 4 and the arrays are
+  const bool vec = (a.V & 3) == 0 && (((uintptr_t)a.p | (uintptr_t)a.q) & 15) == 0;
 
   // ---- this workgroup's partial results (all loads issued before any use)
   if (sampling) {
@@ -209,15 +234,13 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
     const float *qrow = istar < G ? a.q + ((size_t)s * G + istar) * a.V : prow;
     float pv[kUnitsSampling][kVPer], qv[kUnitsSampling][kVPer];
 #pragma unroll
-    for (int uu = 0; uu < kUnitsSampling; ++uu)
-#pragma unroll
-      for (int k = 0; k < kVPer; ++k) {
-        const int unit = u0 + uu;
-        const int j = unit * kVChunk + k * kVThreads + tid;
-        const bool ok = uu < a.upb && unit < units && j < a.V;
-        pv[uu][k] = ok ? prow[j] : 0.f;
-        qv[uu][k] = ok && istar < G ? qrow[j] : 0.f;
-      }
+    for (int uu = 0; uu < kUnitsSampling; ++uu) {
+      const int unit = u0 + uu;
+      // past the workgroup's units: an index past the row, so zeros
+      const int j0 = uu < a.upb && unit < units ? unit * kVChunk + tid * kVPer : a.V;
+      load_run(prow, a.V, j0, vec, pv[uu]);
+      load_run(qrow, a.V, istar < G ? j0 : a.V, vec, qv[uu]);
+    }
     uint64_t sum[kUnitsSampling];
 #pragma unroll
     for (int uu = 0; uu < kUnitsSampling; ++uu) {
@@ -235,14 +258,10 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 #pragma unroll
     for (int uu = 0; uu < kUnitsGreedy; ++uu) {
       const int unit = u0 + uu;
-      const int row_i = unit / a.chunks, c = unit - row_i * a.chunks;
+      const bool live = uu < a.upb && unit < units;
+      const int row_i = live ? unit / a.chunks : 0, c = live ? unit - row_i * a.chunks : 0;
       const float *row = a.p + ((size_t)s * (G + 1) + row_i) * a.V;
-#pragma unroll
-      for (int k = 0; k < kVPer; ++k) {
-        const int j = c * kVChunk + k * kVThreads + tid;
-        const bool ok = uu < a.upb && unit < units && j < a.V;
-        pv[uu][k] = ok ? row[j] : 0.f;
-      }
+      load_run(row, a.V, live ? c * kVChunk + tid * kVPer : a.V, vec, pv[uu]);
     }
     uint64_t best[kUnitsGreedy];
 #pragma unroll
@@ -252,7 +271,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
       best[uu] = 0;
 #pragma unroll
       for (int k = 0; k < kVPer; ++k) {
-        const int j = c * kVChunk + k * kVThreads + tid;
+        const int j = c * kVChunk + tid * kVPer + k;
         const bool ok = uu < a.upb && unit < units && j < a.V;
         const uint64_t key = ok ? argmax_key(pv[uu][k], j) : 0ull;
         best[uu] = key > best[uu] ? key : best[uu];
@@ -300,9 +319,14 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 
   // total weight: the chunk sums (or, if the residual vanished, the
   // verifier's own row, summed here by this workgroup alone)
-  uint64_t W = 0;
-  for (int cc = tid; cc < a.chunks; cc += kVThreads)
-    W += load_coherent64(a.part + (size_t)s * a.chunks + cc);
+  // Each thread keeps its first chunk sum for the scan below, which then
+  // needs no second round trip when the row has at most kVThreads chunks.
+  uint64_t W = 0, cs_first = 0;
+  for (int cc = tid; cc < a.chunks; cc += kVThreads) {
+    const uint64_t v = load_coherent64(a.part + (size_t)s * a.chunks + cc);
+    if (cc == tid) cs_first = v;
+    W += v;
+  }
   W = block_reduce<false>(W, scratch);
   const bool fallback = W == 0 && istar < G;
   if (fallback) {
@@ -324,7 +348,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
     uint64_t cs = 0;
     if (cc < a.chunks) {
       if (!fallback) {
-        cs = load_coherent64(a.part + (size_t)s * a.chunks + cc);
+        cs = c0 == 0 ? cs_first : load_coherent64(a.part + (size_t)s * a.chunks + cc);
       } else {
         for (int k = 0; k < kVChunk; ++k) {
           const int j = cc * kVChunk + k;
@@ -343,28 +367,33 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
     run += total;
   }
   // inside that chunk (no chunk when every weight is zero: the draw has no
-  // token, -1): its weights loaded at once, then k-major rows of kVThreads
-  // consecutive entries scanned in order
+  // token, -1): each thread's kVPer consecutive weights, one block-wide
+  // prefix sum of their sums in thread (= index) order, then the thread
+  // whose run holds the target walks its entries in order
   __shared__ int sh_pick;
   if (tid == 0) sh_pick = -1;
+  __syncthreads();
   if (sh_chunk >= 0) {
-    const int cb = sh_chunk * kVChunk;
-    uint64_t w[kVPer];
+    const int j0 = sh_chunk * kVChunk + tid * kVPer;
+    uint64_t w[kVPer], sum = 0;
 #pragma unroll
     for (int k = 0; k < kVPer; ++k) {
-      const int j = cb + k * kVThreads + tid;
+      const int j = j0 + k;
       w[k] = j < a.V ? draw_weight(a, s, istar, fallback, j) : 0ull;
+      sum += w[k];
     }
-    run = sh_before;
-    for (int k = 0; k < kVPer; ++k) {
-      uint64_t total;
-      const uint64_t incl = block_scan(w[k], scratch, &total);
+    uint64_t total;
+    const uint64_t incl = block_scan(sum, scratch, &total);
+    uint64_t at = sh_before + incl - sum;  // weight of the chunk's entries before this thread's
+    if (sum > 0 && at <= target && at + sum > target) {
       // the first entry whose inclusive prefix passes the target
-      if (w[k] > 0 && run + incl > target && run + incl - w[k] <= target)
-        sh_pick = cb + k * kVThreads + tid;
-      __syncthreads();
-      if (sh_pick >= 0) break;
-      run += total;
+      for (int k = 0; k < kVPer; ++k) {
+        if (at + w[k] > target) {
+          sh_pick = j0 + k;
+          break;
+        }
+        at += w[k];
+      }
     }
   }
   __syncthreads();
