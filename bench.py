@@ -417,9 +417,10 @@ def draft_length_table(sweep, draft_fracs=(0.05, 0.2), alphas=None):
 def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, temperature=0.7,
                     top_p=0.9):
     """The verification round after the verify pass, from the models' logits:
-    the verifier's and the draft's distributions (moe_verify_probs: softmax
-    of logits / temperature, top-p filtering, at the page's settings), then
-    the round (moe_verify_gate), each timed per call, for n_seq sequences with
+    the verifier's and the draft's distributions (moe_verify_probs_pair:
+    softmax of logits / temperature, top-p filtering, at the page's
+    settings, both row sets in one launch sequence), then the round
+    (moe_verify_gate), each timed per call, for n_seq sequences with
     gamma drafted tokens on seeded synthetic logits.  Bytes counted: the
     filter reads and writes every row once ((2 gamma + 1) rows per sequence);
     greedy reads every row of p (n_seq (gamma+1) V fp32); sampling reads
@@ -459,8 +460,10 @@ def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, tempera
         rec = {"vocab": V, "n_seq": n_seq, "gamma": gamma, "temperature": temperature,
                "top_p": top_p}
         rows = n_seq * (2 * gamma + 1)
-        fu = timed_us(lambda: (B.verify_probs(vlog, temperature, top_p, out=p),
-                               B.verify_probs(dlog, temperature, top_p, out=q)))
+        # both distributions through one launch sequence (the same settings)
+        fws = B.Workspace()
+        fu = timed_us(lambda: B.verify_probs_pair(vlog, dlog, temperature, top_p, out_p=p,
+                                                  out_q=q, ws=fws))
         rec["filter_us"] = round(fu, 2)
         rec["filter_GBs"] = round(2 * rows * V * 4 / fu / 1e3, 1)
         for mode, name in ((B.VERIFY_GREEDY, "greedy"), (B.VERIFY_SAMPLING, "sampling")):

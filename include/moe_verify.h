@@ -361,6 +361,24 @@ int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float tem
                      float top_p, float *probs, void *workspace, size_t *workspace_bytes,
                      void *stream);
 
+/* The same filtering for both distributions a round compares, in one
+ * sequence of launches ("Building a Terminal Based LLM Inference Internals
+ * Explorer - Part 3: Speculative Decoding", section "The Flow": the
+ * verifier's and the draft's logits go through the same temperature and
+ * top-p settings):
+ *   logits_p [rows_p][V] -> probs_p [rows_p][V], and
+ *   logits_q [rows_q][V] -> probs_q [rows_q][V], fp32 device,
+ * each row exactly as moe_verify_probs computes it (the outputs are bit for
+ * bit those of two moe_verify_probs calls).  1 <= rows_p, 1 <= rows_q,
+ * rows_p + rows_q <= 65535 (else MOE_ERR_UNSUPPORTED); no output may
+ * overlap an input or the other output (the inputs may overlap each
+ * other); other arguments and the workspace as for moe_verify_probs, for
+ * rows_p + rows_q rows.  Violations return MOE_ERR_INVALID_ARG. */
+int moe_verify_probs_pair(int32_t rows_p, const float *logits_p, float *probs_p, int32_t rows_q,
+                          const float *logits_q, float *probs_q, int32_t vocab,
+                          float temperature, float top_p, void *workspace,
+                          size_t *workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_string(int status);
 

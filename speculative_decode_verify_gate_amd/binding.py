@@ -78,12 +78,15 @@ def load():
     lib.moe_timing_read.argtypes = [P, P]
     lib.moe_verify_gate.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
     lib.moe_verify_probs.argtypes = [i32, i32, P, C.c_float, C.c_float, P, P, sz, P]
+    lib.moe_verify_probs_pair.argtypes = [i32, P, P, i32, P, P, i32, C.c_float, C.c_float, P,
+                                          sz, P]
     for fn in ("moe_route", "moe_route_biased", "moe_expert_pass_perslot",
                "moe_expert_pass_dedup", "moe_expert_pass_dedup_grouped", "moe_pass_bytes",
                "moe_pass_bytes_grouped", "moe_stack_pass", "moe_stack_pass_noalloc",
                "moe_pack_weights",
                "moe_timing_enable",
-               "moe_timing_read", "moe_verify_gate", "moe_verify_probs"):
+               "moe_timing_read", "moe_verify_gate", "moe_verify_probs",
+               "moe_verify_probs_pair"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -443,6 +446,43 @@ def verify_probs(logits, temperature, top_p=1.0, *, out=None, ws=None):
                                                     float(top_p), _ptr(out), _ptr(buf),
                                                     C.byref(have), _stream()))
     return out
+
+
+def verify_probs_pair(logits_p, logits_q, temperature, top_p=1.0, *, out_p=None, out_q=None,
+                      ws=None):
+    """The filtering of verify_probs for the verifier's logits [..., V] and
+    the draft's [..., V] (same V) in one launch sequence
+    (moe_verify_probs_pair).  Returns (p, q), each bit for bit what
+    verify_probs gives for its rows."""
+    lib = load()
+    logits_p = _dev(logits_p, torch.float32, "logits_p")
+    logits_q = _dev(logits_q, torch.float32, "logits_q")
+    V = logits_p.shape[-1]
+    if logits_q.shape[-1] != V:
+        raise ValueError("logits_p and logits_q must have the same vocabulary")
+    rows_p, rows_q = logits_p.numel() // V, logits_q.numel() // V
+    out_p = torch.empty_like(logits_p) if out_p is None else out_p
+    out_q = torch.empty_like(logits_q) if out_q is None else out_q
+    _dev(out_p, torch.float32, "out_p")
+    _dev(out_q, torch.float32, "out_q")
+    if out_p.shape != logits_p.shape or out_q.shape != logits_q.shape:
+        raise ValueError("outputs must have the shapes of their logits")
+    key = ("filter", rows_p + rows_q, V)
+    if key not in _NEED:
+        nb = C.c_size_t(0)
+        _check("moe_verify_probs_pair",
+               lib.moe_verify_probs_pair(rows_p, _ptr(logits_p), _ptr(out_p), rows_q,
+                                         _ptr(logits_q), _ptr(out_q), V, float(temperature),
+                                         float(top_p), None, C.byref(nb), None))
+        _NEED[key] = nb.value
+    ws = ws or Workspace(logits_p.device)
+    buf = ws.get(_NEED[key])
+    have = C.c_size_t(buf.numel())
+    _check("moe_verify_probs_pair",
+           lib.moe_verify_probs_pair(rows_p, _ptr(logits_p), _ptr(out_p), rows_q, _ptr(logits_q),
+                                     _ptr(out_q), V, float(temperature), float(top_p), _ptr(buf),
+                                     C.byref(have), _stream()))
+    return out_p, out_q
 
 
 def timing_enable(kinds=KERNEL_KINDS):

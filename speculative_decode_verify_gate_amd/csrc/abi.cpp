@@ -300,6 +300,44 @@ int launch_route(const moe_shape *s, int L, const float *gate_w, const float *bi
   return status_of(err);
 }
 
+bool overlaps(const void *a, const void *b, size_t n_a, size_t n_b) {
+  const char *x = (const char *)a, *y = (const char *)b;
+  return x < y + n_b && y < x + n_a;
+}
+
+// The filter over one or two row sets (rows_b may be 0): validation, the
+// workspace gate, the launches.
+int verify_probs(int32_t rows_a, const float *logits_a, float *probs_a, int32_t rows_b,
+                 const float *logits_b, float *probs_b, int32_t vocab, float temperature,
+                 float top_p, void *ws, size_t *ws_bytes, void *stream) {
+  if (vocab < 1 || vocab > MOE_MAX_VOCAB || rows_a < 1 || !logits_a || !probs_a || rows_b < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (rows_b > 0 && (!logits_b || !probs_b)) return MOE_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !(temperature < INFINITY) || !(top_p > 0.f) || !(top_p <= 1.f))
+    return MOE_ERR_INVALID_ARG;
+  const size_t na = (size_t)rows_a * vocab * sizeof(float);
+  const size_t nb = (size_t)rows_b * vocab * sizeof(float);
+  // no output may overlap an input or the other output
+  if (overlaps(probs_a, logits_a, na, na)) return MOE_ERR_INVALID_ARG;
+  if (rows_b > 0 && (overlaps(probs_b, logits_b, nb, nb) || overlaps(probs_a, logits_b, na, nb) ||
+                     overlaps(probs_b, logits_a, nb, na) || overlaps(probs_a, probs_b, na, nb)))
+    return MOE_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)rows_a + rows_b;
+  if (rows > 65535) return MOE_ERR_UNSUPPORTED;  // rows are a grid dimension
+  bool launch;
+  int rc;
+  if ((rc = workspace_gate(ws, ws_bytes, kHead + moe::filter_ws_bytes((int)rows, vocab),
+                           &launch)) != MOE_OK ||
+      !launch)
+    return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const hipError_t err = timed(MOE_K_FILTER, st, [&] {
+    return moe::launch_filter(rows_a, logits_a, probs_a, rows_b, logits_b, probs_b, vocab,
+                              temperature, top_p, (unsigned char *)ws + kHead, st);
+  });
+  return status_of(err);
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,26 +420,17 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
 
 int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
                      float top_p, float *probs, void *ws, size_t *ws_bytes, void *stream) {
-  if (rows < 1 || vocab < 1 || vocab > MOE_MAX_VOCAB || !logits || !probs)
-    return MOE_ERR_INVALID_ARG;
-  if (!(temperature > 0.f) || !(temperature < INFINITY) || !(top_p > 0.f) || !(top_p <= 1.f))
-    return MOE_ERR_INVALID_ARG;
-  const size_t n = (size_t)rows * vocab * sizeof(float);
-  const char *a = (const char *)logits, *b = (const char *)probs;
-  if (a < b + n && b < a + n) return MOE_ERR_INVALID_ARG;
-  if (rows > 65535) return MOE_ERR_UNSUPPORTED;  // rows are a grid dimension
-  bool launch;
-  int rc;
-  if ((rc = workspace_gate(ws, ws_bytes, kHead + moe::filter_ws_bytes(rows, vocab), &launch)) !=
-          MOE_OK ||
-      !launch)
-    return rc;
-  hipStream_t st = (hipStream_t)stream;
-  const hipError_t err = timed(MOE_K_FILTER, st, [&] {
-    return moe::launch_filter(rows, vocab, logits, temperature, top_p, probs,
-                              (unsigned char *)ws + kHead, st);
-  });
-  return status_of(err);
+  return verify_probs(rows, logits, probs, 0, nullptr, nullptr, vocab, temperature, top_p, ws,
+                      ws_bytes, stream);
+}
+
+int moe_verify_probs_pair(int32_t rows_p, const float *logits_p, float *probs_p, int32_t rows_q,
+                          const float *logits_q, float *probs_q, int32_t vocab,
+                          float temperature, float top_p, void *ws, size_t *ws_bytes,
+                          void *stream) {
+  if (rows_q < 1) return MOE_ERR_INVALID_ARG;
+  return verify_probs(rows_p, logits_p, probs_p, rows_q, logits_q, probs_q, vocab, temperature,
+                      top_p, ws, ws_bytes, stream);
 }
 
 int moe_expert_pass_perslot(const moe_shape *s, const moe_expert_weights *w, const float *x,

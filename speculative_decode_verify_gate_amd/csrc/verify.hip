@@ -453,8 +453,13 @@ struct FilterArgs {
   int V, chunks;
   float temperature;
   double top_p;
-  const float *logits;
-  float *probs;
+  // Two row sets in one launch (the verifier's rows and the draft's, with
+  // the same settings): rows 0 .. rows_a-1 are rows of logits / probs, the
+  // rest rows of logits_b / probs_b.  The per-row workspace arrays are
+  // indexed by the launch's row.
+  int rows_a;
+  const float *logits, *logits_b;
+  float *probs, *probs_b;
   float2 *stat;        // [rows][chunks]: (chunk max, sum of exp relative to it)
   uint64_t *rowhist;   // [rows][256] first-level mass histogram
   uint64_t *cand;      // [rows][V] candidates: probability bits | index << 32
@@ -462,6 +467,14 @@ struct FilterArgs {
                        // mass; the row's M and S (float bits, S in the high half)
   unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
 };
+
+__device__ inline const float *logits_row(const FilterArgs &a, int row) {
+  return row < a.rows_a ? a.logits + (size_t)row * a.V
+                        : a.logits_b + (size_t)(row - a.rows_a) * a.V;
+}
+__device__ inline float *probs_row(const FilterArgs &a, int row) {
+  return row < a.rows_a ? a.probs + (size_t)row * a.V : a.probs_b + (size_t)(row - a.rows_a) * a.V;
+}
 
 // The filter's integer mass of a probability: floor(P * 2^52).  Every
 // fp32 P >= 2^-29 is then exact (24 significant bits), the rest lose less
@@ -579,7 +592,7 @@ __global__ __launch_bounds__(kFThreads) void filter_stat_kernel(FilterArgs a) {
   const int row = blockIdx.y, c = blockIdx.x;
   __shared__ float fs[kFWaves];
   float v[kFPer];
-  load_chunk(a.logits + (size_t)row * a.V, a.V, c * kFChunk, v, -INFINITY);
+  load_chunk(logits_row(a, row), a.V, c * kFChunk, v, -INFINITY);
   // z = logit * (1 / T): one rounding more than a division, but monotone
   // in the logit (equal logits stay equal), and the same in every launch
   const float inv_t = 1.0f / a.temperature;
@@ -711,12 +724,12 @@ __global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
   __shared__ float fs[kFWaves];
   float v[kFPer];
   const int c0 = c * kFChunk;
-  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, v, -INFINITY);
+  load_chunk(logits_row(a, row), a.V, c0, v, -INFINITY);
   const float2 ms = row_stat(a.stat + (size_t)row * a.chunks, a.chunks, fs);
 #pragma unroll
   for (int k = 0; k < kFPer; ++k) v[k] = prob_of(v[k], a.temperature, ms);
   if (!HIST) {
-    store_chunk(a.probs + (size_t)row * a.V, a.V, c0, v);
+    store_chunk(probs_row(a, row), a.V, c0, v);
     return;
   }
   // the first level: mass per value of bits 29-22, one LDS copy per wave
@@ -876,7 +889,7 @@ __global__ __launch_bounds__(kFThreads) void filter_gather_kernel(FilterArgs a) 
   const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   float p[kFPer];
   const int c0 = c * kFChunk;
-  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, p, -INFINITY);
+  load_chunk(logits_row(a, row), a.V, c0, p, -INFINITY);
   const uint64_t *st = a.state + (size_t)row * 8;
   const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
   const float2 ms = row_ms(st);
@@ -913,7 +926,7 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
   const int row = blockIdx.y, c = blockIdx.x;
   const int c0 = c * kFChunk;
   float p[kFPer];
-  load_chunk(a.logits + (size_t)row * a.V, a.V, c0, p, -INFINITY);
+  load_chunk(logits_row(a, row), a.V, c0, p, -INFINITY);
   const uint64_t *st = a.state + (size_t)row * 8;
   const float pk = __uint_as_float((uint32_t)st[4]);  // the last kept probability
   const uint32_t cut = (uint32_t)st[5];                // ties kept up to this index
@@ -921,7 +934,7 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
   const float2 ms = row_ms(st);
 #pragma unroll
   for (int k = 0; k < kFPer; ++k) p[k] = prob_of(p[k], a.temperature, ms);
-  float *out = a.probs + (size_t)row * a.V;
+  float *out = probs_row(a, row);
 #pragma unroll
   for (int g = 0; g < kFGroups; ++g) {
     const uint32_t j = (uint32_t)entry_of(c0, g);
@@ -949,15 +962,20 @@ size_t filter_ws_bytes(int rows, int V) {
          align_up((size_t)rows * 4 * sizeof(unsigned), 256);
 }
 
-hipError_t launch_filter(int rows, int V, const float *logits, float temperature, float top_p,
-                         float *probs, void *ws, hipStream_t st) {
+hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int rows_b,
+                         const float *logits_b, float *probs_b, int V, float temperature,
+                         float top_p, void *ws, hipStream_t st) {
+  const int rows = rows_a + rows_b;
   FilterArgs a{};
   a.V = V;
   a.chunks = filter_chunks(V);
   a.temperature = temperature;
   a.top_p = top_p;
-  a.logits = logits;
-  a.probs = probs;
+  a.rows_a = rows_a;
+  a.logits = logits_a;
+  a.probs = probs_a;
+  a.logits_b = logits_b;
+  a.probs_b = probs_b;
   unsigned char *b = (unsigned char *)ws;
   a.stat = (float2 *)b;
   b += align_up((size_t)rows * a.chunks * sizeof(float2), 256);

@@ -95,9 +95,13 @@ hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, 
   return hipSuccess;
 }
 size_t filter_ws_bytes(int rows, int V) { return (size_t)rows * (V / 4096 + 1) * 4200; }
-hipError_t launch_filter(int rows, int V, const float *lg, float T, float top_p, float *out,
-                         void *ws, hipStream_t) {
-  CHECK(rows >= 1 && V >= 1 && lg && out && ws && T > 0.f && top_p > 0.f && top_p <= 1.f);
+hipError_t launch_filter(int rows_a, const float *lg_a, float *out_a, int rows_b,
+                         const float *lg_b, float *out_b, int V, float T, float top_p, void *ws,
+                         hipStream_t) {
+  CHECK(rows_a >= 1 && rows_b >= 0 && V >= 1 && lg_a && out_a && ws && T > 0.f && top_p > 0.f &&
+        top_p <= 1.f);
+  CHECK(rows_b == 0 || (lg_b && out_b));
+  CHECK(rows_a + rows_b <= 65535);
   ++g_launches;
   return hipSuccess;
 }
@@ -232,6 +236,21 @@ int main() {
   }
   CHECK(moe_verify_probs(2, 1000, (float *)fake(), 0.7f, 0.9f, (float *)fake(100), nullptr, &nb,
                          nullptr) == MOE_ERR_INVALID_ARG);  // overlapping
+  // the pair: both row sets through one launch sequence, workspace for all rows
+  size_t nb2 = 0;
+  CHECK(moe_verify_probs_pair(36, (float *)fake(), (float *)fake(1u << 30), 32,
+                              (float *)fake(2u << 30), (float *)fake(3u << 30), 129280, 0.7f, 0.9f,
+                              nullptr, &nb2, nullptr) == MOE_OK && nb2 > nb);
+  {
+    Buf ws(nb2);
+    size_t have = nb2;
+    CHECK(moe_verify_probs_pair(36, (float *)fake(), (float *)fake(1u << 30), 32,
+                                (float *)fake(2u << 30), (float *)fake(3u << 30), 129280, 0.7f,
+                                0.9f, ws.p, &have, nullptr) == MOE_OK);
+  }
+  CHECK(moe_verify_probs_pair(36, (float *)fake(), (float *)fake(1u << 30), 32,
+                              (float *)fake(2u << 30), (float *)fake(1u << 30), 129280, 0.7f, 0.9f,
+                              nullptr, &nb2, nullptr) == MOE_ERR_INVALID_ARG);  // outputs overlap
   std::printf("abi driver: %d launches described, %d failed checks\n", moe::g_launches, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

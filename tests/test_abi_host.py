@@ -282,6 +282,43 @@ def test_verify_probs_validation():
                                 C.byref(nb), None) == -2
 
 
+def test_verify_probs_pair_validation():
+    """The paired filter checks each row set as the single call does, and
+    that no output overlaps an input or the other output; its workspace is
+    the single call's for all rows."""
+    lib = B.load()
+    V = 1000
+    n = 2 * V * 4
+    ok = dict(rp=2, lp=FAKE, op=C.c_void_p(0x900000), rq=2, lq=C.c_void_p(0x200000),
+              oq=C.c_void_p(0xA00000), V=V, T=0.7, p=0.9)
+    bad = [dict(rp=0), dict(rq=0), dict(rq=-1), dict(lp=None), dict(op=None), dict(lq=None),
+           dict(oq=None), dict(V=0), dict(T=0.0), dict(p=1.5),
+           dict(op=C.c_void_p(0x100000 + 4000)),            # p's output over p's logits
+           dict(oq=C.c_void_p(0x200000 + n - 4)),           # q's output over q's logits
+           dict(op=C.c_void_p(0x200000 + 8)),               # p's output over q's logits
+           dict(oq=C.c_void_p(0x100000 + 8)),               # q's output over p's logits
+           dict(oq=C.c_void_p(0x900000 + n - 4))]           # the outputs overlap
+    nb = C.c_size_t(0)
+
+    def call(a, ws=None, nbytes=None):
+        return lib.moe_verify_probs_pair(a["rp"], a["lp"], a["op"], a["rq"], a["lq"], a["oq"],
+                                         a["V"], a["T"], a["p"], ws,
+                                         C.byref(nb if nbytes is None else nbytes), None)
+    for kw in bad:
+        assert call(dict(ok, **kw)) == -1, kw
+    # the two logits arrays may overlap (read only)
+    assert call(dict(ok, lq=C.c_void_p(0x100000 + 8))) == 0
+    single = C.c_size_t(0)
+    assert lib.moe_verify_probs(36 + 32, 102400, FAKE, 0.7, 0.9, C.c_void_p(0x10000000), None,
+                                C.byref(single), None) == 0
+    pair = C.c_size_t(0)
+    assert call(dict(ok, rp=36, rq=32, V=102400, op=C.c_void_p(0x10000000),
+                     lq=C.c_void_p(0x20000000), oq=C.c_void_p(0x30000000)), nbytes=pair) == 0
+    assert pair.value == single.value
+    assert call(dict(ok, rp=40000, rq=25536, V=16, op=C.c_void_p(0x10000000),
+                     lq=C.c_void_p(0x20000000), oq=C.c_void_p(0x30000000)), nbytes=pair) == -2
+
+
 def test_binding_workspace_is_zero_filled_and_grow_only():
     """The binding's Workspace needs no bookkeeping between calls: the head
     that holds arrival counters is zero at allocation and every call leaves

@@ -358,6 +358,31 @@ def test_filter_decision_is_exact_on_its_own_probabilities():
             np.testing.assert_array_equal(got[r].view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("V,top_p", [(102400, 0.9), (129280, 0.9), (4099, 0.5), (1000, 1.0),
+                                     (32000, 0.95)])
+def test_filter_pair_equals_two_single_calls(V, top_p):
+    """moe_verify_probs_pair filters the verifier's and the draft's rows in
+    one launch sequence: bit for bit what two moe_verify_probs calls give,
+    also with a ragged vocabulary (scalar loads), row sets of different
+    sizes, and one workspace shared with the single calls."""
+    rng = np.random.default_rng(V + int(top_p * 100))
+    _say(f"[filter] pair V={V} top_p={top_p}")
+    lp = torch.from_numpy(_logit_rows(rng, 9, V, ties=True)).cuda()
+    lq = torch.from_numpy(_logit_rows(rng, 5, V, masked=True)).cuda()
+    ws = B.Workspace()
+    p1 = B.verify_probs(lp, 0.7, top_p, ws=ws).clone()
+    q1 = B.verify_probs(lq, 0.7, top_p, ws=ws).clone()
+    p2, q2 = B.verify_probs_pair(lp, lq, 0.7, top_p, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(p1.view(torch.int32), p2.view(torch.int32))
+    assert torch.equal(q1.view(torch.int32), q2.view(torch.int32))
+    # the draft's rows first this time: the same bits again
+    q3, p3 = B.verify_probs_pair(lq, lp, 0.7, top_p, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(p1.view(torch.int32), p3.view(torch.int32))
+    assert torch.equal(q1.view(torch.int32), q3.view(torch.int32))
+
+
 def test_filter_nucleus_hand_computed():
     lg = np.log(np.array([[0.2, 0.5, 0.3], [0.2, 0.5, 0.3], [0.2, 0.5, 0.3]], np.float32))
     cases = [(0.45, [0, 1, 0]), (0.7, [0, 0.625, 0.375]), (0.81, [0.2, 0.5, 0.3])]
