@@ -79,3 +79,19 @@ def test_verify_round_stays_inside_its_outputs():
         na, out = Guarded((S,), torch.int32), Guarded((S, gamma + 1), torch.int32)
         B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, n_accepted=na.t, out=out.t)
         assert na.intact() and out.intact(), mode
+
+
+@pytest.mark.parametrize("V", [4099, 32000])
+def test_filter_stays_inside_its_outputs(V):
+    # single and paired calls, top_p < 1 (all four launches) and = 1, a
+    # ragged vocabulary (scalar loads) and an aligned one (16-byte stores)
+    rng = np.random.default_rng(V)
+    lp = torch.from_numpy((rng.standard_normal((5, V)) * 3).astype(np.float32)).cuda()
+    lq = torch.from_numpy((rng.standard_normal((3, V)) * 3).astype(np.float32)).cuda()
+    for top_p in (0.9, 1.0):
+        p = Guarded((5, V), torch.float32)
+        B.verify_probs(lp, 0.7, top_p, out=p.t)
+        assert p.intact(), ("single", top_p)
+        p, q = Guarded((5, V), torch.float32), Guarded((3, V), torch.float32)
+        B.verify_probs_pair(lp, lq, 0.7, top_p, out_p=p.t, out_q=q.t)
+        assert p.intact() and q.intact(), ("pair", top_p)
