@@ -42,7 +42,7 @@ constexpr int kVThreads = 256;
 constexpr int kVPer = 8;                       // entries per thread per row
 constexpr int kVChunk = kVThreads * kVPer;     // 2048
 constexpr double kQuant = 1099511627776.0;     // 2^40
-constexpr int kUnitsGreedy = 8;                // units per workgroup, at most
+constexpr int kUnitsGreedy = 4;                // units per workgroup, at most
 constexpr int kUnitsSampling = 4;
 constexpr int kWavesV = kVThreads / 64;
 
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
   const int u0 = blockIdx.x * a.upb;
   const unsigned arrivals = gridDim.x;
   __shared__ uint64_t scratch[kWavesV];
-  __shared__ uint64_t many[kUnitsGreedy][kWavesV];
+  __shared__ uint64_t many[kUnitsGreedy > kUnitsSampling ? kUnitsGreedy : kUnitsSampling][kWavesV];
   __shared__ int sh_i;
   __shared__ int sh_last;
   __shared__ int xs[MOE_MAX_DRAFT + 1];  // this sequence's draft tokens
