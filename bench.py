@@ -884,7 +884,10 @@ def engine_kernels(cfg, eng, layers, x, steps, warmup, engine):
                      "instances_per_launch": round(sum(units) / launches, 2),
                      "traffic": None if tr is None else tr.get("bytes_per_launch"),
                      "traffic_frac_of_algorithmic": None if tr is None else
-                     round(tr.get("bytes_per_launch") / algo, 3)}
+                     round(tr.get("bytes_per_launch") / algo, 3),
+                     # the counters' bytes beyond L2 over the same launch time
+                     "traffic_GBs": None if tr is None or not avg_us > 0 else
+                     round(tr.get("bytes_per_launch") / (avg_us * 1e-6) / 1e9, 1)}
     return out
 
 
@@ -1141,7 +1144,7 @@ def main():
                 "avg_launch_us": up["avg_launch_us"],
                 "algorithmic_bytes_per_launch": up["algorithmic_bytes_per_launch"],
                 "per_engine": {e: {k: {kk: v[kk] for kk in ("achieved", "frac", "avg_launch_us",
-                                                              "traffic")}
+                                                              "traffic", "traffic_GBs")}
                                    for k, v in kern[e].items()} for e in engines}}
 
     fused = None
