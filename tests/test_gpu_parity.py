@@ -90,6 +90,22 @@ def _run_both(cfg, lay_dev, x_dev, idx_dev, w_dev):
     return y_ps, y_dd, int(nu.item()), ws
 
 
+def _check_record(cfg, ws, idx):
+    """The compaction record the dedup pass leaves from byte 256 of its
+    workspace (the head belongs to arrival counters and stays zero), checked
+    bit-exactly against the oracle's compaction of the same routing."""
+    E, slots = cfg.E, idx.size
+    c = O.compact(oshape(cfg), idx)
+    assert int(ws.buf[:256].count_nonzero()) == 0
+    rec = ws.buf[256: 256 + 4 * (3 * E + 2 + slots)].view(torch.int32).cpu().numpy()
+    U = int(c["n_unique"])
+    assert rec[0] == U
+    assert np.array_equal(rec[1:1 + E], c["counts"])
+    assert np.array_equal(rec[1 + E:2 + 2 * E], c["offs"])
+    assert np.array_equal(rec[2 + 2 * E:2 + 2 * E + U], c["uniq"])
+    assert np.array_equal(rec[2 + 3 * E:2 + 3 * E + slots], c["list"])
+
+
 # ------------------------------------------------------------- small shapes
 
 SMALL = [
@@ -131,16 +147,7 @@ def test_small_layer_parity(case, n):
     err = rel_err(y_ps.cpu().numpy(), y_ref)
     _say(f"   rel err {err:.3e}  U={U}  flagged={flagged}")
     assert err <= OUT_RTOL[wdt]
-    # the compaction record, from byte 256 of the dedup workspace (the
-    # head belongs to arrival counters and stays zero)
-    c = O.compact(oshape(cfg), ref["idx"])
-    assert int(ws.buf[:256].count_nonzero()) == 0
-    rec = ws.buf[256: 256 + 4 * (3 * E + 2 + n * k)].view(torch.int32).cpu().numpy()
-    assert rec[0] == c["n_unique"]
-    assert np.array_equal(rec[1:1 + E], c["counts"])
-    assert np.array_equal(rec[1 + E:2 + 2 * E], c["offs"])
-    assert np.array_equal(rec[2 + 2 * E:2 + 2 * E + U], c["uniq"])
-    assert np.array_equal(rec[2 + 3 * E:2 + 3 * E + n * k], c["list"])
+    _check_record(cfg, ws, ref["idx"])
     # byte counts: host library call vs oracle, bit-exact
     assert B.pass_bytes(B.shape_of(cfg), ref["idx"]) == O.pass_bytes(oshape(cfg), ref["idx"])
 
