@@ -419,7 +419,9 @@ def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, tempera
     """The verification round after the verify pass, from the models' logits:
     the verifier's and the draft's distributions (moe_verify_probs_pair:
     softmax of logits / temperature, top-p filtering, at the page's
-    settings, both row sets in one launch sequence), then the round
+    settings, both row sets in one launch sequence; and the verifier's
+    alone, moe_verify_probs, since a draft's rows are filtered while it
+    drafts), then the round
     (moe_verify_gate), each timed per call, for n_seq sequences with
     gamma drafted tokens on seeded synthetic logits.  Bytes counted: the
     filter reads and writes every row once ((2 gamma + 1) rows per sequence);
@@ -466,6 +468,10 @@ def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, tempera
                                                   out_q=q, ws=fws))
         rec["filter_us"] = round(fu, 2)
         rec["filter_GBs"] = round(2 * rows * V * 4 / fu / 1e3, 1)
+        # the verifier's rows alone (the draft's are filtered while drafting)
+        pu = timed_us(lambda: B.verify_probs(vlog, temperature, top_p, out=p, ws=fws))
+        rec["filter_p_us"] = round(pu, 2)
+        rec["filter_p_GBs"] = round(2 * n_seq * (gamma + 1) * V * 4 / pu / 1e3, 1)
         for mode, name in ((B.VERIFY_GREEDY, "greedy"), (B.VERIFY_SAMPLING, "sampling")):
             ws = B.Workspace()
             us = timed_us(lambda: B.verify_gate(p, x, q=q, u=u, r=r, mode=mode, ws=ws))
@@ -473,8 +479,8 @@ def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, tempera
             rec[f"{name}_us"] = round(us, 2)
             rec[f"{name}_GBs"] = round(nbytes / us / 1e3, 1)
         out.append(rec)
-        log(f"  verify V={V}: filter {rec['filter_us']} us, greedy {rec['greedy_us']} us, "
-            f"sampling {rec['sampling_us']} us")
+        log(f"  verify V={V}: filter p+q {rec['filter_us']} us, p {rec['filter_p_us']} us, "
+            f"greedy {rec['greedy_us']} us, sampling {rec['sampling_us']} us")
     return out
 
 

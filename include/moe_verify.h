@@ -80,6 +80,10 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 #define MOE_MAX_SEQ 64     /* sequences per verification-round call */
 #define MOE_MAX_DRAFT 63   /* drafted tokens per sequence and round */
 #define MOE_MAX_VOCAB (1 << 24)
+/* The logits filter may run as one launch up to these sizes (rows of one
+ * call, vocabulary), else as four; both give the same bits. */
+#define MOE_FILTER_ONE_LAUNCH_ROWS 128
+#define MOE_FILTER_ONE_LAUNCH_VOCAB 262144
 
 /* Engines of moe_stack_pass. */
 #define MOE_ENGINE_PERSLOT 0
@@ -352,10 +356,18 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  *          independent of summation order.  probs may not overlap logits.
  * 0 < temperature (finite), 0 < top_p <= 1, 1 <= rows, 1 <= V <=
  * MOE_MAX_VOCAB; violations return MOE_ERR_INVALID_ARG (more than 65535
- * rows: MOE_ERR_UNSUPPORTED).  Workspace as for the other calls (the head
- * is not used; after it come per-row statistics, which each call
- * initialises itself, and a candidate list of up to V 8-byte entries per
- * row, so its size is about twice that of the logits).
+ * rows: MOE_ERR_UNSUPPORTED).  Workspace as for the other calls: after the
+ * head come per-row statistics, which each call initialises itself, and a
+ * candidate list of up to V 8-byte entries per row, so its size is about
+ * twice that of the logits (the head is not used).  With at most
+ * MOE_FILTER_ONE_LAUNCH_ROWS rows, V <= MOE_FILTER_ONE_LAUNCH_VOCAB and a
+ * grid of rows x ceil(V / 4096) workgroups that the device holds at once,
+ * the filter is one launch whose workgroups meet at row
+ * barriers (after a small launch that clears them), else four launches;
+ * both give the same bits.  The barriers' waits are bounded: should a
+ * row's workgroups fail to meet within about a second (not expected: they
+ * are dispatched in index order, a row's consecutively), that row's
+ * outputs are NaN. 
  * Feed the verifier's rows as p_verify and the draft's as q_draft. */
 int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
                      float top_p, float *probs, void *workspace, size_t *workspace_bytes,

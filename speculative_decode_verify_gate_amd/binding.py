@@ -20,6 +20,7 @@ MAX_TOKENS, MAX_TOPK, MAX_SLOTS, MAX_EXPERTS, MAX_SHARED = 64, 16, 512, 256, 4
 KERNEL_KINDS = ("gate", "topk", "compact", "up", "down", "combine", "verify", "filter")
 VERIFY_GREEDY, VERIFY_SAMPLING = 0, 1
 MAX_SEQ, MAX_DRAFT, MAX_VOCAB = 64, 63, 1 << 24
+FILTER_ONE_LAUNCH_ROWS, FILTER_ONE_LAUNCH_VOCAB = 128, 262144
 MAX_GROUPS = 64
 MAX_LAYERS = 64
 ENGINE_PERSLOT, ENGINE_DEDUP = 0, 1

@@ -31,6 +31,8 @@
 // block-wide integer prefix sums.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "coherent.h"
 #include "kernels.h"
 #include "verify.h"
@@ -417,37 +419,62 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 //   renormalised by their mass.
 // Work split: a row is cut into kFChunk-entry chunks, one workgroup each,
 // so a few rows still fill the chip, each thread holding four 16-byte
-// groups of consecutive entries.  Four launches pass results on through
-// the workspace:
-//   stat:   chunk max m_c and sum of exp(z - m_c), z = logit / T; the row's
-//           histogram and counters cleared;
+// groups of consecutive entries.  The phases of a row:
+//   stat:   chunk max m_c and sum of exp(z - m_c), z = logit / T;
 //   prob:   the row's max and sum (a fixed-order reduction of the chunks'
 //           pairs, so every workgroup of the row gets the same bits) and
 //           P = exp(z - M) / S.  Without top-p P is the output.  With it,
 //           the chunk's mass histogram of bits 29-22 is added into the
 //           row's (64-bit integer atomics: the sum does not depend on their
-//           order) and the row's last workgroup selects the bin and hands
-//           M and S on; P itself is not stored;
-//   gather: P again from the logits, M and S (the same bits), the chunk's
-//           entries in the selected bin (candidates) appended to the row's
-//           candidate list; the row's last workgroup finds the last kept
-//           token among them: for a short list by ranking every candidate
-//           in the order and a running sum of the masses in that order,
-//           else by K (bits 21-11, then 10-0), the number of ties at K to
-//           keep and, when only some are kept, the index cut (bits 23-12,
-//           then 11-0 of the tied indices, by counts);
-//   write:  P again, the kept entries renormalised, the rest zeroed.
-// Each launch issues its logits loads before the loads of what the
-// previous launch handed on, so the two round trips overlap.
-// "The row's last workgroup" is the last one to arrive at the row's
-// arrival counter; what the others hand over to it in the same launch is
-// written and read with coherent accesses.
+//           order), and the bin where the mass counted from the top reaches
+//           ceil(top_p W) is selected;
+//   gather: the chunk's entries in the selected bin (candidates) appended
+//           to the row's candidate list; the last kept token is found among
+//           them: for a short list by ranking every candidate in the order
+//           and a running sum of the masses in that order, else by K (bits
+//           21-11, then 10-0), the number of ties at K to keep and, when
+//           only some are kept, the index cut (bits 23-12, then 11-0 of the
+//           tied indices, by counts);
+//   write:  the kept entries renormalised, the rest zeroed.
+// Two schedules run these phases with the same arithmetic, so they give the
+// same bits:
+//   one launch (rows <= kFusedRows, chunks <= kFusedChunks, and a grid the
+//     chip holds at once), after a small launch that
+//     clears the row's synchronisation lines: each workgroup keeps its
+//     chunk in registers from the logits load to the output store, and the
+//     row's workgroups meet three times.  After stat every workgroup polls
+//     all the chunks' statistics and reduces them itself; after the
+//     histogram (each chunk's bins in a slot of its own) the last to arrive
+//     sums them, selects the bin and hands it to every workgroup's line;
+//     after the gather (each chunk's candidates in a stretch of its own,
+//     their count on its line) every workgroup polls the counts and ranks a
+//     short list itself, while a long list is resolved by the first
+//     workgroup and handed out.  The logits are read once and the output
+//     written once.  Workgroups are dispatched in index order (a row's
+//     chunks are consecutive), so the earliest unfinished row always has
+//     all its workgroups placed or placeable: every wait ends.  A wait that
+//     still gives up (after about a second) writes NaN over its chunk of
+//     the output.
+//   four launches (otherwise): stat; prob, whose row's last workgroup
+//     selects the bin and hands M and S on; gather, whose row's last
+//     workgroup resolves; write.  Each launch reads the logits again and
+//     recomputes P with the handed-on M and S; no P is stored between
+//     launches.  Each launch issues its logits loads before the loads of
+//     what the previous launch handed on, so the two round trips overlap.
+// Whatever workgroups hand over to each other inside one launch is written
+// and read with coherent accesses.
 constexpr int kFThreads = 256;
 constexpr int kFGroups = 4;                 // 16-byte groups per thread
 constexpr int kFPer = 4 * kFGroups;         // 16 entries per thread
 constexpr int kFChunk = kFThreads * kFPer;  // 4096 entries per workgroup
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kFirstShift = 22;             // first level: bits 29-22, 256 bins
+// One launch: up to this many rows and chunks per row (every workgroup
+// reads the row's chunk statistics).
+constexpr int kFusedRows = MOE_FILTER_ONE_LAUNCH_ROWS;
+constexpr int kFusedChunks = MOE_FILTER_ONE_LAUNCH_VOCAB / kFChunk;
+static_assert(MOE_FILTER_ONE_LAUNCH_VOCAB % kFChunk == 0, "whole chunks");
+constexpr unsigned kSpinLimit = 1u << 20;  // polls of a row barrier before it gives up
 
 struct FilterArgs {
   int V, chunks;
@@ -466,6 +493,8 @@ struct FilterArgs {
   uint64_t *state;     // [rows][8]: prefix, mask, mass above, target; K, index cut, kept
                        // mass; the row's M and S (float bits, S in the high half)
   unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
+  unsigned *sync;      // one launch: [rows][1 + 3 chunks] 128-byte lines (row barriers)
+  uint64_t *hpart;     // one launch: [rows][chunks][256] the chunks' first-level histograms
 };
 
 __device__ inline const float *logits_row(const FilterArgs &a, int row) {
@@ -559,62 +588,72 @@ __device__ inline void store_chunk(float *row, int V, int c0, const float (&v)[k
   }
 }
 
-// The row's max and sum of exponentials from the chunks' (max, sum): a
-// fixed-order reduction, so every workgroup of the row gets the same bits.
-__device__ inline float2 row_stat(const float2 *st, int chunks, float *fs) {
+// The chunk's max of z = logit * (1 / T) and sum of exp(z - max).  The
+// product is one rounding more than a division, but monotone in the logit
+// (equal logits stay equal), and the same in every phase.  The filter's
+// arithmetic is not contracted into fused multiply-adds: whether the
+// compiler fuses z - M depends on what else uses z in the kernel, so each
+// product, difference and sum is rounded on its own, the same way in every
+// kernel.
+__device__ inline float2 chunk_stat(const float (&v)[kFPer], float temperature, float *fs) {
+#pragma clang fp contract(off)
+  const float inv_t = 1.0f / temperature;
+  float z[kFPer];
   float m = -INFINITY;
-  for (int c = threadIdx.x; c < chunks; c += kFThreads) m = fmaxf(m, st[c].x);
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) {
+    z[k] = v[k] * inv_t;
+    m = fmaxf(m, z[k]);
+  }
   m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
   float S = 0.f;
-  for (int c = threadIdx.x; c < chunks; c += kFThreads) {
-    const float2 t = st[c];
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < kFPer; ++k) S += expf(z[k] - m);
+  }
+  S = block_all(S, fs, [](float x, float y) { return x + y; });
+  return make_float2(m, S);
+}
+
+__device__ inline uint64_t ms_bits(float2 ms) {
+  return (uint64_t)__float_as_uint(ms.x) | ((uint64_t)__float_as_uint(ms.y) << 32);
+}
+__device__ inline float2 ms_of(uint64_t b) {
+  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+
+// The row's max and sum of exponentials from the chunks' (max, sum): a
+// fixed-order reduction, so every workgroup of the row gets the same bits.
+// COH: the pairs were written in this launch (coherent loads).
+template <bool COH>
+__device__ inline float2 row_stat(const float2 *st, int chunks, float *fs) {
+#pragma clang fp contract(off)
+  float2 mine[(kFusedChunks + kFThreads - 1) / kFThreads];
+  float m = -INFINITY;
+  int i = 0;
+  for (int c = threadIdx.x; c < chunks; c += kFThreads, ++i) {
+    const float2 t = COH ? ms_of(load_coherent64((const uint64_t *)(st + c))) : st[c];
+    if (COH) mine[i] = t;
+    m = fmaxf(m, t.x);
+  }
+  m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
+  float S = 0.f;
+  i = 0;
+  for (int c = threadIdx.x; c < chunks; c += kFThreads, ++i) {
+    const float2 t = COH ? mine[i] : st[c];
     if (t.x != -INFINITY) S += t.y * expf(t.x - m);
   }
   S = block_all(S, fs, [](float x, float y) { return x + y; });
   return make_float2(m, S);
 }
 
-// P of a logit given the row's max M and sum S of exp(z - M): every launch
+// P of a logit given the row's max M and sum S of exp(z - M): every phase
 // computes it with this one expression, so all of them get the same bits.
 // exp(z - M) <= 1 and 1 / S <= 1 (S >= 1: the max's own term), so P <= 1
 // and its bits 31-30 are zero; a -inf fill (past the row) gives 0.
 __device__ inline float prob_of(float logit, float temperature, float2 ms) {
+#pragma clang fp contract(off)
   return expf(logit * (1.0f / temperature) - ms.x) * (1.0f / ms.y);
-}
-
-// The row's M and S as the prob launch's last workgroup handed them on.
-__device__ inline float2 row_ms(const uint64_t *st) {
-  const uint64_t b = st[7];
-  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
-}
-
-__global__ __launch_bounds__(kFThreads) void filter_stat_kernel(FilterArgs a) {
-  const int row = blockIdx.y, c = blockIdx.x;
-  __shared__ float fs[kFWaves];
-  float v[kFPer];
-  load_chunk(logits_row(a, row), a.V, c * kFChunk, v, -INFINITY);
-  // z = logit * (1 / T): one rounding more than a division, but monotone
-  // in the logit (equal logits stay equal), and the same in every launch
-  const float inv_t = 1.0f / a.temperature;
-  float m = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kFPer; ++k) {
-    v[k] *= inv_t;
-    m = fmaxf(m, v[k]);
-  }
-  m = block_all(m, fs, [](float x, float y) { return fmaxf(x, y); });
-  float S = 0.f;
-  if (m != -INFINITY) {
-#pragma unroll
-    for (int k = 0; k < kFPer; ++k) S += expf(v[k] - m);
-  }
-  S = block_all(S, fs, [](float x, float y) { return x + y; });
-  if (threadIdx.x == 0) a.stat[(size_t)row * a.chunks + c] = make_float2(m, S);
-  // the row's histogram and counters start at zero for the later launches
-  if (a.top_p < 1.0 && c == 0) {
-    a.rowhist[(size_t)row * 256 + threadIdx.x] = 0;
-    if (threadIdx.x < 4) a.count[(size_t)row * 4 + threadIdx.x] = 0u;
-  }
 }
 
 // Selection over NB mass bins h (bits [shift, shift + log2 NB) of the
@@ -716,69 +755,70 @@ __device__ inline bool arrive_last(unsigned *ctr, unsigned n) {
   return s_last != 0;
 }
 
-// HIST: top_p < 1 (the first-level histogram and selection follow); the
-// plain softmax instantiation reserves no histogram LDS.
-template <bool HIST>
-__global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
-  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
-  __shared__ float fs[kFWaves];
-  float v[kFPer];
-  const int c0 = c * kFChunk;
-  load_chunk(logits_row(a, row), a.V, c0, v, -INFINITY);
-  const float2 ms = row_stat(a.stat + (size_t)row * a.chunks, a.chunks, fs);
-#pragma unroll
-  for (int k = 0; k < kFPer; ++k) v[k] = prob_of(v[k], a.temperature, ms);
-  if (!HIST) {
-    store_chunk(probs_row(a, row), a.V, c0, v);
-    return;
-  }
-  // the first level: mass per value of bits 29-22, one LDS copy per wave
-  __shared__ unsigned long long lh[kFWaves][256];
-  for (int i = tid; i < kFWaves * 256; i += kFThreads) lh[i / 256][i % 256] = 0ull;
+// The chunk's first-level mass histogram (bits 29-22 of P), one LDS copy
+// per wave in lh (kFWaves x 256), added into the row's bins rh.
+__device__ inline void add_chunk_hist(const float (&p)[kFPer], unsigned long long *lh,
+                                      uint64_t *rh) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < kFWaves * 256; i += kFThreads) lh[i] = 0ull;
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kFPer; ++k)
-    if (v[k] > 0.f)
-      atomicAdd(&lh[wave][(__float_as_uint(v[k]) >> kFirstShift) & 255u],
-                (unsigned long long)mass_of(v[k]));
+    if (p[k] > 0.f)
+      atomicAdd(&lh[wave * 256 + ((__float_as_uint(p[k]) >> kFirstShift) & 255u)],
+                (unsigned long long)mass_of(p[k]));
   __syncthreads();
-  uint64_t *rh = a.rowhist + (size_t)row * 256;
-  {
-    const uint64_t t = lh[0][tid] + lh[1][tid] + lh[2][tid] + lh[3][tid];
-    if (t) atomicAdd((unsigned long long *)&rh[tid], (unsigned long long)t);
-  }
-  if (!arrive_last(a.count + (size_t)row * 4, a.chunks)) return;
-  uint32_t prefix = 0, mask = 0xC0000000u;  // bits 31-30 are zero for every entry
-  uint64_t above = 0, target = 0;
-  select_level<256, true>(rh, kFirstShift, target, prefix, mask, above, a.top_p);
-  if (tid == 0) {
-    uint64_t *st = a.state + (size_t)row * 8;
-    st[0] = prefix;
-    st[1] = mask;
-    st[2] = above;
-    st[3] = target;
-    st[7] = (uint64_t)__float_as_uint(ms.x) | ((uint64_t)__float_as_uint(ms.y) << 32);
+  static_assert(kFWaves == 4 && kFThreads == 256, "one bin per thread, four copies");
+  const uint64_t t = lh[tid] + lh[256 + tid] + lh[512 + tid] + lh[768 + tid];
+  if (t) atomicAdd((unsigned long long *)&rh[tid], (unsigned long long)t);
+}
+
+// The chunk's entries in the selected bin appended to the row's candidate
+// list (its length counted at *n_cand).
+__device__ inline void append_candidates(const float (&p)[kFPer], int c0, uint32_t prefix,
+                                         uint32_t mask, uint64_t *cand, unsigned *n_cand) {
+  const int tid = threadIdx.x;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k)
+    mine += ((__float_as_uint(p[k]) & mask) == prefix && p[k] > 0.f) ? 1u : 0u;
+  uint32_t total;
+  const uint32_t off = block_exclusive(mine, total);
+  __shared__ uint32_t s_base;
+  if (tid == 0) s_base = total ? atomicAdd(n_cand, total) : 0u;
+  __syncthreads();
+  uint32_t at = s_base + off;
+#pragma unroll
+  for (int g = 0; g < kFGroups; ++g) {
+    const int j = entry_of(c0, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = __float_as_uint(p[4 * g + e]);
+      if ((key & mask) == prefix && p[4 * g + e] > 0.f)
+        store_coherent64(cand + at++, (uint64_t)key | ((uint64_t)(j + e) << 32));
+    }
   }
 }
 
-// The row's last workgroup after the gather, for at most kDirect
-// candidates: each candidate's rank in the order (probability descending,
-// index ascending) by counting the candidates before it, their masses in
-// that order, a running sum, and the first rank at which the mass above
-// the bin plus the running sum reaches the target: that token is the last
-// one kept, its probability is K and its index the cut (the ties at K
-// after it in the order have larger indices).
-// ord and by_rank are LDS arrays of kDirect entries each (the radix
-// path's bins, which this path does not use).
+// The boundary from at most kDirect candidates (candidate i is cand(i), a
+// coherent load): each
+// candidate's rank in the order (probability descending, index ascending)
+// by counting the candidates before it, their masses in that order, a
+// running sum, and the first rank at which the mass above the bin plus the
+// running sum reaches the target: that token is the last one kept, its
+// probability is K and its index the cut (the ties at K after it in the
+// order have larger indices).  The one thread that finds it writes K, the
+// cut and the kept mass to out[0..2].
+// ord and by_rank are LDS arrays of kDirect entries each.
 constexpr uint32_t kDirect = 512;
-__device__ inline void resolve_direct(const FilterArgs &a, int row, const uint64_t *cand, uint32_t n,
-                                      unsigned long long *ord, unsigned long long *by_rank) {
+template <class Load>
+__device__ inline void resolve_direct(Load cand, uint32_t n, uint64_t above,
+                                      uint64_t target, unsigned long long *ord,
+                                      unsigned long long *by_rank, uint64_t *out) {
   __shared__ uint64_t scratch[kWavesV];
   const int tid = threadIdx.x;
-  uint64_t *st = a.state + (size_t)row * 8;
-  const uint64_t above = st[2], target = st[3];
   for (uint32_t i = tid; i < n; i += kFThreads) {
-    const uint64_t e = load_coherent64(cand + i);
+    const uint64_t e = cand(i);
     ord[i] = ((uint64_t)(uint32_t)e << 32) | (0xFFFFFFFFu - (uint32_t)(e >> 32));
   }
   __syncthreads();
@@ -808,118 +848,162 @@ __device__ inline void resolve_direct(const FilterArgs &a, int row, const uint64
   }
   if (last != 0xFFFFFFFFu) {
     const uint64_t o = by_rank[last];
-    st[4] = o >> 32;
-    st[5] = 0xFFFFFFFFu - (uint32_t)o;
-    st[6] = kept;
+    out[0] = o >> 32;
+    out[1] = 0xFFFFFFFFu - (uint32_t)o;
+    out[2] = kept;
   }
 }
 
-// The row's last workgroup after the gather: K, the number of ties to keep
-// and the index cut, from the row's n candidates (coherent loads).
-__device__ inline void resolve_row(const FilterArgs &a, int row, const uint64_t *cand, uint32_t n) {
-  // mass bins (11-bit levels), then count bins (12-bit levels of 32-bit
-  // counts): 16 KB, so the gather launch keeps enough workgroups resident
-  __shared__ unsigned long long lh[2048];
-  static_assert(2 * kDirect <= 2048, "the direct path's arrays fit the bins");
+// The boundary from the row's n candidates (cand(i), coherent loads), the selection
+// of the first level given: K, the index cut and the kept mass to out[0..2]
+// (written by thread 0 on the radix path).  lh: 1024 LDS entries (the
+// direct path's two arrays; the radix path's 256 mass bins, then 256
+// count bins).  Radix levels are 8 bits wide, so each takes one bin per
+// thread: K from bits 21-14, 13-6 and 7-0 (bits 7-6 already fixed, so
+// the bins outside them stay empty), the index cut from bits 23-16, 15-8
+// and 7-0 of the tied indices.
+template <class Load>
+__device__ inline void resolve_row(Load cand, uint32_t n, uint32_t prefix,
+                                   uint32_t mask, uint64_t above, uint64_t target,
+                                   unsigned long long *lh, uint64_t *out) {
   if (n <= kDirect) {
-    resolve_direct(a, row, cand, n, lh, lh + kDirect);
+    resolve_direct(cand, n, above, target, lh, lh + kDirect, out);
     return;
   }
   uint32_t *lc = (uint32_t *)lh;
   const int tid = threadIdx.x;
-  uint64_t *st = a.state + (size_t)row * 8;
-  uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
-  uint64_t above = st[2], target = st[3];
-  // bits 21-11
-  for (int i = tid; i < 2048; i += kFThreads) lh[i] = 0ull;
-  __syncthreads();
-  for (uint32_t i = tid; i < n; i += kFThreads) {
-    const uint32_t key = (uint32_t)load_coherent64(cand + i);
-    atomicAdd(&lh[(key >> 11) & 2047u], (unsigned long long)mass_of(__uint_as_float(key)));
+  uint64_t bin = 0;
+#pragma unroll 1
+  for (int shift = 14; shift >= 0; shift = shift > 6 ? shift - 8 : shift - 6) {
+    lh[tid] = 0ull;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kFThreads) {
+      const uint32_t key = (uint32_t)cand(i);
+      if ((key & mask) == prefix)
+        atomicAdd(&lh[(key >> shift) & 255u], (unsigned long long)mass_of(__uint_as_float(key)));
+    }
+    __syncthreads();
+    bin = select_level<256, false>((const uint64_t *)lh, shift, target, prefix, mask, above);
+    __syncthreads();  // every thread has read its bin
   }
-  __syncthreads();
-  select_level<2048, false>((const uint64_t *)lh, 11, target, prefix, mask, above);
-  // bits 10-0 of the candidates under that prefix
-  __syncthreads();  // every thread has read its bins
-  for (int i = tid; i < 2048; i += kFThreads) lh[i] = 0ull;
-  __syncthreads();
-  for (uint32_t i = tid; i < n; i += kFThreads) {
-    const uint32_t key = (uint32_t)load_coherent64(cand + i);
-    if ((key & mask) == prefix) atomicAdd(&lh[key & 2047u], (unsigned long long)mass_of(__uint_as_float(key)));
-  }
-  __syncthreads();
-  const uint64_t bin = select_level<2048, false>((const uint64_t *)lh, 0, target, prefix, mask, above);
   const uint32_t K = prefix;                       // the last kept probability's bits
   const uint64_t mk = mass_of(__uint_as_float(K));  // > 0: the target lies in positive mass
   const uint64_t ties = bin / mk;                  // all of equal mass mk
   const uint64_t keep = (target - above + mk - 1) / mk;
   uint32_t cut = 0xFFFFFFFFu;  // every tie kept
   if (keep < ties) {
-    // the keep-th smallest index among the ties: counts of index bits
-    // 23-12, then of bits 11-0 within that bin
-    for (int i = tid; i < 4096; i += kFThreads) lc[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < n; i += kFThreads) {
-      const uint64_t e = load_coherent64(cand + i);
-      if ((uint32_t)e == K) atomicAdd(&lc[(uint32_t)(e >> 32) >> 12], 1u);
+    // the keep-th smallest index among the ties, 8 index bits at a time
+    uint32_t ip = 0, im = 0, base = 0;
+#pragma unroll 1
+    for (int shift = 16; shift >= 0; shift -= 8) {
+      lc[tid] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < n; i += kFThreads) {
+        const uint64_t e = cand(i);
+        const uint32_t j = (uint32_t)(e >> 32);
+        if ((uint32_t)e == K && (j & im) == ip) atomicAdd(&lc[(j >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      ip |= rank_bin<256>(lc, (uint32_t)keep, base) << shift;
+      im |= 255u << shift;
+      __syncthreads();  // every thread has read its bin
     }
-    __syncthreads();
-    uint32_t base = 0;
-    const uint32_t hi = rank_bin<4096>(lc, (uint32_t)keep, base);
-    __syncthreads();
-    for (int i = tid; i < 4096; i += kFThreads) lc[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < n; i += kFThreads) {
-      const uint64_t e = load_coherent64(cand + i);
-      const uint32_t j = (uint32_t)(e >> 32);
-      if ((uint32_t)e == K && (j >> 12) == hi) atomicAdd(&lc[j & 4095u], 1u);
-    }
-    __syncthreads();
-    const uint32_t lo = rank_bin<4096>(lc, (uint32_t)keep, base);
-    cut = (hi << 12) | lo;
+    cut = ip;
   }
   if (tid == 0) {
-    st[4] = K;
-    st[5] = cut;
-    st[6] = above + keep * mk;  // the kept mass
+    out[0] = K;
+    out[1] = cut;
+    out[2] = above + keep * mk;  // the kept mass
+  }
+}
+
+// The chunk's output: P kept (P > K, or P = K at an index up to the cut)
+// renormalised by the kept mass, the rest zero.
+__device__ inline void write_chunk(float *out, int V, int c0, float (&p)[kFPer], uint64_t kbits,
+                                   uint64_t cut64, uint64_t kept) {
+  const float pk = __uint_as_float((uint32_t)kbits);  // the last kept probability
+  const uint32_t cut = (uint32_t)cut64;                // ties kept up to this index
+  const float total = (float)((double)kept / kMassQuant);
+#pragma unroll
+  for (int g = 0; g < kFGroups; ++g) {
+    const uint32_t j = (uint32_t)entry_of(c0, g);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = p[4 * g + e];
+      const bool keep = x > pk || (x == pk && x > 0.f && j + e <= cut);
+      p[4 * g + e] = keep ? x / total : 0.f;
+    }
+  }
+  store_chunk(out, V, c0, p);
+}
+
+// ---- four launches
+
+__global__ __launch_bounds__(kFThreads) void filter_stat_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x;
+  __shared__ float fs[kFWaves];
+  float v[kFPer];
+  load_chunk(logits_row(a, row), a.V, c * kFChunk, v, -INFINITY);
+  const float2 cs = chunk_stat(v, a.temperature, fs);
+  if (threadIdx.x == 0) a.stat[(size_t)row * a.chunks + c] = cs;
+  // the row's histogram and counters start at zero for the later launches
+  if (a.top_p < 1.0 && c == 0) {
+    a.rowhist[(size_t)row * 256 + threadIdx.x] = 0;
+    if (threadIdx.x < 4) a.count[(size_t)row * 4 + threadIdx.x] = 0u;
+  }
+}
+
+// HIST: top_p < 1 (the first-level histogram and selection follow); the
+// plain softmax instantiation reserves no histogram LDS.
+template <bool HIST>
+__global__ __launch_bounds__(kFThreads) void filter_prob_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  __shared__ float fs[kFWaves];
+  float v[kFPer];
+  const int c0 = c * kFChunk;
+  load_chunk(logits_row(a, row), a.V, c0, v, -INFINITY);
+  const float2 ms = row_stat<false>(a.stat + (size_t)row * a.chunks, a.chunks, fs);
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) v[k] = prob_of(v[k], a.temperature, ms);
+  if (!HIST) {
+    store_chunk(probs_row(a, row), a.V, c0, v);
+    return;
+  }
+  __shared__ unsigned long long lh[kFWaves * 256];
+  uint64_t *rh = a.rowhist + (size_t)row * 256;
+  add_chunk_hist(v, lh, rh);
+  if (!arrive_last(a.count + (size_t)row * 4, a.chunks)) return;
+  uint32_t prefix = 0, mask = 0xC0000000u;  // bits 31-30 are zero for every entry
+  uint64_t above = 0, target = 0;
+  select_level<256, true>(rh, kFirstShift, target, prefix, mask, above, a.top_p);
+  if (tid == 0) {
+    uint64_t *st = a.state + (size_t)row * 8;
+    st[0] = prefix;
+    st[1] = mask;
+    st[2] = above;
+    st[3] = target;
+    st[7] = ms_bits(ms);
   }
 }
 
 __global__ __launch_bounds__(kFThreads) void filter_gather_kernel(FilterArgs a) {
-  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int row = blockIdx.y, c = blockIdx.x;
+  __shared__ unsigned long long lh[2 * kDirect];
   float p[kFPer];
   const int c0 = c * kFChunk;
   load_chunk(logits_row(a, row), a.V, c0, p, -INFINITY);
-  const uint64_t *st = a.state + (size_t)row * 8;
+  uint64_t *st = a.state + (size_t)row * 8;
   const uint32_t prefix = (uint32_t)st[0], mask = (uint32_t)st[1];
-  const float2 ms = row_ms(st);
+  const float2 ms = ms_of(st[7]);
 #pragma unroll
   for (int k = 0; k < kFPer; ++k) p[k] = prob_of(p[k], a.temperature, ms);
-  uint32_t mine = 0;
-#pragma unroll
-  for (int k = 0; k < kFPer; ++k)
-    mine += ((__float_as_uint(p[k]) & mask) == prefix && p[k] > 0.f) ? 1u : 0u;
-  uint32_t total;
-  const uint32_t off = block_exclusive(mine, total);
-  __shared__ uint32_t s_base;
-  if (tid == 0) s_base = total ? atomicAdd(a.count + (size_t)row * 4 + 2, total) : 0u;
-  __syncthreads();
   uint64_t *cand = a.cand + (size_t)row * a.V;
-  uint32_t at = s_base + off;
-#pragma unroll
-  for (int g = 0; g < kFGroups; ++g) {
-    const int j = entry_of(c0, g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = __float_as_uint(p[4 * g + e]);
-      if ((key & mask) == prefix && p[4 * g + e] > 0.f)
-        store_coherent64(cand + at++, (uint64_t)key | ((uint64_t)(j + e) << 32));
-    }
-  }
+  append_candidates(p, c0, prefix, mask, cand, a.count + (size_t)row * 4 + 2);
   if (!arrive_last(a.count + (size_t)row * 4 + 1, a.chunks)) return;
   const uint32_t n = __hip_atomic_load(a.count + (size_t)row * 4 + 2, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-  resolve_row(a, row, cand, n);
+  resolve_row([cand](uint32_t i) { return load_coherent64(cand + i); }, n, prefix, mask, st[2],
+              st[3], lh, st + 4);
 }
 
 __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
@@ -928,29 +1012,293 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
   float p[kFPer];
   load_chunk(logits_row(a, row), a.V, c0, p, -INFINITY);
   const uint64_t *st = a.state + (size_t)row * 8;
-  const float pk = __uint_as_float((uint32_t)st[4]);  // the last kept probability
-  const uint32_t cut = (uint32_t)st[5];                // ties kept up to this index
-  const float total = (float)((double)st[6] / kMassQuant);
-  const float2 ms = row_ms(st);
+  const float2 ms = ms_of(st[7]);
 #pragma unroll
   for (int k = 0; k < kFPer; ++k) p[k] = prob_of(p[k], a.temperature, ms);
-  float *out = probs_row(a, row);
-#pragma unroll
-  for (int g = 0; g < kFGroups; ++g) {
-    const uint32_t j = (uint32_t)entry_of(c0, g);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = p[4 * g + e];
-      const bool kept = x > pk || (x == pk && x > 0.f && j + e <= cut);
-      p[4 * g + e] = kept ? x / total : 0.f;
-    }
+  write_chunk(probs_row(a, row), a.V, c0, p, st[4], st[5], st[6]);
+}
+
+// ---- one launch
+
+// Synchronisation lines of a row (128 bytes each, cleared by
+// filter_clear_kernel before the launch).  Device-scope accesses to one
+// line queue behind each other at the memory side, so what many
+// workgroups poll is spread over lines.  Every word below is written once
+// per call and is non-zero once written, so a waiter polls the word itself:
+//   arrival   one count (barrier 2, whose last arrival does the row's part)
+//   stat[c]   chunk c's max and sum (float bits; M is finite or -inf, so
+//             non-zero)
+//   count[c]  chunk c's number of candidates + 1
+//   out[c]    what a last arrival hands to workgroup c, polled only by it:
+//             words 0-1 the selected bin (barrier 2), words 2-3 the boundary
+//             of a long candidate list (barrier 3)
+constexpr int kLineWords = 32;  // 128 bytes
+constexpr int kRowLines = 3;    // stat, count, out: lines per chunk
+__device__ inline unsigned *row_lines(const FilterArgs &a, int row) {
+  return a.sync + (size_t)row * (1 + kRowLines * a.chunks) * kLineWords;
+}
+__device__ inline uint64_t *line_of(unsigned *lines, int kind, int n, int c) {
+  return (uint64_t *)(lines + (size_t)(1 + kind * n + c) * kLineWords);
+}
+constexpr int kStatLine = 0, kCountLine = 1, kOutLine = 2;
+
+// Before the one launch: the row's synchronisation lines start at zero.
+// One workgroup per row.
+__global__ __launch_bounds__(kFThreads) void filter_clear_kernel(FilterArgs a) {
+  unsigned *l = row_lines(a, blockIdx.x);
+  const int words = (1 + kRowLines * a.chunks) * kLineWords;
+  for (int i = threadIdx.x; i < words; i += kFThreads) l[i] = 0u;
+}
+
+// Wait (bounded) until word 0 of line t of `first` is non-zero for every
+// t < n; thread t < n gets line t's word.  False if the wait gave up
+// (the same in every thread).
+__device__ inline bool wait_all(unsigned *lines, int kind, unsigned n, uint64_t &mine) {
+  uint64_t v = 0;
+  const uint64_t *p = threadIdx.x < n ? line_of(lines, kind, (int)n, threadIdx.x) : nullptr;
+  for (unsigned i = 0;; ++i) {
+    if (p && v == 0) v = load_coherent64(p);
+    if (__syncthreads_and(!p || v != 0)) break;
+    if (i == kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(1);
   }
-  store_chunk(out, a.V, c0, p);
+  mine = v;
+  return true;
+}
+
+// Wait (bounded) until the NW words at w are all non-zero: false if the
+// wait gave up.  Every thread gets the words.
+template <int NW>
+__device__ inline bool wait_words(const uint64_t *w, uint64_t (&got)[NW]) {
+  __shared__ uint64_t s_w[NW];
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    for (unsigned i = 0;; ++i) {
+      bool all = true;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) {
+        s_w[k] = load_coherent64(w + k);
+        all = all && s_w[k] != 0;
+      }
+      if (all) break;
+      if (i == kSpinLimit) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    s_ok = ok;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NW; ++k) got[k] = s_w[k];
+  return s_ok != 0;
+}
+
+// Words [first, first + NW) of every workgroup's out line.
+template <int NW>
+__device__ inline void hand_out(unsigned *lines, unsigned n, int first, const uint64_t (&val)[NW]) {
+  for (unsigned i = threadIdx.x; i < n; i += kFThreads)
+#pragma unroll
+    for (int k = 0; k < NW; ++k) store_coherent64(line_of(lines, kOutLine, n, i) + first + k, val[k]);
+}
+
+// A wait gave up: the chunk's output is NaN, so the failure shows.
+__device__ inline void poison_chunk(float *out, int V, int c0) {
+  float nan[kFPer];
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) nan[k] = __builtin_nanf("");
+  store_chunk(out, V, c0, nan);
+}
+
+template <bool HIST>
+__global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
+  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int c0 = c * kFChunk;
+  const unsigned n = (unsigned)a.chunks;
+  unsigned *lines = row_lines(a, row);
+  __shared__ float fs[kFWaves];
+  __shared__ unsigned long long lds[2 * kDirect];  // histogram copies, then the resolve's arrays
+  static_assert(2 * kDirect >= kFWaves * 256, "the histogram copies fit");
+  static_assert(kFusedChunks <= kFThreads, "a chunk per thread in the waits");
+  __shared__ uint64_t res[3];                      // K, index cut, kept mass
+  __shared__ uint32_t off[kFusedChunks + 1];       // candidate offsets of the chunks
+  float v[kFPer];
+  load_chunk(logits_row(a, row), a.V, c0, v, -INFINITY);
+  float *out = probs_row(a, row);
+  // the chunks' statistics: each workgroup reduces all of them itself (the
+  // fixed-order reduction of the four-launch schedule)
+  const float2 cs = chunk_stat(v, a.temperature, fs);
+  if (tid == 0) store_coherent64(line_of(lines, kStatLine, n, c), ms_bits(cs));
+  wait_stores();
+  uint64_t got = 0;
+  if (!wait_all(lines, kStatLine, n, got)) return poison_chunk(out, a.V, c0);
+  float2 ms;
+  {
+    const float2 t = tid < (int)n ? ms_of(got) : make_float2(-INFINITY, 0.f);
+    float m = block_all(t.x, fs, [](float x, float y) { return fmaxf(x, y); });
+    float S;
+    {
+#pragma clang fp contract(off)
+      S = (tid < (int)n && t.x != -INFINITY) ? t.y * expf(t.x - m) : 0.f;
+    }
+    S = block_all(S, fs, [](float x, float y) { return x + y; });
+    ms = make_float2(m, S);
+  }
+#pragma unroll
+  for (int k = 0; k < kFPer; ++k) v[k] = prob_of(v[k], a.temperature, ms);
+  if (!HIST) {
+    store_chunk(out, a.V, c0, v);
+    return;
+  }
+  // the chunk's histogram into its own slot; the row's last arrival sums
+  // them, selects the bin and hands it out
+  uint64_t *part = a.hpart + (size_t)row * a.chunks * 256;
+  {
+    const int wave = tid >> 6;
+    for (int i = tid; i < kFWaves * 256; i += kFThreads) lds[i] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kFPer; ++k)
+      if (v[k] > 0.f)
+        atomicAdd(&lds[wave * 256 + ((__float_as_uint(v[k]) >> kFirstShift) & 255u)],
+                  (unsigned long long)mass_of(v[k]));
+    __syncthreads();
+    store_coherent64(part + (size_t)c * 256 + tid,
+                     lds[tid] + lds[256 + tid] + lds[512 + tid] + lds[768 + tid]);
+  }
+  uint32_t prefix = 0, mask = 0xC0000000u | (255u << kFirstShift);
+  uint64_t above = 0, target = 0;
+  __shared__ int s_last;
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(lines, 1u) == n - 1u;
+  __syncthreads();
+  uint64_t w[2];
+  if (s_last) {
+    uint64_t h = 0;  // the row's bin tid: the chunks' counts (16 loads in flight)
+    for (unsigned q0 = 0; q0 < n; q0 += 16) {
+      uint64_t t[16];
+#pragma unroll
+      for (unsigned j = 0; j < 16; ++j)
+        t[j] = q0 + j < n ? load_coherent64(part + (size_t)(q0 + j) * 256 + tid) : 0ull;
+#pragma unroll
+      for (unsigned j = 0; j < 16; ++j) h += t[j];
+    }
+    __syncthreads();  // every thread has read its copy bins
+    lds[tid] = h;
+    __syncthreads();
+    uint32_t pf = 0, mk = 0xC0000000u;
+    select_level<256, false>((const uint64_t *)lds, kFirstShift, target, pf, mk, above, a.top_p);
+    prefix = pf;
+    // above < W < 2^53 and the bin + 1 <= 256: one word, non-zero
+    w[0] = above | ((uint64_t)((pf >> kFirstShift) + 1) << 54);
+    w[1] = target | (1ull << 63);
+    hand_out<2>(lines, n, 0, {w[0], w[1]});
+  } else {
+    if (!wait_words<2>(line_of(lines, kOutLine, n, c), w)) return poison_chunk(out, a.V, c0);
+    above = w[0] & ((1ull << 54) - 1);
+    prefix = (uint32_t)((w[0] >> 54) - 1) << kFirstShift;
+    target = w[1] & ~(1ull << 63);
+  }
+  // the chunk's candidates (entries in the bin) into its own stretch of the
+  // row's list, their number + 1 into its count line
+  uint64_t *cand = a.cand + (size_t)row * a.V;
+  {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < kFPer; ++k)
+      mine += ((__float_as_uint(v[k]) & mask) == prefix && v[k] > 0.f) ? 1u : 0u;
+    uint32_t total;
+    uint32_t at = block_exclusive(mine, total);
+#pragma unroll
+    for (int g = 0; g < kFGroups; ++g) {
+      const int j = entry_of(c0, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = __float_as_uint(v[4 * g + e]);
+        if ((key & mask) == prefix && v[4 * g + e] > 0.f)
+          store_coherent64(cand + c0 + at++, (uint64_t)key | ((uint64_t)(j + e) << 32));
+      }
+    }
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) store_coherent64(line_of(lines, kCountLine, n, c), (uint64_t)total + 1);
+  }
+  wait_stores();
+  if (!wait_all(lines, kCountLine, n, got)) return poison_chunk(out, a.V, c0);
+  uint32_t nc;
+  {
+    const uint32_t k_t = tid < (int)n ? (uint32_t)got - 1u : 0u;
+    const uint32_t o = block_exclusive(k_t, nc);
+    if (tid < (int)n) off[tid] = o;
+    if (tid == 0) off[n] = nc;
+    __syncthreads();
+  }
+  // candidate i: the chunk whose stretch holds it (binary search of the
+  // offsets), then its place in the stretch
+  auto load = [&](uint32_t i) {
+    uint32_t lo = 0, hi = n;  // off[lo] <= i < off[hi]
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) / 2;
+      if (off[mid] <= i) lo = mid;
+      else hi = mid;
+    }
+    return load_coherent64(cand + (size_t)lo * kFChunk + (i - off[lo]));
+  };
+  if (nc <= kDirect) {
+    // a short list: every workgroup ranks it itself
+    resolve_direct(load, nc, above, target, lds, lds + kDirect, res);
+    __syncthreads();
+    w[0] = res[0] | (res[1] << 32);
+    w[1] = res[2];
+  } else if (c == 0) {
+    // a long list: the first workgroup resolves it and hands the result out
+    resolve_row(load, nc, prefix, mask, above, target, lds, res);
+    __syncthreads();
+    w[0] = res[0] | (res[1] << 32);  // K > 0: non-zero
+    w[1] = res[2];                   // the kept mass > 0
+    hand_out<2>(lines, n, 2, {w[0], w[1]});
+  } else {
+    if (!wait_words<2>(line_of(lines, kOutLine, n, c) + 2, w)) return poison_chunk(out, a.V, c0);
+  }
+  write_chunk(out, a.V, c0, v, (uint32_t)w[0], w[0] >> 32, w[1]);
 }
 
 }  // namespace
 
 int filter_chunks(int V) { return (V + kFChunk - 1) / kFChunk; }
+
+bool filter_one_launch(int rows, int V) {
+  return rows <= kFusedRows && filter_chunks(V) <= kFusedChunks;
+}
+
+namespace {
+
+// Workgroups of the one-launch kernel the current device holds at once (0
+// if unknown).  Beyond that, rows wait for earlier rows to finish before
+// their workgroups are placed: still correct, but slower.  Measured (V =
+// 32,000 to 129,280, top_p = 0.9), the one launch is faster than the four
+// up to this many workgroups and slower beyond it.
+int fused_capacity(bool hist) {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cache[2][kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
+  int cap = cache[hist][dev].load(std::memory_order_relaxed);
+  if (cap > 0) return cap;
+  int per_cu = 0, cus = 0;
+  const void *k = hist ? (const void *)filter_fused_kernel<true> : (const void *)filter_fused_kernel<false>;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cap = per_cu * cus;
+  cache[hist][dev].store(cap, std::memory_order_relaxed);
+  return cap;
+}
+
+}  // namespace
 
 size_t filter_ws_bytes(int rows, int V) {
   const size_t ch = (size_t)filter_chunks(V);
@@ -959,8 +1307,13 @@ size_t filter_ws_bytes(int rows, int V) {
 
          align_up((size_t)rows * V * sizeof(uint64_t), 256) +
          align_up((size_t)rows * 8 * sizeof(uint64_t), 256) +
-         align_up((size_t)rows * 4 * sizeof(unsigned), 256);
+         align_up((size_t)rows * 4 * sizeof(unsigned), 256) +
+         (filter_one_launch(rows, V)
+              ? align_up((size_t)rows * (1 + kRowLines * ch) * kLineWords * sizeof(unsigned), 256) +
+                    (size_t)rows * ch * 256 * sizeof(uint64_t)
+              : 0);
 }
+
 
 hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int rows_b,
                          const float *logits_b, float *probs_b, int V, float temperature,
@@ -986,7 +1339,19 @@ hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int 
   a.state = (uint64_t *)b;
   b += align_up((size_t)rows * 8 * sizeof(uint64_t), 256);
   a.count = (unsigned *)b;
+  b += align_up((size_t)rows * 4 * sizeof(unsigned), 256);
+  a.sync = (unsigned *)b;
+  b += align_up((size_t)rows * (1 + kRowLines * a.chunks) * kLineWords * sizeof(unsigned), 256);
+  a.hpart = (uint64_t *)b;
   const dim3 grid(a.chunks, rows);
+  if (filter_one_launch(rows, V) && (long long)rows * a.chunks <= fused_capacity(top_p < 1.f)) {
+    hipLaunchKernelGGL(filter_clear_kernel, dim3(rows), dim3(kFThreads), 0, st, a);
+    if (top_p < 1.f)
+      hipLaunchKernelGGL(filter_fused_kernel<true>, grid, dim3(kFThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(filter_fused_kernel<false>, grid, dim3(kFThreads), 0, st, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(filter_stat_kernel, grid, dim3(kFThreads), 0, st, a);
   if (top_p < 1.f) {
     hipLaunchKernelGGL(filter_prob_kernel<true>, grid, dim3(kFThreads), 0, st, a);

@@ -29,6 +29,17 @@ def test_header_declares_the_four_calls():
         assert fn in names
 
 
+def test_binding_limits_are_the_header_limits():
+    text = open(HEADER).read()
+    defs = {}
+    for name, val in re.findall(r"^#define (MOE_\w+) (\(?[0-9 <]+\)?)", text, re.M):
+        defs[name] = eval(val, {})  # integers and shifts only
+    for name in ("MAX_TOKENS", "MAX_TOPK", "MAX_SLOTS", "MAX_EXPERTS", "MAX_SHARED",
+                 "MAX_SEQ", "MAX_DRAFT", "MAX_VOCAB", "MAX_GROUPS", "MAX_LAYERS",
+                 "FILTER_ONE_LAUNCH_ROWS", "FILTER_ONE_LAUNCH_VOCAB"):
+        assert getattr(B, name) == defs["MOE_" + name], name
+
+
 def test_library_exports_every_declared_symbol():
     lib = B.load()
     for fn in _declared():

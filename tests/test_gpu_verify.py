@@ -237,6 +237,52 @@ def test_filter_more_workgroups_than_the_chip_holds_at_once():
     _check_nucleus(got, lg, 0.8, 0.9)
 
 
+@pytest.mark.parametrize("V,top_p", [(102400, 0.9), (4099, 0.5), (129280, 1.0), (32000, 0.95)])
+def test_filter_one_launch_equals_four_launches(V, top_p):
+    """The same rows filtered in a call of more than FILTER_ONE_LAUNCH_ROWS
+    rows (four launches) and in calls of 16 rows (at most 512 workgroups,
+    which the chip holds at once: one launch whose workgroups meet at row
+    barriers): bit for bit the same, with rows whose boundary bin holds long
+    candidate lists (radix resolve) among them; no call writes the
+    workspace head."""
+    R = B.FILTER_ONE_LAUNCH_ROWS
+    rng = np.random.default_rng(V + int(top_p * 100) + 7)
+    _say(f"[filter] one launch vs four, V={V} top_p={top_p}")
+    lg = _logit_rows(rng, R + 8, V, ties=True)
+    lg[3, : V // 3] = lg[3, :1]                    # a third of the row tied
+    lg[5] = 1.5                                    # every entry tied
+    lg[R + 2] = np.round(lg[R + 2] * 4) / 4        # many small tie groups
+    lg[R + 4, : V // 2] = -np.inf                  # half masked
+    dev = torch.from_numpy(lg).cuda()
+    ws = B.Workspace()
+    four = B.verify_probs(dev, 0.7, top_p, ws=ws).clone()
+    torch.cuda.synchronize()
+    assert int(ws.buf[:256].count_nonzero()) == 0
+    for r0 in range(0, R + 8, 16):
+        one = B.verify_probs(dev[r0:r0 + 16], 0.7, top_p, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.buf[:256].count_nonzero()) == 0
+        assert torch.equal(four[r0:r0 + 16].view(torch.int32), one.view(torch.int32)), r0
+    _check_nucleus(four[:8].cpu().numpy(), lg[:8], 0.7, top_p)
+
+
+def test_filter_one_launch_at_the_longest_vocabulary():
+    """FILTER_ONE_LAUNCH_VOCAB entries (64 workgroups per row, each reading
+    every chunk's statistics and candidate count): 8 rows in one launch,
+    bit for bit what the four launches of a 129-row call give them."""
+    V = B.FILTER_ONE_LAUNCH_VOCAB
+    rng = np.random.default_rng(42)
+    _say(f"[filter] one launch, V={V}")
+    lg = _logit_rows(rng, B.FILTER_ONE_LAUNCH_ROWS + 1, V, masked=True)
+    lg[2, : V // 2] = lg[2, :1]                    # a long candidate list
+    dev = torch.from_numpy(lg).cuda()
+    ws = B.Workspace()
+    four = B.verify_probs(dev, 0.8, 0.9, ws=ws).clone()
+    one = B.verify_probs(dev[:8], 0.8, 0.9, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(four[:8].view(torch.int32), one.view(torch.int32))
+
+
 def test_filter_all_tied_rows():
     # every token of the row tied: all V entries are candidates at the
     # boundary and the index cut decides; the kept set is the first k
