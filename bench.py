@@ -484,6 +484,39 @@ def verify_gate_leg(vocabs=(102400, 129280), n_seq=4, gamma=8, reps=200, tempera
     return out
 
 
+XGMI_LINK_GBS = 153.0  # one MI355X xGMI link, each direction
+
+
+def shard_doc(whole, share, G, sweep, n_layers):
+    """The share sweep as a document: per n, one GPU's share pass (measured)
+    and, beside it, the per-link bandwidth bound of the ring all-reduce that
+    would sum the G shares' fp32 outputs, 2 (G - 1) / G x N d 4 bytes over
+    one xGMI link (a lower bound: latency and RCCL's launch are not in it).
+    Nothing here runs on a second GPU."""
+    by_n = []
+    for r in sweep:
+        ar = r["tokens"] * whole.d * 4
+        ring_us = 2 * (G - 1) / G * ar / (XGMI_LINK_GBS * 1e3)
+        rec = dict(r)
+        rec["allreduce_MB"] = round(ar / 1e6, 4)
+        rec["allreduce_ring_us_bound"] = round(ring_us, 2)
+        rec["G_gpu_pass_us_lower_bound"] = {
+            name: round(r[name]["us"] + ring_us, 2) for name in ("perslot", "dedup")}
+        by_n.append(rec)
+    return {"kind": "one GPU's share of a d_ff-sharded layer",
+            "workload": f"{whole.name}-shaped layer, every expert (routed and shared) split "
+                        f"along d_ff over {G} GPUs: one share of d_ff {share.f} "
+                        f"({share.expert_bytes} bytes per expert), gate and tokens whole; "
+                        f"{whole.n_seq} sequence(s) x n = {min(share.n_values)}.."
+                        f"{max(share.n_values)} tokens; {n_layers} weight sets rotated",
+            "G": G, "d_ff": whole.f, "share_d_ff": share.f,
+            "xgmi_link_GBs": XGMI_LINK_GBS,
+            "note": "us and GB/s are one GPU's share pass (route + expert pass timed "
+                    "apart; requested bytes of the share); the all-reduce figure is a "
+                    "bandwidth bound, not a measurement",
+            "by_n": by_n}
+
+
 def calibration_json(calib):
     return {"model": "t_us = bytes / BW + t0 (routed expert bytes; shared experts and "
                      "gate in t0)",
@@ -1020,6 +1053,11 @@ def main():
                     help="comma-separated pass sizes: instead of the bench line, K steps of "
                          "route + pass per engine at each size, queued while the GPU is held, "
                          "for a kernel-trace timeline (one JSON document)")
+    ap.add_argument("--shard", type=int, default=None,
+                    help="instead of the bench line: the n sweep on one GPU's share of the "
+                         "config's layer with every expert split along d_ff over SHARD GPUs "
+                         "(gate and tokens whole), with the summing all-reduce's per-link "
+                         "bandwidth bound beside it (one JSON document)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (for scaling HBM "
                          "byte counters) and print its byte counts")
@@ -1056,6 +1094,9 @@ def main():
         return
 
     cfg = synth.CONFIGS["v2stack" if args.rho_sweep else args.config]
+    whole = cfg
+    if args.shard:
+        cfg = synth.share_config(cfg, args.shard)
     n_head = args.n or max(cfg.n_values)
     layer_bytes = (cfg.E + cfg.S) * expert_bytes(cfg)
     n_layers = args.layers or (cfg.layers if args.rho_sweep else
@@ -1080,6 +1121,18 @@ def main():
                            f"{min(cfg.n_values)}..{max(cfg.n_values)} tokens per pass, "
                            f"{n_layers} weight sets rotated",
                "by_n": variants_leg(cfg, eng, layers, cfg.n_values, args.variant_reps)}
+        print(json.dumps(doc), flush=True)
+        return
+
+    if args.shard:
+        xs = {}
+        log("[bench] share sweep warmup")
+        run_sweep(cfg, eng, layers, xs, cfg.n_values[:2], 5, top_up=False)
+        log(f"[bench] share sweep: d_ff {whole.f} / {args.shard} = {cfg.f}")
+        points = SweepLog(args.resume) if args.resume else None
+        sweep = run_sweep(cfg, eng, layers, xs, cfg.n_values, args.reps, points=points)
+        doc = shard_doc(whole, cfg, args.shard, sweep, n_layers)
+        write_details(args.details, doc)
         print(json.dumps(doc), flush=True)
         return
 

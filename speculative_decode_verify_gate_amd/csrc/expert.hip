@@ -111,6 +111,18 @@ constexpr bool kPairDown = !UP && CTMAX > 1;
 template <bool UP, int CTMAX>
 constexpr bool kTwoStreams = UP || kPairDown<UP, CTMAX>;
 
+// Short reductions (SK, down kernel only): with K = d_ff under 32 MFMA
+// steps -- one GPU's share of a layer whose experts are split along d_ff
+// -- a 16-row tile is a few kilobytes and splitting its K over four waves
+// leaves most of them idle.  Then each wave owns two consecutive 16-row
+// tiles over the whole of K (the two-stream path), a workgroup covers
+// 2 * kWavesPerBlock tiles, and each wave stores its own outputs: every
+// output is still summed over K in step order by one wave, the same for a
+// token alone or in a tile of 16.
+constexpr int kShortKSteps = 32;
+template <bool UP, int CTMAX, bool SK>
+constexpr int kTilesPerBlock = SK ? 2 * kWavesPerBlock : (kPairDown<UP, CTMAX> ? 2 : 1);
+
 // Kernel variants: the plain engines, dedup within token groups, and a stack
 // of layers (all layers' instances in one grid, layer-major).
 constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
@@ -120,14 +132,17 @@ constexpr int kPlain = 0, kGrouped = 1, kStack = 2;
 // compaction record of token group `writer` (one workgroup per group).  The
 // dedup engine's routed instances also report U, the number of distinct
 // experts of the pass (of the token group, when grouped), to *n_distinct.
-template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
+template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR, bool SK>
 __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertArgs &a, int layer,
                                                                   int bid, int writer,
                                                                   int *ent_row, int *ent_tok,
                                                                   int *n_distinct) {
+  static_assert(!(UP && SK), "short reductions are the down kernel's");
   constexpr bool DIRECT = CTMAX == 1;
-  constexpr bool PAIR = kPairDown<UP, CTMAX>;
-  constexpr bool TWO = kTwoStreams<UP, CTMAX>;  // a second weight stream (W3, or W2's next tile)
+  constexpr bool PAIR = kPairDown<UP, CTMAX> || SK;  // two W2 tiles per wave
+  constexpr bool TWO = UP || PAIR;  // a second weight stream (W3, or W2's next tile)
+  constexpr int TPB = kTilesPerBlock<UP, CTMAX, SK>;  // 16-row tiles per workgroup
+  constexpr int CS = SK ? 1 : kWavesPerBlock;         // a wave's chunk stride
   constexpr int NB = (UP && BF16) ? 2 : 1;  // 16-byte B loads per lane and step
   using T = WT<BF16>;
   constexpr int SPC = kSpc;
@@ -141,7 +156,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
 
   const int R = UP ? a.f : a.d;  // output rows
   const int K = UP ? a.d : a.f;  // reduction length
-  const int RT = R / kTile / (PAIR ? 2 : 1);  // workgroup tiles per instance
+  const int RT = R / kTile / TPB;  // workgroups per instance
   // A stack runs each layer's grid in turn: its own weights, routing,
   // compaction record, U and buffers; the tokens are shared.  Only the stack
   // instantiation offsets the per-layer arrays.
@@ -169,10 +184,11 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
     obuf += (size_t)layer * rows * a.d;
   }
   const int inst = bid / RT;
-  const int rt = (bid - inst * RT) * (PAIR ? 2 : 1);  // first 16-row tile of the workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // this wave's first 16-row tile (SK: two per wave; else the workgroup's)
+  const int rt = (bid - inst * RT) * TPB + (SK ? 2 * wave : 0);
   const int r = lane & 15;
   const int g = lane >> 4;
   const CompactLayout CL{a.E, a.N * a.k};
@@ -297,7 +313,8 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
   u32x4 rab[SPC][NB], rbb[SPC][NB];  // DIRECT B operands of the two chunk sets
   // the first chunk of this wave leaves before the token lists are read
   // (every window holds at least NW chunks, so chunk `wave` is in window 0)
-  if (wave < nchunks) issue(wave, ra1, ra3);
+  const int first = SK ? 0 : wave;
+  if (first < nchunks) issue(first, ra1, ra3);
 
   // ---- token entries of the instance
   if (have_entries) {
@@ -436,7 +453,7 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
     }
     for (int w0 = 0; w0 < nchunks; w0 += cpw) {
       const int w1 = min(w0 + cpw, nchunks);
-      int c = w0 + wave;  // this wave's chunks: c, c + NW, ... < w1
+      int c = w0 + first;  // this wave's chunks: c, c + CS, ... < w1
       if (!(c0 == 0 && w0 == 0) && c < w1) issue(c, ra1, ra3);
       if (DIRECT) {
         if (c < w1) issue_b(c, rab);
@@ -447,23 +464,39 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
       }
       if (c < w1) {
         // steady state: two chunks per iteration, next chunk always in flight
-        for (; c + 2 * NW < w1; c += 2 * NW) {
-          issue(c + NW, rb1, rb3);
-          if (DIRECT) issue_b(c + NW, rbb);
+        for (; c + 2 * CS < w1; c += 2 * CS) {
+          issue(c + CS, rb1, rb3);
+          if (DIRECT) issue_b(c + CS, rbb);
           compute(c, ra1, ra3, rab);
-          issue(c + 2 * NW, ra1, ra3);
-          if (DIRECT) issue_b(c + 2 * NW, rab);
-          compute(c + NW, rb1, rb3, rbb);
+          issue(c + 2 * CS, ra1, ra3);
+          if (DIRECT) issue_b(c + 2 * CS, rab);
+          compute(c + CS, rb1, rb3, rbb);
         }
-        if (c + NW < w1) {
-          issue(c + NW, rb1, rb3);
-          if (DIRECT) issue_b(c + NW, rbb);
+        if (c + CS < w1) {
+          issue(c + CS, rb1, rb3);
+          if (DIRECT) issue_b(c + CS, rbb);
           compute(c, ra1, ra3, rab);
-          compute(c + NW, rb1, rb3, rbb);
+          compute(c + CS, rb1, rb3, rbb);
         } else {
           compute(c, ra1, ra3, rab);
         }
       }
+    }
+
+    if (SK) {
+      // each wave holds the whole sums of its two tiles: lane rows 4g..4g+3
+      // of each, token column r of every token tile
+#pragma unroll
+      for (int ct = 0; ct < CTMAX; ++ct) {
+        const int col = ct * kTile + r;
+        if (ct < n_ct && col < mg) {
+          float *o = obuf + (size_t)ent_row[c0 + col] * a.d + rt * kTile + 4 * g;
+          *(f32x4 *)o = acc1[ct];
+          *(f32x4 *)(o + kTile) = acc3[ct];
+        }
+      }
+      if (!DIRECT) __syncthreads();  // the staged rows are read before the next group's
+      continue;
     }
 
     // ---- the four waves' partial sums, added in wave order; wave ct then
@@ -524,12 +557,13 @@ __device__ __attribute__((always_inline)) inline void expert_tile(const ExpertAr
 // grid holds half the absent instances and, while U <= fold, every
 // workgroup runs one tile.  The first tile learns U on the way: from the
 // presence mask it builds (up) or from the compaction record (down).
-template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR>
+template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR, bool SK>
 __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(ExpertArgs a) {
   __shared__ int ent_row[MOE_MAX_SLOTS];
   __shared__ int ent_tok[MOE_MAX_SLOTS];
-  // workgroup tiles per instance (paired wide down tiles: half the rows')
-  const int RT = (UP ? a.f : a.d) / kTile / (kPairDown<UP, CTMAX> ? 2 : 1);
+  // workgroups per instance (paired wide down tiles: half the 16-row tiles;
+  // short reductions: an eighth)
+  const int RT = (UP ? a.f : a.d) / kTile / kTilesPerBlock<UP, CTMAX, SK>;
   int U = 0;
   if (VAR == kGrouped) {
     // groups fold one by one: group g's routed slots in the grid are
@@ -537,7 +571,7 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
     const int writer = (int)blockIdx.x < a.G ? (int)blockIdx.x : -1;
     const int slot = blockIdx.x / RT, rt = blockIdx.x - slot * RT;
     if (slot < a.S) {
-      expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, 0, blockIdx.x, writer, ent_row, ent_tok, &U);
+      expert_tile<BF16, UP, CTMAX, TILED, VAR, SK>(a, 0, blockIdx.x, writer, ent_row, ent_tok, &U);
       return;
     }
     const int v = slot - a.S;
@@ -549,9 +583,9 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
     const int vl = v - a.fbase[g];
     const int fg = a.fbase[g + 1] - a.fbase[g], mg = a.ibase[g + 1] - a.ibase[g];
     const int bid = (a.S + a.ibase[g] + vl) * RT + rt;
-    expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, 0, bid, writer, ent_row, ent_tok, &U);
+    expert_tile<BF16, UP, CTMAX, TILED, VAR, SK>(a, 0, bid, writer, ent_row, ent_tok, &U);
     if (fg < mg && vl + fg < U)
-      expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, 0, bid + fg * RT, -1, ent_row, ent_tok, &U);
+      expert_tile<BF16, UP, CTMAX, TILED, VAR, SK>(a, 0, bid + fg * RT, -1, ent_row, ent_tok, &U);
     return;
   }
   const bool folded = a.fold > 0;
@@ -561,42 +595,50 @@ __global__ __launch_bounds__(256, (kMinWaves<UP, CTMAX>)) void expert_kernel(Exp
     layer = bid / bpl;
     bid -= layer * bpl;
   }
-  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid, bid == 0 ? 0 : -1, ent_row, ent_tok,
+  expert_tile<BF16, UP, CTMAX, TILED, VAR, SK>(a, layer, bid, bid == 0 ? 0 : -1, ent_row, ent_tok,
                                            &U);
   if (!folded) return;
   const int slot = bid / RT;
   if (slot < a.S || slot - a.S + a.fold >= U) return;
-  expert_tile<BF16, UP, CTMAX, TILED, VAR>(a, layer, bid + a.fold * RT, -1, ent_row, ent_tok, &U);
+  expert_tile<BF16, UP, CTMAX, TILED, VAR, SK>(a, layer, bid + a.fold * RT, -1, ent_row, ent_tok, &U);
+}
+
+template <bool BF16, bool UP, int CTMAX, bool TILED, int VAR, bool SK>
+hipError_t launch_expert_kernel(const ExpertArgs &a, long long blocks, hipStream_t st) {
+  // the dynamic-LDS limit of each kernel, once per kernel: the most any
+  // shape asks of it (the wide tiles may exceed the default 64 KB)
+  static const hipError_t set = hipFuncSetAttribute(
+      (const void *)expert_kernel<BF16, UP, CTMAX, TILED, VAR, SK>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, expert_lds_bound(CTMAX > 1));
+  if (set != hipSuccess) return set;
+  hipLaunchKernelGGL((expert_kernel<BF16, UP, CTMAX, TILED, VAR, SK>), dim3((unsigned)blocks),
+                     dim3(kBlock), a.lds_bytes, st, a);
+  return hipGetLastError();
 }
 
 template <bool BF16, bool UP, bool TILED, int VAR>
 hipError_t launch_expert_layout(const ExpertArgs &a, hipStream_t st) {
   const int R = UP ? a.f : a.d;
+  const int K = UP ? a.d : a.f;
   const int routed = VAR == kGrouped ? a.fbase[a.G] : (a.fold > 0 ? a.fold : a.n_routed);
-  // wide down tiles are paired (d is a multiple of 32, so the tiles pair up)
-  const bool pair = !UP && a.N > kTile;
-  const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile) / (pair ? 2 : 1);
+  const bool wide = a.N > kTile;
+  // a short reduction gives every wave two whole tiles (eight per
+  // workgroup), when the rows make whole workgroups
+  const bool sk = !UP && K / WT<BF16>::kStep < kShortKSteps &&
+                  (R / kTile) % (2 * kWavesPerBlock) == 0;
+  // else wide down tiles are paired (d is a multiple of 32, so they pair up)
+  const int tpb = sk ? 2 * kWavesPerBlock : (!UP && wide ? 2 : 1);
+  const long long blocks = (long long)a.L * (routed + a.S) * (R / kTile) / tpb;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // the dynamic-LDS limit of each kernel, once per kernel: the most any
-  // shape asks of it (the wide tiles may exceed the default 64 KB)
-  static const hipError_t set_wide = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 4, TILED, VAR>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, expert_lds_bound(true));
-  static const hipError_t set_narrow = hipFuncSetAttribute(
-      (const void *)expert_kernel<BF16, UP, 1, TILED, VAR>,
-      hipFuncAttributeMaxDynamicSharedMemorySize, expert_lds_bound(false));
-  if (set_wide != hipSuccess) return set_wide;
-  if (set_narrow != hipSuccess) return set_narrow;
-  if (a.lds_bytes < 0 || a.lds_bytes > expert_lds_bound(a.N > kTile))
-    return hipErrorInvalidValue;
-  if (a.N > kTile)
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 4, TILED, VAR>), dim3((unsigned)blocks),
-                       dim3(kBlock), a.lds_bytes, st, a);
-  else
-    hipLaunchKernelGGL((expert_kernel<BF16, UP, 1, TILED, VAR>), dim3((unsigned)blocks),
-                       dim3(kBlock), a.lds_bytes, st, a);
-  return hipGetLastError();
+  if (a.lds_bytes < 0 || a.lds_bytes > expert_lds_bound(wide)) return hipErrorInvalidValue;
+  if constexpr (!UP) {
+    if (sk)
+      return wide ? launch_expert_kernel<BF16, UP, 4, TILED, VAR, true>(a, blocks, st)
+                  : launch_expert_kernel<BF16, UP, 1, TILED, VAR, true>(a, blocks, st);
+  }
+  return wide ? launch_expert_kernel<BF16, UP, 4, TILED, VAR, false>(a, blocks, st)
+              : launch_expert_kernel<BF16, UP, 1, TILED, VAR, false>(a, blocks, st);
 }
 
 template <bool BF16, bool UP, int VAR>

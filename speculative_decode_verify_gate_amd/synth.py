@@ -84,6 +84,35 @@ CONFIGS = {
 }
 
 
+def share_config(cfg: LayerConfig, G: int) -> LayerConfig:
+    """One GPU's share of the layer when every expert (routed and shared) is
+    split along d_ff over G GPUs: the same d, E, k and S, d_ff / G.  The
+    gate and the hidden states stay whole (replicated on every GPU).  The
+    kernels need d_ff / G to be a multiple of 32."""
+    if G < 1 or cfg.f % G or (cfg.f // G) % 32:
+        raise ValueError(f"d_ff = {cfg.f} does not split into {G} shares of a multiple of 32")
+    return LayerConfig(f"{cfg.name}_share{G}", cfg.d, cfg.E, cfg.k, cfg.f // G, cfg.S, cfg.wdtype,
+                       cfg.rho, cfg.seed, cfg.n_values, cfg.n_seq, cfg.layers, cfg.rhos)
+
+
+def shard_layer(lay, G: int, g: int):
+    """Share g of G of a layer's weights (make_layer's dict): rows
+    [g f/G, (g+1) f/G) of W1 and W3 and the same columns of W2, for the
+    routed and the shared experts; the gate whole.  Copies, contiguous."""
+    f = lay["w13"].shape[2]
+    if f % G:
+        raise ValueError("d_ff does not split into G shares")
+    a, b = g * (f // G), (g + 1) * (f // G)
+    out = {"gate_w": lay["gate_w"],
+           "w13": lay["w13"][:, :, a:b, :].contiguous(),
+           "w2": lay["w2"][:, :, a:b].contiguous(),
+           "ws13": None, "ws2": None}
+    if lay.get("ws13") is not None:
+        out["ws13"] = lay["ws13"][:, :, a:b, :].contiguous()
+        out["ws2"] = lay["ws2"][:, :, a:b].contiguous()
+    return out
+
+
 def _gen(seed, device):
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))

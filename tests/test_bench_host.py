@@ -43,3 +43,18 @@ def test_no_log_file_without_a_path(tmp_path):
     log = bench.SweepLog(None)
     log.put({"n": 1}, {"x": 1})
     assert list(tmp_path.iterdir()) == []
+
+
+def test_share_document_bounds_the_allreduce_per_link():
+    whole = synth.CONFIGS["v3"]
+    share = synth.share_config(whole, 8)
+    sweep = [{"n": 16, "tokens": 64, "perslot": {"us": 700.0}, "dedup": {"us": 500.0}}]
+    doc = bench.shard_doc(whole, share, 8, sweep, 2)
+    rec = doc["by_n"][0]
+    # 64 tokens x 7168 fp32 = 1,835,008 bytes; a ring moves 2 (G - 1) / G of
+    # them over each link: 3,211,264 bytes at 153 GB/s = 20.99 us
+    assert rec["allreduce_MB"] == round(64 * 7168 * 4 / 1e6, 4)
+    assert rec["allreduce_ring_us_bound"] == 20.99
+    assert rec["G_gpu_pass_us_lower_bound"] == {"perslot": 720.99, "dedup": 520.99}
+    assert doc["share_d_ff"] == 256 and doc["G"] == 8
+    json.dumps(doc)

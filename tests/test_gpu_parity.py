@@ -115,6 +115,9 @@ SMALL = [
     ("bf16-v2like", 512, 64, 6, 352, 2, "bf16"),
     ("bf16-top1", 256, 16, 1, 128, 0, "bf16"),
     ("bf16-single-expert", 128, 1, 1, 96, 0, "bf16"),
+    # d = 160: 10 row tiles, not whole workgroups of eight, so the short
+    # d_ff takes the four-waves-per-tile down kernel
+    ("bf16-rows-in-tens", 160, 8, 2, 192, 1, "bf16"),
 ]
 
 
