@@ -1025,13 +1025,15 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
 // line queue behind each other at the memory side, so what many
 // workgroups poll is spread over lines.  Every word below is written once
 // per call and is non-zero once written, so a waiter polls the word itself:
-//   arrival   one count (barrier 2, whose last arrival does the row's part)
-//   stat[c]   chunk c's max and sum (float bits; M is finite or -inf, so
-//             non-zero)
+//   arrival   one count (the histogram meeting, whose last arrival selects
+//             the bin)
+//   stat[c]   chunk c's max and sum, float bits (non-zero: with a finite max
+//             the sum is at least 1, and a -inf max has non-zero bits)
 //   count[c]  chunk c's number of candidates + 1
-//   out[c]    what a last arrival hands to workgroup c, polled only by it:
-//             words 0-1 the selected bin (barrier 2), words 2-3 the boundary
-//             of a long candidate list (barrier 3)
+//   out[c]    what is handed to workgroup c, polled only by it: words 0-1 the
+//             selected bin (from the histogram meeting's last arrival), words
+//             2-3 the boundary of a long candidate list (from the row's first
+//             workgroup)
 constexpr int kLineWords = 32;  // 128 bytes
 constexpr int kRowLines = 3;    // stat, count, out: lines per chunk
 __device__ inline unsigned *row_lines(const FilterArgs &a, int row) {
