@@ -362,12 +362,12 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  * twice that of the logits (the head is not used).  With at most
  * MOE_FILTER_ONE_LAUNCH_ROWS rows, V <= MOE_FILTER_ONE_LAUNCH_VOCAB and a
  * grid of rows x ceil(V / 4096) workgroups that the device holds at once,
- * the filter is one launch whose workgroups meet at row
- * barriers (after a small launch that clears them), else four launches;
- * both give the same bits.  The barriers' waits are bounded: should a
- * row's workgroups fail to meet within about a second (not expected: they
- * are dispatched in index order, a row's consecutively), that row's
- * outputs are NaN. 
+ * the filter is one launch whose workgroups meet at row barriers (their
+ * words in the workspace carry a tag of the call, so nothing is cleared
+ * between calls), else four launches; both give the same bits.  The
+ * barriers' waits are bounded: should a row's workgroups fail to meet
+ * within about a second (not expected: they are dispatched in index order,
+ * a row's consecutively), that row's outputs are NaN.
  * Feed the verifier's rows as p_verify and the draft's as q_draft. */
 int moe_verify_probs(int32_t rows, int32_t vocab, const float *logits, float temperature,
                      float top_p, float *probs, void *workspace, size_t *workspace_bytes,

@@ -19,8 +19,8 @@ hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, 
 // out), chunked over the chip through a workspace of filter_ws_bytes(rows_a
 // + rows_b, V): rows_a rows of logits_a into probs_a and rows_b (may be 0)
 // rows of logits_b into probs_b, with the same settings, in one sequence of
-// launches: one (after a small clearing launch) when filter_one_launch(rows,
-// V), else four.
+// launches: one when filter_one_launch(rows, V) and the grid fits the device
+// at once, else four.
 size_t filter_ws_bytes(int rows, int V);
 bool filter_one_launch(int rows, int V);
 hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int rows_b,

@@ -32,6 +32,8 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "coherent.h"
 #include "kernels.h"
@@ -439,12 +441,12 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 // Two schedules run these phases with the same arithmetic, so they give the
 // same bits:
 //   one launch (rows <= kFusedRows, chunks <= kFusedChunks, and a grid the
-//     chip holds at once), after a small launch that
-//     clears the row's synchronisation lines: each workgroup keeps its
-//     chunk in registers from the logits load to the output store, and the
-//     row's workgroups meet three times.  After stat every workgroup polls
-//     all the chunks' statistics and reduces them itself; after the
-//     histogram (each chunk's bins in a slot of its own) the last to arrive
+//     chip holds at once): each workgroup keeps its chunk in registers from
+//     the logits load to the output store, and the row's workgroups meet
+//     three times, on synchronisation words tagged with the call (nothing
+//     needs clearing between calls).  After stat every workgroup polls all
+//     the chunks' statistics and reduces them itself; after the histogram
+//     (each chunk's bins in a slot of its own) the row's first workgroup
 //     sums them, selects the bin and hands it to every workgroup's line;
 //     after the gather (each chunk's candidates in a stretch of its own,
 //     their count on its line) every workgroup polls the counts and ranks a
@@ -493,7 +495,8 @@ struct FilterArgs {
   uint64_t *state;     // [rows][8]: prefix, mask, mass above, target; K, index cut, kept
                        // mass; the row's M and S (float bits, S in the high half)
   unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
-  unsigned *sync;      // one launch: [rows][1 + 3 chunks] 128-byte lines (row barriers)
+  unsigned *sync;      // one launch: [rows][4 chunks] 128-byte synchronisation lines
+  uint64_t tag;        // one launch: this call's tag (distinct per call, halves non-zero)
   uint64_t *hpart;     // one launch: [rows][chunks][256] the chunks' first-level histograms
 };
 
@@ -1020,68 +1023,110 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
 
 // ---- one launch
 
-// Synchronisation lines of a row (128 bytes each, cleared by
-// filter_clear_kernel before the launch).  Device-scope accesses to one
-// line queue behind each other at the memory side, so what many
-// workgroups poll is spread over lines.  Every word below is written once
-// per call and is non-zero once written, so a waiter polls the word itself:
-//   arrival   one count (the histogram meeting, whose last arrival selects
-//             the bin)
-//   stat[c]   chunk c's max and sum, float bits (non-zero: with a finite max
-//             the sum is at least 1, and a -inf max has non-zero bits)
-//   count[c]  chunk c's number of candidates + 1
-//   out[c]    what is handed to workgroup c, polled only by it: words 0-1 the
-//             selected bin (from the histogram meeting's last arrival), words
-//             2-3 the boundary of a long candidate list (from the row's first
-//             workgroup)
+// Synchronisation lines of a row, 128 bytes each.  Device-scope accesses to
+// one line queue behind each other at the memory side, so what many
+// workgroups poll is spread over lines.  Nothing clears them: every word a
+// waiter accepts carries the call's 64-bit tag (FilterArgs::tag, distinct
+// for every call of the process, both 32-bit halves non-zero), so what an
+// earlier call or other data left there is never taken for this call's.  A
+// value shares its 64-bit words with the tag: the low half holds the value,
+// the high half one half of the tag, and a slot is accepted when both its
+// words carry their halves.  Per chunk c of the row:
+//   stat[c]   words 0-1: chunk c's max and sum (float bits) | tag halves
+//   count[c]  words 0-1: chunk c's number of candidates | tag halves
+//   hist[c]   word 0: the tag, once chunk c's histogram slot is written
+//   out[c]    polled only by workgroup c, four tagged 32-bit values each:
+//             words 0-3 the selected bin (from the row's first workgroup,
+//             which sums the histograms), words 4-7 the boundary of a long
+//             candidate list (from the same workgroup)
 constexpr int kLineWords = 32;  // 128 bytes
-constexpr int kRowLines = 3;    // stat, count, out: lines per chunk
+constexpr int kRowLines = 4;    // stat, count, hist, out: lines per chunk
+constexpr int kStatLine = 0, kCountLine = 1, kHistLine = 2, kOutLine = 3;
 __device__ inline unsigned *row_lines(const FilterArgs &a, int row) {
-  return a.sync + (size_t)row * (1 + kRowLines * a.chunks) * kLineWords;
+  return a.sync + (size_t)row * kRowLines * a.chunks * kLineWords;
 }
 __device__ inline uint64_t *line_of(unsigned *lines, int kind, int n, int c) {
-  return (uint64_t *)(lines + (size_t)(1 + kind * n + c) * kLineWords);
+  return (uint64_t *)(lines + (size_t)(kind * n + c) * kLineWords);
 }
-constexpr int kStatLine = 0, kCountLine = 1, kOutLine = 2;
-
-// Before the one launch: the row's synchronisation lines start at zero.
-// One workgroup per row.
-__global__ __launch_bounds__(kFThreads) void filter_clear_kernel(FilterArgs a) {
-  unsigned *l = row_lines(a, blockIdx.x);
-  const int words = (1 + kRowLines * a.chunks) * kLineWords;
-  for (int i = threadIdx.x; i < words; i += kFThreads) l[i] = 0u;
+__device__ inline uint64_t with_tag(uint32_t v, uint32_t half) {
+  return (uint64_t)v | ((uint64_t)half << 32);
 }
 
-// Wait (bounded) until word 0 of line t of `first` is non-zero for every
-// t < n; thread t < n gets line t's word.  False if the wait gave up
-// (the same in every thread).
-__device__ inline bool wait_all(unsigned *lines, int kind, unsigned n, uint64_t &mine) {
-  uint64_t v = 0;
+// A value and the call's tag in two words of line c (one 64-bit store each).
+__device__ inline void put_tagged(uint64_t *w, uint32_t v0, uint32_t v1, uint64_t tag) {
+  store_coherent64(w, with_tag(v0, (uint32_t)tag));
+  store_coherent64(w + 1, with_tag(v1, (uint32_t)(tag >> 32)));
+}
+
+// Wait (bounded) until line t of `kind` holds a tagged value for every
+// t < n; thread t < n gets its line's two value halves.  False if the wait
+// gave up (the same in every thread).
+__device__ inline bool wait_tagged(unsigned *lines, int kind, unsigned n, uint64_t tag,
+                                   uint32_t &v0, uint32_t &v1) {
   const uint64_t *p = threadIdx.x < n ? line_of(lines, kind, (int)n, threadIdx.x) : nullptr;
+  uint64_t w0 = 0, w1 = 0;
+  bool ok = p == nullptr;
   for (unsigned i = 0;; ++i) {
-    if (p && v == 0) v = load_coherent64(p);
-    if (__syncthreads_and(!p || v != 0)) break;
+    if (!ok) {
+      w0 = load_coherent64(p);
+      w1 = load_coherent64(p + 1);
+      ok = (uint32_t)(w0 >> 32) == (uint32_t)tag && (uint32_t)(w1 >> 32) == (uint32_t)(tag >> 32);
+    }
+    if (__syncthreads_and(ok)) break;
     if (i == kSpinLimit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
-  mine = v;
+  v0 = (uint32_t)w0;
+  v1 = (uint32_t)w1;
   return true;
 }
 
-// Wait (bounded) until the NW words at w are all non-zero: false if the
-// wait gave up.  Every thread gets the words.
-template <int NW>
-__device__ inline bool wait_words(const uint64_t *w, uint64_t (&got)[NW]) {
-  __shared__ uint64_t s_w[NW];
+// Wait (bounded) until word `word` of line t of `kind` equals the tag, for
+// every t < n.
+__device__ inline bool wait_flags(unsigned *lines, int kind, unsigned n, int word, uint64_t tag) {
+  const uint64_t *p =
+      threadIdx.x < n ? line_of(lines, kind, (int)n, threadIdx.x) + word : nullptr;
+  bool ok = p == nullptr;
+  for (unsigned i = 0;; ++i) {
+    if (!ok) ok = load_coherent64(p) == tag;
+    if (__syncthreads_and(ok)) break;
+    if (i == kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
+// The first workgroup's result for every workgroup of the row: four 32-bit
+// values, each in a word of its own with a half of the tag (words
+// [first, first + 4) of each out line), so no store has to land before
+// another.
+__device__ inline void hand_out(unsigned *lines, unsigned n, int first, const uint32_t (&v)[4],
+                                uint64_t tag) {
+  for (unsigned i = threadIdx.x; i < n; i += kFThreads) {
+    uint64_t *o = line_of(lines, kOutLine, (int)n, i) + first;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      store_coherent64(o + k, with_tag(v[k], (uint32_t)(k & 1 ? tag >> 32 : tag)));
+  }
+}
+
+// Workgroup c's share of a hand-out: wait (bounded) until the four words
+// carry the tag, then every thread gets the values.  False if the wait gave
+// up.
+__device__ inline bool take_out(unsigned *lines, unsigned n, int c, int first, uint64_t tag,
+                                uint32_t (&v)[4]) {
+  __shared__ uint32_t s_v[4];
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
+    const uint64_t *o = line_of(lines, kOutLine, (int)n, c) + first;
     int ok = 1;
     for (unsigned i = 0;; ++i) {
       bool all = true;
 #pragma unroll
-      for (int k = 0; k < NW; ++k) {
-        s_w[k] = load_coherent64(w + k);
-        all = all && s_w[k] != 0;
+      for (int k = 0; k < 4; ++k) {
+        const uint64_t x = load_coherent64(o + k);
+        s_v[k] = (uint32_t)x;
+        all = all && (uint32_t)(x >> 32) == (uint32_t)(k & 1 ? tag >> 32 : tag);
       }
       if (all) break;
       if (i == kSpinLimit) {
@@ -1094,16 +1139,8 @@ __device__ inline bool wait_words(const uint64_t *w, uint64_t (&got)[NW]) {
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < NW; ++k) got[k] = s_w[k];
+  for (int k = 0; k < 4; ++k) v[k] = s_v[k];
   return s_ok != 0;
-}
-
-// Words [first, first + NW) of every workgroup's out line.
-template <int NW>
-__device__ inline void hand_out(unsigned *lines, unsigned n, int first, const uint64_t (&val)[NW]) {
-  for (unsigned i = threadIdx.x; i < n; i += kFThreads)
-#pragma unroll
-    for (int k = 0; k < NW; ++k) store_coherent64(line_of(lines, kOutLine, n, i) + first + k, val[k]);
 }
 
 // A wait gave up: the chunk's output is NaN, so the failure shows.
@@ -1115,10 +1152,11 @@ __device__ inline void poison_chunk(float *out, int V, int c0) {
 }
 
 template <bool HIST>
-__global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
+__device__ __attribute__((always_inline)) inline void filter_fused(const FilterArgs &a) {
   const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int c0 = c * kFChunk;
   const unsigned n = (unsigned)a.chunks;
+  const uint64_t tag = a.tag;
   unsigned *lines = row_lines(a, row);
   __shared__ float fs[kFWaves];
   __shared__ unsigned long long lds[2 * kDirect];  // histogram copies, then the resolve's arrays
@@ -1132,13 +1170,15 @@ __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
   // the chunks' statistics: each workgroup reduces all of them itself (the
   // fixed-order reduction of the four-launch schedule)
   const float2 cs = chunk_stat(v, a.temperature, fs);
-  if (tid == 0) store_coherent64(line_of(lines, kStatLine, n, c), ms_bits(cs));
+  if (tid == 0)
+    put_tagged(line_of(lines, kStatLine, n, c), __float_as_uint(cs.x), __float_as_uint(cs.y), tag);
   wait_stores();
-  uint64_t got = 0;
-  if (!wait_all(lines, kStatLine, n, got)) return poison_chunk(out, a.V, c0);
+  uint32_t lo0 = 0, lo1 = 0;
+  if (!wait_tagged(lines, kStatLine, n, tag, lo0, lo1)) return poison_chunk(out, a.V, c0);
   float2 ms;
   {
-    const float2 t = tid < (int)n ? ms_of(got) : make_float2(-INFINITY, 0.f);
+    const float2 t = tid < (int)n ? make_float2(__uint_as_float(lo0), __uint_as_float(lo1))
+                                  : make_float2(-INFINITY, 0.f);
     float m = block_all(t.x, fs, [](float x, float y) { return fmaxf(x, y); });
     float S;
     {
@@ -1154,7 +1194,7 @@ __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
     store_chunk(out, a.V, c0, v);
     return;
   }
-  // the chunk's histogram into its own slot; the row's last arrival sums
+  // the chunk's histogram into its own slot; the row's first workgroup sums
   // them, selects the bin and hands it out
   uint64_t *part = a.hpart + (size_t)row * a.chunks * 256;
   {
@@ -1169,24 +1209,23 @@ __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
     __syncthreads();
     store_coherent64(part + (size_t)c * 256 + tid,
                      lds[tid] + lds[256 + tid] + lds[512 + tid] + lds[768 + tid]);
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) store_coherent64(line_of(lines, kHistLine, n, c), tag);
   }
   uint32_t prefix = 0, mask = 0xC0000000u | (255u << kFirstShift);
   uint64_t above = 0, target = 0;
-  __shared__ int s_last;
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(lines, 1u) == n - 1u;
-  __syncthreads();
   uint64_t w[2];
-  if (s_last) {
-    uint64_t h = 0;  // the row's bin tid: the chunks' counts (16 loads in flight)
-    for (unsigned q0 = 0; q0 < n; q0 += 16) {
-      uint64_t t[16];
+  if (c == 0) {
+    if (!wait_flags(lines, kHistLine, n, 0, tag)) return poison_chunk(out, a.V, c0);
+    uint64_t h = 0;  // the row's bin tid: the chunks' counts (eight loads in flight)
+    for (unsigned q0 = 0; q0 < n; q0 += 8) {
+      uint64_t t[8];
 #pragma unroll
-      for (unsigned j = 0; j < 16; ++j)
+      for (unsigned j = 0; j < 8; ++j)
         t[j] = q0 + j < n ? load_coherent64(part + (size_t)(q0 + j) * 256 + tid) : 0ull;
 #pragma unroll
-      for (unsigned j = 0; j < 16; ++j) h += t[j];
+      for (unsigned j = 0; j < 8; ++j) h += t[j];
     }
     __syncthreads();  // every thread has read its copy bins
     lds[tid] = h;
@@ -1194,18 +1233,19 @@ __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
     uint32_t pf = 0, mk = 0xC0000000u;
     select_level<256, false>((const uint64_t *)lds, kFirstShift, target, pf, mk, above, a.top_p);
     prefix = pf;
-    // above < W < 2^53 and the bin + 1 <= 256: one word, non-zero
-    w[0] = above | ((uint64_t)((pf >> kFirstShift) + 1) << 54);
-    w[1] = target | (1ull << 63);
-    hand_out<2>(lines, n, 0, {w[0], w[1]});
+    // above < target <= W < 2^53: their high words leave room for the bin
+    const uint32_t v[4] = {(uint32_t)above, (uint32_t)(above >> 32) | ((pf >> kFirstShift) << 24),
+                           (uint32_t)target, (uint32_t)(target >> 32)};
+    hand_out(lines, n, 0, v, tag);
   } else {
-    if (!wait_words<2>(line_of(lines, kOutLine, n, c), w)) return poison_chunk(out, a.V, c0);
-    above = w[0] & ((1ull << 54) - 1);
-    prefix = (uint32_t)((w[0] >> 54) - 1) << kFirstShift;
-    target = w[1] & ~(1ull << 63);
+    uint32_t v[4];
+    if (!take_out(lines, n, c, 0, tag, v)) return poison_chunk(out, a.V, c0);
+    above = (uint64_t)v[0] | ((uint64_t)(v[1] & 0xFFFFFFu) << 32);
+    prefix = (v[1] >> 24) << kFirstShift;
+    target = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
   }
   // the chunk's candidates (entries in the bin) into its own stretch of the
-  // row's list, their number + 1 into its count line
+  // row's list, their number into its count line
   uint64_t *cand = a.cand + (size_t)row * a.V;
   {
     uint32_t mine = 0;
@@ -1226,13 +1266,13 @@ __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
     }
     wait_stores();
     __syncthreads();
-    if (tid == 0) store_coherent64(line_of(lines, kCountLine, n, c), (uint64_t)total + 1);
+    if (tid == 0) put_tagged(line_of(lines, kCountLine, n, c), total, total, tag);
   }
   wait_stores();
-  if (!wait_all(lines, kCountLine, n, got)) return poison_chunk(out, a.V, c0);
+  if (!wait_tagged(lines, kCountLine, n, tag, lo0, lo1)) return poison_chunk(out, a.V, c0);
   uint32_t nc;
   {
-    const uint32_t k_t = tid < (int)n ? (uint32_t)got - 1u : 0u;
+    const uint32_t k_t = tid < (int)n ? lo0 : 0u;
     const uint32_t o = block_exclusive(k_t, nc);
     if (tid < (int)n) off[tid] = o;
     if (tid == 0) off[n] = nc;
@@ -1259,13 +1299,31 @@ __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
     // a long list: the first workgroup resolves it and hands the result out
     resolve_row(load, nc, prefix, mask, above, target, lds, res);
     __syncthreads();
-    w[0] = res[0] | (res[1] << 32);  // K > 0: non-zero
-    w[1] = res[2];                   // the kept mass > 0
-    hand_out<2>(lines, n, 2, {w[0], w[1]});
+    w[0] = res[0] | (res[1] << 32);
+    w[1] = res[2];
+    const uint32_t v[4] = {(uint32_t)res[0], (uint32_t)res[1], (uint32_t)res[2],
+                           (uint32_t)(res[2] >> 32)};
+    hand_out(lines, n, 4, v, tag);
   } else {
-    if (!wait_words<2>(line_of(lines, kOutLine, n, c) + 2, w)) return poison_chunk(out, a.V, c0);
+    uint32_t v[4];
+    if (!take_out(lines, n, c, 4, tag, v)) return poison_chunk(out, a.V, c0);
+    w[0] = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
+    w[1] = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
   }
   write_chunk(out, a.V, c0, v, (uint32_t)w[0], w[0] >> 32, w[1]);
+}
+
+template <bool HIST>
+__global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
+  filter_fused<HIST>(a);
+}
+
+// The same schedule held to 7 waves per SIMD (a few registers spilled):
+// one more workgroup per CU, for grids between the two kernels' capacities
+// (a call of 68 rows of 102,400 entries).
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(7))) void
+filter_fused_dense_kernel(FilterArgs a) {
+  filter_fused<true>(a);
 }
 
 }  // namespace
@@ -1278,25 +1336,47 @@ bool filter_one_launch(int rows, int V) {
 
 namespace {
 
+// A tag for one call of the one-launch filter: a process-wide counter from
+// a random start, mixed (splitmix64), both halves made non-zero.  Distinct
+// for every call of the process; a word left by another process or by
+// other data matches it by chance with odds of about 2^-64.
+uint64_t next_tag() {
+  static std::atomic<uint64_t> counter{[] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ rd() ^
+           (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  }()};
+  uint64_t z = counter.fetch_add(0x9E3779B97F4A7C15ull, std::memory_order_relaxed);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  if ((uint32_t)z == 0) z |= 1u;
+  if ((z >> 32) == 0) z |= 1ull << 32;
+  return z;
+}
+
 // Workgroups of the one-launch kernel the current device holds at once (0
 // if unknown).  Beyond that, rows wait for earlier rows to finish before
 // their workgroups are placed: still correct, but slower.  Measured (V =
 // 32,000 to 129,280, top_p = 0.9), the one launch is faster than the four
 // up to this many workgroups and slower beyond it.
-int fused_capacity(bool hist) {
+// kind: 0 the softmax-only kernel, 1 the top-p kernel, 2 its dense copy.
+int fused_capacity(int kind) {
   constexpr int kDevices = 64;
-  static std::atomic<int> cache[2][kDevices];
+  static std::atomic<int> cache[3][kDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
-  int cap = cache[hist][dev].load(std::memory_order_relaxed);
+  int cap = cache[kind][dev].load(std::memory_order_relaxed);
   if (cap > 0) return cap;
   int per_cu = 0, cus = 0;
-  const void *k = hist ? (const void *)filter_fused_kernel<true> : (const void *)filter_fused_kernel<false>;
+  const void *k = kind == 0   ? (const void *)filter_fused_kernel<false>
+                  : kind == 1 ? (const void *)filter_fused_kernel<true>
+                              : (const void *)filter_fused_dense_kernel;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   cap = per_cu * cus;
-  cache[hist][dev].store(cap, std::memory_order_relaxed);
+  cache[kind][dev].store(cap, std::memory_order_relaxed);
   return cap;
 }
 
@@ -1311,7 +1391,7 @@ size_t filter_ws_bytes(int rows, int V) {
          align_up((size_t)rows * 8 * sizeof(uint64_t), 256) +
          align_up((size_t)rows * 4 * sizeof(unsigned), 256) +
          (filter_one_launch(rows, V)
-              ? align_up((size_t)rows * (1 + kRowLines * ch) * kLineWords * sizeof(unsigned), 256) +
+              ? align_up((size_t)rows * kRowLines * ch * kLineWords * sizeof(unsigned), 256) +
                     (size_t)rows * ch * 256 * sizeof(uint64_t)
               : 0);
 }
@@ -1343,16 +1423,23 @@ hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int 
   a.count = (unsigned *)b;
   b += align_up((size_t)rows * 4 * sizeof(unsigned), 256);
   a.sync = (unsigned *)b;
-  b += align_up((size_t)rows * (1 + kRowLines * a.chunks) * kLineWords * sizeof(unsigned), 256);
+  b += align_up((size_t)rows * kRowLines * a.chunks * kLineWords * sizeof(unsigned), 256);
   a.hpart = (uint64_t *)b;
   const dim3 grid(a.chunks, rows);
-  if (filter_one_launch(rows, V) && (long long)rows * a.chunks <= fused_capacity(top_p < 1.f)) {
-    hipLaunchKernelGGL(filter_clear_kernel, dim3(rows), dim3(kFThreads), 0, st, a);
-    if (top_p < 1.f)
-      hipLaunchKernelGGL(filter_fused_kernel<true>, grid, dim3(kFThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(filter_fused_kernel<false>, grid, dim3(kFThreads), 0, st, a);
-    return hipGetLastError();
+  if (filter_one_launch(rows, V)) {
+    const long long wgs = (long long)rows * a.chunks;
+    const bool hist = top_p < 1.f;
+    const bool fits = wgs <= fused_capacity(hist ? 1 : 0);
+    if (fits || (hist && wgs <= fused_capacity(2))) {
+      a.tag = next_tag();
+      if (!hist)
+        hipLaunchKernelGGL(filter_fused_kernel<false>, grid, dim3(kFThreads), 0, st, a);
+      else if (fits)
+        hipLaunchKernelGGL(filter_fused_kernel<true>, grid, dim3(kFThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL(filter_fused_dense_kernel, grid, dim3(kFThreads), 0, st, a);
+      return hipGetLastError();
+    }
   }
   hipLaunchKernelGGL(filter_stat_kernel, grid, dim3(kFThreads), 0, st, a);
   if (top_p < 1.f) {

@@ -240,11 +240,11 @@ def test_filter_more_workgroups_than_the_chip_holds_at_once():
 @pytest.mark.parametrize("V,top_p", [(102400, 0.9), (4099, 0.5), (129280, 1.0), (32000, 0.95)])
 def test_filter_one_launch_equals_four_launches(V, top_p):
     """The same rows filtered in a call of more than FILTER_ONE_LAUNCH_ROWS
-    rows (four launches) and in calls of 16 rows (at most 512 workgroups,
-    which the chip holds at once: one launch whose workgroups meet at row
-    barriers): bit for bit the same, with rows whose boundary bin holds long
-    candidate lists (radix resolve) among them; no call writes the
-    workspace head."""
+    rows (four launches), in calls of 16 rows (at most 512 workgroups, which
+    the chip holds at once: one launch whose workgroups meet at row
+    barriers) and in a call of 68 rows: bit for bit the same, with rows
+    whose boundary bin holds long candidate lists (radix resolve) among
+    them; no call writes the workspace head."""
     R = B.FILTER_ONE_LAUNCH_ROWS
     rng = np.random.default_rng(V + int(top_p * 100) + 7)
     _say(f"[filter] one launch vs four, V={V} top_p={top_p}")
@@ -263,6 +263,11 @@ def test_filter_one_launch_equals_four_launches(V, top_p):
         torch.cuda.synchronize()
         assert int(ws.buf[:256].count_nonzero()) == 0
         assert torch.equal(four[r0:r0 + 16].view(torch.int32), one.view(torch.int32)), r0
+    # 68 rows: at V = 102,400, 1,700 workgroups, more than the one-launch
+    # kernel holds at six per CU (the denser copy of it takes them)
+    one = B.verify_probs(dev[:68], 0.7, top_p, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(four[:68].view(torch.int32), one.view(torch.int32))
     _check_nucleus(four[:8].cpu().numpy(), lg[:8], 0.7, top_p)
 
 
