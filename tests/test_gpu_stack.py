@@ -79,12 +79,12 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("n", [1, 5, 16, 17, 64])
 @pytest.mark.parametrize("engine", ["perslot", "dedup"])
-def test_stack_equals_per_layer_calls(case, n, engine):
+@pytest.mark.parametrize("L", [1, 3])
+def test_stack_equals_per_layer_calls(case, n, engine, L):
     name, d, E, k, f, S, wdt = case
     if n * k > B.MAX_SLOTS:
         pytest.skip("beyond the slot limit")
     cfg = small_config(name, d, E, k, f, S, wdt)
-    L = 3
     _say(f"[stack] {name} L={L} n={n} {engine}")
     for bias in (False, True):
         stack = _make_stack(cfg, L, bias=bias, tiled=(n % 2 == 1))
@@ -176,6 +176,38 @@ def test_full_v2lite_stack_slice():
             if engine == "dedup":
                 assert int(nu[l].item()) == int(rnu.item())
     del stack
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,n", [("v2lite", 1), ("v2lite", 16), ("v3", 4), ("v3", 16)])
+def test_one_layer_call_at_full_shape(name, n):
+    """One full-shape layer as a one-layer stack (route and pass in one
+    call) equals route followed by each engine's pass, bit for bit."""
+    cfg = synth.CONFIGS[name]
+    shape = B.shape_of(cfg)
+    _say(f"[stack] one {name} layer as one call, N = {n}")
+    lay = B.pack_weights(shape, synth.make_layer(cfg, "cuda", layer=2))
+    torch.cuda.synchronize()
+    stack = {kk: (None if lay[kk] is None else lay[kk].unsqueeze(0))
+             for kk in ("gate_w", "w13", "w2", "ws13", "ws2")}
+    stack["layout"] = "tiled"
+    x = synth.make_hidden(cfg, n // cfg.n_seq, 6, "cuda")   # n tokens over the sequences
+    assert x.shape[0] == n
+    idx0, w0 = B.route(shape, lay["gate_w"], x)
+    for engine in ("perslot", "dedup"):
+        nu = torch.zeros(1, dtype=torch.int32, device="cuda")
+        idx, w, y = B.stack_pass(shape, stack, x, engine, n_unique=nu)
+        nu0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if engine == "dedup":
+            y0 = B.expert_pass_dedup(shape, lay, x, idx0, w0, n_unique=nu0)
+        else:
+            y0 = B.expert_pass_perslot(shape, lay, x, idx0, w0)
+        torch.cuda.synchronize()
+        assert torch.equal(idx[0], idx0) and torch.equal(w[0], w0), engine
+        assert torch.equal(y[0], y0), engine
+        if engine == "dedup":
+            assert int(nu.item()) == int(nu0.item())
+    del lay, stack
     torch.cuda.empty_cache()
 
 
