@@ -361,8 +361,9 @@ int moe_verify_gate(int32_t n_seq, int32_t gamma, int32_t vocab, int32_t mode,
  * candidate list of up to V 8-byte entries per row, so its size is about
  * twice that of the logits (the head is not used).  With at most
  * MOE_FILTER_ONE_LAUNCH_ROWS rows, V <= MOE_FILTER_ONE_LAUNCH_VOCAB and a
- * grid of rows x ceil(V / 4096) workgroups that the device holds at once,
- * the filter is one launch whose workgroups meet at row barriers (their
+ * grid of rows x ceil(V / 4096) workgroups that the device holds at once
+ * (else rows x ceil(V / 8192), two 4096-entry chunks per workgroup), the
+ * filter is one launch whose workgroups meet at row barriers (their
  * words in the workspace carry a tag of the call, so nothing is cleared
  * between calls), else four launches; both give the same bits.  The
  * barriers' waits are bounded: should a row's workgroups fail to meet

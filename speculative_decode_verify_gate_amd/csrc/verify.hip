@@ -441,13 +441,15 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(VerifyArgs a) {
 // Two schedules run these phases with the same arithmetic, so they give the
 // same bits:
 //   one launch (rows <= kFusedRows, chunks <= kFusedChunks, and a grid the
-//     chip holds at once): each workgroup keeps its chunk in registers from
-//     the logits load to the output store, and the row's workgroups meet
-//     three times, on synchronisation words tagged with the call (nothing
-//     needs clearing between calls).  After stat every workgroup polls all
-//     the chunks' statistics and reduces them itself; after the histogram
-//     (each chunk's bins in a slot of its own) the row's first workgroup
-//     sums them, selects the bin and hands it to every workgroup's line;
+//     chip holds at once, with one chunk per workgroup or else two): each
+//     workgroup keeps its chunks from the logits load to the output store
+//     (the first in registers, a second in LDS), and the row's workgroups
+//     meet three times, on synchronisation words tagged with the call
+//     (nothing needs clearing between calls).  After stat every workgroup
+//     polls all the chunks' statistics and reduces them itself; after the
+//     histogram (each workgroup's bins in a slot of its own) the row's first
+//     workgroup sums them, selects the bin and hands it to every
+//     workgroup's line;
 //     after the gather (each chunk's candidates in a stretch of its own,
 //     their count on its line) every workgroup polls the counts and ranks a
 //     short list itself, while a long list is resolved by the first
@@ -1031,11 +1033,12 @@ __global__ __launch_bounds__(kFThreads) void filter_write_kernel(FilterArgs a) {
 // earlier call or other data left there is never taken for this call's.  A
 // value shares its 64-bit words with the tag: the low half holds the value,
 // the high half one half of the tag, and a slot is accepted when both its
-// words carry their halves.  Per chunk c of the row:
+// words carry their halves.  Per chunk c and workgroup w of the row (a
+// workgroup holds one or two consecutive chunks):
 //   stat[c]   words 0-1: chunk c's max and sum (float bits) | tag halves
 //   count[c]  words 0-1: chunk c's number of candidates | tag halves
-//   hist[c]   word 0: the tag, once chunk c's histogram slot is written
-//   out[c]    polled only by workgroup c, four tagged 32-bit values each:
+//   hist[w]   word 0: the tag, once workgroup w's histogram slot is written
+//   out[w]    polled only by workgroup w, four tagged 32-bit values each:
 //             words 0-3 the selected bin (from the row's first workgroup,
 //             which sums the histograms), words 4-7 the boundary of a long
 //             candidate list (from the same workgroup)
@@ -1082,10 +1085,11 @@ __device__ inline bool wait_tagged(unsigned *lines, int kind, unsigned n, uint64
 }
 
 // Wait (bounded) until word `word` of line t of `kind` equals the tag, for
-// every t < n.
-__device__ inline bool wait_flags(unsigned *lines, int kind, unsigned n, int word, uint64_t tag) {
+// every t < count (n lines of each kind).
+__device__ inline bool wait_flags(unsigned *lines, int kind, unsigned n, unsigned count, int word,
+                                  uint64_t tag) {
   const uint64_t *p =
-      threadIdx.x < n ? line_of(lines, kind, (int)n, threadIdx.x) + word : nullptr;
+      threadIdx.x < count ? line_of(lines, kind, (int)n, threadIdx.x) + word : nullptr;
   bool ok = p == nullptr;
   for (unsigned i = 0;; ++i) {
     if (!ok) ok = load_coherent64(p) == tag;
@@ -1096,13 +1100,13 @@ __device__ inline bool wait_flags(unsigned *lines, int kind, unsigned n, int wor
   return true;
 }
 
-// The first workgroup's result for every workgroup of the row: four 32-bit
-// values, each in a word of its own with a half of the tag (words
-// [first, first + 4) of each out line), so no store has to land before
-// another.
-__device__ inline void hand_out(unsigned *lines, unsigned n, int first, const uint32_t (&v)[4],
-                                uint64_t tag) {
-  for (unsigned i = threadIdx.x; i < n; i += kFThreads) {
+// The first workgroup's result for each of the row's `count` workgroups:
+// four 32-bit values, each in a word of its own with a half of the tag
+// (words [first, first + 4) of each out line), so no store has to land
+// before another.
+__device__ inline void hand_out(unsigned *lines, unsigned n, unsigned count, int first,
+                                const uint32_t (&v)[4], uint64_t tag) {
+  for (unsigned i = threadIdx.x; i < count; i += kFThreads) {
     uint64_t *o = line_of(lines, kOutLine, (int)n, i) + first;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -1143,19 +1147,30 @@ __device__ inline bool take_out(unsigned *lines, unsigned n, int c, int first, u
   return s_ok != 0;
 }
 
-// A wait gave up: the chunk's output is NaN, so the failure shows.
-__device__ inline void poison_chunk(float *out, int V, int c0) {
+// A wait gave up: the output of workgroup wg's chunks (the first `mine` of
+// its CPW) is NaN, so the failure shows.
+template <int CPW>
+__device__ inline void poison_chunks(float *out, int V, int wg, int mine) {
   float nan[kFPer];
 #pragma unroll
   for (int k = 0; k < kFPer; ++k) nan[k] = __builtin_nanf("");
-  store_chunk(out, V, c0, nan);
+#pragma unroll
+  for (int j = 0; j < CPW; ++j)
+    if (j < mine) store_chunk(out, V, (wg * CPW + j) * kFChunk, nan);
 }
 
-template <bool HIST>
+template <bool HIST, int CPW>
 __device__ __attribute__((always_inline)) inline void filter_fused(const FilterArgs &a) {
-  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
-  const int c0 = c * kFChunk;
-  const unsigned n = (unsigned)a.chunks;
+  static_assert(CPW == 1 || CPW == 2, "one or two chunks per workgroup");
+  const int row = blockIdx.y, wg = blockIdx.x, tid = threadIdx.x;
+  const unsigned n = (unsigned)a.chunks;    // 4096-entry chunks of the row
+  const unsigned nw = (n + CPW - 1) / CPW;  // the row's workgroups
+  // this workgroup's chunks: wg * CPW (entries from c0) and, with two per
+  // workgroup, the next one when the row has it (the same in every thread,
+  // so the per-chunk steps keep the workgroup's barriers together)
+  const int c0 = wg * CPW * kFChunk;
+  const bool two = CPW == 2 && (unsigned)(wg * CPW + 1) < n;
+  const int mine = two ? 2 : 1;
   const uint64_t tag = a.tag;
   unsigned *lines = row_lines(a, row);
   __shared__ float fs[kFWaves];
@@ -1164,17 +1179,35 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
   static_assert(kFusedChunks <= kFThreads, "a chunk per thread in the waits");
   __shared__ uint64_t res[3];                      // K, index cut, kept mass
   __shared__ uint32_t off[kFusedChunks + 1];       // candidate offsets of the chunks
-  float v[kFPer];
+  // the second chunk's probabilities between the phases (top-p, two chunks
+  // per workgroup), element k of thread t at k * kFThreads + t: the first
+  // chunk stays in registers
+  __shared__ float hold[HIST && CPW == 2 ? kFPer * kFThreads : 1];
+  float v[kFPer], u[kFPer];
   load_chunk(logits_row(a, row), a.V, c0, v, -INFINITY);
+  // (past the row: -inf fill, probability 0)
+  if constexpr (CPW == 2) load_chunk(logits_row(a, row), a.V, c0 + kFChunk, u, -INFINITY);
   float *out = probs_row(a, row);
   // the chunks' statistics: each workgroup reduces all of them itself (the
   // fixed-order reduction of the four-launch schedule)
-  const float2 cs = chunk_stat(v, a.temperature, fs);
-  if (tid == 0)
-    put_tagged(line_of(lines, kStatLine, n, c), __float_as_uint(cs.x), __float_as_uint(cs.y), tag);
+  {
+    const float2 cs = chunk_stat(v, a.temperature, fs);
+    if (tid == 0)
+      put_tagged(line_of(lines, kStatLine, n, wg * CPW), __float_as_uint(cs.x),
+                 __float_as_uint(cs.y), tag);
+  }
+  if constexpr (CPW == 2) {
+    if (two) {
+      const float2 cs = chunk_stat(u, a.temperature, fs);
+      if (tid == 0)
+        put_tagged(line_of(lines, kStatLine, n, wg * CPW + 1), __float_as_uint(cs.x),
+                   __float_as_uint(cs.y), tag);
+    }
+  }
   wait_stores();
   uint32_t lo0 = 0, lo1 = 0;
-  if (!wait_tagged(lines, kStatLine, n, tag, lo0, lo1)) return poison_chunk(out, a.V, c0);
+  if (!wait_tagged(lines, kStatLine, n, tag, lo0, lo1))
+    return poison_chunks<CPW>(out, a.V, wg, mine);
   float2 ms;
   {
     const float2 t = tid < (int)n ? make_float2(__uint_as_float(lo0), __uint_as_float(lo1))
@@ -1190,12 +1223,19 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
   }
 #pragma unroll
   for (int k = 0; k < kFPer; ++k) v[k] = prob_of(v[k], a.temperature, ms);
+  if constexpr (CPW == 2) {
+#pragma unroll
+    for (int k = 0; k < kFPer; ++k) u[k] = prob_of(u[k], a.temperature, ms);
+  }
   if (!HIST) {
     store_chunk(out, a.V, c0, v);
+    if (two) store_chunk(out, a.V, c0 + kFChunk, u);
     return;
   }
-  // the chunk's histogram into its own slot; the row's first workgroup sums
-  // them, selects the bin and hands it out
+  // the workgroup's histogram (its chunks' bins: integer masses, so how the
+  // chunks are grouped does not change the row's sums) into its own slot;
+  // the row's first workgroup sums the slots, selects the bin and hands it
+  // out
   uint64_t *part = a.hpart + (size_t)row * a.chunks * 256;
   {
     const int wave = tid >> 6;
@@ -1206,24 +1246,33 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
       if (v[k] > 0.f)
         atomicAdd(&lds[wave * 256 + ((__float_as_uint(v[k]) >> kFirstShift) & 255u)],
                   (unsigned long long)mass_of(v[k]));
+    if constexpr (CPW == 2) {
+#pragma unroll
+      for (int k = 0; k < kFPer; ++k) {
+        if (u[k] > 0.f)
+          atomicAdd(&lds[wave * 256 + ((__float_as_uint(u[k]) >> kFirstShift) & 255u)],
+                    (unsigned long long)mass_of(u[k]));
+        hold[k * kFThreads + tid] = u[k];
+      }
+    }
     __syncthreads();
-    store_coherent64(part + (size_t)c * 256 + tid,
+    store_coherent64(part + (size_t)wg * 256 + tid,
                      lds[tid] + lds[256 + tid] + lds[512 + tid] + lds[768 + tid]);
     wait_stores();
     __syncthreads();
-    if (tid == 0) store_coherent64(line_of(lines, kHistLine, n, c), tag);
+    if (tid == 0) store_coherent64(line_of(lines, kHistLine, n, wg), tag);
   }
   uint32_t prefix = 0, mask = 0xC0000000u | (255u << kFirstShift);
   uint64_t above = 0, target = 0;
   uint64_t w[2];
-  if (c == 0) {
-    if (!wait_flags(lines, kHistLine, n, 0, tag)) return poison_chunk(out, a.V, c0);
-    uint64_t h = 0;  // the row's bin tid: the chunks' counts (eight loads in flight)
-    for (unsigned q0 = 0; q0 < n; q0 += 8) {
+  if (wg == 0) {
+    if (!wait_flags(lines, kHistLine, n, nw, 0, tag)) return poison_chunks<CPW>(out, a.V, wg, mine);
+    uint64_t h = 0;  // the row's bin tid: the slots' counts (eight loads in flight)
+    for (unsigned q0 = 0; q0 < nw; q0 += 8) {
       uint64_t t[8];
 #pragma unroll
       for (unsigned j = 0; j < 8; ++j)
-        t[j] = q0 + j < n ? load_coherent64(part + (size_t)(q0 + j) * 256 + tid) : 0ull;
+        t[j] = q0 + j < nw ? load_coherent64(part + (size_t)(q0 + j) * 256 + tid) : 0ull;
 #pragma unroll
       for (unsigned j = 0; j < 8; ++j) h += t[j];
     }
@@ -1234,42 +1283,53 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
     select_level<256, false>((const uint64_t *)lds, kFirstShift, target, pf, mk, above, a.top_p);
     prefix = pf;
     // above < target <= W < 2^53: their high words leave room for the bin
-    const uint32_t v[4] = {(uint32_t)above, (uint32_t)(above >> 32) | ((pf >> kFirstShift) << 24),
-                           (uint32_t)target, (uint32_t)(target >> 32)};
-    hand_out(lines, n, 0, v, tag);
+    const uint32_t hv[4] = {(uint32_t)above, (uint32_t)(above >> 32) | ((pf >> kFirstShift) << 24),
+                            (uint32_t)target, (uint32_t)(target >> 32)};
+    hand_out(lines, n, nw, 0, hv, tag);
   } else {
-    uint32_t v[4];
-    if (!take_out(lines, n, c, 0, tag, v)) return poison_chunk(out, a.V, c0);
-    above = (uint64_t)v[0] | ((uint64_t)(v[1] & 0xFFFFFFu) << 32);
-    prefix = (v[1] >> 24) << kFirstShift;
-    target = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
+    uint32_t hv[4];
+    if (!take_out(lines, n, wg, 0, tag, hv)) return poison_chunks<CPW>(out, a.V, wg, mine);
+    above = (uint64_t)hv[0] | ((uint64_t)(hv[1] & 0xFFFFFFu) << 32);
+    prefix = (hv[1] >> 24) << kFirstShift;
+    target = (uint64_t)hv[2] | ((uint64_t)hv[3] << 32);
   }
-  // the chunk's candidates (entries in the bin) into its own stretch of the
-  // row's list, their number into its count line
+  // each chunk's candidates (entries in the bin) into its own stretch of
+  // the row's list, their number into its count line
   uint64_t *cand = a.cand + (size_t)row * a.V;
-  {
-    uint32_t mine = 0;
+  auto emit = [&](const float (&p)[kFPer], int c) {
+    uint32_t cnt = 0;
 #pragma unroll
     for (int k = 0; k < kFPer; ++k)
-      mine += ((__float_as_uint(v[k]) & mask) == prefix && v[k] > 0.f) ? 1u : 0u;
+      cnt += ((__float_as_uint(p[k]) & mask) == prefix && p[k] > 0.f) ? 1u : 0u;
     uint32_t total;
-    uint32_t at = block_exclusive(mine, total);
+    uint32_t at = block_exclusive(cnt, total);
+    const int e0 = c * kFChunk;
 #pragma unroll
     for (int g = 0; g < kFGroups; ++g) {
-      const int j = entry_of(c0, g);
+      const int j = entry_of(e0, g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t key = __float_as_uint(v[4 * g + e]);
-        if ((key & mask) == prefix && v[4 * g + e] > 0.f)
-          store_coherent64(cand + c0 + at++, (uint64_t)key | ((uint64_t)(j + e) << 32));
+        const uint32_t key = __float_as_uint(p[4 * g + e]);
+        if ((key & mask) == prefix && p[4 * g + e] > 0.f)
+          store_coherent64(cand + e0 + at++, (uint64_t)key | ((uint64_t)(j + e) << 32));
       }
     }
     wait_stores();
     __syncthreads();
     if (tid == 0) put_tagged(line_of(lines, kCountLine, n, c), total, total, tag);
+  };
+  emit(v, wg * CPW);
+  if constexpr (CPW == 2) {
+    if (two) {
+      float t[kFPer];
+#pragma unroll
+      for (int k = 0; k < kFPer; ++k) t[k] = hold[k * kFThreads + tid];
+      emit(t, wg * CPW + 1);
+    }
   }
   wait_stores();
-  if (!wait_tagged(lines, kCountLine, n, tag, lo0, lo1)) return poison_chunk(out, a.V, c0);
+  if (!wait_tagged(lines, kCountLine, n, tag, lo0, lo1))
+    return poison_chunks<CPW>(out, a.V, wg, mine);
   uint32_t nc;
   {
     const uint32_t k_t = tid < (int)n ? lo0 : 0u;
@@ -1295,35 +1355,44 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
     __syncthreads();
     w[0] = res[0] | (res[1] << 32);
     w[1] = res[2];
-  } else if (c == 0) {
+  } else if (wg == 0) {
     // a long list: the first workgroup resolves it and hands the result out
     resolve_row(load, nc, prefix, mask, above, target, lds, res);
     __syncthreads();
     w[0] = res[0] | (res[1] << 32);
     w[1] = res[2];
-    const uint32_t v[4] = {(uint32_t)res[0], (uint32_t)res[1], (uint32_t)res[2],
-                           (uint32_t)(res[2] >> 32)};
-    hand_out(lines, n, 4, v, tag);
+    const uint32_t rv[4] = {(uint32_t)res[0], (uint32_t)res[1], (uint32_t)res[2],
+                            (uint32_t)(res[2] >> 32)};
+    hand_out(lines, n, nw, 4, rv, tag);
   } else {
-    uint32_t v[4];
-    if (!take_out(lines, n, c, 4, tag, v)) return poison_chunk(out, a.V, c0);
-    w[0] = (uint64_t)v[0] | ((uint64_t)v[1] << 32);
-    w[1] = (uint64_t)v[2] | ((uint64_t)v[3] << 32);
+    uint32_t rv[4];
+    if (!take_out(lines, n, wg, 4, tag, rv)) return poison_chunks<CPW>(out, a.V, wg, mine);
+    w[0] = (uint64_t)rv[0] | ((uint64_t)rv[1] << 32);
+    w[1] = (uint64_t)rv[2] | ((uint64_t)rv[3] << 32);
   }
   write_chunk(out, a.V, c0, v, (uint32_t)w[0], w[0] >> 32, w[1]);
+  if constexpr (CPW == 2) {
+    if (two) {
+      float t[kFPer];
+#pragma unroll
+      for (int k = 0; k < kFPer; ++k) t[k] = hold[k * kFThreads + tid];
+      write_chunk(out, a.V, c0 + kFChunk, t, (uint32_t)w[0], w[0] >> 32, w[1]);
+    }
+  }
 }
 
 template <bool HIST>
 __global__ __launch_bounds__(kFThreads) void filter_fused_kernel(FilterArgs a) {
-  filter_fused<HIST>(a);
+  filter_fused<HIST, 1>(a);
 }
 
-// The same schedule held to 7 waves per SIMD (a few registers spilled):
-// one more workgroup per CU, for grids between the two kernels' capacities
-// (a call of 68 rows of 102,400 entries).
-__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(7))) void
-filter_fused_dense_kernel(FilterArgs a) {
-  filter_fused<true>(a);
+// Two chunks per workgroup (the second one's probabilities held in LDS),
+// for grids past the one-chunk kernel's capacity (a call of 68 rows of
+// 102,400 or 129,280 entries): half the workgroups, each holding twice the
+// entries.
+template <bool HIST>
+__global__ __launch_bounds__(kFThreads) void filter_fused_pair_kernel(FilterArgs a) {
+  filter_fused<HIST, 2>(a);
 }
 
 }  // namespace
@@ -1360,10 +1429,11 @@ uint64_t next_tag() {
 // their workgroups are placed: still correct, but slower.  Measured (V =
 // 32,000 to 129,280, top_p = 0.9), the one launch is faster than the four
 // up to this many workgroups and slower beyond it.
-// kind: 0 the softmax-only kernel, 1 the top-p kernel, 2 its dense copy.
+// kind: 0 the softmax-only kernel, 1 the top-p kernel, 2 and 3 the same
+// with two chunks per workgroup.
 int fused_capacity(int kind) {
   constexpr int kDevices = 64;
-  static std::atomic<int> cache[3][kDevices];
+  static std::atomic<int> cache[4][kDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
   int cap = cache[kind][dev].load(std::memory_order_relaxed);
@@ -1371,7 +1441,8 @@ int fused_capacity(int kind) {
   int per_cu = 0, cus = 0;
   const void *k = kind == 0   ? (const void *)filter_fused_kernel<false>
                   : kind == 1 ? (const void *)filter_fused_kernel<true>
-                              : (const void *)filter_fused_dense_kernel;
+                  : kind == 2 ? (const void *)filter_fused_pair_kernel<false>
+                              : (const void *)filter_fused_pair_kernel<true>;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kFThreads, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -1427,17 +1498,25 @@ hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int 
   a.hpart = (uint64_t *)b;
   const dim3 grid(a.chunks, rows);
   if (filter_one_launch(rows, V)) {
-    const long long wgs = (long long)rows * a.chunks;
+    // the first kernel whose grid the chip holds at once: one chunk per
+    // workgroup, else two
     const bool hist = top_p < 1.f;
-    const bool fits = wgs <= fused_capacity(hist ? 1 : 0);
-    if (fits || (hist && wgs <= fused_capacity(2))) {
+    const int pairs = (a.chunks + 1) / 2;
+    const dim3 grid2(pairs, rows);
+    if ((long long)rows * a.chunks <= fused_capacity(hist ? 1 : 0)) {
       a.tag = next_tag();
-      if (!hist)
-        hipLaunchKernelGGL(filter_fused_kernel<false>, grid, dim3(kFThreads), 0, st, a);
-      else if (fits)
+      if (hist)
         hipLaunchKernelGGL(filter_fused_kernel<true>, grid, dim3(kFThreads), 0, st, a);
       else
-        hipLaunchKernelGGL(filter_fused_dense_kernel, grid, dim3(kFThreads), 0, st, a);
+        hipLaunchKernelGGL(filter_fused_kernel<false>, grid, dim3(kFThreads), 0, st, a);
+      return hipGetLastError();
+    }
+    if ((long long)rows * pairs <= fused_capacity(hist ? 3 : 2)) {
+      a.tag = next_tag();
+      if (hist)
+        hipLaunchKernelGGL(filter_fused_pair_kernel<true>, grid2, dim3(kFThreads), 0, st, a);
+      else
+        hipLaunchKernelGGL(filter_fused_pair_kernel<false>, grid2, dim3(kFThreads), 0, st, a);
       return hipGetLastError();
     }
   }

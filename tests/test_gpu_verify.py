@@ -237,14 +237,15 @@ def test_filter_more_workgroups_than_the_chip_holds_at_once():
     _check_nucleus(got, lg, 0.8, 0.9)
 
 
-@pytest.mark.parametrize("V,top_p", [(102400, 0.9), (4099, 0.5), (129280, 1.0), (32000, 0.95)])
+@pytest.mark.parametrize("V,top_p", [(102400, 0.9), (4099, 0.5), (129280, 1.0), (129280, 0.9),
+                                     (32000, 0.95)])
 def test_filter_one_launch_equals_four_launches(V, top_p):
     """The same rows filtered in a call of more than FILTER_ONE_LAUNCH_ROWS
     rows (four launches), in calls of 16 rows (at most 512 workgroups, which
     the chip holds at once: one launch whose workgroups meet at row
-    barriers) and in a call of 68 rows: bit for bit the same, with rows
-    whose boundary bin holds long candidate lists (radix resolve) among
-    them; no call writes the workspace head."""
+    barriers) and in a call of 68 rows (at V = 102,400 and 129,280 two
+    chunks per workgroup): bit for bit the same, with rows whose boundary bin holds long candidate lists (radix
+    resolve) among them; no call writes the workspace head."""
     R = B.FILTER_ONE_LAUNCH_ROWS
     rng = np.random.default_rng(V + int(top_p * 100) + 7)
     _say(f"[filter] one launch vs four, V={V} top_p={top_p}")
@@ -263,12 +264,39 @@ def test_filter_one_launch_equals_four_launches(V, top_p):
         torch.cuda.synchronize()
         assert int(ws.buf[:256].count_nonzero()) == 0
         assert torch.equal(four[r0:r0 + 16].view(torch.int32), one.view(torch.int32)), r0
-    # 68 rows: at V = 102,400, 1,700 workgroups, more than the one-launch
-    # kernel holds at six per CU (the denser copy of it takes them)
+    # 68 rows: at V = 102,400, 1,700 one-chunk workgroups, more than the
+    # one-launch kernel holds at six per CU (two chunks per workgroup take
+    # them)
     one = B.verify_probs(dev[:68], 0.7, top_p, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(four[:68].view(torch.int32), one.view(torch.int32))
     _check_nucleus(four[:8].cpu().numpy(), lg[:8], 0.7, top_p)
+
+
+@pytest.mark.parametrize("top_p", [0.9, 1.0])
+def test_filter_two_chunks_per_workgroup(top_p):
+    """32 rows of 63 chunks minus a ragged tail (2,016 workgroups at one
+    chunk each, more than either one-chunk kernel holds at once): one launch
+    with two chunks per workgroup, the last workgroup of each row holding
+    one, bit for bit what the four launches of a 136-row call give, with
+    tied rows (long candidate lists) among them."""
+    V = 63 * 4096 - 100
+    rng = np.random.default_rng(63 + int(top_p * 10))
+    _say(f"[filter] two chunks per workgroup, V={V} top_p={top_p}")
+    lg = _logit_rows(rng, B.FILTER_ONE_LAUNCH_ROWS + 8, V, masked=True)
+    lg[1, : V // 2] = lg[1, :1]                    # a long candidate list
+    lg[4] = 0.25                                   # every entry tied
+    lg[7, 4096:] = -np.inf                         # all mass in the first chunk
+    lg[9, : V - 50] = -np.inf                      # all mass in the last one
+    dev = torch.from_numpy(lg).cuda()
+    ws = B.Workspace()
+    four = B.verify_probs(dev, 0.8, top_p, ws=ws).clone()
+    for r0 in (0, 32):
+        one = B.verify_probs(dev[r0:r0 + 32], 0.8, top_p, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.buf[:256].count_nonzero()) == 0
+        assert torch.equal(four[r0:r0 + 32].view(torch.int32), one.view(torch.int32)), r0
+    _check_nucleus(four[:10].cpu().numpy(), lg[:10], 0.8, top_p)
 
 
 def test_filter_one_launch_at_the_longest_vocabulary():
