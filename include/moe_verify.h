@@ -392,6 +392,16 @@ int moe_verify_probs_pair(int32_t rows_p, const float *logits_p, float *probs_p,
                           float temperature, float top_p, void *workspace,
                           size_t *workspace_bytes, void *stream);
 
+/* For tests of the one-launch filter's failure path: the number of polls
+ * after which a workgroup waiting at a row barrier of moe_verify_probs /
+ * moe_verify_probs_pair gives up and writes NaN over its chunks of the
+ * output (0 restores the default, about a second of polling).  A small
+ * limit makes workgroups give up while the others are still on their way,
+ * so some outputs come out NaN; every call still ends.  Applies to calls
+ * made after it, process-wide; the four-launch filter and every other call
+ * have no such waits.  Always MOE_OK. */
+int moe_filter_spin_limit(uint32_t polls);
+
 /* Human-readable name of a status code (static storage). */
 const char *moe_status_string(int status);
 

@@ -75,6 +75,7 @@ def load():
     lib.moe_pack_weights.argtypes = [P, i32, P, P, P, P, P]
     lib.moe_status_string.argtypes = [C.c_int]
     lib.moe_status_string.restype = C.c_char_p
+    lib.moe_filter_spin_limit.argtypes = [C.c_uint32]
     lib.moe_timing_enable.argtypes = [C.c_int]
     lib.moe_timing_read.argtypes = [P, P]
     lib.moe_verify_gate.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
@@ -484,6 +485,13 @@ def verify_probs_pair(logits_p, logits_q, temperature, top_p=1.0, *, out_p=None,
                                      _ptr(out_q), V, float(temperature), float(top_p), _ptr(buf),
                                      C.byref(have), _stream()))
     return out_p, out_q
+
+
+def filter_spin_limit(polls=0):
+    """Polls after which a one-launch filter workgroup stops waiting at a row
+    barrier and writes NaN over its chunks (moe_filter_spin_limit; 0: the
+    default).  For tests of that failure path."""
+    _check("moe_filter_spin_limit", load().moe_filter_spin_limit(int(polls)))
 
 
 def timing_enable(kinds=KERNEL_KINDS):

@@ -433,6 +433,11 @@ int moe_verify_probs_pair(int32_t rows_p, const float *logits_p, float *probs_p,
                       top_p, ws, ws_bytes, stream);
 }
 
+int moe_filter_spin_limit(uint32_t polls) {
+  moe::set_filter_spin_limit(polls);
+  return MOE_OK;
+}
+
 int moe_expert_pass_perslot(const moe_shape *s, const moe_expert_weights *w, const float *x,
                             int32_t n, const int32_t *idx, const float *tw, float *y,
                             void *ws, size_t *ws_bytes, void *stream) {

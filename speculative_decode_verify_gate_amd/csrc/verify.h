@@ -22,6 +22,9 @@ hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, 
 // launches: one when filter_one_launch(rows, V) and the grid fits the device
 // at once, else four.
 size_t filter_ws_bytes(int rows, int V);
+// Polls of a row barrier before a one-launch workgroup gives up and writes
+// NaN over its chunks (0: the default, about a second).
+void set_filter_spin_limit(unsigned polls);
 bool filter_one_launch(int rows, int V);
 hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int rows_b,
                          const float *logits_b, float *probs_b, int V, float temperature,

@@ -478,7 +478,7 @@ constexpr int kFirstShift = 22;             // first level: bits 29-22, 256 bins
 constexpr int kFusedRows = MOE_FILTER_ONE_LAUNCH_ROWS;
 constexpr int kFusedChunks = MOE_FILTER_ONE_LAUNCH_VOCAB / kFChunk;
 static_assert(MOE_FILTER_ONE_LAUNCH_VOCAB % kFChunk == 0, "whole chunks");
-constexpr unsigned kSpinLimit = 1u << 20;  // polls of a row barrier before it gives up
+constexpr unsigned kSpinLimit = 1u << 20;  // polls of a row barrier before it gives up (default)
 
 struct FilterArgs {
   int V, chunks;
@@ -499,6 +499,7 @@ struct FilterArgs {
   unsigned *count;     // [rows][4]: arrivals (prob, gather), candidates
   unsigned *sync;      // one launch: [rows][4 chunks] 128-byte synchronisation lines
   uint64_t tag;        // one launch: this call's tag (distinct per call, halves non-zero)
+  unsigned spin;       // one launch: polls of a row barrier before it gives up
   uint64_t *hpart;     // one launch: [rows][chunks][256] the chunks' first-level histograms
 };
 
@@ -1065,7 +1066,7 @@ __device__ inline void put_tagged(uint64_t *w, uint32_t v0, uint32_t v1, uint64_
 // t < n; thread t < n gets its line's two value halves.  False if the wait
 // gave up (the same in every thread).
 __device__ inline bool wait_tagged(unsigned *lines, int kind, unsigned n, uint64_t tag,
-                                   uint32_t &v0, uint32_t &v1) {
+                                   unsigned spin, uint32_t &v0, uint32_t &v1) {
   const uint64_t *p = threadIdx.x < n ? line_of(lines, kind, (int)n, threadIdx.x) : nullptr;
   uint64_t w0 = 0, w1 = 0;
   bool ok = p == nullptr;
@@ -1076,7 +1077,7 @@ __device__ inline bool wait_tagged(unsigned *lines, int kind, unsigned n, uint64
       ok = (uint32_t)(w0 >> 32) == (uint32_t)tag && (uint32_t)(w1 >> 32) == (uint32_t)(tag >> 32);
     }
     if (__syncthreads_and(ok)) break;
-    if (i == kSpinLimit) return false;
+    if (i >= spin) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   v0 = (uint32_t)w0;
@@ -1087,14 +1088,14 @@ __device__ inline bool wait_tagged(unsigned *lines, int kind, unsigned n, uint64
 // Wait (bounded) until word `word` of line t of `kind` equals the tag, for
 // every t < count (n lines of each kind).
 __device__ inline bool wait_flags(unsigned *lines, int kind, unsigned n, unsigned count, int word,
-                                  uint64_t tag) {
+                                  uint64_t tag, unsigned spin) {
   const uint64_t *p =
       threadIdx.x < count ? line_of(lines, kind, (int)n, threadIdx.x) + word : nullptr;
   bool ok = p == nullptr;
   for (unsigned i = 0;; ++i) {
     if (!ok) ok = load_coherent64(p) == tag;
     if (__syncthreads_and(ok)) break;
-    if (i == kSpinLimit) return false;
+    if (i >= spin) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   return true;
@@ -1118,7 +1119,7 @@ __device__ inline void hand_out(unsigned *lines, unsigned n, unsigned count, int
 // carry the tag, then every thread gets the values.  False if the wait gave
 // up.
 __device__ inline bool take_out(unsigned *lines, unsigned n, int c, int first, uint64_t tag,
-                                uint32_t (&v)[4]) {
+                                unsigned spin, uint32_t (&v)[4]) {
   __shared__ uint32_t s_v[4];
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
@@ -1133,7 +1134,7 @@ __device__ inline bool take_out(unsigned *lines, unsigned n, int c, int first, u
         all = all && (uint32_t)(x >> 32) == (uint32_t)(k & 1 ? tag >> 32 : tag);
       }
       if (all) break;
-      if (i == kSpinLimit) {
+      if (i >= spin) {
         ok = 0;
         break;
       }
@@ -1206,7 +1207,7 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
   }
   wait_stores();
   uint32_t lo0 = 0, lo1 = 0;
-  if (!wait_tagged(lines, kStatLine, n, tag, lo0, lo1))
+  if (!wait_tagged(lines, kStatLine, n, tag, a.spin, lo0, lo1))
     return poison_chunks<CPW>(out, a.V, wg, mine);
   float2 ms;
   {
@@ -1266,7 +1267,7 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
   uint64_t above = 0, target = 0;
   uint64_t w[2];
   if (wg == 0) {
-    if (!wait_flags(lines, kHistLine, n, nw, 0, tag)) return poison_chunks<CPW>(out, a.V, wg, mine);
+    if (!wait_flags(lines, kHistLine, n, nw, 0, tag, a.spin)) return poison_chunks<CPW>(out, a.V, wg, mine);
     uint64_t h = 0;  // the row's bin tid: the slots' counts (eight loads in flight)
     for (unsigned q0 = 0; q0 < nw; q0 += 8) {
       uint64_t t[8];
@@ -1288,7 +1289,7 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
     hand_out(lines, n, nw, 0, hv, tag);
   } else {
     uint32_t hv[4];
-    if (!take_out(lines, n, wg, 0, tag, hv)) return poison_chunks<CPW>(out, a.V, wg, mine);
+    if (!take_out(lines, n, wg, 0, tag, a.spin, hv)) return poison_chunks<CPW>(out, a.V, wg, mine);
     above = (uint64_t)hv[0] | ((uint64_t)(hv[1] & 0xFFFFFFu) << 32);
     prefix = (hv[1] >> 24) << kFirstShift;
     target = (uint64_t)hv[2] | ((uint64_t)hv[3] << 32);
@@ -1328,7 +1329,7 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
     }
   }
   wait_stores();
-  if (!wait_tagged(lines, kCountLine, n, tag, lo0, lo1))
+  if (!wait_tagged(lines, kCountLine, n, tag, a.spin, lo0, lo1))
     return poison_chunks<CPW>(out, a.V, wg, mine);
   uint32_t nc;
   {
@@ -1366,7 +1367,7 @@ __device__ __attribute__((always_inline)) inline void filter_fused(const FilterA
     hand_out(lines, n, nw, 4, rv, tag);
   } else {
     uint32_t rv[4];
-    if (!take_out(lines, n, wg, 4, tag, rv)) return poison_chunks<CPW>(out, a.V, wg, mine);
+    if (!take_out(lines, n, wg, 4, tag, a.spin, rv)) return poison_chunks<CPW>(out, a.V, wg, mine);
     w[0] = (uint64_t)rv[0] | ((uint64_t)rv[1] << 32);
     w[1] = (uint64_t)rv[2] | ((uint64_t)rv[3] << 32);
   }
@@ -1424,6 +1425,9 @@ uint64_t next_tag() {
   return z;
 }
 
+// Polls of a row barrier before a one-launch workgroup gives up.
+std::atomic<unsigned> g_spin{kSpinLimit};
+
 // Workgroups of the one-launch kernel the current device holds at once (0
 // if unknown).  Beyond that, rows wait for earlier rows to finish before
 // their workgroups are placed: still correct, but slower.  Measured (V =
@@ -1452,6 +1456,10 @@ int fused_capacity(int kind) {
 }
 
 }  // namespace
+
+void set_filter_spin_limit(unsigned polls) {
+  g_spin.store(polls ? polls : kSpinLimit, std::memory_order_relaxed);
+}
 
 size_t filter_ws_bytes(int rows, int V) {
   const size_t ch = (size_t)filter_chunks(V);
@@ -1496,6 +1504,7 @@ hipError_t launch_filter(int rows_a, const float *logits_a, float *probs_a, int 
   a.sync = (unsigned *)b;
   b += align_up((size_t)rows * kRowLines * a.chunks * kLineWords * sizeof(unsigned), 256);
   a.hpart = (uint64_t *)b;
+  a.spin = g_spin.load(std::memory_order_relaxed);
   const dim3 grid(a.chunks, rows);
   if (filter_one_launch(rows, V)) {
     // the first kernel whose grid the chip holds at once: one chunk per

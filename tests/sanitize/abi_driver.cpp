@@ -95,6 +95,8 @@ hipError_t launch_verify(int n_seq, int gamma, int V, int mode, const float *p, 
   return hipSuccess;
 }
 size_t filter_ws_bytes(int rows, int V) { return (size_t)rows * (V / 4096 + 1) * 4200; }
+static unsigned g_spin_limit = 0;
+void set_filter_spin_limit(unsigned polls) { g_spin_limit = polls; }
 hipError_t launch_filter(int rows_a, const float *lg_a, float *out_a, int rows_b,
                          const float *lg_b, float *out_b, int V, float T, float top_p, void *ws,
                          hipStream_t) {
@@ -251,6 +253,9 @@ int main() {
   CHECK(moe_verify_probs_pair(36, (float *)fake(), (float *)fake(1u << 30), 32,
                               (float *)fake(2u << 30), (float *)fake(1u << 30), 129280, 0.7f, 0.9f,
                               nullptr, &nb2, nullptr) == MOE_ERR_INVALID_ARG);  // outputs overlap
+  // the filter's barrier limit: passed through, 0 restores the default
+  CHECK(moe_filter_spin_limit(3) == MOE_OK && moe::g_spin_limit == 3);
+  CHECK(moe_filter_spin_limit(0) == MOE_OK && moe::g_spin_limit == 0);
   std::printf("abi driver: %d launches described, %d failed checks\n", moe::g_launches, g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -299,6 +299,46 @@ def test_filter_two_chunks_per_workgroup(top_p):
     _check_nucleus(four[:10].cpu().numpy(), lg[:10], 0.8, top_p)
 
 
+@pytest.mark.parametrize("rows,V", [(36, 102400), (68, 129280)])
+def test_filter_barrier_timeout_writes_nan_and_ends(rows, V):
+    """The one-launch filter's failure path, forced from the host: with the
+    row barriers' waits cut to two polls, workgroups give up while the row's
+    others are still on their way.  The call still ends, each 4096-entry
+    chunk of the output is either NaN throughout (its workgroup gave up) or
+    bit for bit the normal result, some chunks are NaN, the workspace head
+    stays zero, and with the default limit back the next call (a new tag,
+    nothing cleared) is exact again."""
+    rng = np.random.default_rng(rows)
+    _say(f"[filter] barrier time-out, rows={rows} V={V}")
+    lg = torch.from_numpy(_logit_rows(rng, rows, V, masked=True)).cuda()
+    ws = B.Workspace()
+    ref = B.verify_probs(lg, 0.7, 0.9, ws=ws).clone()
+    torch.cuda.synchronize()
+    try:
+        B.filter_spin_limit(1)
+        got = B.verify_probs(lg, 0.7, 0.9, ws=ws).clone()
+        torch.cuda.synchronize()
+    finally:
+        B.filter_spin_limit(0)
+    assert int(ws.buf[:256].count_nonzero()) == 0
+    g, r = got.cpu().numpy(), ref.cpu().numpy()
+    n_nan = 0
+    for row in range(rows):
+        for c0 in range(0, V, 4096):
+            gc, rc = g[row, c0:c0 + 4096], r[row, c0:c0 + 4096]
+            isn = np.isnan(gc)
+            if isn.any():
+                assert isn.all(), (row, c0)
+                n_nan += 1
+            else:
+                np.testing.assert_array_equal(gc.view(np.int32), rc.view(np.int32))
+    _say(f"   {n_nan} of {rows * ((V + 4095) // 4096)} chunks gave up")
+    assert n_nan > 0
+    again = B.verify_probs(lg, 0.7, 0.9, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int32), ref.view(torch.int32))
+
+
 def test_filter_one_launch_at_the_longest_vocabulary():
     """FILTER_ONE_LAUNCH_VOCAB entries (64 workgroups per row, each reading
     every chunk's statistics and candidate count): 8 rows in one launch,
