@@ -1077,7 +1077,7 @@ __device__ inline bool wait_tagged(unsigned *lines, int kind, unsigned n, uint64
       ok = (uint32_t)(w0 >> 32) == (uint32_t)tag && (uint32_t)(w1 >> 32) == (uint32_t)(tag >> 32);
     }
     if (__syncthreads_and(ok)) break;
-    if (i >= spin) return false;
+    if (i + 1 >= spin) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   v0 = (uint32_t)w0;
@@ -1095,7 +1095,7 @@ __device__ inline bool wait_flags(unsigned *lines, int kind, unsigned n, unsigne
   for (unsigned i = 0;; ++i) {
     if (!ok) ok = load_coherent64(p) == tag;
     if (__syncthreads_and(ok)) break;
-    if (i >= spin) return false;
+    if (i + 1 >= spin) return false;
     __builtin_amdgcn_s_sleep(1);
   }
   return true;
@@ -1134,7 +1134,7 @@ __device__ inline bool take_out(unsigned *lines, unsigned n, int c, int first, u
         all = all && (uint32_t)(x >> 32) == (uint32_t)(k & 1 ? tag >> 32 : tag);
       }
       if (all) break;
-      if (i >= spin) {
+      if (i + 1 >= spin) {
         ok = 0;
         break;
       }

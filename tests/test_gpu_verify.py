@@ -302,12 +302,15 @@ def test_filter_two_chunks_per_workgroup(top_p):
 @pytest.mark.parametrize("rows,V", [(36, 102400), (68, 129280)])
 def test_filter_barrier_timeout_writes_nan_and_ends(rows, V):
     """The one-launch filter's failure path, forced from the host: with the
-    row barriers' waits cut to two polls, workgroups give up while the row's
-    others are still on their way.  The call still ends, each 4096-entry
-    chunk of the output is either NaN throughout (its workgroup gave up) or
-    bit for bit the normal result, some chunks are NaN, the workspace head
-    stays zero, and with the default limit back the next call (a new tag,
-    nothing cleared) is exact again."""
+    row barriers' waits cut to one poll, workgroups give up while the row's
+    others are still on their way.  Some must: the bin a workgroup waits for
+    after its histogram can only be handed out after the first workgroup has
+    seen that workgroup's flag and summed every slot, several memory round
+    trips after the one poll.  The call still ends, each 4096-entry chunk of
+    the output is either NaN throughout (its workgroup gave up) or bit for
+    bit the normal result, the workspace head stays zero, and with the
+    default limit back the next call (a new tag, nothing cleared) is exact
+    again."""
     rng = np.random.default_rng(rows)
     _say(f"[filter] barrier time-out, rows={rows} V={V}")
     lg = torch.from_numpy(_logit_rows(rng, rows, V, masked=True)).cuda()
